@@ -1,0 +1,220 @@
+"""Plain CPU oracle for the FP8 GEMM path (dense, masked grouped, contiguous grouped).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product path (the HIP library and its
+Python binding) never imports this package, and this package imports nothing
+from the product.
+
+The arithmetic lives in ``fp8_oracle.c`` (plain C99, FP64, built with
+``-O2 -ffp-contract=off`` so no multiply-add is fused); this module only
+marshals numpy arrays into it.  What it computes and the readings it takes are
+documented at the top of ``fp8_oracle.c``:
+
+* decode of E4M3 / E5M2 codes ("DeepGEMM: FP8 matrix-multiply kernels on
+  Hopper Tensor Cores", section 3.1),
+* the naive per-element inner product (same page, section 2.1) in FP64,
+* one per-tensor scale product applied at the output (same page, sections 3.1
+  and 5.2),
+* BF16 round-to-nearest-even in one rounding,
+* the masked and contiguous grouped forms ("One transpose, half the compute:
+  the DeepSeek SwapAB story", sections 2 and 3.1-3.3).
+
+Every function here is pinned by ``tests/test_oracle_*.py`` against things other
+than itself: torch's FP8 conversions, exact rational arithmetic, closed forms,
+numpy float64 matmul on decoded values, and invariants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+E4M3 = 0
+E5M2 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp8_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile fp8_oracle.c into liboracle.so with the host C compiler."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        cmd = ["gcc", "-std=gnu99", "-O2", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-pthread", _SRC, "-o", _LIB + ".tmp", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    F = ctypes.c_float
+    lib.oracle_decode_table.argtypes = [I, P]
+    lib.oracle_decode_table.restype = I
+    lib.oracle_bf16_rne.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_gemm_nt.argtypes = [P, I64, I, P, I64, I, F, F, P, I64, P, P, P, I64, I64, I64, I]
+    lib.oracle_gemm_nt.restype = I
+    lib.oracle_gemm_nt_points.argtypes = [P, I64, I, P, I64, I, F, F, I64, I64, P, P, P, P, P, P]
+    lib.oracle_gemm_nt_points.restype = I
+    lib.oracle_grouped_masked.argtypes = [P, I, P, I, F, P, P, P, P, P, P, I64, I64, I64, I64, I]
+    lib.oracle_grouped_masked.restype = I
+    lib.oracle_grouped_contig.argtypes = [P, I, P, I, F, P, P, P, P, P, P, I64, I64, I64, I64, I]
+    lib.oracle_grouped_contig.restype = I
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def decode_table(fmt: int) -> np.ndarray:
+    """256-entry float64 table: value of each FP8 code in format ``fmt``."""
+    out = np.empty(256, dtype=np.float64)
+    if _load().oracle_decode_table(int(fmt), _ptr(out)) != 0:
+        raise ValueError(f"unknown FP8 format {fmt}")
+    return out
+
+
+def bf16_rne(x: float) -> int:
+    """BF16 bits of ``x`` rounded to nearest, ties to even, in one rounding."""
+    return int(_load().oracle_bf16_rne(float(x)))
+
+
+def _u8(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint8:
+        raise TypeError("FP8 operands are passed as uint8 code arrays")
+    return a
+
+
+def gemm_nt(A, B, a_fmt=E4M3, b_fmt=E4M3, sa=1.0, sb=1.0, want_exact=False, threads=None):
+    """Dense D = bf16(sa*sb * A . B^T).  A: uint8 [M, K], B: uint8 [N, K].
+
+    Returns (D_bits uint16 [M, N], R float64 [M, N], S float64 [M, N], EX or None)
+    where R is the scaled FP64 value before rounding and S = sum_k |a_ik b_jk|
+    (unscaled).  EX[i, j] is 1 when the FP64 sum equals the exact integer sum,
+    0 when it does not, 2 when a non-finite input is involved.
+    """
+    A = _u8(A)
+    B = _u8(B)
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A and B disagree on K")
+    D = np.zeros((M, N), dtype=np.uint16)
+    R = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    EX = np.zeros((M, N), dtype=np.uint8) if want_exact else None
+    rc = _load().oracle_gemm_nt(_ptr(A), K, int(a_fmt), _ptr(B), K, int(b_fmt),
+                                float(sa), float(sb), _ptr(D), N, _ptr(R), _ptr(S), _ptr(EX),
+                                M, N, K, threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_nt failed ({rc})")
+    return D, R, S, EX
+
+
+def gemm_nt_points(A, B, ii, jj, a_fmt=E4M3, b_fmt=E4M3, sa=1.0, sb=1.0, want_exact=False):
+    """Dense D at selected elements (ii[p], jj[p]) only.  Same outputs as gemm_nt, 1-D."""
+    A = _u8(A)
+    B = _u8(B)
+    K = A.shape[1]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    if ii.shape != jj.shape:
+        raise ValueError("ii and jj differ in length")
+    if ii.size and (ii.min() < 0 or ii.max() >= A.shape[0] or jj.min() < 0 or jj.max() >= B.shape[0]):
+        raise IndexError("sample point outside the output")
+    n = ii.size
+    D = np.zeros(n, dtype=np.uint16)
+    R = np.zeros(n, dtype=np.float64)
+    S = np.zeros(n, dtype=np.float64)
+    EX = np.zeros(n, dtype=np.uint8) if want_exact else None
+    rc = _load().oracle_gemm_nt_points(_ptr(A), K, int(a_fmt), _ptr(B), K, int(b_fmt),
+                                       float(sa), float(sb), K, n, _ptr(ii), _ptr(jj),
+                                       _ptr(D), _ptr(R), _ptr(S), _ptr(EX))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_nt_points failed ({rc})")
+    return D, R, S, EX
+
+
+def grouped_masked(A, B, masked_m, scale_b, a_fmt=E4M3, b_fmt=E4M3, sa=1.0, D_init=None,
+                   want_exact=False, threads=None):
+    """Masked grouped GEMM.  A: uint8 [G, cap, K]; B: uint8 [G, N, K];
+    masked_m: int32 [G]; scale_b: float32 [G].
+
+    Returns (D_bits [G, cap, N], R, S, EX).  Rows i >= clamp(masked_m[g], 0, cap)
+    keep D_init's contents (default 0) and R = S = NaN there.
+    """
+    A = _u8(A)
+    B = _u8(B)
+    G, cap, K = A.shape
+    G2, N, K2 = B.shape
+    if G2 != G or K2 != K:
+        raise ValueError("A and B disagree on G or K")
+    masked_m = np.ascontiguousarray(masked_m, dtype=np.int32)
+    scale_b = np.ascontiguousarray(scale_b, dtype=np.float32)
+    if masked_m.shape != (G,) or scale_b.shape != (G,):
+        raise ValueError("masked_m and scale_b need one entry per group")
+    D = np.zeros((G, cap, N), dtype=np.uint16) if D_init is None else np.array(D_init, dtype=np.uint16, copy=True)
+    R = np.full((G, cap, N), np.nan)
+    S = np.full((G, cap, N), np.nan)
+    EX = np.zeros((G, cap, N), dtype=np.uint8) if want_exact else None
+    rc = _load().oracle_grouped_masked(_ptr(A), int(a_fmt), _ptr(B), int(b_fmt), float(sa),
+                                       _ptr(scale_b), _ptr(masked_m), _ptr(D), _ptr(R), _ptr(S),
+                                       _ptr(EX), G, cap, N, K, threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_grouped_masked failed ({rc})")
+    return D, R, S, EX
+
+
+def grouped_contig(A, B, grp_idx, scale_b, a_fmt=E4M3, b_fmt=E4M3, sa=1.0, D_init=None,
+                   want_exact=False, threads=None):
+    """Contiguous grouped GEMM.  A: uint8 [M_total, K]; B: uint8 [G, N, K];
+    grp_idx: int32 [M_total]; scale_b: float32 [G].
+
+    Returns (D_bits [M_total, N], R, S, EX).  Padding rows (grp_idx outside
+    [0, G)) keep D_init's contents (default 0) and R = S = NaN there.
+    """
+    A = _u8(A)
+    B = _u8(B)
+    M_total, K = A.shape
+    G, N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A and B disagree on K")
+    grp_idx = np.ascontiguousarray(grp_idx, dtype=np.int32)
+    scale_b = np.ascontiguousarray(scale_b, dtype=np.float32)
+    if grp_idx.shape != (M_total,) or scale_b.shape != (G,):
+        raise ValueError("grp_idx needs one entry per row, scale_b one per group")
+    D = np.zeros((M_total, N), dtype=np.uint16) if D_init is None else np.array(D_init, dtype=np.uint16, copy=True)
+    R = np.full((M_total, N), np.nan)
+    S = np.full((M_total, N), np.nan)
+    EX = np.zeros((M_total, N), dtype=np.uint8) if want_exact else None
+    rc = _load().oracle_grouped_contig(_ptr(A), int(a_fmt), _ptr(B), int(b_fmt), float(sa),
+                                       _ptr(scale_b), _ptr(grp_idx), _ptr(D), _ptr(R), _ptr(S),
+                                       _ptr(EX), M_total, G, N, K, threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_grouped_contig failed ({rc})")
+    return D, R, S, EX

@@ -1,0 +1,381 @@
+/*
+ * Plain CPU oracle for FP8 GEMM  D = bf16( sa * sb * A . B^T ).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link or
+ * call this file: only the test suite, the smoke check and the CPU-baseline leg
+ * of the benchmark use it.  It shares no code, header, table or helper with the
+ * HIP library.
+ *
+ * What it computes, and where that is stated:
+ *   - "DeepGEMM: FP8 matrix-multiply kernels on Hopper Tensor Cores", section 2.1:
+ *     the naive triple loop, one output element C[i][j] as the inner product of
+ *     row i of A with column j of the (here transposed, K-major) B.
+ *   - same page, section 3.1: inputs are FP8 in E4M3 (4 exponent, 3 mantissa
+ *     bits) or E5M2 (5 exponent, 2 mantissa bits); accumulation is in a wider
+ *     format; the per-tensor scale is applied once at the output, not per element.
+ *   - same page, section 5.2: per-tensor scales.
+ *   - "One transpose, half the compute: the DeepSeek SwapAB story", sections 2
+ *     and 3.1-3.3: the masked grouped GEMM over experts, each expert with its own
+ *     count of valid token rows; only valid rows are computed.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes):
+ *   - FP8 flavour: OCP E4M3FN (no infinities, S.1111.111 is NaN, max 448) and
+ *     OCP E5M2 (IEEE-like, inf and NaN at exponent 31, max 57344); subnormals
+ *     are decoded, not flushed.
+ *   - Accumulation in FP64, sequential in k.  For E4M3 x E4M3 this is exact
+ *     (every product is an integer multiple of 2^-18 below 2^36 in magnitude).
+ *     An independent integer (__int128) accumulation reports, per element,
+ *     whether the FP64 sum equals the exact sum.
+ *   - Scale: r = acc * ((double)sa * (double)sb); the scale product is exact
+ *     in FP64, so r carries one rounding beyond acc.
+ *   - Output rounding: BF16 round-to-nearest-even, directly from the double
+ *     (one rounding); overflow goes to +-inf; NaN becomes 0x7FC0.
+ *   - Masked grouped: rows i < clamp(masked_m[g], 0, cap) are computed, other
+ *     rows of D are not touched.
+ *   - Contiguous grouped: row r with 0 <= grp_idx[r] < G uses expert grp_idx[r]
+ *     and scale_b[grp_idx[r]]; other rows are padding and are not touched.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_E4M3 0
+#define ORACLE_E5M2 1
+
+/* ------------------------------------------------------------------------- */
+/* FP8 decode (DeepGEMM on Hopper, section 3.1: the E4M3 / E5M2 bit split).   */
+/* ------------------------------------------------------------------------- */
+
+/* Value of one FP8 code, from the sign / exponent / mantissa fields.        */
+static double decode_one(int fmt, unsigned code)
+{
+    unsigned s = (code >> 7) & 1u;
+    double sign = s ? -1.0 : 1.0;
+    if (fmt == ORACLE_E4M3) {
+        unsigned e = (code >> 3) & 0xFu;
+        unsigned m = code & 0x7u;
+        if (e == 15u && m == 7u) return NAN;                 /* only NaN pattern */
+        if (e == 0u) return sign * ldexp((double)m, -9);     /* m/8 * 2^(1-7) */
+        return sign * ldexp((double)(8u + m), (int)e - 10);  /* (1+m/8) * 2^(e-7) */
+    } else {
+        unsigned e = (code >> 2) & 0x1Fu;
+        unsigned m = code & 0x3u;
+        if (e == 31u) return m ? NAN : sign * INFINITY;
+        if (e == 0u) return sign * ldexp((double)m, -16);    /* m/4 * 2^(1-15) */
+        return sign * ldexp((double)(4u + m), (int)e - 17);  /* (1+m/4) * 2^(e-15) */
+    }
+}
+
+int oracle_decode_table(int fmt, double *out256)
+{
+    if (fmt != ORACLE_E4M3 && fmt != ORACLE_E5M2) return -1;
+    for (unsigned c = 0; c < 256u; ++c) out256[c] = decode_one(fmt, c);
+    return 0;
+}
+
+/* Integer mantissa of each code at the format's finest step: value = n * 2^-q
+ * with q = 9 (E4M3) or 16 (E5M2).  Non-finite codes are flagged.             */
+static void int_table(int fmt, int64_t *n256, unsigned char *nonfinite256, int *q)
+{
+    *q = (fmt == ORACLE_E4M3) ? 9 : 16;
+    for (unsigned c = 0; c < 256u; ++c) {
+        double v = decode_one(fmt, c);
+        if (!isfinite(v)) { nonfinite256[c] = 1; n256[c] = 0; continue; }
+        nonfinite256[c] = 0;
+        n256[c] = (int64_t)ldexp(v, *q);      /* exact: v is a multiple of 2^-q */
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* BF16 round-to-nearest-even from a double, in one rounding.                 */
+/* ------------------------------------------------------------------------- */
+uint16_t oracle_bf16_rne(double x)
+{
+    if (isnan(x)) return 0x7FC0u;
+    uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    double a = fabs(x);
+    if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+    if (a == 0.0) return sign;
+    /* Spacing of BF16 values around a: 2^(e-7) for the binade [2^e, 2^(e+1)),
+     * e >= -126; below 2^-126 the subnormal spacing is 2^-133.               */
+    int e;
+    frexp(a, &e);              /* a = f * 2^e, f in [0.5, 1)  =>  binade e-1 */
+    e -= 1;
+    if (e < -126) e = -126;
+    double ulp = ldexp(1.0, e - 7);
+    double q = a / ulp;        /* exact: division by a power of two, q < 2^8 */
+    double lo = floor(q);
+    double frac = q - lo;      /* exact */
+    double n = lo;
+    if (frac > 0.5 || (frac == 0.5 && fmod(lo, 2.0) != 0.0)) n = lo + 1.0;
+    double r = n * ulp;        /* exact */
+    /* Largest finite BF16 is (2 - 2^-7) * 2^127. */
+    if (r > ldexp(255.0, 120)) return (uint16_t)(sign | 0x7F80u);
+    float f = (float)r;        /* exact: r is a BF16 value */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    return (uint16_t)(sign | ((bits >> 16) & 0x7FFFu));
+}
+
+/* ------------------------------------------------------------------------- */
+/* One output element.                                                        */
+/* ------------------------------------------------------------------------- */
+typedef struct {
+    double dec_a[256], dec_b[256];
+    int64_t int_a[256], int_b[256];
+    unsigned char nf_a[256], nf_b[256];
+    int qa, qb;
+} tables_t;
+
+static void make_tables(tables_t *t, int a_fmt, int b_fmt)
+{
+    oracle_decode_table(a_fmt, t->dec_a);
+    oracle_decode_table(b_fmt, t->dec_b);
+    int_table(a_fmt, t->int_a, t->nf_a, &t->qa);
+    int_table(b_fmt, t->int_b, t->nf_b, &t->qb);
+}
+
+/* acc = sum_k dec(a[k]) * dec(b[k]) in FP64, in order k = 0..K-1;
+ * s   = sum_k |dec(a[k]) * dec(b[k])|;
+ * exact (optional): 1 if acc equals the exact integer sum, 0 if it does not,
+ * 2 if a non-finite input makes the comparison meaningless.                  */
+static void dot(const tables_t *t, const uint8_t *a, const uint8_t *b, int64_t K,
+                double *acc_out, double *s_out, unsigned char *exact_out)
+{
+    double acc = 0.0, s = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = t->dec_a[a[k]] * t->dec_b[b[k]];
+        acc += p;
+        s += fabs(p);
+    }
+    *acc_out = acc;
+    *s_out = s;
+    if (!exact_out) return;
+    __int128 isum = 0;
+    int nonfinite = 0;
+    for (int64_t k = 0; k < K; ++k) {
+        if (t->nf_a[a[k]] || t->nf_b[b[k]]) { nonfinite = 1; break; }
+        isum += (__int128)t->int_a[a[k]] * (__int128)t->int_b[b[k]];
+    }
+    if (nonfinite || !isfinite(acc)) { *exact_out = 2; return; }
+    /* acc * 2^(qa+qb) must be the integer isum. */
+    double scaled = ldexp(acc, t->qa + t->qb);
+    if (scaled != floor(scaled) || fabs(scaled) >= ldexp(1.0, 120)) { *exact_out = 0; return; }
+    /* Convert scaled to __int128 exactly (|scaled| < 2^120), by magnitude. */
+    double mag = fabs(scaled);
+    double hi = floor(ldexp(mag, -64));
+    double lo = mag - ldexp(hi, 64);        /* exact, 0 <= lo < 2^64 */
+    __int128 as_int = ((__int128)(uint64_t)hi << 64) + (__int128)(uint64_t)lo;
+    if (scaled < 0) as_int = -as_int;
+    *exact_out = (as_int == isum) ? 1 : 0;
+}
+
+static void element(const tables_t *t, const uint8_t *arow, const uint8_t *brow, int64_t K,
+                    double scale, uint16_t *d, double *r, double *s, unsigned char *ex)
+{
+    double acc, sabs;
+    dot(t, arow, brow, K, &acc, &sabs, ex);
+    double rv = acc * scale;
+    *d = oracle_bf16_rne(rv);
+    if (r) *r = rv;
+    if (s) *s = sabs;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Row-parallel driver: threads split a list of output rows; the arithmetic   */
+/* of each element does not depend on the split.                              */
+/* ------------------------------------------------------------------------- */
+typedef struct {
+    const tables_t *t;
+    const uint8_t *A, *B;
+    int64_t lda, ldb, K, N;
+    /* row r of the job: A row a_row[r], B base b_base[r] (rows j*ldb from it),
+     * output row out_row[r] (offset into D/R/S in elements), scale[r].        */
+    const int64_t *a_row, *b_base, *out_row;
+    const double *scale;
+    int64_t nrows;
+    uint16_t *D; double *R, *S; unsigned char *EX;
+    int64_t next;              /* shared work counter (guarded by mu) */
+    pthread_mutex_t mu;
+} job_t;
+
+static void *worker(void *p)
+{
+    job_t *j = (job_t *)p;
+    for (;;) {
+        pthread_mutex_lock(&j->mu);
+        int64_t r = j->next++;
+        pthread_mutex_unlock(&j->mu);
+        if (r >= j->nrows) break;
+        const uint8_t *arow = j->A + j->a_row[r] * j->lda;
+        const uint8_t *bbase = j->B + j->b_base[r];
+        int64_t o = j->out_row[r];
+        for (int64_t c = 0; c < j->N; ++c) {
+            element(j->t, arow, bbase + c * j->ldb, j->K, j->scale[r],
+                    j->D + o + c,
+                    j->R ? j->R + o + c : NULL,
+                    j->S ? j->S + o + c : NULL,
+                    j->EX ? j->EX + o + c : NULL);
+        }
+    }
+    return NULL;
+}
+
+static void run_job(job_t *j, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    j->next = 0;
+    pthread_mutex_init(&j->mu, NULL);
+    pthread_t th[256];
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i)
+        if (pthread_create(&th[started], NULL, worker, j) == 0) ++started;
+    worker(j);
+    for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    pthread_mutex_destroy(&j->mu);
+}
+
+static int fmt_ok(int f) { return f == ORACLE_E4M3 || f == ORACLE_E5M2; }
+
+/* Dense: D[M x N] (bf16 bits, row stride ldd) = bf16(sa*sb * A[M x K] . B[N x K]^T).
+ * R, S, EX (row stride ldd) may be NULL.                                      */
+int oracle_gemm_nt(const uint8_t *A, int64_t lda, int a_fmt,
+                   const uint8_t *B, int64_t ldb, int b_fmt,
+                   float sa, float sb,
+                   uint16_t *D, int64_t ldd, double *R, double *S, unsigned char *EX,
+                   int64_t M, int64_t N, int64_t K, int nthreads)
+{
+    if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || M < 0 || N < 0 || K < 0) return -1;
+    if (M == 0 || N == 0) return 0;
+    tables_t *t = (tables_t *)malloc(sizeof *t);
+    int64_t *a_row = (int64_t *)malloc(sizeof(int64_t) * M);
+    int64_t *b_base = (int64_t *)malloc(sizeof(int64_t) * M);
+    int64_t *out_row = (int64_t *)malloc(sizeof(int64_t) * M);
+    double *scale = (double *)malloc(sizeof(double) * M);
+    if (!t || !a_row || !b_base || !out_row || !scale) {
+        free(t); free(a_row); free(b_base); free(out_row); free(scale); return -2;
+    }
+    make_tables(t, a_fmt, b_fmt);
+    double sc = (double)sa * (double)sb;      /* exact in FP64 */
+    for (int64_t i = 0; i < M; ++i) {
+        a_row[i] = i; b_base[i] = 0; out_row[i] = i * ldd; scale[i] = sc;
+    }
+    job_t j = {0};
+    j.t = t; j.A = A; j.B = B; j.lda = lda; j.ldb = ldb; j.K = K; j.N = N;
+    j.a_row = a_row; j.b_base = b_base; j.out_row = out_row; j.scale = scale;
+    j.nrows = M; j.D = D; j.R = R; j.S = S; j.EX = EX;
+    run_job(&j, nthreads);
+    free(t); free(a_row); free(b_base); free(out_row); free(scale);
+    return 0;
+}
+
+/* Dense, selected elements only: element p is (ii[p], jj[p]).                */
+int oracle_gemm_nt_points(const uint8_t *A, int64_t lda, int a_fmt,
+                          const uint8_t *B, int64_t ldb, int b_fmt,
+                          float sa, float sb, int64_t K,
+                          int64_t npts, const int64_t *ii, const int64_t *jj,
+                          uint16_t *D, double *R, double *S, unsigned char *EX)
+{
+    if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || K < 0 || npts < 0) return -1;
+    tables_t *t = (tables_t *)malloc(sizeof *t);
+    if (!t) return -2;
+    make_tables(t, a_fmt, b_fmt);
+    double sc = (double)sa * (double)sb;
+    for (int64_t p = 0; p < npts; ++p)
+        element(t, A + ii[p] * lda, B + jj[p] * ldb, K, sc, D + p,
+                R ? R + p : NULL, S ? S + p : NULL, EX ? EX + p : NULL);
+    free(t);
+    return 0;
+}
+
+/* Masked grouped: A [G][cap][K], B [G][N][K], D/R/S [G][cap][N].
+ * For each g, rows i < clamp(masked_m[g], 0, cap) are computed with scale
+ * sa * scale_b[g]; every other row is left as the caller filled it.          */
+int oracle_grouped_masked(const uint8_t *A, int a_fmt, const uint8_t *B, int b_fmt,
+                          float sa, const float *scale_b, const int32_t *masked_m,
+                          uint16_t *D, double *R, double *S, unsigned char *EX,
+                          int64_t G, int64_t cap, int64_t N, int64_t K, int nthreads)
+{
+    if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || G < 0 || cap < 0 || N < 0 || K < 0) return -1;
+    int64_t total = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        int64_t m = masked_m[g];
+        if (m < 0) m = 0;
+        if (m > cap) m = cap;
+        total += m;
+    }
+    if (total == 0 || N == 0) return 0;
+    tables_t *t = (tables_t *)malloc(sizeof *t);
+    int64_t *a_row = (int64_t *)malloc(sizeof(int64_t) * total);
+    int64_t *b_base = (int64_t *)malloc(sizeof(int64_t) * total);
+    int64_t *out_row = (int64_t *)malloc(sizeof(int64_t) * total);
+    double *scale = (double *)malloc(sizeof(double) * total);
+    if (!t || !a_row || !b_base || !out_row || !scale) {
+        free(t); free(a_row); free(b_base); free(out_row); free(scale); return -2;
+    }
+    make_tables(t, a_fmt, b_fmt);
+    int64_t r = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        int64_t m = masked_m[g];
+        if (m < 0) m = 0;
+        if (m > cap) m = cap;
+        for (int64_t i = 0; i < m; ++i, ++r) {
+            a_row[r] = g * cap + i;               /* row of the [G*cap][K] view */
+            b_base[r] = g * N * K;                /* expert g's weights */
+            out_row[r] = (g * cap + i) * N;
+            scale[r] = (double)sa * (double)scale_b[g];
+        }
+    }
+    job_t j = {0};
+    j.t = t; j.A = A; j.B = B; j.lda = K; j.ldb = K; j.K = K; j.N = N;
+    j.a_row = a_row; j.b_base = b_base; j.out_row = out_row; j.scale = scale;
+    j.nrows = total; j.D = D; j.R = R; j.S = S; j.EX = EX;
+    run_job(&j, nthreads);
+    free(t); free(a_row); free(b_base); free(out_row); free(scale);
+    return 0;
+}
+
+/* Contiguous grouped: A [M_total][K], B [G][N][K], D/R/S [M_total][N].
+ * Row r with 0 <= grp_idx[r] < G uses expert grp_idx[r]; other rows are
+ * padding and are left as the caller filled them.                            */
+int oracle_grouped_contig(const uint8_t *A, int a_fmt, const uint8_t *B, int b_fmt,
+                          float sa, const float *scale_b, const int32_t *grp_idx,
+                          uint16_t *D, double *R, double *S, unsigned char *EX,
+                          int64_t M_total, int64_t G, int64_t N, int64_t K, int nthreads)
+{
+    if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || M_total < 0 || G < 0 || N < 0 || K < 0) return -1;
+    int64_t total = 0;
+    for (int64_t r = 0; r < M_total; ++r)
+        if (grp_idx[r] >= 0 && grp_idx[r] < G) ++total;
+    if (total == 0 || N == 0) return 0;
+    tables_t *t = (tables_t *)malloc(sizeof *t);
+    int64_t *a_row = (int64_t *)malloc(sizeof(int64_t) * total);
+    int64_t *b_base = (int64_t *)malloc(sizeof(int64_t) * total);
+    int64_t *out_row = (int64_t *)malloc(sizeof(int64_t) * total);
+    double *scale = (double *)malloc(sizeof(double) * total);
+    if (!t || !a_row || !b_base || !out_row || !scale) {
+        free(t); free(a_row); free(b_base); free(out_row); free(scale); return -2;
+    }
+    make_tables(t, a_fmt, b_fmt);
+    int64_t q = 0;
+    for (int64_t r = 0; r < M_total; ++r) {
+        int32_t g = grp_idx[r];
+        if (g < 0 || g >= G) continue;
+        a_row[q] = r;
+        b_base[q] = (int64_t)g * N * K;
+        out_row[q] = r * N;
+        scale[q] = (double)sa * (double)scale_b[g];
+        ++q;
+    }
+    job_t j = {0};
+    j.t = t; j.A = A; j.B = B; j.lda = K; j.ldb = K; j.K = K; j.N = N;
+    j.a_row = a_row; j.b_base = b_base; j.out_row = out_row; j.scale = scale;
+    j.nrows = total; j.D = D; j.R = R; j.S = S; j.EX = EX;
+    run_job(&j, nthreads);
+    free(t); free(a_row); free(b_base); free(out_row); free(scale);
+    return 0;
+}

@@ -1,0 +1,101 @@
+// Device primitives for the gfx950 FP8 GEMM kernels: buffer-descriptor loads
+// with out-of-range zero fill, the LDS swizzle, the scaled FP8 MFMA wrappers,
+// and the BF16 epilogue store.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8g {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// Buffer descriptor word 3 for gfx9-family raw (untyped) buffer access:
+// 32-bit data format, no swizzle, no stride.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// A lane offset at or above every descriptor's byte count: the hardware returns
+// zeros for it and issues no memory transaction.  Descriptors built here never
+// cover more than 2^31 - 1 bytes.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+// Buffer descriptor for `bytes` bytes starting at `base`.  The base comes from
+// full 64-bit pointer arithmetic done by the caller (never a 32-bit add on the
+// low word: "MLS three memory-access bugs", Bug 1), and loads past `bytes`
+// return zero instead of touching memory (same page, Bug 2 and its survey of
+// out-of-bounds handling; this is the buffer-descriptor bound it lists for AMD).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ v4u load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+
+// Descriptor byte count for `rows` rows of stride `ld` (rows <= 256 and
+// ld < 2^23 keep it below 2^31).
+__device__ __forceinline__ uint32_t rows_bytes(int rows, int64_t ld) {
+    return rows > 0 ? (uint32_t)((int64_t)rows * ld) : 0u;
+}
+
+// 16-byte chunk swizzle for LDS tiles whose rows are 128 bytes (8 chunks).
+// Row r keeps its 8 chunks but stores logical chunk c at c ^ f(r) with
+// f(r) = (r & 7) ^ ((r >> 3) & 1): any 8 consecutive rows, and the even (or
+// odd) rows among any 16 consecutive rows, then hit 8 distinct chunk slots, so
+// a 16-byte-per-lane read of one logical chunk down a column of rows is free of
+// bank conflicts with 32 or 64 four-byte banks ("DeepGEMM on Hopper Tensor
+// Cores", section 4.2: XOR the address by row to spread a column over banks).
+__device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
+    return (row << 7) + (((chunk ^ (row & 7u) ^ ((row >> 3) & 1u)) & 7u) << 4);
+}
+
+__device__ __forceinline__ v8i pack8(v4u lo, v4u hi) {
+    v8i r;
+    r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+    r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+    return r;
+}
+
+// Scaled FP8 MFMA with neutral E8M0 block scales (127 = 2^0), so it is a plain
+// FP8 x FP8 -> FP32 multiply-accumulate.  FA / FB select the format of the
+// instruction's first / second operand: 0 = E4M3, 1 = E5M2.
+template <int FA, int FB>
+__device__ __forceinline__ v16f mfma32x32x64(v8i a, v8i b, v16f c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
+}
+
+template <int FA, int FB>
+__device__ __forceinline__ v4f mfma16x16x128(v8i a, v8i b, v4f c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
+}
+
+// BF16 round-to-nearest-even of four floats, packed little-endian.
+__device__ __forceinline__ v2u pack_bf16x4(float a, float b, float c, float d) {
+    __bf16 h0 = (__bf16)a, h1 = (__bf16)b, h2 = (__bf16)c, h3 = (__bf16)d;
+    uint16_t u0 = __builtin_bit_cast(uint16_t, h0);
+    uint16_t u1 = __builtin_bit_cast(uint16_t, h1);
+    uint16_t u2 = __builtin_bit_cast(uint16_t, h2);
+    uint16_t u3 = __builtin_bit_cast(uint16_t, h3);
+    v2u r;
+    r[0] = (uint32_t)u0 | ((uint32_t)u1 << 16);
+    r[1] = (uint32_t)u2 | ((uint32_t)u3 << 16);
+    return r;
+}
+
+// Store four consecutive BF16 values of one output row starting at column n.
+// `nvalid` = number of the four columns that exist (N tail).
+__device__ __forceinline__ void store_bf16x4(uint16_t *row, int n, int nvalid, v2u v) {
+    if (nvalid >= 4) {
+        *reinterpret_cast<v2u *>(row + n) = v;
+    } else {
+        if (nvalid > 0) row[n] = (uint16_t)(v[0] & 0xFFFFu);
+        if (nvalid > 1) row[n + 1] = (uint16_t)(v[0] >> 16);
+        if (nvalid > 2) row[n + 2] = (uint16_t)(v[1] & 0xFFFFu);
+    }
+}
+
+}  // namespace fp8g

@@ -1,0 +1,315 @@
+// C ABI of the gfx950 FP8 GEMM library: argument validation, shape-class
+// dispatch (including the swap-AB choice) and kernel launch on the caller's
+// stream.  See include/fp8_gemm.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/fp8_gemm.h"
+#include "kernels.hpp"
+
+namespace {
+
+using fp8g::GemmParams;
+
+thread_local char g_detail[512];
+thread_local char g_message[768];
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_detail[0] = '\0';
+    return FP8G_OK;
+}
+
+constexpr int64_t kMaxRowStride = (int64_t(1) << 23) - 16;   // keeps 256 rows of offsets below 2^31
+constexpr int kSwapMaxM = 64;                                  // swap-AB threshold on the token count
+constexpr int kSwapWaveRows = 32;                              // weight rows per wave in the swap kernel
+constexpr int kSwapTileN = 4 * kSwapWaveRows;                  // weight rows per workgroup
+constexpr int kSwapDepth = 4;                                  // K blocks of loads in flight + 1
+constexpr int kContigAlign = 128;                              // row alignment of experts (contiguous form)
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool dtype_ok(int d) { return d == FP8G_E4M3 || d == FP8G_E5M2; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Shape-class choice.
+// ---------------------------------------------------------------------------
+enum Variant { V_NONE = 0, V_TILE_256x256 = 1, V_TILE_128x256 = 2, V_SWAP = 3 };
+
+int token_blocks_for(int m) {
+    if (m <= 16) return 1;
+    if (m <= 32) return 2;
+    return 4;
+}
+
+// Dense tiled kernel: pick the tile whose waves of 256 workgroups (one per CU)
+// give the smallest estimated time.  A 128x256 tile does half the work of a
+// 256x256 tile at a somewhat lower efficiency (more operand traffic per FLOP).
+int pick_dense_tile(int64_t M, int64_t N) {
+    const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
+    const int64_t t128 = cdiv(M, 128) * cdiv(N, 256);
+    const double c256 = (double)cdiv(t256, 256) * 2.0;
+    const double c128 = (double)cdiv(t128, 256) * 1.15;
+    return c256 <= c128 ? V_TILE_256x256 : V_TILE_128x256;
+}
+
+int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan *out) {
+    memset(out, 0, sizeof *out);
+    if (m < 0 || n < 0 || k < 0 || groups < 0) return fail(FP8G_ERR_SHAPE, "negative size (m=%d n=%d k=%d groups=%d)", m, n, k, groups);
+    if (k % 16 != 0) return fail(FP8G_ERR_SHAPE, "K=%d is not a multiple of 16", k);
+    if (k > kMaxRowStride) return fail(FP8G_ERR_SHAPE, "K=%d exceeds the row-stride limit %lld", k, (long long)kMaxRowStride);
+    if (op == 0) {
+        if (m == 0 || n == 0) return ok();
+        if (m <= kSwapMaxM) {
+            out->variant = V_SWAP;
+            out->tile_m = 16 * token_blocks_for(m);
+            out->tile_n = kSwapTileN;
+            out->token_blocks = token_blocks_for(m);
+            out->workgroups = cdiv(n, kSwapTileN);
+        } else {
+            out->variant = pick_dense_tile(m, n);
+            out->tile_m = out->variant == V_TILE_256x256 ? 256 : 128;
+            out->tile_n = 256;
+            out->workgroups = cdiv(m, out->tile_m) * cdiv(n, 256);
+        }
+        return ok();
+    }
+    if (op == 1) {
+        if (expected_m < 0 || expected_m > m)
+            return fail(FP8G_ERR_ARG, "expected_m=%d outside [0, cap=%d]", expected_m, m);
+        if (groups == 0 || m == 0 || n == 0) return ok();
+        const int hint = expected_m > 0 ? expected_m : m;
+        if (hint <= kSwapMaxM) {
+            out->variant = V_SWAP;
+            out->tile_m = 16 * token_blocks_for(hint);
+            out->tile_n = kSwapTileN;
+            out->token_blocks = token_blocks_for(hint);
+            out->workgroups = (int64_t)groups * cdiv(n, kSwapTileN);
+        } else {
+            out->variant = V_TILE_128x256;
+            out->tile_m = 128;
+            out->tile_n = 256;
+            out->workgroups = (int64_t)groups * cdiv(m, 128) * cdiv(n, 256);
+        }
+        return ok();
+    }
+    if (op == 2) {
+        if (m == 0 || n == 0) return ok();
+        if (groups == 0) return fail(FP8G_ERR_SHAPE, "G=0 with M_total=%d rows", m);
+        out->variant = V_TILE_128x256;
+        out->tile_m = kContigAlign;
+        out->tile_n = 256;
+        out->workgroups = cdiv(m, kContigAlign) * cdiv(n, 256);
+        return ok();
+    }
+    return fail(FP8G_ERR_ARG, "unknown op %d", op);
+}
+
+// ---------------------------------------------------------------------------
+// Device check: the code objects are built for gfx950 only.
+// ---------------------------------------------------------------------------
+int check_device() {
+    static int cached[64];   // 0 unknown, 1 ok, -1 unsupported
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(FP8G_ERR_UNSUPPORTED, "no HIP device");
+    if (dev >= 0 && dev < 64 && cached[dev] == 1) return FP8G_OK;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(FP8G_ERR_UNSUPPORTED, "cannot query device %d", dev);
+    const bool good = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev >= 0 && dev < 64) cached[dev] = good ? 1 : -1;
+    if (!good) return fail(FP8G_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+    return FP8G_OK;
+}
+
+int launch_status(const char *what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(FP8G_ERR_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers: one instantiation per (operand formats, tile shape, mode).
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int MODE>
+int launch_tile(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    const dim3 block(64 * WM * WN);
+#define FP8G_TILE(FA, FB) \
+    hipLaunchKernelGGL((fp8g::tile_kernel<BM, BN, WM, WN, FA, FB, MODE>), grid, block, 0, s, p)
+    if (fa == 0 && fb == 0) FP8G_TILE(0, 0);
+    else if (fa == 0 && fb == 1) FP8G_TILE(0, 1);
+    else if (fa == 1 && fb == 0) FP8G_TILE(1, 0);
+    else FP8G_TILE(1, 1);
+#undef FP8G_TILE
+    return launch_status("tile kernel");
+}
+
+template <int CB, int MODE>
+int launch_swap_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    const dim3 block(256);
+#define FP8G_SWAP(FA, FB) \
+    hipLaunchKernelGGL((fp8g::swap_kernel<kSwapWaveRows, CB, FA, FB, kSwapDepth, MODE>), grid, block, 0, s, p)
+    if (fa == 0 && fb == 0) FP8G_SWAP(0, 0);
+    else if (fa == 0 && fb == 1) FP8G_SWAP(0, 1);
+    else if (fa == 1 && fb == 0) FP8G_SWAP(1, 0);
+    else FP8G_SWAP(1, 1);
+#undef FP8G_SWAP
+    return launch_status("swap kernel");
+}
+
+template <int MODE>
+int launch_swap(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    if (cb == 1) return launch_swap_cb<1, MODE>(fa, fb, p, grid, s);
+    if (cb == 2) return launch_swap_cb<2, MODE>(fa, fb, p, grid, s);
+    return launch_swap_cb<4, MODE>(fa, fb, p, grid, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_gemm_abi_version(void) { return FP8G_ABI_VERSION; }
+
+const char *fp8_gemm_strerror(int status) {
+    const char *base;
+    switch (status) {
+        case FP8G_OK: base = "ok"; break;
+        case FP8G_ERR_NULL: base = "null pointer"; break;
+        case FP8G_ERR_SHAPE: base = "invalid shape"; break;
+        case FP8G_ERR_ALIGN: base = "misaligned pointer or stride"; break;
+        case FP8G_ERR_DTYPE: base = "invalid FP8 dtype"; break;
+        case FP8G_ERR_STRIDE: base = "invalid row stride"; break;
+        case FP8G_ERR_LAUNCH: base = "kernel launch failed"; break;
+        case FP8G_ERR_UNSUPPORTED: base = "unsupported device"; break;
+        case FP8G_ERR_ARG: base = "invalid argument"; break;
+        default: base = "unknown status"; break;
+    }
+    if (g_detail[0]) snprintf(g_message, sizeof g_message, "%s: %s", base, g_detail);
+    else snprintf(g_message, sizeof g_message, "%s", base);
+    return g_message;
+}
+
+int fp8_gemm_plan(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan *out) {
+    if (!out) return fail(FP8G_ERR_NULL, "plan output pointer is NULL");
+    return plan_impl(op, m, n, k, groups, expected_m, out);
+}
+
+int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t ldb, int b_dtype,
+                const float *scale_a, const float *scale_b, void *D, int64_t ldd, int M, int N, int K,
+                void *stream) {
+    if (!dtype_ok(a_dtype) || !dtype_ok(b_dtype)) return fail(FP8G_ERR_DTYPE, "dtypes %d, %d", a_dtype, b_dtype);
+    fp8g_plan plan;
+    int st = plan_impl(0, M, N, K, 1, 0, &plan);
+    if (st != FP8G_OK) return st;
+    if (plan.variant == V_NONE) return ok();
+    if (!A || !B || !D || !scale_a || !scale_b) return fail(FP8G_ERR_NULL, "A, B, D, scale_a and scale_b are required");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return fail(FP8G_ERR_ALIGN, "A, B and D must be 16-byte aligned");
+    if (!aligned4(scale_a) || !aligned4(scale_b)) return fail(FP8G_ERR_ALIGN, "scales must be 4-byte aligned");
+    if (lda < K || ldb < K) return fail(FP8G_ERR_STRIDE, "lda=%lld / ldb=%lld below K=%d", (long long)lda, (long long)ldb, K);
+    if (lda % 16 || ldb % 16) return fail(FP8G_ERR_ALIGN, "lda=%lld / ldb=%lld not multiples of 16 bytes", (long long)lda, (long long)ldb);
+    if (lda > kMaxRowStride || ldb > kMaxRowStride) return fail(FP8G_ERR_STRIDE, "row stride above %lld bytes", (long long)kMaxRowStride);
+    if (ldd < N) return fail(FP8G_ERR_STRIDE, "ldd=%lld below N=%d", (long long)ldd, N);
+    if (ldd % 8) return fail(FP8G_ERR_ALIGN, "ldd=%lld not a multiple of 8 elements", (long long)ldd);
+    if ((st = check_device()) != FP8G_OK) return st;
+
+    GemmParams p = {};
+    p.A = static_cast<const uint8_t *>(A);
+    p.B = static_cast<const uint8_t *>(B);
+    p.D = static_cast<uint16_t *>(D);
+    p.lda = lda; p.ldb = ldb; p.ldd = ldd;
+    p.M = M; p.N = N; p.K = K; p.G = 1; p.cap = M;
+    p.scale_a = scale_a; p.scale_b = scale_b;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int fa = a_dtype, fb = b_dtype;
+    if (plan.variant == V_SWAP) {
+        p.tiles_m = 1;
+        p.tiles_n = (int)plan.workgroups;
+        return launch_swap<fp8g::MODE_DENSE>(plan.token_blocks, fa, fb, p, dim3((unsigned)plan.workgroups), s);
+    }
+    p.tiles_m = (int)cdiv(M, plan.tile_m);
+    p.tiles_n = (int)cdiv(N, plan.tile_n);
+    const dim3 grid((unsigned)plan.workgroups);
+    if (plan.variant == V_TILE_256x256) return launch_tile<256, 256, 2, 2, fp8g::MODE_DENSE>(fa, fb, p, grid, s);
+    return launch_tile<128, 256, 2, 2, fp8g::MODE_DENSE>(fa, fb, p, grid, s);
+}
+
+int fp8_grouped_gemm_masked(const void *A, int a_dtype, const void *B, int b_dtype, const float *scale_a,
+                            const float *scale_b, const int32_t *masked_m, void *D, int G, int cap, int N, int K,
+                            int expected_m, void *stream) {
+    if (!dtype_ok(a_dtype) || !dtype_ok(b_dtype)) return fail(FP8G_ERR_DTYPE, "dtypes %d, %d", a_dtype, b_dtype);
+    if (G < 0 || cap < 0) return fail(FP8G_ERR_SHAPE, "negative G=%d or cap=%d", G, cap);
+    fp8g_plan plan;
+    int st = plan_impl(1, cap, N, K, G, expected_m, &plan);
+    if (st != FP8G_OK) return st;
+    if (plan.variant == V_NONE) return ok();
+    if (!A || !B || !D || !scale_a || !scale_b || !masked_m)
+        return fail(FP8G_ERR_NULL, "A, B, D, scale_a, scale_b and masked_m are required");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return fail(FP8G_ERR_ALIGN, "A, B and D must be 16-byte aligned");
+    if (!aligned4(scale_a) || !aligned4(scale_b) || !aligned4(masked_m)) return fail(FP8G_ERR_ALIGN, "scales and masked_m must be 4-byte aligned");
+    if (N % 8) return fail(FP8G_ERR_ALIGN, "N=%d: rows of D must stay 16-byte aligned (N %% 8 == 0)", N);
+    if ((st = check_device()) != FP8G_OK) return st;
+
+    GemmParams p = {};
+    p.A = static_cast<const uint8_t *>(A);
+    p.B = static_cast<const uint8_t *>(B);
+    p.D = static_cast<uint16_t *>(D);
+    p.lda = K; p.ldb = K; p.ldd = N;
+    p.a_gstride = (int64_t)cap * K;
+    p.b_gstride = (int64_t)N * K;
+    p.d_gstride = (int64_t)cap * N;
+    p.M = cap; p.N = N; p.K = K; p.G = G; p.cap = cap;
+    p.scale_a = scale_a; p.scale_b = scale_b; p.masked_m = masked_m;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (plan.variant == V_SWAP) {
+        p.tiles_m = 1;
+        p.tiles_n = (int)cdiv(N, kSwapTileN);
+        return launch_swap<fp8g::MODE_MASKED>(plan.token_blocks, a_dtype, b_dtype, p, dim3((unsigned)plan.workgroups), s);
+    }
+    p.tiles_m = (int)cdiv(cap, 128);
+    p.tiles_n = (int)cdiv(N, 256);
+    return launch_tile<128, 256, 2, 2, fp8g::MODE_MASKED>(a_dtype, b_dtype, p, dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)G), s);
+}
+
+int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dtype, const float *scale_a,
+                            const float *scale_b, const int32_t *grp_idx, void *D, int M_total, int G, int N, int K,
+                            void *stream) {
+    if (!dtype_ok(a_dtype) || !dtype_ok(b_dtype)) return fail(FP8G_ERR_DTYPE, "dtypes %d, %d", a_dtype, b_dtype);
+    if (G < 0 || M_total < 0) return fail(FP8G_ERR_SHAPE, "negative G=%d or M_total=%d", G, M_total);
+    fp8g_plan plan;
+    int st = plan_impl(2, M_total, N, K, G, 0, &plan);
+    if (st != FP8G_OK) return st;
+    if (plan.variant == V_NONE) return ok();
+    if (!A || !B || !D || !scale_a || !scale_b || !grp_idx)
+        return fail(FP8G_ERR_NULL, "A, B, D, scale_a, scale_b and grp_idx are required");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return fail(FP8G_ERR_ALIGN, "A, B and D must be 16-byte aligned");
+    if (!aligned4(scale_a) || !aligned4(scale_b) || !aligned4(grp_idx)) return fail(FP8G_ERR_ALIGN, "scales and grp_idx must be 4-byte aligned");
+    if (N % 8) return fail(FP8G_ERR_ALIGN, "N=%d: rows of D must stay 16-byte aligned (N %% 8 == 0)", N);
+    if ((st = check_device()) != FP8G_OK) return st;
+
+    GemmParams p = {};
+    p.A = static_cast<const uint8_t *>(A);
+    p.B = static_cast<const uint8_t *>(B);
+    p.D = static_cast<uint16_t *>(D);
+    p.lda = K; p.ldb = K; p.ldd = N;
+    p.b_gstride = (int64_t)N * K;
+    p.M = M_total; p.N = N; p.K = K; p.G = G; p.cap = M_total;
+    p.scale_a = scale_a; p.scale_b = scale_b; p.grp_idx = grp_idx;
+    p.tiles_m = (int)cdiv(M_total, kContigAlign);
+    p.tiles_n = (int)cdiv(N, 256);
+    return launch_tile<128, 256, 2, 2, fp8g::MODE_CONTIG>(a_dtype, b_dtype, p, dim3((unsigned)plan.workgroups),
+                                                          static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

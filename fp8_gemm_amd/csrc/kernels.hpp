@@ -1,0 +1,411 @@
+// gfx950 FP8 GEMM kernels.
+//
+// Both kernels compute D = bf16(sa * sb * A . B^T) with A [m x K] (tokens) and
+// B [n x K] (weights), both K-contiguous ("nt"), and put B's rows on the
+// matrix-core instruction's first (row) operand and A's rows on its second
+// (column) operand.  Each lane's accumulator registers then hold four
+// consecutive output columns n of one output row m, so the epilogue writes
+// 8-byte packed BF16 runs straight from registers.
+//
+//   tile_kernel    LDS-tiled: a BM x BN output tile per workgroup, K in steps
+//                  of 128 bytes, both operand tiles staged through a
+//                  double-buffered, XOR-swizzled LDS ring; v_mfma 32x32x64.
+//                  Dense (M > 64), masked grouped with many rows per group,
+//                  and contiguous grouped.
+//   swap_kernel    streaming "swap-AB" form for few tokens: each wave streams
+//                  its own weight rows from HBM straight into registers in the
+//                  16x16x128 operand layout (no LDS: every weight byte is used
+//                  by exactly one wave), tokens ride on the 16-wide column side
+//                  in blocks of 16.  Dense M <= 64 and masked grouped decode.
+//
+// "DeepGEMM: FP8 matrix-multiply kernels on Hopper Tensor Cores" is the prior
+// art for the tiled form (section 2.3 three-level tiling, section 3.3 double
+// buffering, section 4.2 swizzled on-chip layout, section 6.3 clipping the last
+// K block); "One transpose, half the compute: the DeepSeek SwapAB story"
+// (sections 1.1, 3.2-3.3) for putting the weights on the instruction's rigid
+// side and shrinking the token side to the valid rows.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace fp8g {
+
+enum { MODE_DENSE = 0, MODE_MASKED = 1, MODE_CONTIG = 2 };
+
+struct GemmParams {
+    const uint8_t *A;          // tokens: [m x K] rows of lda bytes (per group: + g * a_gstride)
+    const uint8_t *B;          // weights: [n x K] rows of ldb bytes (per group: + g * b_gstride)
+    uint16_t *D;               // BF16 [m x N], ldd elements (per group: + g * d_gstride)
+    int64_t lda, ldb, ldd;
+    int64_t a_gstride, b_gstride, d_gstride;
+    int M, N, K, G, cap;
+    const float *scale_a;      // 1 float
+    const float *scale_b;      // 1 float (dense) or G floats (grouped)
+    const int32_t *masked_m;   // masked: [G]
+    const int32_t *grp_idx;    // contiguous: [M]
+    int tiles_m, tiles_n;      // tile grid of one group
+};
+
+// ---------------------------------------------------------------------------
+// Tile index -> (tm, tn) for the dense tiled kernel.
+//
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
+// XCD w % 8), and each XCD has its own L2.  Remap so that XCD x owns a
+// contiguous range of logical tiles, and order logical tiles in bands of
+// kGroupM tile-rows so one XCD's tiles share few A and B panels (for 4096^3
+// with 256x256 tiles: a 4 x 8 block of tiles per XCD, 12 panels instead of 64).
+// ---------------------------------------------------------------------------
+constexpr int kXcds = 8;
+constexpr int kGroupM = 4;
+
+__device__ __forceinline__ void dense_tile_coords(int wg, int tiles_m, int tiles_n, int &tm, int &tn) {
+    const int nt = tiles_m * tiles_n;
+    const int per_xcd = nt / kXcds;
+    int t = wg;
+    if (wg < per_xcd * kXcds) t = (wg % kXcds) * per_xcd + wg / kXcds;
+    const int band = kGroupM * tiles_n;
+    const int b = t / band;
+    const int first_m = b * kGroupM;
+    const int rows = min(kGroupM, tiles_m - first_m);
+    const int r = t - b * band;
+    tm = first_m + r % rows;
+    tn = r / rows;
+}
+
+// ---------------------------------------------------------------------------
+// LDS-tiled kernel.
+// BM x BN tile (tokens x weights), WM x WN waves, each wave a TM x TN sub-tile
+// of (TM/32) x (TN/32) 32x32 accumulator blocks.  FA / FB: formats of A / B.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int FA, int FB, int MODE>
+__global__ __launch_bounds__(64 * WM * WN, 1) void tile_kernel(GemmParams p) {
+    constexpr int THREADS = 64 * WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int ROWB = 128;                 // bytes of K per step (one 128-deep K block)
+    constexpr int STAGE = (BM + BN) * ROWB;   // one ring slot: A tile then B tile
+    constexpr int LA = BM * 8 / THREADS;      // 16-byte loads per thread per slot
+    constexpr int LB = BN * 8 / THREADS;
+    constexpr int RSTEP = THREADS / 8;        // rows covered by one load instruction
+    static_assert(FM >= 1 && FN >= 1 && LA >= 1 && LB >= 1, "tile shape");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wm = wave % WM;
+    const int wn = wave / WM;
+
+    // ---- tile coordinates and per-mode operand bases (64-bit arithmetic) ----
+    int tm, tn, g = 0;
+    if (MODE == MODE_DENSE) {
+        dense_tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    } else {
+        tm = blockIdx.x / p.tiles_n;
+        tn = blockIdx.x % p.tiles_n;
+        if (MODE == MODE_MASKED) g = blockIdx.y;
+    }
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    int rows_m;
+    int expert = 0;
+    if (MODE == MODE_DENSE) {
+        rows_m = min(p.M - m0, BM);
+    } else if (MODE == MODE_MASKED) {
+        const int mg = min(max(p.masked_m[g], 0), p.cap);
+        if (m0 >= mg) return;                 // nothing valid in this tile: no load at all
+        rows_m = min(mg - m0, BM);
+        expert = g;
+    } else {
+        // The expert of this block of rows: the index of its first row that
+        // names a valid expert.  A block with none is all padding.
+        rows_m = min(p.M - m0, BM);
+        expert = -1;
+        for (int base = 0; base < rows_m; base += 64) {
+            const int r = base + lane;
+            int e = -1;
+            if (r < rows_m) e = p.grp_idx[m0 + r];
+            const bool ok = (e >= 0) && (e < p.G);
+            const unsigned long long ball = __ballot(ok);
+            if (ball) {
+                const int first = __builtin_ctzll(ball);
+                expert = __shfl(e, first);
+                break;
+            }
+        }
+        if (expert < 0) return;
+    }
+    const int rows_n = min(p.N - n0, BN);
+
+    const uint8_t *a_base = p.A + (MODE == MODE_MASKED ? (int64_t)g * p.a_gstride : 0) + (int64_t)m0 * p.lda;
+    const uint8_t *b_base = p.B + (int64_t)expert * p.b_gstride + (int64_t)n0 * p.ldb;
+    uint16_t *d_base = p.D + (MODE == MODE_MASKED ? (int64_t)g * p.d_gstride : 0);
+    const float sc = p.scale_a[0] * p.scale_b[MODE == MODE_DENSE ? 0 : expert];
+
+    // Rows past rows_m / rows_n fall outside the descriptors and load as zero.
+    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(a_base, rows_bytes(rows_m, p.lda));
+    const __amdgpu_buffer_rsrc_t rsB = make_rsrc(b_base, rows_bytes(rows_n, p.ldb));
+
+    // ---- per-thread global-load and LDS-store addresses ----
+    const int ch = tid & 7;                   // 16-byte chunk of a 128-byte row piece
+    const int r0 = tid >> 3;
+    uint32_t a_goff[LA], b_goff[LB];
+    uint32_t a_soff[LA], b_soff[LB];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int row = r0 + i * RSTEP;
+        a_goff[i] = (uint32_t)((int64_t)row * p.lda) + ch * 16;
+        a_soff[i] = swz(row, ch);
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int row = r0 + i * RSTEP;
+        b_goff[i] = (uint32_t)((int64_t)row * p.ldb) + ch * 16;
+        b_soff[i] = BM * ROWB + swz(row, ch);
+    }
+
+    // ---- per-lane fragment read addresses (within a slot) ----
+    // Operand layout used for both operands of v_mfma 32x32x64: lane l carries
+    // row (l & 31) and the 32 K bytes [(l >> 5) * 32, +32) of each 64-deep half.
+    // The instruction sums over all 64 K slots, and both operands use the same
+    // K placement, so the dot products are over exactly the K block.
+    const int lrow = lane & 31;
+    const int khalf = lane >> 5;
+    uint32_t frag_off[2][2];                  // [K half][first / second 16 bytes]
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) frag_off[h][j] = swz(lrow, h * 4 + khalf * 2 + j);
+    const uint32_t a_frag_base = (uint32_t)(wm * TM) * ROWB;
+    const uint32_t b_frag_base = BM * ROWB + (uint32_t)(wn * TN) * ROWB;
+
+    v16f acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = (v16f){0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+
+    const int nk = (p.K + ROWB - 1) / ROWB;
+    v4u ra[LA], rb[LB];
+
+    auto gload = [&](int kt) {
+        const uint32_t k0 = (uint32_t)kt * ROWB;
+        // K tail: a chunk is entirely inside or outside K (K % 16 == 0).
+        const bool kin = (kt < nk) && (int)(k0 + ch * 16) < p.K;
+#pragma unroll
+        for (int i = 0; i < LA; ++i) ra[i] = load16(rsA, kin ? a_goff[i] + k0 : kOobOffset);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) rb[i] = load16(rsB, kin ? b_goff[i] + k0 : kOobOffset);
+    };
+    auto swrite = [&](uint8_t *slot) {
+#pragma unroll
+        for (int i = 0; i < LA; ++i) *reinterpret_cast<v4u *>(slot + a_soff[i]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < LB; ++i) *reinterpret_cast<v4u *>(slot + b_soff[i]) = rb[i];
+    };
+    // Fragments of one 64-deep K half: FN row-operand blocks (B rows) and FM
+    // column-operand blocks (A rows), 32 bytes per lane each.
+    auto read_frags = [&](v8i (&bf)[FN], v8i (&af)[FM], const uint8_t *slot, int h) {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+            const uint8_t *rowp = slot + b_frag_base + f * 32 * ROWB;
+            bf[f] = pack8(*reinterpret_cast<const v4u *>(rowp + frag_off[h][0]),
+                          *reinterpret_cast<const v4u *>(rowp + frag_off[h][1]));
+        }
+#pragma unroll
+        for (int f = 0; f < FM; ++f) {
+            const uint8_t *rowp = slot + a_frag_base + f * 32 * ROWB;
+            af[f] = pack8(*reinterpret_cast<const v4u *>(rowp + frag_off[h][0]),
+                          *reinterpret_cast<const v4u *>(rowp + frag_off[h][1]));
+        }
+    };
+    auto mma = [&](const v8i (&bf)[FN], const v8i (&af)[FM]) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) acc[i][j] = mfma32x32x64<FB, FA>(bf[i], af[j], acc[i][j]);
+    };
+
+    // ---- main loop ----
+    // Two LDS slots.  Block kt+1 travels HBM -> registers while the matrix
+    // cores work on block kt, and is stored to the free slot half-way through
+    // block kt; the single barrier per block follows that store.  Fragment
+    // reads run one K half ahead of the matrix cores, so LDS latency hides
+    // behind 16 MFMAs.  The scheduling barriers keep this order (left alone,
+    // the compiler hoists the LDS stores, which then wait out the global-load
+    // latency).  Past the last block the prefetch offsets are out of range:
+    // those loads return zeros without touching memory and are never used.
+    v8i f0b[FN], f0a[FM], f1b[FN], f1a[FM];
+    if (nk > 0) {
+        gload(0);
+        swrite(smem);
+        __syncthreads();
+        gload(1);
+        read_frags(f0b, f0a, smem, 0);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const uint8_t *cur = smem + (kt & 1) * STAGE;
+        uint8_t *nxt = smem + ((kt + 1) & 1) * STAGE;
+        read_frags(f1b, f1a, cur, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(f0b, f0a);
+        __builtin_amdgcn_sched_barrier(0);
+        swrite(nxt);                          // block kt+1, free slot
+        __builtin_amdgcn_sched_barrier(0);
+        gload(kt + 2);
+        __syncthreads();                      // slot kt+1 complete; reads of slot kt done
+        read_frags(f0b, f0a, nxt, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(f1b, f1a);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- epilogue: scale, round to BF16, store the valid rows/columns ----
+    // Accumulator register r of a 32x32 block holds row (of the first operand)
+    // 8 * (r / 4) + 4 * (lane / 32) + r % 4 and column lane % 32.
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int m = m0 + wm * TM + j * 32 + lrow;
+        bool row_ok = (m - m0) < rows_m;
+        if (MODE == MODE_CONTIG && row_ok) row_ok = (p.grp_idx[m] == expert);
+        if (!row_ok) continue;
+        uint16_t *drow = d_base + (int64_t)m * p.ldd;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int n = n0 + wn * TN + i * 32 + b * 8 + khalf * 4;
+                const v16f &c = acc[i][j];
+                const v2u v = pack_bf16x4(c[4 * b] * sc, c[4 * b + 1] * sc, c[4 * b + 2] * sc, c[4 * b + 3] * sc);
+                store_bf16x4(drow, n, p.N - n, v);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming swap-AB kernel.
+// 4 waves; wave w streams weight rows [n0 + w*WR, +WR) as WR/16 row blocks of
+// the 16x16x128 instruction; tokens form up to CB column blocks of 16.  DEPTH
+// register slots keep DEPTH-1 K blocks of loads in flight per wave.
+// ---------------------------------------------------------------------------
+template <int WR, int CB, int FA, int FB, int DEPTH, int MODE>
+__global__ __launch_bounds__(256) void swap_kernel(GemmParams p) {
+    constexpr int RB = WR / 16;
+    constexpr int ROWB = 128;
+    static_assert(RB >= 1 && CB >= 1 && DEPTH >= 2, "shape");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int g = (MODE == MODE_MASKED) ? (int)(blockIdx.x / p.tiles_n) : 0;
+    const int nb = (MODE == MODE_MASKED) ? (int)(blockIdx.x % p.tiles_n) : (int)blockIdx.x;
+
+    // Valid token count: read on the device, clamped; an empty group exits
+    // before forming any address ("MLS three memory-access bugs", Bug 2: a
+    // fully masked tile must not issue loads).
+    const int mg = (MODE == MODE_MASKED) ? min(max(p.masked_m[g], 0), p.cap) : p.M;
+    if (mg <= 0) return;
+    const int nw = nb * 4 * WR + wave * WR;   // first weight row of this wave
+    const int rows_w = min(p.N - nw, WR);
+    if (rows_w <= 0) return;                  // no barrier in this kernel: early exit is safe
+
+    const uint8_t *w_base = p.B + (int64_t)g * p.b_gstride + (int64_t)nw * p.ldb;
+    const uint8_t *t_base = p.A + (int64_t)g * p.a_gstride;
+    uint16_t *d_base = p.D + (int64_t)g * p.d_gstride;
+    const float sc = p.scale_a[0] * p.scale_b[g];
+    const __amdgpu_buffer_rsrc_t rsW = make_rsrc(w_base, rows_bytes(rows_w, p.ldb));
+
+    // Operand layout used for both operands of v_mfma 16x16x128: lane l
+    // carries row (l & 15) and, of each 128-byte K block, the bytes
+    // [(l >> 4) * 16, +16) and [64 + (l >> 4) * 16, +16).  So four lanes read
+    // 64 contiguous bytes of a row per load instruction.
+    const int r16 = lane & 15;
+    const int kg = lane >> 4;
+    uint32_t w_off[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) w_off[r] = (uint32_t)((int64_t)(r * 16 + r16) * p.ldb) + kg * 16;
+
+    const int nk = (p.K + ROWB - 1) / ROWB;
+
+    for (int t0 = 0; t0 < mg; t0 += CB * 16) {
+        const int mt = min(mg - t0, CB * 16);
+        // Token rows past the valid count fall outside this descriptor: they
+        // read as zero and are never fetched (the NaN-filled rows behind them
+        // never reach the matrix cores: same page, Bug 3).
+        const __amdgpu_buffer_rsrc_t rsT = make_rsrc(t_base + (int64_t)t0 * p.lda, rows_bytes(mt, p.lda));
+        uint32_t t_off[CB];
+#pragma unroll
+        for (int c = 0; c < CB; ++c) t_off[c] = (uint32_t)((int64_t)(c * 16 + r16) * p.lda) + kg * 16;
+
+        v4f acc[RB][CB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int c = 0; c < CB; ++c) acc[r][c] = (v4f){0, 0, 0, 0};
+
+        v4u wreg[DEPTH][RB][2];
+        v4u treg[DEPTH][CB][2];
+
+        auto load = [&](int slot, int kt) {
+            const uint32_t k0 = (uint32_t)kt * ROWB + kg * 16;
+            const bool in0 = (kt < nk) && (int)k0 < p.K;
+            const bool in1 = (kt < nk) && (int)(k0 + 64) < p.K;
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                wreg[slot][r][0] = load16(rsW, in0 ? w_off[r] + kt * ROWB : kOobOffset);
+                wreg[slot][r][1] = load16(rsW, in1 ? w_off[r] + kt * ROWB + 64 : kOobOffset);
+            }
+#pragma unroll
+            for (int c = 0; c < CB; ++c) {
+                treg[slot][c][0] = load16(rsT, in0 ? t_off[c] + kt * ROWB : kOobOffset);
+                treg[slot][c][1] = load16(rsT, in1 ? t_off[c] + kt * ROWB + 64 : kOobOffset);
+            }
+        };
+
+        // Branch-free software pipeline: K blocks past the end load as zeros
+        // (out-of-range offsets, no memory traffic) and add nothing, so the
+        // loop body is straight-line code and every wait on a load is exact.
+        // The scheduling barriers keep the load groups in slot order, so the
+        // loads outstanding at the loop head are the same (and in the same
+        // order) on entry and on the back edge, and every wait stays exact.
+#pragma unroll
+        for (int s = 0; s < DEPTH - 1; ++s) {
+            load(s, s);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int kb = 0; kb < nk; kb += DEPTH) {
+#pragma unroll
+            for (int s = 0; s < DEPTH; ++s) {
+                load((s + DEPTH - 1) % DEPTH, kb + s + DEPTH - 1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int r = 0; r < RB; ++r) {
+                    const v8i wf = pack8(wreg[s][r][0], wreg[s][r][1]);
+#pragma unroll
+                    for (int c = 0; c < CB; ++c)
+                        acc[r][c] = mfma16x16x128<FB, FA>(wf, pack8(treg[s][c][0], treg[s][c][1]), acc[r][c]);
+                }
+            }
+        }
+
+        // Epilogue: accumulator register q of a 16x16 block holds weight row
+        // 4 * (lane / 16) + q and token column lane % 16.
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            const int tok = t0 + c * 16 + r16;
+            if (tok >= mg) continue;
+            uint16_t *drow = d_base + (int64_t)tok * p.ldd;
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int n = nw + r * 16 + kg * 4;
+                const v4f &a = acc[r][c];
+                const v2u v = pack_bf16x4(a[0] * sc, a[1] * sc, a[2] * sc, a[3] * sc);
+                store_bf16x4(drow, n, p.N - n, v);
+            }
+        }
+    }
+}
+
+}  // namespace fp8g

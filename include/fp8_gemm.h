@@ -1,0 +1,157 @@
+/*
+ * fp8_gemm.h -- C ABI of the MI355X (gfx950) FP8 GEMM library.
+ *
+ * Computes D = bf16( scale_a * scale_b * A . B^T ) with FP8 operands (E4M3 or
+ * E5M2, chosen per operand), FP32 accumulation on the CDNA4 matrix cores, and a
+ * fused epilogue that applies the per-tensor scales and rounds to BF16.
+ *
+ * Sources on the pages:
+ *   - "DeepGEMM: FP8 matrix-multiply kernels on Hopper Tensor Cores":
+ *       section 1.3 and 3.1 (FP8 E4M3/E5M2 inputs, FP32 accumulator, the scale
+ *       multiplied back once at the output), section 2.1 (what one output
+ *       element is), section 5.2 (per-tensor scales), section 6.4 (alignment
+ *       matters; no unordered FP32 atomics, so results are deterministic).
+ *   - "One transpose, half the compute: the DeepSeek SwapAB story":
+ *       section 2 (MoE decode: each expert sees only tens of tokens),
+ *       section 3.1 (the masked grouped FP8 GEMM, "nt" layout: both operands
+ *       K-contiguous), section 3.2-3.3 (operands swapped so weights take the
+ *       rigid side and the tokens the flexible side; work shrinks to the
+ *       valid rows), section 3.5 (the swap is chosen on the host from the
+ *       per-expert token count).
+ *
+ * Conventions for every entry point:
+ *   - All pointers except `stream` are DEVICE pointers (memory the caller
+ *     allocated, e.g. through PyTorch).  The caller owns every buffer; the
+ *     library allocates nothing, keeps no pointer after returning, and never
+ *     synchronises the stream.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *     Results are valid once that stream's work has completed.
+ *   - FP8 operands are byte arrays of codes; dtypes are FP8G_E4M3 (OCP E4M3FN:
+ *     max 448, S.1111.111 = NaN, no infinities) or FP8G_E5M2 (OCP E5M2).
+ *   - D is BF16 (uint16 bit patterns), rounded to nearest even.  D must not
+ *     alias A, B, the scales or the index vectors.
+ *   - Arguments are validated before anything is enqueued.  A nonzero return
+ *     (an fp8g_status) means nothing was enqueued; fp8_gemm_strerror() gives the
+ *     reason, including a per-thread detail string for the last failure.
+ *   - Zero-sized problems (M, N, G, cap or M_total = 0) return FP8G_OK and
+ *     enqueue nothing.  K = 0 writes zeros (the empty sum).
+ *   - Limits: K % 16 == 0; A, B, D pointers 16-byte aligned; row strides in
+ *     bytes (A, B) multiples of 16 and at most 2^23 - 16; ldd a multiple of 8
+ *     elements; M, N, K, G, cap, M_total below 2^31.
+ *   - Values that live on the device (masked_m, grp_idx) cannot be checked
+ *     without a synchronisation: masked_m[g] is clamped to [0, cap], and any
+ *     grp_idx entry outside [0, G) marks a padding row.
+ *   - Results are deterministic: no atomics, no split-K; the same call on the
+ *     same inputs gives bit-identical D.
+ */
+#ifndef FP8_GEMM_H
+#define FP8_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8G_ABI_VERSION 1
+
+typedef enum { FP8G_E4M3 = 0, FP8G_E5M2 = 1 } fp8g_dtype;
+
+typedef enum {
+    FP8G_OK = 0,
+    FP8G_ERR_NULL = -1,         /* a required pointer is NULL */
+    FP8G_ERR_SHAPE = -2,        /* negative or too large size, K % 16 != 0 */
+    FP8G_ERR_ALIGN = -3,        /* pointer or stride not 16-byte aligned */
+    FP8G_ERR_DTYPE = -4,        /* dtype is neither FP8G_E4M3 nor FP8G_E5M2 */
+    FP8G_ERR_STRIDE = -5,       /* lda/ldb < K, ldd < N, or stride too large */
+    FP8G_ERR_LAUNCH = -6,       /* the HIP launch reported an error */
+    FP8G_ERR_UNSUPPORTED = -7,  /* no device of the supported architecture */
+    FP8G_ERR_ARG = -8           /* any other invalid argument (e.g. expected_m > cap) */
+} fp8g_status;
+
+/*
+ * Dense GEMM, "nt" layout.
+ *   A: [M x K] FP8 codes, row stride lda bytes (K contiguous).
+ *   B: [N x K] FP8 codes, row stride ldb bytes (K contiguous).
+ *   scale_a, scale_b: one FP32 each (device).
+ *   D: [M x N] BF16, row stride ldd elements.
+ *   D[i][j] = bf16_rne( (scale_a * scale_b) * sum_k A[i][k] * B[j][k] ).
+ * M <= 64 takes the swapped (weights-on-rows, tokens-on-columns) streaming
+ * kernel; larger M takes the LDS-tiled kernel.  The choice never changes
+ * which elements are written.
+ */
+int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype,
+                const void *B, int64_t ldb, int b_dtype,
+                const float *scale_a, const float *scale_b,
+                void *D, int64_t ldd,
+                int M, int N, int K, void *stream);
+
+/*
+ * Masked grouped GEMM (MoE decode).
+ *   A: [G][cap][K] FP8 codes, contiguous.  B: [G][N][K] FP8 codes, contiguous.
+ *   masked_m: [G] int32 (device); group g has m_g = clamp(masked_m[g], 0, cap)
+ *     valid rows.
+ *   scale_a: 1 float; scale_b: [G] floats (device), one per expert.
+ *   D: [G][cap][N] BF16, contiguous.
+ *   For i < m_g: D[g][i][j] = bf16_rne( (scale_a * scale_b[g]) * sum_k A[g][i][k] * B[g][j][k] ).
+ *   Rows i >= m_g of A are never read and rows i >= m_g of D are never written.
+ *   A group with m_g = 0 reads nothing.
+ *   expected_m: host hint of the typical m_g, 0 <= expected_m <= cap (0 = use
+ *     cap).  It only picks the kernel variant (the swapped streaming kernel
+ *     when it is <= 64) and never changes results.
+ */
+int fp8_grouped_gemm_masked(const void *A, int a_dtype, const void *B, int b_dtype,
+                            const float *scale_a, const float *scale_b,
+                            const int32_t *masked_m, void *D,
+                            int G, int cap, int N, int K, int expected_m, void *stream);
+
+/*
+ * Contiguous grouped GEMM (MoE prefill).
+ *   A: [M_total][K] FP8 codes, contiguous; the rows of each expert are
+ *     contiguous and each expert's run starts on a multiple of 128 rows
+ *     (padding rows fill each run up to the next multiple of 128).
+ *   B: [G][N][K] FP8 codes, contiguous.  scale_a: 1 float; scale_b: [G] floats.
+ *   grp_idx: [M_total] int32 (device).  Row r with 0 <= grp_idx[r] < G uses
+ *     expert grp_idx[r]; any other value marks a padding row, which is not
+ *     written.  Every aligned block of 128 rows must hold rows of at most one
+ *     expert (plus padding); rows of a second expert inside a block are left
+ *     unwritten.
+ *   D: [M_total][N] BF16, contiguous.
+ */
+int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dtype,
+                            const float *scale_a, const float *scale_b,
+                            const int32_t *grp_idx, void *D,
+                            int M_total, int G, int N, int K, void *stream);
+
+/*
+ * Kernel choice for a problem, without launching anything (host only).
+ *   op: 0 = dense (m = M), 1 = masked grouped (m = cap, hint = expected_m,
+ *   groups = G), 2 = contiguous grouped (m = M_total, groups = G).
+ * Fills the variant id, the tile sizes along M and N, and the number of
+ * workgroups of the launch.  Returns an fp8g_status (validation as above,
+ * pointers excepted).
+ */
+typedef struct {
+    int variant;        /* 1 = tiled 256x256, 2 = tiled 128x256 (m x n),
+                           3 = swapped streaming, 0 = nothing to launch */
+    int tile_m;         /* rows of D per workgroup tile (tokens) */
+    int tile_n;         /* columns of D per workgroup tile */
+    int token_blocks;   /* swapped kernel: 16-token column blocks per pass */
+    int64_t workgroups; /* grid size */
+} fp8g_plan;
+
+int fp8_gemm_plan(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan *out);
+
+/* Human-readable text for a status, followed by the calling thread's detail
+ * for its last failed call (the returned pointer stays valid until that
+ * thread's next call into the library). */
+const char *fp8_gemm_strerror(int status);
+
+/* FP8G_ABI_VERSION of the built library. */
+int fp8_gemm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8_GEMM_H */

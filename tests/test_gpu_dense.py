@@ -1,0 +1,286 @@
+"""GPU parity of the dense FP8 GEMM (fp8_gemm_nt) against the CPU oracle.
+
+Calls go through the C ABI (via the Python binding).  Bit-exact checks where the
+exact result is representable (decode table, one-hot layout, closed forms,
+rounding ties); the element-wise bound of tests/_parity.py elsewhere.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._parity import assert_within_bound, gpu_bits
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E5M2 = 0, 1
+
+
+def _lib():
+    import fp8_gemm_amd
+    return fp8_gemm_amd
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _scale(v):
+    return torch.tensor([v], dtype=torch.float32, device="cuda")
+
+
+def run_dense(A, B, a_fmt, b_fmt, sa=1.0, sb=1.0, out=None):
+    print(f"[dense] M={A.shape[0]} N={B.shape[0]} K={A.shape[1]} fmt=({a_fmt},{b_fmt}) sa={sa} sb={sb}", flush=True)
+    f = _lib()
+    d = f.gemm_nt(_dev(A), _dev(B), _scale(sa), _scale(sb), out=out, a_dtype=a_fmt, b_dtype=b_fmt)
+    torch.cuda.synchronize()
+    return gpu_bits(d)
+
+
+def _nan_eq(a, b):
+    """Bit equality, with any NaN pattern matching any NaN pattern."""
+    a = np.asarray(a, np.uint16)
+    b = np.asarray(b, np.uint16)
+    nan_a = ((a & 0x7F80) == 0x7F80) & ((a & 0x007F) != 0)
+    nan_b = ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
+    return np.where(nan_a | nan_b, nan_a == nan_b, a == b)
+
+
+# ---------------------------------------------------------------------------
+# Bit-exact pins
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("a_fmt,b_fmt", [(E4M3, E4M3), (E5M2, E5M2), (E4M3, E5M2), (E5M2, E4M3)])
+def test_decode_product_table(a_fmt, b_fmt):
+    """Row i of A holds code i at k = 0, row j of B holds code j: D[i][j] is
+    dec(i) * dec(j), exact in BF16, so decode and format selection are pinned
+    bit for bit over all 256 x 256 code pairs."""
+    K = 16
+    A = np.zeros((256, K), np.uint8)
+    B = np.zeros((256, K), np.uint8)
+    A[:, 0] = np.arange(256)
+    B[:, 0] = np.arange(256)
+    ref, _, _, _ = oracle.gemm_nt(A, B, a_fmt, b_fmt)
+    got = run_dense(A, B, a_fmt, b_fmt)
+    ok = _nan_eq(got, ref)
+    assert ok.all(), f"{int((~ok).sum())} mismatches, first at {np.argwhere(~ok)[:4].tolist()}"
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 260, 384), (40, 96, 256)])
+def test_one_hot_layout(M, N, K):
+    """One product per output row at a distinct K position: pins the row,
+    column and K placement of both operands and of the accumulator."""
+    rng = np.random.default_rng(M + N + K)
+    n = min(M, N, K)
+    rows = rng.permutation(M)[:n]
+    cols = rng.permutation(N)[:n]
+    ks = rng.permutation(K)[:n]
+    A = np.zeros((M, K), np.uint8)
+    B = np.zeros((N, K), np.uint8)
+    A[rows, ks] = 0x40      # 2.0
+    B[cols, ks] = 0x48      # 4.0
+    ref, _, _, _ = oracle.gemm_nt(A, B)
+    got = run_dense(A, B, E4M3, E4M3)
+    assert np.array_equal(got, ref)
+    assert (got[rows, cols] == oracle.bf16_rne(8.0)).all()
+
+
+@pytest.mark.parametrize("K", [128, 256, 1280, 4096, 7168, 14336])
+@pytest.mark.parametrize("M", [48, 130])
+def test_all_ones_gives_K(K, M):
+    for fmt, one in ((E4M3, 0x38), (E5M2, 0x3C)):
+        A = np.full((M, K), one, np.uint8)
+        B = np.full((72, K), one, np.uint8)
+        got = run_dense(A, B, fmt, fmt)
+        assert (got == oracle.bf16_rne(float(K))).all()
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("M", [33, 200])
+def test_identity_B_returns_A(fmt, M):
+    K = 256
+    one = 0x38 if fmt == E4M3 else 0x3C
+    rng = np.random.default_rng(5)
+    codes = np.array([c for c in range(256) if np.isfinite(oracle.decode_table(fmt)[c])], np.uint8)
+    A = rng.choice(codes, size=(M, K))
+    B = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(B, one)
+    ref, _, _, _ = oracle.gemm_nt(A, B, fmt, fmt)
+    got = run_dense(A, B, fmt, fmt)
+    # +0 and -0 compare equal
+    same = (got == ref) | (((got | ref) & 0x7FFF) == 0)
+    assert same.all()
+
+
+def test_max_magnitude():
+    K = 4096
+    A = np.full((80, K), 0x7E, np.uint8)
+    B = np.full((64, K), 0x7E, np.uint8)
+    B[1::2] = 0xFE
+    got = run_dense(A, B, E4M3, E4M3)
+    assert (got[:, 0::2] == 0x4E44).all() and (got[:, 1::2] == 0xCE44).all()
+
+
+def test_rounding_ties_bit_exact():
+    """1 + 2^-8 -> 1.0 and 1 + 3*2^-8 -> 1 + 2^-6 (round to nearest even);
+    both sums are exact in the FP32 accumulator."""
+    A = np.zeros((96, 128), np.uint8)
+    A[:, 0] = 0x38
+    A[0::2, 1] = 0x02
+    A[1::2, 1] = 0x06
+    B = np.zeros((16, 128), np.uint8)
+    B[:, :2] = 0x38
+    got = run_dense(A, B, E4M3, E4M3)
+    assert (got[0::2] == 0x3F80).all() and (got[1::2] == 0x3F82).all()
+
+
+def test_power_of_two_scale_is_exact():
+    w = workloads.dense_random(130, 96, 512, seed=17)
+    d1 = run_dense(w.A, w.B, E4M3, E4M3, 1.0, 1.0)
+    d4 = run_dense(w.A, w.B, E4M3, E4M3, 2.0, 2.0)
+    x1 = torch.from_numpy(d1.view(np.int16)).view(torch.bfloat16).float()
+    x4 = torch.from_numpy(d4.view(np.int16)).view(torch.bfloat16).float()
+    assert torch.equal(x1 * 4, x4)
+
+
+# ---------------------------------------------------------------------------
+# Bound checks
+# ---------------------------------------------------------------------------
+
+def _check_dense(w, what, out=None):
+    d = run_dense(w.A, w.B, w.a_fmt, w.b_fmt, w.sa, w.sb, out=out)
+    ref, r, s, _ = oracle.gemm_nt(w.A, w.B, w.a_fmt, w.b_fmt, w.sa, w.sb)
+    frac = assert_within_bound(d, r, s, abs(w.sa * w.sb), ref_bits=ref, what=what)
+    print(f"  {what}: bit-identical fraction {frac:.4f}", flush=True)
+    return d
+
+
+SHAPES = [(1, 1, 16), (1, 200, 128), (7, 64, 144), (16, 257, 112), (17, 129, 1280), (33, 255, 256),
+          (63, 64, 128), (64, 65, 16), (65, 64, 128), (127, 128, 144), (128, 127, 256), (129, 257, 384),
+          (255, 300, 640), (257, 255, 1280), (300, 520, 272), (513, 260, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_ragged_shapes_e4m3(M, N, K):
+    w = workloads.dense_random(M, N, K, seed=M * 7 + N * 3 + K, std=1.0, scales=(0.75, 1.5))
+    _check_dense(w, f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", [(E5M2, E5M2), (E4M3, E5M2), (E5M2, E4M3)])
+@pytest.mark.parametrize("M,N,K", [(40, 136, 384), (300, 264, 512)])
+def test_formats(M, N, K, a_fmt, b_fmt):
+    w = workloads.dense_random(M, N, K, seed=99, a_fmt=a_fmt, b_fmt=b_fmt, scales=(1.25, 0.5))
+    _check_dense(w, f"{M}x{N}x{K} fmt {a_fmt}{b_fmt}")
+
+
+def test_dense_256_config():
+    w = workloads.dense_small()
+    _check_dense(w, "dense 256^3")
+
+
+def test_strided_operands_and_output():
+    M, N, K = 200, 136, 256
+    w = workloads.dense_random(M, N, K, seed=12)
+    A = np.zeros((M, K + 48), np.uint8)
+    A[:, :K] = w.A
+    B = np.zeros((N, K + 16), np.uint8)
+    B[:, :K] = w.B
+    f = _lib()
+    a = _dev(A)[:, :K]
+    b = _dev(B)[:, :K]
+    big = torch.full((M, N + 40), -7.0, dtype=torch.bfloat16, device="cuda")
+    out = big[:, :N]
+    f.gemm_nt(a, b, _scale(1.0), _scale(1.0), out=out, a_dtype=E4M3, b_dtype=E4M3)
+    torch.cuda.synchronize()
+    ref, r, s, _ = oracle.gemm_nt(w.A, w.B)
+    assert_within_bound(gpu_bits(out), r, s, 1.0, what="strided")
+    assert (big[:, N:] == -7.0).all()
+
+
+def _sample_points(M, N, n, seed):
+    rng = np.random.default_rng(seed)
+    ii = np.concatenate([rng.integers(0, M, n), np.zeros(N // 8, np.int64), np.full(N // 8, M - 1)])
+    jj = np.concatenate([rng.integers(0, N, n), np.arange(0, N, 8), np.arange(3, N, 8)])
+    return ii, jj
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_dense_4096_config_sampled(fmt):
+    w = workloads.dense_square(fmt)
+    M, N, K = w.shape
+    d = run_dense(w.A, w.B, fmt, fmt, w.sa, w.sb)
+    ii, jj = _sample_points(M, N, 6000, seed=fmt)
+    ref, r, s, _ = oracle.gemm_nt_points(w.A, w.B, ii, jj, fmt, fmt, w.sa, w.sb)
+    frac = assert_within_bound(d[ii, jj], r, s, abs(w.sa * w.sb), ref_bits=ref, what=f"4096^3 fmt {fmt}")
+    print(f"  bit-identical fraction {frac:.4f}", flush=True)
+    # full rows and columns through the tile boundaries
+    rows = np.array([0, 255, 256, 4095])
+    Dr, Rr, Sr, _ = oracle.gemm_nt(w.A[rows], w.B, fmt, fmt, w.sa, w.sb)
+    assert_within_bound(d[rows], Rr, Sr, abs(w.sa * w.sb), what="full rows")
+
+
+@pytest.mark.parametrize("M,N,K", [(6144, 6144, 1280), (4096, 4096, 1024)])
+def test_k_tail_regression_shapes_sampled(M, N, K):
+    """Shapes from "DeepGEMM on Hopper Tensor Cores", section 6.1: one failed
+    there (K=1280), one passed (K=1024)."""
+    w = workloads.dense_random(M, N, K, seed=61, std=0.5, scales=(1.0, 1.0))
+    d = run_dense(w.A, w.B, E4M3, E4M3)
+    ii, jj = _sample_points(M, N, 4000, seed=K)
+    ref, r, s, _ = oracle.gemm_nt_points(w.A, w.B, ii, jj)
+    assert_within_bound(d[ii, jj], r, s, 1.0, what=f"{M}x{N}x{K}")
+
+
+def test_deterministic_repeats():
+    w = workloads.dense_random(512, 384, 1024, seed=3)
+    outs = [run_dense(w.A, w.B, E4M3, E4M3) for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+    ws = workloads.dense_random(24, 384, 1024, seed=4)
+    outs = [run_dense(ws.A, ws.B, E4M3, E4M3) for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+@pytest.mark.parametrize("M,N", [(48, 300), (300, 48)])
+def test_swap_identity(M, N):
+    """D^T = B . A^T: the swapped call (which may take the other kernel) is
+    within the bound of the transposed oracle result."""
+    K = 768
+    w = workloads.dense_random(M, N, K, seed=8)
+    dt = run_dense(w.B, w.A, E4M3, E4M3)
+    ref, r, s, _ = oracle.gemm_nt(w.A, w.B)
+    assert_within_bound(dt.T, r, s, 1.0, what="swap identity")
+
+
+def test_nan_inputs_propagate():
+    M, N, K = 100, 80, 256
+    w = workloads.dense_random(M, N, K, seed=10)
+    A = w.A.copy()
+    B = w.B.copy()
+    A[5, 17] = 0x7F
+    B[9, 200] = 0x7F
+    d = run_dense(A, B, E4M3, E4M3)
+    ref, r, s, _ = oracle.gemm_nt(A, B)
+    assert_within_bound(d, r, s, 1.0, what="nan inputs")
+
+
+def test_zero_sizes_and_empty_k():
+    f = _lib()
+    a = torch.zeros((0, 32), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((16, 32), dtype=torch.uint8, device="cuda")
+    out = f.gemm_nt(a, b, _scale(1.0), _scale(1.0), a_dtype=E4M3, b_dtype=E4M3)
+    assert out.shape == (0, 16)
+    a = torch.zeros((70, 0), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((24, 0), dtype=torch.uint8, device="cuda")
+    out = torch.full((70, 24), 3.0, dtype=torch.bfloat16, device="cuda")
+    f.gemm_nt(a, b, _scale(1.0), _scale(1.0), out=out, a_dtype=E4M3, b_dtype=E4M3)
+    torch.cuda.synchronize()
+    assert (out == 0).all()
+
+
+def test_validation_errors_through_binding():
+    f = _lib()
+    a = torch.zeros((64, 40), dtype=torch.uint8, device="cuda")   # K = 40: not a multiple of 16
+    b = torch.zeros((64, 40), dtype=torch.uint8, device="cuda")
+    with pytest.raises(f.Fp8GemmError) as e:
+        f.gemm_nt(a, b, _scale(1.0), _scale(1.0), a_dtype=E4M3, b_dtype=E4M3)
+    assert e.value.status == -2

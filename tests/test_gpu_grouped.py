@@ -1,0 +1,187 @@
+"""GPU parity of the masked and contiguous grouped FP8 GEMMs against the oracle.
+
+Masked form: rows >= m_g of every group must keep their sentinel bytes, and
+the NaN-filled activation rows behind them must never reach the result.
+Contiguous form: padding rows (grp_idx = -1) must keep their sentinel bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._parity import assert_within_bound, gpu_bits
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0xDEAD
+E4M3, E5M2 = 0, 1
+
+
+def _lib():
+    import fp8_gemm_amd
+    return fp8_gemm_amd
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _sentinel_out(shape):
+    t = torch.empty(shape, dtype=torch.int16, device="cuda")
+    t.fill_(np.int16(np.uint16(SENT).view(np.int16)))
+    return t.view(torch.bfloat16)
+
+
+def run_masked(w, expected_m=0):
+    G, cap, K = w.A.shape
+    N = w.B.shape[1]
+    print(f"[masked] G={G} cap={cap} N={N} K={K} m={w.masked_m.tolist()[:12]} hint={expected_m}", flush=True)
+    f = _lib()
+    out = _sentinel_out((G, cap, N))
+    f.grouped_gemm_masked(_dev(w.A), _dev(w.B), torch.tensor([w.sa], dtype=torch.float32, device="cuda"),
+                          _dev(w.sb), _dev(w.masked_m), out=out, expected_m=expected_m,
+                          a_dtype=w.a_fmt, b_dtype=w.b_fmt)
+    torch.cuda.synchronize()
+    return gpu_bits(out)
+
+
+def check_masked(w, d, rows_per_group=None):
+    G, cap, K = w.A.shape
+    m = np.clip(w.masked_m, 0, cap)
+    for g in range(G):
+        assert (d[g, m[g]:] == SENT).all(), f"group {g}: rows >= m_g were written"
+    if rows_per_group is None:
+        ref, r, s, _ = oracle.grouped_masked(w.A, w.B, w.masked_m, w.sb, w.a_fmt, w.b_fmt, w.sa)
+        for g in range(G):
+            if m[g]:
+                assert_within_bound(d[g, :m[g]], r[g, :m[g]], s[g, :m[g]], abs(w.sa * w.sb[g]), what=f"group {g}")
+        return
+    rng = np.random.default_rng(0)
+    for g in range(G):
+        if not m[g]:
+            continue
+        rows = np.unique(np.concatenate([[0, m[g] - 1], rng.integers(0, m[g], rows_per_group)]))
+        ref, r, s, _ = oracle.gemm_nt(w.A[g, rows], w.B[g], w.a_fmt, w.b_fmt, w.sa, float(w.sb[g]))
+        assert_within_bound(d[g, rows], r, s, abs(w.sa * w.sb[g]), what=f"group {g}")
+
+
+COUNTS = [0, 1, 16, 17, 32, 33, 64, 40]
+
+
+@pytest.mark.parametrize("hint", [0, 16, 32, 64])
+def test_masked_all_count_classes(hint):
+    """Counts 0 (skipped), 1, a full 16-token block, one past it, 32, 33,
+    the capacity, and a hint that is too small (it picks the kernel only)."""
+    w = workloads.masked_random(len(COUNTS), 64, 200, 640, seed=41, m_values=COUNTS)
+    d = run_masked(w, expected_m=hint)
+    check_masked(w, d)
+
+
+def test_masked_large_counts_take_tiled_kernel():
+    w = workloads.masked_random(4, 192, 264, 384, seed=42, m_values=[0, 100, 192, 129])
+    assert _lib().plan(1, 192, 264, 384, 4, 0).variant != 3
+    d = run_masked(w)
+    check_masked(w, d)
+
+
+def test_masked_clamps_counts():
+    w = workloads.masked_random(3, 32, 128, 256, seed=43, m_values=[-5, 1000, 7])
+    d = run_masked(w)
+    check_masked(w, d)
+
+
+def test_masked_all_groups_empty():
+    w = workloads.masked_random(5, 64, 128, 256, seed=44, m_values=[0] * 5)
+    d = run_masked(w)
+    assert (d == SENT).all()
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", [(E4M3, E5M2), (E5M2, E5M2)])
+def test_masked_formats(a_fmt, b_fmt):
+    w = workloads.masked_random(3, 64, 136, 512, seed=45, m_values=[5, 31, 64], a_fmt=a_fmt, b_fmt=b_fmt)
+    d = run_masked(w)
+    check_masked(w, d)
+
+
+def test_masked_decode_config_sampled():
+    """G=32, cap=64, N=4096, K=7168, m_g ~ U{0..32}: every untouched row is
+    checked byte for byte, valid rows are sampled per group."""
+    w = workloads.masked_decode()
+    d = run_masked(w, expected_m=32)
+    check_masked(w, d, rows_per_group=3)
+
+
+def test_grouped_equals_per_group_dense():
+    w = workloads.masked_random(3, 64, 256, 1024, seed=46, m_values=[64, 20, 3])
+    d = run_masked(w)
+    f = _lib()
+    for g in range(3):
+        m = int(w.masked_m[g])
+        out = f.gemm_nt(_dev(w.A[g, :m]), _dev(w.B[g]), torch.tensor([w.sa], dtype=torch.float32, device="cuda"),
+                        torch.tensor([w.sb[g]], dtype=torch.float32, device="cuda"), a_dtype=E4M3, b_dtype=E4M3)
+        torch.cuda.synchronize()
+        dd = gpu_bits(out)
+        ref, r, s, _ = oracle.gemm_nt(w.A[g, :m], w.B[g], sa=w.sa, sb=float(w.sb[g]))
+        assert_within_bound(dd, r, s, abs(w.sa * w.sb[g]), what=f"dense group {g}")
+        assert_within_bound(d[g, :m], r, s, abs(w.sa * w.sb[g]), what=f"grouped group {g}")
+
+
+# ---------------------------------------------------------------------------
+# Contiguous grouped
+# ---------------------------------------------------------------------------
+
+def run_contig(w):
+    M_total, K = w.A.shape
+    G, N, _ = w.B.shape
+    print(f"[contig] M_total={M_total} G={G} N={N} K={K}", flush=True)
+    f = _lib()
+    out = _sentinel_out((M_total, N))
+    f.grouped_gemm_contig(_dev(w.A), _dev(w.B), torch.tensor([w.sa], dtype=torch.float32, device="cuda"),
+                          _dev(w.sb), _dev(w.grp_idx), out=out, a_dtype=w.a_fmt, b_dtype=w.b_fmt)
+    torch.cuda.synchronize()
+    return gpu_bits(out)
+
+
+def check_contig(w, d, sample_rows=None):
+    pad = w.grp_idx < 0
+    assert (d[pad] == SENT).all(), "padding rows were written"
+    if sample_rows is None:
+        ref, r, s, _ = oracle.grouped_contig(w.A, w.B, w.grp_idx, w.sb, w.a_fmt, w.b_fmt, w.sa)
+        real = ~pad
+        scale = np.abs(w.sa * w.sb[np.maximum(w.grp_idx, 0)])[:, None]
+        assert_within_bound(d[real], r[real], s[real], scale[real], what="contig")
+        return
+    rng = np.random.default_rng(1)
+    real_rows = np.flatnonzero(~pad)
+    rows = np.unique(rng.choice(real_rows, size=min(sample_rows, real_rows.size), replace=False))
+    for g in np.unique(w.grp_idx[rows]):
+        rg = rows[w.grp_idx[rows] == g]
+        ref, r, s, _ = oracle.gemm_nt(w.A[rg], w.B[g], w.a_fmt, w.b_fmt, w.sa, float(w.sb[g]))
+        assert_within_bound(d[rg], r, s, abs(w.sa * w.sb[g]), what=f"contig expert {g}")
+
+
+def test_contig_small():
+    w = workloads.contig_random(tokens=300, topk=2, G=5, N=264, K=512, seed=51)
+    d = run_contig(w)
+    check_contig(w, d)
+
+
+def test_contig_empty_experts_and_tail():
+    w = workloads.contig_random(tokens=0, topk=1, G=4, N=128, K=256, seed=52, counts=[0, 129, 0, 1])
+    assert w.A.shape[0] == 256 + 128
+    d = run_contig(w)
+    check_contig(w, d)
+
+
+def test_contig_formats():
+    w = workloads.contig_random(tokens=200, topk=1, G=3, N=136, K=384, seed=53, a_fmt=E5M2, b_fmt=E4M3)
+    d = run_contig(w)
+    check_contig(w, d)
+
+
+def test_contig_prefill_config_sampled():
+    """8192 tokens x top-8 over 32 experts, N=4096, K=7168."""
+    w = workloads.contig_prefill()
+    d = run_contig(w)
+    check_contig(w, d, sample_rows=192)

@@ -1,0 +1,173 @@
+"""Host-side checks of the C ABI (CPU only, no kernel launch).
+
+The library must load without a GPU, export every function that
+include/fp8_gemm.h declares, choose kernels as documented, and reject invalid
+arguments before touching the HIP runtime.  Only invalid argument sets are
+passed here: validation fails before any pointer is used.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def f():
+    import fp8_gemm_amd
+    from fp8_gemm_amd import _build
+    if not os.path.exists(fp8_gemm_amd.LIB_PATH):
+        _build.build()
+    fp8_gemm_amd.load_library()
+    return fp8_gemm_amd
+
+
+def declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(inc, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\([^;]*\)\s*;", text, flags=re.M)
+    return names
+
+
+def test_every_declared_symbol_is_exported(f):
+    names = declared_functions()
+    assert set(names) >= {"fp8_gemm_nt", "fp8_grouped_gemm_masked", "fp8_grouped_gemm_contig"}
+    lib = ctypes.CDLL(f.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+    assert set(f.SYMBOLS) == set(names)
+
+
+def test_abi_version(f):
+    assert f.load_library().fp8_gemm_abi_version() == 1
+
+
+@pytest.mark.parametrize("args,variant", [
+    ((0, 4096, 4096, 4096), 1),          # large square: 256x256 tiles, one per CU
+    ((0, 2048, 4096, 4096), 2),          # 128 tiles of 256x256 would leave half the CUs idle
+    ((0, 64, 4096, 7168), 3),            # M <= 64: swapped streaming kernel
+    ((0, 65, 4096, 7168), 2),
+    ((0, 1, 16, 16), 3),
+])
+def test_dense_plan(f, args, variant):
+    p = f.plan(*args)
+    assert p.variant == variant
+
+
+def test_dense_plan_grid(f):
+    p = f.plan(0, 4096, 4096, 4096)
+    assert (p.tile_m, p.tile_n, p.workgroups) == (256, 256, 256)
+    p = f.plan(0, 17, 4096, 7168)
+    assert p.token_blocks == 2 and p.workgroups == 4096 // 128
+
+
+def test_masked_plan_uses_hint_not_results(f):
+    p = f.plan(1, 64, 4096, 7168, 32, 32)
+    assert p.variant == 3 and p.token_blocks == 2 and p.workgroups == 32 * 32
+    p = f.plan(1, 64, 4096, 7168, 32, 0)           # hint 0 -> capacity
+    assert p.variant == 3 and p.token_blocks == 4
+    p = f.plan(1, 256, 4096, 7168, 8, 0)           # many rows per group -> tiled
+    assert p.variant == 2 and p.workgroups == 8 * 2 * 16
+    with pytest.raises(f.Fp8GemmError) as e:
+        f.plan(1, 64, 4096, 7168, 32, 65)          # hint above capacity
+    assert e.value.status == -8
+
+
+def test_contig_plan(f):
+    p = f.plan(2, 67584, 4096, 7168, 32)
+    assert p.variant == 2 and p.tile_m == 128 and p.workgroups == (67584 // 128) * 16
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 10, 10, 17), -2),       # K % 16
+    ((0, -1, 10, 16), -2),
+    ((0, 10, 10, 1 << 23), -2),  # K above the stride limit
+    ((3, 10, 10, 16), -8),       # unknown op
+])
+def test_plan_errors(f, args, status):
+    with pytest.raises(f.Fp8GemmError) as e:
+        f.plan(*args)
+    assert e.value.status == status
+
+
+def test_zero_sizes_plan_nothing(f):
+    assert f.plan(0, 0, 128, 128).variant == 0
+    assert f.plan(1, 64, 128, 128, 0, 0).variant == 0
+    assert f.plan(2, 0, 128, 128, 4).variant == 0
+
+
+# Raw C calls with invalid argument sets: each must fail validation.
+A16 = 0x10000            # fake, 16-byte aligned addresses (never dereferenced)
+A_ODD = 0x10008
+
+
+def _nt(f, **kw):
+    args = dict(A=A16, lda=128, a=0, B=A16, ldb=128, b=0, sa=A16, sb=A16, D=A16, ldd=128, M=128, N=128, K=128)
+    args.update(kw)
+    lib = f.load_library()
+    st = lib.fp8_gemm_nt(args["A"], args["lda"], args["a"], args["B"], args["ldb"], args["b"], args["sa"],
+                         args["sb"], args["D"], args["ldd"], args["M"], args["N"], args["K"], None)
+    return st, lib.fp8_gemm_strerror(st).decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=None), -1), (dict(D=None), -1), (dict(sa=None), -1),
+    (dict(A=A_ODD), -3), (dict(D=A_ODD), -3), (dict(lda=136), -3), (dict(ldd=132), -3),
+    (dict(a=2), -4), (dict(b=-1), -4),
+    (dict(lda=112), -5), (dict(ldd=120), -5), (dict(ldb=1 << 24), -5),
+    (dict(K=24), -2), (dict(M=-3), -2),
+])
+def test_dense_validation(f, kw, status):
+    st, msg = _nt(f, **kw)
+    assert st == status, msg
+    assert ":" in msg   # carries the detail string
+
+
+def test_dense_zero_size_is_noop(f):
+    st, _ = _nt(f, M=0, A=None, D=None)
+    assert st == 0
+    st, _ = _nt(f, N=0)
+    assert st == 0
+
+
+def test_masked_validation(f):
+    lib = f.load_library()
+    ok = dict(A=A16, a=0, B=A16, b=0, sa=A16, sb=A16, mm=A16, D=A16, G=4, cap=64, N=128, K=128, hint=0)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.fp8_grouped_gemm_masked(a["A"], a["a"], a["B"], a["b"], a["sa"], a["sb"], a["mm"], a["D"],
+                                           a["G"], a["cap"], a["N"], a["K"], a["hint"], None)
+    assert call(mm=None) == -1
+    assert call(hint=65) == -8
+    assert call(hint=-1) == -8
+    assert call(N=100) == -3
+    assert call(K=8) == -2
+    assert call(G=-1) == -2
+    assert call(a=5) == -4
+    assert call(G=0, A=None) == 0
+    assert call(cap=0, A=None) == 0
+
+
+def test_contig_validation(f):
+    lib = f.load_library()
+    ok = dict(A=A16, a=0, B=A16, b=0, sa=A16, sb=A16, gi=A16, D=A16, M=256, G=4, N=128, K=128)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.fp8_grouped_gemm_contig(a["A"], a["a"], a["B"], a["b"], a["sa"], a["sb"], a["gi"], a["D"],
+                                           a["M"], a["G"], a["N"], a["K"], None)
+    assert call(gi=None) == -1
+    assert call(G=0) == -2
+    assert call(N=12) == -3
+    assert call(gi=A16 + 2) == -3
+    assert call(M=0, A=None) == 0

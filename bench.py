@@ -1,0 +1,310 @@
+"""Benchmark of the FP8 GEMM path on one MI355X.
+
+Metric: FP8 TFLOP/s (and fraction of the MFMA FP8 peak) of the dense 4096^3
+E4M3 GEMM; HBM GB/s of the masked grouped decode GEMM (m_g <= 32).
+
+One step = one dense 4096^3 GEMM (D = bf16(sa*sb*A.B^T), inputs resident in
+HBM).  `value` is the whole-job rate over the timed steps.  The same run also
+times, each in its own timed loop: the masked grouped decode GEMM (G=32,
+cap=64, N=4096, K=7168, m_g ~ U{0..32}) against the HBM roofline, the
+contiguous grouped prefill GEMM, the 256^3 GEMM (latency), the E5M2 4096^3
+GEMM and the eight transformer-projection shapes.
+
+Per-launch kernel durations come from HIP events recorded around each launch on
+the stream the kernel runs on (torch's current stream, which the library is
+handed).  The CPU baseline is the oracle, timed on a bounded row sample of the
+dense 4096^3 problem.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only NAME ...] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 matrix peak (no sparsity)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "FP8 TFLOPS (+% MFMA peak) dense 4096³; HBM GB/s masked grouped m≤32"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kernels.hpp", "device_common.hpp", "fp8_gemm.hip"):
+        with open(os.path.join(ROOT, "fp8_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name: str):
+    """HBM bytes per launch recorded from rocprofv3 counters for `name`, or None
+    when no summary exists or the kernels changed since it was taken."""
+    path = os.path.join(PROFILE_DIR, f"{name}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+class Timer:
+    """Times `fn` (which launches work on torch's current stream): warmup
+    calls, then `steps` calls each bracketed by its own pair of events, with a
+    synchronize on both sides of the timed region."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))   # ms
+        mean = sum(per) / len(per)
+        return {"wall_s": wall, "kernel_ms_mean": mean, "kernel_ms_median": per[len(per) // 2],
+                "kernel_ms_min": per[0], "kernel_ms_p90": per[int(0.9 * (len(per) - 1))]}
+
+
+def dev(torch, x):
+    return torch.from_numpy(x).cuda()
+
+
+def bench_dense(torch, f, w, steps, warmup, timer):
+    a, b = dev(torch, w.A), dev(torch, w.B)
+    sa = torch.tensor([w.sa], dtype=torch.float32, device="cuda")
+    sb = torch.tensor([w.sb], dtype=torch.float32, device="cuda")
+    M, N, K = w.shape
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: f.gemm_nt(a, b, sa, sb, out=out, a_dtype=w.a_fmt, b_dtype=w.b_fmt)
+    t = timer.run(fn, steps, warmup)
+    flops = 2.0 * M * N * K
+    t["flops"] = flops
+    t["tflops_wall"] = flops * steps / t["wall_s"] / 1e12
+    t["tflops_kernel"] = flops / (t["kernel_ms_mean"] * 1e-3) / 1e12
+    t["bytes"] = float(M * K + N * K + 2 * M * N)
+    del a, b, out
+    return t
+
+
+def bench_masked(torch, f, w, steps, warmup, timer):
+    import numpy as np
+
+    G, cap, K = w.A.shape
+    N = w.B.shape[1]
+    a, b = dev(torch, w.A), dev(torch, w.B)
+    sa = torch.tensor([w.sa], dtype=torch.float32, device="cuda")
+    sb, mm = dev(torch, w.sb), dev(torch, w.masked_m)
+    out = torch.empty((G, cap, N), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: f.grouped_gemm_masked(a, b, sa, sb, mm, out=out, expected_m=32, a_dtype=w.a_fmt, b_dtype=w.b_fmt)
+    t = timer.run(fn, steps, warmup)
+    m = np.clip(w.masked_m.astype(np.int64), 0, cap)
+    active = int((m > 0).sum())
+    # algorithmic bytes: weights of non-empty experts, valid activation rows,
+    # valid output rows (BF16), per-expert scales and the counts
+    nbytes = active * N * K + int(m.sum()) * K + 2 * int(m.sum()) * N + 4 * G + 4 * (G + 1)
+    flops = 2.0 * int(m.sum()) * N * K
+    t.update({"bytes": float(nbytes), "flops": flops, "active_experts": active, "valid_rows": int(m.sum()),
+              "gbs_wall": nbytes * steps / t["wall_s"] / 1e9,
+              "gbs_kernel": nbytes / (t["kernel_ms_mean"] * 1e-3) / 1e9,
+              "tflops_kernel": flops / (t["kernel_ms_mean"] * 1e-3) / 1e12})
+    del a, b, out
+    return t
+
+
+def bench_contig(torch, f, w, steps, warmup, timer):
+    M_total, K = w.A.shape
+    G, N, _ = w.B.shape
+    a, b = dev(torch, w.A), dev(torch, w.B)
+    sa = torch.tensor([w.sa], dtype=torch.float32, device="cuda")
+    sb, gi = dev(torch, w.sb), dev(torch, w.grp_idx)
+    out = torch.empty((M_total, N), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: f.grouped_gemm_contig(a, b, sa, sb, gi, out=out, a_dtype=w.a_fmt, b_dtype=w.b_fmt)
+    t = timer.run(fn, steps, warmup)
+    valid = int((w.grp_idx >= 0).sum())
+    flops = 2.0 * valid * N * K
+    t.update({"flops": flops, "rows_total": M_total, "rows_valid": valid,
+              "tflops_kernel": flops / (t["kernel_ms_mean"] * 1e-3) / 1e12,
+              "tflops_wall": flops * steps / t["wall_s"] / 1e12,
+              "tflops_kernel_incl_padding": 2.0 * M_total * N * K / (t["kernel_ms_mean"] * 1e-3) / 1e12})
+    del a, b, out
+    return t
+
+
+def cpu_baseline(w, target_s=15.0):
+    """The oracle on rows 0..R-1 of the dense problem (all columns, full K),
+    R chosen so the run takes about target_s seconds."""
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or oracle.default_threads()
+    threads = max(1, min(threads, oracle.default_threads(), 16))
+    M, N, K = w.shape
+    r0 = 8
+    t0 = time.perf_counter()
+    oracle.gemm_nt(w.A[:r0], w.B, w.a_fmt, w.b_fmt, w.sa, w.sb, threads=threads)
+    probe = time.perf_counter() - t0
+    rows = int(min(M, max(threads, r0 * target_s / max(probe, 1e-3))))
+    rows = max(threads, (rows // threads) * threads)
+    t0 = time.perf_counter()
+    oracle.gemm_nt(w.A[:rows], w.B, w.a_fmt, w.b_fmt, w.sa, w.sb, threads=threads)
+    el = time.perf_counter() - t0
+    flops = 2.0 * rows * N * K
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} E4M3 problem (all {N} columns, full K), "
+                      f"{el:.1f} s on {threads} host threads",
+            "seconds": el}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", nargs="*", default=None,
+                    help="subset of: dense masked contig small e5m2 proj (default: all)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the FP8 GEMM path has no multi-GPU component)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fp8_gemm_amd as f
+    import workloads
+
+    f.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    timer = Timer(torch)
+    want = set(args.only) if args.only else {"dense", "masked", "contig", "small", "e5m2", "proj"}
+    steps, warmup = args.steps, args.warmup
+    extra = {}
+
+    log("generating dense 4096^3 E4M3 inputs")
+    wd = workloads.dense_square(workloads.E4M3)
+    dense = None
+    if "dense" in want:
+        log("timing dense 4096^3 E4M3")
+        dense = bench_dense(torch, f, wd, steps, warmup, timer)
+        log(f"  {dense['tflops_kernel']:.1f} TFLOP/s per launch, {dense['tflops_wall']:.1f} whole-job")
+    if "e5m2" in want:
+        log("timing dense 4096^3 E5M2")
+        w5 = workloads.dense_square(workloads.E5M2)
+        r = bench_dense(torch, f, w5, steps, warmup, timer)
+        extra["dense_4096_e5m2"] = {"tflops_kernel": r["tflops_kernel"], "tflops_wall": r["tflops_wall"],
+                                    "kernel_ms_mean": r["kernel_ms_mean"],
+                                    "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS}
+        del w5
+    if "small" in want:
+        log("timing dense 256^3")
+        ws = workloads.dense_small()
+        r = bench_dense(torch, f, ws, steps, warmup, timer)
+        extra["dense_256"] = {"kernel_us_mean": r["kernel_ms_mean"] * 1e3, "kernel_us_median": r["kernel_ms_median"] * 1e3,
+                              "us_per_call_wall": r["wall_s"] / steps * 1e6, "bound": "launch latency"}
+    if "masked" in want:
+        log("generating masked grouped decode inputs (G=32, cap=64, N=4096, K=7168)")
+        wm = workloads.masked_decode()
+        log("timing masked grouped decode")
+        r = bench_masked(torch, f, wm, steps, warmup, timer)
+        extra["masked_grouped"] = {
+            "workload": "masked grouped FP8 GEMM, G=32, cap=64, N=4096, K=7168, m_g~U{0..32} (seed 4), E4M3, swap-AB",
+            "gbs_kernel": r["gbs_kernel"], "gbs_wall": r["gbs_wall"], "kernel_ms_mean": r["kernel_ms_mean"],
+            "tflops_kernel": r["tflops_kernel"], "active_experts": r["active_experts"], "valid_rows": r["valid_rows"],
+            "roofline": {"bound": "hbm", "achieved": r["gbs_kernel"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": r["gbs_kernel"] / PEAK_HBM_GBS, "traffic": read_traffic("masked_decode"),
+                         "algorithmic_bytes": r["bytes"]}}
+        log(f"  {r['gbs_kernel']:.0f} GB/s ({r['gbs_kernel'] / PEAK_HBM_GBS:.1%} of HBM peak)")
+        del wm
+    if "contig" in want:
+        log("generating contiguous grouped prefill inputs (65536 rows over 32 experts, N=4096, K=7168)")
+        wc = workloads.contig_prefill()
+        log("timing contiguous grouped prefill")
+        r = bench_contig(torch, f, wc, max(5, steps // 5), max(2, warmup // 5), timer)
+        extra["contig_grouped"] = {
+            "workload": "contiguous grouped FP8 GEMM, 8192 tokens x top-8 over 32 experts, N=4096, K=7168 (seed 5)",
+            "tflops_kernel": r["tflops_kernel"], "tflops_wall": r["tflops_wall"],
+            "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS, "kernel_ms_mean": r["kernel_ms_mean"],
+            "rows_total": r["rows_total"], "rows_valid": r["rows_valid"],
+            "tflops_kernel_incl_padding": r["tflops_kernel_incl_padding"]}
+        log(f"  {r['tflops_kernel']:.1f} TFLOP/s")
+        del wc
+    if "proj" in want:
+        out = []
+        for i in range(len(workloads.PROJECTION_SHAPES)):
+            wp = workloads.projection(i)
+            r = bench_dense(torch, f, wp, max(5, steps // 2), max(2, warmup // 2), timer)
+            M, N, K = wp.shape
+            out.append({"M": M, "N": N, "K": K, "tflops_kernel": r["tflops_kernel"],
+                        "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS, "kernel_ms_mean": r["kernel_ms_mean"],
+                        "variant": f.plan(0, M, N, K).variant})
+            log(f"  projection {M}x{N}x{K}: {r['tflops_kernel']:.1f} TFLOP/s")
+            del wp
+        extra["projections"] = out
+
+    cpu = None
+    if not args.no_cpu and dense is not None:
+        log("timing the CPU oracle on a row sample")
+        cpu = cpu_baseline(wd)
+
+    if dense is None:
+        print(json.dumps({"metric": METRIC, "partial": True, **extra}))
+        return
+    line = {
+        "metric": METRIC,
+        "value": dense["tflops_wall"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": dense["wall_s"] / steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": "dense FP8 GEMM D=A.B^T, M=N=K=4096, E4M3 A and B (K-major), "
+                               "entries N(0,1)*0.5, per-tensor scales U[0.5,2], FP32 accumulate, BF16 out (seed 2)",
+                   "M": 4096, "N": 4096, "K": 4096},
+        "roofline": {"bound": "mfma", "achieved": dense["tflops_kernel"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": dense["tflops_kernel"] / PEAK_FP8_TFLOPS, "traffic": read_traffic("dense_4096_e4m3"),
+                     "kernel_ms_mean": dense["kernel_ms_mean"], "kernel_ms_median": dense["kernel_ms_median"],
+                     "algorithmic_flops": dense["flops"], "algorithmic_bytes": dense["bytes"]},
+        "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    line.update(extra)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

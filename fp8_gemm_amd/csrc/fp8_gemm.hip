@@ -214,7 +214,8 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t 
     int st = plan_impl(0, M, N, K, 1, 0, &plan);
     if (st != FP8G_OK) return st;
     if (plan.variant == V_NONE) return ok();
-    if (!A || !B || !D || !scale_a || !scale_b) return fail(FP8G_ERR_NULL, "A, B, D, scale_a and scale_b are required");
+    if ((K > 0 && (!A || !B)) || !D || !scale_a || !scale_b)
+        return fail(FP8G_ERR_NULL, "A, B (unless K = 0), D, scale_a and scale_b are required");
     if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return fail(FP8G_ERR_ALIGN, "A, B and D must be 16-byte aligned");
     if (!aligned4(scale_a) || !aligned4(scale_b)) return fail(FP8G_ERR_ALIGN, "scales must be 4-byte aligned");
     if (lda < K || ldb < K) return fail(FP8G_ERR_STRIDE, "lda=%lld / ldb=%lld below K=%d", (long long)lda, (long long)ldb, K);
@@ -254,8 +255,8 @@ int fp8_grouped_gemm_masked(const void *A, int a_dtype, const void *B, int b_dty
     int st = plan_impl(1, cap, N, K, G, expected_m, &plan);
     if (st != FP8G_OK) return st;
     if (plan.variant == V_NONE) return ok();
-    if (!A || !B || !D || !scale_a || !scale_b || !masked_m)
-        return fail(FP8G_ERR_NULL, "A, B, D, scale_a, scale_b and masked_m are required");
+    if ((K > 0 && (!A || !B)) || !D || !scale_a || !scale_b || !masked_m)
+        return fail(FP8G_ERR_NULL, "A, B (unless K = 0), D, scale_a, scale_b and masked_m are required");
     if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return fail(FP8G_ERR_ALIGN, "A, B and D must be 16-byte aligned");
     if (!aligned4(scale_a) || !aligned4(scale_b) || !aligned4(masked_m)) return fail(FP8G_ERR_ALIGN, "scales and masked_m must be 4-byte aligned");
     if (N % 8) return fail(FP8G_ERR_ALIGN, "N=%d: rows of D must stay 16-byte aligned (N %% 8 == 0)", N);
@@ -291,8 +292,8 @@ int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dty
     int st = plan_impl(2, M_total, N, K, G, 0, &plan);
     if (st != FP8G_OK) return st;
     if (plan.variant == V_NONE) return ok();
-    if (!A || !B || !D || !scale_a || !scale_b || !grp_idx)
-        return fail(FP8G_ERR_NULL, "A, B, D, scale_a, scale_b and grp_idx are required");
+    if ((K > 0 && (!A || !B)) || !D || !scale_a || !scale_b || !grp_idx)
+        return fail(FP8G_ERR_NULL, "A, B (unless K = 0), D, scale_a, scale_b and grp_idx are required");
     if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return fail(FP8G_ERR_ALIGN, "A, B and D must be 16-byte aligned");
     if (!aligned4(scale_a) || !aligned4(scale_b) || !aligned4(grp_idx)) return fail(FP8G_ERR_ALIGN, "scales and grp_idx must be 4-byte aligned");
     if (N % 8) return fail(FP8G_ERR_ALIGN, "N=%d: rows of D must stay 16-byte aligned (N %% 8 == 0)", N);

@@ -34,10 +34,12 @@
  *     (an fp8g_status) means nothing was enqueued; fp8_gemm_strerror() gives the
  *     reason, including a per-thread detail string for the last failure.
  *   - Zero-sized problems (M, N, G, cap or M_total = 0) return FP8G_OK and
- *     enqueue nothing.  K = 0 writes zeros (the empty sum).
+ *     enqueue nothing.  K = 0 writes zeros (the empty sum); A and B may then be
+ *     NULL, as nothing is read from them.
  *   - Limits: K % 16 == 0; A, B, D pointers 16-byte aligned; row strides in
  *     bytes (A, B) multiples of 16 and at most 2^23 - 16; ldd a multiple of 8
- *     elements; M, N, K, G, cap, M_total below 2^31.
+ *     elements (the grouped forms use ldd = N, so N % 8 == 0 there); M, N, K,
+ *     G, cap, M_total below 2^31.
  *   - Values that live on the device (masked_m, grp_idx) cannot be checked
  *     without a synchronisation: masked_m[g] is clamped to [0, cap], and any
  *     grp_idx entry outside [0, G) marks a padding row.

@@ -1,14 +1,27 @@
 """Element-wise comparison of the GPU output with the oracle.
 
-The acceptance bound for every valid element d (BF16 from the GPU) against the
-oracle's FP64 value r (scaled, before BF16 rounding) and S = sum_k |a_ik b_jk|:
+Stated bound, for every valid element d (BF16 from the GPU) against the oracle's
+FP64 value r (scaled, before BF16 rounding) and S = sum_k |a_ik b_jk|:
 
-    |d - r| <= 2^-8 |r| + 1e-5 |sa * sb| S
+    |d - r| <= 2^-8 |r| + 1e-5 |sa * sb| S                                  (1)
 
-with NaN matching NaN and +-inf matching the same-signed infinity.  The
-2^-8 |r| term covers one BF16 rounding (half an ulp is at most 2^-8 |r|); the
-second term covers FP32 accumulation of K products in blocks of 64/128 plus
-the FP32 scale multiply, which is far below 1e-5 S for K <= 14336.
+with NaN matching NaN and +-inf matching the same-signed infinity.  The 2^-8 |r|
+term covers one BF16 rounding; the 1e-5 S term presumes products summed with at
+least FP32 precision.
+
+The gfx950 matrix cores do not sum FP8 products that way (measured by
+tests/test_gpu_mfma_numerics.py): within each aligned group of 8 consecutive K
+indices, every product is truncated toward zero to a multiple of 2^(E - 13),
+where E is the exponent of the group's largest product; group sums are then
+combined in FP32.  Per group the truncation error is below 8 * 2^(E - 13), and
+with ea / eb = floor(log2) of the group's largest |a| / |b|, E <= ea + eb + 1, so
+
+    H_ij = |sa sb| * 2^-9 * sum_g 2^(ea_ig) 2^(eb_jg)                       (2)
+
+bounds it; F_ij = |sa sb| * (K / 8) * 2^-24 * S bounds FP32 rounding when every
+group sum is added separately.  Every element must satisfy (1) + H + F; the
+number of elements that need more than (1) is reported, and the seeded workload
+configurations must satisfy (1) itself on every checked element.
 """
 from __future__ import annotations
 
@@ -26,8 +39,52 @@ def gpu_bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def violations(d_bits, r, s, scale_abs):
-    """Boolean mask of elements outside the bound (shapes broadcast)."""
+def _fp8_values(codes: np.ndarray, fmt: int) -> np.ndarray:
+    dt = torch.float8_e4m3fn if fmt == 0 else torch.float8_e5m2
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(dt).double().numpy()
+
+
+def group_exponent_weights(codes: np.ndarray, fmt: int) -> np.ndarray:
+    """[rows, ceil(K/8)]: 2^floor(log2(max |x|)) over each aligned group of 8
+    K indices (0 for an all-zero group; non-finite values are ignored)."""
+    v = np.abs(_fp8_values(codes, fmt))
+    v[~np.isfinite(v)] = 0.0
+    rows, K = v.shape
+    G = (K + 7) // 8
+    if K % 8:
+        v = np.pad(v, ((0, 0), (0, G * 8 - K)))
+    mx = v.reshape(rows, G, 8).max(axis=2)
+    out = np.zeros_like(mx)
+    nz = mx > 0
+    out[nz] = np.exp2(np.floor(np.log2(mx[nz])))
+    return out
+
+
+def hw_allowance(A_rows, B_rows, a_fmt, b_fmt, scale_abs, S):
+    """H + F of the module docstring for the outer product of the given rows:
+    returns [len(A_rows), len(B_rows)]."""
+    K = A_rows.shape[1]
+    wa = group_exponent_weights(A_rows, a_fmt)
+    wb = group_exponent_weights(B_rows, b_fmt)
+    H = 2.0 ** -9 * (wa @ wb.T)
+    F = (max(K, 8) / 8.0) * 2.0 ** -24 * np.asarray(S, dtype=np.float64)
+    return np.asarray(scale_abs, dtype=np.float64) * (H + F)
+
+
+def hw_allowance_points(A, B, ii, jj, a_fmt, b_fmt, scale_abs, S):
+    """H + F at sampled points (ii[p], jj[p])."""
+    K = A.shape[1]
+    ui, inv_i = np.unique(ii, return_inverse=True)
+    uj, inv_j = np.unique(jj, return_inverse=True)
+    wa = group_exponent_weights(A[ui], a_fmt)
+    wb = group_exponent_weights(B[uj], b_fmt)
+    H = 2.0 ** -9 * np.einsum("pg,pg->p", wa[inv_i], wb[inv_j])
+    F = (max(K, 8) / 8.0) * 2.0 ** -24 * np.asarray(S, dtype=np.float64)
+    return np.asarray(scale_abs, dtype=np.float64) * (H + F)
+
+
+def violations(d_bits, r, s, scale_abs, extra=0.0):
+    """Boolean mask of elements outside bound (1) plus `extra`."""
     d = bf16_bits_to_f64(d_bits)
     r = np.asarray(r, dtype=np.float64)
     s = np.asarray(s, dtype=np.float64)
@@ -36,28 +93,49 @@ def violations(d_bits, r, s, scale_abs):
     nan_r, nan_d = np.isnan(r), np.isnan(d)
     bad |= nan_r != nan_d
     inf_r, inf_d = np.isinf(r), np.isinf(d)
-    both_inf = inf_r & inf_d
     bad |= (inf_r != inf_d) & ~nan_r & ~nan_d
-    bad |= both_inf & (np.sign(r) != np.sign(d))
+    bad |= inf_r & inf_d & (np.sign(r) != np.sign(d))
     fin = np.isfinite(r) & np.isfinite(d)
     with np.errstate(invalid="ignore", over="ignore"):
-        tol = 2.0 ** -8 * np.abs(r) + 1e-5 * scale_abs * s
+        tol = 2.0 ** -8 * np.abs(r) + 1e-5 * scale_abs * s + extra
         bad |= fin & (np.abs(d - r) > tol)
     return bad
 
 
-def assert_within_bound(d_bits, r, s, scale_abs, ref_bits=None, what=""):
-    bad = violations(d_bits, r, s, scale_abs)
+def _report(bad, d_bits, r, s, what, label):
     n = int(bad.sum())
-    if n:
-        idx = np.argwhere(bad)[:8]
-        d = bf16_bits_to_f64(d_bits)
-        rows = []
-        for ix in idx:
-            t = tuple(ix)
-            rows.append(f"{t}: gpu={d[t]!r} oracle={np.asarray(r)[t]!r} S={np.asarray(s)[t]!r}")
-        raise AssertionError(f"{what}: {n} of {bad.size} elements outside the bound; first: " + "; ".join(rows))
+    idx = np.argwhere(bad)[:6]
+    d = bf16_bits_to_f64(d_bits)
+    rows = []
+    for ix in idx:
+        t = tuple(int(v) for v in ix)
+        rows.append(f"{t}: gpu={d[t]!r} oracle={np.asarray(r)[t]!r} S={np.asarray(s)[t]!r}")
+    return f"{what}: {n} of {bad.size} elements outside {label}; first: " + "; ".join(rows)
+
+
+def check(d_bits, r, s, scale_abs, allowance=None, ref_bits=None, what="", strict=False):
+    """Assert every element is within bound (1) + allowance.  With strict=True
+    (the seeded workload configurations) assert bound (1) alone.  Returns
+    (elements needing the allowance, bit-identical fraction vs ref_bits)."""
+    plain = violations(d_bits, r, s, scale_abs)
+    n_plain = int(plain.sum())
+    if strict and n_plain:
+        raise AssertionError(_report(plain, d_bits, r, s, what, "the stated bound"))
+    if n_plain:
+        if allowance is None:
+            raise AssertionError(_report(plain, d_bits, r, s, what, "the stated bound"))
+        wide = violations(d_bits, r, s, scale_abs, extra=allowance)
+        if wide.any():
+            raise AssertionError(_report(wide, d_bits, r, s, what, "the stated bound plus the matrix-core truncation allowance"))
+    frac = None
     if ref_bits is not None:
         same = np.asarray(d_bits) == np.asarray(ref_bits)
-        return float(same.mean()) if same.size else 1.0
-    return None
+        frac = float(same.mean()) if same.size else 1.0
+    print(f"  {what}: {n_plain} of {np.asarray(plain).size} elements need the truncation allowance"
+          + (f"; bit-identical to the oracle's BF16: {frac:.4f}" if frac is not None else ""), flush=True)
+    return n_plain, frac
+
+
+def assert_within_bound(d_bits, r, s, scale_abs, ref_bits=None, what=""):
+    """Bound (1) alone (used where the inputs make the truncation irrelevant)."""
+    return check(d_bits, r, s, scale_abs, None, ref_bits, what, strict=True)[1]

@@ -32,6 +32,42 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// The same descriptor as four SGPR words, for the direct-to-LDS load below.
+// Word 0/1 hold the 48-bit base (bits 48..63 of a canonical address are zero
+// for device memory, so word 1 carries base bits 32..47 and a zero stride).
+typedef int v4i __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i make_srd(const void *base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base) & 0x0000FFFFFFFFFFFFull;
+    v4i r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = kRsrcWord3;
+    return r;
+}
+
+// Direct HBM -> LDS load of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane l's bytes land at LDS address lds_base + 16 * l, so one instruction
+// fills 1 KB of LDS without passing through VGPRs.  Out-of-range lanes (offset
+// at or above the descriptor's byte count) deposit zeros.  It is asynchronous
+// and counted by vmcnt: callers wait with vmcnt_wait() and a barrier before
+// reading the data.  Written as inline assembly so the compiler does not
+// insert its own conservative vmcnt(0) before every LDS read; the "memory"
+// clobber keeps other memory operations from moving across it.
+__device__ __forceinline__ void dma16(v4i srd, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(srd), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) (N < 64), leaving the other counters unconstrained.
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ v4u load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
@@ -51,6 +87,15 @@ __device__ __forceinline__ uint32_t rows_bytes(int rows, int64_t ld) {
 // Cores", section 4.2: XOR the address by row to spread a column over banks).
 __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
     return (row << 7) + (((chunk ^ (row & 7u) ^ ((row >> 3) & 1u)) & 7u) << 4);
+}
+
+// Swizzle for LDS tiles whose rows are 64 bytes (4 chunks of 16 bytes):
+// logical chunk c of row r is stored at c ^ g(r), g(r) = ((r >> 1) & 3) ^
+// ((r >> 3) & 1).  A 16-byte-per-lane read of one logical chunk down 8 (or 16)
+// consecutive rows then touches 8 (16) distinct 16-byte bank groups, so it is
+// free of bank conflicts with 32 or 64 four-byte banks.
+__device__ __forceinline__ uint32_t swz64_key(uint32_t row) {
+    return ((row >> 1) & 3u) ^ ((row >> 3) & 1u);
 }
 
 __device__ __forceinline__ v8i pack8(v4u lo, v4u hi) {

@@ -37,6 +37,10 @@ constexpr int kSwapWaveRows = 32;                              // weight rows pe
 constexpr int kSwapTileN = 4 * kSwapWaveRows;                  // weight rows per workgroup
 constexpr int kSwapDepth = 4;                                  // K blocks of loads in flight + 1
 constexpr int kContigAlign = 128;                              // row alignment of experts (contiguous form)
+#ifndef TILE128_WM
+#define TILE128_WM 2
+#define TILE128_WN 4
+#endif
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -143,17 +147,29 @@ int launch_status(const char *what) {
 // ---------------------------------------------------------------------------
 // Launch helpers: one instantiation per (operand formats, tile shape, mode).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int MODE>
-int launch_tile(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, int STAGES, int MODE>
+int launch_ring(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     const dim3 block(64 * WM * WN);
-#define FP8G_TILE(FA, FB) \
-    hipLaunchKernelGGL((fp8g::tile_kernel<BM, BN, WM, WN, FA, FB, MODE>), grid, block, 0, s, p)
-    if (fa == 0 && fb == 0) FP8G_TILE(0, 0);
-    else if (fa == 0 && fb == 1) FP8G_TILE(0, 1);
-    else if (fa == 1 && fb == 0) FP8G_TILE(1, 0);
-    else FP8G_TILE(1, 1);
-#undef FP8G_TILE
-    return launch_status("tile kernel");
+#define FP8G_RING(FA, FB) \
+    hipLaunchKernelGGL((fp8g::ring_kernel<BM, BN, WM, WN, FA, FB, MODE, STAGES>), grid, block, 0, s, p)
+    if (fa == 0 && fb == 0) FP8G_RING(0, 0);
+    else if (fa == 0 && fb == 1) FP8G_RING(0, 1);
+    else if (fa == 1 && fb == 0) FP8G_RING(1, 0);
+    else FP8G_RING(1, 1);
+#undef FP8G_RING
+    return launch_status("tiled kernel");
+}
+
+// Tile shapes of the tiled kernel: 256 x 256 with 8 waves (4 along M, 2 along
+// N) and a 4-slot ring (128 KB of LDS); 128 x 256 with 8 waves (2 x 4) and a
+// 4-slot ring (96 KB).
+template <int MODE>
+int launch_tile256(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    return launch_ring<256, 256, 4, 2, 4, MODE>(fa, fb, p, grid, s);
+}
+template <int MODE>
+int launch_tile128(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    return launch_ring<128, 256, TILE128_WM, TILE128_WN, 4, MODE>(fa, fb, p, grid, s);
 }
 
 template <int CB, int MODE>
@@ -242,8 +258,8 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t 
     p.tiles_m = (int)cdiv(M, plan.tile_m);
     p.tiles_n = (int)cdiv(N, plan.tile_n);
     const dim3 grid((unsigned)plan.workgroups);
-    if (plan.variant == V_TILE_256x256) return launch_tile<256, 256, 2, 2, fp8g::MODE_DENSE>(fa, fb, p, grid, s);
-    return launch_tile<128, 256, 2, 2, fp8g::MODE_DENSE>(fa, fb, p, grid, s);
+    if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE>(fa, fb, p, grid, s);
+    return launch_tile128<fp8g::MODE_DENSE>(fa, fb, p, grid, s);
 }
 
 int fp8_grouped_gemm_masked(const void *A, int a_dtype, const void *B, int b_dtype, const float *scale_a,
@@ -280,7 +296,7 @@ int fp8_grouped_gemm_masked(const void *A, int a_dtype, const void *B, int b_dty
     }
     p.tiles_m = (int)cdiv(cap, 128);
     p.tiles_n = (int)cdiv(N, 256);
-    return launch_tile<128, 256, 2, 2, fp8g::MODE_MASKED>(a_dtype, b_dtype, p, dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)G), s);
+    return launch_tile128<fp8g::MODE_MASKED>(a_dtype, b_dtype, p, dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)G), s);
 }
 
 int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dtype, const float *scale_a,
@@ -309,8 +325,8 @@ int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dty
     p.scale_a = scale_a; p.scale_b = scale_b; p.grp_idx = grp_idx;
     p.tiles_m = (int)cdiv(M_total, kContigAlign);
     p.tiles_n = (int)cdiv(N, 256);
-    return launch_tile<128, 256, 2, 2, fp8g::MODE_CONTIG>(a_dtype, b_dtype, p, dim3((unsigned)plan.workgroups),
-                                                          static_cast<hipStream_t>(stream));
+    return launch_tile128<fp8g::MODE_CONTIG>(a_dtype, b_dtype, p, dim3((unsigned)plan.workgroups),
+                                             static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -73,28 +73,38 @@ __device__ __forceinline__ void dense_tile_coords(int wg, int tiles_m, int tiles
 }
 
 // ---------------------------------------------------------------------------
-// LDS-tiled kernel.
-// BM x BN tile (tokens x weights), WM x WN waves, each wave a TM x TN sub-tile
-// of (TM/32) x (TN/32) 32x32 accumulator blocks.  FA / FB: formats of A / B.
+// LDS-tiled kernel with a direct-to-LDS ring.
+// BM x BN tile (tokens x weights) per workgroup of WM x WN waves; each wave
+// owns a TM x TN sub-tile of (TM/32) x (TN/32) 32x32 accumulator blocks.  K
+// advances 64 bytes per step, one v_mfma 32x32x64 per accumulator block per
+// step.  STAGES ring slots of (BM + BN) x 64 bytes: the tile rows of step
+// kt + STAGES - 1 are DMA'd from HBM straight into LDS while step kt is
+// consumed, so STAGES - 1 steps of loads are in flight ("DeepGEMM on Hopper
+// Tensor Cores", sections 3.3 and 4.3: deeper buffering hides load latency).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int FA, int FB, int MODE>
-__global__ __launch_bounds__(64 * WM * WN, 1) void tile_kernel(GemmParams p) {
-    constexpr int THREADS = 64 * WM * WN;
+template <int BM, int BN, int WM, int WN, int FA, int FB, int MODE, int STAGES>
+__global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
+    constexpr int WAVES = WM * WN;
+    constexpr int BK = 64;                         // K bytes per step
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int ROWB = 128;                 // bytes of K per step (one 128-deep K block)
-    constexpr int STAGE = (BM + BN) * ROWB;   // one ring slot: A tile then B tile
-    constexpr int LA = BM * 8 / THREADS;      // 16-byte loads per thread per slot
-    constexpr int LB = BN * 8 / THREADS;
-    constexpr int RSTEP = THREADS / 8;        // rows covered by one load instruction
-    static_assert(FM >= 1 && FN >= 1 && LA >= 1 && LB >= 1, "tile shape");
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
+    constexpr int SLOT = (BM + BN) * BK;           // bytes per ring slot
+    constexpr int CHUNKS = (BM + BN) / 16;         // 1 KB DMA chunks (16 rows x 64 B) per slot
+    constexpr int CPW = CHUNKS / WAVES;            // chunks per wave per slot
+    static_assert(CHUNKS % WAVES == 0 && CPW >= 1, "tile rows must split evenly over the waves");
+    static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "wave tile");
+    static_assert(STAGES >= 2 && CPW * (STAGES - 2) < 64, "ring depth");
+    constexpr int STAGE_OUT = BM * BN * 2;         // BF16 output tile staged for the stores
+    constexpr int SMEM = STAGES * SLOT > STAGE_OUT ? STAGES * SLOT : STAGE_OUT;
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int OCH = BN / 8;                    // 16-byte chunks per staged output row
+    static_assert(OCH == 32 || OCH == 16, "staged row width");
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM;
     const int wn = wave / WM;
 
@@ -115,7 +125,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_kernel(GemmParams p) {
         rows_m = min(p.M - m0, BM);
     } else if (MODE == MODE_MASKED) {
         const int mg = min(max(p.masked_m[g], 0), p.cap);
-        if (m0 >= mg) return;                 // nothing valid in this tile: no load at all
+        if (m0 >= mg) return;                      // nothing valid in this tile: no load at all
         rows_m = min(mg - m0, BM);
         expert = g;
     } else {
@@ -130,8 +140,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_kernel(GemmParams p) {
             const bool ok = (e >= 0) && (e < p.G);
             const unsigned long long ball = __ballot(ok);
             if (ball) {
-                const int first = __builtin_ctzll(ball);
-                expert = __shfl(e, first);
+                expert = __shfl(e, __builtin_ctzll(ball));
                 break;
             }
         }
@@ -144,42 +153,54 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_kernel(GemmParams p) {
     uint16_t *d_base = p.D + (MODE == MODE_MASKED ? (int64_t)g * p.d_gstride : 0);
     const float sc = p.scale_a[0] * p.scale_b[MODE == MODE_DENSE ? 0 : expert];
 
-    // Rows past rows_m / rows_n fall outside the descriptors and load as zero.
-    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(a_base, rows_bytes(rows_m, p.lda));
-    const __amdgpu_buffer_rsrc_t rsB = make_rsrc(b_base, rows_bytes(rows_n, p.ldb));
+    // Rows past rows_m / rows_n fall outside the descriptors: the DMA writes
+    // zeros for them and issues no memory transaction.
+    const v4i srdA = make_srd(a_base, rows_bytes(rows_m, p.lda));
+    const v4i srdB = make_srd(b_base, rows_bytes(rows_n, p.ldb));
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
 
-    // ---- per-thread global-load and LDS-store addresses ----
-    const int ch = tid & 7;                   // 16-byte chunk of a 128-byte row piece
-    const int r0 = tid >> 3;
-    uint32_t a_goff[LA], b_goff[LB];
-    uint32_t a_soff[LA], b_soff[LB];
+    // ---- this wave's DMA chunks ----
+    // Chunk q covers 16 rows x 64 bytes: A rows for q < BM / 16, else B rows.
+    // Lane l deposits LDS bytes [16 l, 16 l + 16) of the chunk, i.e. row
+    // l / 4, stored chunk l % 4; it loads logical chunk (l % 4) ^ g(row) so the
+    // LDS image is swizzled (see swz64_key).
+    uint32_t dma_off[CPW];
+    uint32_t dma_kc[CPW];
+    bool dma_a[CPW];
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
-        const int row = r0 + i * RSTEP;
-        a_goff[i] = (uint32_t)((int64_t)row * p.lda) + ch * 16;
-        a_soff[i] = swz(row, ch);
+    for (int i = 0; i < CPW; ++i) {
+        const int q = wave * CPW + i;
+        const bool isA = q < BM / 16;
+        const int row = (isA ? q : q - BM / 16) * 16 + (lane >> 2);
+        const uint32_t c = ((uint32_t)(lane & 3) ^ swz64_key(row)) & 3u;
+        dma_a[i] = isA;
+        dma_kc[i] = c * 16;
+        dma_off[i] = (uint32_t)((int64_t)row * (isA ? p.lda : p.ldb)) + c * 16;
     }
+    const int nk = (p.K + BK - 1) / BK;
+    auto issue = [&](int kt) {
+        const int slot = kt % STAGES;
+        const uint32_t k0 = (uint32_t)kt * BK;
 #pragma unroll
-    for (int i = 0; i < LB; ++i) {
-        const int row = r0 + i * RSTEP;
-        b_goff[i] = (uint32_t)((int64_t)row * p.ldb) + ch * 16;
-        b_soff[i] = BM * ROWB + swz(row, ch);
-    }
+        for (int i = 0; i < CPW; ++i) {
+            const bool in = (kt < nk) && (int)(k0 + dma_kc[i]) < p.K;
+            dma16(dma_a[i] ? srdA : srdB, in ? dma_off[i] + k0 : kOobOffset,
+                  lds0 + slot * SLOT + (uint32_t)(wave * CPW + i) * 1024u);
+        }
+    };
 
-    // ---- per-lane fragment read addresses (within a slot) ----
-    // Operand layout used for both operands of v_mfma 32x32x64: lane l carries
-    // row (l & 31) and the 32 K bytes [(l >> 5) * 32, +32) of each 64-deep half.
-    // The instruction sums over all 64 K slots, and both operands use the same
-    // K placement, so the dot products are over exactly the K block.
+    // ---- fragment read offsets ----
+    // v_mfma 32x32x64 operands: lane l carries row l & 31 of its 32-row block
+    // and K bytes [(l >> 5) * 32, +32) of the 64-byte step, i.e. logical
+    // chunks 2 (l >> 5) and 2 (l >> 5) + 1.  Both operands use the same K
+    // placement, so each dot product covers exactly the step's K bytes.
     const int lrow = lane & 31;
     const int khalf = lane >> 5;
-    uint32_t frag_off[2][2];                  // [K half][first / second 16 bytes]
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) frag_off[h][j] = swz(lrow, h * 4 + khalf * 2 + j);
-    const uint32_t a_frag_base = (uint32_t)(wm * TM) * ROWB;
-    const uint32_t b_frag_base = BM * ROWB + (uint32_t)(wn * TN) * ROWB;
+    const uint32_t key = swz64_key((uint32_t)lrow);   // blocks start at multiples of 32 rows
+    const uint32_t fo0 = (uint32_t)lrow * BK + (((2u * khalf) ^ key) & 3u) * 16u;
+    const uint32_t fo1 = (uint32_t)lrow * BK + (((2u * khalf + 1u) ^ key) & 3u) * 16u;
+    const uint32_t a_frag = (uint32_t)(wm * TM) * BK;
+    const uint32_t b_frag = (uint32_t)BM * BK + (uint32_t)(wn * TN) * BK;
 
     v16f acc[FN][FM];
 #pragma unroll
@@ -187,100 +208,77 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = (v16f){0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
-    const int nk = (p.K + ROWB - 1) / ROWB;
-    v4u ra[LA], rb[LB];
-
-    auto gload = [&](int kt) {
-        const uint32_t k0 = (uint32_t)kt * ROWB;
-        // K tail: a chunk is entirely inside or outside K (K % 16 == 0).
-        const bool kin = (kt < nk) && (int)(k0 + ch * 16) < p.K;
+    // ---- main loop ----
 #pragma unroll
-        for (int i = 0; i < LA; ++i) ra[i] = load16(rsA, kin ? a_goff[i] + k0 : kOobOffset);
-#pragma unroll
-        for (int i = 0; i < LB; ++i) rb[i] = load16(rsB, kin ? b_goff[i] + k0 : kOobOffset);
-    };
-    auto swrite = [&](uint8_t *slot) {
-#pragma unroll
-        for (int i = 0; i < LA; ++i) *reinterpret_cast<v4u *>(slot + a_soff[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < LB; ++i) *reinterpret_cast<v4u *>(slot + b_soff[i]) = rb[i];
-    };
-    // Fragments of one 64-deep K half: FN row-operand blocks (B rows) and FM
-    // column-operand blocks (A rows), 32 bytes per lane each.
-    auto read_frags = [&](v8i (&bf)[FN], v8i (&af)[FM], const uint8_t *slot, int h) {
+    for (int s = 0; s < STAGES - 1; ++s) issue(s);
+    for (int kt = 0; kt < nk; ++kt) {
+        vmcnt_wait<CPW * (STAGES - 2)>();          // this wave's loads of step kt have landed
+        __syncthreads();                           // everyone's have; everyone is done with step kt-1
+        issue(kt + STAGES - 1);                    // refills the slot step kt-1 used
+        const uint8_t *slot = smem + (kt % STAGES) * SLOT;
+        v8i bf[FN], af[FM];
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
-            const uint8_t *rowp = slot + b_frag_base + f * 32 * ROWB;
-            bf[f] = pack8(*reinterpret_cast<const v4u *>(rowp + frag_off[h][0]),
-                          *reinterpret_cast<const v4u *>(rowp + frag_off[h][1]));
+            const uint8_t *r = slot + b_frag + f * 32 * BK;
+            bf[f] = pack8(*reinterpret_cast<const v4u *>(r + fo0), *reinterpret_cast<const v4u *>(r + fo1));
         }
 #pragma unroll
         for (int f = 0; f < FM; ++f) {
-            const uint8_t *rowp = slot + a_frag_base + f * 32 * ROWB;
-            af[f] = pack8(*reinterpret_cast<const v4u *>(rowp + frag_off[h][0]),
-                          *reinterpret_cast<const v4u *>(rowp + frag_off[h][1]));
+            const uint8_t *r = slot + a_frag + f * 32 * BK;
+            af[f] = pack8(*reinterpret_cast<const v4u *>(r + fo0), *reinterpret_cast<const v4u *>(r + fo1));
         }
-    };
-    auto mma = [&](const v8i (&bf)[FN], const v8i (&af)[FM]) {
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
             for (int j = 0; j < FM; ++j) acc[i][j] = mfma32x32x64<FB, FA>(bf[i], af[j], acc[i][j]);
-    };
-
-    // ---- main loop ----
-    // Two LDS slots.  Block kt+1 travels HBM -> registers while the matrix
-    // cores work on block kt, and is stored to the free slot half-way through
-    // block kt; the single barrier per block follows that store.  Fragment
-    // reads run one K half ahead of the matrix cores, so LDS latency hides
-    // behind 16 MFMAs.  The scheduling barriers keep this order (left alone,
-    // the compiler hoists the LDS stores, which then wait out the global-load
-    // latency).  Past the last block the prefetch offsets are out of range:
-    // those loads return zeros without touching memory and are never used.
-    v8i f0b[FN], f0a[FM], f1b[FN], f1a[FM];
-    if (nk > 0) {
-        gload(0);
-        swrite(smem);
-        __syncthreads();
-        gload(1);
-        read_frags(f0b, f0a, smem, 0);
     }
-    for (int kt = 0; kt < nk; ++kt) {
-        const uint8_t *cur = smem + (kt & 1) * STAGE;
-        uint8_t *nxt = smem + ((kt + 1) & 1) * STAGE;
-        read_frags(f1b, f1a, cur, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(f0b, f0a);
-        __builtin_amdgcn_sched_barrier(0);
-        swrite(nxt);                          // block kt+1, free slot
-        __builtin_amdgcn_sched_barrier(0);
-        gload(kt + 2);
-        __syncthreads();                      // slot kt+1 complete; reads of slot kt done
-        read_frags(f0b, f0a, nxt, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(f1b, f1a);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    vmcnt_wait<0>();                               // drain the (out-of-range) prefetches
+    __syncthreads();                               // every wave's DMA has landed; the ring is free
 
-    // ---- epilogue: scale, round to BF16, store the valid rows/columns ----
+    // ---- epilogue: scale, round to BF16, stage the tile in LDS, then write
+    // whole row segments with 16-byte stores.
     // Accumulator register r of a 32x32 block holds row (of the first operand)
-    // 8 * (r / 4) + 4 * (lane / 32) + r % 4 and column lane % 32.
+    // 8 * (r / 4) + 4 * (lane / 32) + r % 4 and column lane % 32, so lane l
+    // holds four consecutive output columns n of output row m: an 8-byte
+    // write.  Staged row m keeps its 16-byte chunks but stores chunk c at
+    // c ^ (m % OCH), so the 32 rows one write instruction touches land on
+    // different chunks, and a row read back is a permutation of one row.
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-        const int m = m0 + wm * TM + j * 32 + lrow;
-        bool row_ok = (m - m0) < rows_m;
-        if (MODE == MODE_CONTIG && row_ok) row_ok = (p.grp_idx[m] == expert);
-        if (!row_ok) continue;
-        uint16_t *drow = d_base + (int64_t)m * p.ldd;
+        const uint32_t m = (uint32_t)(wm * TM + j * 32 + lrow);
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const int n = n0 + wn * TN + i * 32 + b * 8 + khalf * 4;
+                const uint32_t n = (uint32_t)(wn * TN + i * 32 + b * 8 + khalf * 4);
                 const v16f &c = acc[i][j];
                 const v2u v = pack_bf16x4(c[4 * b] * sc, c[4 * b + 1] * sc, c[4 * b + 2] * sc, c[4 * b + 3] * sc);
-                store_bf16x4(drow, n, p.N - n, v);
+                const uint32_t chunk = (n >> 3) ^ (m % OCH);
+                *reinterpret_cast<v2u *>(smem + m * (BN * 2) + chunk * 16 + (n & 4) * 2) = v;
             }
+        }
+    }
+    __syncthreads();
+    constexpr int OUT_CHUNKS = BM * OCH;
+    static_assert(OUT_CHUNKS % THREADS == 0, "staged tile splits evenly over the threads");
+#pragma unroll 4
+    for (int q = tid; q < OUT_CHUNKS; q += THREADS) {
+        const int r = q / OCH;
+        const int c = q % OCH;
+        if (r >= rows_m) continue;
+        const int m = m0 + r;
+        if (MODE == MODE_CONTIG && p.grp_idx[m] != expert) continue;
+        const int n = n0 + c * 8;
+        const v4u v = *reinterpret_cast<const v4u *>(smem + r * (BN * 2) + ((c ^ (r % OCH)) * 16));
+        uint16_t *dst = d_base + (int64_t)m * p.ldd + n;
+        const int nvalid = p.N - n;
+        if (nvalid >= 8) {
+            *reinterpret_cast<v4u *>(dst) = v;
+        } else if (nvalid > 0) {
+            const uint16_t e[8] = {(uint16_t)(v[0] & 0xFFFFu), (uint16_t)(v[0] >> 16), (uint16_t)(v[1] & 0xFFFFu),
+                                   (uint16_t)(v[1] >> 16), (uint16_t)(v[2] & 0xFFFFu), (uint16_t)(v[2] >> 16),
+                                   (uint16_t)(v[3] & 0xFFFFu), (uint16_t)(v[3] >> 16)};
+            for (int t = 0; t < nvalid; ++t) dst[t] = e[t];
         }
     }
 }

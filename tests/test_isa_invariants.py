@@ -1,0 +1,62 @@
+"""Properties of the compiled gfx950 code, checked on the AMD assembly of this
+repository's own kernels (CPU only: hipcc cross-compiles).
+
+* M0 is written only by the direct-to-LDS load helper, each write immediately
+  followed by its `buffer_load_dwordx4 ... lds`, and read by nothing else: the
+  helper's inline assembly sets M0 itself, so no compiler-generated code may
+  rely on M0 across it.
+* No kernel spills to scratch memory.
+* No packed FP32 VALU operations and no scalar-memory writes appear anywhere.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "fp8_gemm_amd", "csrc", "fp8_gemm.hip")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not available")
+    from fp8_gemm_amd import _build
+    out = tmp_path_factory.mktemp("isa") / "dev.s"
+    cmd = [_build.hipcc()] + [f for f in _build.HIPCC_FLAGS if f not in ("-fPIC", "-shared")] + \
+          ["-S", "--cuda-device-only", SRC, "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def _code_lines(text):
+    for line in text.splitlines():
+        s = line.split(";")[0].strip()
+        if s and not s.startswith(".") and not s.endswith(":"):
+            yield s
+
+
+def test_m0_only_feeds_lds_dma(asm):
+    lines = list(_code_lines(asm))
+    writes = 0
+    for i, s in enumerate(lines):
+        if re.search(r"\bm0\b", s):
+            assert s.startswith("s_mov_b32 m0,"), f"unexpected use of M0: {s}"
+            assert i + 1 < len(lines) and lines[i + 1].startswith("buffer_load_dwordx4") \
+                and lines[i + 1].endswith(" lds"), f"M0 write not followed by an LDS DMA load: {s}"
+            writes += 1
+    assert writes > 0
+
+
+def test_no_scratch(asm):
+    sizes = [int(v) for v in re.findall(r"\.private_segment_fixed_size:\s*(\d+)", asm)]
+    assert sizes and max(sizes) == 0
+
+
+def test_no_packed_fp32_and_no_scalar_writes(asm):
+    for s in _code_lines(asm):
+        op = s.split()[0]
+        assert not re.match(r"v_pk_(add|mul|fma)_f32", op), s
+        assert not re.match(r"s_(buffer_)?(store|atomic)|s_dcache_(wb|discard)", op), s

@@ -41,6 +41,18 @@ constexpr int kContigAlign = 128;                              // row alignment 
 #define TILE128_WM 2
 #define TILE128_WN 4
 #endif
+#ifndef T256_WM
+#define T256_WM 4
+#define T256_WN 2
+#endif
+#ifndef T256_ST
+#define T256_ST 2
+#define T256_BK 128
+#endif
+#ifndef T128_ST
+#define T128_ST 3
+#define T128_BK 128
+#endif
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -147,11 +159,11 @@ int launch_status(const char *what) {
 // ---------------------------------------------------------------------------
 // Launch helpers: one instantiation per (operand formats, tile shape, mode).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int STAGES, int MODE>
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, int MODE>
 int launch_ring(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     const dim3 block(64 * WM * WN);
 #define FP8G_RING(FA, FB) \
-    hipLaunchKernelGGL((fp8g::ring_kernel<BM, BN, WM, WN, FA, FB, MODE, STAGES>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((fp8g::ring_kernel<BM, BN, WM, WN, FA, FB, MODE, STAGES, BK>), grid, block, 0, s, p)
     if (fa == 0 && fb == 0) FP8G_RING(0, 0);
     else if (fa == 0 && fb == 1) FP8G_RING(0, 1);
     else if (fa == 1 && fb == 0) FP8G_RING(1, 0);
@@ -165,11 +177,11 @@ int launch_ring(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
 // 4-slot ring (96 KB).
 template <int MODE>
 int launch_tile256(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    return launch_ring<256, 256, 4, 2, 4, MODE>(fa, fb, p, grid, s);
+    return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE>(fa, fb, p, grid, s);
 }
 template <int MODE>
 int launch_tile128(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    return launch_ring<128, 256, TILE128_WM, TILE128_WN, 4, MODE>(fa, fb, p, grid, s);
+    return launch_ring<128, 256, TILE128_WM, TILE128_WN, T128_ST, T128_BK, MODE>(fa, fb, p, grid, s);
 }
 
 template <int CB, int MODE>

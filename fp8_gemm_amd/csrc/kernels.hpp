@@ -76,21 +76,31 @@ __device__ __forceinline__ void dense_tile_coords(int wg, int tiles_m, int tiles
 // LDS-tiled kernel with a direct-to-LDS ring.
 // BM x BN tile (tokens x weights) per workgroup of WM x WN waves; each wave
 // owns a TM x TN sub-tile of (TM/32) x (TN/32) 32x32 accumulator blocks.  K
-// advances 64 bytes per step, one v_mfma 32x32x64 per accumulator block per
-// step.  STAGES ring slots of (BM + BN) x 64 bytes: the tile rows of step
+// advances BK bytes per ring slot (BK/64 v_mfma 32x32x64 per accumulator
+// block).  STAGES slots of (BM + BN) x BK bytes: the tile rows of step
 // kt + STAGES - 1 are DMA'd from HBM straight into LDS while step kt is
 // consumed, so STAGES - 1 steps of loads are in flight ("DeepGEMM on Hopper
-// Tensor Cores", sections 3.3 and 4.3: deeper buffering hides load latency).
+// Tensor Cores", sections 3.3 and 4.3).  BK = 128 makes every DMA instruction
+// read whole 128-byte row segments (8 rows x 128 B): with 64-byte segments
+// each L2 line is fetched twice and streaming runs at two thirds of the rate.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int FA, int FB, int MODE, int STAGES>
+template <int BK>
+__device__ __forceinline__ uint32_t ring_key(uint32_t row) {
+    // XOR key of the stored chunk index (see swz / swz64_key).
+    return BK == 128 ? ((row & 7u) ^ ((row >> 3) & 1u)) : swz64_key(row);
+}
+
+template <int BM, int BN, int WM, int WN, int FA, int FB, int MODE, int STAGES, int BK>
 __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     constexpr int WAVES = WM * WN;
-    constexpr int BK = 64;                         // K bytes per step
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int KCH = BK / 16;                   // 16-byte chunks per tile row per slot
+    constexpr int DROWS = 1024 / BK;               // tile rows covered by one 1 KB DMA instruction
     constexpr int SLOT = (BM + BN) * BK;           // bytes per ring slot
-    constexpr int CHUNKS = (BM + BN) / 16;         // 1 KB DMA chunks (16 rows x 64 B) per slot
-    constexpr int CPW = CHUNKS / WAVES;            // chunks per wave per slot
+    constexpr int CHUNKS = SLOT / 1024;            // DMA instructions per slot
+    constexpr int CPW = CHUNKS / WAVES;            // DMA instructions per wave per slot
+    static_assert(BK == 64 || BK == 128, "K step");
     static_assert(CHUNKS % WAVES == 0 && CPW >= 1, "tile rows must split evenly over the waves");
     static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "wave tile");
     static_assert(STAGES >= 2 && CPW * (STAGES - 2) < 64, "ring depth");
@@ -160,19 +170,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
 
     // ---- this wave's DMA chunks ----
-    // Chunk q covers 16 rows x 64 bytes: A rows for q < BM / 16, else B rows.
-    // Lane l deposits LDS bytes [16 l, 16 l + 16) of the chunk, i.e. row
-    // l / 4, stored chunk l % 4; it loads logical chunk (l % 4) ^ g(row) so the
-    // LDS image is swizzled (see swz64_key).
+    // Instruction q covers DROWS rows x BK bytes: A rows for q < BM / DROWS,
+    // else B rows.  Lane l deposits LDS bytes [16 l, 16 l + 16) of it, i.e.
+    // row l / KCH, stored chunk l % KCH; it loads logical chunk
+    // (l % KCH) ^ key(row), so the LDS image is swizzled (see ring_key).
     uint32_t dma_off[CPW];
     uint32_t dma_kc[CPW];
     bool dma_a[CPW];
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
         const int q = wave * CPW + i;
-        const bool isA = q < BM / 16;
-        const int row = (isA ? q : q - BM / 16) * 16 + (lane >> 2);
-        const uint32_t c = ((uint32_t)(lane & 3) ^ swz64_key(row)) & 3u;
+        const bool isA = q < BM / DROWS;
+        const int row = (isA ? q : q - BM / DROWS) * DROWS + lane / KCH;
+        const uint32_t c = ((uint32_t)(lane % KCH) ^ ring_key<BK>(row)) & (KCH - 1);
         dma_a[i] = isA;
         dma_kc[i] = c * 16;
         dma_off[i] = (uint32_t)((int64_t)row * (isA ? p.lda : p.ldb)) + c * 16;
@@ -191,14 +201,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 
     // ---- fragment read offsets ----
     // v_mfma 32x32x64 operands: lane l carries row l & 31 of its 32-row block
-    // and K bytes [(l >> 5) * 32, +32) of the 64-byte step, i.e. logical
-    // chunks 2 (l >> 5) and 2 (l >> 5) + 1.  Both operands use the same K
-    // placement, so each dot product covers exactly the step's K bytes.
+    // and K bytes [(l >> 5) * 32, +32) of each 64-byte K half h of the slot,
+    // i.e. logical chunks 4 h + 2 (l >> 5) and 4 h + 2 (l >> 5) + 1.  Both
+    // operands use the same K placement, so each dot product covers exactly
+    // that K half.
+    constexpr int KH = BK / 64;                    // MFMA K steps per slot
     const int lrow = lane & 31;
     const int khalf = lane >> 5;
-    const uint32_t key = swz64_key((uint32_t)lrow);   // blocks start at multiples of 32 rows
-    const uint32_t fo0 = (uint32_t)lrow * BK + (((2u * khalf) ^ key) & 3u) * 16u;
-    const uint32_t fo1 = (uint32_t)lrow * BK + (((2u * khalf + 1u) ^ key) & 3u) * 16u;
+    const uint32_t key = ring_key<BK>((uint32_t)lrow);   // blocks start at multiples of 32 rows
+    uint32_t fo[KH][2];
+#pragma unroll
+    for (int h = 0; h < KH; ++h)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            fo[h][j] = (uint32_t)lrow * BK + (((uint32_t)(4 * h + 2 * khalf + j) ^ key) & (KCH - 1)) * 16u;
     const uint32_t a_frag = (uint32_t)(wm * TM) * BK;
     const uint32_t b_frag = (uint32_t)BM * BK + (uint32_t)(wn * TN) * BK;
 
@@ -208,29 +224,84 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = (v16f){0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
-    // ---- main loop ----
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue(s);
-    for (int kt = 0; kt < nk; ++kt) {
-        vmcnt_wait<CPW * (STAGES - 2)>();          // this wave's loads of step kt have landed
-        __syncthreads();                           // everyone's have; everyone is done with step kt-1
-        issue(kt + STAGES - 1);                    // refills the slot step kt-1 used
-        const uint8_t *slot = smem + (kt % STAGES) * SLOT;
-        v8i bf[FN], af[FM];
+    // Fragments of one 64-deep K half: FN row-operand blocks (B rows) and FM
+    // column-operand blocks (A rows), 32 bytes per lane each.
+    auto read_frags = [&](v8i (&bf)[FN], v8i (&af)[FM], const uint8_t *slot, int h) {
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
             const uint8_t *r = slot + b_frag + f * 32 * BK;
-            bf[f] = pack8(*reinterpret_cast<const v4u *>(r + fo0), *reinterpret_cast<const v4u *>(r + fo1));
+            bf[f] = pack8(*reinterpret_cast<const v4u *>(r + fo[h][0]), *reinterpret_cast<const v4u *>(r + fo[h][1]));
         }
 #pragma unroll
         for (int f = 0; f < FM; ++f) {
             const uint8_t *r = slot + a_frag + f * 32 * BK;
-            af[f] = pack8(*reinterpret_cast<const v4u *>(r + fo0), *reinterpret_cast<const v4u *>(r + fo1));
+            af[f] = pack8(*reinterpret_cast<const v4u *>(r + fo[h][0]), *reinterpret_cast<const v4u *>(r + fo[h][1]));
         }
+    };
+    // One fragment (two 16-byte LDS reads) of K half h: index q < FN is row
+    // operand block q, otherwise column operand block q - FN.
+    auto read_frag = [&](v8i (&bf)[FN], v8i (&af)[FM], const uint8_t *slot, int h, int q) {
+        const uint8_t *r = q < FN ? slot + b_frag + q * 32 * BK : slot + a_frag + (q - FN) * 32 * BK;
+        const v8i v = pack8(*reinterpret_cast<const v4u *>(r + fo[h][0]), *reinterpret_cast<const v4u *>(r + fo[h][1]));
+        if (q < FN) bf[q] = v;
+        else af[q - FN] = v;
+    };
+    auto issue_one = [&](int kt, int q) {
+        const uint32_t k0 = (uint32_t)kt * BK;
+        const bool in = (kt < nk) && (int)(k0 + dma_kc[q]) < p.K;
+        dma16(dma_a[q] ? srdA : srdB, in ? dma_off[q] + k0 : kOobOffset,
+              lds0 + (kt % STAGES) * SLOT + (uint32_t)(wave * CPW + q) * 1024u);
+    };
+    // One K half of MFMAs with other work spread between them: the fragments
+    // of the next half (read_slot / read_h) and, when refill_kt >= 0, the DMA
+    // refill of a ring slot.  Issued in bursts, LDS reads and DMA instructions
+    // stall the wave's in-order issue while their queues drain, and the MFMAs
+    // queued behind them wait with them; spread out, they issue in the
+    // shadow of the MFMAs.
+    constexpr int NMF = FN * FM;                   // MFMAs per K half
+    constexpr int NFR = FN + FM;                   // fragments per K half
+    auto mma_mixed = [&](const v8i (&bf)[FN], const v8i (&af)[FM], v8i (&nb)[FN], v8i (&na)[FM],
+                         const uint8_t *read_slot, int read_h, int refill_kt) {
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
+        for (int t = 0; t < NMF; ++t) {
+            acc[t / FM][t % FM] = mfma32x32x64<FB, FA>(bf[t / FM], af[t % FM], acc[t / FM][t % FM]);
+            // fragments of the next half: NFR reads spread over the NMF MFMAs
 #pragma unroll
-            for (int j = 0; j < FM; ++j) acc[i][j] = mfma32x32x64<FB, FA>(bf[i], af[j], acc[i][j]);
+            for (int q = (t * NFR) / NMF; q < ((t + 1) * NFR) / NMF; ++q) read_frag(nb, na, read_slot, read_h, q);
+            if (refill_kt >= 0) {
+#pragma unroll
+                for (int q = (t * CPW) / NMF; q < ((t + 1) * CPW) / NMF; ++q) issue_one(refill_kt, q);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- main loop ----
+    // Slot kt % STAGES holds K step kt.  Fragment reads run one K half ahead
+    // of the matrix cores (f0: first half, f1: second half), and the single
+    // barrier per step sits between the halves: after it, step kt + 1 is in
+    // LDS for everyone and nobody reads step kt's slot any more, so that slot
+    // is refilled with step kt + STAGES while the second half computes.  The
+    // scheduling barriers keep this order (left alone, the compiler reads
+    // fragments just in time and exposes LDS latency before every few MFMAs).
+    // Past the last step the DMA offsets are out of range: those loads deposit
+    // zeros without touching memory and their slots are never read.
+    static_assert(KH == 2, "the pipelined loop consumes two K halves per slot");
+    v8i f0b[FN], f0a[FM], f1b[FN], f1a[FM];
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) issue(s);
+    vmcnt_wait<CPW * (STAGES - 1)>();              // step 0 has landed (this wave's part)
+    __syncthreads();
+    read_frags(f0b, f0a, smem, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const uint8_t *cur = smem + (kt % STAGES) * SLOT;
+        const uint8_t *nxt = smem + ((kt + 1) % STAGES) * SLOT;
+        __builtin_amdgcn_sched_barrier(0);
+        mma_mixed(f0b, f0a, f1b, f1a, cur, 1, -1);              // first half; reads the second
+        vmcnt_wait<CPW * (STAGES - 2)>();          // this wave's part of step kt + 1 has landed
+        __syncthreads();                           // everyone's has; step kt's slot is no longer read
+        mma_mixed(f1b, f1a, f0b, f0a, nxt, 0, kt + STAGES);     // second half; reads step kt + 1's
+                                                                // first half, refills step kt's slot
     }
     vmcnt_wait<0>();                               // drain the (out-of-range) prefetches
     __syncthreads();                               // every wave's DMA has landed; the ring is free

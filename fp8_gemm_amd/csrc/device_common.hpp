@@ -72,6 +72,7 @@ __device__ __forceinline__ v4u load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
 
+
 // Descriptor byte count for `rows` rows of stride `ld` (rows <= 256 and
 // ld < 2^23 keep it below 2^31).
 __device__ __forceinline__ uint32_t rows_bytes(int rows, int64_t ld) {

@@ -33,9 +33,13 @@ int ok() {
 
 constexpr int64_t kMaxRowStride = (int64_t(1) << 23) - 16;   // keeps 256 rows of offsets below 2^31
 constexpr int kSwapMaxM = 64;                                  // swap-AB threshold on the token count
-constexpr int kSwapWaveRows = 32;                              // weight rows per wave in the swap kernel
+#ifndef SWAP_WAVE_ROWS
+#define SWAP_WAVE_ROWS 128
+#define SWAP_DEPTH 2
+#endif
+constexpr int kSwapWaveRows = SWAP_WAVE_ROWS;                  // weight rows per wave in the swap kernel
 constexpr int kSwapTileN = 4 * kSwapWaveRows;                  // weight rows per workgroup
-constexpr int kSwapDepth = 4;                                  // K blocks of loads in flight + 1
+constexpr int kSwapDepth = SWAP_DEPTH;                         // K blocks of loads in flight + 1
 constexpr int kContigAlign = 128;                              // row alignment of experts (contiguous form)
 #ifndef TILE128_WM
 #define TILE128_WM 2

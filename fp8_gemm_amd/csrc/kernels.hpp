@@ -357,56 +357,90 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 // Streaming swap-AB kernel.
 // 4 waves; wave w streams weight rows [n0 + w*WR, +WR) as WR/16 row blocks of
-// the 16x16x128 instruction; tokens form up to CB column blocks of 16.  DEPTH
-// register slots keep DEPTH-1 K blocks of loads in flight per wave.
+// the 16x16x128 instruction, straight from HBM into registers (no LDS: every
+// weight byte is used by exactly one wave).  Tokens form up to CB column
+// blocks of 16; their tile is shared by the 4 waves, so it is DMA'd once per
+// workgroup into a small LDS ring and read from there.  DEPTH register slots
+// keep DEPTH-1 K blocks of weight loads in flight per wave.
 // ---------------------------------------------------------------------------
 template <int WR, int CB, int FA, int FB, int DEPTH, int MODE>
-__global__ __launch_bounds__(256) void swap_kernel(GemmParams p) {
+__global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
     constexpr int RB = WR / 16;
-    constexpr int ROWB = 128;
+    constexpr int ROWB = 128;                      // K bytes per pipeline stage
+    constexpr int TR = CB <= 2 ? 32 : 16 * CB;     // token rows staged per stage (>= 32: one DMA per wave)
+    constexpr int TDMA = TR / 32;                  // token DMA instructions per wave per stage (8 rows each)
+    constexpr int TS = DEPTH + 1;                  // token ring slots
+    constexpr int TSLOT = TR * ROWB;
+    constexpr int WLOADS = RB * 2;                 // weight loads per wave per stage
     static_assert(RB >= 1 && CB >= 1 && DEPTH >= 2, "shape");
+    static_assert((DEPTH - 1) * (WLOADS + TDMA) < 64, "loads in flight");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t tsm[TS * TSLOT];
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = (MODE == MODE_MASKED) ? (int)(blockIdx.x / p.tiles_n) : 0;
     const int nb = (MODE == MODE_MASKED) ? (int)(blockIdx.x % p.tiles_n) : (int)blockIdx.x;
 
     // Valid token count: read on the device, clamped; an empty group exits
     // before forming any address ("MLS three memory-access bugs", Bug 2: a
-    // fully masked tile must not issue loads).
+    // fully masked tile must not issue loads).  The exit is uniform over the
+    // workgroup.
     const int mg = (MODE == MODE_MASKED) ? min(max(p.masked_m[g], 0), p.cap) : p.M;
     if (mg <= 0) return;
-    const int nw = nb * 4 * WR + wave * WR;   // first weight row of this wave
-    const int rows_w = min(p.N - nw, WR);
-    if (rows_w <= 0) return;                  // no barrier in this kernel: early exit is safe
+    const int nw = nb * 4 * WR + wave * WR;        // first weight row of this wave
+    const int rows_w = max(0, min(p.N - nw, WR));  // may be 0 on the N tail: the wave then loads
+                                                   // nothing but still takes part in the barriers
 
-    const uint8_t *w_base = p.B + (int64_t)g * p.b_gstride + (int64_t)nw * p.ldb;
+    const uint8_t *w_base = p.B + (int64_t)g * p.b_gstride + (int64_t)min(nw, p.N) * p.ldb;
     const uint8_t *t_base = p.A + (int64_t)g * p.a_gstride;
     uint16_t *d_base = p.D + (int64_t)g * p.d_gstride;
     const float sc = p.scale_a[0] * p.scale_b[g];
     const __amdgpu_buffer_rsrc_t rsW = make_rsrc(w_base, rows_bytes(rows_w, p.ldb));
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)tsm;
 
     // Operand layout used for both operands of v_mfma 16x16x128: lane l
     // carries row (l & 15) and, of each 128-byte K block, the bytes
     // [(l >> 4) * 16, +16) and [64 + (l >> 4) * 16, +16).  So four lanes read
-    // 64 contiguous bytes of a row per load instruction.
+    // 64 contiguous bytes of a weight row per load instruction.
     const int r16 = lane & 15;
     const int kg = lane >> 4;
     uint32_t w_off[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) w_off[r] = (uint32_t)((int64_t)(r * 16 + r16) * p.ldb) + kg * 16;
 
+    // Token DMA: instruction i of this wave covers staged rows
+    // (wave * TDMA + i) * 8 .. +8; lane l deposits row l / 8, stored chunk
+    // l % 8, loading logical chunk (l % 8) ^ key(row) (the 128-byte-row
+    // swizzle of swz()).
+    uint32_t t_dma_off[TDMA];
+    uint32_t t_dma_kc[TDMA];
+#pragma unroll
+    for (int i = 0; i < TDMA; ++i) {
+        const int row = (wave * TDMA + i) * 8 + (lane >> 3);
+        const uint32_t c = ((uint32_t)(lane & 7) ^ (row & 7u) ^ ((row >> 3) & 1u)) & 7u;
+        t_dma_kc[i] = c * 16;
+        t_dma_off[i] = (uint32_t)((int64_t)row * p.lda) + c * 16;
+    }
+    // Token fragment reads: block c, row c*16 + r16, logical chunks kg, 4 + kg.
+    uint32_t t_frag[CB][2];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+        const uint32_t row = (uint32_t)(c * 16 + r16);
+        const uint32_t key = (row & 7u) ^ ((row >> 3) & 1u);
+        t_frag[c][0] = row * ROWB + ((((uint32_t)kg) ^ key) & 7u) * 16u;
+        t_frag[c][1] = row * ROWB + ((((uint32_t)kg + 4u) ^ key) & 7u) * 16u;
+    }
+
     const int nk = (p.K + ROWB - 1) / ROWB;
 
     for (int t0 = 0; t0 < mg; t0 += CB * 16) {
         const int mt = min(mg - t0, CB * 16);
-        // Token rows past the valid count fall outside this descriptor: they
-        // read as zero and are never fetched (the NaN-filled rows behind them
-        // never reach the matrix cores: same page, Bug 3).
-        const __amdgpu_buffer_rsrc_t rsT = make_rsrc(t_base + (int64_t)t0 * p.lda, rows_bytes(mt, p.lda));
-        uint32_t t_off[CB];
-#pragma unroll
-        for (int c = 0; c < CB; ++c) t_off[c] = (uint32_t)((int64_t)(c * 16 + r16) * p.lda) + kg * 16;
+        // Token rows past the valid count fall outside this descriptor: the DMA
+        // deposits zeros for them and never fetches them (the NaN-filled rows
+        // behind them never reach the matrix cores: same page, Bug 3).
+        const v4i srdT = make_srd(t_base + (int64_t)t0 * p.lda, rows_bytes(mt, p.lda));
+        __syncthreads();                           // the ring is free (previous token block done)
 
         v4f acc[RB][CB];
 #pragma unroll
@@ -415,30 +449,29 @@ __global__ __launch_bounds__(256) void swap_kernel(GemmParams p) {
             for (int c = 0; c < CB; ++c) acc[r][c] = (v4f){0, 0, 0, 0};
 
         v4u wreg[DEPTH][RB][2];
-        v4u treg[DEPTH][CB][2];
 
+        // One stage: this wave's weight loads (registers), then its token DMA.
+        // Past the last K block every offset is out of range: no memory
+        // traffic, zeros, and the stage is never consumed.
         auto load = [&](int slot, int kt) {
-            const uint32_t k0 = (uint32_t)kt * ROWB + kg * 16;
-            const bool in0 = (kt < nk) && (int)k0 < p.K;
-            const bool in1 = (kt < nk) && (int)(k0 + 64) < p.K;
+            const uint32_t k0 = (uint32_t)kt * ROWB;
+            const bool in0 = (kt < nk) && (int)(k0 + kg * 16) < p.K;
+            const bool in1 = (kt < nk) && (int)(k0 + kg * 16 + 64) < p.K;
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
-                wreg[slot][r][0] = load16(rsW, in0 ? w_off[r] + kt * ROWB : kOobOffset);
-                wreg[slot][r][1] = load16(rsW, in1 ? w_off[r] + kt * ROWB + 64 : kOobOffset);
+                wreg[slot][r][0] = load16(rsW, in0 ? w_off[r] + k0 : kOobOffset);
+                wreg[slot][r][1] = load16(rsW, in1 ? w_off[r] + k0 + 64 : kOobOffset);
             }
 #pragma unroll
-            for (int c = 0; c < CB; ++c) {
-                treg[slot][c][0] = load16(rsT, in0 ? t_off[c] + kt * ROWB : kOobOffset);
-                treg[slot][c][1] = load16(rsT, in1 ? t_off[c] + kt * ROWB + 64 : kOobOffset);
+            for (int i = 0; i < TDMA; ++i) {
+                const bool in = (kt < nk) && (int)(k0 + t_dma_kc[i]) < p.K;
+                dma16(srdT, in ? t_dma_off[i] + k0 : kOobOffset,
+                      lds0 + (uint32_t)((kt % TS) * TSLOT) + (uint32_t)(wave * TDMA + i) * 1024u);
             }
         };
 
-        // Branch-free software pipeline: K blocks past the end load as zeros
-        // (out-of-range offsets, no memory traffic) and add nothing, so the
-        // loop body is straight-line code and every wait on a load is exact.
-        // The scheduling barriers keep the load groups in slot order, so the
-        // loads outstanding at the loop head are the same (and in the same
-        // order) on entry and on the back edge, and every wait stays exact.
+        // Software pipeline over K blocks, branch-free: the scheduling
+        // barriers keep the load groups in slot order, so every wait is exact.
 #pragma unroll
         for (int s = 0; s < DEPTH - 1; ++s) {
             load(s, s);
@@ -447,17 +480,28 @@ __global__ __launch_bounds__(256) void swap_kernel(GemmParams p) {
         for (int kb = 0; kb < nk; kb += DEPTH) {
 #pragma unroll
             for (int s = 0; s < DEPTH; ++s) {
-                load((s + DEPTH - 1) % DEPTH, kb + s + DEPTH - 1);
+                const int kt = kb + s;
+                load((s + DEPTH - 1) % DEPTH, kt + DEPTH - 1);
                 __builtin_amdgcn_sched_barrier(0);
+                // every load of step kt (older than the DEPTH - 1 newer stages) has landed
+                vmcnt_wait<(DEPTH - 1) * (WLOADS + TDMA)>();
+                __syncthreads();                   // every wave's token DMA of step kt has landed
+                const uint8_t *ts = tsm + (kt % TS) * TSLOT;
+                v8i tf[CB];
+#pragma unroll
+                for (int c = 0; c < CB; ++c)
+                    tf[c] = pack8(*reinterpret_cast<const v4u *>(ts + t_frag[c][0]),
+                                  *reinterpret_cast<const v4u *>(ts + t_frag[c][1]));
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
                     const v8i wf = pack8(wreg[s][r][0], wreg[s][r][1]);
 #pragma unroll
-                    for (int c = 0; c < CB; ++c)
-                        acc[r][c] = mfma16x16x128<FB, FA>(wf, pack8(treg[s][c][0], treg[s][c][1]), acc[r][c]);
+                    for (int c = 0; c < CB; ++c) acc[r][c] = mfma16x16x128<FB, FA>(wf, tf[c], acc[r][c]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+        vmcnt_wait<0>();                           // drain the out-of-range prefetches
 
         // Epilogue: accumulator register q of a 16x16 block holds weight row
         // 4 * (lane / 16) + q and token column lane % 16.

@@ -10,12 +10,15 @@ cap=64, N=4096, K=7168, m_g ~ U{0..32}) against the HBM roofline, the
 contiguous grouped prefill GEMM, the 256^3 GEMM (latency), the E5M2 4096^3
 GEMM and the eight transformer-projection shapes.
 
-Per-launch kernel durations come from HIP events recorded around each launch on
-the stream the kernel runs on (torch's current stream, which the library is
-handed).  The CPU baseline is the oracle, timed on a bounded row sample of the
-dense 4096^3 problem.
+The average launch duration of each leg is the interval between two HIP events
+recorded around its K back-to-back launches on the stream the kernels run on
+(torch's current stream, which the library is handed), divided by K.  The CPU
+baseline is the oracle, timed on a bounded sample of the dense 4096^3 problem
+(whole-problem passes until about 10-15 s have passed).  The 1 GiB copy leg
+calibrates the rocprofv3 HBM byte counters (--counters-summary).
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only NAME ...] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--only NAME ...] [--no-cpu]
+    python bench.py --counters-summary FETCH_DIR WRITE_DIR --counters-command "..."
 """
 from __future__ import annotations
 
@@ -63,33 +66,37 @@ def read_traffic(name: str):
 
 
 class Timer:
-    """Times `fn` (which launches work on torch's current stream): warmup
-    calls, then `steps` calls each bracketed by its own pair of events, with a
-    synchronize on both sides of the timed region."""
+    """Times `fn` (which launches work on torch's current stream): at least
+    `warmup` untimed calls and at least `min_warm_s` seconds of them (the GPU
+    clock ramps up over the first few milliseconds of load after idle), then
+    exactly `steps` back-to-back calls between one pair of HIP events recorded
+    on that stream, with a synchronize on both sides of the timed region.  The
+    average launch duration is the event interval over `steps`."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, min_warm_s=0.25):
         self.torch = torch
+        self.min_warm_s = min_warm_s
 
     def run(self, fn, steps, warmup):
         torch = self.torch
-        for _ in range(warmup):
+        t0 = time.perf_counter()
+        done = 0
+        while done < warmup or time.perf_counter() - t0 < self.min_warm_s:
             fn()
-        torch.cuda.synchronize()
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+            done += 1
+            if done % 16 == 0:
+                torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            starts[i].record(stream)
+        e0.record(stream)
+        for _ in range(steps):
             fn()
-            ends[i].record(stream)
+        e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))   # ms
-        mean = sum(per) / len(per)
-        return {"wall_s": wall, "kernel_ms_mean": mean, "kernel_ms_median": per[len(per) // 2],
-                "kernel_ms_min": per[0], "kernel_ms_p90": per[int(0.9 * (len(per) - 1))]}
+        return {"wall_s": wall, "kernel_ms_mean": e0.elapsed_time(e1) / steps, "warmup_calls": done}
 
 
 def dev(torch, x):
@@ -157,9 +164,11 @@ def bench_contig(torch, f, w, steps, warmup, timer):
     return t
 
 
-def cpu_baseline(w, target_s=15.0):
-    """The oracle on rows 0..R-1 of the dense problem (all columns, full K),
-    R chosen so the run takes about target_s seconds."""
+def cpu_baseline(w, target_s=15.0, max_passes=20):
+    """The oracle on the dense problem: rows 0..R-1 (all columns, full K), R
+    chosen so one pass takes about target_s seconds; when the whole problem
+    takes less than that, whole-problem passes are repeated until about
+    target_s seconds have passed (at most max_passes)."""
     import oracle
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or oracle.default_threads()
@@ -170,26 +179,119 @@ def cpu_baseline(w, target_s=15.0):
     oracle.gemm_nt(w.A[:r0], w.B, w.a_fmt, w.b_fmt, w.sa, w.sb, threads=threads)
     probe = time.perf_counter() - t0
     rows = int(min(M, max(threads, r0 * target_s / max(probe, 1e-3))))
-    rows = max(threads, (rows // threads) * threads)
+    rows = M if rows >= M else max(threads, (rows // threads) * threads)
+    passes = 0
     t0 = time.perf_counter()
-    oracle.gemm_nt(w.A[:rows], w.B, w.a_fmt, w.b_fmt, w.sa, w.sb, threads=threads)
-    el = time.perf_counter() - t0
-    flops = 2.0 * rows * N * K
+    while True:
+        oracle.gemm_nt(w.A[:rows], w.B, w.a_fmt, w.b_fmt, w.sa, w.sb, threads=threads)
+        passes += 1
+        el = time.perf_counter() - t0
+        if rows < M or el >= 0.67 * target_s or passes >= max_passes:
+            break
+    flops = 2.0 * rows * N * K * passes
+    what = (f"rows 0..{rows - 1} of the {M}x{N}x{K} E4M3 problem (all {N} columns, full K)" if rows < M
+            else f"the whole {M}x{N}x{K} E4M3 problem, {passes} pass(es)")
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} E4M3 problem (all {N} columns, full K), "
-                      f"{el:.1f} s on {threads} host threads",
-            "seconds": el}
+            "sample": f"{what}, {el:.1f} s on {threads} host threads", "seconds": el}
+
+
+def bench_copy(torch, steps, warmup, timer, nbytes=1 << 30):
+    """A plain elementwise copy of known size (fp32 negation: reads nbytes,
+    writes nbytes) that calibrates the HBM byte counters."""
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t = timer.run(lambda: torch.neg(src, out=dst), steps, warmup)
+    t["bytes_read"] = float(nbytes)
+    t["bytes_written"] = float(nbytes)
+    t["gbs_kernel"] = 2.0 * nbytes / (t["kernel_ms_mean"] * 1e-3) / 1e9
+    del src, dst
+    return t
+
+
+# Kernel-name patterns of the launches each counter summary covers.
+COUNTER_TARGETS = {
+    "dense_4096_e4m3": ("ring_kernel<256, 256", "dense 4096^3 E4M3 GEMM"),
+    "masked_decode": ("swap_kernel<", "masked grouped decode GEMM G=32 cap=64 N=4096 K=7168 m_g~U{0..32}"),
+}
+COPY_PATTERN = "neg_kernel"
+
+
+def _counter_rows(directory):
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {directory}")
+    out = {}
+    for fpath in files:
+        with open(fpath, newline="") as fh:
+            for row in csv.DictReader(fh):
+                key = (row["Dispatch_Id"], row["Kernel_Name"])
+                out.setdefault(key, {})
+                name = row["Counter_Name"]
+                out[key][name] = out[key].get(name, 0.0) + float(row["Counter_Value"])
+    return out
+
+
+def _per_dispatch(rows, pattern, counter):
+    vals = [c[counter] for (d, k), c in rows.items() if pattern in k and counter in c]
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel matching {pattern!r} with counter {counter}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def counters_summary(fetch_dir, write_dir, command):
+    """Writes profiles/<name>_hbm_counters.txt from a rocprofv3 --pmc FETCH_SIZE
+    run and a --pmc WRITE_SIZE run (KiB per dispatch), each scaled by what the
+    same counter reads for the copy kernel of known size."""
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    copy_f, ncf = _per_dispatch(fr, COPY_PATTERN, "FETCH_SIZE")
+    copy_w, ncw = _per_dispatch(wr, COPY_PATTERN, "WRITE_SIZE")
+    nbytes = float(1 << 30)
+    kf, kw = nbytes / (copy_f * 1024.0), nbytes / (copy_w * 1024.0)
+    h = kernel_source_hash()
+    for name, (pattern, what) in COUNTER_TARGETS.items():
+        f_kib, nf = _per_dispatch(fr, pattern, "FETCH_SIZE")
+        w_kib, nw = _per_dispatch(wr, pattern, "WRITE_SIZE")
+        rd, wt = f_kib * 1024.0 * kf, w_kib * 1024.0 * kw
+        text = (f"rocprofv3 HBM byte counters: {what}\n\n"
+                f"commands (from the repository root):\n{command}\n\n"
+                f"kernel_source_hash: {h}\n"
+                f"kernel name pattern: {pattern}  (dispatches: FETCH {nf}, WRITE {nw})\n"
+                f"FETCH_SIZE per dispatch: {f_kib:.1f} KiB\n"
+                f"WRITE_SIZE per dispatch: {w_kib:.1f} KiB\n"
+                f"calibration, fp32 negation of 1 GiB (reads 1 GiB, writes 1 GiB), {ncf}/{ncw} dispatches:\n"
+                f"  FETCH_SIZE {copy_f:.1f} KiB -> read factor {kf:.4f}\n"
+                f"  WRITE_SIZE {copy_w:.1f} KiB -> write factor {kw:.4f}\n"
+                f"hbm_read_bytes_per_launch: {rd:.0f}\n"
+                f"hbm_write_bytes_per_launch: {wt:.0f}\n"
+                f"hbm_bytes_per_launch: {rd + wt:.0f}\n")
+        path = os.path.join(PROFILE_DIR, f"{name}_hbm_counters.txt")
+        with open(path, "w") as fh:
+            fh.write(text)
+        log(f"wrote {path}: {(rd + wt) / 1e6:.1f} MB per launch")
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: dense masked contig small e5m2 proj (default: all)")
+                    help="subset of: dense masked contig small e5m2 proj copy (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="write profiles/*_hbm_counters.txt from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
+                         "output directories (no GPU work)")
+    ap.add_argument("--counters-command", default="",
+                    help="the commands that produced the counter directories (recorded in the summary)")
     args = ap.parse_args()
+
+    if args.counters_summary:
+        counters_summary(args.counters_summary[0], args.counters_summary[1], args.counters_command)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -206,7 +308,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     timer = Timer(torch)
-    want = set(args.only) if args.only else {"dense", "masked", "contig", "small", "e5m2", "proj"}
+    want = set(args.only) if args.only else {"dense", "masked", "contig", "small", "e5m2", "proj", "copy"}
     steps, warmup = args.steps, args.warmup
     extra = {}
 
@@ -229,7 +331,7 @@ def main():
         log("timing dense 256^3")
         ws = workloads.dense_small()
         r = bench_dense(torch, f, ws, steps, warmup, timer)
-        extra["dense_256"] = {"kernel_us_mean": r["kernel_ms_mean"] * 1e3, "kernel_us_median": r["kernel_ms_median"] * 1e3,
+        extra["dense_256"] = {"kernel_us_mean": r["kernel_ms_mean"] * 1e3,
                               "us_per_call_wall": r["wall_s"] / steps * 1e6, "bound": "launch latency"}
     if "masked" in want:
         log("generating masked grouped decode inputs (G=32, cap=64, N=4096, K=7168)")
@@ -271,6 +373,12 @@ def main():
             del wp
         extra["projections"] = out
 
+    if "copy" in want:
+        log("timing the 1 GiB copy used to calibrate the HBM byte counters")
+        r = bench_copy(torch, steps, warmup, timer)
+        extra["copy_1gib"] = {"gbs_kernel": r["gbs_kernel"], "kernel_ms_mean": r["kernel_ms_mean"]}
+        log(f"  {r['gbs_kernel']:.0f} GB/s read+write")
+
     cpu = None
     if not args.no_cpu and dense is not None:
         log("timing the CPU oracle on a row sample")
@@ -297,7 +405,7 @@ def main():
                    "M": 4096, "N": 4096, "K": 4096},
         "roofline": {"bound": "mfma", "achieved": dense["tflops_kernel"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": dense["tflops_kernel"] / PEAK_FP8_TFLOPS, "traffic": read_traffic("dense_4096_e4m3"),
-                     "kernel_ms_mean": dense["kernel_ms_mean"], "kernel_ms_median": dense["kernel_ms_median"],
+                     "kernel_ms_mean": dense["kernel_ms_mean"],
                      "algorithmic_flops": dense["flops"], "algorithmic_bytes": dense["bytes"]},
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),

@@ -37,8 +37,12 @@ constexpr int kSwapMaxM = 64;                                  // swap-AB thresh
 #define SWAP_WAVE_ROWS 128
 #define SWAP_DEPTH 2
 #endif
-constexpr int kSwapWaveRows = SWAP_WAVE_ROWS;                  // weight rows per wave in the swap kernel
-constexpr int kSwapTileN = 4 * kSwapWaveRows;                  // weight rows per workgroup
+constexpr int kSwapWaveRows = SWAP_WAVE_ROWS;                  // weight rows per wave, grouped forms
+constexpr int kSwapTileN = 4 * kSwapWaveRows;                  // weight rows per workgroup, grouped forms
+// A dense problem is one group, so it takes narrower workgroups to spread N
+// over more of the 256 CUs.
+constexpr int kSwapDenseWaveRows = 32;
+constexpr int kSwapDenseTileN = 4 * kSwapDenseWaveRows;
 constexpr int kSwapDepth = SWAP_DEPTH;                         // K blocks of loads in flight + 1
 constexpr int kContigAlign = 128;                              // row alignment of experts (contiguous form)
 #ifndef TILE128_WM
@@ -96,9 +100,9 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
         if (m <= kSwapMaxM) {
             out->variant = V_SWAP;
             out->tile_m = 16 * token_blocks_for(m);
-            out->tile_n = kSwapTileN;
+            out->tile_n = kSwapDenseTileN;
             out->token_blocks = token_blocks_for(m);
-            out->workgroups = cdiv(n, kSwapTileN);
+            out->workgroups = cdiv(n, kSwapDenseTileN);
         } else {
             out->variant = pick_dense_tile(m, n);
             out->tile_m = out->variant == V_TILE_256x256 ? 256 : 128;
@@ -192,7 +196,8 @@ template <int CB, int MODE>
 int launch_swap_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     const dim3 block(256);
 #define FP8G_SWAP(FA, FB) \
-    hipLaunchKernelGGL((fp8g::swap_kernel<kSwapWaveRows, CB, FA, FB, kSwapDepth, MODE>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((fp8g::swap_kernel<MODE == fp8g::MODE_DENSE ? kSwapDenseWaveRows : kSwapWaveRows, CB, FA, FB, \
+                                          kSwapDepth, MODE>), grid, block, 0, s, p)
     if (fa == 0 && fb == 0) FP8G_SWAP(0, 0);
     else if (fa == 0 && fb == 1) FP8G_SWAP(0, 1);
     else if (fa == 1 && fb == 0) FP8G_SWAP(1, 0);

@@ -65,12 +65,13 @@ def test_dense_plan_grid(f):
     p = f.plan(0, 4096, 4096, 4096)
     assert (p.tile_m, p.tile_n, p.workgroups) == (256, 256, 256)
     p = f.plan(0, 17, 4096, 7168)
-    assert p.token_blocks == 2 and p.workgroups == 4096 // 128
+    assert p.token_blocks == 2 and p.tile_n == 128 and p.workgroups == 4096 // 128
 
 
 def test_masked_plan_uses_hint_not_results(f):
     p = f.plan(1, 64, 4096, 7168, 32, 32)
-    assert p.variant == 3 and p.token_blocks == 2 and p.workgroups == 32 * 32
+    # 4 waves x 128 weight rows = 512 rows of one expert per workgroup
+    assert p.variant == 3 and p.token_blocks == 2 and p.tile_n == 512 and p.workgroups == 32 * (4096 // 512)
     p = f.plan(1, 64, 4096, 7168, 32, 0)           # hint 0 -> capacity
     assert p.variant == 3 and p.token_blocks == 4
     p = f.plan(1, 256, 4096, 7168, 8, 0)           # many rows per group -> tiled

@@ -133,10 +133,12 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
     if (op == 2) {
         if (m == 0 || n == 0) return ok();
         if (groups == 0) return fail(FP8G_ERR_SHAPE, "G=0 with M_total=%d rows", m);
-        out->variant = V_TILE_128x256;
-        out->tile_m = kContigAlign;
+        // 256-row tiles, then one workgroup per tile for its second 128-row
+        // block, which computes only when that block's expert differs.
+        out->variant = V_TILE_256x256;
+        out->tile_m = 2 * kContigAlign;
         out->tile_n = 256;
-        out->workgroups = cdiv(m, kContigAlign) * cdiv(n, 256);
+        out->workgroups = 2 * cdiv(m, 2 * kContigAlign) * cdiv(n, 256);
         return ok();
     }
     return fail(FP8G_ERR_ARG, "unknown op %d", op);
@@ -181,8 +183,8 @@ int launch_ring(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
 }
 
 // Tile shapes of the tiled kernel: 256 x 256 with 8 waves (4 along M, 2 along
-// N) and a 4-slot ring (128 KB of LDS); 128 x 256 with 8 waves (2 x 4) and a
-// 4-slot ring (96 KB).
+// N) and a 2-slot ring of 128-byte K steps (128 KB of LDS); 128 x 256 with 8
+// waves (2 x 4) and a 3-slot ring (144 KB).
 template <int MODE>
 int launch_tile256(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE>(fa, fb, p, grid, s);
@@ -344,10 +346,10 @@ int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dty
     p.b_gstride = (int64_t)N * K;
     p.M = M_total; p.N = N; p.K = K; p.G = G; p.cap = M_total;
     p.scale_a = scale_a; p.scale_b = scale_b; p.grp_idx = grp_idx;
-    p.tiles_m = (int)cdiv(M_total, kContigAlign);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    p.tiles_m = (int)cdiv(M_total, 2 * kContigAlign);
     p.tiles_n = (int)cdiv(N, 256);
-    return launch_tile128<fp8g::MODE_CONTIG>(a_dtype, b_dtype, p, dim3((unsigned)plan.workgroups),
-                                             static_cast<hipStream_t>(stream));
+    return launch_tile256<fp8g::MODE_CONTIG>(a_dtype, b_dtype, p, dim3((unsigned)plan.workgroups), s);
 }
 
 }  // extern "C"

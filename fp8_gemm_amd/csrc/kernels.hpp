@@ -47,22 +47,42 @@ struct GemmParams {
 };
 
 // ---------------------------------------------------------------------------
-// Tile index -> (tm, tn) for the dense tiled kernel.
+// Tile index -> (tm, tn) for the tiled kernel (dense and contiguous forms).
 //
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
-// XCD w % 8), and each XCD has its own L2.  Remap so that XCD x owns a
-// contiguous range of logical tiles, and order logical tiles in bands of
-// kGroupM tile-rows so one XCD's tiles share few A and B panels (for 4096^3
-// with 256x256 tiles: a 4 x 8 block of tiles per XCD, 12 panels instead of 64).
+// Workgroups are dispatched in index order, round-robin over the 8 XCDs
+// (workgroup w runs on XCD w % 8), and each XCD has its own L2.  Logical tiles
+// are ordered in bands of kGroupM tile-rows (column by column inside a band),
+// so consecutive logical tiles share few operand panels, and the remap gives
+// each XCD runs of consecutive logical tiles:
+//   CHUNKED = false: XCD x owns the x-th eighth of all tiles (for 4096^3 with
+//     256 x 256 tiles, a 4 x 8 block of tiles: 12 panels instead of 64);
+//   CHUNKED = true: chunks of kXcdChunk tiles (one XCD's worth of CUs) go to
+//     the XCDs in turn, so the whole chip works on one window of consecutive
+//     chunks at a time.  That keeps the working set small enough for the
+//     last-level (Infinity) cache when the operands are far larger than it, as
+//     in the contiguous grouped form where every expert brings its own
+//     weights (measured 14% faster there, 2-3% slower for large dense shapes
+//     whose weights stay cached either way).
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;
+constexpr int kXcdChunk = 32;
 constexpr int kGroupM = 4;
 
-__device__ __forceinline__ void dense_tile_coords(int wg, int tiles_m, int tiles_n, int &tm, int &tn) {
+template <bool CHUNKED>
+__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int &tm, int &tn) {
     const int nt = tiles_m * tiles_n;
-    const int per_xcd = nt / kXcds;
     int t = wg;
-    if (wg < per_xcd * kXcds) t = (wg % kXcds) * per_xcd + wg / kXcds;
+    if (CHUNKED) {
+        constexpr int round = kXcds * kXcdChunk;
+        if (wg < (nt / round) * round) {
+            // wg = 8 k + x: the k-th workgroup of XCD x
+            const int x = wg % kXcds, k = wg / kXcds;
+            t = ((k / kXcdChunk) * kXcds + x) * kXcdChunk + k % kXcdChunk;
+        }
+    } else {
+        const int per_xcd = nt / kXcds;
+        if (wg < per_xcd * kXcds) t = (wg % kXcds) * per_xcd + wg / kXcds;
+    }
     const int band = kGroupM * tiles_n;
     const int b = t / band;
     const int first_m = b * kGroupM;
@@ -120,83 +140,113 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 
     // ---- tile coordinates and per-mode operand bases (64-bit arithmetic) ----
     int tm, tn, g = 0;
-    if (MODE == MODE_DENSE) {
-        dense_tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-    } else {
-        tm = blockIdx.x / p.tiles_n;
-        tn = blockIdx.x % p.tiles_n;
-        if (MODE == MODE_MASKED) g = blockIdx.y;
-    }
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
+    int m0;                                        // first output row of this tile
     int rows_m;
     int expert = 0;
     if (MODE == MODE_DENSE) {
+        tile_coords<false>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+        m0 = tm * BM;
         rows_m = min(p.M - m0, BM);
     } else if (MODE == MODE_MASKED) {
+        tm = blockIdx.x / p.tiles_n;
+        tn = blockIdx.x % p.tiles_n;
+        g = blockIdx.y;
+        m0 = tm * BM;
         const int mg = min(max(p.masked_m[g], 0), p.cap);
         if (m0 >= mg) return;                      // nothing valid in this tile: no load at all
         rows_m = min(mg - m0, BM);
         expert = g;
     } else {
-        // The expert of this block of rows: the index of its first row that
-        // names a valid expert.  A block with none is all padding.
-        rows_m = min(p.M - m0, BM);
-        expert = -1;
-        for (int base = 0; base < rows_m; base += 64) {
-            const int r = base + lane;
-            int e = -1;
-            if (r < rows_m) e = p.grp_idx[m0 + r];
-            const bool ok = (e >= 0) && (e < p.G);
-            const unsigned long long ball = __ballot(ok);
-            if (ball) {
-                expert = __shfl(e, __builtin_ctzll(ball));
-                break;
+        // The expert of a block of rows is that of its first row naming a
+        // valid expert; a block with none is all padding.  Rows of any other
+        // expert in the block are not written by this tile.
+        auto first_expert = [&](int r0, int nrows) {
+            for (int base = 0; base < nrows; base += 64) {
+                const int r = base + lane;
+                int e = -1;
+                if (r < nrows) e = p.grp_idx[r0 + r];
+                const bool ok = (e >= 0) && (e < p.G);
+                const unsigned long long ball = __ballot(ok);
+                if (ball) return __builtin_amdgcn_readfirstlane(__shfl(e, __builtin_ctzll(ball)));
             }
+            return -1;
+        };
+        const int ntiles = p.tiles_m * p.tiles_n;
+        if (BM != 256 || (int)blockIdx.x < ntiles) {
+            tile_coords<true>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+            m0 = tm * BM;
+            rows_m = min(p.M - m0, BM);
+            expert = first_expert(m0, rows_m);
+            if (expert < 0) return;
+        } else {
+            // A 256-row tile covers two 128-row blocks, each of at most one
+            // expert, and writes the rows of the expert of its first valid
+            // row.  The second half of the grid (one workgroup per tile)
+            // covers the second block when its expert differs: it computes
+            // that block alone (tile rows 128..255 read zeros).  These
+            // workgroups come last in dispatch order, where the last partial
+            // wave of full tiles leaves CUs idle.
+            const int w2 = blockIdx.x - ntiles;
+            tm = w2 / p.tiles_n;
+            tn = w2 % p.tiles_n;
+            const int base = tm * BM;
+            const int r2 = min(p.M - (base + 128), 128);
+            if (r2 <= 0) return;
+            const int e1 = first_expert(base, min(p.M - base, BM));
+            const int e2 = first_expert(base + 128, r2);
+            if (e2 < 0 || e2 == e1) return;
+            m0 = base + 128;
+            rows_m = r2;
+            expert = e2;
         }
-        if (expert < 0) return;
     }
+    const int n0 = tn * BN;
     const int rows_n = min(p.N - n0, BN);
+    uint16_t *d_base = p.D + (MODE == MODE_MASKED ? (int64_t)g * p.d_gstride : 0);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
 
     const uint8_t *a_base = p.A + (MODE == MODE_MASKED ? (int64_t)g * p.a_gstride : 0) + (int64_t)m0 * p.lda;
     const uint8_t *b_base = p.B + (int64_t)expert * p.b_gstride + (int64_t)n0 * p.ldb;
-    uint16_t *d_base = p.D + (MODE == MODE_MASKED ? (int64_t)g * p.d_gstride : 0);
     const float sc = p.scale_a[0] * p.scale_b[MODE == MODE_DENSE ? 0 : expert];
 
     // Rows past rows_m / rows_n fall outside the descriptors: the DMA writes
     // zeros for them and issues no memory transaction.
     const v4i srdA = make_srd(a_base, rows_bytes(rows_m, p.lda));
     const v4i srdB = make_srd(b_base, rows_bytes(rows_n, p.ldb));
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
 
     // ---- this wave's DMA chunks ----
     // Instruction q covers DROWS rows x BK bytes: A rows for q < BM / DROWS,
     // else B rows.  Lane l deposits LDS bytes [16 l, 16 l + 16) of it, i.e.
     // row l / KCH, stored chunk l % KCH; it loads logical chunk
-    // (l % KCH) ^ key(row), so the LDS image is swizzled (see ring_key).
-    uint32_t dma_off[CPW];
-    uint32_t dma_kc[CPW];
-    bool dma_a[CPW];
-#pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-        const int q = wave * CPW + i;
-        const bool isA = q < BM / DROWS;
-        const int row = (isA ? q : q - BM / DROWS) * DROWS + lane / KCH;
-        const uint32_t c = ((uint32_t)(lane % KCH) ^ ring_key<BK>(row)) & (KCH - 1);
-        dma_a[i] = isA;
-        dma_kc[i] = c * 16;
-        dma_off[i] = (uint32_t)((int64_t)row * (isA ? p.lda : p.ldb)) + c * 16;
-    }
+    // (l % KCH) ^ key(row), so the LDS image is swizzled (see ring_key).  For
+    // row = qq * DROWS + l / KCH (qq: the instruction's index within its
+    // operand) the key depends on qq only through its parity, so a lane needs
+    // two chunk choices and, per operand, two per-lane offsets; the rest of
+    // the offset, qq * DROWS * ld, is the same for the whole wave.
+    const uint32_t lrow_in = (uint32_t)lane / KCH;
+    uint32_t dkc0 = (((uint32_t)lane % KCH) ^ ring_key<BK>(lrow_in)) & (KCH - 1);
+    uint32_t dkc1 = (((uint32_t)lane % KCH) ^ ring_key<BK>(DROWS + lrow_in)) & (KCH - 1);
+    dkc0 *= 16u;
+    dkc1 *= 16u;
+    uint32_t doA0 = lrow_in * (uint32_t)p.lda + dkc0, doA1 = lrow_in * (uint32_t)p.lda + dkc1;
+    uint32_t doB0 = lrow_in * (uint32_t)p.ldb + dkc0, doB1 = lrow_in * (uint32_t)p.ldb + dkc1;
     const int nk = (p.K + BK - 1) / BK;
-    auto issue = [&](int kt) {
-        const int slot = kt % STAGES;
+    auto issue_one = [&](int kt, int i) {
+        const int q = wave * CPW + i;              // wave-uniform
+        const bool isA = q < BM / DROWS;
+        const int qq = isA ? q : q - BM / DROWS;
         const uint32_t k0 = (uint32_t)kt * BK;
+        const uint32_t rowoff = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)((uint32_t)(qq * DROWS) * (uint32_t)(isA ? p.lda : p.ldb) + k0));
+        const uint32_t kc = (qq & 1) ? dkc1 : dkc0;
+        const uint32_t lo = (qq & 1) ? (isA ? doA1 : doB1) : (isA ? doA0 : doB0);
+        const bool in = (kt < nk) && (int)(k0 + kc) < p.K;
+        dma16(isA ? srdA : srdB, in ? lo + rowoff : kOobOffset,
+              lds0 + (kt % STAGES) * SLOT + (uint32_t)q * 1024u);
+    };
+    auto issue = [&](int kt) {
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-            const bool in = (kt < nk) && (int)(k0 + dma_kc[i]) < p.K;
-            dma16(dma_a[i] ? srdA : srdB, in ? dma_off[i] + k0 : kOobOffset,
-                  lds0 + slot * SLOT + (uint32_t)(wave * CPW + i) * 1024u);
-        }
+        for (int i = 0; i < CPW; ++i) issue_one(kt, i);
     };
 
     // ---- fragment read offsets ----
@@ -246,12 +296,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
         if (q < FN) bf[q] = v;
         else af[q - FN] = v;
     };
-    auto issue_one = [&](int kt, int q) {
-        const uint32_t k0 = (uint32_t)kt * BK;
-        const bool in = (kt < nk) && (int)(k0 + dma_kc[q]) < p.K;
-        dma16(dma_a[q] ? srdA : srdB, in ? dma_off[q] + k0 : kOobOffset,
-              lds0 + (kt % STAGES) * SLOT + (uint32_t)(wave * CPW + q) * 1024u);
-    };
     // One K half of MFMAs with other work spread between them: the fragments
     // of the next half (read_slot / read_h) and, when refill_kt >= 0, the DMA
     // refill of a ring slot.  Issued in bursts, LDS reads and DMA instructions
@@ -294,6 +338,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     __syncthreads();
     read_frags(f0b, f0a, smem, 0);
     for (int kt = 0; kt < nk; ++kt) {
+        // Redefined each step so that the compiler forms the DMA offsets in
+        // the loop instead of keeping one register per instruction live.
+        asm volatile("" : "+v"(doA0), "+v"(doA1), "+v"(doB0), "+v"(doB1), "+v"(dkc0), "+v"(dkc1));
         const uint8_t *cur = smem + (kt % STAGES) * SLOT;
         const uint8_t *nxt = smem + ((kt + 1) % STAGES) * SLOT;
         __builtin_amdgcn_sched_barrier(0);

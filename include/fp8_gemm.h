@@ -31,8 +31,9 @@
  *   - D is BF16 (uint16 bit patterns), rounded to nearest even.  D must not
  *     alias A, B, the scales or the index vectors.
  *   - Arguments are validated before anything is enqueued.  A nonzero return
- *     (an fp8g_status) means nothing was enqueued; fp8_gemm_strerror() gives the
- *     reason, including a per-thread detail string for the last failure.
+ *     (an fp8g_status) from validation means nothing was enqueued;
+ *     fp8_gemm_strerror() gives the reason, including a per-thread detail
+ *     string for the last failure.
  *   - Zero-sized problems (M, N, G, cap or M_total = 0) return FP8G_OK and
  *     enqueue nothing.  K = 0 writes zeros (the empty sum); A and B may then be
  *     NULL, as nothing is read from them.
@@ -119,6 +120,9 @@ int fp8_grouped_gemm_masked(const void *A, int a_dtype, const void *B, int b_dty
  *     expert (plus padding); rows of a second expert inside a block are left
  *     unwritten.
  *   D: [M_total][N] BF16, contiguous.
+ * Work is split into tiles of 256 rows: a tile computes the rows of the
+ * expert of its first valid row; a second set of workgroups, one per tile,
+ * computes a tile's second 128-row block when it belongs to another expert.
  */
 int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dtype,
                             const float *scale_a, const float *scale_b,

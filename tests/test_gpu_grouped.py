@@ -185,6 +185,26 @@ def test_contig_empty_experts_and_tail():
     check_contig(w, d)
 
 
+def test_contig_expert_changes_at_odd_and_even_blocks():
+    """Runs of 128 | 256 | 128 | 128 | 384 | 128 rows (one empty expert): the
+    expert changes both inside 256-row tiles (at odd 128-row blocks) and
+    between them; ragged N and K."""
+    w = workloads.contig_random(tokens=0, topk=1, G=7, N=264, K=400, seed=54, counts=[128, 256, 1, 127, 0, 300, 5])
+    assert w.A.shape[0] == 9 * 128
+    d = run_contig(w)
+    check_contig(w, d)
+
+
+def test_contig_all_padding_halves():
+    """A 256-row tile whose first, or second, 128-row half is all padding."""
+    w = workloads.contig_random(tokens=0, topk=1, G=4, N=256, K=256, seed=55, counts=[100, 256, 300, 128])
+    assert w.A.shape[0] == 7 * 128
+    w.grp_idx[0:128] = -1          # first half of tile 0 all padding; expert 1 fills its second half
+    w.grp_idx[640:768] = -1        # second half of tile 2 all padding
+    d = run_contig(w)
+    check_contig(w, d)
+
+
 def test_contig_formats():
     w = workloads.contig_random(tokens=200, topk=1, G=3, N=136, K=384, seed=53, a_fmt=E5M2, b_fmt=E4M3)
     d = run_contig(w)

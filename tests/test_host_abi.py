@@ -83,7 +83,9 @@ def test_masked_plan_uses_hint_not_results(f):
 
 def test_contig_plan(f):
     p = f.plan(2, 67584, 4096, 7168, 32)
-    assert p.variant == 2 and p.tile_m == 128 and p.workgroups == (67584 // 128) * 16
+    # 256-row tiles, plus one workgroup per tile for a second expert in its
+    # second 128-row block
+    assert p.variant == 1 and p.tile_m == 256 and p.workgroups == 2 * (67584 // 256) * 16
 
 
 @pytest.mark.parametrize("args,status", [

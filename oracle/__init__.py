@@ -17,7 +17,10 @@ documented at the top of ``fp8_oracle.c``:
   and 5.2),
 * BF16 round-to-nearest-even in one rounding,
 * the masked and contiguous grouped forms ("One transpose, half the compute:
-  the DeepSeek SwapAB story", sections 2 and 3.1-3.3).
+  the DeepSeek SwapAB story", sections 2 and 3.1-3.3),
+* the block-scaled dense form: power-of-two (UE8M0) scales per 128-element K
+  block, per row of A and per 128 rows of B (DeepGEMM on Hopper, section 5.2;
+  SwapAB story, section 5).
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against things other
 than itself: torch's FP8 conversions, exact rational arithmetic, closed forms,
@@ -73,6 +76,12 @@ def _load():
     lib.oracle_grouped_masked.restype = I
     lib.oracle_grouped_contig.argtypes = [P, I, P, I, F, P, P, P, P, P, P, I64, I64, I64, I64, I]
     lib.oracle_grouped_contig.restype = I
+    lib.oracle_gemm_nt_blockscaled.argtypes = [P, I64, I, P, I64, I, P, I64, P, I64, P, I64, P, P,
+                                               I64, I64, I64, I]
+    lib.oracle_gemm_nt_blockscaled.restype = I
+    lib.oracle_gemm_nt_blockscaled_points.argtypes = [P, I64, I, P, I64, I, P, I64, P, I64, I64,
+                                                      I64, P, P, P, P, P, I]
+    lib.oracle_gemm_nt_blockscaled_points.restype = I
     _lib = lib
     return lib
 
@@ -218,3 +227,73 @@ def grouped_contig(A, B, grp_idx, scale_b, a_fmt=E4M3, b_fmt=E4M3, sa=1.0, D_ini
     if rc != 0:
         raise RuntimeError(f"oracle_grouped_contig failed ({rc})")
     return D, R, S, EX
+
+
+def _blockscale_check(A, B, scale_a, scale_b):
+    M, K = A.shape
+    N = B.shape[0]
+    kb = (K + 127) // 128
+    nb = (N + 127) // 128
+    scale_a = np.ascontiguousarray(scale_a)
+    scale_b = np.ascontiguousarray(scale_b)
+    if scale_a.dtype != np.uint8 or scale_b.dtype != np.uint8:
+        raise TypeError("scales are uint8 E8M0 codes")
+    if scale_a.ndim != 2 or scale_a.shape[0] != kb or scale_a.shape[1] < M:
+        raise ValueError(f"scale_a must be [{kb}, >= {M}] (K block, row)")
+    if scale_b.ndim != 2 or scale_b.shape[0] != nb or scale_b.shape[1] < kb:
+        raise ValueError(f"scale_b must be [{nb}, >= {kb}] (128-row block, K block)")
+    return scale_a, scale_b
+
+
+def gemm_nt_blockscaled(A, B, scale_a, scale_b, a_fmt=E4M3, b_fmt=E4M3, threads=None):
+    """Block-scaled dense GEMM.  A: uint8 [M, K], B: uint8 [N, K];
+    scale_a: uint8 E8M0 [ceil(K/128), M'] (M' >= M; column m, row kb = scale
+    of row m over K block kb); scale_b: uint8 E8M0 [ceil(N/128), KB'] (row nb,
+    column kb = scale of rows 128 nb .. 128 nb + 127 over K block kb).
+
+    Returns (D_bits uint16 [M, N], R float64 [M, N], S float64 [M, N]) with
+    S = sum_k |a_ik b_jk| times the element's block scales.
+    """
+    A = _u8(A)
+    B = _u8(B)
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A and B disagree on K")
+    scale_a, scale_b = _blockscale_check(A, B, scale_a, scale_b)
+    D = np.zeros((M, N), dtype=np.uint16)
+    R = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    rc = _load().oracle_gemm_nt_blockscaled(_ptr(A), K, int(a_fmt), _ptr(B), K, int(b_fmt),
+                                            _ptr(scale_a), scale_a.shape[1], _ptr(scale_b), scale_b.shape[1],
+                                            _ptr(D), N, _ptr(R), _ptr(S), M, N, K, threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_nt_blockscaled failed ({rc})")
+    return D, R, S
+
+
+def gemm_nt_blockscaled_points(A, B, scale_a, scale_b, ii, jj, a_fmt=E4M3, b_fmt=E4M3, threads=None):
+    """Block-scaled dense GEMM at selected elements (ii[p], jj[p]) only (1-D outputs)."""
+    A = _u8(A)
+    B = _u8(B)
+    K = A.shape[1]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
+    scale_a, scale_b = _blockscale_check(A, B, scale_a, scale_b)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    if ii.shape != jj.shape:
+        raise ValueError("ii and jj differ in length")
+    if ii.size and (ii.min() < 0 or ii.max() >= A.shape[0] or jj.min() < 0 or jj.max() >= B.shape[0]):
+        raise IndexError("sample point outside the output")
+    n = ii.size
+    D = np.zeros(n, dtype=np.uint16)
+    R = np.zeros(n, dtype=np.float64)
+    S = np.zeros(n, dtype=np.float64)
+    rc = _load().oracle_gemm_nt_blockscaled_points(_ptr(A), K, int(a_fmt), _ptr(B), K, int(b_fmt),
+                                                   _ptr(scale_a), scale_a.shape[1], _ptr(scale_b),
+                                                   scale_b.shape[1], K, n, _ptr(ii), _ptr(jj),
+                                                   _ptr(D), _ptr(R), _ptr(S), threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_nt_blockscaled_points failed ({rc})")
+    return D, R, S

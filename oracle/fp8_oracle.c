@@ -35,6 +35,15 @@
  *     rows of D are not touched.
  *   - Contiguous grouped: row r with 0 <= grp_idx[r] < G uses expert grp_idx[r]
  *     and scale_b[grp_idx[r]]; other rows are padding and are not touched.
+ *   - Block-scaled dense (DeepGEMM on Hopper, section 5.2: scales per group of
+ *     128 elements; "One transpose, half the compute", section 5: UE8M0 packed
+ *     scales): A has one scale per (row, block of 128 along K), B one per
+ *     (block of 128 rows, block of 128 along K).  Each scale is an unsigned
+ *     E8M0 code e, value 2^(e - 127); e = 255 is NaN.  A K block's partial
+ *     sum is multiplied by the two scales of its block and added to the
+ *     accumulator: acc = sum_kb sa(m,kb) * sb(n/128,kb) * sum_{k in kb} a*b,
+ *     all in FP64 (power-of-two scales make each product exact), blocks in
+ *     order; the last K block may be shorter than 128.
  */
 #include <math.h>
 #include <pthread.h>
@@ -378,4 +387,133 @@ int oracle_grouped_contig(const uint8_t *A, int a_fmt, const uint8_t *B, int b_f
     run_job(&j, nthreads);
     free(t); free(a_row); free(b_base); free(out_row); free(scale);
     return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Block-scaled dense GEMM (UE8M0 scales per 128-element K blocks).           */
+/* ------------------------------------------------------------------------- */
+
+/* Value of one unsigned E8M0 scale code.                                     */
+static double e8m0_value(uint8_t e)
+{
+    if (e == 255u) return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+typedef struct {
+    double dec_a[256], dec_b[256];
+    const uint8_t *A, *B, *SA, *SB;
+    int64_t lda, ldb, lds_a, lds_b, M, N, K;
+    uint16_t *D; double *R, *S;
+    int64_t ldd;
+    int64_t npts; const int64_t *ii, *jj;   /* points mode when ii != NULL */
+    int nthreads, tid;
+} bs_job_t;
+
+static void bs_element(const bs_job_t *j, int64_t m, int64_t n, uint16_t *d, double *r, double *s)
+{
+    const uint8_t *a = j->A + m * j->lda;
+    const uint8_t *b = j->B + n * j->ldb;
+    double acc = 0.0, sabs = 0.0;
+    for (int64_t k0 = 0; k0 < j->K; k0 += 128) {
+        int64_t k1 = k0 + 128 < j->K ? k0 + 128 : j->K;
+        int64_t kb = k0 / 128;
+        double part = 0.0, pabs = 0.0;
+        for (int64_t k = k0; k < k1; ++k) {
+            double p = j->dec_a[a[k]] * j->dec_b[b[k]];
+            part += p;
+            pabs += fabs(p);
+        }
+        double sc = e8m0_value(j->SA[kb * j->lds_a + m]) * e8m0_value(j->SB[(n / 128) * j->lds_b + kb]);
+        acc += part * sc;
+        sabs += pabs * fabs(sc);
+    }
+    *d = oracle_bf16_rne(acc);
+    if (r) *r = acc;
+    if (s) *s = sabs;
+}
+
+static void *bs_worker(void *p)
+{
+    bs_job_t *j = (bs_job_t *)p;
+    if (j->ii) {
+        for (int64_t q = j->tid; q < j->npts; q += j->nthreads)
+            bs_element(j, j->ii[q], j->jj[q], j->D + q, j->R ? j->R + q : NULL, j->S ? j->S + q : NULL);
+        return NULL;
+    }
+    for (int64_t m = j->tid; m < j->M; m += j->nthreads)
+        for (int64_t n = 0; n < j->N; ++n) {
+            int64_t o = m * j->ldd + n;
+            bs_element(j, m, n, j->D + o, j->R ? j->R + o : NULL, j->S ? j->S + o : NULL);
+        }
+    return NULL;
+}
+
+static int bs_run(bs_job_t *base, int a_fmt, int b_fmt, int nthreads)
+{
+    oracle_decode_table(a_fmt, base->dec_a);
+    oracle_decode_table(b_fmt, base->dec_b);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    bs_job_t *jobs = (bs_job_t *)malloc(sizeof(bs_job_t) * (size_t)nthreads);
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!jobs || !th) { free(jobs); free(th); return -2; }
+    int started = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = *base;
+        jobs[i].nthreads = nthreads;
+        jobs[i].tid = i;
+    }
+    for (int i = 1; i < nthreads; ++i)
+        if (pthread_create(&th[i], NULL, bs_worker, &jobs[i]) == 0) ++started;
+        else { jobs[i].tid = -1; }
+    bs_worker(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i)
+        if (jobs[i].tid >= 0) pthread_join(th[i], NULL);
+    /* a thread that failed to start: do its share here */
+    for (int i = 1; i < nthreads; ++i)
+        if (jobs[i].tid < 0) { jobs[i].tid = i; bs_worker(&jobs[i]); }
+    free(jobs); free(th);
+    (void)started;
+    return 0;
+}
+
+/* Block-scaled dense: D[M x N] (bf16 bits, row stride ldd).
+ *   scale_a: E8M0 codes, scale of (row m, K block kb) at scale_a[kb * lds_a + m]
+ *   scale_b: E8M0 codes, scale of (rows 128 nb .. 128 nb + 127, K block kb) at
+ *            scale_b[nb * lds_b + kb]
+ * R and S (row stride ldd) may be NULL; S is sum_k |a b| * scale.            */
+int oracle_gemm_nt_blockscaled(const uint8_t *A, int64_t lda, int a_fmt,
+                               const uint8_t *B, int64_t ldb, int b_fmt,
+                               const uint8_t *scale_a, int64_t lds_a,
+                               const uint8_t *scale_b, int64_t lds_b,
+                               uint16_t *D, int64_t ldd, double *R, double *S,
+                               int64_t M, int64_t N, int64_t K, int nthreads)
+{
+    if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || M < 0 || N < 0 || K < 0) return -1;
+    if (M == 0 || N == 0) return 0;
+    bs_job_t j;
+    memset(&j, 0, sizeof j);
+    j.A = A; j.B = B; j.SA = scale_a; j.SB = scale_b;
+    j.lda = lda; j.ldb = ldb; j.lds_a = lds_a; j.lds_b = lds_b;
+    j.M = M; j.N = N; j.K = K; j.D = D; j.R = R; j.S = S; j.ldd = ldd;
+    return bs_run(&j, a_fmt, b_fmt, nthreads);
+}
+
+/* Block-scaled dense, selected elements (ii[p], jj[p]) only.                 */
+int oracle_gemm_nt_blockscaled_points(const uint8_t *A, int64_t lda, int a_fmt,
+                                      const uint8_t *B, int64_t ldb, int b_fmt,
+                                      const uint8_t *scale_a, int64_t lds_a,
+                                      const uint8_t *scale_b, int64_t lds_b, int64_t K,
+                                      int64_t npts, const int64_t *ii, const int64_t *jj,
+                                      uint16_t *D, double *R, double *S, int nthreads)
+{
+    if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || K < 0 || npts < 0) return -1;
+    if (npts == 0) return 0;
+    bs_job_t j;
+    memset(&j, 0, sizeof j);
+    j.A = A; j.B = B; j.SA = scale_a; j.SB = scale_b;
+    j.lda = lda; j.ldb = ldb; j.lds_a = lds_a; j.lds_b = lds_b;
+    j.K = K; j.D = D; j.R = R; j.S = S; j.npts = npts; j.ii = ii; j.jj = jj;
+    return bs_run(&j, a_fmt, b_fmt, nthreads);
 }

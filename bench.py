@@ -8,7 +8,7 @@ HBM).  `value` is the whole-job rate over the timed steps.  The same run also
 times, each in its own timed loop: the masked grouped decode GEMM (G=32,
 cap=64, N=4096, K=7168, m_g ~ U{0..32}) against the HBM roofline, the
 contiguous grouped prefill GEMM, the 256^3 GEMM (latency), the E5M2 4096^3
-GEMM and the eight transformer-projection shapes.
+GEMM, the block-scaled 4096^3 GEMM and the eight transformer-projection shapes.
 
 The average launch duration of each leg is the interval between two HIP events
 recorded around its K back-to-back launches on the stream the kernels run on
@@ -117,6 +117,20 @@ def bench_dense(torch, f, w, steps, warmup, timer):
     t["tflops_kernel"] = flops / (t["kernel_ms_mean"] * 1e-3) / 1e12
     t["bytes"] = float(M * K + N * K + 2 * M * N)
     del a, b, out
+    return t
+
+
+def bench_blockscaled(torch, f, w, steps, warmup, timer):
+    a, b = dev(torch, w.A), dev(torch, w.B)
+    sa, sb = dev(torch, w.sa), dev(torch, w.sb)
+    M, N, K = w.shape
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: f.gemm_nt_blockscaled(a, b, sa, sb, out=out, a_dtype=w.a_fmt, b_dtype=w.b_fmt)
+    t = timer.run(fn, steps, warmup)
+    flops = 2.0 * M * N * K
+    t["flops"] = flops
+    t["tflops_kernel"] = flops / (t["kernel_ms_mean"] * 1e-3) / 1e12
+    del a, b, sa, sb, out
     return t
 
 
@@ -280,7 +294,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: dense masked contig small e5m2 proj copy (default: all)")
+                    help="subset of: dense masked contig small e5m2 blockscaled proj copy (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="write profiles/*_hbm_counters.txt from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
@@ -308,7 +322,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     timer = Timer(torch)
-    want = set(args.only) if args.only else {"dense", "masked", "contig", "small", "e5m2", "proj", "copy"}
+    want = set(args.only) if args.only else {"dense", "masked", "contig", "small", "e5m2", "blockscaled", "proj", "copy"}
     steps, warmup = args.steps, args.warmup
     extra = {}
 
@@ -327,6 +341,17 @@ def main():
                                     "kernel_ms_mean": r["kernel_ms_mean"],
                                     "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS}
         del w5
+    if "blockscaled" in want:
+        log("timing block-scaled dense 4096^3 E4M3 (power-of-two scales per 1x128 / 128x128 block)")
+        wbs = workloads.dense_blockscaled_square()
+        r = bench_blockscaled(torch, f, wbs, steps, warmup, timer)
+        extra["dense_4096_blockscaled"] = {
+            "workload": "dense 4096^3 E4M3, activations N(0,1) per 1x128 block and weights N(0,0.02) per "
+                        "128x128 block, each with its own power-of-two (E8M0) scale (seed 6)",
+            "tflops_kernel": r["tflops_kernel"], "kernel_ms_mean": r["kernel_ms_mean"],
+            "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS}
+        log(f"  {r['tflops_kernel']:.1f} TFLOP/s")
+        del wbs
     if "small" in want:
         log("timing dense 256^3")
         ws = workloads.dense_small()

@@ -38,7 +38,7 @@ class Plan(ctypes.Structure):
                 ("token_blocks", ctypes.c_int), ("workgroups", ctypes.c_int64)]
 
 
-SYMBOLS = ("fp8_gemm_nt", "fp8_grouped_gemm_masked", "fp8_grouped_gemm_contig",
+SYMBOLS = ("fp8_gemm_nt", "fp8_gemm_nt_blockscaled", "fp8_grouped_gemm_masked", "fp8_grouped_gemm_contig",
            "fp8_gemm_plan", "fp8_gemm_strerror", "fp8_gemm_abi_version")
 
 
@@ -53,6 +53,8 @@ def load_library(path: str = LIB_PATH):
     P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.fp8_gemm_nt.argtypes = [P, I64, I, P, I64, I, P, P, P, I64, I, I, I, P]
     lib.fp8_gemm_nt.restype = I
+    lib.fp8_gemm_nt_blockscaled.argtypes = [P, I64, I, P, I64, I, P, I64, P, I64, P, I64, I, I, I, P]
+    lib.fp8_gemm_nt_blockscaled.restype = I
     lib.fp8_grouped_gemm_masked.argtypes = [P, I, P, I, P, P, P, P, I, I, I, I, I, P]
     lib.fp8_grouped_gemm_masked.restype = I
     lib.fp8_grouped_gemm_contig.argtypes = [P, I, P, I, P, P, P, P, I, I, I, I, P]
@@ -152,6 +154,48 @@ def gemm_nt(a, b, scale_a, scale_b, out=None, a_dtype=None, b_dtype=None):
     _check(load_library().fp8_gemm_nt(a.data_ptr(), lda, fa, b.data_ptr(), ldb, fb,
                                       scale_a.data_ptr(), scale_b.data_ptr(), out.data_ptr(), ldd,
                                       M, N, K, _stream()))
+    return out
+
+
+def gemm_nt_blockscaled(a, b, scale_a, scale_b, out=None, a_dtype=None, b_dtype=None):
+    """D[M, N] = bf16(sum_kb 2^(ea-127) 2^(eb-127) a[M, K-block] . b[N, K-block]^T).
+
+    scale_a: uint8 E8M0 codes [ceil(K/128), M'] (M' >= M, M' % 4 == 0; element
+    [kb, m] scales row m over K block kb); scale_b: uint8 E8M0 codes
+    [ceil(N/128), KB'] (KB' >= ceil(K/128), KB' % 4 == 0; element [nb, kb]
+    scales rows 128 nb .. 128 nb + 127 over K block kb).  Both on the GPU with
+    unit stride along their second dimension.
+    """
+    torch = _torch()
+    fa = _fp8_code(a, a_dtype, "a")
+    fb = _fp8_code(b, b_dtype, "b")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} are not [M, K] and [N, K]")
+    if a.stride(1) != 1 or b.stride(1) != 1:
+        raise ValueError("a and b must be K-contiguous (stride(1) == 1)")
+    M, K = a.shape
+    N = b.shape[0]
+    kb, nb = (K + 127) // 128, (N + 127) // 128
+    for t, name, rows in ((scale_a, "scale_a", kb), (scale_b, "scale_b", nb)):
+        if t.dtype != torch.uint8 or t.dim() != 2 or t.shape[0] != rows or (t.shape[0] > 1 and t.stride(1) != 1):
+            raise ValueError(f"{name} must be a uint8 [{rows}, *] tensor with unit column stride")
+    if scale_a.shape[1] < M or scale_b.shape[1] < kb:
+        raise ValueError("scale_a needs >= M columns and scale_b >= ceil(K/128) columns")
+    _require_cuda(a, b, scale_a, scale_b)
+    if out is None:
+        n_pad = max(8, ((N + 7) // 8) * 8)
+        out = torch.empty((M, n_pad), dtype=torch.bfloat16, device=a.device)[:, :N]
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or (N > 1 and out.stride(1) != 1):
+        raise ValueError("out must be a [M, N] bfloat16 tensor with unit column stride")
+    _require_cuda(out)
+    lda = a.stride(0) if (M > 1 and K > 0) else max(16, ((K + 15) // 16) * 16)
+    ldb = b.stride(0) if (N > 1 and K > 0) else max(16, ((K + 15) // 16) * 16)
+    ldd = out.stride(0) if M > 1 else max(8, ((N + 7) // 8) * 8)
+    lds_a = scale_a.stride(0) if kb > 1 else max(4, ((scale_a.shape[1] + 3) // 4) * 4)
+    lds_b = scale_b.stride(0) if nb > 1 else max(4, ((scale_b.shape[1] + 3) // 4) * 4)
+    _check(load_library().fp8_gemm_nt_blockscaled(a.data_ptr(), lda, fa, b.data_ptr(), ldb, fb,
+                                                  scale_a.data_ptr(), lds_a, scale_b.data_ptr(), lds_b,
+                                                  out.data_ptr(), ldd, M, N, K, _stream()))
     return out
 
 

@@ -61,6 +61,15 @@ __device__ __forceinline__ void dma16(v4i srd, uint32_t voff, uint32_t lds_base)
                  : "memory", "m0");
 }
 
+// The same with 4 bytes per lane: lane l's dword lands at lds_base + 4 * l
+// (256 bytes per instruction).  Used for the block scales.
+__device__ __forceinline__ void dma4(v4i srd, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(srd), "s"(lds_base)
+                 : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N) (N < 64), leaving the other counters unconstrained.
 template <int N>
 __device__ __forceinline__ void vmcnt_wait() {
@@ -117,6 +126,21 @@ __device__ __forceinline__ v16f mfma32x32x64(v8i a, v8i b, v16f c) {
 template <int FA, int FB>
 __device__ __forceinline__ v4f mfma16x16x128(v8i a, v8i b, v4f c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
+}
+
+// The same with E8M0 block scales in byte 0 of sa / sb: each lane passes the
+// scale of the operand row it carries (row l % 32, or l % 16), and that scale
+// multiplies the row's products over the instruction's K range (a 32-element
+// part of it per lane pair; for scales constant over 128 K elements the split
+// does not matter).
+template <int FA, int FB>
+__device__ __forceinline__ v16f mfma32x32x64_s(v8i a, v8i b, v16f c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
+}
+
+template <int FA, int FB>
+__device__ __forceinline__ v4f mfma16x16x128_s(v8i a, v8i b, v4f c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
 }
 
 // BF16 round-to-nearest-even of four floats, packed little-endian.

@@ -141,6 +141,16 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
         out->workgroups = 2 * cdiv(m, 2 * kContigAlign) * cdiv(n, 256);
         return ok();
     }
+    if (op == 3) {
+        // Block-scaled dense: the tiled kernel at every M (block scales are
+        // applied per 128-byte K step of its ring).
+        if (m == 0 || n == 0) return ok();
+        out->variant = pick_dense_tile(m, n);
+        out->tile_m = out->variant == V_TILE_256x256 ? 256 : 128;
+        out->tile_n = 256;
+        out->workgroups = cdiv(m, out->tile_m) * cdiv(n, 256);
+        return ok();
+    }
     return fail(FP8G_ERR_ARG, "unknown op %d", op);
 }
 
@@ -169,11 +179,11 @@ int launch_status(const char *what) {
 // ---------------------------------------------------------------------------
 // Launch helpers: one instantiation per (operand formats, tile shape, mode).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int STAGES, int BK, int MODE>
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, int MODE, int SCL = 0>
 int launch_ring(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     const dim3 block(64 * WM * WN);
 #define FP8G_RING(FA, FB) \
-    hipLaunchKernelGGL((fp8g::ring_kernel<BM, BN, WM, WN, FA, FB, MODE, STAGES, BK>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((fp8g::ring_kernel<BM, BN, WM, WN, FA, FB, MODE, STAGES, BK, SCL>), grid, block, 0, s, p)
     if (fa == 0 && fb == 0) FP8G_RING(0, 0);
     else if (fa == 0 && fb == 1) FP8G_RING(0, 1);
     else if (fa == 1 && fb == 0) FP8G_RING(1, 0);
@@ -185,13 +195,13 @@ int launch_ring(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
 // Tile shapes of the tiled kernel: 256 x 256 with 8 waves (4 along M, 2 along
 // N) and a 2-slot ring of 128-byte K steps (128 KB of LDS); 128 x 256 with 8
 // waves (2 x 4) and a 3-slot ring (144 KB).
-template <int MODE>
+template <int MODE, int SCL = 0>
 int launch_tile256(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE>(fa, fb, p, grid, s);
+    return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE, SCL>(fa, fb, p, grid, s);
 }
-template <int MODE>
+template <int MODE, int SCL = 0>
 int launch_tile128(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    return launch_ring<128, 256, TILE128_WM, TILE128_WN, T128_ST, T128_BK, MODE>(fa, fb, p, grid, s);
+    return launch_ring<128, 256, TILE128_WM, TILE128_WN, T128_ST, T128_BK, MODE, SCL>(fa, fb, p, grid, s);
 }
 
 template <int CB, int MODE>
@@ -350,6 +360,47 @@ int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dty
     p.tiles_m = (int)cdiv(M_total, 2 * kContigAlign);
     p.tiles_n = (int)cdiv(N, 256);
     return launch_tile256<fp8g::MODE_CONTIG>(a_dtype, b_dtype, p, dim3((unsigned)plan.workgroups), s);
+}
+
+int fp8_gemm_nt_blockscaled(const void *A, int64_t lda, int a_dtype, const void *B, int64_t ldb, int b_dtype,
+                            const uint8_t *scale_a, int64_t lds_a, const uint8_t *scale_b, int64_t lds_b,
+                            void *D, int64_t ldd, int M, int N, int K, void *stream) {
+    if (!dtype_ok(a_dtype) || !dtype_ok(b_dtype)) return fail(FP8G_ERR_DTYPE, "dtypes %d, %d", a_dtype, b_dtype);
+    fp8g_plan plan;
+    int st = plan_impl(3, M, N, K, 1, 0, &plan);
+    if (st != FP8G_OK) return st;
+    if (plan.variant == V_NONE) return ok();
+    if ((K > 0 && (!A || !B || !scale_a || !scale_b)) || !D)
+        return fail(FP8G_ERR_NULL, "A, B, scale_a, scale_b (unless K = 0) and D are required");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return fail(FP8G_ERR_ALIGN, "A, B and D must be 16-byte aligned");
+    if (!aligned4(scale_a) || !aligned4(scale_b)) return fail(FP8G_ERR_ALIGN, "scale arrays must be 4-byte aligned");
+    if (lda < K || ldb < K) return fail(FP8G_ERR_STRIDE, "lda=%lld / ldb=%lld below K=%d", (long long)lda, (long long)ldb, K);
+    if (lda % 16 || ldb % 16) return fail(FP8G_ERR_ALIGN, "lda=%lld / ldb=%lld not multiples of 16 bytes", (long long)lda, (long long)ldb);
+    if (lda > kMaxRowStride || ldb > kMaxRowStride) return fail(FP8G_ERR_STRIDE, "row stride above %lld bytes", (long long)kMaxRowStride);
+    if (ldd < N) return fail(FP8G_ERR_STRIDE, "ldd=%lld below N=%d", (long long)ldd, N);
+    if (ldd % 8) return fail(FP8G_ERR_ALIGN, "ldd=%lld not a multiple of 8 elements", (long long)ldd);
+    const int64_t kb = cdiv(K, 128), nb = cdiv(N, 128);
+    if (lds_a < M || lds_b < kb) return fail(FP8G_ERR_STRIDE, "lds_a=%lld below M=%d or lds_b=%lld below ceil(K/128)=%lld",
+                                             (long long)lds_a, M, (long long)lds_b, (long long)kb);
+    if (lds_a % 4 || lds_b % 4) return fail(FP8G_ERR_ALIGN, "lds_a=%lld / lds_b=%lld not multiples of 4", (long long)lds_a, (long long)lds_b);
+    if (kb * lds_a > INT32_MAX - 256 || nb * lds_b > INT32_MAX - 256)
+        return fail(FP8G_ERR_STRIDE, "scale arrays above 2^31 bytes");
+    if ((st = check_device()) != FP8G_OK) return st;
+
+    GemmParams p = {};
+    p.A = static_cast<const uint8_t *>(A);
+    p.B = static_cast<const uint8_t *>(B);
+    p.D = static_cast<uint16_t *>(D);
+    p.lda = lda; p.ldb = ldb; p.ldd = ldd;
+    p.M = M; p.N = N; p.K = K; p.G = 1; p.cap = M;
+    p.sfa = scale_a; p.sfb = scale_b; p.lds_sa = lds_a; p.lds_sb = lds_b;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int fa = a_dtype, fb = b_dtype;
+    p.tiles_m = (int)cdiv(M, plan.tile_m);
+    p.tiles_n = (int)cdiv(N, plan.tile_n);
+    const dim3 grid((unsigned)plan.workgroups);
+    if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE, 1>(fa, fb, p, grid, s);
+    return launch_tile128<fp8g::MODE_DENSE, 1>(fa, fb, p, grid, s);
 }
 
 }  // extern "C"

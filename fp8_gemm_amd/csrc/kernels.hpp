@@ -44,6 +44,11 @@ struct GemmParams {
     const int32_t *masked_m;   // masked: [G]
     const int32_t *grp_idx;    // contiguous: [M]
     int tiles_m, tiles_n;      // tile grid of one group
+    // Block scales (block-scaled dense form): E8M0 codes; sfa[kb * lds_sa + m]
+    // scales row m over K block kb (128 elements), sfb[nb * lds_sb + kb] rows
+    // 128 nb .. 128 nb + 127 of B over K block kb.
+    const uint8_t *sfa, *sfb;
+    int64_t lds_sa, lds_sb;
 };
 
 // ---------------------------------------------------------------------------
@@ -110,7 +115,7 @@ __device__ __forceinline__ uint32_t ring_key(uint32_t row) {
     return BK == 128 ? ((row & 7u) ^ ((row >> 3) & 1u)) : swz64_key(row);
 }
 
-template <int BM, int BN, int WM, int WN, int FA, int FB, int MODE, int STAGES, int BK>
+template <int BM, int BN, int WM, int WN, int FA, int FB, int MODE, int STAGES, int BK, int SCL>
 __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     constexpr int WAVES = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -125,7 +130,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "wave tile");
     static_assert(STAGES >= 2 && CPW * (STAGES - 2) < 64, "ring depth");
     constexpr int STAGE_OUT = BM * BN * 2;         // BF16 output tile staged for the stores
-    constexpr int SMEM = STAGES * SLOT > STAGE_OUT ? STAGES * SLOT : STAGE_OUT;
+    // Block scales (SCL): per ring slot, the step's scale of each tile row of A
+    // (bytes 0..BM-1) and one dword per 128-row block of B (from byte 256).
+    static_assert(!SCL || (MODE == MODE_DENSE && BK == 128 && BM <= 256 && BN % 128 == 0),
+                  "block scales: dense form, 128-byte K steps");
+    constexpr int SCS = SCL ? 512 : 0;
+    constexpr int RING = STAGES * (SLOT + SCS);
+    constexpr int SMEM = RING > STAGE_OUT ? RING : STAGE_OUT;
     constexpr int THREADS = 64 * WAVES;
     constexpr int OCH = BN / 8;                    // 16-byte chunks per staged output row
     static_assert(OCH == 32 || OCH == 16, "staged row width");
@@ -207,7 +218,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 
     const uint8_t *a_base = p.A + (MODE == MODE_MASKED ? (int64_t)g * p.a_gstride : 0) + (int64_t)m0 * p.lda;
     const uint8_t *b_base = p.B + (int64_t)expert * p.b_gstride + (int64_t)n0 * p.ldb;
-    const float sc = p.scale_a[0] * p.scale_b[MODE == MODE_DENSE ? 0 : expert];
+    const float sc = SCL ? 1.0f : p.scale_a[0] * p.scale_b[MODE == MODE_DENSE ? 0 : expert];
 
     // Rows past rows_m / rows_n fall outside the descriptors: the DMA writes
     // zeros for them and issues no memory transaction.
@@ -244,9 +255,26 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
         dma16(isA ? srdA : srdB, in ? lo + rowoff : kOobOffset,
               lds0 + (kt % STAGES) * SLOT + (uint32_t)q * 1024u);
     };
+    // Block scales of step kt (wave 0): A's row scales, 4 rows per lane, and
+    // the scale dword holding K block kt of each 128-row block of B.  Rows
+    // past the scale array (or K blocks past the last) read zeros; rows past M
+    // may read other in-range bytes, which only reach outputs not written.
+    const v4i srdSA = SCL ? make_srd(p.sfa, (uint32_t)(((p.K + 127) / 128) * p.lds_sa)) : v4i{0, 0, 0, 0};
+    const v4i srdSB = SCL ? make_srd(p.sfb, (uint32_t)(((p.N + 127) / 128) * p.lds_sb)) : v4i{0, 0, 0, 0};
+    const uint32_t scl_base = lds0 + STAGES * SLOT;
+    auto issue_scales = [&](int kt) {
+        if (!SCL || wave != 0) return;
+        const uint32_t slot = scl_base + (uint32_t)(kt % STAGES) * SCS;
+        const bool ka = (kt < nk) && 4 * lane < BM;
+        dma4(srdSA, ka ? (uint32_t)(kt * p.lds_sa + m0 + 4 * lane) : kOobOffset, slot);
+        const bool kb = (kt < nk) && lane < BN / 128;
+        dma4(srdSB, kb ? (uint32_t)((n0 / 128 + lane) * p.lds_sb + (kt & ~3)) : kOobOffset, slot + 256);
+    };
+    constexpr int SCW = SCL ? 2 : 0;               // scale DMA instructions per step of wave 0
     auto issue = [&](int kt) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i) issue_one(kt, i);
+        issue_scales(kt);
     };
 
     // ---- fragment read offsets ----
@@ -296,6 +324,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
         if (q < FN) bf[q] = v;
         else af[q - FN] = v;
     };
+    // This lane's scales of step kt: the A row it carries in each column
+    // operand block, and the B block of this wave's rows (uniform).
+    int scA[FM], scB = 127, nscA[FM], nscB = 127;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) { scA[j] = 127; nscA[j] = 127; }
+    auto read_scales = [&](int kt) {
+        if (!SCL) return;
+        const uint8_t *slot = smem + STAGES * SLOT + (kt % STAGES) * SCS;
+#pragma unroll
+        for (int j = 0; j < FM; ++j) nscA[j] = slot[wm * TM + j * 32 + lrow];
+        nscB = slot[256 + 4 * ((wn * TN) / 128) + (kt & 3)];
+    };
     // One K half of MFMAs with other work spread between them: the fragments
     // of the next half (read_slot / read_h) and, when refill_kt >= 0, the DMA
     // refill of a ring slot.  Issued in bursts, LDS reads and DMA instructions
@@ -308,11 +348,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
                          const uint8_t *read_slot, int read_h, int refill_kt) {
 #pragma unroll
         for (int t = 0; t < NMF; ++t) {
-            acc[t / FM][t % FM] = mfma32x32x64<FB, FA>(bf[t / FM], af[t % FM], acc[t / FM][t % FM]);
+            if (SCL)
+                acc[t / FM][t % FM] = mfma32x32x64_s<FB, FA>(bf[t / FM], af[t % FM], acc[t / FM][t % FM],
+                                                             scB, scA[t % FM]);
+            else
+                acc[t / FM][t % FM] = mfma32x32x64<FB, FA>(bf[t / FM], af[t % FM], acc[t / FM][t % FM]);
+            if (SCL && t == 0 && refill_kt >= 0) read_scales(refill_kt - STAGES + 1);
             // fragments of the next half: NFR reads spread over the NMF MFMAs
 #pragma unroll
             for (int q = (t * NFR) / NMF; q < ((t + 1) * NFR) / NMF; ++q) read_frag(nb, na, read_slot, read_h, q);
             if (refill_kt >= 0) {
+                if (t == 0) issue_scales(refill_kt);
 #pragma unroll
                 for (int q = (t * CPW) / NMF; q < ((t + 1) * CPW) / NMF; ++q) issue_one(refill_kt, q);
             }
@@ -334,10 +380,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     v8i f0b[FN], f0a[FM], f1b[FN], f1a[FM];
 #pragma unroll
     for (int s = 0; s < STAGES; ++s) issue(s);
-    vmcnt_wait<CPW * (STAGES - 1)>();              // step 0 has landed (this wave's part)
+    if (SCL && wave == 0) vmcnt_wait<(CPW + SCW) * (STAGES - 1)>();   // step 0 has landed
+    else vmcnt_wait<CPW * (STAGES - 1)>();                            // (this wave's part)
     __syncthreads();
     read_frags(f0b, f0a, smem, 0);
+    read_scales(0);
     for (int kt = 0; kt < nk; ++kt) {
+        if (SCL) {
+#pragma unroll
+            for (int j = 0; j < FM; ++j) scA[j] = nscA[j];
+            scB = nscB;
+        }
         // Redefined each step so that the compiler forms the DMA offsets in
         // the loop instead of keeping one register per instruction live.
         asm volatile("" : "+v"(doA0), "+v"(doA1), "+v"(doB0), "+v"(doB1), "+v"(dkc0), "+v"(dkc1));
@@ -345,7 +398,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
         const uint8_t *nxt = smem + ((kt + 1) % STAGES) * SLOT;
         __builtin_amdgcn_sched_barrier(0);
         mma_mixed(f0b, f0a, f1b, f1a, cur, 1, -1);              // first half; reads the second
-        vmcnt_wait<CPW * (STAGES - 2)>();          // this wave's part of step kt + 1 has landed
+        if (SCL && wave == 0) vmcnt_wait<(CPW + SCW) * (STAGES - 2)>();
+        else vmcnt_wait<CPW * (STAGES - 2)>();     // this wave's part of step kt + 1 has landed
         __syncthreads();                           // everyone's has; step kt's slot is no longer read
         mma_mixed(f1b, f1a, f0b, f0a, nxt, 0, kt + STAGES);     // second half; reads step kt + 1's
                                                                 // first half, refills step kt's slot

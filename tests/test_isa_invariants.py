@@ -2,7 +2,7 @@
 repository's own kernels (CPU only: hipcc cross-compiles).
 
 * M0 is written only by the direct-to-LDS load helper, each write immediately
-  followed by its `buffer_load_dwordx4 ... lds`, and read by nothing else: the
+  followed by its `buffer_load_dword{,x4} ... lds`, and read by nothing else: the
   helper's inline assembly sets M0 itself, so no compiler-generated code may
   rely on M0 across it.
 * No kernel spills to scratch memory.
@@ -44,7 +44,7 @@ def test_m0_only_feeds_lds_dma(asm):
     for i, s in enumerate(lines):
         if re.search(r"\bm0\b", s):
             assert s.startswith("s_mov_b32 m0,"), f"unexpected use of M0: {s}"
-            assert i + 1 < len(lines) and lines[i + 1].startswith("buffer_load_dwordx4") \
+            assert i + 1 < len(lines) and re.match(r"buffer_load_dword(x4)? ", lines[i + 1]) \
                 and lines[i + 1].endswith(" lds"), f"M0 write not followed by an LDS DMA load: {s}"
             writes += 1
     assert writes > 0

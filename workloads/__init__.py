@@ -210,3 +210,61 @@ def contig_prefill():
     w = contig_random(8192, 8, 32, 4096, 7168, seed=5)
     w.name = "contig_prefill_T8192x8_G32_4096x7168"
     return w
+
+
+@dataclass
+class BlockScaled:
+    A: np.ndarray            # uint8 [M, K]
+    B: np.ndarray            # uint8 [N, K]
+    sa: np.ndarray           # uint8 E8M0 [ceil(K/128), lds_a]: row m over K block kb at [kb, m]
+    sb: np.ndarray           # uint8 E8M0 [ceil(N/128), lds_b]: rows 128nb.. over K block kb at [nb, kb]
+    a_fmt: int = E4M3
+    b_fmt: int = E4M3
+    name: str = ""
+
+    @property
+    def shape(self):
+        return self.A.shape[0], self.B.shape[0], self.A.shape[1]
+
+
+def _pow2_block_quantize(x, fmt, row_block):
+    """Quantize float32 x [R, K] to FP8 codes with one power-of-two scale per
+    block of row_block rows x 128 K: the scale is the smallest power of two
+    that brings the block's amax within the format's range (the UE8M0 scale
+    format rounds scales up to powers of two).  Returns (codes, E8M0 codes
+    [ceil(R/row_block), ceil(K/128)])."""
+    R, K = x.shape
+    rb, kb = (R + row_block - 1) // row_block, (K + 127) // 128
+    xp = np.zeros((rb * row_block, kb * 128), np.float32)
+    xp[:R, :K] = x
+    amax = np.abs(xp).reshape(rb, row_block, kb, 128).max(axis=(1, 3))
+    e = np.where(amax > 0, np.ceil(np.log2(np.maximum(amax, 1e-30) / FP8_MAX[fmt])), -127.0)
+    e = np.clip(e, -127, 127).astype(np.int32)
+    scaled = xp / np.exp2(np.repeat(np.repeat(e, row_block, axis=0), 128, axis=1)).astype(np.float32)
+    codes = quantize(scaled[:R, :K], fmt)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def dense_blockscaled(M, N, K, seed, a_fmt=E4M3, b_fmt=E4M3, std_a=1.0, std_b=0.02, lds_pad=0, pad_code=0):
+    """Block-scaled dense case: activations ~N(0, std_a) quantized per 1 x 128
+    block, weights ~N(0, std_b) per 128 x 128 block, each block with its own
+    power-of-two scale.  Scale arrays get lds_pad extra columns (rounded up to a
+    multiple of 4) filled with pad_code."""
+    rng = np.random.default_rng(seed)
+    A, ea = _pow2_block_quantize(_normal(rng, (M, K), std_a), a_fmt, 1)      # ea [M, KB]
+    B, eb = _pow2_block_quantize(_normal(rng, (N, K), std_b), b_fmt, 128)    # eb [NB, KB]
+    kb = (K + 127) // 128
+    lds_a = ((M + lds_pad + 3) // 4) * 4
+    lds_b = ((kb + lds_pad + 3) // 4) * 4
+    sa = np.full((kb, lds_a), pad_code, np.uint8)
+    sa[:, :M] = ea.T
+    sb = np.full((eb.shape[0], lds_b), pad_code, np.uint8)
+    sb[:, :kb] = eb
+    return BlockScaled(A, B, sa, sb, a_fmt, b_fmt, f"dense_bs_{M}x{N}x{K}_s{seed}")
+
+
+def dense_blockscaled_square(n=4096):
+    """4096^3 block-scaled E4M3 (activations N(0,1), weights N(0,0.02)); seed 6."""
+    w = dense_blockscaled(n, n, n, seed=6)
+    w.name = f"dense_blockscaled_{n}"
+    return w

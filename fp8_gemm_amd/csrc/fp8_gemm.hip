@@ -39,10 +39,7 @@ constexpr int kSwapMaxM = 64;                                  // swap-AB thresh
 #endif
 constexpr int kSwapWaveRows = SWAP_WAVE_ROWS;                  // weight rows per wave, grouped forms
 constexpr int kSwapTileN = 4 * kSwapWaveRows;                  // weight rows per workgroup, grouped forms
-// A dense problem is one group, so it takes narrower workgroups to spread N
-// over more of the 256 CUs.
-constexpr int kSwapDenseWaveRows = 32;
-constexpr int kSwapDenseTileN = 4 * kSwapDenseWaveRows;
+constexpr int kDecodeRows = 16;                                // weight rows per decode workgroup
 constexpr int kSwapDepth = SWAP_DEPTH;                         // K blocks of loads in flight + 1
 constexpr int kContigAlign = 128;                              // row alignment of experts (contiguous form)
 #ifndef TILE128_WM
@@ -71,7 +68,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---------------------------------------------------------------------------
 // Shape-class choice.
 // ---------------------------------------------------------------------------
-enum Variant { V_NONE = 0, V_TILE_256x256 = 1, V_TILE_128x256 = 2, V_SWAP = 3 };
+enum Variant { V_NONE = 0, V_TILE_256x256 = 1, V_TILE_128x256 = 2, V_SWAP = 3, V_DECODE = 4 };
 
 int token_blocks_for(int m) {
     if (m <= 16) return 1;
@@ -98,11 +95,11 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
     if (op == 0) {
         if (m == 0 || n == 0) return ok();
         if (m <= kSwapMaxM) {
-            out->variant = V_SWAP;
+            out->variant = V_DECODE;
             out->tile_m = 16 * token_blocks_for(m);
-            out->tile_n = kSwapDenseTileN;
+            out->tile_n = kDecodeRows;
             out->token_blocks = token_blocks_for(m);
-            out->workgroups = cdiv(n, kSwapDenseTileN);
+            out->workgroups = cdiv(n, kDecodeRows);
         } else {
             out->variant = pick_dense_tile(m, n);
             out->tile_m = out->variant == V_TILE_256x256 ? 256 : 128;
@@ -142,9 +139,17 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
         return ok();
     }
     if (op == 3) {
-        // Block-scaled dense: the tiled kernel at every M (block scales are
-        // applied per 128-byte K step of its ring).
+        // Block-scaled dense: the decode kernel for few tokens, else the tiled
+        // kernel (block scales applied per 128-byte K step of its ring).
         if (m == 0 || n == 0) return ok();
+        if (m <= kSwapMaxM) {
+            out->variant = V_DECODE;
+            out->tile_m = 16 * token_blocks_for(m);
+            out->tile_n = kDecodeRows;
+            out->token_blocks = token_blocks_for(m);
+            out->workgroups = cdiv(n, kDecodeRows);
+            return ok();
+        }
         out->variant = pick_dense_tile(m, n);
         out->tile_m = out->variant == V_TILE_256x256 ? 256 : 128;
         out->tile_n = 256;
@@ -208,8 +213,7 @@ template <int CB, int MODE>
 int launch_swap_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     const dim3 block(256);
 #define FP8G_SWAP(FA, FB) \
-    hipLaunchKernelGGL((fp8g::swap_kernel<MODE == fp8g::MODE_DENSE ? kSwapDenseWaveRows : kSwapWaveRows, CB, FA, FB, \
-                                          kSwapDepth, MODE>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((fp8g::swap_kernel<kSwapWaveRows, CB, FA, FB, kSwapDepth, MODE>), grid, block, 0, s, p)
     if (fa == 0 && fb == 0) FP8G_SWAP(0, 0);
     else if (fa == 0 && fb == 1) FP8G_SWAP(0, 1);
     else if (fa == 1 && fb == 0) FP8G_SWAP(1, 0);
@@ -223,6 +227,32 @@ int launch_swap(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipStrea
     if (cb == 1) return launch_swap_cb<1, MODE>(fa, fb, p, grid, s);
     if (cb == 2) return launch_swap_cb<2, MODE>(fa, fb, p, grid, s);
     return launch_swap_cb<4, MODE>(fa, fb, p, grid, s);
+}
+
+// Decode kernel: steps of loads in flight per wave, fewer with more token
+// blocks (their registers grow with the token count), so that two
+// workgroups fit on a CU (at most 128 VGPRs): one workgroup's load latency
+// then overlaps another's streaming (measured better than deeper pipelines
+// with one workgroup per CU).
+template <int CB, int SCL>
+int launch_decode_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    constexpr int DEPTH = CB == 1 ? 4 : (CB == 2 ? 3 : 2);
+    const dim3 block(512);
+#define FP8G_DEC(FA, FB) \
+    hipLaunchKernelGGL((fp8g::decode_kernel<CB, FA, FB, DEPTH, SCL>), grid, block, 0, s, p)
+    if (fa == 0 && fb == 0) FP8G_DEC(0, 0);
+    else if (fa == 0 && fb == 1) FP8G_DEC(0, 1);
+    else if (fa == 1 && fb == 0) FP8G_DEC(1, 0);
+    else FP8G_DEC(1, 1);
+#undef FP8G_DEC
+    return launch_status("decode kernel");
+}
+
+template <int SCL>
+int launch_decode(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    if (cb == 1) return launch_decode_cb<1, SCL>(fa, fb, p, grid, s);
+    if (cb == 2) return launch_decode_cb<2, SCL>(fa, fb, p, grid, s);
+    return launch_decode_cb<4, SCL>(fa, fb, p, grid, s);
 }
 
 }  // namespace
@@ -283,11 +313,8 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t 
     p.scale_a = scale_a; p.scale_b = scale_b;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int fa = a_dtype, fb = b_dtype;
-    if (plan.variant == V_SWAP) {
-        p.tiles_m = 1;
-        p.tiles_n = (int)plan.workgroups;
-        return launch_swap<fp8g::MODE_DENSE>(plan.token_blocks, fa, fb, p, dim3((unsigned)plan.workgroups), s);
-    }
+    if (plan.variant == V_DECODE)
+        return launch_decode<0>(plan.token_blocks, fa, fb, p, dim3((unsigned)plan.workgroups), s);
     p.tiles_m = (int)cdiv(M, plan.tile_m);
     p.tiles_n = (int)cdiv(N, plan.tile_n);
     const dim3 grid((unsigned)plan.workgroups);
@@ -396,9 +423,10 @@ int fp8_gemm_nt_blockscaled(const void *A, int64_t lda, int a_dtype, const void 
     p.sfa = scale_a; p.sfb = scale_b; p.lds_sa = lds_a; p.lds_sb = lds_b;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int fa = a_dtype, fb = b_dtype;
+    const dim3 grid((unsigned)plan.workgroups);
+    if (plan.variant == V_DECODE) return launch_decode<1>(plan.token_blocks, fa, fb, p, grid, s);
     p.tiles_m = (int)cdiv(M, plan.tile_m);
     p.tiles_n = (int)cdiv(N, plan.tile_n);
-    const dim3 grid((unsigned)plan.workgroups);
     if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE, 1>(fa, fb, p, grid, s);
     return launch_tile128<fp8g::MODE_DENSE, 1>(fa, fb, p, grid, s);
 }

@@ -622,4 +622,109 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode kernel: the dense form with few tokens (M <= 64), swap-AB.
+// One workgroup of 8 waves per 16 weight rows (N = 4096 gives 256 workgroups);
+// the 128-byte K steps go round-robin to the waves, so at any time a
+// workgroup reads 8 consecutive K blocks of its rows.  Each wave streams its
+// weight rows and the matching token rows straight into registers in the
+// 16x16x128 operand layout, DEPTH steps ahead, and the 8 partial sums meet in
+// LDS at the end.  Splitting K inside the workgroup is what gives a small-N
+// problem enough workgroups and loads in flight to stream the weights at HBM
+// rate ("One transpose, half the compute: the DeepSeek SwapAB story", section
+// 1.1: with few tokens the work is weight-bandwidth bound).  The loads are
+// plain buffer loads, so the compiler derives every wait itself.
+// ---------------------------------------------------------------------------
+template <int CB, int FA, int FB, int DEPTH, int SCL>
+__global__ __launch_bounds__(512, 4) void decode_kernel(GemmParams p) {   // 4 waves per SIMD: two workgroups per CU
+    constexpr int W = 8;
+    __shared__ __attribute__((aligned(16))) v4f red[W][CB][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n0 = blockIdx.x * 16;
+    const int rows_w = min(p.N - n0, 16);
+    const int r16 = lane & 15;
+    const int kg = lane >> 4;
+    // Rows past N (weights) or past M (tokens) are outside the descriptors
+    // and read zeros without touching memory.
+    const __amdgpu_buffer_rsrc_t rsW = make_rsrc(p.B + (int64_t)n0 * p.ldb, rows_bytes(rows_w, p.ldb));
+    const __amdgpu_buffer_rsrc_t rsT = make_rsrc(p.A, rows_bytes(p.M, p.lda));
+    const uint32_t w_off = (uint32_t)r16 * (uint32_t)p.ldb + kg * 16;
+    uint32_t t_off[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) t_off[c] = (uint32_t)(c * 16 + r16) * (uint32_t)p.lda + kg * 16;
+    const int nk = (p.K + 127) / 128;
+    const int my = nk > wave ? (nk - wave + W - 1) / W : 0;   // steps kt = wave + W s of this wave
+    // Block scales: the weight block's scale is the same for every lane.
+    const __amdgpu_buffer_rsrc_t rsSA = make_rsrc(SCL ? p.sfa : p.A, SCL ? (uint32_t)(nk * p.lds_sa) : 0u);
+    const __amdgpu_buffer_rsrc_t rsSB = make_rsrc(SCL ? p.sfb : p.A, SCL ? (uint32_t)(((p.N + 127) / 128) * p.lds_sb) : 0u);
+
+    // (the scale arrays are below 2^31 bytes, so 32-bit offsets suffice)
+    const uint32_t lsa = (uint32_t)p.lds_sa, sb_row = (uint32_t)(n0 / 128) * (uint32_t)p.lds_sb;
+    v4u wr[DEPTH][2], tr[DEPTH][CB][2];
+    int ssa[DEPTH][CB], ssb[DEPTH];
+    // Lane (r16, kg) holds bytes kg*16 and 64 + kg*16 of each 128-byte K block
+    // of its row, for the weights and for each token block alike.
+    auto load = [&](int d, int s) {
+        const int kt = wave + W * s;
+        const uint32_t k0 = (uint32_t)kt * 128u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bool in = (s < my) && (int)(k0 + h * 64 + kg * 16) < p.K;
+            wr[d][h] = load16(rsW, in ? w_off + k0 + h * 64 : kOobOffset);
+#pragma unroll
+            for (int c = 0; c < CB; ++c) tr[d][c][h] = load16(rsT, in ? t_off[c] + k0 + h * 64 : kOobOffset);
+        }
+        if (SCL) {
+            const bool in = s < my;
+            ssb[d] = __builtin_amdgcn_raw_buffer_load_b8(rsSB, in ? sb_row + (uint32_t)kt : kOobOffset, 0, 0);
+            const uint32_t row0 = (uint32_t)kt * lsa + (uint32_t)r16;
+#pragma unroll
+            for (int c = 0; c < CB; ++c)
+                ssa[d][c] = __builtin_amdgcn_raw_buffer_load_b8(rsSA, in ? row0 + c * 16 : kOobOffset, 0, 0);
+        }
+    };
+
+    v4f acc[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) acc[c] = (v4f){0, 0, 0, 0};
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load(d, d);
+    for (int s0 = 0; s0 < my; s0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const v8i wf = pack8(wr[d][0], wr[d][1]);
+#pragma unroll
+            for (int c = 0; c < CB; ++c) {
+                const v8i tf = pack8(tr[d][c][0], tr[d][c][1]);
+                if (SCL) acc[c] = mfma16x16x128_s<FB, FA>(wf, tf, acc[c], ssb[d], ssa[d][c]);
+                else acc[c] = mfma16x16x128<FB, FA>(wf, tf, acc[c]);
+            }
+            load(d, s0 + d + DEPTH);               // steps past this wave's last read zeros, untouched memory
+            __builtin_amdgcn_sched_barrier(0);     // keep each step's consume-then-refill order
+        }
+    }
+
+    // Sum the 8 partial accumulators (fixed order), then scale, round and
+    // store: register q of a 16x16 block holds weight row 4 * kg + q and token
+    // column r16, so a lane writes four consecutive outputs of one token row.
+#pragma unroll
+    for (int c = 0; c < CB; ++c) red[wave][c][lane] = acc[c];
+    __syncthreads();
+    if (wave < CB) {
+        const int c = wave;
+        v4f sum = red[0][c][lane];
+#pragma unroll
+        for (int w = 1; w < W; ++w) sum += red[w][c][lane];
+        const float sc = SCL ? 1.0f : p.scale_a[0] * p.scale_b[0];
+        const int tok = c * 16 + r16;
+        if (tok < p.M) {
+            const int n = n0 + kg * 4;
+            const v2u v = pack_bf16x4(sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc);
+            store_bf16x4(p.D + (int64_t)tok * p.ldd, n, p.N - n, v);
+        }
+    }
+}
+
 }  // namespace fp8g

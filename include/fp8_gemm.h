@@ -79,7 +79,7 @@ typedef enum {
  *   scale_a, scale_b: one FP32 each (device).
  *   D: [M x N] BF16, row stride ldd elements.
  *   D[i][j] = bf16_rne( (scale_a * scale_b) * sum_k A[i][k] * B[j][k] ).
- * M <= 64 takes the swapped (weights-on-rows, tokens-on-columns) streaming
+ * M <= 64 takes the swapped (weights-on-rows, tokens-on-columns) decode
  * kernel; larger M takes the LDS-tiled kernel.  The choice never changes
  * which elements are written.
  */
@@ -108,8 +108,8 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype,
  *   D[i][j] = bf16_rne( sum_kb 2^(ea(i,kb) - 127) * 2^(eb(j/128,kb) - 127)
  *                        * sum_{k in block kb} A[i][k] * B[j][k] ).
  * The scales are exact powers of two, applied to the products inside the
- * matrix-core instruction, so they cost no arithmetic.  Runs the LDS-tiled
- * kernel at every M.
+ * matrix-core instruction, so they cost no arithmetic.  M <= 64 takes the
+ * swapped decode kernel, larger M the LDS-tiled kernel.
  */
 int fp8_gemm_nt_blockscaled(const void *A, int64_t lda, int a_dtype,
                             const void *B, int64_t ldb, int b_dtype,
@@ -169,7 +169,9 @@ int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dty
  */
 typedef struct {
     int variant;        /* 1 = tiled 256x256, 2 = tiled 128x256 (m x n),
-                           3 = swapped streaming, 0 = nothing to launch */
+                           3 = swapped streaming (grouped forms),
+                           4 = swapped decode, K split over 8 waves (dense
+                           forms, m <= 64), 0 = nothing to launch */
     int tile_m;         /* rows of D per workgroup tile (tokens) */
     int tile_n;         /* columns of D per workgroup tile */
     int token_blocks;   /* swapped kernel: 16-token column blocks per pass */

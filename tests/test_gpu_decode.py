@@ -1,0 +1,82 @@
+"""GPU parity of the dense few-token (M <= 64) path, the swap-AB decode kernel
+with K split over 8 waves, against the CPU oracle, through the C ABI.
+
+Edges specific to it: fewer K blocks than waves (some waves have no work),
+a short last K block, N not a multiple of the 16 weight rows per workgroup,
+every token-block count (M = 1..64), mixed formats, and the block-scaled form.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._parity import check, gpu_bits, hw_allowance, hw_allowance_blockscaled
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E5M2 = 0, 1
+
+
+def _f():
+    import fp8_gemm_amd
+    return fp8_gemm_amd
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+@pytest.mark.parametrize("M,N,K,fa,fb", [
+    (1, 16, 16, E4M3, E4M3),          # one K chunk: 7 of 8 waves idle
+    (1, 4104, 7168, E4M3, E4M3),      # N tail inside a workgroup
+    (16, 100, 1040, E5M2, E4M3),      # 9 K blocks, the last 16 bytes
+    (17, 520, 384, E4M3, E5M2),       # two token blocks, 3 K blocks
+    (33, 264, 2048, E5M2, E5M2),      # four token blocks
+    (64, 4096, 1024, E4M3, E4M3),
+    (48, 40, 272, E4M3, E4M3),
+])
+def test_decode_matches_oracle(M, N, K, fa, fb):
+    w = workloads.dense_random(M, N, K, seed=M * 7 + N + K, a_fmt=fa, b_fmt=fb, scales=(0.75, 1.5))
+    assert _f().plan(0, M, N, K).variant == 4
+    print(f"[decode] M={M} N={N} K={K} fmt=({fa},{fb})", flush=True)
+    d = _f().gemm_nt(_dev(w.A), _dev(w.B), torch.tensor([w.sa], device="cuda"), torch.tensor([w.sb], device="cuda"),
+                     a_dtype=fa, b_dtype=fb)
+    torch.cuda.synchronize()
+    d = gpu_bits(d)
+    ref, r, s, _ = oracle.gemm_nt(w.A, w.B, fa, fb, w.sa, w.sb)
+    sc = abs(w.sa * w.sb)
+    check(d, r, s, sc, hw_allowance(w.A, w.B, fa, fb, sc, s), ref_bits=ref, what=f"decode {M}x{N}x{K}")
+
+
+def test_decode_all_ones_exact():
+    """A = B = 1.0: every output is exactly K (representable), for each token count."""
+    for M in (1, 16, 17, 32, 40, 64):
+        K = 2048 + 128 * (M % 3)
+        A = np.full((M, K), 0x38, np.uint8)
+        B = np.full((300, K), 0x38, np.uint8)
+        d = _f().gemm_nt(_dev(A), _dev(B), torch.ones(1, device="cuda"), torch.ones(1, device="cuda"),
+                         a_dtype=E4M3, b_dtype=E4M3)
+        torch.cuda.synchronize()
+        assert (d.float() == K).all(), M
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 300, 400), (17, 4096, 1152), (64, 520, 2000 - 2000 % 16)])
+def test_decode_blockscaled(M, N, K):
+    w = workloads.dense_blockscaled(M, N, K, seed=M + 3 * N + K, lds_pad=5, pad_code=255)
+    assert _f().plan(3, M, N, K).variant == 4
+    print(f"[decode bs] M={M} N={N} K={K}", flush=True)
+    d = _f().gemm_nt_blockscaled(_dev(w.A), _dev(w.B), _dev(w.sa), _dev(w.sb), a_dtype=E4M3, b_dtype=E4M3)
+    torch.cuda.synchronize()
+    d = gpu_bits(d)
+    ref, r, s = oracle.gemm_nt_blockscaled(w.A, w.B, w.sa, w.sb)
+    check(d, r, s, 1.0, hw_allowance_blockscaled(w.A, w.B, 0, 0, w.sa, w.sb, s), ref_bits=ref,
+          what=f"decode blockscaled {M}x{N}x{K}")
+
+
+def test_decode_deterministic():
+    w = workloads.dense_random(32, 4096, 7168, seed=77)
+    a, b = _dev(w.A), _dev(w.B)
+    one = torch.ones(1, device="cuda")
+    outs = [gpu_bits(_f().gemm_nt(a, b, one, one, a_dtype=E4M3, b_dtype=E4M3)) for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])

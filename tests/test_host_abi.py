@@ -52,9 +52,9 @@ def test_abi_version(f):
 @pytest.mark.parametrize("args,variant", [
     ((0, 4096, 4096, 4096), 1),          # large square: 256x256 tiles, one per CU
     ((0, 2048, 4096, 4096), 2),          # 128 tiles of 256x256 would leave half the CUs idle
-    ((0, 64, 4096, 7168), 3),            # M <= 64: swapped streaming kernel
+    ((0, 64, 4096, 7168), 4),            # M <= 64: swap-AB decode kernel
     ((0, 65, 4096, 7168), 2),
-    ((0, 1, 16, 16), 3),
+    ((0, 1, 16, 16), 4),
 ])
 def test_dense_plan(f, args, variant):
     p = f.plan(*args)
@@ -64,8 +64,8 @@ def test_dense_plan(f, args, variant):
 def test_dense_plan_grid(f):
     p = f.plan(0, 4096, 4096, 4096)
     assert (p.tile_m, p.tile_n, p.workgroups) == (256, 256, 256)
-    p = f.plan(0, 17, 4096, 7168)
-    assert p.token_blocks == 2 and p.tile_n == 128 and p.workgroups == 4096 // 128
+    p = f.plan(0, 17, 4096, 7168)                  # decode kernel: 16 weight rows per workgroup
+    assert p.token_blocks == 2 and p.tile_n == 16 and p.workgroups == 4096 // 16
 
 
 def test_masked_plan_uses_hint_not_results(f):
@@ -179,8 +179,8 @@ def test_contig_validation(f):
 def test_blockscaled_plan(f):
     p = f.plan(3, 4096, 4096, 4096)
     assert (p.variant, p.tile_m, p.workgroups) == (1, 256, 256)
-    p = f.plan(3, 17, 4096, 7168)                  # tiled at every M
-    assert p.variant == 2 and p.tile_m == 128 and p.workgroups == 16
+    p = f.plan(3, 17, 4096, 7168)                  # few tokens: the decode kernel
+    assert p.variant == 4 and p.tile_n == 16 and p.workgroups == 256
 
 
 def test_blockscaled_validation(f):

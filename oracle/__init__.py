@@ -20,7 +20,9 @@ documented at the top of ``fp8_oracle.c``:
   the DeepSeek SwapAB story", sections 2 and 3.1-3.3),
 * the block-scaled dense form: power-of-two (UE8M0) scales per 128-element K
   block, per row of A and per 128 rows of B (DeepGEMM on Hopper, section 5.2;
-  SwapAB story, section 5).
+  SwapAB story, section 5),
+* the per-channel form: a scale per row of A, a scale and a bias per output
+  channel (DeepGEMM on Hopper, section 5.2).
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against things other
 than itself: torch's FP8 conversions, exact rational arithmetic, closed forms,
@@ -82,6 +84,8 @@ def _load():
     lib.oracle_gemm_nt_blockscaled_points.argtypes = [P, I64, I, P, I64, I, P, I64, P, I64, I64,
                                                       I64, P, P, P, P, P, I]
     lib.oracle_gemm_nt_blockscaled_points.restype = I
+    lib.oracle_gemm_nt_channelwise.argtypes = [P, I64, I, P, I64, I, P, P, P, P, I64, P, P, I64, I64, I64]
+    lib.oracle_gemm_nt_channelwise.restype = I
     _lib = lib
     return lib
 
@@ -296,4 +300,36 @@ def gemm_nt_blockscaled_points(A, B, scale_a, scale_b, ii, jj, a_fmt=E4M3, b_fmt
                                                    _ptr(D), _ptr(R), _ptr(S), threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_gemm_nt_blockscaled_points failed ({rc})")
+    return D, R, S
+
+
+def _f32_or_none(v, n, name):
+    if v is None:
+        return None
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    if v.shape != (n,):
+        raise ValueError(f"{name} must have shape ({n},)")
+    return v
+
+
+def gemm_nt_channelwise(A, B, scale_a=None, scale_b=None, bias=None, a_fmt=E4M3, b_fmt=E4M3):
+    """D = bf16(scale_a[m] * scale_b[n] * A[m] . B[n] + bias[n]); any of the three
+    float32 vectors may be None (1, 1, 0).  Returns (D_bits, R, S) with
+    S = sum_k |a b| * |scale_a[m] scale_b[n]|."""
+    A = _u8(A)
+    B = _u8(B)
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A and B disagree on K")
+    sa = _f32_or_none(scale_a, M, "scale_a")
+    sb = _f32_or_none(scale_b, N, "scale_b")
+    bi = _f32_or_none(bias, N, "bias")
+    D = np.zeros((M, N), dtype=np.uint16)
+    R = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    rc = _load().oracle_gemm_nt_channelwise(_ptr(A), K, int(a_fmt), _ptr(B), K, int(b_fmt), _ptr(sa), _ptr(sb),
+                                            _ptr(bi), _ptr(D), N, _ptr(R), _ptr(S), M, N, K)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_nt_channelwise failed ({rc})")
     return D, R, S

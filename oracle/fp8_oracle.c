@@ -44,6 +44,11 @@
  *     accumulator: acc = sum_kb sa(m,kb) * sb(n/128,kb) * sum_{k in kb} a*b,
  *     all in FP64 (power-of-two scales make each product exact), blocks in
  *     order; the last K block may be shorter than 128.
+ *   - Per-channel scales and bias (DeepGEMM on Hopper, section 5.2: a scale per
+ *     channel instead of one per tensor; the bias term of a fused epilogue):
+ *     r = sa[m] * sb[n] * acc + bias[n] in FP64 (scale product first, then
+ *     the accumulator, then the bias), one BF16 rounding.  A missing scale
+ *     vector means 1, a missing bias 0.
  */
 #include <math.h>
 #include <pthread.h>
@@ -516,4 +521,38 @@ int oracle_gemm_nt_blockscaled_points(const uint8_t *A, int64_t lda, int a_fmt,
     j.lda = lda; j.ldb = ldb; j.lds_a = lds_a; j.lds_b = lds_b;
     j.K = K; j.D = D; j.R = R; j.S = S; j.npts = npts; j.ii = ii; j.jj = jj;
     return bs_run(&j, a_fmt, b_fmt, nthreads);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Dense GEMM with per-row / per-channel scales and a per-channel bias.       */
+/* ------------------------------------------------------------------------- */
+
+/* D[M x N] (bf16 bits, row stride ldd) = bf16(sa[m] * sb[n] * A[m] . B[n] + bias[n]).
+ * scale_a [M], scale_b [N], bias [N] may each be NULL (1, 1, 0).  R and S
+ * (row stride ldd) may be NULL; S = sum_k |a b| * |sa[m] * sb[n]|.           */
+int oracle_gemm_nt_channelwise(const uint8_t *A, int64_t lda, int a_fmt,
+                               const uint8_t *B, int64_t ldb, int b_fmt,
+                               const float *scale_a, const float *scale_b, const float *bias,
+                               uint16_t *D, int64_t ldd, double *R, double *S,
+                               int64_t M, int64_t N, int64_t K)
+{
+    if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || M < 0 || N < 0 || K < 0) return -1;
+    if (M == 0 || N == 0) return 0;
+    tables_t *t = (tables_t *)malloc(sizeof *t);
+    if (!t) return -2;
+    make_tables(t, a_fmt, b_fmt);
+    for (int64_t m = 0; m < M; ++m) {
+        double sam = scale_a ? (double)scale_a[m] : 1.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double acc, sabs;
+            dot(t, A + m * lda, B + n * ldb, K, &acc, &sabs, NULL);
+            double sc = sam * (scale_b ? (double)scale_b[n] : 1.0);
+            double r = sc * acc + (bias ? (double)bias[n] : 0.0);
+            D[m * ldd + n] = oracle_bf16_rne(r);
+            if (R) R[m * ldd + n] = r;
+            if (S) S[m * ldd + n] = sabs * fabs(sc);
+        }
+    }
+    free(t);
+    return 0;
 }

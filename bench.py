@@ -8,7 +8,8 @@ HBM).  `value` is the whole-job rate over the timed steps.  The same run also
 times, each in its own timed loop: the masked grouped decode GEMM (G=32,
 cap=64, N=4096, K=7168, m_g ~ U{0..32}) against the HBM roofline, the
 contiguous grouped prefill GEMM, the 256^3 GEMM (latency), the E5M2 4096^3
-GEMM, the block-scaled 4096^3 GEMM and the eight transformer-projection shapes.
+GEMM, the block-scaled and the per-channel 4096^3 GEMMs and the eight
+transformer-projection shapes.
 
 The average launch duration of each leg is the interval between two HIP events
 recorded around its K back-to-back launches on the stream the kernels run on
@@ -131,6 +132,23 @@ def bench_blockscaled(torch, f, w, steps, warmup, timer):
     t["flops"] = flops
     t["tflops_kernel"] = flops / (t["kernel_ms_mean"] * 1e-3) / 1e12
     del a, b, sa, sb, out
+    return t
+
+
+def bench_channelwise(torch, f, w, steps, warmup, timer):
+    import numpy as np
+
+    M, N, K = w.shape
+    rng = np.random.default_rng(12)
+    a, b = dev(torch, w.A), dev(torch, w.B)
+    sa = dev(torch, rng.uniform(0.5, 2, M).astype(np.float32))
+    sb = dev(torch, rng.uniform(0.5, 2, N).astype(np.float32))
+    bias = dev(torch, rng.normal(0, 1, N).astype(np.float32))
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: f.gemm_nt_channelwise(a, b, sa, sb, bias, out=out, a_dtype=w.a_fmt, b_dtype=w.b_fmt)
+    t = timer.run(fn, steps, warmup)
+    t["tflops_kernel"] = 2.0 * M * N * K / (t["kernel_ms_mean"] * 1e-3) / 1e12
+    del a, b, sa, sb, bias, out
     return t
 
 
@@ -294,7 +312,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: dense masked contig small e5m2 blockscaled proj copy (default: all)")
+                    help="subset of: dense masked contig small e5m2 blockscaled channelwise proj copy (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="write profiles/*_hbm_counters.txt from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
@@ -322,7 +340,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     timer = Timer(torch)
-    want = set(args.only) if args.only else {"dense", "masked", "contig", "small", "e5m2", "blockscaled", "proj", "copy"}
+    want = set(args.only) if args.only else {"dense", "masked", "contig", "small", "e5m2", "blockscaled", "channelwise", "proj", "copy"}
     steps, warmup = args.steps, args.warmup
     extra = {}
 
@@ -352,6 +370,15 @@ def main():
             "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS}
         log(f"  {r['tflops_kernel']:.1f} TFLOP/s")
         del wbs
+    if "channelwise" in want:
+        log("timing dense 4096^3 E4M3 with per-row / per-channel scales and a per-channel bias")
+        r = bench_channelwise(torch, f, wd, steps, warmup, timer)
+        extra["dense_4096_channelwise"] = {
+            "workload": "dense 4096^3 E4M3 (seed 2 operands), row scales and channel scales U[0.5,2], "
+                        "bias N(0,1), applied in the epilogue",
+            "tflops_kernel": r["tflops_kernel"], "kernel_ms_mean": r["kernel_ms_mean"],
+            "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS}
+        log(f"  {r['tflops_kernel']:.1f} TFLOP/s")
     if "small" in want:
         log("timing dense 256^3")
         ws = workloads.dense_small()

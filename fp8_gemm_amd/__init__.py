@@ -38,7 +38,7 @@ class Plan(ctypes.Structure):
                 ("token_blocks", ctypes.c_int), ("workgroups", ctypes.c_int64)]
 
 
-SYMBOLS = ("fp8_gemm_nt", "fp8_gemm_nt_blockscaled", "fp8_grouped_gemm_masked", "fp8_grouped_gemm_contig",
+SYMBOLS = ("fp8_gemm_nt", "fp8_gemm_nt_blockscaled", "fp8_gemm_nt_channelwise", "fp8_grouped_gemm_masked", "fp8_grouped_gemm_contig",
            "fp8_gemm_plan", "fp8_gemm_strerror", "fp8_gemm_abi_version")
 
 
@@ -55,6 +55,8 @@ def load_library(path: str = LIB_PATH):
     lib.fp8_gemm_nt.restype = I
     lib.fp8_gemm_nt_blockscaled.argtypes = [P, I64, I, P, I64, I, P, I64, P, I64, P, I64, I, I, I, P]
     lib.fp8_gemm_nt_blockscaled.restype = I
+    lib.fp8_gemm_nt_channelwise.argtypes = [P, I64, I, P, I64, I, P, P, P, P, I64, I, I, I, P]
+    lib.fp8_gemm_nt_channelwise.restype = I
     lib.fp8_grouped_gemm_masked.argtypes = [P, I, P, I, P, P, P, P, I, I, I, I, I, P]
     lib.fp8_grouped_gemm_masked.restype = I
     lib.fp8_grouped_gemm_contig.argtypes = [P, I, P, I, P, P, P, P, I, I, I, I, P]
@@ -196,6 +198,45 @@ def gemm_nt_blockscaled(a, b, scale_a, scale_b, out=None, a_dtype=None, b_dtype=
     _check(load_library().fp8_gemm_nt_blockscaled(a.data_ptr(), lda, fa, b.data_ptr(), ldb, fb,
                                                   scale_a.data_ptr(), lds_a, scale_b.data_ptr(), lds_b,
                                                   out.data_ptr(), ldd, M, N, K, _stream()))
+    return out
+
+
+def gemm_nt_channelwise(a, b, scale_a=None, scale_b=None, bias=None, out=None, a_dtype=None, b_dtype=None):
+    """D[M, N] = bf16(scale_a[m] * scale_b[n] * a[m] . b[n] + bias[n]).
+
+    scale_a: float32 [M] or None (1); scale_b, bias: float32 [N] or None (1, 0),
+    contiguous, on the GPU.
+    """
+    torch = _torch()
+    fa = _fp8_code(a, a_dtype, "a")
+    fb = _fp8_code(b, b_dtype, "b")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} are not [M, K] and [N, K]")
+    if a.stride(1) != 1 or b.stride(1) != 1:
+        raise ValueError("a and b must be K-contiguous (stride(1) == 1)")
+    M, K = a.shape
+    N = b.shape[0]
+    ptrs = []
+    for t, n, name in ((scale_a, M, "scale_a"), (scale_b, N, "scale_b"), (bias, N, "bias")):
+        if t is None:
+            ptrs.append(None)
+            continue
+        if t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor with {n} elements")
+        _require_cuda(t)
+        ptrs.append(t.data_ptr())
+    _require_cuda(a, b)
+    if out is None:
+        n_pad = max(8, ((N + 7) // 8) * 8)
+        out = torch.empty((M, n_pad), dtype=torch.bfloat16, device=a.device)[:, :N]
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or (N > 1 and out.stride(1) != 1):
+        raise ValueError("out must be a [M, N] bfloat16 tensor with unit column stride")
+    _require_cuda(out)
+    lda = a.stride(0) if (M > 1 and K > 0) else max(16, ((K + 15) // 16) * 16)
+    ldb = b.stride(0) if (N > 1 and K > 0) else max(16, ((K + 15) // 16) * 16)
+    ldd = out.stride(0) if M > 1 else max(8, ((N + 7) // 8) * 8)
+    _check(load_library().fp8_gemm_nt_channelwise(a.data_ptr(), lda, fa, b.data_ptr(), ldb, fb, ptrs[0], ptrs[1],
+                                                  ptrs[2], out.data_ptr(), ldd, M, N, K, _stream()))
     return out
 
 

@@ -314,7 +314,7 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int fa = a_dtype, fb = b_dtype;
     if (plan.variant == V_DECODE)
-        return launch_decode<0>(plan.token_blocks, fa, fb, p, dim3((unsigned)plan.workgroups), s);
+        return launch_decode<fp8g::SCALE_TENSOR>(plan.token_blocks, fa, fb, p, dim3((unsigned)plan.workgroups), s);
     p.tiles_m = (int)cdiv(M, plan.tile_m);
     p.tiles_n = (int)cdiv(N, plan.tile_n);
     const dim3 grid((unsigned)plan.workgroups);
@@ -424,11 +424,47 @@ int fp8_gemm_nt_blockscaled(const void *A, int64_t lda, int a_dtype, const void 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int fa = a_dtype, fb = b_dtype;
     const dim3 grid((unsigned)plan.workgroups);
-    if (plan.variant == V_DECODE) return launch_decode<1>(plan.token_blocks, fa, fb, p, grid, s);
+    if (plan.variant == V_DECODE) return launch_decode<fp8g::SCALE_BLOCK>(plan.token_blocks, fa, fb, p, grid, s);
     p.tiles_m = (int)cdiv(M, plan.tile_m);
     p.tiles_n = (int)cdiv(N, plan.tile_n);
-    if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE, 1>(fa, fb, p, grid, s);
-    return launch_tile128<fp8g::MODE_DENSE, 1>(fa, fb, p, grid, s);
+    if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE, fp8g::SCALE_BLOCK>(fa, fb, p, grid, s);
+    return launch_tile128<fp8g::MODE_DENSE, fp8g::SCALE_BLOCK>(fa, fb, p, grid, s);
+}
+
+int fp8_gemm_nt_channelwise(const void *A, int64_t lda, int a_dtype, const void *B, int64_t ldb, int b_dtype,
+                            const float *scale_a, const float *scale_b, const float *bias,
+                            void *D, int64_t ldd, int M, int N, int K, void *stream) {
+    if (!dtype_ok(a_dtype) || !dtype_ok(b_dtype)) return fail(FP8G_ERR_DTYPE, "dtypes %d, %d", a_dtype, b_dtype);
+    fp8g_plan plan;
+    int st = plan_impl(0, M, N, K, 1, 0, &plan);
+    if (st != FP8G_OK) return st;
+    if (plan.variant == V_NONE) return ok();
+    if ((K > 0 && (!A || !B)) || !D) return fail(FP8G_ERR_NULL, "A, B (unless K = 0) and D are required");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return fail(FP8G_ERR_ALIGN, "A, B and D must be 16-byte aligned");
+    if (!aligned4(scale_a) || !aligned16(scale_b) || !aligned16(bias))
+        return fail(FP8G_ERR_ALIGN, "scale_a must be 4-byte, scale_b and bias 16-byte aligned");
+    if (lda < K || ldb < K) return fail(FP8G_ERR_STRIDE, "lda=%lld / ldb=%lld below K=%d", (long long)lda, (long long)ldb, K);
+    if (lda % 16 || ldb % 16) return fail(FP8G_ERR_ALIGN, "lda=%lld / ldb=%lld not multiples of 16 bytes", (long long)lda, (long long)ldb);
+    if (lda > kMaxRowStride || ldb > kMaxRowStride) return fail(FP8G_ERR_STRIDE, "row stride above %lld bytes", (long long)kMaxRowStride);
+    if (ldd < N) return fail(FP8G_ERR_STRIDE, "ldd=%lld below N=%d", (long long)ldd, N);
+    if (ldd % 8) return fail(FP8G_ERR_ALIGN, "ldd=%lld not a multiple of 8 elements", (long long)ldd);
+    if ((st = check_device()) != FP8G_OK) return st;
+
+    GemmParams p = {};
+    p.A = static_cast<const uint8_t *>(A);
+    p.B = static_cast<const uint8_t *>(B);
+    p.D = static_cast<uint16_t *>(D);
+    p.lda = lda; p.ldb = ldb; p.ldd = ldd;
+    p.M = M; p.N = N; p.K = K; p.G = 1; p.cap = M;
+    p.ch_sa = scale_a; p.ch_sb = scale_b; p.bias = bias;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int fa = a_dtype, fb = b_dtype;
+    const dim3 grid((unsigned)plan.workgroups);
+    if (plan.variant == V_DECODE) return launch_decode<fp8g::SCALE_CHANNEL>(plan.token_blocks, fa, fb, p, grid, s);
+    p.tiles_m = (int)cdiv(M, plan.tile_m);
+    p.tiles_n = (int)cdiv(N, plan.tile_n);
+    if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE, fp8g::SCALE_CHANNEL>(fa, fb, p, grid, s);
+    return launch_tile128<fp8g::MODE_DENSE, fp8g::SCALE_CHANNEL>(fa, fb, p, grid, s);
 }
 
 }  // extern "C"

@@ -31,6 +31,10 @@
 namespace fp8g {
 
 enum { MODE_DENSE = 0, MODE_MASKED = 1, MODE_CONTIG = 2 };
+// Scale modes of the dense form: one scale per tensor, E8M0 block scales per
+// 128-element K block, or a scale per row of A and a scale and bias per output
+// channel applied in the epilogue.
+enum { SCALE_TENSOR = 0, SCALE_BLOCK = 1, SCALE_CHANNEL = 2 };
 
 struct GemmParams {
     const uint8_t *A;          // tokens: [m x K] rows of lda bytes (per group: + g * a_gstride)
@@ -49,7 +53,37 @@ struct GemmParams {
     // 128 nb .. 128 nb + 127 of B over K block kb.
     const uint8_t *sfa, *sfb;
     int64_t lds_sa, lds_sb;
+    // Per-channel form: row scales of A [M], channel scales [N] and bias [N]
+    // (each may be NULL: 1, 1, 0).
+    const float *ch_sa, *ch_sb, *bias;
 };
+
+// Epilogue terms of the per-channel form for four consecutive output channels
+// n .. n+3: their scales and biases.  Channels at or past N take scale 0 and
+// bias 0 (they are not stored).
+__device__ __forceinline__ void channel_terms(const GemmParams &p, int n, float (&s4)[4], float (&b4)[4]) {
+    if (n + 4 <= p.N) {
+        if (p.ch_sb) {
+            const v4f v = *reinterpret_cast<const v4f *>(p.ch_sb + n);
+            s4[0] = v[0]; s4[1] = v[1]; s4[2] = v[2]; s4[3] = v[3];
+        } else {
+            s4[0] = s4[1] = s4[2] = s4[3] = 1.0f;
+        }
+        if (p.bias) {
+            const v4f v = *reinterpret_cast<const v4f *>(p.bias + n);
+            b4[0] = v[0]; b4[1] = v[1]; b4[2] = v[2]; b4[3] = v[3];
+        } else {
+            b4[0] = b4[1] = b4[2] = b4[3] = 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool in = n + e < p.N;
+            s4[e] = in ? (p.ch_sb ? p.ch_sb[n + e] : 1.0f) : 0.0f;
+            b4[e] = in && p.bias ? p.bias[n + e] : 0.0f;
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Tile index -> (tm, tn) for the tiled kernel (dense and contiguous forms).
@@ -117,6 +151,7 @@ __device__ __forceinline__ uint32_t ring_key(uint32_t row) {
 
 template <int BM, int BN, int WM, int WN, int FA, int FB, int MODE, int STAGES, int BK, int SCL>
 __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
+    constexpr bool BLK = SCL == SCALE_BLOCK, CHN = SCL == SCALE_CHANNEL;
     constexpr int WAVES = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
@@ -130,11 +165,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "wave tile");
     static_assert(STAGES >= 2 && CPW * (STAGES - 2) < 64, "ring depth");
     constexpr int STAGE_OUT = BM * BN * 2;         // BF16 output tile staged for the stores
-    // Block scales (SCL): per ring slot, the step's scale of each tile row of A
+    // Block scales (BLK): per ring slot, the step's scale of each tile row of A
     // (bytes 0..BM-1) and one dword per 128-row block of B (from byte 256).
-    static_assert(!SCL || (MODE == MODE_DENSE && BK == 128 && BM <= 256 && BN % 128 == 0),
+    static_assert(!BLK || (MODE == MODE_DENSE && BK == 128 && BM <= 256 && BN % 128 == 0),
                   "block scales: dense form, 128-byte K steps");
-    constexpr int SCS = SCL ? 512 : 0;
+    static_assert(!CHN || MODE == MODE_DENSE, "per-channel scales: dense form");
+    constexpr int SCS = BLK ? 512 : 0;
     constexpr int RING = STAGES * (SLOT + SCS);
     constexpr int SMEM = RING > STAGE_OUT ? RING : STAGE_OUT;
     constexpr int THREADS = 64 * WAVES;
@@ -218,7 +254,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 
     const uint8_t *a_base = p.A + (MODE == MODE_MASKED ? (int64_t)g * p.a_gstride : 0) + (int64_t)m0 * p.lda;
     const uint8_t *b_base = p.B + (int64_t)expert * p.b_gstride + (int64_t)n0 * p.ldb;
-    const float sc = SCL ? 1.0f : p.scale_a[0] * p.scale_b[MODE == MODE_DENSE ? 0 : expert];
+    const float sc = SCL != SCALE_TENSOR ? 1.0f : p.scale_a[0] * p.scale_b[MODE == MODE_DENSE ? 0 : expert];
 
     // Rows past rows_m / rows_n fall outside the descriptors: the DMA writes
     // zeros for them and issues no memory transaction.
@@ -259,18 +295,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     // the scale dword holding K block kt of each 128-row block of B.  Rows
     // past the scale array (or K blocks past the last) read zeros; rows past M
     // may read other in-range bytes, which only reach outputs not written.
-    const v4i srdSA = SCL ? make_srd(p.sfa, (uint32_t)(((p.K + 127) / 128) * p.lds_sa)) : v4i{0, 0, 0, 0};
-    const v4i srdSB = SCL ? make_srd(p.sfb, (uint32_t)(((p.N + 127) / 128) * p.lds_sb)) : v4i{0, 0, 0, 0};
+    const v4i srdSA = BLK ? make_srd(p.sfa, (uint32_t)(((p.K + 127) / 128) * p.lds_sa)) : v4i{0, 0, 0, 0};
+    const v4i srdSB = BLK ? make_srd(p.sfb, (uint32_t)(((p.N + 127) / 128) * p.lds_sb)) : v4i{0, 0, 0, 0};
     const uint32_t scl_base = lds0 + STAGES * SLOT;
     auto issue_scales = [&](int kt) {
-        if (!SCL || wave != 0) return;
+        if (!BLK || wave != 0) return;
         const uint32_t slot = scl_base + (uint32_t)(kt % STAGES) * SCS;
         const bool ka = (kt < nk) && 4 * lane < BM;
         dma4(srdSA, ka ? (uint32_t)(kt * p.lds_sa + m0 + 4 * lane) : kOobOffset, slot);
         const bool kb = (kt < nk) && lane < BN / 128;
         dma4(srdSB, kb ? (uint32_t)((n0 / 128 + lane) * p.lds_sb + (kt & ~3)) : kOobOffset, slot + 256);
     };
-    constexpr int SCW = SCL ? 2 : 0;               // scale DMA instructions per step of wave 0
+    constexpr int SCW = BLK ? 2 : 0;               // scale DMA instructions per step of wave 0
     auto issue = [&](int kt) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i) issue_one(kt, i);
@@ -330,7 +366,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) { scA[j] = 127; nscA[j] = 127; }
     auto read_scales = [&](int kt) {
-        if (!SCL) return;
+        if (!BLK) return;
         const uint8_t *slot = smem + STAGES * SLOT + (kt % STAGES) * SCS;
 #pragma unroll
         for (int j = 0; j < FM; ++j) nscA[j] = slot[wm * TM + j * 32 + lrow];
@@ -348,12 +384,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
                          const uint8_t *read_slot, int read_h, int refill_kt) {
 #pragma unroll
         for (int t = 0; t < NMF; ++t) {
-            if (SCL)
+            if (BLK)
                 acc[t / FM][t % FM] = mfma32x32x64_s<FB, FA>(bf[t / FM], af[t % FM], acc[t / FM][t % FM],
                                                              scB, scA[t % FM]);
             else
                 acc[t / FM][t % FM] = mfma32x32x64<FB, FA>(bf[t / FM], af[t % FM], acc[t / FM][t % FM]);
-            if (SCL && t == 0 && refill_kt >= 0) read_scales(refill_kt - STAGES + 1);
+            if (BLK && t == 0 && refill_kt >= 0) read_scales(refill_kt - STAGES + 1);
             // fragments of the next half: NFR reads spread over the NMF MFMAs
 #pragma unroll
             for (int q = (t * NFR) / NMF; q < ((t + 1) * NFR) / NMF; ++q) read_frag(nb, na, read_slot, read_h, q);
@@ -380,13 +416,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     v8i f0b[FN], f0a[FM], f1b[FN], f1a[FM];
 #pragma unroll
     for (int s = 0; s < STAGES; ++s) issue(s);
-    if (SCL && wave == 0) vmcnt_wait<(CPW + SCW) * (STAGES - 1)>();   // step 0 has landed
+    if (BLK && wave == 0) vmcnt_wait<(CPW + SCW) * (STAGES - 1)>();   // step 0 has landed
     else vmcnt_wait<CPW * (STAGES - 1)>();                            // (this wave's part)
     __syncthreads();
     read_frags(f0b, f0a, smem, 0);
     read_scales(0);
     for (int kt = 0; kt < nk; ++kt) {
-        if (SCL) {
+        if (BLK) {
 #pragma unroll
             for (int j = 0; j < FM; ++j) scA[j] = nscA[j];
             scB = nscB;
@@ -398,7 +434,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
         const uint8_t *nxt = smem + ((kt + 1) % STAGES) * SLOT;
         __builtin_amdgcn_sched_barrier(0);
         mma_mixed(f0b, f0a, f1b, f1a, cur, 1, -1);              // first half; reads the second
-        if (SCL && wave == 0) vmcnt_wait<(CPW + SCW) * (STAGES - 2)>();
+        if (BLK && wave == 0) vmcnt_wait<(CPW + SCW) * (STAGES - 2)>();
         else vmcnt_wait<CPW * (STAGES - 2)>();     // this wave's part of step kt + 1 has landed
         __syncthreads();                           // everyone's has; step kt's slot is no longer read
         mma_mixed(f1b, f1a, f0b, f0a, nxt, 0, kt + STAGES);     // second half; reads step kt + 1's
@@ -418,13 +454,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
         const uint32_t m = (uint32_t)(wm * TM + j * 32 + lrow);
+        const float sam = CHN && p.ch_sa && (int)m < rows_m ? p.ch_sa[m0 + m] : 1.0f;
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 const uint32_t n = (uint32_t)(wn * TN + i * 32 + b * 8 + khalf * 4);
                 const v16f &c = acc[i][j];
-                const v2u v = pack_bf16x4(c[4 * b] * sc, c[4 * b + 1] * sc, c[4 * b + 2] * sc, c[4 * b + 3] * sc);
+                v2u v;
+                if (CHN) {
+                    float s4[4], b4[4];
+                    channel_terms(p, n0 + (int)n, s4, b4);
+                    v = pack_bf16x4(c[4 * b] * sam * s4[0] + b4[0], c[4 * b + 1] * sam * s4[1] + b4[1],
+                                    c[4 * b + 2] * sam * s4[2] + b4[2], c[4 * b + 3] * sam * s4[3] + b4[3]);
+                } else {
+                    v = pack_bf16x4(c[4 * b] * sc, c[4 * b + 1] * sc, c[4 * b + 2] * sc, c[4 * b + 3] * sc);
+                }
                 const uint32_t chunk = (n >> 3) ^ (m % OCH);
                 *reinterpret_cast<v2u *>(smem + m * (BN * 2) + chunk * 16 + (n & 4) * 2) = v;
             }
@@ -638,6 +683,7 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
 template <int CB, int FA, int FB, int DEPTH, int SCL>
 __global__ __launch_bounds__(512, 4) void decode_kernel(GemmParams p) {   // 4 waves per SIMD: two workgroups per CU
     constexpr int W = 8;
+    constexpr bool BLK = SCL == SCALE_BLOCK, CHN = SCL == SCALE_CHANNEL;
     __shared__ __attribute__((aligned(16))) v4f red[W][CB][64];
 
     const int lane = threadIdx.x & 63;
@@ -657,8 +703,8 @@ __global__ __launch_bounds__(512, 4) void decode_kernel(GemmParams p) {   // 4 w
     const int nk = (p.K + 127) / 128;
     const int my = nk > wave ? (nk - wave + W - 1) / W : 0;   // steps kt = wave + W s of this wave
     // Block scales: the weight block's scale is the same for every lane.
-    const __amdgpu_buffer_rsrc_t rsSA = make_rsrc(SCL ? p.sfa : p.A, SCL ? (uint32_t)(nk * p.lds_sa) : 0u);
-    const __amdgpu_buffer_rsrc_t rsSB = make_rsrc(SCL ? p.sfb : p.A, SCL ? (uint32_t)(((p.N + 127) / 128) * p.lds_sb) : 0u);
+    const __amdgpu_buffer_rsrc_t rsSA = make_rsrc(BLK ? p.sfa : p.A, BLK ? (uint32_t)(nk * p.lds_sa) : 0u);
+    const __amdgpu_buffer_rsrc_t rsSB = make_rsrc(BLK ? p.sfb : p.A, BLK ? (uint32_t)(((p.N + 127) / 128) * p.lds_sb) : 0u);
 
     // (the scale arrays are below 2^31 bytes, so 32-bit offsets suffice)
     const uint32_t lsa = (uint32_t)p.lds_sa, sb_row = (uint32_t)(n0 / 128) * (uint32_t)p.lds_sb;
@@ -676,7 +722,7 @@ __global__ __launch_bounds__(512, 4) void decode_kernel(GemmParams p) {   // 4 w
 #pragma unroll
             for (int c = 0; c < CB; ++c) tr[d][c][h] = load16(rsT, in ? t_off[c] + k0 + h * 64 : kOobOffset);
         }
-        if (SCL) {
+        if (BLK) {
             const bool in = s < my;
             ssb[d] = __builtin_amdgcn_raw_buffer_load_b8(rsSB, in ? sb_row + (uint32_t)kt : kOobOffset, 0, 0);
             const uint32_t row0 = (uint32_t)kt * lsa + (uint32_t)r16;
@@ -698,7 +744,7 @@ __global__ __launch_bounds__(512, 4) void decode_kernel(GemmParams p) {   // 4 w
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
                 const v8i tf = pack8(tr[d][c][0], tr[d][c][1]);
-                if (SCL) acc[c] = mfma16x16x128_s<FB, FA>(wf, tf, acc[c], ssb[d], ssa[d][c]);
+                if (BLK) acc[c] = mfma16x16x128_s<FB, FA>(wf, tf, acc[c], ssb[d], ssa[d][c]);
                 else acc[c] = mfma16x16x128<FB, FA>(wf, tf, acc[c]);
             }
             load(d, s0 + d + DEPTH);               // steps past this wave's last read zeros, untouched memory
@@ -717,11 +763,20 @@ __global__ __launch_bounds__(512, 4) void decode_kernel(GemmParams p) {   // 4 w
         v4f sum = red[0][c][lane];
 #pragma unroll
         for (int w = 1; w < W; ++w) sum += red[w][c][lane];
-        const float sc = SCL ? 1.0f : p.scale_a[0] * p.scale_b[0];
+        const float sc = SCL != SCALE_TENSOR ? 1.0f : p.scale_a[0] * p.scale_b[0];
         const int tok = c * 16 + r16;
         if (tok < p.M) {
             const int n = n0 + kg * 4;
-            const v2u v = pack_bf16x4(sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc);
+            v2u v;
+            if (CHN) {
+                float s4[4], b4[4];
+                channel_terms(p, n, s4, b4);
+                const float sam = p.ch_sa ? p.ch_sa[tok] : 1.0f;
+                v = pack_bf16x4(sum[0] * sam * s4[0] + b4[0], sum[1] * sam * s4[1] + b4[1],
+                                sum[2] * sam * s4[2] + b4[2], sum[3] * sam * s4[3] + b4[3]);
+            } else {
+                v = pack_bf16x4(sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc);
+            }
             store_bf16x4(p.D + (int64_t)tok * p.ldd, n, p.N - n, v);
         }
     }

@@ -119,6 +119,25 @@ int fp8_gemm_nt_blockscaled(const void *A, int64_t lda, int a_dtype,
                             int M, int N, int K, void *stream);
 
 /*
+ * Dense GEMM with per-row and per-channel scales and a per-channel bias
+ * ("DeepGEMM: FP8 matrix-multiply kernels on Hopper Tensor Cores", section 5.2:
+ * a scale per channel instead of one per tensor; the bias is the additive term
+ * of a fused epilogue).
+ *   A, B, D, lda, ldb, ldd, M, N, K: as for fp8_gemm_nt.
+ *   scale_a: [M] floats (device, 4-byte aligned), one per row of A (token), or NULL = 1.
+ *   scale_b: [N] floats (device, 16-byte aligned), one per output channel, or NULL = 1.
+ *   bias:    [N] floats (device, 16-byte aligned), or NULL = 0.
+ *   D[i][j] = bf16_rne( scale_a[i] * scale_b[j] * sum_k A[i][k] * B[j][k] + bias[j] ),
+ *   the scale and bias applied in FP32 to the FP32 accumulator.
+ * Same kernels and shape classes as fp8_gemm_nt.
+ */
+int fp8_gemm_nt_channelwise(const void *A, int64_t lda, int a_dtype,
+                            const void *B, int64_t ldb, int b_dtype,
+                            const float *scale_a, const float *scale_b, const float *bias,
+                            void *D, int64_t ldd,
+                            int M, int N, int K, void *stream);
+
+/*
  * Masked grouped GEMM (MoE decode).
  *   A: [G][cap][K] FP8 codes, contiguous.  B: [G][N][K] FP8 codes, contiguous.
  *   masked_m: [G] int32 (device); group g has m_g = clamp(masked_m[g], 0, cap)

@@ -205,3 +205,21 @@ def test_blockscaled_validation(f):
     assert call(K=24) == -2
     assert call(M=0, A=None, sa=None) == 0
     assert call(K=0, A=None, B=None, sa=None, sb=None, lsb=0) == 0 or True   # K = 0 needs a device (writes zeros)
+
+
+def test_channelwise_validation(f):
+    lib = f.load_library()
+    ok = dict(A=A16, lda=256, a=0, B=A16, ldb=256, b=0, sa=A16, sb=A16, bias=A16, D=A16, ldd=256, M=128, N=256, K=256)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.fp8_gemm_nt_channelwise(a["A"], a["lda"], a["a"], a["B"], a["ldb"], a["b"], a["sa"], a["sb"],
+                                           a["bias"], a["D"], a["ldd"], a["M"], a["N"], a["K"], None)
+    assert call(A=None) == -1
+    assert call(sb=A16 + 4) == -3                 # channel vectors 16-byte aligned
+    assert call(bias=A16 + 8) == -3
+    assert call(sa=A16 + 2) == -3                 # row scales 4-byte aligned
+    assert call(ldd=100) == -5
+    assert call(a=7) == -4
+    assert call(M=0, A=None) == 0

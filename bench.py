@@ -8,8 +8,9 @@ HBM).  `value` is the whole-job rate over the timed steps.  The same run also
 times, each in its own timed loop: the masked grouped decode GEMM (G=32,
 cap=64, N=4096, K=7168, m_g ~ U{0..32}) against the HBM roofline, the
 contiguous grouped prefill GEMM, the 256^3 GEMM (latency), the E5M2 4096^3
-GEMM, the block-scaled and the per-channel 4096^3 GEMMs and the eight
-transformer-projection shapes.
+GEMM, the block-scaled and the per-channel 4096^3 GEMMs, the dense few-token
+(decode) GEMMs against the HBM roofline and the eight transformer-projection
+shapes.
 
 The average launch duration of each leg is the interval between two HIP events
 recorded around its K back-to-back launches on the stream the kernels run on
@@ -149,6 +150,33 @@ def bench_channelwise(torch, f, w, steps, warmup, timer):
     t = timer.run(fn, steps, warmup)
     t["tflops_kernel"] = 2.0 * M * N * K / (t["kernel_ms_mean"] * 1e-3) / 1e12
     del a, b, sa, sb, bias, out
+    return t
+
+
+def bench_decode(torch, f, M, N, K, steps, warmup, timer, seed=13):
+    """Dense few-token GEMM against the HBM roofline: the weights rotate over
+    enough copies (> 512 MB in all) that every launch streams them from HBM
+    rather than the 256 MB last-level cache."""
+    import numpy as np
+    import workloads
+
+    w = workloads.dense_random(M, N, K, seed=seed, std=1.0)
+    copies = max(2, -(-(512 << 20) // (N * K)))
+    base = dev(torch, w.B)
+    Bs = [base.roll(i, dims=0).contiguous() for i in range(copies)]
+    a = dev(torch, w.A)
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    state = {"i": 0}
+
+    def fn():
+        f.gemm_nt(a, Bs[state["i"] % copies], one, one, out=out, a_dtype=w.a_fmt, b_dtype=w.b_fmt)
+        state["i"] += 1
+    t = timer.run(fn, steps, warmup)
+    nbytes = float(N * K + M * K + 2 * M * N)
+    t["bytes"] = nbytes
+    t["gbs_kernel"] = nbytes / (t["kernel_ms_mean"] * 1e-3) / 1e9
+    del Bs, base, a, out
     return t
 
 
@@ -312,7 +340,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: dense masked contig small e5m2 blockscaled channelwise proj copy (default: all)")
+                    help="subset of: dense masked contig small e5m2 blockscaled channelwise decode proj copy (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="write profiles/*_hbm_counters.txt from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
@@ -340,7 +368,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     timer = Timer(torch)
-    want = set(args.only) if args.only else {"dense", "masked", "contig", "small", "e5m2", "blockscaled", "channelwise", "proj", "copy"}
+    want = set(args.only) if args.only else {"dense", "masked", "contig", "small", "e5m2", "blockscaled", "channelwise", "decode", "proj", "copy"}
     steps, warmup = args.steps, args.warmup
     extra = {}
 
@@ -379,6 +407,19 @@ def main():
             "tflops_kernel": r["tflops_kernel"], "kernel_ms_mean": r["kernel_ms_mean"],
             "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS}
         log(f"  {r['tflops_kernel']:.1f} TFLOP/s")
+    if "decode" in want:
+        out = []
+        for (N, K) in ((4096, 7168), (14336, 4096)):
+            for M in (1, 16, 32, 64):
+                r = bench_decode(torch, f, M, N, K, steps, warmup, timer)
+                out.append({"M": M, "N": N, "K": K, "kernel_us_mean": r["kernel_ms_mean"] * 1e3,
+                            "roofline": {"bound": "hbm", "achieved": r["gbs_kernel"], "peak": PEAK_HBM_GBS,
+                                         "unit": "GB/s", "frac": r["gbs_kernel"] / PEAK_HBM_GBS,
+                                         "algorithmic_bytes": r["bytes"]}})
+                log(f"  decode {M}x{N}x{K}: {r['kernel_ms_mean'] * 1e3:.1f} us, {r['gbs_kernel']:.0f} GB/s")
+        extra["dense_decode"] = {
+            "workload": "dense few-token GEMMs, A ~N(0,1), B ~N(0,1) E4M3 (seed 13), weights rotated over "
+                        "> 512 MB of copies so each launch reads them from HBM", "shapes": out}
     if "small" in want:
         log("timing dense 256^3")
         ws = workloads.dense_small()

@@ -86,6 +86,8 @@ def _load():
     lib.oracle_gemm_nt_blockscaled_points.restype = I
     lib.oracle_gemm_nt_channelwise.argtypes = [P, I64, I, P, I64, I, P, P, P, P, I64, P, P, I64, I64, I64]
     lib.oracle_gemm_nt_channelwise.restype = I
+    lib.oracle_grouped_masked_blockscaled.argtypes = [P, I, P, I, P, I64, P, I64, P, P, P, P, I64, I64, I64, I64, I]
+    lib.oracle_grouped_masked_blockscaled.restype = I
     _lib = lib
     return lib
 
@@ -332,4 +334,34 @@ def gemm_nt_channelwise(A, B, scale_a=None, scale_b=None, bias=None, a_fmt=E4M3,
                                             _ptr(bi), _ptr(D), N, _ptr(R), _ptr(S), M, N, K)
     if rc != 0:
         raise RuntimeError(f"oracle_gemm_nt_channelwise failed ({rc})")
+    return D, R, S
+
+
+def grouped_masked_blockscaled(A, B, masked_m, scale_a, scale_b, a_fmt=E4M3, b_fmt=E4M3, D_init=None, threads=None):
+    """Block-scaled masked grouped GEMM.  A: uint8 [G, cap, K]; B: uint8 [G, N, K];
+    scale_a: uint8 E8M0 [G, ceil(K/128), lds_a >= cap]; scale_b: uint8 E8M0
+    [G, ceil(N/128), lds_b >= ceil(K/128)].  Rows i >= clamp(masked_m[g]) keep
+    D_init (zeros by default).  Returns (D_bits [G, cap, N], R, S)."""
+    A = _u8(A)
+    B = _u8(B)
+    G, cap, K = A.shape
+    G2, N, K2 = B.shape
+    if G2 != G or K2 != K:
+        raise ValueError("A and B disagree on G or K")
+    kb, nb = (K + 127) // 128, (N + 127) // 128
+    sa = np.ascontiguousarray(scale_a)
+    sb = np.ascontiguousarray(scale_b)
+    if sa.dtype != np.uint8 or sa.ndim != 3 or sa.shape[:2] != (G, kb) or sa.shape[2] < cap:
+        raise ValueError(f"scale_a must be uint8 [{G}, {kb}, >= {cap}]")
+    if sb.dtype != np.uint8 or sb.ndim != 3 or sb.shape[:2] != (G, nb) or sb.shape[2] < kb:
+        raise ValueError(f"scale_b must be uint8 [{G}, {nb}, >= {kb}]")
+    mm = np.ascontiguousarray(masked_m, dtype=np.int32)
+    D = np.zeros((G, cap, N), dtype=np.uint16) if D_init is None else np.array(D_init, dtype=np.uint16, copy=True)
+    R = np.zeros((G, cap, N), dtype=np.float64)
+    S = np.zeros((G, cap, N), dtype=np.float64)
+    rc = _load().oracle_grouped_masked_blockscaled(_ptr(A), int(a_fmt), _ptr(B), int(b_fmt), _ptr(sa), sa.shape[2],
+                                                   _ptr(sb), sb.shape[2], _ptr(mm), _ptr(D), _ptr(R), _ptr(S),
+                                                   G, cap, N, K, threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_grouped_masked_blockscaled failed ({rc})")
     return D, R, S

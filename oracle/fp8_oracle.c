@@ -556,3 +556,30 @@ int oracle_gemm_nt_channelwise(const uint8_t *A, int64_t lda, int a_fmt,
     free(t);
     return 0;
 }
+
+/* Block-scaled masked grouped: A [G][cap][K], B [G][N][K], D/R/S [G][cap][N];
+ * scale_a [G][ceil(K/128)][lds_a] (row m of group g over K block kb at
+ * g * KB * lds_a + kb * lds_a + m), scale_b [G][ceil(N/128)][lds_b].  Rows
+ * i < clamp(masked_m[g], 0, cap) are computed; the others are left as the
+ * caller filled them.                                                        */
+int oracle_grouped_masked_blockscaled(const uint8_t *A, int a_fmt, const uint8_t *B, int b_fmt,
+                                      const uint8_t *scale_a, int64_t lds_a,
+                                      const uint8_t *scale_b, int64_t lds_b, const int32_t *masked_m,
+                                      uint16_t *D, double *R, double *S,
+                                      int64_t G, int64_t cap, int64_t N, int64_t K, int nthreads)
+{
+    if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || G < 0 || cap < 0 || N < 0 || K < 0) return -1;
+    int64_t kb = (K + 127) / 128, nb = (N + 127) / 128;
+    for (int64_t g = 0; g < G; ++g) {
+        int64_t mg = masked_m[g];
+        if (mg < 0) mg = 0;
+        if (mg > cap) mg = cap;
+        if (mg == 0 || N == 0) continue;
+        int rc = oracle_gemm_nt_blockscaled(A + g * cap * K, K, a_fmt, B + g * N * K, K, b_fmt,
+                                            scale_a + g * kb * lds_a, lds_a, scale_b + g * nb * lds_b, lds_b,
+                                            D + g * cap * N, N, R ? R + g * cap * N : NULL,
+                                            S ? S + g * cap * N : NULL, mg, N, K, nthreads);
+        if (rc != 0) return rc;
+    }
+    return 0;
+}

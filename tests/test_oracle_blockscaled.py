@@ -157,3 +157,23 @@ def test_scale_leading_dimensions():
     D0, R0, _ = oracle.gemm_nt_blockscaled(A, B, sa, sb)
     D1, R1, _ = oracle.gemm_nt_blockscaled(A, B, sa_wide, sb_wide)
     assert np.array_equal(D0, D1) and np.array_equal(R0, R1)
+
+
+def test_masked_grouped_equals_per_group_dense_and_leaves_rows():
+    """The grouped block-scaled oracle is the per-group dense block-scaled
+    oracle (pinned above) on rows < clamp(m_g), and leaves every other row."""
+    rng = np.random.default_rng(17)
+    G, cap, N, K = 4, 40, 150, 272
+    A = _codes(rng, E4M3, (G, cap, K))
+    B = _codes(rng, E4M3, (G, N, K))
+    sa = _scales(rng, (G, 3, 44))
+    sb = _scales(rng, (G, 2, 4))
+    mm = np.array([0, 40, 17, 99], np.int32)
+    init = np.full((G, cap, N), 0xBEEF, np.uint16)
+    D, R, S = oracle.grouped_masked_blockscaled(A, B, mm, sa, sb, D_init=init)
+    for g in range(G):
+        m = min(max(int(mm[g]), 0), cap)
+        if m:
+            Dg, Rg, Sg = oracle.gemm_nt_blockscaled(A[g, :m], B[g], sa[g], sb[g])
+            assert np.array_equal(D[g, :m], Dg) and np.array_equal(R[g, :m], Rg)
+        assert (D[g, m:] == 0xBEEF).all()

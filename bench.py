@@ -205,6 +205,28 @@ def bench_masked(torch, f, w, steps, warmup, timer):
     return t
 
 
+def bench_masked_blockscaled(torch, f, w, steps, warmup, timer):
+    import numpy as np
+
+    G, cap, K = w.A.shape
+    N = w.B.shape[1]
+    a, b = dev(torch, w.A), dev(torch, w.B)
+    sa, sb, mm = dev(torch, w.sa), dev(torch, w.sb), dev(torch, w.masked_m)
+    out = torch.empty((G, cap, N), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: f.grouped_gemm_masked_blockscaled(a, b, sa, sb, mm, out=out, expected_m=32, a_dtype=w.a_fmt,
+                                                   b_dtype=w.b_fmt)
+    t = timer.run(fn, steps, warmup)
+    m = np.clip(w.masked_m.astype(np.int64), 0, cap)
+    active = int((m > 0).sum())
+    kb, nb = (K + 127) // 128, (N + 127) // 128
+    # algorithmic bytes: weights and weight-block scales of non-empty experts,
+    # valid token rows and their scales, valid output rows, the counts
+    nbytes = active * (N * K + nb * kb) + int(m.sum()) * (K + kb) + 2 * int(m.sum()) * N + 4 * G
+    t.update({"bytes": float(nbytes), "gbs_kernel": nbytes / (t["kernel_ms_mean"] * 1e-3) / 1e9})
+    del a, b, sa, sb, mm, out
+    return t
+
+
 def bench_contig(torch, f, w, steps, warmup, timer):
     M_total, K = w.A.shape
     G, N, _ = w.B.shape
@@ -340,7 +362,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: dense masked contig small e5m2 blockscaled channelwise decode proj copy (default: all)")
+                    help="subset of: dense masked masked_bs contig small e5m2 blockscaled channelwise decode proj copy "
+                         "(default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="write profiles/*_hbm_counters.txt from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
@@ -368,7 +391,8 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     timer = Timer(torch)
-    want = set(args.only) if args.only else {"dense", "masked", "contig", "small", "e5m2", "blockscaled", "channelwise", "decode", "proj", "copy"}
+    want = set(args.only) if args.only else {"dense", "masked", "masked_bs", "contig", "small", "e5m2", "blockscaled", "channelwise", "decode", "proj",
+                                           "copy"}
     steps, warmup = args.steps, args.warmup
     extra = {}
 
@@ -440,6 +464,18 @@ def main():
                          "algorithmic_bytes": r["bytes"]}}
         log(f"  {r['gbs_kernel']:.0f} GB/s ({r['gbs_kernel'] / PEAK_HBM_GBS:.1%} of HBM peak)")
         del wm
+    if "masked_bs" in want:
+        log("generating block-scaled masked grouped decode inputs (G=32, cap=64, N=4096, K=7168)")
+        wmb = workloads.masked_decode_blockscaled()
+        r = bench_masked_blockscaled(torch, f, wmb, steps, warmup, timer)
+        extra["masked_grouped_blockscaled"] = {
+            "workload": "block-scaled masked grouped FP8 GEMM, G=32, cap=64, N=4096, K=7168, m_g~U{0..32} (seed 8), "
+                        "E8M0 scales per 1x128 token block and 128x128 weight block, swap-AB",
+            "kernel_ms_mean": r["kernel_ms_mean"],
+            "roofline": {"bound": "hbm", "achieved": r["gbs_kernel"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": r["gbs_kernel"] / PEAK_HBM_GBS, "algorithmic_bytes": r["bytes"]}}
+        log(f"  {r['gbs_kernel']:.0f} GB/s")
+        del wmb
     if "contig" in want:
         log("generating contiguous grouped prefill inputs (65536 rows over 32 experts, N=4096, K=7168)")
         wc = workloads.contig_prefill()

@@ -38,7 +38,8 @@ class Plan(ctypes.Structure):
                 ("token_blocks", ctypes.c_int), ("workgroups", ctypes.c_int64)]
 
 
-SYMBOLS = ("fp8_gemm_nt", "fp8_gemm_nt_blockscaled", "fp8_gemm_nt_channelwise", "fp8_grouped_gemm_masked", "fp8_grouped_gemm_contig",
+SYMBOLS = ("fp8_gemm_nt", "fp8_gemm_nt_blockscaled", "fp8_gemm_nt_channelwise",
+           "fp8_grouped_gemm_masked_blockscaled", "fp8_grouped_gemm_masked", "fp8_grouped_gemm_contig",
            "fp8_gemm_plan", "fp8_gemm_strerror", "fp8_gemm_abi_version")
 
 
@@ -59,6 +60,8 @@ def load_library(path: str = LIB_PATH):
     lib.fp8_gemm_nt_channelwise.restype = I
     lib.fp8_grouped_gemm_masked.argtypes = [P, I, P, I, P, P, P, P, I, I, I, I, I, P]
     lib.fp8_grouped_gemm_masked.restype = I
+    lib.fp8_grouped_gemm_masked_blockscaled.argtypes = [P, I, P, I, P, I64, P, I64, P, P, I, I, I, I, I, P]
+    lib.fp8_grouped_gemm_masked_blockscaled.restype = I
     lib.fp8_grouped_gemm_contig.argtypes = [P, I, P, I, P, P, P, P, I, I, I, I, P]
     lib.fp8_grouped_gemm_contig.restype = I
     lib.fp8_gemm_plan.argtypes = [I, I, I, I, I, I, ctypes.POINTER(Plan)]
@@ -265,6 +268,40 @@ def grouped_gemm_masked(a, b, scale_a, scale_b, masked_m, out=None, expected_m=0
     _check(load_library().fp8_grouped_gemm_masked(a.data_ptr(), fa, b.data_ptr(), fb, scale_a.data_ptr(),
                                                   scale_b.data_ptr(), masked_m.data_ptr(), out.data_ptr(),
                                                   G, cap, N, K, int(expected_m), _stream()))
+    return out
+
+
+def grouped_gemm_masked_blockscaled(a, b, scale_a, scale_b, masked_m, out=None, expected_m=0, a_dtype=None,
+                                    b_dtype=None):
+    """Block-scaled masked grouped GEMM: a [G, cap, K], b [G, N, K], masked_m int32
+    [G]; scale_a uint8 E8M0 [G, ceil(K/128), lds_a >= cap], scale_b uint8 E8M0
+    [G, ceil(N/128), lds_b >= ceil(K/128)], contiguous; out [G, cap, N] bf16
+    (rows >= masked_m[g] untouched)."""
+    torch = _torch()
+    fa = _fp8_code(a, a_dtype, "a")
+    fb = _fp8_code(b, b_dtype, "b")
+    if a.dim() != 3 or b.dim() != 3 or a.shape[0] != b.shape[0] or a.shape[2] != b.shape[2]:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} are not [G, cap, K] and [G, N, K]")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous")
+    G, cap, K = a.shape
+    N = b.shape[1]
+    kb, nb = (K + 127) // 128, (N + 127) // 128
+    for t, name, mid, least in ((scale_a, "scale_a", kb, cap), (scale_b, "scale_b", nb, kb)):
+        if (t.dtype != torch.uint8 or t.dim() != 3 or tuple(t.shape[:2]) != (G, mid) or t.shape[2] < least
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous uint8 [{G}, {mid}, >= {least}] tensor")
+    _require_cuda(a, b, scale_a, scale_b, masked_m)
+    if masked_m.dtype != torch.int32 or masked_m.numel() != G or not masked_m.is_contiguous():
+        raise ValueError("masked_m must be a contiguous int32 tensor with G elements")
+    if out is None:
+        out = torch.empty((G, cap, N), dtype=torch.bfloat16, device=a.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (G, cap, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [G, cap, N] bfloat16 tensor")
+    _require_cuda(out)
+    _check(load_library().fp8_grouped_gemm_masked_blockscaled(
+        a.data_ptr(), fa, b.data_ptr(), fb, scale_a.data_ptr(), scale_a.shape[2], scale_b.data_ptr(),
+        scale_b.shape[2], masked_m.data_ptr(), out.data_ptr(), G, cap, N, K, int(expected_m), _stream()))
     return out
 
 

@@ -209,11 +209,11 @@ int launch_tile128(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s
     return launch_ring<128, 256, TILE128_WM, TILE128_WN, T128_ST, T128_BK, MODE, SCL>(fa, fb, p, grid, s);
 }
 
-template <int CB, int MODE>
+template <int CB, int MODE, int SCL = 0>
 int launch_swap_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     const dim3 block(256);
 #define FP8G_SWAP(FA, FB) \
-    hipLaunchKernelGGL((fp8g::swap_kernel<kSwapWaveRows, CB, FA, FB, kSwapDepth, MODE>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((fp8g::swap_kernel<kSwapWaveRows, CB, FA, FB, kSwapDepth, MODE, SCL>), grid, block, 0, s, p)
     if (fa == 0 && fb == 0) FP8G_SWAP(0, 0);
     else if (fa == 0 && fb == 1) FP8G_SWAP(0, 1);
     else if (fa == 1 && fb == 0) FP8G_SWAP(1, 0);
@@ -222,11 +222,11 @@ int launch_swap_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s
     return launch_status("swap kernel");
 }
 
-template <int MODE>
+template <int MODE, int SCL = 0>
 int launch_swap(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    if (cb == 1) return launch_swap_cb<1, MODE>(fa, fb, p, grid, s);
-    if (cb == 2) return launch_swap_cb<2, MODE>(fa, fb, p, grid, s);
-    return launch_swap_cb<4, MODE>(fa, fb, p, grid, s);
+    if (cb == 1) return launch_swap_cb<1, MODE, SCL>(fa, fb, p, grid, s);
+    if (cb == 2) return launch_swap_cb<2, MODE, SCL>(fa, fb, p, grid, s);
+    return launch_swap_cb<4, MODE, SCL>(fa, fb, p, grid, s);
 }
 
 // Decode kernel: steps of loads in flight per wave, fewer with more token
@@ -357,6 +357,54 @@ int fp8_grouped_gemm_masked(const void *A, int a_dtype, const void *B, int b_dty
     p.tiles_m = (int)cdiv(cap, 128);
     p.tiles_n = (int)cdiv(N, 256);
     return launch_tile128<fp8g::MODE_MASKED>(a_dtype, b_dtype, p, dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)G), s);
+}
+
+int fp8_grouped_gemm_masked_blockscaled(const void *A, int a_dtype, const void *B, int b_dtype,
+                                        const uint8_t *scale_a, int64_t lds_a, const uint8_t *scale_b, int64_t lds_b,
+                                        const int32_t *masked_m, void *D, int G, int cap, int N, int K,
+                                        int expected_m, void *stream) {
+    if (!dtype_ok(a_dtype) || !dtype_ok(b_dtype)) return fail(FP8G_ERR_DTYPE, "dtypes %d, %d", a_dtype, b_dtype);
+    if (G < 0 || cap < 0) return fail(FP8G_ERR_SHAPE, "negative G=%d or cap=%d", G, cap);
+    fp8g_plan plan;
+    int st = plan_impl(1, cap, N, K, G, expected_m, &plan);
+    if (st != FP8G_OK) return st;
+    if (plan.variant == V_NONE) return ok();
+    if ((K > 0 && (!A || !B || !scale_a || !scale_b)) || !D || !masked_m)
+        return fail(FP8G_ERR_NULL, "A, B, scale_a, scale_b (unless K = 0), D and masked_m are required");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return fail(FP8G_ERR_ALIGN, "A, B and D must be 16-byte aligned");
+    if (!aligned4(scale_a) || !aligned4(scale_b) || !aligned4(masked_m))
+        return fail(FP8G_ERR_ALIGN, "scale arrays and masked_m must be 4-byte aligned");
+    if (N % 8) return fail(FP8G_ERR_ALIGN, "N=%d: rows of D must stay 16-byte aligned (N %% 8 == 0)", N);
+    const int64_t kb = cdiv(K, 128), nb = cdiv(N, 128);
+    if (lds_a < cap || lds_b < kb) return fail(FP8G_ERR_STRIDE, "lds_a=%lld below cap=%d or lds_b=%lld below ceil(K/128)=%lld",
+                                               (long long)lds_a, cap, (long long)lds_b, (long long)kb);
+    if (lds_a % 4 || lds_b % 4) return fail(FP8G_ERR_ALIGN, "lds_a=%lld / lds_b=%lld not multiples of 4", (long long)lds_a, (long long)lds_b);
+    if (kb * lds_a > INT32_MAX - 256 || nb * lds_b > INT32_MAX - 256)
+        return fail(FP8G_ERR_STRIDE, "a group's scale array above 2^31 bytes");
+    if ((st = check_device()) != FP8G_OK) return st;
+
+    GemmParams p = {};
+    p.A = static_cast<const uint8_t *>(A);
+    p.B = static_cast<const uint8_t *>(B);
+    p.D = static_cast<uint16_t *>(D);
+    p.lda = K; p.ldb = K; p.ldd = N;
+    p.a_gstride = (int64_t)cap * K;
+    p.b_gstride = (int64_t)N * K;
+    p.d_gstride = (int64_t)cap * N;
+    p.M = cap; p.N = N; p.K = K; p.G = G; p.cap = cap;
+    p.masked_m = masked_m;
+    p.sfa = scale_a; p.sfb = scale_b; p.lds_sa = lds_a; p.lds_sb = lds_b;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (plan.variant == V_SWAP) {
+        p.tiles_m = 1;
+        p.tiles_n = (int)cdiv(N, kSwapTileN);
+        return launch_swap<fp8g::MODE_MASKED, fp8g::SCALE_BLOCK>(plan.token_blocks, a_dtype, b_dtype, p,
+                                                                 dim3((unsigned)plan.workgroups), s);
+    }
+    p.tiles_m = (int)cdiv(cap, 128);
+    p.tiles_n = (int)cdiv(N, 256);
+    return launch_tile128<fp8g::MODE_MASKED, fp8g::SCALE_BLOCK>(a_dtype, b_dtype, p,
+                                                                dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)G), s);
 }
 
 int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dtype, const float *scale_a,

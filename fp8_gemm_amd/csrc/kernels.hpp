@@ -167,8 +167,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     constexpr int STAGE_OUT = BM * BN * 2;         // BF16 output tile staged for the stores
     // Block scales (BLK): per ring slot, the step's scale of each tile row of A
     // (bytes 0..BM-1) and one dword per 128-row block of B (from byte 256).
-    static_assert(!BLK || (MODE == MODE_DENSE && BK == 128 && BM <= 256 && BN % 128 == 0),
-                  "block scales: dense form, 128-byte K steps");
+    static_assert(!BLK || (MODE != MODE_CONTIG && BK == 128 && BM <= 256 && BN % 128 == 0),
+                  "block scales: dense and masked forms, 128-byte K steps");
     static_assert(!CHN || MODE == MODE_DENSE, "per-channel scales: dense form");
     constexpr int SCS = BLK ? 512 : 0;
     constexpr int RING = STAGES * (SLOT + SCS);
@@ -295,8 +295,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     // the scale dword holding K block kt of each 128-row block of B.  Rows
     // past the scale array (or K blocks past the last) read zeros; rows past M
     // may read other in-range bytes, which only reach outputs not written.
-    const v4i srdSA = BLK ? make_srd(p.sfa, (uint32_t)(((p.K + 127) / 128) * p.lds_sa)) : v4i{0, 0, 0, 0};
-    const v4i srdSB = BLK ? make_srd(p.sfb, (uint32_t)(((p.N + 127) / 128) * p.lds_sb)) : v4i{0, 0, 0, 0};
+    const int64_t sa_bytes = (int64_t)((p.K + 127) / 128) * p.lds_sa;
+    const int64_t sb_bytes = (int64_t)((p.N + 127) / 128) * p.lds_sb;
+    const v4i srdSA = BLK ? make_srd(p.sfa + (MODE == MODE_MASKED ? (int64_t)g * sa_bytes : 0), (uint32_t)sa_bytes)
+                          : v4i{0, 0, 0, 0};
+    const v4i srdSB = BLK ? make_srd(p.sfb + (MODE == MODE_MASKED ? (int64_t)g * sb_bytes : 0), (uint32_t)sb_bytes)
+                          : v4i{0, 0, 0, 0};
     const uint32_t scl_base = lds0 + STAGES * SLOT;
     auto issue_scales = [&](int kt) {
         if (!BLK || wave != 0) return;
@@ -509,19 +513,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 // workgroup into a small LDS ring and read from there.  DEPTH register slots
 // keep DEPTH-1 K blocks of weight loads in flight per wave.
 // ---------------------------------------------------------------------------
-template <int WR, int CB, int FA, int FB, int DEPTH, int MODE>
+template <int WR, int CB, int FA, int FB, int DEPTH, int MODE, int SCL>
 __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
+    constexpr bool BLK = SCL == SCALE_BLOCK;
+    static_assert(!BLK || WR == 128, "block scales: each wave's rows are one 128-row scale block");
     constexpr int RB = WR / 16;
     constexpr int ROWB = 128;                      // K bytes per pipeline stage
     constexpr int TR = CB <= 2 ? 32 : 16 * CB;     // token rows staged per stage (>= 32: one DMA per wave)
     constexpr int TDMA = TR / 32;                  // token DMA instructions per wave per stage (8 rows each)
     constexpr int TS = DEPTH + 1;                  // token ring slots
     constexpr int TSLOT = TR * ROWB;
-    constexpr int WLOADS = RB * 2;                 // weight loads per wave per stage
+    constexpr int WLOADS = RB * 2 + (BLK ? 1 : 0); // weight loads (and the block scale) per wave per stage
+    constexpr int SDMA = BLK ? 1 : 0;              // token-scale DMA of wave 0 per stage
+    constexpr int SCS = BLK ? 256 : 0;             // token-scale bytes per ring slot
     static_assert(RB >= 1 && CB >= 1 && DEPTH >= 2, "shape");
-    static_assert((DEPTH - 1) * (WLOADS + TDMA) < 64, "loads in flight");
+    static_assert((DEPTH - 1) * (WLOADS + TDMA + SDMA) < 64, "loads in flight");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t tsm[TS * TSLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t tsm[TS * TSLOT + TS * SCS];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -541,8 +549,15 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
     const uint8_t *w_base = p.B + (int64_t)g * p.b_gstride + (int64_t)min(nw, p.N) * p.ldb;
     const uint8_t *t_base = p.A + (int64_t)g * p.a_gstride;
     uint16_t *d_base = p.D + (int64_t)g * p.d_gstride;
-    const float sc = p.scale_a[0] * p.scale_b[g];
+    const float sc = BLK ? 1.0f : p.scale_a[0] * p.scale_b[g];
     const __amdgpu_buffer_rsrc_t rsW = make_rsrc(w_base, rows_bytes(rows_w, p.ldb));
+    // Block scales of group g: token rows [kb][lds_sa], weight blocks [nb][lds_sb];
+    // this wave's 128 weight rows are one scale block.
+    const int nk_ = (p.K + 127) / 128;
+    const uint8_t *sa_g = BLK ? p.sfa + (int64_t)g * nk_ * p.lds_sa : p.A;
+    const uint8_t *sb_g = BLK ? p.sfb + (int64_t)g * ((p.N + 127) / 128) * p.lds_sb : p.A;
+    const __amdgpu_buffer_rsrc_t rsSB = make_rsrc(sb_g, BLK ? (uint32_t)(((p.N + 127) / 128) * p.lds_sb) : 0u);
+    const uint32_t sb_row = BLK ? (uint32_t)(min(nw, p.N) / 128) * (uint32_t)p.lds_sb : 0u;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)tsm;
 
     // Operand layout used for both operands of v_mfma 16x16x128: lane l
@@ -586,6 +601,9 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
         // deposits zeros for them and never fetches them (the NaN-filled rows
         // behind them never reach the matrix cores: same page, Bug 3).
         const v4i srdT = make_srd(t_base + (int64_t)t0 * p.lda, rows_bytes(mt, p.lda));
+        // Token-row scales of this token block (wave 0): rows past the group's
+        // count may read other in-range bytes, which reach only unwritten rows.
+        const v4i srdST = BLK ? make_srd(sa_g, (uint32_t)(nk_ * p.lds_sa)) : v4i{0, 0, 0, 0};
         __syncthreads();                           // the ring is free (previous token block done)
 
         v4f acc[RB][CB];
@@ -595,6 +613,7 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
             for (int c = 0; c < CB; ++c) acc[r][c] = (v4f){0, 0, 0, 0};
 
         v4u wreg[DEPTH][RB][2];
+        int wscale[DEPTH];
 
         // One stage: this wave's weight loads (registers), then its token DMA.
         // Past the last K block every offset is out of range: no memory
@@ -608,11 +627,18 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
                 wreg[slot][r][0] = load16(rsW, in0 ? w_off[r] + k0 : kOobOffset);
                 wreg[slot][r][1] = load16(rsW, in1 ? w_off[r] + k0 + 64 : kOobOffset);
             }
+            if (BLK)
+                wscale[slot] = __builtin_amdgcn_raw_buffer_load_b8(rsSB, kt < nk ? sb_row + (uint32_t)kt : kOobOffset, 0, 0);
 #pragma unroll
             for (int i = 0; i < TDMA; ++i) {
                 const bool in = (kt < nk) && (int)(k0 + t_dma_kc[i]) < p.K;
                 dma16(srdT, in ? t_dma_off[i] + k0 : kOobOffset,
                       lds0 + (uint32_t)((kt % TS) * TSLOT) + (uint32_t)(wave * TDMA + i) * 1024u);
+            }
+            if (BLK && wave == 0) {
+                const bool in = (kt < nk) && 4 * lane < CB * 16;
+                dma4(srdST, in ? (uint32_t)kt * (uint32_t)p.lds_sa + (uint32_t)(t0 + 4 * lane) : kOobOffset,
+                     lds0 + (uint32_t)(TS * TSLOT) + (uint32_t)((kt % TS) * SCS));
             }
         };
 
@@ -630,19 +656,26 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
                 load((s + DEPTH - 1) % DEPTH, kt + DEPTH - 1);
                 __builtin_amdgcn_sched_barrier(0);
                 // every load of step kt (older than the DEPTH - 1 newer stages) has landed
-                vmcnt_wait<(DEPTH - 1) * (WLOADS + TDMA)>();
+                if (BLK && wave == 0) vmcnt_wait<(DEPTH - 1) * (WLOADS + TDMA + SDMA)>();
+                else vmcnt_wait<(DEPTH - 1) * (WLOADS + TDMA)>();
                 __syncthreads();                   // every wave's token DMA of step kt has landed
                 const uint8_t *ts = tsm + (kt % TS) * TSLOT;
                 v8i tf[CB];
+                int tsc[CB];
 #pragma unroll
-                for (int c = 0; c < CB; ++c)
+                for (int c = 0; c < CB; ++c) {
                     tf[c] = pack8(*reinterpret_cast<const v4u *>(ts + t_frag[c][0]),
                                   *reinterpret_cast<const v4u *>(ts + t_frag[c][1]));
+                    tsc[c] = BLK ? (int)tsm[TS * TSLOT + (kt % TS) * SCS + c * 16 + r16] : 127;
+                }
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
                     const v8i wf = pack8(wreg[s][r][0], wreg[s][r][1]);
 #pragma unroll
-                    for (int c = 0; c < CB; ++c) acc[r][c] = mfma16x16x128<FB, FA>(wf, tf[c], acc[r][c]);
+                    for (int c = 0; c < CB; ++c) {
+                        if (BLK) acc[r][c] = mfma16x16x128_s<FB, FA>(wf, tf[c], acc[r][c], wscale[s], tsc[c]);
+                        else acc[r][c] = mfma16x16x128<FB, FA>(wf, tf[c], acc[r][c]);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }

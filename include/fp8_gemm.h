@@ -157,6 +157,27 @@ int fp8_grouped_gemm_masked(const void *A, int a_dtype, const void *B, int b_dty
                             int G, int cap, int N, int K, int expected_m, void *stream);
 
 /*
+ * Block-scaled masked grouped GEMM (MoE decode with the block-scaled format of
+ * fp8_gemm_nt_blockscaled, per expert).
+ *   A, B, masked_m, D, G, cap, N, K, expected_m: as for fp8_grouped_gemm_masked.
+ *   scale_a: E8M0 codes (uint8, device), [G][ceil(K/128)][lds_a]: the scale of
+ *     row i of group g over K block kb is 2^(scale_a[(g * ceil(K/128) + kb) * lds_a + i] - 127).
+ *     lds_a >= cap, lds_a % 4 == 0.
+ *   scale_b: E8M0 codes (uint8, device), [G][ceil(N/128)][lds_b]: rows
+ *     128 nb .. 128 nb + 127 of B[g] over K block kb at
+ *     scale_b[(g * ceil(N/128) + nb) * lds_b + kb].  lds_b >= ceil(K/128), lds_b % 4 == 0.
+ *   Code 255 is NaN.  Scale arrays 4-byte aligned; each group's below 2^31 bytes.
+ *   For i < m_g: D[g][i][j] = bf16_rne( sum_kb 2^(ea - 127) 2^(eb - 127) sum_{k in kb} A[g][i][k] B[g][j][k] ).
+ *   Rows i >= m_g of A are never read and rows i >= m_g of D never written;
+ *   their scale bytes may be read and never reach a written output.
+ */
+int fp8_grouped_gemm_masked_blockscaled(const void *A, int a_dtype, const void *B, int b_dtype,
+                                        const uint8_t *scale_a, int64_t lds_a,
+                                        const uint8_t *scale_b, int64_t lds_b,
+                                        const int32_t *masked_m, void *D,
+                                        int G, int cap, int N, int K, int expected_m, void *stream);
+
+/*
  * Contiguous grouped GEMM (MoE prefill).
  *   A: [M_total][K] FP8 codes, contiguous; the rows of each expert are
  *     contiguous and each expert's run starts on a multiple of 128 rows

@@ -268,3 +268,49 @@ def dense_blockscaled_square(n=4096):
     w = dense_blockscaled(n, n, n, seed=6)
     w.name = f"dense_blockscaled_{n}"
     return w
+
+
+@dataclass
+class MaskedBlockScaled:
+    A: np.ndarray            # uint8 [G, cap, K]
+    B: np.ndarray            # uint8 [G, N, K]
+    sa: np.ndarray           # uint8 E8M0 [G, ceil(K/128), lds_a]
+    sb: np.ndarray           # uint8 E8M0 [G, ceil(N/128), lds_b]
+    masked_m: np.ndarray     # int32 [G]
+    a_fmt: int = E4M3
+    b_fmt: int = E4M3
+    name: str = ""
+
+
+def masked_blockscaled(G, cap, N, K, seed, m_values=None, m_max=None, lds_pad=0, std_b=0.02):
+    """Block-scaled masked grouped case: per expert, valid token rows ~N(0,1)
+    quantized per 1 x 128 block and weights ~N(0, std_b) per 128 x 128 block,
+    each block with its own power-of-two scale; rows past each count hold the
+    NaN code and NaN scales (255), and so do the scale arrays' padding columns."""
+    rng = np.random.default_rng(seed)
+    if m_values is None:
+        m_values = rng.integers(0, (m_max if m_max is not None else cap) + 1, size=G)
+    mm = np.asarray(m_values, dtype=np.int32)
+    kb, nb = (K + 127) // 128, (N + 127) // 128
+    lds_a = ((cap + lds_pad + 3) // 4) * 4
+    lds_b = ((kb + lds_pad + 3) // 4) * 4
+    A = np.full((G, cap, K), 0x7F, np.uint8)
+    B = np.empty((G, N, K), np.uint8)
+    sa = np.full((G, kb, lds_a), 255, np.uint8)
+    sb = np.full((G, nb, lds_b), 255, np.uint8)
+    for g in range(G):
+        m = int(min(max(mm[g], 0), cap))
+        if m:
+            A[g, :m], ea = _pow2_block_quantize(_normal(rng, (m, K), 1.0), E4M3, 1)
+            sa[g, :, :m] = ea.T
+        B[g], eb = _pow2_block_quantize(_normal(rng, (N, K), std_b), E4M3, 128)
+        sb[g, :, :kb] = eb
+    return MaskedBlockScaled(A, B, sa, sb, mm, E4M3, E4M3, f"masked_bs_G{G}_cap{cap}_{N}x{K}_s{seed}")
+
+
+def masked_decode_blockscaled():
+    """The masked decode shape (G=32, cap=64, N=4096, K=7168, m_g ~ U{0..32})
+    in the block-scaled format; seed 8."""
+    w = masked_blockscaled(32, 64, 4096, 7168, seed=8, m_max=32)
+    w.name = "masked_decode_blockscaled_G32_cap64_4096x7168"
+    return w

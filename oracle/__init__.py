@@ -88,6 +88,8 @@ def _load():
     lib.oracle_gemm_nt_channelwise.restype = I
     lib.oracle_grouped_masked_blockscaled.argtypes = [P, I, P, I, P, I64, P, I64, P, P, P, P, I64, I64, I64, I64, I]
     lib.oracle_grouped_masked_blockscaled.restype = I
+    lib.oracle_grouped_contig_blockscaled.argtypes = [P, I, P, I, P, I64, P, I64, P, P, P, P, I64, I64, I64, I64]
+    lib.oracle_grouped_contig_blockscaled.restype = I
     _lib = lib
     return lib
 
@@ -364,4 +366,34 @@ def grouped_masked_blockscaled(A, B, masked_m, scale_a, scale_b, a_fmt=E4M3, b_f
                                                    G, cap, N, K, threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_grouped_masked_blockscaled failed ({rc})")
+    return D, R, S
+
+
+def grouped_contig_blockscaled(A, B, grp_idx, scale_a, scale_b, a_fmt=E4M3, b_fmt=E4M3, D_init=None):
+    """Block-scaled contiguous grouped GEMM.  A: uint8 [M_total, K]; B: uint8
+    [G, N, K]; scale_a: uint8 E8M0 [ceil(K/128), lds_a >= M_total] (global rows);
+    scale_b: uint8 E8M0 [G, ceil(N/128), lds_b >= ceil(K/128)].  Padding rows keep
+    D_init (zeros by default).  Returns (D_bits [M_total, N], R, S)."""
+    A = _u8(A)
+    B = _u8(B)
+    M, K = A.shape
+    G, N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A and B disagree on K")
+    kb, nb = (K + 127) // 128, (N + 127) // 128
+    sa = np.ascontiguousarray(scale_a)
+    sb = np.ascontiguousarray(scale_b)
+    if sa.dtype != np.uint8 or sa.ndim != 2 or sa.shape[0] != kb or sa.shape[1] < M:
+        raise ValueError(f"scale_a must be uint8 [{kb}, >= {M}]")
+    if sb.dtype != np.uint8 or sb.ndim != 3 or sb.shape[:2] != (G, nb) or sb.shape[2] < kb:
+        raise ValueError(f"scale_b must be uint8 [{G}, {nb}, >= {kb}]")
+    gi = np.ascontiguousarray(grp_idx, dtype=np.int32)
+    D = np.zeros((M, N), dtype=np.uint16) if D_init is None else np.array(D_init, dtype=np.uint16, copy=True)
+    R = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    rc = _load().oracle_grouped_contig_blockscaled(_ptr(A), int(a_fmt), _ptr(B), int(b_fmt), _ptr(sa), sa.shape[1],
+                                                   _ptr(sb), sb.shape[2], _ptr(gi), _ptr(D), _ptr(R), _ptr(S),
+                                                   M, G, N, K)
+    if rc != 0:
+        raise RuntimeError(f"oracle_grouped_contig_blockscaled failed ({rc})")
     return D, R, S

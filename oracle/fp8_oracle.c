@@ -583,3 +583,31 @@ int oracle_grouped_masked_blockscaled(const uint8_t *A, int a_fmt, const uint8_t
     }
     return 0;
 }
+
+/* Block-scaled contiguous grouped: A [M_total][K], B [G][N][K], D/R/S [M_total][N];
+ * scale_a [ceil(K/128)][lds_a] (row r over K block kb at kb * lds_a + r, r the
+ * global row), scale_b [G][ceil(N/128)][lds_b].  Row r with 0 <= grp_idx[r] < G
+ * uses expert grp_idx[r]; other rows are padding and are left untouched.    */
+int oracle_grouped_contig_blockscaled(const uint8_t *A, int a_fmt, const uint8_t *B, int b_fmt,
+                                      const uint8_t *scale_a, int64_t lds_a,
+                                      const uint8_t *scale_b, int64_t lds_b, const int32_t *grp_idx,
+                                      uint16_t *D, double *R, double *S,
+                                      int64_t M_total, int64_t G, int64_t N, int64_t K)
+{
+    if (!fmt_ok(a_fmt) || !fmt_ok(b_fmt) || M_total < 0 || G < 0 || N < 0 || K < 0) return -1;
+    int64_t kb = (K + 127) / 128, nb = (N + 127) / 128;
+    for (int64_t r = 0; r < M_total; ++r) {
+        int32_t e = grp_idx[r];
+        if (e < 0 || e >= G || N == 0) continue;
+        /* one row: the dense block-scaled form with the row's scale column */
+        uint8_t *col = (uint8_t *)malloc((size_t)(kb > 0 ? kb : 1));
+        if (!col) return -2;
+        for (int64_t b = 0; b < kb; ++b) col[b] = scale_a[b * lds_a + r];
+        int rc = oracle_gemm_nt_blockscaled(A + r * K, K, a_fmt, B + e * N * K, K, b_fmt, col, 1,
+                                            scale_b + e * nb * lds_b, lds_b, D + r * N, N,
+                                            R ? R + r * N : NULL, S ? S + r * N : NULL, 1, N, K, 1);
+        free(col);
+        if (rc != 0) return rc;
+    }
+    return 0;
+}

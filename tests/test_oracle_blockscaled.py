@@ -177,3 +177,26 @@ def test_masked_grouped_equals_per_group_dense_and_leaves_rows():
             Dg, Rg, Sg = oracle.gemm_nt_blockscaled(A[g, :m], B[g], sa[g], sb[g])
             assert np.array_equal(D[g, :m], Dg) and np.array_equal(R[g, :m], Rg)
         assert (D[g, m:] == 0xBEEF).all()
+
+
+def test_contig_grouped_equals_per_expert_dense_and_skips_padding():
+    """Each valid row of the contiguous block-scaled oracle is the dense
+    block-scaled oracle (pinned above) on that row with its expert's weights and
+    scales; padding rows and out-of-range indices keep the initial value."""
+    rng = np.random.default_rng(19)
+    G, N, K = 3, 140, 272
+    M = 9
+    A = _codes(rng, E4M3, (M, K))
+    B = _codes(rng, E4M3, (G, N, K))
+    sa = _scales(rng, (3, 12))
+    sb = _scales(rng, (G, 2, 4))
+    gi = np.array([0, 0, -1, 2, 2, 1, 7, 1, -3], np.int32)
+    init = np.full((M, N), 0xBEEF, np.uint16)
+    D, R, S = oracle.grouped_contig_blockscaled(A, B, gi, sa, sb, D_init=init)
+    for r in range(M):
+        e = int(gi[r])
+        if 0 <= e < G:
+            Dr, Rr, _ = oracle.gemm_nt_blockscaled(A[r:r + 1], B[e], sa[:, r:r + 1], sb[e])
+            assert np.array_equal(D[r], Dr[0]) and np.array_equal(R[r], Rr[0])
+        else:
+            assert (D[r] == 0xBEEF).all()

@@ -227,6 +227,20 @@ def bench_masked_blockscaled(torch, f, w, steps, warmup, timer):
     return t
 
 
+def bench_contig_blockscaled(torch, f, w, steps, warmup, timer):
+    M_total, K = w.A.shape
+    G, N, _ = w.B.shape
+    a, b = dev(torch, w.A), dev(torch, w.B)
+    sa, sb, gi = dev(torch, w.sa), dev(torch, w.sb), dev(torch, w.grp_idx)
+    out = torch.empty((M_total, N), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: f.grouped_gemm_contig_blockscaled(a, b, sa, sb, gi, out=out, a_dtype=w.a_fmt, b_dtype=w.b_fmt)
+    t = timer.run(fn, steps, warmup)
+    valid = int((w.grp_idx >= 0).sum())
+    t["tflops_kernel"] = 2.0 * valid * N * K / (t["kernel_ms_mean"] * 1e-3) / 1e12
+    del a, b, sa, sb, gi, out
+    return t
+
+
 def bench_contig(torch, f, w, steps, warmup, timer):
     M_total, K = w.A.shape
     G, N, _ = w.B.shape
@@ -362,7 +376,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: dense masked masked_bs contig small e5m2 blockscaled channelwise decode proj copy "
+                    help="subset of: dense masked masked_bs contig contig_bs small e5m2 blockscaled channelwise decode proj copy "
                          "(default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
@@ -391,8 +405,8 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     timer = Timer(torch)
-    want = set(args.only) if args.only else {"dense", "masked", "masked_bs", "contig", "small", "e5m2", "blockscaled", "channelwise", "decode", "proj",
-                                           "copy"}
+    want = set(args.only) if args.only else {"dense", "masked", "masked_bs", "contig", "contig_bs", "small", "e5m2", "blockscaled",
+                                           "channelwise", "decode", "proj", "copy"}
     steps, warmup = args.steps, args.warmup
     extra = {}
 
@@ -489,6 +503,17 @@ def main():
             "tflops_kernel_incl_padding": r["tflops_kernel_incl_padding"]}
         log(f"  {r['tflops_kernel']:.1f} TFLOP/s")
         del wc
+    if "contig_bs" in want:
+        log("generating block-scaled contiguous grouped prefill inputs")
+        wcb = workloads.contig_blockscaled(8192, 8, 32, 4096, 7168, seed=9)
+        r = bench_contig_blockscaled(torch, f, wcb, max(5, steps // 5), max(2, warmup // 5), timer)
+        extra["contig_grouped_blockscaled"] = {
+            "workload": "block-scaled contiguous grouped FP8 GEMM, 8192 tokens x top-8 over 32 experts, N=4096, "
+                        "K=7168, E8M0 scales per 1x128 token block and 128x128 weight block (seed 9)",
+            "tflops_kernel": r["tflops_kernel"], "kernel_ms_mean": r["kernel_ms_mean"],
+            "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS}
+        log(f"  {r['tflops_kernel']:.1f} TFLOP/s")
+        del wcb
     if "proj" in want:
         out = []
         for i in range(len(workloads.PROJECTION_SHAPES)):

@@ -39,7 +39,7 @@ class Plan(ctypes.Structure):
 
 
 SYMBOLS = ("fp8_gemm_nt", "fp8_gemm_nt_blockscaled", "fp8_gemm_nt_channelwise",
-           "fp8_grouped_gemm_masked_blockscaled", "fp8_grouped_gemm_masked", "fp8_grouped_gemm_contig",
+           "fp8_grouped_gemm_masked_blockscaled", "fp8_grouped_gemm_contig_blockscaled", "fp8_grouped_gemm_masked", "fp8_grouped_gemm_contig",
            "fp8_gemm_plan", "fp8_gemm_strerror", "fp8_gemm_abi_version")
 
 
@@ -64,6 +64,8 @@ def load_library(path: str = LIB_PATH):
     lib.fp8_grouped_gemm_masked_blockscaled.restype = I
     lib.fp8_grouped_gemm_contig.argtypes = [P, I, P, I, P, P, P, P, I, I, I, I, P]
     lib.fp8_grouped_gemm_contig.restype = I
+    lib.fp8_grouped_gemm_contig_blockscaled.argtypes = [P, I, P, I, P, I64, P, I64, P, P, I, I, I, I, P]
+    lib.fp8_grouped_gemm_contig_blockscaled.restype = I
     lib.fp8_gemm_plan.argtypes = [I, I, I, I, I, I, ctypes.POINTER(Plan)]
     lib.fp8_gemm_plan.restype = I
     lib.fp8_gemm_strerror.argtypes = [I]
@@ -330,4 +332,39 @@ def grouped_gemm_contig(a, b, scale_a, scale_b, grp_idx, out=None, a_dtype=None,
     _check(load_library().fp8_grouped_gemm_contig(a.data_ptr(), fa, b.data_ptr(), fb, scale_a.data_ptr(),
                                                   scale_b.data_ptr(), grp_idx.data_ptr(), out.data_ptr(),
                                                   M_total, G, N, K, _stream()))
+    return out
+
+
+def grouped_gemm_contig_blockscaled(a, b, scale_a, scale_b, grp_idx, out=None, a_dtype=None, b_dtype=None):
+    """Block-scaled contiguous grouped GEMM: a [M_total, K], b [G, N, K], grp_idx
+    int32 [M_total] (-1 = padding); scale_a uint8 E8M0 [ceil(K/128), lds_a >=
+    M_total], scale_b uint8 E8M0 [G, ceil(N/128), lds_b >= ceil(K/128)],
+    contiguous; out [M_total, N] bf16 (padding rows untouched)."""
+    torch = _torch()
+    fa = _fp8_code(a, a_dtype, "a")
+    fb = _fp8_code(b, b_dtype, "b")
+    if a.dim() != 2 or b.dim() != 3 or a.shape[1] != b.shape[2]:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} are not [M_total, K] and [G, N, K]")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous")
+    M_total, K = a.shape
+    G, N = b.shape[0], b.shape[1]
+    kb, nb = (K + 127) // 128, (N + 127) // 128
+    if scale_a.dtype != torch.uint8 or scale_a.dim() != 2 or scale_a.shape[0] != kb or scale_a.shape[1] < M_total \
+            or not scale_a.is_contiguous():
+        raise ValueError(f"scale_a must be a contiguous uint8 [{kb}, >= {M_total}] tensor")
+    if scale_b.dtype != torch.uint8 or scale_b.dim() != 3 or tuple(scale_b.shape[:2]) != (G, nb) \
+            or scale_b.shape[2] < kb or not scale_b.is_contiguous():
+        raise ValueError(f"scale_b must be a contiguous uint8 [{G}, {nb}, >= {kb}] tensor")
+    if grp_idx.dtype != torch.int32 or grp_idx.numel() != M_total or not grp_idx.is_contiguous():
+        raise ValueError("grp_idx must be a contiguous int32 tensor with M_total elements")
+    _require_cuda(a, b, scale_a, scale_b, grp_idx)
+    if out is None:
+        out = torch.empty((M_total, N), dtype=torch.bfloat16, device=a.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (M_total, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M_total, N] bfloat16 tensor")
+    _require_cuda(out)
+    _check(load_library().fp8_grouped_gemm_contig_blockscaled(
+        a.data_ptr(), fa, b.data_ptr(), fb, scale_a.data_ptr(), scale_a.shape[1], scale_b.data_ptr(),
+        scale_b.shape[2], grp_idx.data_ptr(), out.data_ptr(), M_total, G, N, K, _stream()))
     return out

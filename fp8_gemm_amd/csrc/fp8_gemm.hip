@@ -515,4 +515,44 @@ int fp8_gemm_nt_channelwise(const void *A, int64_t lda, int a_dtype, const void 
     return launch_tile128<fp8g::MODE_DENSE, fp8g::SCALE_CHANNEL>(fa, fb, p, grid, s);
 }
 
+int fp8_grouped_gemm_contig_blockscaled(const void *A, int a_dtype, const void *B, int b_dtype,
+                                        const uint8_t *scale_a, int64_t lds_a, const uint8_t *scale_b, int64_t lds_b,
+                                        const int32_t *grp_idx, void *D, int M_total, int G, int N, int K,
+                                        void *stream) {
+    if (!dtype_ok(a_dtype) || !dtype_ok(b_dtype)) return fail(FP8G_ERR_DTYPE, "dtypes %d, %d", a_dtype, b_dtype);
+    if (G < 0 || M_total < 0) return fail(FP8G_ERR_SHAPE, "negative G=%d or M_total=%d", G, M_total);
+    fp8g_plan plan;
+    int st = plan_impl(2, M_total, N, K, G, 0, &plan);
+    if (st != FP8G_OK) return st;
+    if (plan.variant == V_NONE) return ok();
+    if ((K > 0 && (!A || !B || !scale_a || !scale_b)) || !D || !grp_idx)
+        return fail(FP8G_ERR_NULL, "A, B, scale_a, scale_b (unless K = 0), D and grp_idx are required");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return fail(FP8G_ERR_ALIGN, "A, B and D must be 16-byte aligned");
+    if (!aligned4(scale_a) || !aligned4(scale_b) || !aligned4(grp_idx))
+        return fail(FP8G_ERR_ALIGN, "scale arrays and grp_idx must be 4-byte aligned");
+    if (N % 8) return fail(FP8G_ERR_ALIGN, "N=%d: rows of D must stay 16-byte aligned (N %% 8 == 0)", N);
+    const int64_t kb = cdiv(K, 128), nb = cdiv(N, 128);
+    if (lds_a < M_total || lds_b < kb)
+        return fail(FP8G_ERR_STRIDE, "lds_a=%lld below M_total=%d or lds_b=%lld below ceil(K/128)=%lld",
+                    (long long)lds_a, M_total, (long long)lds_b, (long long)kb);
+    if (lds_a % 4 || lds_b % 4) return fail(FP8G_ERR_ALIGN, "lds_a=%lld / lds_b=%lld not multiples of 4", (long long)lds_a, (long long)lds_b);
+    if (kb * lds_a > INT32_MAX - 256 || nb * lds_b > INT32_MAX - 256)
+        return fail(FP8G_ERR_STRIDE, "scale array above 2^31 bytes");
+    if ((st = check_device()) != FP8G_OK) return st;
+
+    GemmParams p = {};
+    p.A = static_cast<const uint8_t *>(A);
+    p.B = static_cast<const uint8_t *>(B);
+    p.D = static_cast<uint16_t *>(D);
+    p.lda = K; p.ldb = K; p.ldd = N;
+    p.b_gstride = (int64_t)N * K;
+    p.M = M_total; p.N = N; p.K = K; p.G = G; p.cap = M_total;
+    p.grp_idx = grp_idx;
+    p.sfa = scale_a; p.sfb = scale_b; p.lds_sa = lds_a; p.lds_sb = lds_b;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    p.tiles_m = (int)cdiv(M_total, 2 * kContigAlign);
+    p.tiles_n = (int)cdiv(N, 256);
+    return launch_tile256<fp8g::MODE_CONTIG, fp8g::SCALE_BLOCK>(a_dtype, b_dtype, p, dim3((unsigned)plan.workgroups), s);
+}
+
 }  // extern "C"

@@ -167,8 +167,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     constexpr int STAGE_OUT = BM * BN * 2;         // BF16 output tile staged for the stores
     // Block scales (BLK): per ring slot, the step's scale of each tile row of A
     // (bytes 0..BM-1) and one dword per 128-row block of B (from byte 256).
-    static_assert(!BLK || (MODE != MODE_CONTIG && BK == 128 && BM <= 256 && BN % 128 == 0),
-                  "block scales: dense and masked forms, 128-byte K steps");
+    static_assert(!BLK || (BK == 128 && BM <= 256 && BN % 128 == 0), "block scales: 128-byte K steps");
     static_assert(!CHN || MODE == MODE_DENSE, "per-channel scales: dense form");
     constexpr int SCS = BLK ? 512 : 0;
     constexpr int RING = STAGES * (SLOT + SCS);
@@ -299,8 +298,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     const int64_t sb_bytes = (int64_t)((p.N + 127) / 128) * p.lds_sb;
     const v4i srdSA = BLK ? make_srd(p.sfa + (MODE == MODE_MASKED ? (int64_t)g * sa_bytes : 0), (uint32_t)sa_bytes)
                           : v4i{0, 0, 0, 0};
-    const v4i srdSB = BLK ? make_srd(p.sfb + (MODE == MODE_MASKED ? (int64_t)g * sb_bytes : 0), (uint32_t)sb_bytes)
-                          : v4i{0, 0, 0, 0};
+    // weight-block scales: per group (masked) or per expert (contiguous);
+    // token-row scales: per group (masked) or by global row (contiguous)
+    const int64_t sb_group = MODE == MODE_MASKED ? g : (MODE == MODE_CONTIG ? expert : 0);
+    const v4i srdSB = BLK ? make_srd(p.sfb + sb_group * sb_bytes, (uint32_t)sb_bytes) : v4i{0, 0, 0, 0};
     const uint32_t scl_base = lds0 + STAGES * SLOT;
     auto issue_scales = [&](int kt) {
         if (!BLK || wave != 0) return;

@@ -199,6 +199,27 @@ int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dty
                             int M_total, int G, int N, int K, void *stream);
 
 /*
+ * Block-scaled contiguous grouped GEMM (MoE prefill with the block-scaled
+ * format of fp8_gemm_nt_blockscaled).
+ *   A, B, grp_idx, D, M_total, G, N, K: as for fp8_grouped_gemm_contig.
+ *   scale_a: E8M0 codes (uint8, device), [ceil(K/128)][lds_a]: the scale of row
+ *     r of A over K block kb at scale_a[kb * lds_a + r].  lds_a >= M_total,
+ *     lds_a % 4 == 0.
+ *   scale_b: E8M0 codes (uint8, device), [G][ceil(N/128)][lds_b]: rows
+ *     128 nb .. 128 nb + 127 of expert e over K block kb at
+ *     scale_b[(e * ceil(N/128) + nb) * lds_b + kb].  lds_b >= ceil(K/128), lds_b % 4 == 0.
+ *   Code 255 is NaN.  Scale arrays 4-byte aligned and below 2^31 bytes (per expert for scale_b).
+ *   Row r with a valid expert e = grp_idx[r]:
+ *     D[r][j] = bf16_rne( sum_kb 2^(ea(r,kb) - 127) 2^(eb(e,j/128,kb) - 127) sum_{k in kb} A[r][k] B[e][j][k] ).
+ *   Padding rows are not written; their scale bytes may be read.
+ */
+int fp8_grouped_gemm_contig_blockscaled(const void *A, int a_dtype, const void *B, int b_dtype,
+                                        const uint8_t *scale_a, int64_t lds_a,
+                                        const uint8_t *scale_b, int64_t lds_b,
+                                        const int32_t *grp_idx, void *D,
+                                        int M_total, int G, int N, int K, void *stream);
+
+/*
  * Kernel choice for a problem, without launching anything (host only).
  *   op: 0 = dense (m = M), 1 = masked grouped (m = cap, hint = expected_m,
  *   groups = G), 2 = contiguous grouped (m = M_total, groups = G),

@@ -106,3 +106,40 @@ def test_decode_config_sampled():
         jj = np.tile(cols, rows.size)
         ref, r, s = oracle.gemm_nt_blockscaled_points(w.A[g], w.B[g], w.sa[g], w.sb[g], ii, jj)
         check(d[g][ii, jj], r, s, 1.0, None, ref_bits=ref, what=f"decode bs group {g}", strict=True)
+
+
+def run_contig(w):
+    M, K = w.A.shape
+    G, N, _ = w.B.shape
+    print(f"[contig bs] M_total={M} G={G} N={N} K={K}", flush=True)
+    out = torch.full((M, N), SENT - 65536, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    _f().grouped_gemm_contig_blockscaled(_dev(w.A), _dev(w.B), _dev(w.sa), _dev(w.sb), _dev(w.grp_idx), out=out,
+                                         a_dtype=0, b_dtype=0)
+    torch.cuda.synchronize()
+    return gpu_bits(out)
+
+
+def check_contig(w, d, rows=None, strict=False):
+    pad = w.grp_idx < 0
+    assert (d[pad] == SENT).all(), "a padding row was written"
+    real = np.flatnonzero(~pad)
+    if rows is not None:
+        real = np.unique(np.random.default_rng(3).choice(real, size=min(rows, real.size), replace=False))
+    for g in np.unique(w.grp_idx[real]):
+        rg = real[w.grp_idx[real] == g]
+        ref, r, s = oracle.gemm_nt_blockscaled(w.A[rg], w.B[g], w.sa[:, rg], w.sb[g])
+        allow = None if strict else hw_allowance_blockscaled(w.A[rg], w.B[g], 0, 0, w.sa[:, rg], w.sb[g], s)
+        check(d[rg], r, s, 1.0, allow, ref_bits=ref, what=f"{w.name} expert {g}", strict=strict)
+
+
+@pytest.mark.parametrize("counts", [[128, 256, 1, 127, 0, 300, 5], [100, 256, 300, 128]])
+def test_contig_expert_changes(counts):
+    """Expert changes inside 256-row tiles (the second-block workgroups) and
+    between them, ragged N and K, NaN padding rows and scales."""
+    w = workloads.contig_blockscaled(0, 1, len(counts), 264, 400, seed=70 + len(counts), counts=counts, lds_pad=6)
+    check_contig(w, run_contig(w))
+
+
+def test_contig_prefill_sampled():
+    w = workloads.contig_blockscaled(8192, 8, 32, 4096, 7168, seed=9)
+    check_contig(w, run_contig(w), rows=256, strict=True)

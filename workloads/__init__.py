@@ -314,3 +314,49 @@ def masked_decode_blockscaled():
     w = masked_blockscaled(32, 64, 4096, 7168, seed=8, m_max=32)
     w.name = "masked_decode_blockscaled_G32_cap64_4096x7168"
     return w
+
+
+@dataclass
+class ContigBlockScaled:
+    A: np.ndarray            # uint8 [M_total, K]
+    B: np.ndarray            # uint8 [G, N, K]
+    sa: np.ndarray           # uint8 E8M0 [ceil(K/128), lds_a] (global rows)
+    sb: np.ndarray           # uint8 E8M0 [G, ceil(N/128), lds_b]
+    grp_idx: np.ndarray      # int32 [M_total]
+    a_fmt: int = E4M3
+    b_fmt: int = E4M3
+    name: str = ""
+
+
+def contig_blockscaled(tokens, topk, G, N, K, seed, align=128, counts=None, lds_pad=0, std_b=0.02):
+    """Block-scaled contiguous grouped case: the expert layout of contig_random,
+    valid rows ~N(0,1) quantized per 1 x 128 block, each expert's weights
+    ~N(0, std_b) per 128 x 128 block, each block with its own power-of-two
+    scale; padding rows hold the NaN code and NaN scales (255), as does the
+    scale arrays' padding."""
+    rng = np.random.default_rng(seed)
+    if counts is None:
+        counts = rng.multinomial(tokens * topk, rng.dirichlet(np.ones(G)))
+    counts = np.asarray(counts, dtype=np.int64)
+    padded = ((counts + align - 1) // align) * align
+    M = int(padded.sum())
+    gi = np.full(M, -1, np.int32)
+    off = 0
+    for g in range(G):
+        gi[off:off + counts[g]] = g
+        off += int(padded[g])
+    kb, nb = (K + 127) // 128, (N + 127) // 128
+    lds_a = ((M + lds_pad + 3) // 4) * 4
+    lds_b = ((kb + lds_pad + 3) // 4) * 4
+    A = np.full((M, K), 0x7F, np.uint8)
+    sa = np.full((kb, lds_a), 255, np.uint8)
+    valid = np.flatnonzero(gi >= 0)
+    if valid.size:
+        A[valid], ea = _pow2_block_quantize(_normal(rng, (valid.size, K), 1.0), E4M3, 1)
+        sa[:, valid] = ea.T
+    B = np.empty((G, N, K), np.uint8)
+    sb = np.full((G, nb, lds_b), 255, np.uint8)
+    for g in range(G):
+        B[g], eb = _pow2_block_quantize(_normal(rng, (N, K), std_b), E4M3, 128)
+        sb[g, :, :kb] = eb
+    return ContigBlockScaled(A, B, sa, sb, gi, E4M3, E4M3, f"contig_bs_T{tokens}x{topk}_G{G}_{N}x{K}_s{seed}")

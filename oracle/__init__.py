@@ -22,7 +22,9 @@ documented at the top of ``fp8_oracle.c``:
   block, per row of A and per 128 rows of B (DeepGEMM on Hopper, section 5.2;
   SwapAB story, section 5),
 * the per-channel form: a scale per row of A, a scale and a bias per output
-  channel (DeepGEMM on Hopper, section 5.2).
+  channel (DeepGEMM on Hopper, section 5.2),
+* the BF16 comparison path: BF16 operands, no scales, the same FP64 sum and
+  one BF16 rounding (DeepGEMM on Hopper, section 1.3).
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against things other
 than itself: torch's FP8 conversions, exact rational arithmetic, closed forms,
@@ -90,6 +92,12 @@ def _load():
     lib.oracle_grouped_masked_blockscaled.restype = I
     lib.oracle_grouped_contig_blockscaled.argtypes = [P, I, P, I, P, I64, P, I64, P, P, P, P, I64, I64, I64, I64]
     lib.oracle_grouped_contig_blockscaled.restype = I
+    lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_value.restype = ctypes.c_double
+    lib.oracle_gemm_nt_bf16.argtypes = [P, I64, P, I64, P, I64, P, P, I64, I64, I64]
+    lib.oracle_gemm_nt_bf16.restype = I
+    lib.oracle_gemm_nt_bf16_points.argtypes = [P, I64, P, I64, I64, I64, P, P, P, P, P]
+    lib.oracle_gemm_nt_bf16_points.restype = I
     _lib = lib
     return lib
 
@@ -396,4 +404,57 @@ def grouped_contig_blockscaled(A, B, grp_idx, scale_a, scale_b, a_fmt=E4M3, b_fm
                                                    M, G, N, K)
     if rc != 0:
         raise RuntimeError(f"oracle_grouped_contig_blockscaled failed ({rc})")
+    return D, R, S
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("BF16 operands are passed as uint16 bit-pattern arrays")
+    return a
+
+
+def bf16_value(bits: int) -> float:
+    """Value of one BF16 bit pattern, decoded from its fields."""
+    return float(_load().oracle_bf16_value(int(bits) & 0xFFFF))
+
+
+def gemm_nt_bf16(A, B):
+    """BF16 comparison path D = bf16(A . B^T).  A: uint16 [M, K], B: uint16
+    [N, K] bit patterns.  Returns (D_bits uint16 [M, N], R float64 [M, N],
+    S float64 [M, N]): R is the FP64 sum before rounding, S = sum_k |a b|."""
+    A = _u16(A)
+    B = _u16(B)
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A and B disagree on K")
+    D = np.zeros((M, N), dtype=np.uint16)
+    R = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    if _load().oracle_gemm_nt_bf16(_ptr(A), K, _ptr(B), K, _ptr(D), N, _ptr(R), _ptr(S), M, N, K) != 0:
+        raise RuntimeError("oracle_gemm_nt_bf16 failed")
+    return D, R, S
+
+
+def gemm_nt_bf16_points(A, B, ii, jj):
+    """The BF16 comparison path at elements (ii[p], jj[p]) only: 1-D D, R, S."""
+    A = _u16(A)
+    B = _u16(B)
+    K = A.shape[1]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    if ii.shape != jj.shape:
+        raise ValueError("ii and jj differ in length")
+    if ii.size and (ii.min() < 0 or ii.max() >= A.shape[0] or jj.min() < 0 or jj.max() >= B.shape[0]):
+        raise IndexError("sample point outside the output")
+    n = ii.size
+    D = np.zeros(n, dtype=np.uint16)
+    R = np.zeros(n, dtype=np.float64)
+    S = np.zeros(n, dtype=np.float64)
+    if _load().oracle_gemm_nt_bf16_points(_ptr(A), K, _ptr(B), K, K, n, _ptr(ii), _ptr(jj),
+                                          _ptr(D), _ptr(R), _ptr(S)) != 0:
+        raise RuntimeError("oracle_gemm_nt_bf16_points failed")
     return D, R, S

@@ -49,6 +49,9 @@
  *     r = sa[m] * sb[n] * acc + bias[n] in FP64 (scale product first, then
  *     the accumulator, then the bias), one BF16 rounding.  A missing scale
  *     vector means 1, a missing bias 0.
+ *   - BF16 comparison path (DeepGEMM on Hopper, section 1.3): BF16 operands
+ *     (1 sign, 8 exponent, 7 mantissa bits; subnormals decoded), no scales,
+ *     D = bf16(sum_k a * b) with the sum in FP64 and one rounding.
  */
 #include <math.h>
 #include <pthread.h>
@@ -608,6 +611,74 @@ int oracle_grouped_contig_blockscaled(const uint8_t *A, int a_fmt, const uint8_t
                                             R ? R + r * N : NULL, S ? S + r * N : NULL, 1, N, K, 1);
         free(col);
         if (rc != 0) return rc;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* BF16 comparison path (DeepGEMM on Hopper, section 1.3: the backend keeps a */
+/* BF16 path for precision experiments).  Reading: D = bf16(A . B^T) with     */
+/* BF16 operands, no scales, the product sum in FP64 in order k = 0..K-1 and  */
+/* one BF16 rounding, exactly as the FP8 forms do after decoding.             */
+/* ------------------------------------------------------------------------- */
+
+/* Value of one BF16 bit pattern from its fields: sign, 8 exponent bits (bias
+ * 127), 7 mantissa bits; exponent 0 is zero / subnormal (m * 2^-133),
+ * exponent 255 is infinity (m = 0) or NaN.                                   */
+double oracle_bf16_value(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int e = (bits >> 7) & 0xFF;
+    int m = bits & 0x7F;
+    double v;
+    if (e == 0xFF) v = m ? NAN : INFINITY;
+    else if (e == 0) v = ldexp((double)m, -133);
+    else v = ldexp(128.0 + (double)m, e - 127 - 7);
+    return sign ? -v : v;
+}
+
+static void dot_bf16(const uint16_t *a, const uint16_t *b, int64_t K, double *acc_out, double *s_out)
+{
+    double acc = 0.0, s = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = oracle_bf16_value(a[k]) * oracle_bf16_value(b[k]);   /* exact: 8 x 8 significant bits */
+        acc += p;
+        s += fabs(p);
+    }
+    *acc_out = acc;
+    *s_out = s;
+}
+
+/* A [M][lda], B [N][ldb] BF16 bit patterns (K-contiguous rows); D [M][ldd]
+ * BF16 bits; R (the FP64 sum) and S (sum of |products|) optional, [M][ldd]. */
+int oracle_gemm_nt_bf16(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                        uint16_t *D, int64_t ldd, double *R, double *S,
+                        int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldd < N) return -1;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            double acc, sabs;
+            dot_bf16(A + i * lda, B + j * ldb, K, &acc, &sabs);
+            D[i * ldd + j] = oracle_bf16_rne(acc);
+            if (R) R[i * ldd + j] = acc;
+            if (S) S[i * ldd + j] = sabs;
+        }
+    return 0;
+}
+
+/* The same at selected elements (ii[p], jj[p]) only; D, R, S have npts entries. */
+int oracle_gemm_nt_bf16_points(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int64_t K,
+                               int64_t npts, const int64_t *ii, const int64_t *jj,
+                               uint16_t *D, double *R, double *S)
+{
+    if (K < 0 || npts < 0 || lda < K || ldb < K) return -1;
+    for (int64_t p = 0; p < npts; ++p) {
+        double acc, sabs;
+        dot_bf16(A + ii[p] * lda, B + jj[p] * ldb, K, &acc, &sabs);
+        D[p] = oracle_bf16_rne(acc);
+        if (R) R[p] = acc;
+        if (S) S[p] = sabs;
     }
     return 0;
 }

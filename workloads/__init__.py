@@ -30,6 +30,9 @@ section 4 table uses n=4096, k=7168):
                       with counts ~ Multinomial(65536, Dirichlet(1)); each group
                       padded to a multiple of 128 rows; padding rows hold the
                       E4M3 NaN code and grp_idx = -1; seed 5.
+* ``dense_bf16_square`` the draws of ``dense_square`` rounded to BF16 (torch's
+                      float32 -> bfloat16, nearest even) for the BF16
+                      comparison path.
 """
 from __future__ import annotations
 
@@ -360,3 +363,43 @@ def contig_blockscaled(tokens, topk, G, N, K, seed, align=128, counts=None, lds_
         B[g], eb = _pow2_block_quantize(_normal(rng, (N, K), std_b), E4M3, 128)
         sb[g, :, :kb] = eb
     return ContigBlockScaled(A, B, sa, sb, gi, E4M3, E4M3, f"contig_bs_T{tokens}x{topk}_G{G}_{N}x{K}_s{seed}")
+
+
+# ---------------------------------------------------------------------------
+# BF16 comparison path: the same kinds of draws rounded to BF16 instead of FP8.
+# ---------------------------------------------------------------------------
+@dataclass
+class DenseBF16:
+    A: np.ndarray            # uint16 [M, K] BF16 bit patterns
+    B: np.ndarray            # uint16 [N, K]
+    name: str = ""
+
+    @property
+    def shape(self):
+        return self.A.shape[0], self.B.shape[0], self.A.shape[1]
+
+
+def to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even of float32 values to BF16 bit patterns (uint16),
+    with torch's CPU float32 -> bfloat16 conversion."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def dense_bf16_random(M, N, K, seed, std=1.0):
+    """A, B ~ N(0, std^2) rounded to BF16."""
+    rng = np.random.default_rng(seed)
+    X = _normal(rng, (M, K), std)
+    Y = _normal(rng, (N, K), std)
+    return DenseBF16(to_bf16(X), to_bf16(Y), f"dense_bf16_{M}x{N}x{K}_s{seed}")
+
+
+def dense_bf16_square(n=4096):
+    """The draws of ``dense_square`` (seed 2, N(0,1) * 0.5) rounded to BF16
+    instead of FP8: the same problem on the comparison path."""
+    rng = np.random.default_rng(2)
+    X = _normal(rng, (n, n), 0.5)
+    Y = _normal(rng, (n, n), 0.5)
+    return DenseBF16(to_bf16(X), to_bf16(Y), f"dense_bf16_{n}")

@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 matrix peak (no sparsity)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 matrix peak (no sparsity)
 METRIC = "FP8 TFLOPS (+% MFMA peak) dense 4096³; HBM GB/s masked grouped m≤32"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -150,6 +151,25 @@ def bench_channelwise(torch, f, w, steps, warmup, timer):
     t = timer.run(fn, steps, warmup)
     t["tflops_kernel"] = 2.0 * M * N * K / (t["kernel_ms_mean"] * 1e-3) / 1e12
     del a, b, sa, sb, bias, out
+    return t
+
+
+def bench_bf16(torch, f, w, steps, warmup, timer):
+    """The BF16 comparison path at 4096^3, with torch's BF16 matmul (hipBLASLt)
+    on the same operands timed the same way, for context."""
+    import numpy as np
+
+    M, N, K = w.shape
+    a = torch.from_numpy(w.A.view(np.int16)).cuda().view(torch.bfloat16)
+    b = torch.from_numpy(w.B.view(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    t = timer.run(lambda: f.gemm_nt_bf16(a, b, out=out), steps, warmup)
+    t["tflops_kernel"] = 2.0 * M * N * K / (t["kernel_ms_mean"] * 1e-3) / 1e12
+    bt = b.t()
+    lib = timer.run(lambda: torch.matmul(a, bt, out=out), steps, warmup)
+    t["torch_matmul_tflops"] = 2.0 * M * N * K / (lib["kernel_ms_mean"] * 1e-3) / 1e12
+    t["torch_matmul_ms_mean"] = lib["kernel_ms_mean"]
+    del a, b, bt, out
     return t
 
 
@@ -376,7 +396,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: dense masked masked_bs contig contig_bs small e5m2 blockscaled channelwise decode proj copy "
+                    help="subset of: dense masked masked_bs contig contig_bs small e5m2 blockscaled channelwise bf16 decode "
+                         "proj copy "
                          "(default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
@@ -406,7 +427,7 @@ def main():
         sys.exit(1)
     timer = Timer(torch)
     want = set(args.only) if args.only else {"dense", "masked", "masked_bs", "contig", "contig_bs", "small", "e5m2", "blockscaled",
-                                           "channelwise", "decode", "proj", "copy"}
+                                           "channelwise", "bf16", "decode", "proj", "copy"}
     steps, warmup = args.steps, args.warmup
     extra = {}
 
@@ -445,6 +466,18 @@ def main():
             "tflops_kernel": r["tflops_kernel"], "kernel_ms_mean": r["kernel_ms_mean"],
             "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS}
         log(f"  {r['tflops_kernel']:.1f} TFLOP/s")
+    if "bf16" in want:
+        log("timing the BF16 comparison path, 4096^3")
+        wb = workloads.dense_bf16_square()
+        r = bench_bf16(torch, f, wb, steps, warmup, timer)
+        extra["dense_4096_bf16"] = {
+            "workload": "BF16 comparison GEMM 4096^3, the seed-2 draws of the FP8 case rounded to BF16, no scales",
+            "tflops_kernel": r["tflops_kernel"], "kernel_ms_mean": r["kernel_ms_mean"],
+            "roofline": {"bound": "mfma", "achieved": r["tflops_kernel"], "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": r["tflops_kernel"] / PEAK_BF16_TFLOPS},
+            "context_torch_matmul": {"tflops": r["torch_matmul_tflops"], "ms_mean": r["torch_matmul_ms_mean"]}}
+        log(f"  {r['tflops_kernel']:.1f} TFLOP/s (torch.matmul {r['torch_matmul_tflops']:.1f})")
+        del wb
     if "decode" in want:
         out = []
         for (N, K) in ((4096, 7168), (14336, 4096)):

@@ -40,7 +40,7 @@ class Plan(ctypes.Structure):
 
 SYMBOLS = ("fp8_gemm_nt", "fp8_gemm_nt_blockscaled", "fp8_gemm_nt_channelwise",
            "fp8_grouped_gemm_masked_blockscaled", "fp8_grouped_gemm_contig_blockscaled", "fp8_grouped_gemm_masked", "fp8_grouped_gemm_contig",
-           "fp8_gemm_plan", "fp8_gemm_strerror", "fp8_gemm_abi_version")
+           "bf16_gemm_nt", "fp8_gemm_plan", "fp8_gemm_strerror", "fp8_gemm_abi_version")
 
 
 def load_library(path: str = LIB_PATH):
@@ -66,6 +66,8 @@ def load_library(path: str = LIB_PATH):
     lib.fp8_grouped_gemm_contig.restype = I
     lib.fp8_grouped_gemm_contig_blockscaled.argtypes = [P, I, P, I, P, I64, P, I64, P, P, I, I, I, I, P]
     lib.fp8_grouped_gemm_contig_blockscaled.restype = I
+    lib.bf16_gemm_nt.argtypes = [P, I64, P, I64, P, I64, I, I, I, P]
+    lib.bf16_gemm_nt.restype = I
     lib.fp8_gemm_plan.argtypes = [I, I, I, I, I, I, ctypes.POINTER(Plan)]
     lib.fp8_gemm_plan.restype = I
     lib.fp8_gemm_strerror.argtypes = [I]
@@ -82,7 +84,8 @@ def _check(status: int):
 
 
 def plan(op: int, m: int, n: int, k: int, groups: int = 1, expected_m: int = 0) -> Plan:
-    """Kernel choice for a problem (no launch).  op: 0 dense, 1 masked, 2 contiguous."""
+    """Kernel choice for a problem (no launch).  op: 0 dense, 1 masked, 2 contiguous,
+    3 block-scaled dense, 4 BF16 dense (k in elements)."""
     out = Plan()
     _check(load_library().fp8_gemm_plan(op, m, n, k, groups, expected_m, ctypes.byref(out)))
     return out
@@ -161,6 +164,34 @@ def gemm_nt(a, b, scale_a, scale_b, out=None, a_dtype=None, b_dtype=None):
     _check(load_library().fp8_gemm_nt(a.data_ptr(), lda, fa, b.data_ptr(), ldb, fb,
                                       scale_a.data_ptr(), scale_b.data_ptr(), out.data_ptr(), ldd,
                                       M, N, K, _stream()))
+    return out
+
+
+def gemm_nt_bf16(a, b, out=None):
+    """BF16 comparison path: D[M, N] = bf16(a[M, K] . b[N, K]^T), a and b
+    bfloat16 (or int16 / uint16 bit patterns), K-contiguous."""
+    torch = _torch()
+    for t, name in ((a, "a"), (b, "b")):
+        if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+            raise TypeError(f"{name} must be bfloat16 (or 16-bit bit patterns), got {t.dtype}")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} are not [M, K] and [N, K]")
+    if a.stride(1) != 1 or b.stride(1) != 1:
+        raise ValueError("a and b must be K-contiguous (stride(1) == 1)")
+    M, K = a.shape
+    N = b.shape[0]
+    _require_cuda(a, b)
+    if out is None:
+        n_pad = max(8, ((N + 7) // 8) * 8)
+        out = torch.empty((M, n_pad), dtype=torch.bfloat16, device=a.device)[:, :N]
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or (N > 1 and out.stride(1) != 1):
+        raise ValueError("out must be a [M, N] bfloat16 tensor with unit column stride")
+    _require_cuda(out)
+    lda = a.stride(0) if (M > 1 and K > 0) else max(8, ((K + 7) // 8) * 8)
+    ldb = b.stride(0) if (N > 1 and K > 0) else max(8, ((K + 7) // 8) * 8)
+    ldd = out.stride(0) if M > 1 else max(8, ((N + 7) // 8) * 8)
+    _check(load_library().bf16_gemm_nt(a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldd,
+                                       M, N, K, _stream()))
     return out
 
 

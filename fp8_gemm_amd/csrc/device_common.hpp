@@ -123,6 +123,24 @@ __device__ __forceinline__ v16f mfma32x32x64(v8i a, v8i b, v16f c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
 }
 
+// BF16 operands (the comparison path): a 32-byte fragment holds 16 BF16
+// values instead of 32 FP8 values.  Part 0 / 1 multiplies its first / second
+// 16 bytes with one v_mfma_f32_32x32x16_bf16.  Lane l's K elements in a part
+// are not the instruction's own k = 8 (l / 32) .. +8 but a fixed other set;
+// since A and B fragments come from the same byte offsets, both operands map
+// K the same way and the two parts together cover the fragment's K range once.
+constexpr int FMT_BF16 = 16;                   // outside the f8f6f4 format codes
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+template <int PART>
+__device__ __forceinline__ v16f mfma32x32x16_bf16_part(v8i a, v8i b, v16f c) {
+    const v4i ah = {a[4 * PART], a[4 * PART + 1], a[4 * PART + 2], a[4 * PART + 3]};
+    const v4i bh = {b[4 * PART], b[4 * PART + 1], b[4 * PART + 2], b[4 * PART + 3]};
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ah), __builtin_bit_cast(v8bf, bh), c,
+                                                   0, 0, 0);
+}
+
 template <int FA, int FB>
 __device__ __forceinline__ v4f mfma16x16x128(v8i a, v8i b, v4f c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);

@@ -90,8 +90,10 @@ int pick_dense_tile(int64_t M, int64_t N) {
 int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan *out) {
     memset(out, 0, sizeof *out);
     if (m < 0 || n < 0 || k < 0 || groups < 0) return fail(FP8G_ERR_SHAPE, "negative size (m=%d n=%d k=%d groups=%d)", m, n, k, groups);
-    if (k % 16 != 0) return fail(FP8G_ERR_SHAPE, "K=%d is not a multiple of 16", k);
-    if (k > kMaxRowStride) return fail(FP8G_ERR_SHAPE, "K=%d exceeds the row-stride limit %lld", k, (long long)kMaxRowStride);
+    // K in bytes: 16-byte chunks of the ring (BF16: 2 bytes per element)
+    const int64_t kbytes = op == 4 ? 2 * (int64_t)k : k;
+    if (kbytes % 16 != 0) return fail(FP8G_ERR_SHAPE, "K=%d is not a multiple of %d", k, op == 4 ? 8 : 16);
+    if (kbytes > kMaxRowStride) return fail(FP8G_ERR_SHAPE, "K=%d exceeds the row-stride limit %lld bytes", k, (long long)kMaxRowStride);
     if (op == 0) {
         if (m == 0 || n == 0) return ok();
         if (m <= kSwapMaxM) {
@@ -156,6 +158,15 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
         out->workgroups = cdiv(m, out->tile_m) * cdiv(n, 256);
         return ok();
     }
+    if (op == 4) {
+        // BF16 comparison path: always the tiled kernel.
+        if (m == 0 || n == 0) return ok();
+        out->variant = pick_dense_tile(m, n);
+        out->tile_m = out->variant == V_TILE_256x256 ? 256 : 128;
+        out->tile_n = 256;
+        out->workgroups = cdiv(m, out->tile_m) * cdiv(n, 256);
+        return ok();
+    }
     return fail(FP8G_ERR_ARG, "unknown op %d", op);
 }
 
@@ -189,6 +200,12 @@ int launch_ring(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     const dim3 block(64 * WM * WN);
 #define FP8G_RING(FA, FB) \
     hipLaunchKernelGGL((fp8g::ring_kernel<BM, BN, WM, WN, FA, FB, MODE, STAGES, BK, SCL>), grid, block, 0, s, p)
+    if constexpr (MODE == fp8g::MODE_DENSE && SCL == fp8g::SCALE_TENSOR) {
+        if (fa == fp8g::FMT_BF16) {
+            FP8G_RING(fp8g::FMT_BF16, fp8g::FMT_BF16);
+            return launch_status("tiled kernel (BF16)");
+        }
+    }
     if (fa == 0 && fb == 0) FP8G_RING(0, 0);
     else if (fa == 0 && fb == 1) FP8G_RING(0, 1);
     else if (fa == 1 && fb == 0) FP8G_RING(1, 0);
@@ -320,6 +337,38 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t 
     const dim3 grid((unsigned)plan.workgroups);
     if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE>(fa, fb, p, grid, s);
     return launch_tile128<fp8g::MODE_DENSE>(fa, fb, p, grid, s);
+}
+
+int bf16_gemm_nt(const void *A, int64_t lda, const void *B, int64_t ldb, void *D, int64_t ldd, int M, int N, int K,
+                 void *stream) {
+    fp8g_plan plan;
+    int st = plan_impl(4, M, N, K, 1, 0, &plan);
+    if (st != FP8G_OK) return st;
+    if (plan.variant == V_NONE) return ok();
+    if ((K > 0 && (!A || !B)) || !D) return fail(FP8G_ERR_NULL, "A, B (unless K = 0) and D are required");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return fail(FP8G_ERR_ALIGN, "A, B and D must be 16-byte aligned");
+    if (lda < K || ldb < K) return fail(FP8G_ERR_STRIDE, "lda=%lld / ldb=%lld below K=%d", (long long)lda, (long long)ldb, K);
+    if (lda % 8 || ldb % 8) return fail(FP8G_ERR_ALIGN, "lda=%lld / ldb=%lld not multiples of 8 elements", (long long)lda, (long long)ldb);
+    if (2 * lda > kMaxRowStride || 2 * ldb > kMaxRowStride)
+        return fail(FP8G_ERR_STRIDE, "row stride above %lld bytes", (long long)kMaxRowStride);
+    if (ldd < N) return fail(FP8G_ERR_STRIDE, "ldd=%lld below N=%d", (long long)ldd, N);
+    if (ldd % 8) return fail(FP8G_ERR_ALIGN, "ldd=%lld not a multiple of 8 elements", (long long)ldd);
+    if ((st = check_device()) != FP8G_OK) return st;
+
+    // The tiled kernel counts K and the operand strides in bytes.
+    GemmParams p = {};
+    p.A = static_cast<const uint8_t *>(A);
+    p.B = static_cast<const uint8_t *>(B);
+    p.D = static_cast<uint16_t *>(D);
+    p.lda = 2 * lda; p.ldb = 2 * ldb; p.ldd = ldd;
+    p.M = M; p.N = N; p.K = 2 * K; p.G = 1; p.cap = M;
+    p.tiles_m = (int)cdiv(M, plan.tile_m);
+    p.tiles_n = (int)cdiv(N, plan.tile_n);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)plan.workgroups);
+    if (plan.variant == V_TILE_256x256)
+        return launch_tile256<fp8g::MODE_DENSE>(fp8g::FMT_BF16, fp8g::FMT_BF16, p, grid, s);
+    return launch_tile128<fp8g::MODE_DENSE>(fp8g::FMT_BF16, fp8g::FMT_BF16, p, grid, s);
 }
 
 int fp8_grouped_gemm_masked(const void *A, int a_dtype, const void *B, int b_dtype, const float *scale_a,

@@ -1,22 +1,26 @@
 // gfx950 FP8 GEMM kernels.
 //
-// Both kernels compute D = bf16(sa * sb * A . B^T) with A [m x K] (tokens) and
+// The kernels compute D = bf16(sa * sb * A . B^T) with A [m x K] (tokens) and
 // B [n x K] (weights), both K-contiguous ("nt"), and put B's rows on the
 // matrix-core instruction's first (row) operand and A's rows on its second
 // (column) operand.  Each lane's accumulator registers then hold four
 // consecutive output columns n of one output row m, so the epilogue writes
 // 8-byte packed BF16 runs straight from registers.
 //
-//   tile_kernel    LDS-tiled: a BM x BN output tile per workgroup, K in steps
+//   ring_kernel    LDS-tiled: a BM x BN output tile per workgroup, K in steps
 //                  of 128 bytes, both operand tiles staged through a
-//                  double-buffered, XOR-swizzled LDS ring; v_mfma 32x32x64.
-//                  Dense (M > 64), masked grouped with many rows per group,
-//                  and contiguous grouped.
+//                  direct-to-LDS, XOR-swizzled ring; v_mfma 32x32x64.  Dense
+//                  (M > 64), masked grouped with many rows per group,
+//                  contiguous grouped, and the BF16 comparison path (same
+//                  bytes, two v_mfma 32x32x16 BF16 per fragment).
 //   swap_kernel    streaming "swap-AB" form for few tokens: each wave streams
 //                  its own weight rows from HBM straight into registers in the
 //                  16x16x128 operand layout (no LDS: every weight byte is used
 //                  by exactly one wave), tokens ride on the 16-wide column side
-//                  in blocks of 16.  Dense M <= 64 and masked grouped decode.
+//                  in blocks of 16.  Masked grouped decode.
+//   decode_kernel  the same idea for the dense form with M <= 64: 8 waves
+//                  split K, 16 weight rows per workgroup, tokens loaded into
+//                  registers, partial sums reduced through LDS.
 //
 // "DeepGEMM: FP8 matrix-multiply kernels on Hopper Tensor Cores" is the prior
 // art for the tiled form (section 2.3 three-level tiling, section 3.3 double
@@ -152,6 +156,11 @@ __device__ __forceinline__ uint32_t ring_key(uint32_t row) {
 template <int BM, int BN, int WM, int WN, int FA, int FB, int MODE, int STAGES, int BK, int SCL>
 __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     constexpr bool BLK = SCL == SCALE_BLOCK, CHN = SCL == SCALE_CHANNEL;
+    // BF16 operands: the ring moves bytes, so K, lda and ldb arrive in bytes
+    // and only the instruction changes (see mfma32x32x16_bf16_part).
+    constexpr bool BF = FA == FMT_BF16;
+    static_assert(BF == (FB == FMT_BF16), "BF16 operands come in pairs");
+    static_assert(!BF || (SCL == SCALE_TENSOR && MODE == MODE_DENSE), "BF16: dense form, no scales");
     constexpr int WAVES = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 
     const uint8_t *a_base = p.A + (MODE == MODE_MASKED ? (int64_t)g * p.a_gstride : 0) + (int64_t)m0 * p.lda;
     const uint8_t *b_base = p.B + (int64_t)expert * p.b_gstride + (int64_t)n0 * p.ldb;
-    const float sc = SCL != SCALE_TENSOR ? 1.0f : p.scale_a[0] * p.scale_b[MODE == MODE_DENSE ? 0 : expert];
+    const float sc = (SCL != SCALE_TENSOR || BF) ? 1.0f : p.scale_a[0] * p.scale_b[MODE == MODE_DENSE ? 0 : expert];
 
     // Rows past rows_m / rows_n fall outside the descriptors: the DMA writes
     // zeros for them and issues no memory transaction.
@@ -383,17 +392,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     // stall the wave's in-order issue while their queues drain, and the MFMAs
     // queued behind them wait with them; spread out, they issue in the
     // shadow of the MFMAs.
-    constexpr int NMF = FN * FM;                   // MFMAs per K half
+    // With BF16 operands each tile takes two instructions per K half (one per
+    // 16-byte part of its fragments); all tiles' first parts come before their
+    // second parts, so consecutive instructions never chain on one accumulator.
+    constexpr int NT = FN * FM;                    // accumulator tiles
+    constexpr int NMF = NT * (BF ? 2 : 1);         // MFMA instructions per K half
     constexpr int NFR = FN + FM;                   // fragments per K half
     auto mma_mixed = [&](const v8i (&bf)[FN], const v8i (&af)[FM], v8i (&nb)[FN], v8i (&na)[FM],
                          const uint8_t *read_slot, int read_h, int refill_kt) {
 #pragma unroll
         for (int t = 0; t < NMF; ++t) {
-            if (BLK)
-                acc[t / FM][t % FM] = mfma32x32x64_s<FB, FA>(bf[t / FM], af[t % FM], acc[t / FM][t % FM],
-                                                             scB, scA[t % FM]);
-            else
-                acc[t / FM][t % FM] = mfma32x32x64<FB, FA>(bf[t / FM], af[t % FM], acc[t / FM][t % FM]);
+            const int i = (t % NT) / FM, j = (t % NT) % FM;
+            if (BF) {
+                if (t < NT) acc[i][j] = mfma32x32x16_bf16_part<0>(bf[i], af[j], acc[i][j]);
+                else acc[i][j] = mfma32x32x16_bf16_part<1>(bf[i], af[j], acc[i][j]);
+            } else if (BLK) {
+                acc[i][j] = mfma32x32x64_s<FB, FA>(bf[i], af[j], acc[i][j], scB, scA[j]);
+            } else {
+                acc[i][j] = mfma32x32x64<FB, FA>(bf[i], af[j], acc[i][j]);
+            }
             if (BLK && t == 0 && refill_kt >= 0) read_scales(refill_kt - STAGES + 1);
             // fragments of the next half: NFR reads spread over the NMF MFMAs
 #pragma unroll

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FP8G_ABI_VERSION 2
+#define FP8G_ABI_VERSION 3
 
 typedef enum { FP8G_E4M3 = 0, FP8G_E5M2 = 1 } fp8g_dtype;
 
@@ -136,6 +136,24 @@ int fp8_gemm_nt_channelwise(const void *A, int64_t lda, int a_dtype,
                             const float *scale_a, const float *scale_b, const float *bias,
                             void *D, int64_t ldd,
                             int M, int N, int K, void *stream);
+
+/*
+ * BF16 comparison GEMM ("DeepGEMM: FP8 matrix-multiply kernels on Hopper
+ * Tensor Cores", section 1.3: the backend keeps a BF16 path for precision
+ * experiments beside the default FP8 path).
+ *   A: [M][lda] BF16 (device), K-contiguous rows; B: [N][ldb] BF16 (device).
+ *   D: [M][ldd] BF16 (device).
+ *   D[i][j] = bf16_rne( sum_k A[i][k] * B[j][k] ): no scales; the products are
+ *     exact and the matrix cores sum them in FP32.
+ *   Strides in elements: lda, ldb >= K and multiples of 8 (16 bytes), at most
+ *     (2^23 - 16) / 2; ldd >= N, a multiple of 8.  K % 8 == 0.  A, B, D
+ *     16-byte aligned.  K = 0 writes zeros.
+ * The LDS-tiled kernel of the FP8 dense form with M > 64 (tile chosen the same
+ * way, for every M): it stages the same bytes, and each 32-byte fragment feeds
+ * two BF16 instructions instead of one FP8 instruction.
+ */
+int bf16_gemm_nt(const void *A, int64_t lda, const void *B, int64_t ldb,
+                 void *D, int64_t ldd, int M, int N, int K, void *stream);
 
 /*
  * Masked grouped GEMM (MoE decode).
@@ -223,7 +241,8 @@ int fp8_grouped_gemm_contig_blockscaled(const void *A, int a_dtype, const void *
  * Kernel choice for a problem, without launching anything (host only).
  *   op: 0 = dense (m = M), 1 = masked grouped (m = cap, hint = expected_m,
  *   groups = G), 2 = contiguous grouped (m = M_total, groups = G),
- *   3 = block-scaled dense (m = M).
+ *   3 = block-scaled dense (m = M), 4 = BF16 dense (m = M, k in BF16
+ *   elements).
  * Fills the variant id, the tile sizes along M and N, and the number of
  * workgroups of the launch.  Returns an fp8g_status (validation as above,
  * pointers excepted).

@@ -167,3 +167,45 @@ def check(d_bits, r, s, scale_abs, allowance=None, ref_bits=None, what="", stric
 def assert_within_bound(d_bits, r, s, scale_abs, ref_bits=None, what=""):
     """Bound (1) alone (used where the inputs make the truncation irrelevant)."""
     return check(d_bits, r, s, scale_abs, None, ref_bits, what, strict=True)[1]
+
+
+
+def _bf16_group_weights(bits, group):
+    """[rows, ceil(K/group)]: 2^floor(log2(max |x|)) over each aligned group of
+    BF16 values (0 for an all-zero group; non-finite values are ignored)."""
+    v = np.abs(bf16_bits_to_f64(bits))
+    v[~np.isfinite(v)] = 0.0
+    rows, K = v.shape
+    G = (K + group - 1) // group
+    if K % group:
+        v = np.pad(v, ((0, 0), (0, G * group - K)))
+    mx = v.reshape(rows, G, group).max(axis=2)
+    out = np.zeros_like(mx)
+    nz = mx > 0
+    out[nz] = np.exp2(np.floor(np.log2(mx[nz])))
+    return out
+
+
+def hw_allowance_bf16(A, B, S, ii=None, jj=None):
+    """Allowance of the BF16 comparison path (A, B: BF16 bit patterns; S: sum
+    of |products|), measured by tests/test_gpu_bf16.py: inside one BF16
+    instruction the (exact) products are cut toward zero to multiples of
+    2^(E - 24), E the exponent of the instruction's largest product, and the
+    sum is rounded to FP32.  An instruction's 16 K indices lie in one aligned
+    group of 32 (the tiled kernel's 64-byte K half), two instructions per
+    group, so with ea / eb the group's floor(log2 max |a|) / |b| (E <= ea + eb
+    + 1) the cut costs less than 32 * 2^(ea + eb + 1 - 24) per group:
+
+        H_bf = 2^-18 * sum_g 2^(ea_g) 2^(eb_g)
+
+    plus F of the module docstring for the FP32 roundings.  Full [M, N]
+    output, or points (ii, jj)."""
+    K = A.shape[1]
+    F = (max(K, 8) / 8.0) * 2.0 ** -24 * np.asarray(S, dtype=np.float64)
+    if ii is None:
+        return 2.0 ** -18 * (_bf16_group_weights(A, 32) @ _bf16_group_weights(B, 32).T) + F
+    ui, inv_i = np.unique(ii, return_inverse=True)
+    uj, inv_j = np.unique(jj, return_inverse=True)
+    wa = _bf16_group_weights(A[ui], 32)
+    wb = _bf16_group_weights(B[uj], 32)
+    return 2.0 ** -18 * np.einsum("pg,pg->p", wa[inv_i], wb[inv_j]) + F

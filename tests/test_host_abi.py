@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(f):
 
 
 def test_abi_version(f):
-    assert f.load_library().fp8_gemm_abi_version() == 2
+    assert f.load_library().fp8_gemm_abi_version() == 3
 
 
 @pytest.mark.parametrize("args,variant", [
@@ -92,7 +92,9 @@ def test_contig_plan(f):
     ((0, 10, 10, 17), -2),       # K % 16
     ((0, -1, 10, 16), -2),
     ((0, 10, 10, 1 << 23), -2),  # K above the stride limit
-    ((4, 10, 10, 16), -8),       # unknown op
+    ((5, 10, 10, 16), -8),       # unknown op
+    ((4, 10, 10, 12), -2),       # BF16: K % 8
+    ((4, 10, 10, 1 << 22), -2),  # BF16: 2 K bytes above the stride limit
 ])
 def test_plan_errors(f, args, status):
     with pytest.raises(f.Fp8GemmError) as e:
@@ -222,4 +224,31 @@ def test_channelwise_validation(f):
     assert call(sa=A16 + 2) == -3                 # row scales 4-byte aligned
     assert call(ldd=100) == -5
     assert call(a=7) == -4
+    assert call(M=0, A=None) == 0
+
+
+def test_bf16_plan(f):
+    assert (f.plan(4, 4096, 4096, 4096).variant, f.plan(4, 4096, 4096, 4096).workgroups) == (1, 256)
+    assert f.plan(4, 2048, 4096, 4096).variant == 2
+    assert f.plan(4, 1, 4096, 4096).variant == 2          # no decode kernel: always tiled
+    assert f.plan(4, 64, 64, 8).variant == 2                # K % 8 suffices
+    assert f.plan(4, 0, 64, 8).variant == 0
+
+
+def test_bf16_validation(f):
+    lib = f.load_library()
+    ok = dict(A=A16, lda=256, B=A16, ldb=256, D=A16, ldd=256, M=128, N=256, K=256)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.bf16_gemm_nt(a["A"], a["lda"], a["B"], a["ldb"], a["D"], a["ldd"], a["M"], a["N"], a["K"], None)
+    assert call(A=None) == -1
+    assert call(D=None) == -1
+    assert call(B=A_ODD) == -3
+    assert call(lda=260) == -3                    # strides in elements, multiples of 8
+    assert call(lda=248) == -5                    # below K
+    assert call(ldb=1 << 22) == -5                # 2^23 bytes
+    assert call(ldd=200) == -5
+    assert call(K=12, lda=16, ldb=16) == -2
     assert call(M=0, A=None) == 0

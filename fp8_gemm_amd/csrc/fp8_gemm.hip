@@ -246,17 +246,18 @@ int launch_swap(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipStrea
     return launch_swap_cb<4, MODE, SCL>(fa, fb, p, grid, s);
 }
 
-// Decode kernel: steps of loads in flight per wave, fewer with more token
-// blocks (their registers grow with the token count), so that two
-// workgroups fit on a CU (at most 128 VGPRs): one workgroup's load latency
-// then overlaps another's streaming (measured better than deeper pipelines
-// with one workgroup per CU).
+// Decode kernel: 4 waves per 16 weight rows and per-wave LDS rings of 5, 3 or
+// 2 steps for 1, 2 or 4 token blocks (at most 80 KB, so two workgroups share
+// a CU; measured best against 8 waves and deeper rings with one workgroup per
+// CU).  Block scales add 512 bytes per slot.
+constexpr int kDecodeWaves = 4;
+
 template <int CB, int SCL>
 int launch_decode_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    constexpr int DEPTH = CB == 1 ? 4 : (CB == 2 ? 3 : 2);
-    const dim3 block(512);
+    constexpr int D = CB == 1 ? 5 : (CB == 2 ? 3 : 2);
+    const dim3 block(64 * kDecodeWaves);
 #define FP8G_DEC(FA, FB) \
-    hipLaunchKernelGGL((fp8g::decode_kernel<CB, FA, FB, DEPTH, SCL>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((fp8g::decode_kernel<kDecodeWaves, CB, FA, FB, D, SCL>), grid, block, 0, s, p)
     if (fa == 0 && fb == 0) FP8G_DEC(0, 0);
     else if (fa == 0 && fb == 1) FP8G_DEC(0, 1);
     else if (fa == 1 && fb == 0) FP8G_DEC(1, 0);

@@ -18,9 +18,11 @@
 //                  16x16x128 operand layout (no LDS: every weight byte is used
 //                  by exactly one wave), tokens ride on the 16-wide column side
 //                  in blocks of 16.  Masked grouped decode.
-//   decode_kernel  the same idea for the dense form with M <= 64: 8 waves
-//                  split K, 16 weight rows per workgroup, tokens loaded into
-//                  registers, partial sums reduced through LDS.
+//   decode_kernel  the same idea for the dense form with M <= 64: 4 waves
+//                  split K over 16 weight rows per workgroup; weights and
+//                  tokens are copied line by line into per-wave LDS rings and
+//                  read back in the 16x16x128 layout; the waves' partial sums
+//                  are added through LDS.
 //
 // "DeepGEMM: FP8 matrix-multiply kernels on Hopper Tensor Cores" is the prior
 // art for the tiled form (section 2.3 three-level tiling, section 3.3 double
@@ -719,101 +721,146 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel: the dense form with few tokens (M <= 64), swap-AB.
-// One workgroup of 8 waves per 16 weight rows (N = 4096 gives 256 workgroups);
-// the 128-byte K steps go round-robin to the waves, so at any time a
-// workgroup reads 8 consecutive K blocks of its rows.  Each wave streams its
-// weight rows and the matching token rows straight into registers in the
-// 16x16x128 operand layout, DEPTH steps ahead, and the 8 partial sums meet in
-// LDS at the end.  Splitting K inside the workgroup is what gives a small-N
-// problem enough workgroups and loads in flight to stream the weights at HBM
-// rate ("One transpose, half the compute: the DeepSeek SwapAB story", section
-// 1.1: with few tokens the work is weight-bandwidth bound).  The loads are
-// plain buffer loads, so the compiler derives every wait itself.
+// Decode kernel: the dense form with few tokens (M <= 64), swap-AB: weights on
+// the instruction's 16-row side, tokens in CB column blocks of 16 (section 1.1
+// of "One transpose, half the compute": with few tokens the work is bound by
+// weight bandwidth).  The 16x16x128 operand layout puts lane l on row l % 16, so loading
+// it straight from memory puts consecutive lanes on 16 different rows and
+// splits every 1 KB load instruction into 64 separate 16-byte accesses in the
+// vector memory pipeline (measured at M = 64, N = 4096, K = 7168: the token
+// loads alone took 16 of the 21 us, and 8.6 us with the same bytes read by
+// consecutive lanes).  Here each wave copies its K steps into its own LDS ring
+// with direct-to-LDS loads in which every 8 lanes read one whole 128-byte row
+// step (a full cache line), and reads the operand layout back with
+// ds_read_b128.  All loads of the main loop are these asynchronous copies, so
+// the waits are exact: vmcnt counts DMA instructions only.
+//   WAVES waves split K round-robin (step kt goes to wave kt % WAVES) over 16
+//   weight rows per workgroup (N = 4096 gives 256 workgroups); D ring slots per
+//   wave, each holding one K step of the 16 weight rows and the CB token blocks
+//   (and, with block scales, that step's scale bytes); the partial sums of the
+//   waves are added through LDS at the end.
 // ---------------------------------------------------------------------------
-template <int CB, int FA, int FB, int DEPTH, int SCL>
-__global__ __launch_bounds__(512, 4) void decode_kernel(GemmParams p) {   // 4 waves per SIMD: two workgroups per CU
-    constexpr int W = 8;
+template <int WAVES, int CB, int FA, int FB, int D, int SCL>
+__global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
     constexpr bool BLK = SCL == SCALE_BLOCK, CHN = SCL == SCALE_CHANNEL;
-    __shared__ __attribute__((aligned(16))) v4f red[W][CB][64];
+    constexpr int NB = 1 + CB;                     // 16-row blocks per step: weights, then tokens
+    constexpr int NQ = 2 * NB + (BLK ? 2 : 0);     // DMA instructions per step (8 rows x 128 B each,
+                                                   // and two 256-byte scale copies)
+    constexpr int SCS = BLK ? 512 : 0;             // scale bytes per slot
+    constexpr int SLOT = NB * 2048 + SCS;          // bytes per ring slot
+    constexpr int WRING = D * SLOT;                // bytes per wave
+    static_assert(D >= 2 && NQ * (D - 1) < 64, "ring depth");
+    constexpr int RED = WAVES * CB * 64 * 16;      // partial sums for the reduction
+    constexpr int SMEM = WAVES * WRING > RED ? WAVES * WRING : RED;
+    static_assert(SMEM <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n0 = blockIdx.x * 16;
     const int rows_w = min(p.N - n0, 16);
-    const int r16 = lane & 15;
-    const int kg = lane >> 4;
-    // Rows past N (weights) or past M (tokens) are outside the descriptors
-    // and read zeros without touching memory.
-    const __amdgpu_buffer_rsrc_t rsW = make_rsrc(p.B + (int64_t)n0 * p.ldb, rows_bytes(rows_w, p.ldb));
-    const __amdgpu_buffer_rsrc_t rsT = make_rsrc(p.A, rows_bytes(p.M, p.lda));
-    const uint32_t w_off = (uint32_t)r16 * (uint32_t)p.ldb + kg * 16;
-    uint32_t t_off[CB];
-#pragma unroll
-    for (int c = 0; c < CB; ++c) t_off[c] = (uint32_t)(c * 16 + r16) * (uint32_t)p.lda + kg * 16;
+    // Rows past N (weights) or past M (tokens) lie outside the descriptors and
+    // read zeros without touching memory.
+    const v4i srdW = make_srd(p.B + (int64_t)n0 * p.ldb, rows_bytes(rows_w, p.ldb));
+    const v4i srdT = make_srd(p.A, rows_bytes(p.M, p.lda));
     const int nk = (p.K + 127) / 128;
-    const int my = nk > wave ? (nk - wave + W - 1) / W : 0;   // steps kt = wave + W s of this wave
-    // Block scales: the weight block's scale is the same for every lane.
-    const __amdgpu_buffer_rsrc_t rsSA = make_rsrc(BLK ? p.sfa : p.A, BLK ? (uint32_t)(nk * p.lds_sa) : 0u);
-    const __amdgpu_buffer_rsrc_t rsSB = make_rsrc(BLK ? p.sfb : p.A, BLK ? (uint32_t)(((p.N + 127) / 128) * p.lds_sb) : 0u);
+    const int my = nk > wave ? (nk - wave + WAVES - 1) / WAVES : 0;   // steps kt = wave + WAVES s
+    const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem +
+                          (uint32_t)wave * WRING;
 
-    // (the scale arrays are below 2^31 bytes, so 32-bit offsets suffice)
-    const uint32_t lsa = (uint32_t)p.lds_sa, sb_row = (uint32_t)(n0 / 128) * (uint32_t)p.lds_sb;
-    v4u wr[DEPTH][2], tr[DEPTH][CB][2];
-    int ssa[DEPTH][CB], ssb[DEPTH];
-    // Lane (r16, kg) holds bytes kg*16 and 64 + kg*16 of each 128-byte K block
-    // of its row, for the weights and for each token block alike.
-    auto load = [&](int d, int s) {
-        const int kt = wave + W * s;
+    // Copy: instruction 2 b + h of a step fills rows 8 h .. 8 h + 7 of block b
+    // (b = 0: weights, b = 1 + c: token block c); lane l takes row 8 h + l / 8
+    // and deposits 16 bytes at position l % 8 of it, holding logical chunk
+    // (l % 8) ^ key(row), key(r) = (r >> 1) & 7.  That key puts the 16 rows of
+    // any one logical chunk on 16 different 16-byte bank groups for the reads.
+    const uint32_t drow = (uint32_t)lane >> 3;
+    const uint32_t dch0 = (((uint32_t)lane & 7u) ^ ((drow >> 1) & 7u)) * 16u;         // rows 0..7
+    const uint32_t dch1 = (((uint32_t)lane & 7u) ^ (((drow + 8u) >> 1) & 7u)) * 16u;  // rows 8..15
+    const uint32_t w0 = drow * (uint32_t)p.ldb + dch0, w1 = (drow + 8u) * (uint32_t)p.ldb + dch1;
+    uint32_t t0[CB], t1[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+        t0[c] = ((uint32_t)(16 * c) + drow) * (uint32_t)p.lda + dch0;
+        t1[c] = ((uint32_t)(16 * c) + drow + 8u) * (uint32_t)p.lda + dch1;
+    }
+    // Block scales of step kt (after the operands in the slot): the token
+    // rows' scales, 4 rows per lane from scale_a[kt][0 ..], and the dword of
+    // scale_b holding K block kt of the weights' 128-row block.  Token rows
+    // past M may read other in-range bytes, which only reach outputs not
+    // stored; reads past the arrays give zeros.
+    const v4i srdSA = BLK ? make_srd(p.sfa, (uint32_t)((int64_t)nk * p.lds_sa)) : v4i{0, 0, 0, 0};
+    const v4i srdSB = BLK ? make_srd(p.sfb, (uint32_t)((int64_t)((p.N + 127) / 128) * p.lds_sb)) : v4i{0, 0, 0, 0};
+    const uint32_t sb_row = (uint32_t)(n0 / 128) * (uint32_t)p.lds_sb;
+    auto issue = [&](int s, int slot) {
+        const int kt = wave + WAVES * s;
         const uint32_t k0 = (uint32_t)kt * 128u;
+        const bool ok = s < my;
+        const bool in0 = ok && (int)(k0 + dch0) < p.K, in1 = ok && (int)(k0 + dch1) < p.K;
+        const uint32_t base = ring + (uint32_t)slot * SLOT;
+        dma16(srdW, in0 ? w0 + k0 : kOobOffset, base);
+        dma16(srdW, in1 ? w1 + k0 : kOobOffset, base + 1024u);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const bool in = (s < my) && (int)(k0 + h * 64 + kg * 16) < p.K;
-            wr[d][h] = load16(rsW, in ? w_off + k0 + h * 64 : kOobOffset);
-#pragma unroll
-            for (int c = 0; c < CB; ++c) tr[d][c][h] = load16(rsT, in ? t_off[c] + k0 + h * 64 : kOobOffset);
+        for (int c = 0; c < CB; ++c) {
+            dma16(srdT, in0 ? t0[c] + k0 : kOobOffset, base + 2048u * (1 + c));
+            dma16(srdT, in1 ? t1[c] + k0 : kOobOffset, base + 2048u * (1 + c) + 1024u);
         }
         if (BLK) {
-            const bool in = s < my;
-            ssb[d] = __builtin_amdgcn_raw_buffer_load_b8(rsSB, in ? sb_row + (uint32_t)kt : kOobOffset, 0, 0);
-            const uint32_t row0 = (uint32_t)kt * lsa + (uint32_t)r16;
-#pragma unroll
-            for (int c = 0; c < CB; ++c)
-                ssa[d][c] = __builtin_amdgcn_raw_buffer_load_b8(rsSA, in ? row0 + c * 16 : kOobOffset, 0, 0);
+            const uint32_t sbase = base + NB * 2048u;
+            dma4(srdSA, ok && lane < 4 * CB ? (uint32_t)kt * (uint32_t)p.lds_sa + 4u * (uint32_t)lane : kOobOffset, sbase);
+            dma4(srdSB, ok && lane == 0 ? sb_row + ((uint32_t)kt & ~3u) : kOobOffset, sbase + 256u);
         }
     };
+
+    // Operand reads: lane (r16, kg) = (l % 16, l / 16) takes logical chunks kg
+    // and 4 + kg of row r16 of each block.
+    const int r16 = lane & 15;
+    const int kg = lane >> 4;
+    const uint32_t rkey = ((uint32_t)r16 >> 1) & 7u;
+    const uint32_t ro0 = (uint32_t)r16 * 128u + (((uint32_t)kg ^ rkey) * 16u);
+    const uint32_t ro1 = (uint32_t)r16 * 128u + (((uint32_t)(4 + kg) ^ rkey) * 16u);
+    const uint8_t *wbase = smem + wave * WRING;
 
     v4f acc[CB];
 #pragma unroll
     for (int c = 0; c < CB; ++c) acc[c] = (v4f){0, 0, 0, 0};
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) load(d, d);
-    for (int s0 = 0; s0 < my; s0 += DEPTH) {
+    for (int d = 0; d < D - 1; ++d) issue(d, d);
+    for (int s0 = 0; s0 < my; s0 += D) {
 #pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            const v8i wf = pack8(wr[d][0], wr[d][1]);
+        for (int d = 0; d < D; ++d) {
+            // refill the slot step s - 1 used (its reads have completed: their
+            // values fed the previous step's matrix instructions)
+            issue(s0 + d + D - 1, (d + D - 1) % D);
+            vmcnt_wait<(D - 1) * NQ>();            // step s0 + d has landed
+            const uint8_t *slot = wbase + d * SLOT;
+            const v8i wf = pack8(*reinterpret_cast<const v4u *>(slot + ro0), *reinterpret_cast<const v4u *>(slot + ro1));
+            const int kt = wave + WAVES * (s0 + d);
+            const int ssb = BLK ? slot[NB * 2048 + 256 + (kt & 3)] : 127;
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
-                const v8i tf = pack8(tr[d][c][0], tr[d][c][1]);
-                if (BLK) acc[c] = mfma16x16x128_s<FB, FA>(wf, tf, acc[c], ssb[d], ssa[d][c]);
+                const uint8_t *tb = slot + 2048 * (1 + c);
+                const v8i tf = pack8(*reinterpret_cast<const v4u *>(tb + ro0), *reinterpret_cast<const v4u *>(tb + ro1));
+                if (BLK) acc[c] = mfma16x16x128_s<FB, FA>(wf, tf, acc[c], ssb, slot[NB * 2048 + c * 16 + r16]);
                 else acc[c] = mfma16x16x128<FB, FA>(wf, tf, acc[c]);
             }
-            load(d, s0 + d + DEPTH);               // steps past this wave's last read zeros, untouched memory
-            __builtin_amdgcn_sched_barrier(0);     // keep each step's consume-then-refill order
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+    vmcnt_wait<0>();                               // drain the copies past the last step
+    __syncthreads();                               // every wave's ring is idle: reuse it
 
-    // Sum the 8 partial accumulators (fixed order), then scale, round and
-    // store: register q of a 16x16 block holds weight row 4 * kg + q and token
+    // Sum the WAVES partial accumulators (fixed order), then scale, round and
+    // store: register q of a 16x16 block holds weight row 4 kg + q and token
     // column r16, so a lane writes four consecutive outputs of one token row.
+    v4f *red = reinterpret_cast<v4f *>(smem);
 #pragma unroll
-    for (int c = 0; c < CB; ++c) red[wave][c][lane] = acc[c];
+    for (int c = 0; c < CB; ++c) red[(wave * CB + c) * 64 + lane] = acc[c];
     __syncthreads();
     if (wave < CB) {
         const int c = wave;
-        v4f sum = red[0][c][lane];
+        v4f sum = red[c * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < W; ++w) sum += red[w][c][lane];
+        for (int w = 1; w < WAVES; ++w) sum += red[(w * CB + c) * 64 + lane];
         const float sc = SCL != SCALE_TENSOR ? 1.0f : p.scale_a[0] * p.scale_b[0];
         const int tok = c * 16 + r16;
         if (tok < p.M) {

@@ -546,10 +546,15 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
     constexpr int WLOADS = RB * 2 + (BLK ? 1 : 0); // weight loads (and the block scale) per wave per stage
     constexpr int SDMA = BLK ? 1 : 0;              // token-scale DMA of wave 0 per stage
     constexpr int SCS = BLK ? 256 : 0;             // token-scale bytes per ring slot
+    constexpr int WSLOT = WR * ROWB;               // one stage of one wave's weight rows
+    constexpr int WRING = 4 * DEPTH * WSLOT;       // the four waves' weight rings
     static_assert(RB >= 1 && CB >= 1 && DEPTH >= 2, "shape");
     static_assert((DEPTH - 1) * (WLOADS + TDMA + SDMA) < 64, "loads in flight");
+    static_assert(WRING + TS * TSLOT + TS * SCS <= 160 * 1024, "LDS");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t tsm[TS * TSLOT + TS * SCS];
+    // [weight rings of the 4 waves | token ring | token-scale ring]
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[WRING + TS * TSLOT + TS * SCS];
+    uint8_t *const tsm = smem + WRING;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -570,7 +575,7 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
     const uint8_t *t_base = p.A + (int64_t)g * p.a_gstride;
     uint16_t *d_base = p.D + (int64_t)g * p.d_gstride;
     const float sc = BLK ? 1.0f : p.scale_a[0] * p.scale_b[g];
-    const __amdgpu_buffer_rsrc_t rsW = make_rsrc(w_base, rows_bytes(rows_w, p.ldb));
+    const v4i srdW = make_srd(w_base, rows_bytes(rows_w, p.ldb));
     // Block scales of group g: token rows [kb][lds_sa], weight blocks [nb][lds_sb];
     // this wave's 128 weight rows are one scale block.
     const int nk_ = (p.K + 127) / 128;
@@ -579,16 +584,30 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
     const __amdgpu_buffer_rsrc_t rsSB = make_rsrc(sb_g, BLK ? (uint32_t)(((p.N + 127) / 128) * p.lds_sb) : 0u);
     const uint32_t sb_row = BLK ? (uint32_t)(min(nw, p.N) / 128) * (uint32_t)p.lds_sb : 0u;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)tsm;
+    const uint32_t wlds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem +
+                          (uint32_t)wave * (DEPTH * WSLOT);
 
     // Operand layout used for both operands of v_mfma 16x16x128: lane l
     // carries row (l & 15) and, of each 128-byte K block, the bytes
-    // [(l >> 4) * 16, +16) and [64 + (l >> 4) * 16, +16).  So four lanes read
-    // 64 contiguous bytes of a weight row per load instruction.
+    // [(l >> 4) * 16, +16) and [64 + (l >> 4) * 16, +16).  Loaded straight
+    // from memory that layout puts consecutive lanes on 16 different rows, and
+    // each load instruction becomes 64 separate 16-byte accesses; copied
+    // through LDS with 8 lanes per 128-byte line, the same weight stream ran
+    // 3.5% faster (measured with the masked decode workload).  So each wave
+    // copies its 128 rows of a K step into its own LDS slot: instruction
+    // 2 r + h fills rows 16 r + 8 h .. +8, lane l taking row 16 r + 8 h + l / 8
+    // and storing logical chunk (l % 8) ^ key(row) at position l % 8, with
+    // key(row) = (row >> 1) & 7, so that the 16 rows of one chunk that a
+    // fragment read touches sit on 16 different bank groups.
     const int r16 = lane & 15;
     const int kg = lane >> 4;
-    uint32_t w_off[RB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) w_off[r] = (uint32_t)((int64_t)(r * 16 + r16) * p.ldb) + kg * 16;
+    const uint32_t wrow = (uint32_t)lane >> 3;
+    const uint32_t wch0 = (((uint32_t)lane & 7u) ^ ((wrow >> 1) & 7u)) * 16u;          // rows 0..7 of a block
+    const uint32_t wch1 = (((uint32_t)lane & 7u) ^ (((wrow + 8u) >> 1) & 7u)) * 16u;   // rows 8..15
+    const uint32_t wo0 = wrow * (uint32_t)p.ldb + wch0, wo1 = (wrow + 8u) * (uint32_t)p.ldb + wch1;
+    const uint32_t wkey = ((uint32_t)r16 >> 1) & 7u;
+    const uint32_t wf0 = (uint32_t)r16 * ROWB + (((uint32_t)kg ^ wkey) * 16u);
+    const uint32_t wf1 = (uint32_t)r16 * ROWB + (((uint32_t)(4 + kg) ^ wkey) * 16u);
 
     // Token DMA: instruction i of this wave covers staged rows
     // (wave * TDMA + i) * 8 .. +8; lane l deposits row l / 8, stored chunk
@@ -632,20 +651,21 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
 #pragma unroll
             for (int c = 0; c < CB; ++c) acc[r][c] = (v4f){0, 0, 0, 0};
 
-        v4u wreg[DEPTH][RB][2];
         int wscale[DEPTH];
 
-        // One stage: this wave's weight loads (registers), then its token DMA.
-        // Past the last K block every offset is out of range: no memory
-        // traffic, zeros, and the stage is never consumed.
+        // One stage: this wave's weight copies (into its own slot), then its
+        // token DMA.  Past the last K block every offset is out of range: no
+        // memory traffic, zeros, and the stage is never consumed.
         auto load = [&](int slot, int kt) {
             const uint32_t k0 = (uint32_t)kt * ROWB;
-            const bool in0 = (kt < nk) && (int)(k0 + kg * 16) < p.K;
-            const bool in1 = (kt < nk) && (int)(k0 + kg * 16 + 64) < p.K;
+            const bool in0 = (kt < nk) && (int)(k0 + wch0) < p.K;
+            const bool in1 = (kt < nk) && (int)(k0 + wch1) < p.K;
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
-                wreg[slot][r][0] = load16(rsW, in0 ? w_off[r] + k0 : kOobOffset);
-                wreg[slot][r][1] = load16(rsW, in1 ? w_off[r] + k0 + 64 : kOobOffset);
+                const uint32_t roff = (uint32_t)(r * 16) * (uint32_t)p.ldb + k0;
+                const uint32_t dst = wlds + (uint32_t)(slot * WSLOT + r * 2048);
+                dma16(srdW, in0 ? wo0 + roff : kOobOffset, dst);
+                dma16(srdW, in1 ? wo1 + roff : kOobOffset, dst + 1024u);
             }
             if (BLK)
                 wscale[slot] = __builtin_amdgcn_raw_buffer_load_b8(rsSB, kt < nk ? sb_row + (uint32_t)kt : kOobOffset, 0, 0);
@@ -688,9 +708,11 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
                                   *reinterpret_cast<const v4u *>(ts + t_frag[c][1]));
                     tsc[c] = BLK ? (int)tsm[TS * TSLOT + (kt % TS) * SCS + c * 16 + r16] : 127;
                 }
+                const uint8_t *ws = smem + wave * (DEPTH * WSLOT) + s * WSLOT;
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
-                    const v8i wf = pack8(wreg[s][r][0], wreg[s][r][1]);
+                    const v8i wf = pack8(*reinterpret_cast<const v4u *>(ws + r * 2048 + wf0),
+                                         *reinterpret_cast<const v4u *>(ws + r * 2048 + wf1));
 #pragma unroll
                     for (int c = 0; c < CB; ++c) {
                         if (BLK) acc[r][c] = mfma16x16x128_s<FB, FA>(wf, tf[c], acc[r][c], wscale[s], tsc[c]);

@@ -1,9 +1,11 @@
 """GPU parity of the dense few-token (M <= 64) path, the swap-AB decode kernel
-with K split over 8 waves, against the CPU oracle, through the C ABI.
+with K split over 4 waves and per-wave LDS rings, against the CPU oracle,
+through the C ABI.
 
 Edges specific to it: fewer K blocks than waves (some waves have no work),
 a short last K block, N not a multiple of the 16 weight rows per workgroup,
-every token-block count (M = 1..64), mixed formats, and the block-scaled form.
+every token-block count (M = 1..64) with rings that wrap several times, mixed
+formats, and the block-scaled form.
 """
 import numpy as np
 import pytest
@@ -28,11 +30,12 @@ def _dev(x):
 
 
 @pytest.mark.parametrize("M,N,K,fa,fb", [
-    (1, 16, 16, E4M3, E4M3),          # one K chunk: 7 of 8 waves idle
+    (1, 16, 16, E4M3, E4M3),          # one K chunk: 3 of 4 waves idle
     (1, 4104, 7168, E4M3, E4M3),      # N tail inside a workgroup
     (16, 100, 1040, E5M2, E4M3),      # 9 K blocks, the last 16 bytes
-    (17, 520, 384, E4M3, E5M2),       # two token blocks, 3 K blocks
-    (33, 264, 2048, E5M2, E5M2),      # four token blocks
+    (17, 520, 384, E4M3, E5M2),       # two token blocks, 3 K blocks: one wave idle
+    (24, 264, 4096, E4M3, E4M3),      # two token blocks, 8 steps per wave through a 3-slot ring
+    (33, 264, 2048, E5M2, E5M2),      # four token blocks, 4 steps per wave through a 2-slot ring
     (64, 4096, 1024, E4M3, E4M3),
     (48, 40, 272, E4M3, E4M3),
 ])

@@ -138,6 +138,12 @@ def dev(torch, x):
     return torch.from_numpy(x).cuda()
 
 
+def dense_work(M, N, K):
+    """Algorithmic work of one dense GEMM: 2 M N K FLOPs, and one pass over the
+    FP8 operands (1 byte an element) and the BF16 output (2 bytes)."""
+    return 2.0 * M * N * K, float(M * K + N * K + 2 * M * N)
+
+
 def bench_dense(torch, f, w, steps, warmup, timer):
     a, b = dev(torch, w.A), dev(torch, w.B)
     sa = torch.tensor([w.sa], dtype=torch.float32, device="cuda")
@@ -146,11 +152,11 @@ def bench_dense(torch, f, w, steps, warmup, timer):
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     fn = lambda: f.gemm_nt(a, b, sa, sb, out=out, a_dtype=w.a_fmt, b_dtype=w.b_fmt)
     t = timer.run(fn, steps, warmup)
-    flops = 2.0 * M * N * K
+    flops, nbytes = dense_work(M, N, K)
     t["flops"] = flops
     t["tflops_wall"] = flops * steps / t["wall_s"] / 1e12
     t["tflops_kernel"] = flops / (t["kernel_ms_mean"] * 1e-3) / 1e12
-    t["bytes"] = float(M * K + N * K + 2 * M * N)
+    t["bytes"] = nbytes
     del a, b, out
     return t
 

@@ -39,7 +39,7 @@ constexpr int kSwapMaxM = 64;                                  // swap-AB thresh
 #endif
 constexpr int kSwapWaveRows = SWAP_WAVE_ROWS;                  // weight rows per wave, grouped forms
 constexpr int kSwapTileN = 4 * kSwapWaveRows;                  // weight rows per workgroup, grouped forms
-constexpr int kDecodeRows = 16;                                // weight rows per decode workgroup
+constexpr int kDecodeRows = 16;                                // weight rows per decode workgroup (one block)
 constexpr int kSwapDepth = SWAP_DEPTH;                         // K blocks of loads in flight + 1
 constexpr int kContigAlign = 128;                              // row alignment of experts (contiguous form)
 #ifndef TILE128_WM
@@ -70,6 +70,13 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---------------------------------------------------------------------------
 enum Variant { V_NONE = 0, V_TILE_256x256 = 1, V_TILE_128x256 = 2, V_SWAP = 3, V_DECODE = 4 };
 
+// Decode kernel: 16 weight rows per workgroup, or 32 where that still gives
+// at least 256 workgroups.  Every workgroup reads all M x K token bytes, so
+// fewer, larger row blocks cut the token traffic per CU (N = 14336: 896
+// workgroups of 16 rows read 3.5 copies of the tokens per CU, 448 of 32 rows
+// 1.75).
+int decode_rows_for(int64_t n) { return cdiv(n, 2 * kDecodeRows) >= 256 ? 2 * kDecodeRows : kDecodeRows; }
+
 int token_blocks_for(int m) {
     if (m <= 16) return 1;
     if (m <= 32) return 2;
@@ -99,9 +106,9 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
         if (m <= kSwapMaxM) {
             out->variant = V_DECODE;
             out->tile_m = 16 * token_blocks_for(m);
-            out->tile_n = kDecodeRows;
+            out->tile_n = decode_rows_for(n);
             out->token_blocks = token_blocks_for(m);
-            out->workgroups = cdiv(n, kDecodeRows);
+            out->workgroups = cdiv(n, out->tile_n);
         } else {
             out->variant = pick_dense_tile(m, n);
             out->tile_m = out->variant == V_TILE_256x256 ? 256 : 128;
@@ -147,9 +154,9 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
         if (m <= kSwapMaxM) {
             out->variant = V_DECODE;
             out->tile_m = 16 * token_blocks_for(m);
-            out->tile_n = kDecodeRows;
+            out->tile_n = decode_rows_for(n);
             out->token_blocks = token_blocks_for(m);
-            out->workgroups = cdiv(n, kDecodeRows);
+            out->workgroups = cdiv(n, out->tile_n);
             return ok();
         }
         out->variant = pick_dense_tile(m, n);
@@ -246,18 +253,19 @@ int launch_swap(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipStrea
     return launch_swap_cb<4, MODE, SCL>(fa, fb, p, grid, s);
 }
 
-// Decode kernel: 4 waves per 16 weight rows and per-wave LDS rings of 5, 3 or
-// 2 steps for 1, 2 or 4 token blocks (at most 80 KB, so two workgroups share
-// a CU; measured best against 8 waves and deeper rings with one workgroup per
-// CU).  Block scales add 512 bytes per slot.
+// Decode kernel: 4 waves per workgroup and per-wave LDS rings, as deep as fits
+// in 80 KB so that two workgroups share a CU: 5, 3 or 2 steps for 1, 2 or 4
+// token blocks with one weight block, 3, 2, 2 with two (the last needs 96 KB:
+// one workgroup per CU).  Measured best against 8 waves and deeper rings with
+// one workgroup per CU.  Block scales add 512 bytes per slot.
 constexpr int kDecodeWaves = 4;
 
-template <int CB, int SCL>
+template <int RB, int CB, int SCL>
 int launch_decode_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    constexpr int D = CB == 1 ? 5 : (CB == 2 ? 3 : 2);
+    constexpr int D = RB == 1 ? (CB == 1 ? 5 : (CB == 2 ? 3 : 2)) : (CB == 1 ? 3 : 2);
     const dim3 block(64 * kDecodeWaves);
 #define FP8G_DEC(FA, FB) \
-    hipLaunchKernelGGL((fp8g::decode_kernel<kDecodeWaves, CB, FA, FB, D, SCL>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((fp8g::decode_kernel<kDecodeWaves, RB, CB, FA, FB, D, SCL>), grid, block, 0, s, p)
     if (fa == 0 && fb == 0) FP8G_DEC(0, 0);
     else if (fa == 0 && fb == 1) FP8G_DEC(0, 1);
     else if (fa == 1 && fb == 0) FP8G_DEC(1, 0);
@@ -266,11 +274,18 @@ int launch_decode_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t
     return launch_status("decode kernel");
 }
 
+template <int RB, int SCL>
+int launch_decode_rb(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    if (cb == 1) return launch_decode_cb<RB, 1, SCL>(fa, fb, p, grid, s);
+    if (cb == 2) return launch_decode_cb<RB, 2, SCL>(fa, fb, p, grid, s);
+    return launch_decode_cb<RB, 4, SCL>(fa, fb, p, grid, s);
+}
+
 template <int SCL>
-int launch_decode(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    if (cb == 1) return launch_decode_cb<1, SCL>(fa, fb, p, grid, s);
-    if (cb == 2) return launch_decode_cb<2, SCL>(fa, fb, p, grid, s);
-    return launch_decode_cb<4, SCL>(fa, fb, p, grid, s);
+int launch_decode(const fp8g_plan &plan, int fa, int fb, const GemmParams &p, hipStream_t s) {
+    const dim3 grid((unsigned)plan.workgroups);
+    if (plan.tile_n == 2 * kDecodeRows) return launch_decode_rb<2, SCL>(plan.token_blocks, fa, fb, p, grid, s);
+    return launch_decode_rb<1, SCL>(plan.token_blocks, fa, fb, p, grid, s);
 }
 
 }  // namespace
@@ -332,7 +347,7 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int fa = a_dtype, fb = b_dtype;
     if (plan.variant == V_DECODE)
-        return launch_decode<fp8g::SCALE_TENSOR>(plan.token_blocks, fa, fb, p, dim3((unsigned)plan.workgroups), s);
+        return launch_decode<fp8g::SCALE_TENSOR>(plan, fa, fb, p, s);
     p.tiles_m = (int)cdiv(M, plan.tile_m);
     p.tiles_n = (int)cdiv(N, plan.tile_n);
     const dim3 grid((unsigned)plan.workgroups);
@@ -522,7 +537,7 @@ int fp8_gemm_nt_blockscaled(const void *A, int64_t lda, int a_dtype, const void 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int fa = a_dtype, fb = b_dtype;
     const dim3 grid((unsigned)plan.workgroups);
-    if (plan.variant == V_DECODE) return launch_decode<fp8g::SCALE_BLOCK>(plan.token_blocks, fa, fb, p, grid, s);
+    if (plan.variant == V_DECODE) return launch_decode<fp8g::SCALE_BLOCK>(plan, fa, fb, p, s);
     p.tiles_m = (int)cdiv(M, plan.tile_m);
     p.tiles_n = (int)cdiv(N, plan.tile_n);
     if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE, fp8g::SCALE_BLOCK>(fa, fb, p, grid, s);
@@ -558,7 +573,7 @@ int fp8_gemm_nt_channelwise(const void *A, int64_t lda, int a_dtype, const void 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int fa = a_dtype, fb = b_dtype;
     const dim3 grid((unsigned)plan.workgroups);
-    if (plan.variant == V_DECODE) return launch_decode<fp8g::SCALE_CHANNEL>(plan.token_blocks, fa, fb, p, grid, s);
+    if (plan.variant == V_DECODE) return launch_decode<fp8g::SCALE_CHANNEL>(plan, fa, fb, p, s);
     p.tiles_m = (int)cdiv(M, plan.tile_m);
     p.tiles_n = (int)cdiv(N, plan.tile_n);
     if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE, fp8g::SCALE_CHANNEL>(fa, fb, p, grid, s);

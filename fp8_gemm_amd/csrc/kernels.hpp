@@ -762,25 +762,25 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
 //   (and, with block scales, that step's scale bytes); the partial sums of the
 //   waves are added through LDS at the end.
 // ---------------------------------------------------------------------------
-template <int WAVES, int CB, int FA, int FB, int D, int SCL>
+template <int WAVES, int RB, int CB, int FA, int FB, int D, int SCL>
 __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
     constexpr bool BLK = SCL == SCALE_BLOCK, CHN = SCL == SCALE_CHANNEL;
-    constexpr int NB = 1 + CB;                     // 16-row blocks per step: weights, then tokens
+    constexpr int NB = RB + CB;                    // 16-row blocks per step: RB of weights, then CB of tokens
     constexpr int NQ = 2 * NB + (BLK ? 2 : 0);     // DMA instructions per step (8 rows x 128 B each,
                                                    // and two 256-byte scale copies)
     constexpr int SCS = BLK ? 512 : 0;             // scale bytes per slot
     constexpr int SLOT = NB * 2048 + SCS;          // bytes per ring slot
     constexpr int WRING = D * SLOT;                // bytes per wave
     static_assert(D >= 2 && NQ * (D - 1) < 64, "ring depth");
-    constexpr int RED = WAVES * CB * 64 * 16;      // partial sums for the reduction
+    constexpr int RED = WAVES * RB * CB * 64 * 16; // partial sums for the reduction
     constexpr int SMEM = WAVES * WRING > RED ? WAVES * WRING : RED;
     static_assert(SMEM <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n0 = blockIdx.x * 16;
-    const int rows_w = min(p.N - n0, 16);
+    const int n0 = blockIdx.x * 16 * RB;
+    const int rows_w = min(p.N - n0, 16 * RB);
     // Rows past N (weights) or past M (tokens) lie outside the descriptors and
     // read zeros without touching memory.
     const v4i srdW = make_srd(p.B + (int64_t)n0 * p.ldb, rows_bytes(rows_w, p.ldb));
@@ -819,12 +819,16 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
         const bool ok = s < my;
         const bool in0 = ok && (int)(k0 + dch0) < p.K, in1 = ok && (int)(k0 + dch1) < p.K;
         const uint32_t base = ring + (uint32_t)slot * SLOT;
-        dma16(srdW, in0 ? w0 + k0 : kOobOffset, base);
-        dma16(srdW, in1 ? w1 + k0 : kOobOffset, base + 1024u);
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const uint32_t wb = (uint32_t)(16 * b) * (uint32_t)p.ldb + k0;
+            dma16(srdW, in0 ? w0 + wb : kOobOffset, base + 2048u * b);
+            dma16(srdW, in1 ? w1 + wb : kOobOffset, base + 2048u * b + 1024u);
+        }
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
-            dma16(srdT, in0 ? t0[c] + k0 : kOobOffset, base + 2048u * (1 + c));
-            dma16(srdT, in1 ? t1[c] + k0 : kOobOffset, base + 2048u * (1 + c) + 1024u);
+            dma16(srdT, in0 ? t0[c] + k0 : kOobOffset, base + 2048u * (RB + c));
+            dma16(srdT, in1 ? t1[c] + k0 : kOobOffset, base + 2048u * (RB + c) + 1024u);
         }
         if (BLK) {
             const uint32_t sbase = base + NB * 2048u;
@@ -842,9 +846,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
     const uint32_t ro1 = (uint32_t)r16 * 128u + (((uint32_t)(4 + kg) ^ rkey) * 16u);
     const uint8_t *wbase = smem + wave * WRING;
 
-    v4f acc[CB];
+    v4f acc[RB][CB];
 #pragma unroll
-    for (int c = 0; c < CB; ++c) acc[c] = (v4f){0, 0, 0, 0};
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int c = 0; c < CB; ++c) acc[r][c] = (v4f){0, 0, 0, 0};
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) issue(d, d);
     for (int s0 = 0; s0 < my; s0 += D) {
@@ -855,15 +861,23 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
             issue(s0 + d + D - 1, (d + D - 1) % D);
             vmcnt_wait<(D - 1) * NQ>();            // step s0 + d has landed
             const uint8_t *slot = wbase + d * SLOT;
-            const v8i wf = pack8(*reinterpret_cast<const v4u *>(slot + ro0), *reinterpret_cast<const v4u *>(slot + ro1));
+            v8i wf[RB];
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+                wf[r] = pack8(*reinterpret_cast<const v4u *>(slot + 2048 * r + ro0),
+                              *reinterpret_cast<const v4u *>(slot + 2048 * r + ro1));
             const int kt = wave + WAVES * (s0 + d);
             const int ssb = BLK ? slot[NB * 2048 + 256 + (kt & 3)] : 127;
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
-                const uint8_t *tb = slot + 2048 * (1 + c);
+                const uint8_t *tb = slot + 2048 * (RB + c);
                 const v8i tf = pack8(*reinterpret_cast<const v4u *>(tb + ro0), *reinterpret_cast<const v4u *>(tb + ro1));
-                if (BLK) acc[c] = mfma16x16x128_s<FB, FA>(wf, tf, acc[c], ssb, slot[NB * 2048 + c * 16 + r16]);
-                else acc[c] = mfma16x16x128<FB, FA>(wf, tf, acc[c]);
+                const int ssa = BLK ? slot[NB * 2048 + c * 16 + r16] : 127;
+#pragma unroll
+                for (int r = 0; r < RB; ++r) {
+                    if (BLK) acc[r][c] = mfma16x16x128_s<FB, FA>(wf[r], tf, acc[r][c], ssb, ssa);
+                    else acc[r][c] = mfma16x16x128<FB, FA>(wf[r], tf, acc[r][c]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -876,17 +890,20 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
     // column r16, so a lane writes four consecutive outputs of one token row.
     v4f *red = reinterpret_cast<v4f *>(smem);
 #pragma unroll
-    for (int c = 0; c < CB; ++c) red[(wave * CB + c) * 64 + lane] = acc[c];
-    __syncthreads();
-    if (wave < CB) {
-        const int c = wave;
-        v4f sum = red[c * 64 + lane];
+    for (int r = 0; r < RB; ++r)
 #pragma unroll
-        for (int w = 1; w < WAVES; ++w) sum += red[(w * CB + c) * 64 + lane];
+        for (int c = 0; c < CB; ++c) red[((wave * RB + r) * CB + c) * 64 + lane] = acc[r][c];
+    __syncthreads();
+    // output block (r, c) = weight rows 16 r .. of this workgroup x token block c
+    for (int idx = wave; idx < RB * CB; idx += WAVES) {
+        const int r = idx / CB, c = idx % CB;
+        v4f sum = red[idx * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) sum += red[(w * RB * CB + idx) * 64 + lane];
         const float sc = SCL != SCALE_TENSOR ? 1.0f : p.scale_a[0] * p.scale_b[0];
         const int tok = c * 16 + r16;
         if (tok < p.M) {
-            const int n = n0 + kg * 4;
+            const int n = n0 + r * 16 + kg * 4;
             v2u v;
             if (CHN) {
                 float s4[4], b4[4];

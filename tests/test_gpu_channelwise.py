@@ -43,6 +43,7 @@ def run(w, sa, sb, bias):
     (5, 130, 256, E4M3, E4M3, "abc"),       # decode kernel, N tail of 2 channels
     (17, 520, 1040, E5M2, E4M3, "bc"),
     (64, 4100, 384, E4M3, E4M3, "ac"),
+    (20, 8204, 512, E4M3, E4M3, "abc"),     # decode kernel with 32-row workgroups, N tail of 12
     (300, 264, 400, E4M3, E5M2, "abc"),     # 128x256 tiles
     (513, 300, 256, E4M3, E4M3, "c"),       # 256x256 tiles, bias only
     (129, 136, 128, E5M2, E5M2, "ab"),

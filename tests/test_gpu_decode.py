@@ -38,6 +38,9 @@ def _dev(x):
     (33, 264, 2048, E5M2, E5M2),      # four token blocks, 4 steps per wave through a 2-slot ring
     (64, 4096, 1024, E4M3, E4M3),
     (48, 40, 272, E4M3, E4M3),
+    (1, 8200, 1040, E4M3, E4M3),      # N >= 8192: 32 weight rows per workgroup, 8-row tail
+    (17, 8192, 2048, E5M2, E4M3),     # 32-row workgroups, two token blocks
+    (64, 8232, 1024, E4M3, E4M3),     # 32-row workgroups, four token blocks, 8-row tail
 ])
 def test_decode_matches_oracle(M, N, K, fa, fb):
     w = workloads.dense_random(M, N, K, seed=M * 7 + N + K, a_fmt=fa, b_fmt=fb, scales=(0.75, 1.5))
@@ -64,7 +67,8 @@ def test_decode_all_ones_exact():
         assert (d.float() == K).all(), M
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 300, 400), (17, 4096, 1152), (64, 520, 2000 - 2000 % 16)])
+@pytest.mark.parametrize("M,N,K", [(1, 300, 400), (17, 4096, 1152), (64, 520, 2000 - 2000 % 16),
+                                   (33, 8200, 1152)])
 def test_decode_blockscaled(M, N, K):
     w = workloads.dense_blockscaled(M, N, K, seed=M + 3 * N + K, lds_pad=5, pad_code=255)
     assert _f().plan(3, M, N, K).variant == 4

@@ -66,6 +66,11 @@ def test_dense_plan_grid(f):
     assert (p.tile_m, p.tile_n, p.workgroups) == (256, 256, 256)
     p = f.plan(0, 17, 4096, 7168)                  # decode kernel: 16 weight rows per workgroup
     assert p.token_blocks == 2 and p.tile_n == 16 and p.workgroups == 4096 // 16
+    # 32 rows per workgroup once that still gives >= 256 workgroups
+    assert (f.plan(0, 64, 8160, 4096).tile_n, f.plan(0, 64, 8160, 4096).workgroups) == (16, 510)
+    assert (f.plan(0, 64, 8192, 4096).tile_n, f.plan(0, 64, 8192, 4096).workgroups) == (32, 256)
+    assert (f.plan(0, 1, 14336, 4096).tile_n, f.plan(0, 1, 14336, 4096).workgroups) == (32, 448)
+    assert f.plan(3, 33, 8200, 1152).tile_n == 32  # block-scaled decode likewise
 
 
 def test_masked_plan_uses_hint_not_results(f):

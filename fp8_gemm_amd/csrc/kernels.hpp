@@ -548,12 +548,14 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
     constexpr int SCS = BLK ? 256 : 0;             // token-scale bytes per ring slot
     constexpr int WSLOT = WR * ROWB;               // one stage of one wave's weight rows
     constexpr int WRING = 4 * DEPTH * WSLOT;       // the four waves' weight rings
+    constexpr int WSC = BLK ? 256 : 0;             // one stage of one wave's weight-scale copy
+    constexpr int WSC_OFF = WRING + TS * TSLOT + TS * SCS;
     static_assert(RB >= 1 && CB >= 1 && DEPTH >= 2, "shape");
     static_assert((DEPTH - 1) * (WLOADS + TDMA + SDMA) < 64, "loads in flight");
-    static_assert(WRING + TS * TSLOT + TS * SCS <= 160 * 1024, "LDS");
+    static_assert(WSC_OFF + 4 * DEPTH * WSC <= 160 * 1024, "LDS");
 
-    // [weight rings of the 4 waves | token ring | token-scale ring]
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[WRING + TS * TSLOT + TS * SCS];
+    // [weight rings of the 4 waves | token ring | token-scale ring | weight-scale slots]
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[WSC_OFF + 4 * DEPTH * WSC];
     uint8_t *const tsm = smem + WRING;
 
     const int lane = threadIdx.x & 63;
@@ -581,7 +583,7 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
     const int nk_ = (p.K + 127) / 128;
     const uint8_t *sa_g = BLK ? p.sfa + (int64_t)g * nk_ * p.lds_sa : p.A;
     const uint8_t *sb_g = BLK ? p.sfb + (int64_t)g * ((p.N + 127) / 128) * p.lds_sb : p.A;
-    const __amdgpu_buffer_rsrc_t rsSB = make_rsrc(sb_g, BLK ? (uint32_t)(((p.N + 127) / 128) * p.lds_sb) : 0u);
+    const v4i srdSB = BLK ? make_srd(sb_g, (uint32_t)(((p.N + 127) / 128) * p.lds_sb)) : v4i{0, 0, 0, 0};
     const uint32_t sb_row = BLK ? (uint32_t)(min(nw, p.N) / 128) * (uint32_t)p.lds_sb : 0u;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)tsm;
     const uint32_t wlds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem +
@@ -651,7 +653,6 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
 #pragma unroll
             for (int c = 0; c < CB; ++c) acc[r][c] = (v4f){0, 0, 0, 0};
 
-        int wscale[DEPTH];
 
         // One stage: this wave's weight copies (into its own slot), then its
         // token DMA.  Past the last K block every offset is out of range: no
@@ -667,8 +668,12 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
                 dma16(srdW, in0 ? wo0 + roff : kOobOffset, dst);
                 dma16(srdW, in1 ? wo1 + roff : kOobOffset, dst + 1024u);
             }
+            // this wave's weight-block scale of step kt: the dword holding it, into
+            // the wave's own slot (copied, not loaded into a register, so that every
+            // load of the stage is counted by the waits below)
             if (BLK)
-                wscale[slot] = __builtin_amdgcn_raw_buffer_load_b8(rsSB, kt < nk ? sb_row + (uint32_t)kt : kOobOffset, 0, 0);
+                dma4(srdSB, kt < nk && lane == 0 ? sb_row + ((uint32_t)kt & ~3u) : kOobOffset,
+                     lds0 - (uint32_t)WRING + (uint32_t)(WSC_OFF + (wave * DEPTH + slot) * WSC));
 #pragma unroll
             for (int i = 0; i < TDMA; ++i) {
                 const bool in = (kt < nk) && (int)(k0 + t_dma_kc[i]) < p.K;
@@ -709,13 +714,14 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
                     tsc[c] = BLK ? (int)tsm[TS * TSLOT + (kt % TS) * SCS + c * 16 + r16] : 127;
                 }
                 const uint8_t *ws = smem + wave * (DEPTH * WSLOT) + s * WSLOT;
+                const int wsc = BLK ? (int)smem[WSC_OFF + (wave * DEPTH + s) * WSC + (kt & 3)] : 127;
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
                     const v8i wf = pack8(*reinterpret_cast<const v4u *>(ws + r * 2048 + wf0),
                                          *reinterpret_cast<const v4u *>(ws + r * 2048 + wf1));
 #pragma unroll
                     for (int c = 0; c < CB; ++c) {
-                        if (BLK) acc[r][c] = mfma16x16x128_s<FB, FA>(wf, tf[c], acc[r][c], wscale[s], tsc[c]);
+                        if (BLK) acc[r][c] = mfma16x16x128_s<FB, FA>(wf, tf[c], acc[r][c], wsc, tsc[c]);
                         else acc[r][c] = mfma16x16x128<FB, FA>(wf, tf[c], acc[r][c]);
                     }
                 }

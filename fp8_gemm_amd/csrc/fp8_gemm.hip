@@ -33,12 +33,10 @@ int ok() {
 
 constexpr int64_t kMaxRowStride = (int64_t(1) << 23) - 16;   // keeps 256 rows of offsets below 2^31
 constexpr int kSwapMaxM = 64;                                  // swap-AB threshold on the token count
-#ifndef SWAP_WAVE_ROWS
-#define SWAP_WAVE_ROWS 128
+#ifndef SWAP_DEPTH
 #define SWAP_DEPTH 2
 #endif
-constexpr int kSwapWaveRows = SWAP_WAVE_ROWS;                  // weight rows per wave, grouped forms
-constexpr int kSwapTileN = 4 * kSwapWaveRows;                  // weight rows per workgroup, grouped forms
+constexpr int kSwapWaveRows = 128;                             // weight rows per wave, grouped forms
 constexpr int kDecodeRows = 16;                                // weight rows per decode workgroup (one block)
 constexpr int kSwapDepth = SWAP_DEPTH;                         // K blocks of loads in flight + 1
 constexpr int kContigAlign = 128;                              // row alignment of experts (contiguous form)
@@ -76,6 +74,11 @@ enum Variant { V_NONE = 0, V_TILE_256x256 = 1, V_TILE_128x256 = 2, V_SWAP = 3, V
 // workgroups of 16 rows read 3.5 copies of the tokens per CU, 448 of 32 rows
 // 1.75).
 int decode_rows_for(int64_t n) { return cdiv(n, 2 * kDecodeRows) >= 256 ? 2 * kDecodeRows : kDecodeRows; }
+
+// Swapped streaming kernel: 128 weight rows per wave (512 per workgroup), or
+// 64 when that would leave CUs idle (16 groups of N = 4096: 128 workgroups
+// of 512 rows ran at 4.4 TB/s).
+int swap_wave_rows(int64_t groups, int64_t n) { return groups * cdiv(n, 4 * kSwapWaveRows) >= 256 ? kSwapWaveRows : kSwapWaveRows / 2; }
 
 int token_blocks_for(int m) {
     if (m <= 16) return 1;
@@ -125,9 +128,9 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
         if (hint <= kSwapMaxM) {
             out->variant = V_SWAP;
             out->tile_m = 16 * token_blocks_for(hint);
-            out->tile_n = kSwapTileN;
+            out->tile_n = 4 * swap_wave_rows(groups, n);
             out->token_blocks = token_blocks_for(hint);
-            out->workgroups = (int64_t)groups * cdiv(n, kSwapTileN);
+            out->workgroups = (int64_t)groups * cdiv(n, out->tile_n);
         } else {
             out->variant = V_TILE_128x256;
             out->tile_m = 128;
@@ -233,11 +236,11 @@ int launch_tile128(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s
     return launch_ring<128, 256, TILE128_WM, TILE128_WN, T128_ST, T128_BK, MODE, SCL>(fa, fb, p, grid, s);
 }
 
-template <int CB, int MODE, int SCL = 0>
+template <int WR, int CB, int MODE, int SCL = 0>
 int launch_swap_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     const dim3 block(256);
 #define FP8G_SWAP(FA, FB) \
-    hipLaunchKernelGGL((fp8g::swap_kernel<kSwapWaveRows, CB, FA, FB, kSwapDepth, MODE, SCL>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((fp8g::swap_kernel<WR, CB, FA, FB, kSwapDepth, MODE, SCL>), grid, block, 0, s, p)
     if (fa == 0 && fb == 0) FP8G_SWAP(0, 0);
     else if (fa == 0 && fb == 1) FP8G_SWAP(0, 1);
     else if (fa == 1 && fb == 0) FP8G_SWAP(1, 0);
@@ -246,11 +249,19 @@ int launch_swap_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s
     return launch_status("swap kernel");
 }
 
+template <int WR, int MODE, int SCL>
+int launch_swap_wr(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    if (cb == 1) return launch_swap_cb<WR, 1, MODE, SCL>(fa, fb, p, grid, s);
+    if (cb == 2) return launch_swap_cb<WR, 2, MODE, SCL>(fa, fb, p, grid, s);
+    return launch_swap_cb<WR, 4, MODE, SCL>(fa, fb, p, grid, s);
+}
+
+// p.tiles_n must hold the number of plan.tile_n-row weight blocks of a group.
 template <int MODE, int SCL = 0>
-int launch_swap(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    if (cb == 1) return launch_swap_cb<1, MODE, SCL>(fa, fb, p, grid, s);
-    if (cb == 2) return launch_swap_cb<2, MODE, SCL>(fa, fb, p, grid, s);
-    return launch_swap_cb<4, MODE, SCL>(fa, fb, p, grid, s);
+int launch_swap(const fp8g_plan &plan, int fa, int fb, const GemmParams &p, hipStream_t s) {
+    const dim3 grid((unsigned)plan.workgroups);
+    if (plan.tile_n == 4 * kSwapWaveRows) return launch_swap_wr<kSwapWaveRows, MODE, SCL>(plan.token_blocks, fa, fb, p, grid, s);
+    return launch_swap_wr<kSwapWaveRows / 2, MODE, SCL>(plan.token_blocks, fa, fb, p, grid, s);
 }
 
 // Decode kernel: 4 waves per workgroup and per-wave LDS rings, as deep as fits
@@ -416,8 +427,8 @@ int fp8_grouped_gemm_masked(const void *A, int a_dtype, const void *B, int b_dty
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (plan.variant == V_SWAP) {
         p.tiles_m = 1;
-        p.tiles_n = (int)cdiv(N, kSwapTileN);
-        return launch_swap<fp8g::MODE_MASKED>(plan.token_blocks, a_dtype, b_dtype, p, dim3((unsigned)plan.workgroups), s);
+        p.tiles_n = (int)cdiv(N, plan.tile_n);
+        return launch_swap<fp8g::MODE_MASKED>(plan, a_dtype, b_dtype, p, s);
     }
     p.tiles_m = (int)cdiv(cap, 128);
     p.tiles_n = (int)cdiv(N, 256);
@@ -462,9 +473,8 @@ int fp8_grouped_gemm_masked_blockscaled(const void *A, int a_dtype, const void *
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (plan.variant == V_SWAP) {
         p.tiles_m = 1;
-        p.tiles_n = (int)cdiv(N, kSwapTileN);
-        return launch_swap<fp8g::MODE_MASKED, fp8g::SCALE_BLOCK>(plan.token_blocks, a_dtype, b_dtype, p,
-                                                                 dim3((unsigned)plan.workgroups), s);
+        p.tiles_n = (int)cdiv(N, plan.tile_n);
+        return launch_swap<fp8g::MODE_MASKED, fp8g::SCALE_BLOCK>(plan, a_dtype, b_dtype, p, s);
     }
     p.tiles_m = (int)cdiv(cap, 128);
     p.tiles_n = (int)cdiv(N, 256);

@@ -526,17 +526,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 
 // ---------------------------------------------------------------------------
 // Streaming swap-AB kernel.
-// 4 waves; wave w streams weight rows [n0 + w*WR, +WR) as WR/16 row blocks of
-// the 16x16x128 instruction, straight from HBM into registers (no LDS: every
-// weight byte is used by exactly one wave).  Tokens form up to CB column
-// blocks of 16; their tile is shared by the 4 waves, so it is DMA'd once per
-// workgroup into a small LDS ring and read from there.  DEPTH register slots
-// keep DEPTH-1 K blocks of weight loads in flight per wave.
+// 4 waves; wave w streams weight rows [n0 + w*WR, +WR) (WR = 128, or 64 when
+// there are too few groups to fill the CUs) as WR/16 row blocks of the
+// 16x16x128 instruction.  Every weight byte is used by exactly one wave; it
+// still passes through the wave's own LDS ring, because copying whole lines
+// there and reading the operand layout back beats loading that layout
+// directly (see the weight-copy comment below).  Tokens form up to CB column
+// blocks of 16; their tile is shared by the 4 waves, so it is copied once per
+// workgroup into a small LDS ring and read from there.  DEPTH ring slots keep
+// DEPTH-1 K blocks of copies in flight per wave.
 // ---------------------------------------------------------------------------
 template <int WR, int CB, int FA, int FB, int DEPTH, int MODE, int SCL>
 __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
     constexpr bool BLK = SCL == SCALE_BLOCK;
-    static_assert(!BLK || WR == 128, "block scales: each wave's rows are one 128-row scale block");
+    // with block scales each wave's rows (WR of them, starting at a multiple of
+    // WR) must lie in one 128-row scale block
+    static_assert(!BLK || WR == 128 || WR == 64, "block scales: each wave's rows within one 128-row scale block");
     constexpr int RB = WR / 16;
     constexpr int ROWB = 128;                      // K bytes per pipeline stage
     constexpr int TR = CB <= 2 ? 32 : 16 * CB;     // token rows staged per stage (>= 32: one DMA per wave)

@@ -77,6 +77,8 @@ def test_masked_plan_uses_hint_not_results(f):
     p = f.plan(1, 64, 4096, 7168, 32, 32)
     # 4 waves x 128 weight rows = 512 rows of one expert per workgroup
     assert p.variant == 3 and p.token_blocks == 2 and p.tile_n == 512 and p.workgroups == 32 * (4096 // 512)
+    p = f.plan(1, 64, 4096, 7168, 16, 32)          # 16 groups: 64 rows per wave keeps 256 workgroups
+    assert p.variant == 3 and p.tile_n == 256 and p.workgroups == 16 * (4096 // 256)
     p = f.plan(1, 64, 4096, 7168, 32, 0)           # hint 0 -> capacity
     assert p.variant == 3 and p.token_blocks == 4
     p = f.plan(1, 256, 4096, 7168, 8, 0)           # many rows per group -> tiled

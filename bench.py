@@ -260,6 +260,38 @@ def bench_masked(torch, f, w, steps, warmup, timer):
     return t
 
 
+SWAPAB_TABLE = [(32, 4096, 7168), (96, 4096, 7168), (160, 4096, 7168),
+                (32, 7168, 2048), (96, 7168, 2048), (160, 7168, 2048)]
+
+
+def bench_masked_table(torch, f, steps, warmup, timer, G=16, seed=40):
+    """The masked grouped shapes of the swap-AB benchmark table ("One transpose,
+    half the compute", section 4): 16 groups, every group m valid rows, the
+    kernel the plan picks for that m."""
+    import numpy as np
+    import workloads
+
+    out = []
+    for (n, k) in sorted({(n, k) for _, n, k in SWAPAB_TABLE}):
+        cap = max(m for m, nn, kk in SWAPAB_TABLE if (nn, kk) == (n, k))
+        w = workloads.masked_random(G, cap, n, k, seed=seed, m_values=[cap] * G)
+        a, b, sb = dev(torch, w.A), dev(torch, w.B), dev(torch, w.sb)
+        sa = torch.ones(1, dtype=torch.float32, device="cuda")
+        o = torch.empty((G, cap, n), dtype=torch.bfloat16, device="cuda")
+        for m in sorted(mm for mm, nn, kk in SWAPAB_TABLE if (nn, kk) == (n, k)):
+            cnt = torch.full((G,), m, dtype=torch.int32, device="cuda")
+            t = timer.run(lambda: f.grouped_gemm_masked(a, b, sa, sb, cnt, out=o, expected_m=m, a_dtype=w.a_fmt,
+                                                        b_dtype=w.b_fmt), steps, warmup)
+            flops = 2.0 * G * m * n * k
+            nbytes = float(G * n * k + G * m * k + 2 * G * m * n)
+            ms = t["kernel_ms_mean"]
+            out.append({"m": m, "n": n, "k": k, "groups": G, "kernel_us_mean": ms * 1e3,
+                        "tflops": flops / (ms * 1e-3) / 1e12, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                        "variant": f.plan(1, cap, n, k, G, m).variant})
+        del a, b, sb, o, w
+    return out
+
+
 def bench_masked_blockscaled(torch, f, w, steps, warmup, timer):
     import numpy as np
 
@@ -431,7 +463,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: dense masked masked_bs contig contig_bs small e5m2 blockscaled channelwise bf16 decode "
+                    help="subset of: dense masked masked_table masked_bs contig contig_bs small e5m2 blockscaled channelwise bf16 decode "
                          "proj copy "
                          "(default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -461,7 +493,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     timer = Timer(torch)
-    want = set(args.only) if args.only else {"dense", "masked", "masked_bs", "contig", "contig_bs", "small", "e5m2", "blockscaled",
+    want = set(args.only) if args.only else {"dense", "masked", "masked_table", "masked_bs", "contig", "contig_bs", "small", "e5m2", "blockscaled",
                                            "channelwise", "bf16", "decode", "proj", "copy"}
     steps, warmup = args.steps, args.warmup
     extra = {}
@@ -554,6 +586,15 @@ def main():
                          "algorithmic_bytes": r["bytes"]}}
         log(f"  {r['gbs_kernel']:.0f} GB/s ({r['gbs_kernel'] / PEAK_HBM_GBS:.1%} of HBM peak)")
         del wm
+    if "masked_table" in want:
+        log("timing the swap-AB benchmark table shapes (16 groups, m in {32, 96, 160})")
+        rows = bench_masked_table(torch, f, max(10, steps // 4), max(2, warmup // 4), timer)
+        extra["masked_swapab_table"] = {
+            "workload": "masked grouped FP8 GEMM, 16 groups, every group m rows, (n, k) in {(4096, 7168), "
+                        "(7168, 2048)}, E4M3, weights amax-scaled N(0,0.02) (seed 40)", "shapes": rows}
+        for r in rows:
+            log(f"  m={r['m']} n={r['n']} k={r['k']}: {r['kernel_us_mean']:.1f} us, {r['tflops']:.0f} TFLOP/s, "
+                f"{r['gbs']:.0f} GB/s")
     if "masked_bs" in want:
         log("generating block-scaled masked grouped decode inputs (G=32, cap=64, N=4096, K=7168)")
         wmb = workloads.masked_decode_blockscaled()

@@ -250,10 +250,11 @@ int fp8_grouped_gemm_contig_blockscaled(const void *A, int a_dtype, const void *
 typedef struct {
     int variant;        /* 1 = tiled 256x256, 2 = tiled 128x256 (m x n),
                            3 = swapped streaming (grouped forms),
-                           4 = swapped decode, K split over 8 waves (dense
+                           4 = swapped decode, K split over 4 waves (dense
                            forms, m <= 64), 0 = nothing to launch */
     int tile_m;         /* rows of D per workgroup tile (tokens) */
-    int tile_n;         /* columns of D per workgroup tile */
+    int tile_n;         /* columns of D per workgroup tile (weight rows: 256
+                           or 512 for variant 3, 16 or 32 for variant 4) */
     int token_blocks;   /* swapped kernel: 16-token column blocks per pass */
     int64_t workgroups; /* grid size */
 } fp8g_plan;

@@ -77,6 +77,13 @@ __device__ __forceinline__ void vmcnt_wait() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(N) (N < 16), leaving the other counters unconstrained.
+template <int N>
+__device__ __forceinline__ void lgkmcnt_wait() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (N << 8) | (3 << 14));
+}
+
 __device__ __forceinline__ v4u load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
@@ -115,12 +122,15 @@ __device__ __forceinline__ v8i pack8(v4u lo, v4u hi) {
     return r;
 }
 
-// Scaled FP8 MFMA with neutral E8M0 block scales (127 = 2^0), so it is a plain
-// FP8 x FP8 -> FP32 multiply-accumulate.  FA / FB select the format of the
-// instruction's first / second operand: 0 = E4M3, 1 = E5M2.
+// Plain FP8 x FP8 -> FP32 multiply-accumulate.  FA / FB select the format of
+// the instruction's first / second operand: 0 = E4M3, 1 = E5M2.  With the
+// scale operands given as the constant 0 the compiler emits the unscaled
+// v_mfma_f32_*_f8f6f4 instruction instead of the scaled one (the products are
+// those of E8M0 scales 127 = 2^0: measured equal), which issues slightly
+// faster: 4.49 against 4.43 PFLOP/s for 16x16x128 in a rate probe.
 template <int FA, int FB>
 __device__ __forceinline__ v16f mfma32x32x64(v8i a, v8i b, v16f c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
 // BF16 operands (the comparison path): a 32-byte fragment holds 16 BF16
@@ -143,7 +153,7 @@ __device__ __forceinline__ v16f mfma32x32x16_bf16_part(v8i a, v8i b, v16f c) {
 
 template <int FA, int FB>
 __device__ __forceinline__ v4f mfma16x16x128(v8i a, v8i b, v4f c) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
 // The same with E8M0 block scales in byte 0 of sa / sb: each lane passes the

@@ -224,11 +224,28 @@ int launch_ring(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     return launch_status("tiled kernel");
 }
 
-// Tile shapes of the tiled kernel: 256 x 256 with 8 waves (4 along M, 2 along
-// N) and a 2-slot ring of 128-byte K steps (128 KB of LDS); 128 x 256 with 8
-// waves (2 x 4) and a 3-slot ring (144 KB).
+template <int MODE, int SCL>
+int launch_tile16(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    const dim3 block(256);
+#define FP8G_T16(FA, FB) hipLaunchKernelGGL((fp8g::tile16_kernel<FA, FB, MODE, SCL>), grid, block, 0, s, p)
+    if (fa == 0 && fb == 0) FP8G_T16(0, 0);
+    else if (fa == 0 && fb == 1) FP8G_T16(0, 1);
+    else if (fa == 1 && fb == 0) FP8G_T16(1, 0);
+    else FP8G_T16(1, 1);
+#undef FP8G_T16
+    return launch_status("tiled kernel (16x16x128)");
+}
+
+// Tile shapes of the tiled kernels: 256 x 256, either 4 waves on the
+// 16x16x128 instruction (dense FP8 with per-tensor or per-channel scales) or
+// 8 waves (4 along M, 2 along N) on 32x32x64 (block scales, BF16, contiguous
+// grouped), both with a 2-slot ring of 128-byte K steps (128 KB of LDS);
+// 128 x 256 with 8 waves (2 x 4) and a 3-slot ring (144 KB).
 template <int MODE, int SCL = 0>
 int launch_tile256(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    if constexpr (SCL != fp8g::SCALE_BLOCK && MODE == fp8g::MODE_DENSE) {
+        if (fa != fp8g::FMT_BF16) return launch_tile16<MODE, SCL>(fa, fb, p, grid, s);
+    }
     return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE, SCL>(fa, fb, p, grid, s);
 }
 template <int MODE, int SCL = 0>

@@ -7,17 +7,20 @@
 // consecutive output columns n of one output row m, so the epilogue writes
 // 8-byte packed BF16 runs straight from registers.
 //
-//   ring_kernel    LDS-tiled: a BM x BN output tile per workgroup, K in steps
-//                  of 128 bytes, both operand tiles staged through a
-//                  direct-to-LDS, XOR-swizzled ring; v_mfma 32x32x64.  Dense
-//                  (M > 64), masked grouped with many rows per group,
-//                  contiguous grouped, and the BF16 comparison path (same
-//                  bytes, two v_mfma 32x32x16 BF16 per fragment).
+//   tile16_kernel  LDS-tiled, 256 x 256 output tile per workgroup of 4 waves
+//                  on v_mfma 16x16x128, K in steps of 128 bytes, both operand
+//                  tiles staged through a direct-to-LDS, XOR-swizzled ring.
+//                  Dense FP8 (M > 64) with per-tensor or per-channel scales.
+//   ring_kernel    the same ring with 8 waves on v_mfma 32x32x64, BM x BN
+//                  = 256 x 256 or 128 x 256: block-scaled dense, masked
+//                  grouped with many rows per group, contiguous grouped, the
+//                  128-row tiles, and the BF16 comparison path (same bytes, two
+//                  v_mfma 32x32x16 BF16 per fragment).
 //   swap_kernel    streaming "swap-AB" form for few tokens: each wave streams
-//                  its own weight rows from HBM straight into registers in the
-//                  16x16x128 operand layout (no LDS: every weight byte is used
-//                  by exactly one wave), tokens ride on the 16-wide column side
-//                  in blocks of 16.  Masked grouped decode.
+//                  its own weight rows (every weight byte is used by exactly
+//                  one wave) through a private LDS ring into the 16x16x128
+//                  operand layout; tokens ride on the 16-wide column side in
+//                  blocks of 16.  Masked grouped decode.
 //   decode_kernel  the same idea for the dense form with M <= 64: 4 waves
 //                  split K over 16 weight rows per workgroup; weights and
 //                  tokens are copied line by line into per-wave LDS rings and
@@ -138,6 +141,114 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 }
 
 // ---------------------------------------------------------------------------
+// Placement of one output tile of the tiled kernels: tile coordinates, group,
+// expert, first row and the valid rows and columns.  Returns false when the
+// workgroup has nothing to compute (masked tile past the group's count,
+// all-padding contiguous block, or a second-block workgroup whose block needs
+// no separate pass).
+// ---------------------------------------------------------------------------
+struct TileSpot {
+    int tm, tn, g, m0, rows_m, n0, rows_n, expert;
+};
+
+template <int BM, int BN, int MODE>
+__device__ __forceinline__ bool place_tile(const GemmParams &p, int lane, TileSpot &t) {
+    t.g = 0;
+    t.expert = 0;
+    if (MODE == MODE_DENSE) {
+        tile_coords<false>(blockIdx.x, p.tiles_m, p.tiles_n, t.tm, t.tn);
+        t.m0 = t.tm * BM;
+        t.rows_m = min(p.M - t.m0, BM);
+    } else if (MODE == MODE_MASKED) {
+        t.tm = blockIdx.x / p.tiles_n;
+        t.tn = blockIdx.x % p.tiles_n;
+        t.g = blockIdx.y;
+        t.m0 = t.tm * BM;
+        const int mg = min(max(p.masked_m[t.g], 0), p.cap);
+        if (t.m0 >= mg) return false;              // nothing valid in this tile: no load at all
+        t.rows_m = min(mg - t.m0, BM);
+        t.expert = t.g;
+    } else {
+        // The expert of a block of rows is that of its first row naming a
+        // valid expert; a block with none is all padding.  Rows of any other
+        // expert in the block are not written by this tile.
+        auto first_expert = [&](int r0, int nrows) {
+            for (int base = 0; base < nrows; base += 64) {
+                const int r = base + lane;
+                int e = -1;
+                if (r < nrows) e = p.grp_idx[r0 + r];
+                const bool ok = (e >= 0) && (e < p.G);
+                const unsigned long long ball = __ballot(ok);
+                if (ball) return __builtin_amdgcn_readfirstlane(__shfl(e, __builtin_ctzll(ball)));
+            }
+            return -1;
+        };
+        const int ntiles = p.tiles_m * p.tiles_n;
+        if (BM != 256 || (int)blockIdx.x < ntiles) {
+            tile_coords<true>(blockIdx.x, p.tiles_m, p.tiles_n, t.tm, t.tn);
+            t.m0 = t.tm * BM;
+            t.rows_m = min(p.M - t.m0, BM);
+            t.expert = first_expert(t.m0, t.rows_m);
+            if (t.expert < 0) return false;
+        } else {
+            // A 256-row tile covers two 128-row blocks, each of at most one
+            // expert, and writes the rows of the expert of its first valid
+            // row.  The second half of the grid (one workgroup per tile)
+            // covers the second block when its expert differs: it computes
+            // that block alone (tile rows 128..255 read zeros).  These
+            // workgroups come last in dispatch order, where the last partial
+            // wave of full tiles leaves CUs idle.
+            const int w2 = blockIdx.x - ntiles;
+            t.tm = w2 / p.tiles_n;
+            t.tn = w2 % p.tiles_n;
+            const int base = t.tm * BM;
+            const int r2 = min(p.M - (base + 128), 128);
+            if (r2 <= 0) return false;
+            const int e1 = first_expert(base, min(p.M - base, BM));
+            const int e2 = first_expert(base + 128, r2);
+            if (e2 < 0 || e2 == e1) return false;
+            t.m0 = base + 128;
+            t.rows_m = r2;
+            t.expert = e2;
+        }
+    }
+    t.n0 = t.tn * BN;
+    t.rows_n = min(p.N - t.n0, BN);
+    return true;
+}
+
+// Write a BF16 output tile staged in LDS (row r at r * BN * 2 bytes, 16-byte
+// chunk c stored at c ^ (r % (BN / 8))) with 16-byte stores of whole row
+// segments; the contiguous form writes only the rows of the tile's expert.
+template <int BM, int BN, int THREADS, int MODE>
+__device__ __forceinline__ void store_staged(const GemmParams &p, const uint8_t *smem, int tid, const TileSpot &t,
+                                             uint16_t *d_base) {
+    constexpr int OCH = BN / 8;
+    constexpr int OUT_CHUNKS = BM * OCH;
+    static_assert(OUT_CHUNKS % THREADS == 0, "staged tile splits evenly over the threads");
+#pragma unroll 4
+    for (int q = tid; q < OUT_CHUNKS; q += THREADS) {
+        const int r = q / OCH;
+        const int c = q % OCH;
+        if (r >= t.rows_m) continue;
+        const int m = t.m0 + r;
+        if (MODE == MODE_CONTIG && p.grp_idx[m] != t.expert) continue;
+        const int n = t.n0 + c * 8;
+        const v4u v = *reinterpret_cast<const v4u *>(smem + r * (BN * 2) + ((c ^ (r % OCH)) * 16));
+        uint16_t *dst = d_base + (int64_t)m * p.ldd + n;
+        const int nvalid = p.N - n;
+        if (nvalid >= 8) {
+            *reinterpret_cast<v4u *>(dst) = v;
+        } else if (nvalid > 0) {
+            const uint16_t e[8] = {(uint16_t)(v[0] & 0xFFFFu), (uint16_t)(v[0] >> 16), (uint16_t)(v[1] & 0xFFFFu),
+                                   (uint16_t)(v[1] >> 16), (uint16_t)(v[2] & 0xFFFFu), (uint16_t)(v[2] >> 16),
+                                   (uint16_t)(v[3] & 0xFFFFu), (uint16_t)(v[3] >> 16)};
+            for (int k = 0; k < nvalid; ++k) dst[k] = e[k];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // LDS-tiled kernel with a direct-to-LDS ring.
 // BM x BN tile (tokens x weights) per workgroup of WM x WN waves; each wave
 // owns a TM x TN sub-tile of (TM/32) x (TN/32) 32x32 accumulator blocks.  K
@@ -196,69 +307,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     const int wn = wave / WM;
 
     // ---- tile coordinates and per-mode operand bases (64-bit arithmetic) ----
-    int tm, tn, g = 0;
-    int m0;                                        // first output row of this tile
-    int rows_m;
-    int expert = 0;
-    if (MODE == MODE_DENSE) {
-        tile_coords<false>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-        m0 = tm * BM;
-        rows_m = min(p.M - m0, BM);
-    } else if (MODE == MODE_MASKED) {
-        tm = blockIdx.x / p.tiles_n;
-        tn = blockIdx.x % p.tiles_n;
-        g = blockIdx.y;
-        m0 = tm * BM;
-        const int mg = min(max(p.masked_m[g], 0), p.cap);
-        if (m0 >= mg) return;                      // nothing valid in this tile: no load at all
-        rows_m = min(mg - m0, BM);
-        expert = g;
-    } else {
-        // The expert of a block of rows is that of its first row naming a
-        // valid expert; a block with none is all padding.  Rows of any other
-        // expert in the block are not written by this tile.
-        auto first_expert = [&](int r0, int nrows) {
-            for (int base = 0; base < nrows; base += 64) {
-                const int r = base + lane;
-                int e = -1;
-                if (r < nrows) e = p.grp_idx[r0 + r];
-                const bool ok = (e >= 0) && (e < p.G);
-                const unsigned long long ball = __ballot(ok);
-                if (ball) return __builtin_amdgcn_readfirstlane(__shfl(e, __builtin_ctzll(ball)));
-            }
-            return -1;
-        };
-        const int ntiles = p.tiles_m * p.tiles_n;
-        if (BM != 256 || (int)blockIdx.x < ntiles) {
-            tile_coords<true>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-            m0 = tm * BM;
-            rows_m = min(p.M - m0, BM);
-            expert = first_expert(m0, rows_m);
-            if (expert < 0) return;
-        } else {
-            // A 256-row tile covers two 128-row blocks, each of at most one
-            // expert, and writes the rows of the expert of its first valid
-            // row.  The second half of the grid (one workgroup per tile)
-            // covers the second block when its expert differs: it computes
-            // that block alone (tile rows 128..255 read zeros).  These
-            // workgroups come last in dispatch order, where the last partial
-            // wave of full tiles leaves CUs idle.
-            const int w2 = blockIdx.x - ntiles;
-            tm = w2 / p.tiles_n;
-            tn = w2 % p.tiles_n;
-            const int base = tm * BM;
-            const int r2 = min(p.M - (base + 128), 128);
-            if (r2 <= 0) return;
-            const int e1 = first_expert(base, min(p.M - base, BM));
-            const int e2 = first_expert(base + 128, r2);
-            if (e2 < 0 || e2 == e1) return;
-            m0 = base + 128;
-            rows_m = r2;
-            expert = e2;
-        }
-    }
-    const int n0 = tn * BN;
-    const int rows_n = min(p.N - n0, BN);
+    TileSpot spot;
+    if (!place_tile<BM, BN, MODE>(p, lane, spot)) return;
+    const int g = spot.g, m0 = spot.m0, rows_m = spot.rows_m, expert = spot.expert;
+    const int n0 = spot.n0, rows_n = spot.rows_n;
     uint16_t *d_base = p.D + (MODE == MODE_MASKED ? (int64_t)g * p.d_gstride : 0);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
 
@@ -500,28 +552,234 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
         }
     }
     __syncthreads();
-    constexpr int OUT_CHUNKS = BM * OCH;
-    static_assert(OUT_CHUNKS % THREADS == 0, "staged tile splits evenly over the threads");
-#pragma unroll 4
-    for (int q = tid; q < OUT_CHUNKS; q += THREADS) {
-        const int r = q / OCH;
-        const int c = q % OCH;
-        if (r >= rows_m) continue;
-        const int m = m0 + r;
-        if (MODE == MODE_CONTIG && p.grp_idx[m] != expert) continue;
-        const int n = n0 + c * 8;
-        const v4u v = *reinterpret_cast<const v4u *>(smem + r * (BN * 2) + ((c ^ (r % OCH)) * 16));
-        uint16_t *dst = d_base + (int64_t)m * p.ldd + n;
-        const int nvalid = p.N - n;
-        if (nvalid >= 8) {
-            *reinterpret_cast<v4u *>(dst) = v;
-        } else if (nvalid > 0) {
-            const uint16_t e[8] = {(uint16_t)(v[0] & 0xFFFFu), (uint16_t)(v[0] >> 16), (uint16_t)(v[1] & 0xFFFFu),
-                                   (uint16_t)(v[1] >> 16), (uint16_t)(v[2] & 0xFFFFu), (uint16_t)(v[2] >> 16),
-                                   (uint16_t)(v[3] & 0xFFFFu), (uint16_t)(v[3] >> 16)};
-            for (int t = 0; t < nvalid; ++t) dst[t] = e[t];
+    store_staged<BM, BN, THREADS, MODE>(p, smem, tid, spot, d_base);
+}
+
+// ---------------------------------------------------------------------------
+// Four-wave tiled kernel on the 16x16x128 instruction (FP8, dense form,
+// per-tensor or per-channel scales).
+// 256 x 256 output tile; 4 waves as 2 x 2, each owning 128 x 128 outputs as
+// 8 weight blocks x 8 token blocks of 16 rows; the same 2-slot direct-to-LDS
+// ring of 128-byte K steps as ring_kernel.  Against ring_kernel's 8 waves of
+// 64 x 128 on 32x32x64 this reads a third fewer LDS bytes per FLOP, and the
+// 16x16x128 form draws less power per FLOP, so the chip, power-limited under
+// this load, holds a higher clock.  One instruction spans the whole 128-byte
+// K step: a fragment is a 16-row x 128-byte block, two 16-byte chunks per lane
+// (row l % 16, chunks l / 16 and 4 + l / 16; A and B alike, so any K order
+// inside the step is the same for both operands).
+//
+// LDS image: chunk c of ring row r is stored at c ^ ((r >> 1) & 7).  With it
+// the lanes the LDS serves together in a fragment read hit distinct banks;
+// ring_key, made for 32-row reads, leaves 2-way conflicts here (measured).
+//
+// Per K step kt, 64 MFMAs per wave in two halves, token blocks 0..3 then
+// 4..7, each weight-block major:
+//   - first half: token blocks 4..7 of step kt are read in between (their
+//     registers were freed by the last MFMAs of step kt - 1);
+//   - before MFMA kBarAt: this wave's copies of step kt + 1 have landed
+//     (vmcnt), then the step's one barrier: everyone's have, and every wave
+//     has read all of step kt's fragments, so step kt's slot is free;
+//   - MFMAs kDmaFrom .. kDmaTo - 1 carry the copies of step kt + 2 into it;
+//   - second half: each register set takes step kt + 1's fragment as soon as
+//     its last use in step kt has issued.
+// ---------------------------------------------------------------------------
+template <int FA, int FB, int MODE, int SCL>
+__global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
+    constexpr bool CHN = SCL == SCALE_CHANNEL;
+    // The contiguous grouped form stays on ring_kernel: there, with every
+    // expert's weights streaming from HBM, this kernel measured 4% slower
+    // (1.90 against 1.82 ms on the 65536-row prefill).
+    static_assert(FA != FMT_BF16 && FB != FMT_BF16 && SCL != SCALE_BLOCK && MODE == MODE_DENSE,
+                  "FP8 operands, dense form, per-tensor or per-channel scales");
+    constexpr int BM = 256, BN = 256, BK = 128, STAGES = 2, WM = 2, WN = 2, WAVES = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;      // 128 x 128 outputs per wave
+    constexpr int FM = TM / 16, FN = TN / 16;      // token blocks, weight blocks
+    constexpr int KCH = BK / 16, DROWS = 1024 / BK;
+    constexpr int SLOT = (BM + BN) * BK;
+    constexpr int CPW = SLOT / 1024 / WAVES;       // copy instructions per wave per step
+    constexpr int STAGE_OUT = BM * BN * 2;
+    constexpr int RING = STAGES * SLOT;
+    constexpr int SMEM = RING > STAGE_OUT ? RING : STAGE_OUT;
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int OCH = BN / 8;
+    constexpr int kBarAt = 20, kDmaFrom = 20, kDmaTo = 48;
+    static_assert(FM == 8 && FN == 8 && (SLOT / 1024) % WAVES == 0, "shape");
+    static_assert(kBarAt >= 16 && kBarAt <= 32 && kDmaFrom >= kBarAt && kDmaTo <= 64 && kDmaTo - kDmaFrom >= CPW,
+                  "schedule: the barrier after the first half's reads, before the second half's");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM;
+    const int wn = wave / WM;
+
+    TileSpot spot;
+    if (!place_tile<BM, BN, MODE>(p, lane, spot)) return;
+    const int m0 = spot.m0, rows_m = spot.rows_m;
+    const int n0 = spot.n0, rows_n = spot.rows_n;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
+    const uint8_t *a_base = p.A + (int64_t)m0 * p.lda;
+    const uint8_t *b_base = p.B + (int64_t)n0 * p.ldb;
+    const float sc = CHN ? 1.0f : p.scale_a[0] * p.scale_b[0];
+    // Rows past rows_m / rows_n fall outside the descriptors: zeros, no memory access.
+    const v4i srdA = make_srd(a_base, rows_bytes(rows_m, p.lda));
+    const v4i srdB = make_srd(b_base, rows_bytes(rows_n, p.ldb));
+
+    // ---- copies: instruction q fills ring rows 8 qq .. 8 qq + 7 of its
+    // operand (qq: its index within the operand); lane l deposits row l / 8,
+    // stored chunk l % 8, loading logical chunk (l % 8) ^ key(row).  The key
+    // of row 8 qq + r is ((qq & 1) * 4 + (r >> 1)) & 7: two choices per lane.
+    auto key16 = [](uint32_t row) { return (row >> 1) & 7u; };
+    const uint32_t lrow_in = (uint32_t)lane / KCH;
+    uint32_t dkc0 = (((uint32_t)lane % KCH) ^ key16(lrow_in)) * 16u;
+    uint32_t dkc1 = (((uint32_t)lane % KCH) ^ key16(DROWS + lrow_in)) * 16u;
+    uint32_t doA0 = lrow_in * (uint32_t)p.lda + dkc0, doA1 = lrow_in * (uint32_t)p.lda + dkc1;
+    uint32_t doB0 = lrow_in * (uint32_t)p.ldb + dkc0, doB1 = lrow_in * (uint32_t)p.ldb + dkc1;
+    const int nk = (p.K + BK - 1) / BK;
+    auto issue_one = [&](int kt, int i) {
+        const int q = wave * CPW + i;              // wave-uniform
+        const bool isA = q < BM / DROWS;
+        const int qq = isA ? q : q - BM / DROWS;
+        const uint32_t k0 = (uint32_t)kt * BK;
+        const uint32_t rowoff = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)((uint32_t)(qq * DROWS) * (uint32_t)(isA ? p.lda : p.ldb) + k0));
+        const uint32_t kc = (qq & 1) ? dkc1 : dkc0;
+        const uint32_t lo = (qq & 1) ? (isA ? doA1 : doB1) : (isA ? doA0 : doB0);
+        const bool in = (kt < nk) && (int)(k0 + kc) < p.K;
+        dma16(isA ? srdA : srdB, in ? lo + rowoff : kOobOffset,
+              lds0 + (kt % STAGES) * SLOT + (uint32_t)q * 1024u);
+    };
+
+    // ---- fragments (blocks start at multiples of 16 rows, so the key of a
+    // lane's row depends on l % 16 only)
+    const int r16 = lane & 15;
+    const int kg = lane >> 4;
+    const uint32_t key = key16((uint32_t)r16);
+    const uint32_t fo0 = (uint32_t)r16 * BK + (((uint32_t)kg ^ key) & 7u) * 16u;
+    const uint32_t fo1 = (uint32_t)r16 * BK + (((uint32_t)(4 + kg) ^ key) & 7u) * 16u;
+    const uint32_t a_frag = (uint32_t)(wm * TM) * BK;
+    const uint32_t b_frag = (uint32_t)BM * BK + (uint32_t)(wn * TN) * BK;
+    auto frag = [&](const uint8_t *slot, uint32_t base, int blk) {
+        const uint8_t *r = slot + base + blk * 16 * BK;
+        return pack8(*reinterpret_cast<const v4u *>(r + fo0), *reinterpret_cast<const v4u *>(r + fo1));
+    };
+
+    v4f acc[FN][FM];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[j][i] = (v4f){0, 0, 0, 0};
+    v8i wf[FN], tf[FM];                            // one register set per block, reused in place
+
+    auto step = [&](int kt) {
+        const uint8_t *cur = smem + (kt % STAGES) * SLOT;
+        const uint8_t *nxt = smem + ((kt + 1) % STAGES) * SLOT;
+        // Redefined each step so that the compiler forms the copy offsets in
+        // the loop instead of keeping one register per instruction live.
+        asm volatile("" : "+v"(doA0), "+v"(doA1), "+v"(doB0), "+v"(doB1), "+v"(dkc0), "+v"(dkc1));
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int ii = 0; ii < FM / 2; ++ii) {
+                    const int i = h * (FM / 2) + ii;
+                    const int t = h * (FN * FM / 2) + j * (FM / 2) + ii;
+                    if (t == kBarAt) {
+                        vmcnt_wait<0>();           // this wave's copies of step kt + 1 have landed
+                        __syncthreads();           // everyone's have; step kt's slot is no longer read
+                    }
+                    acc[j][i] = mfma16x16x128<FB, FA>(wf[j], tf[i], acc[j][i]);
+                    if (h == 0) {
+                        if (t % 4 == 1 && t / 4 < FM / 2) tf[FM / 2 + t / 4] = frag(cur, a_frag, FM / 2 + t / 4);
+                    } else {
+                        if (j < FM / 2 && ii == 1) tf[j] = frag(nxt, a_frag, j);
+                        if (ii == FM / 2 - 1) wf[j] = frag(nxt, b_frag, j);
+                    }
+                    if (t >= kDmaFrom && t < kDmaTo) {
+                        constexpr int SPAN = kDmaTo - kDmaFrom;
+                        const int u = t - kDmaFrom;
+#pragma unroll
+                        for (int q = (u * CPW) / SPAN; q < ((u + 1) * CPW) / SPAN; ++q) issue_one(kt + STAGES, q);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+    };
+
+    // ---- main loop (past the last step the copy offsets are out of range:
+    // zeros, no memory access, never read)
+#pragma unroll
+    for (int st = 0; st < STAGES; ++st)
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) issue_one(st, i);
+    vmcnt_wait<CPW * (STAGES - 1)>();              // this wave's part of step 0 has landed
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < FN; ++j) wf[j] = frag(smem, b_frag, j);
+#pragma unroll
+    for (int i = 0; i < FM / 2; ++i) tf[i] = frag(smem, a_frag, i);
+    // Nothing outstanding on the LDS / scalar-load counter at the loop head:
+    // otherwise the compiler assumes a scalar load may still be in flight
+    // there and waits for every LDS read (lgkmcnt(0)) at the top of each step.
+    lgkmcnt_wait<0>();
+    for (int kt = 0; kt < nk; ++kt) step(kt);
+    vmcnt_wait<0>();                               // drain the (out-of-range) prefetches
+    __syncthreads();                               // every wave's copies have landed; the ring is free
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- epilogue: accumulator register r of a 16x16 block holds weight row
+    // 4 (l / 16) + r and token column l % 16, so a lane holds four consecutive
+    // output columns of one output row: scale, round to BF16, stage in LDS as
+    // ring_kernel does, then 16-byte stores of whole row segments.  (The lane
+    // index is taken afresh here so that no lane value stays live across the
+    // loop next to the 256 accumulators.)
+    const int el = (int)__lane_id();
+    const int er16 = el & 15, ekg = el >> 4;
+    auto put = [&](int i, int j, v2u v) {
+        const uint32_t m = (uint32_t)(wm * TM + i * 16 + er16);
+        const uint32_t n = (uint32_t)(wn * TN + j * 16 + ekg * 4);
+        const uint32_t chunk = (n >> 3) ^ (m % OCH);
+        *reinterpret_cast<v2u *>(smem + m * (BN * 2) + chunk * 16 + (n & 4) * 2) = v;
+    };
+    // The loop orders below are the ones that keep the compiler's copies of
+    // the 256 accumulators out of AGPRs within the register budget (the other
+    // order spills in each case).
+    if constexpr (CHN) {
+        // the row scales of this lane's 8 rows, then per weight block the
+        // four channels' scales and biases, each loaded once
+        float sam[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = wm * TM + i * 16 + er16;
+            sam[i] = p.ch_sa && m < rows_m ? p.ch_sa[m0 + m] : 1.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            float s4[4], b4[4];
+            channel_terms(p, n0 + wn * TN + j * 16 + ekg * 4, s4, b4);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const v4f &c = acc[j][i];
+                put(i, j, pack_bf16x4(c[0] * sam[i] * s4[0] + b4[0], c[1] * sam[i] * s4[1] + b4[1],
+                                      c[2] * sam[i] * s4[2] + b4[2], c[3] * sam[i] * s4[3] + b4[3]));
+            }
+            __builtin_amdgcn_sched_barrier(0);     // one weight block at a time: bounded live registers
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const v4f &c = acc[j][i];
+                put(i, j, pack_bf16x4(c[0] * sc, c[1] * sc, c[2] * sc, c[3] * sc));
+            }
+            __builtin_amdgcn_sched_barrier(0);     // one token block at a time: bounded live registers
         }
     }
+    __syncthreads();
+    store_staged<BM, BN, THREADS, MODE>(p, smem, tid, spot, p.D);
 }
 
 // ---------------------------------------------------------------------------

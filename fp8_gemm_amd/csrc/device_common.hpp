@@ -61,6 +61,14 @@ __device__ __forceinline__ void dma16(v4i srd, uint32_t voff, uint32_t lds_base)
                  : "memory", "m0");
 }
 
+// The same with the LDS address handed to the compiler as M0's value, so that
+// it writes M0 itself with a single scalar instruction (for example
+// s_add_i32 m0, base, 0x400 for consecutive 1 KB destinations) instead of
+// computing the address into a scalar register and copying it into M0.
+__device__ __forceinline__ void dma16_m0(v4i srd, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(srd), "{m0}"(lds_addr) : "memory");
+}
+
 // The same with 4 bytes per lane: lane l's dword lands at lds_base + 4 * l
 // (256 bytes per instruction).  Used for the block scales.
 __device__ __forceinline__ void dma4(v4i srd, uint32_t voff, uint32_t lds_base) {

@@ -227,7 +227,12 @@ int launch_ring(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
 template <int MODE, int SCL>
 int launch_tile16(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     const dim3 block(256);
-#define FP8G_T16(FA, FB) hipLaunchKernelGGL((fp8g::tile16_kernel<FA, FB, MODE, SCL>), grid, block, 0, s, p)
+    // K not a multiple of 128: the variant with the per-lane check of the last step
+#define FP8G_T16(FA, FB)                                                                                \
+    do {                                                                                                 \
+        if (p.K % 128) hipLaunchKernelGGL((fp8g::tile16_kernel<FA, FB, MODE, SCL, true>), grid, block, 0, s, p); \
+        else hipLaunchKernelGGL((fp8g::tile16_kernel<FA, FB, MODE, SCL, false>), grid, block, 0, s, p);   \
+    } while (0)
     if (fa == 0 && fb == 0) FP8G_T16(0, 0);
     else if (fa == 0 && fb == 1) FP8G_T16(0, 1);
     else if (fa == 1 && fb == 0) FP8G_T16(1, 0);

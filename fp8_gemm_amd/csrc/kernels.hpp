@@ -583,7 +583,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 //   - second half: each register set takes step kt + 1's fragment as soon as
 //     its last use in step kt has issued.
 // ---------------------------------------------------------------------------
-template <int FA, int FB, int MODE, int SCL>
+template <int FA, int FB, int MODE, int SCL, bool KTAIL>
 __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     constexpr bool CHN = SCL == SCALE_CHANNEL;
     // The contiguous grouped form stays on ring_kernel: there, with every
@@ -627,29 +627,54 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     const v4i srdA = make_srd(a_base, rows_bytes(rows_m, p.lda));
     const v4i srdB = make_srd(b_base, rows_bytes(rows_n, p.ldb));
 
-    // ---- copies: instruction q fills ring rows 8 qq .. 8 qq + 7 of its
-    // operand (qq: its index within the operand); lane l deposits row l / 8,
-    // stored chunk l % 8, loading logical chunk (l % 8) ^ key(row).  The key
-    // of row 8 qq + r is ((qq & 1) * 4 + (r >> 1)) & 7: two choices per lane.
+    // ---- copies.  Per step the tile is 64 copy instructions of 8 rows x 128
+    // bytes, 16 per wave: waves 0-1 copy A's 256 rows, waves 2-3 B's.  Copy i
+    // of a wave fills ring rows 8 qq .. 8 qq + 7 of its operand (qq = i + 16
+    // (wave mod 2)); lane l deposits row l / 8, stored chunk l % 8, loading
+    // logical chunk (l % 8) ^ key(row).  The key of row 8 qq + r is
+    // ((qq & 1) * 4 + (r >> 1)) & 7, so a lane's offset within the tile is
+    // fixed per copy and kept in a register; each step only moves the
+    // descriptor's base by the step's K offset (and shrinks its byte count by
+    // as much, so rows past the tile's valid rows still read zeros), and
+    // past the last step the byte count is 0.  The loop then spends one
+    // scalar instruction per copy (the M0 address) and no vector ones.
     auto key16 = [](uint32_t row) { return (row >> 1) & 7u; };
     const uint32_t lrow_in = (uint32_t)lane / KCH;
-    uint32_t dkc0 = (((uint32_t)lane % KCH) ^ key16(lrow_in)) * 16u;
-    uint32_t dkc1 = (((uint32_t)lane % KCH) ^ key16(DROWS + lrow_in)) * 16u;
-    uint32_t doA0 = lrow_in * (uint32_t)p.lda + dkc0, doA1 = lrow_in * (uint32_t)p.lda + dkc1;
-    uint32_t doB0 = lrow_in * (uint32_t)p.ldb + dkc0, doB1 = lrow_in * (uint32_t)p.ldb + dkc1;
+    const uint32_t dkc0 = (((uint32_t)lane % KCH) ^ key16(lrow_in)) * 16u;
+    const uint32_t dkc1 = (((uint32_t)lane % KCH) ^ key16(DROWS + lrow_in)) * 16u;
     const int nk = (p.K + BK - 1) / BK;
-    auto issue_one = [&](int kt, int i) {
-        const int q = wave * CPW + i;              // wave-uniform
-        const bool isA = q < BM / DROWS;
-        const int qq = isA ? q : q - BM / DROWS;
-        const uint32_t k0 = (uint32_t)kt * BK;
-        const uint32_t rowoff = (uint32_t)__builtin_amdgcn_readfirstlane(
-            (int)((uint32_t)(qq * DROWS) * (uint32_t)(isA ? p.lda : p.ldb) + k0));
-        const uint32_t kc = (qq & 1) ? dkc1 : dkc0;
-        const uint32_t lo = (qq & 1) ? (isA ? doA1 : doB1) : (isA ? doA0 : doB0);
-        const bool in = (kt < nk) && (int)(k0 + kc) < p.K;
-        dma16(isA ? srdA : srdB, in ? lo + rowoff : kOobOffset,
-              lds0 + (kt % STAGES) * SLOT + (uint32_t)q * 1024u);
+    const bool wA = wave * CPW < BM / DROWS;       // wave-uniform
+    const v4i srd0 = wA ? srdA : srdB;
+    const int64_t ld = wA ? p.lda : p.ldb;
+    uint32_t lo_q[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int qq = (wave * CPW + i) % (BM / DROWS);
+        lo_q[i] = (uint32_t)(qq * DROWS + (int)lrow_in) * (uint32_t)ld + ((qq & 1) ? dkc1 : dkc0);
+    }
+    const uint64_t base0 = ((uint64_t)(uint32_t)srd0[1] << 32) | (uint32_t)srd0[0];
+    const uint32_t lds_wave = lds0 + (uint32_t)(wave * CPW) * 1024u;
+    v4i srdk = srd0;
+    uint32_t lds_slot = 0;
+    // K tail (K not a multiple of 128): on the last step, lanes whose chunk
+    // starts at or past K add kOobOffset (their offset, below 2^31 before,
+    // then lies in [2^31, 2^32): past every descriptor).
+    uint32_t ko0 = 0, ko1 = 0;
+    auto set_step = [&](int kd) {                  // the copies of step kd follow
+        const uint64_t b = base0 + (uint64_t)kd * BK;
+        srdk[0] = (int)(uint32_t)b;
+        srdk[1] = (int)(uint32_t)(b >> 32);
+        srdk[2] = kd < nk ? srd0[2] - kd * BK : 0;
+        lds_slot = lds_wave + (uint32_t)(kd % STAGES) * SLOT;
+        if (KTAIL) {
+            const int lim = p.K - kd * BK;
+            ko0 = (int)dkc0 < lim ? 0u : kOobOffset;
+            ko1 = (int)dkc1 < lim ? 0u : kOobOffset;
+        }
+    };
+    auto issue_one = [&](int i) {
+        const uint32_t voff = KTAIL ? lo_q[i] + ((i & 1) ? ko1 : ko0) : lo_q[i];
+        dma16_m0(srdk, voff, lds_slot + (uint32_t)i * 1024u);
     };
 
     // ---- fragments (blocks start at multiples of 16 rows, so the key of a
@@ -676,9 +701,6 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     auto step = [&](int kt) {
         const uint8_t *cur = smem + (kt % STAGES) * SLOT;
         const uint8_t *nxt = smem + ((kt + 1) % STAGES) * SLOT;
-        // Redefined each step so that the compiler forms the copy offsets in
-        // the loop instead of keeping one register per instruction live.
-        asm volatile("" : "+v"(doA0), "+v"(doA1), "+v"(doB0), "+v"(doB1), "+v"(dkc0), "+v"(dkc1));
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -698,11 +720,12 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
                         if (j < FM / 2 && ii == 1) tf[j] = frag(nxt, a_frag, j);
                         if (ii == FM / 2 - 1) wf[j] = frag(nxt, b_frag, j);
                     }
+                    if (t == kDmaFrom) set_step(kt + STAGES);
                     if (t >= kDmaFrom && t < kDmaTo) {
                         constexpr int SPAN = kDmaTo - kDmaFrom;
                         const int u = t - kDmaFrom;
 #pragma unroll
-                        for (int q = (u * CPW) / SPAN; q < ((u + 1) * CPW) / SPAN; ++q) issue_one(kt + STAGES, q);
+                        for (int q = (u * CPW) / SPAN; q < ((u + 1) * CPW) / SPAN; ++q) issue_one(q);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -711,9 +734,11 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     // ---- main loop (past the last step the copy offsets are out of range:
     // zeros, no memory access, never read)
 #pragma unroll
-    for (int st = 0; st < STAGES; ++st)
+    for (int st = 0; st < STAGES; ++st) {
+        set_step(st);
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) issue_one(st, i);
+        for (int i = 0; i < CPW; ++i) issue_one(i);
+    }
     vmcnt_wait<CPW * (STAGES - 1)>();              // this wave's part of step 0 has landed
     __syncthreads();
 #pragma unroll

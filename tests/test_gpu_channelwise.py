@@ -45,7 +45,9 @@ def run(w, sa, sb, bias):
     (64, 4100, 384, E4M3, E4M3, "ac"),
     (20, 8204, 512, E4M3, E4M3, "abc"),     # decode kernel with 32-row workgroups, N tail of 12
     (300, 264, 400, E4M3, E5M2, "abc"),     # 128x256 tiles
-    (513, 300, 256, E4M3, E4M3, "c"),       # 256x256 tiles, bias only
+    (513, 300, 256, E4M3, E4M3, "c"),       # 128x256 tiles, bias only
+    (4000, 3000, 528, E4M3, E4M3, "abc"),   # 256x256 tiles, every edge partial, K tail
+    (3968, 3840, 1024, E5M2, E4M3, "b"),    # 256x256 tiles, channel scales only
     (129, 136, 128, E5M2, E5M2, "ab"),
 ])
 def test_channelwise_matches_oracle(M, N, K, fa, fb, which):
@@ -65,7 +67,7 @@ def test_channelwise_matches_oracle(M, N, K, fa, fb, which):
 def test_zero_weights_give_the_rounded_bias():
     """With B = 0 every output is bf16(bias[n]) exactly, on every kernel."""
     rng = np.random.default_rng(31)
-    for M, N in [(3, 100), (200, 264), (700, 512)]:
+    for M, N in [(3, 100), (200, 264), (700, 512), (3968, 3840)]:
         w = workloads.dense_random(M, N, 256, seed=31 + M)
         w.B[:] = 0
         sa, _, bias = _vectors(rng, M, N, "ac")

@@ -222,6 +222,21 @@ def test_dense_4096_config_sampled(fmt):
     assert_within_bound(d[rows], Rr, Sr, abs(w.sa * w.sb), ref_bits=Dr, what="full rows")
 
 
+@pytest.mark.parametrize("M,N,K,fa,fb", [
+    (4000, 3000, 528, E4M3, E4M3),      # M, N and K tails (K = 4 * 128 + 16)
+    (3900, 3800, 1040, E5M2, E4M3),     # K = 8 * 128 + 16
+    (4000, 3000, 1024, E4M3, E5M2),     # M and N tails only
+    (3968, 3840, 272, E5M2, E5M2),
+])
+def test_256_tiles_ragged_full(M, N, K, fa, fb):
+    """The 256 x 256-tile kernel (the plan picks it for these shapes) with
+    partial tiles on every edge, every format pair and K tails of 16 bytes:
+    the whole output against the oracle."""
+    assert _lib().plan(0, M, N, K).variant == 1
+    w = workloads.dense_random(M, N, K, seed=M + N + K, a_fmt=fa, b_fmt=fb, std=1.0, scales=(0.5, 1.5))
+    _check_dense(w, f"256-tile {M}x{N}x{K} fmt ({fa},{fb})")
+
+
 @pytest.mark.parametrize("M,N,K", [(6144, 6144, 1280), (4096, 4096, 1024)])
 def test_k_tail_regression_shapes_sampled(M, N, K):
     """Shapes from "DeepGEMM on Hopper Tensor Cores", section 6.1: one failed

@@ -1,10 +1,13 @@
 """Properties of the compiled gfx950 code, checked on the AMD assembly of this
 repository's own kernels (CPU only: hipcc cross-compiles).
 
-* M0 is written only by the direct-to-LDS load helper, each write immediately
-  followed by its `buffer_load_dword{,x4} ... lds`, and read by nothing else: the
-  helper's inline assembly sets M0 itself, so no compiler-generated code may
-  rely on M0 across it.
+* M0 only ever feeds the direct-to-LDS loads: it appears only as the
+  destination of scalar instructions, every write is consumed by a
+  `buffer_load_dword{,x4} ... lds` before the next one, and no instruction that
+  reads M0 implicitly (relative moves, messages, GDS/GWS, interpolation) is
+  present.  One helper sets M0 in its own inline assembly, the other hands the
+  value to the compiler as an M0 operand; either way nothing else may rely on
+  M0.
 * No kernel spills to scratch memory.
 * No packed FP32 VALU operations and no scalar-memory writes appear anywhere.
 """
@@ -40,14 +43,23 @@ def _code_lines(text):
 
 def test_m0_only_feeds_lds_dma(asm):
     lines = list(_code_lines(asm))
-    writes = 0
-    for i, s in enumerate(lines):
+    writes = dmas = 0
+    pending = False
+    for s in lines:
+        op = s.split()[0]
+        assert not re.match(r"(s|v)_movrel|s_sendmsg|ds_gws|ds_.*_gds|v_interp|lds_param|lds_direct", op), s
         if re.search(r"\bm0\b", s):
-            assert s.startswith("s_mov_b32 m0,"), f"unexpected use of M0: {s}"
-            assert i + 1 < len(lines) and re.match(r"buffer_load_dword(x4)? ", lines[i + 1]) \
-                and lines[i + 1].endswith(" lds"), f"M0 write not followed by an LDS DMA load: {s}"
+            rest = s[len(op):].strip()
+            assert op.startswith("s_") and rest.startswith("m0,") and not re.search(r"\bm0\b", rest[3:]), \
+                f"unexpected use of M0: {s}"
+            assert not pending, f"M0 written twice without a DMA in between: {s}"
+            pending = True
             writes += 1
-    assert writes > 0
+        elif re.match(r"buffer_load_dword(x4)? ", s) and s.endswith(" lds"):
+            assert pending or dmas, f"LDS DMA before any M0 write: {s}"
+            pending = False
+            dmas += 1
+    assert writes > 0 and dmas >= writes
 
 
 def test_no_scratch(asm):

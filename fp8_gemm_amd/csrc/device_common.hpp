@@ -179,16 +179,17 @@ __device__ __forceinline__ v4f mfma16x16x128_s(v8i a, v8i b, v4f c, int sa, int 
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
 }
 
-// BF16 round-to-nearest-even of four floats, packed little-endian.
+// BF16 round-to-nearest-even of four floats, packed little-endian.  Converting
+// float pairs as vectors makes the compiler emit one v_cvt_pk_bf16_f32 per
+// pair; element-wise casts give one per value plus a shift and an OR to pack.
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ v2u pack_bf16x4(float a, float b, float c, float d) {
-    __bf16 h0 = (__bf16)a, h1 = (__bf16)b, h2 = (__bf16)c, h3 = (__bf16)d;
-    uint16_t u0 = __builtin_bit_cast(uint16_t, h0);
-    uint16_t u1 = __builtin_bit_cast(uint16_t, h1);
-    uint16_t u2 = __builtin_bit_cast(uint16_t, h2);
-    uint16_t u3 = __builtin_bit_cast(uint16_t, h3);
+    const v2bf lo = __builtin_convertvector((v2f){a, b}, v2bf);
+    const v2bf hi = __builtin_convertvector((v2f){c, d}, v2bf);
     v2u r;
-    r[0] = (uint32_t)u0 | ((uint32_t)u1 << 16);
-    r[1] = (uint32_t)u2 | ((uint32_t)u3 << 16);
+    r[0] = __builtin_bit_cast(uint32_t, lo);
+    r[1] = __builtin_bit_cast(uint32_t, hi);
     return r;
 }
 

@@ -238,7 +238,12 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const uint8_t 
         uint16_t *dst = d_base + (int64_t)m * p.ldd + n;
         const int nvalid = p.N - n;
         if (nvalid >= 8) {
-            *reinterpret_cast<v4u *>(dst) = v;
+            // dense form: written through (the next launch need not wait for
+            // the write-back of this output); the grouped forms' outputs are
+            // larger than the L2s and stream out regardless (measured 0.5%
+            // slower written through on the contiguous prefill)
+            if (MODE == MODE_DENSE) store16_wt(dst, v);
+            else *reinterpret_cast<v4u *>(dst) = v;
         } else if (nvalid > 0) {
             const uint16_t e[8] = {(uint16_t)(v[0] & 0xFFFFu), (uint16_t)(v[0] >> 16), (uint16_t)(v[1] & 0xFFFFu),
                                    (uint16_t)(v[1] >> 16), (uint16_t)(v[2] & 0xFFFFu), (uint16_t)(v[2] >> 16),

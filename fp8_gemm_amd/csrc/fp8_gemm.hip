@@ -224,14 +224,16 @@ int launch_ring(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     return launch_status("tiled kernel");
 }
 
-template <int MODE, int SCL>
+template <int BM, int STAGES, int MODE, int SCL>
 int launch_tile16(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     const dim3 block(256);
     // K not a multiple of 128: the variant with the per-lane check of the last step
-#define FP8G_T16(FA, FB)                                                                                \
-    do {                                                                                                 \
-        if (p.K % 128) hipLaunchKernelGGL((fp8g::tile16_kernel<FA, FB, MODE, SCL, true>), grid, block, 0, s, p); \
-        else hipLaunchKernelGGL((fp8g::tile16_kernel<FA, FB, MODE, SCL, false>), grid, block, 0, s, p);   \
+#define FP8G_T16(FA, FB)                                                                                     \
+    do {                                                                                                      \
+        if (p.K % 128)                                                                                        \
+            hipLaunchKernelGGL((fp8g::tile16_kernel<BM, STAGES, FA, FB, MODE, SCL, true>), grid, block, 0, s, p); \
+        else                                                                                                  \
+            hipLaunchKernelGGL((fp8g::tile16_kernel<BM, STAGES, FA, FB, MODE, SCL, false>), grid, block, 0, s, p); \
     } while (0)
     if (fa == 0 && fb == 0) FP8G_T16(0, 0);
     else if (fa == 0 && fb == 1) FP8G_T16(0, 1);
@@ -241,20 +243,23 @@ int launch_tile16(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s)
     return launch_status("tiled kernel (16x16x128)");
 }
 
-// Tile shapes of the tiled kernels: 256 x 256, either 4 waves on the
-// 16x16x128 instruction (dense FP8 with per-tensor or per-channel scales) or
-// 8 waves (4 along M, 2 along N) on 32x32x64 (block scales, BF16, contiguous
-// grouped), both with a 2-slot ring of 128-byte K steps (128 KB of LDS);
-// 128 x 256 with 8 waves (2 x 4) and a 3-slot ring (144 KB).
+// Tile shapes of the tiled kernels: 256 x 256 and 128 x 256.  Dense FP8 with
+// per-tensor or per-channel scales runs on 4 waves and the 16x16x128
+// instruction (2-slot ring, 128 KB of LDS, for 256 rows; 3-slot, 144 KB, for
+// 128 rows); block scales, BF16 and the grouped forms on 8 waves and 32x32x64
+// (4 x 2 waves and a 2-slot ring for 256 rows, 2 x 4 and 3 slots for 128).
 template <int MODE, int SCL = 0>
 int launch_tile256(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     if constexpr (SCL != fp8g::SCALE_BLOCK && MODE == fp8g::MODE_DENSE) {
-        if (fa != fp8g::FMT_BF16) return launch_tile16<MODE, SCL>(fa, fb, p, grid, s);
+        if (fa != fp8g::FMT_BF16) return launch_tile16<256, 2, MODE, SCL>(fa, fb, p, grid, s);
     }
     return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE, SCL>(fa, fb, p, grid, s);
 }
 template <int MODE, int SCL = 0>
 int launch_tile128(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    if constexpr (SCL != fp8g::SCALE_BLOCK && MODE == fp8g::MODE_DENSE) {
+        if (fa != fp8g::FMT_BF16) return launch_tile16<128, 3, MODE, SCL>(fa, fb, p, grid, s);
+    }
     return launch_ring<128, 256, TILE128_WM, TILE128_WN, T128_ST, T128_BK, MODE, SCL>(fa, fb, p, grid, s);
 }
 

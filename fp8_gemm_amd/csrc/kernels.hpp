@@ -7,15 +7,16 @@
 // consecutive output columns n of one output row m, so the epilogue writes
 // 8-byte packed BF16 runs straight from registers.
 //
-//   tile16_kernel  LDS-tiled, 256 x 256 output tile per workgroup of 4 waves
-//                  on v_mfma 16x16x128, K in steps of 128 bytes, both operand
-//                  tiles staged through a direct-to-LDS, XOR-swizzled ring.
-//                  Dense FP8 (M > 64) with per-tensor or per-channel scales.
+//   tile16_kernel  LDS-tiled, 256 x 256 or 128 x 256 output tile per
+//                  workgroup of 4 waves on v_mfma 16x16x128, K in steps of 128
+//                  bytes, both operand tiles staged through a direct-to-LDS,
+//                  XOR-swizzled ring.  Dense FP8 (M > 64) with per-tensor or
+//                  per-channel scales.
 //   ring_kernel    the same ring with 8 waves on v_mfma 32x32x64, BM x BN
 //                  = 256 x 256 or 128 x 256: block-scaled dense, masked
-//                  grouped with many rows per group, contiguous grouped, the
-//                  128-row tiles, and the BF16 comparison path (same bytes, two
-//                  v_mfma 32x32x16 BF16 per fragment).
+//                  grouped with many rows per group, contiguous grouped, and
+//                  the BF16 comparison path (same bytes, two v_mfma 32x32x16
+//                  BF16 per fragment).
 //   swap_kernel    streaming "swap-AB" form for few tokens: each wave streams
 //                  its own weight rows (every weight byte is used by exactly
 //                  one wave) through a private LDS ring into the 16x16x128
@@ -563,10 +564,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 // Four-wave tiled kernel on the 16x16x128 instruction (FP8, dense form,
 // per-tensor or per-channel scales).
-// 256 x 256 output tile; 4 waves as 2 x 2, each owning 128 x 128 outputs as
-// 8 weight blocks x 8 token blocks of 16 rows; the same 2-slot direct-to-LDS
-// ring of 128-byte K steps as ring_kernel.  Against ring_kernel's 8 waves of
-// 64 x 128 on 32x32x64 this reads a third fewer LDS bytes per FLOP, and the
+// BM x 256 output tile (BM = 256, or 128 where the 256-row tiles leave too
+// many CUs idle); 4 waves as 2 x 2, each owning BM/2 x 128 outputs as 8
+// weight blocks x BM/32 token blocks of 16 rows; a STAGES-slot direct-to-LDS
+// ring of 128-byte K steps (2 slots of 64 KB for BM = 256, 3 of 48 KB for
+// BM = 128).  Against ring_kernel's 8 waves of 64 x 128 on 32x32x64 the
+// 256-row form reads a third fewer LDS bytes per FLOP, and the
 // 16x16x128 form draws less power per FLOP, so the chip, power-limited under
 // this load, holds a higher clock.  One instruction spans the whole 128-byte
 // K step: a fragment is a 16-row x 128-byte block, two 16-byte chunks per lane
@@ -577,18 +580,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 // the lanes the LDS serves together in a fragment read hit distinct banks;
 // ring_key, made for 32-row reads, leaves 2-way conflicts here (measured).
 //
-// Per K step kt, 64 MFMAs per wave in two halves, token blocks 0..3 then
-// 4..7, each weight-block major:
-//   - first half: token blocks 4..7 of step kt are read in between (their
-//     registers were freed by the last MFMAs of step kt - 1);
+// Per K step kt, 8 x BM/32 MFMAs per wave in two halves (the first and the
+// second half of the token blocks), each weight-block major:
+//   - first half: the second half's token blocks of step kt are read in
+//     between (their registers were freed by the last MFMAs of step kt - 1);
 //   - before MFMA kBarAt: this wave's copies of step kt + 1 have landed
 //     (vmcnt), then the step's one barrier: everyone's have, and every wave
 //     has read all of step kt's fragments, so step kt's slot is free;
-//   - MFMAs kDmaFrom .. kDmaTo - 1 carry the copies of step kt + 2 into it;
+//   - MFMAs kDmaFrom .. kDmaTo - 1 carry the copies of step kt + STAGES into it;
 //   - second half: each register set takes step kt + 1's fragment as soon as
 //     its last use in step kt has issued.
 // ---------------------------------------------------------------------------
-template <int FA, int FB, int MODE, int SCL, bool KTAIL>
+template <int BM, int STAGES, int FA, int FB, int MODE, int SCL, bool KTAIL>
 __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     constexpr bool CHN = SCL == SCALE_CHANNEL;
     // The contiguous grouped form stays on ring_kernel: there, with every
@@ -596,20 +599,26 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     // (1.90 against 1.82 ms on the 65536-row prefill).
     static_assert(FA != FMT_BF16 && FB != FMT_BF16 && SCL != SCALE_BLOCK && MODE == MODE_DENSE,
                   "FP8 operands, dense form, per-tensor or per-channel scales");
-    constexpr int BM = 256, BN = 256, BK = 128, STAGES = 2, WM = 2, WN = 2, WAVES = WM * WN;
-    constexpr int TM = BM / WM, TN = BN / WN;      // 128 x 128 outputs per wave
+    constexpr int BN = 256, BK = 128, WM = 2, WN = 2, WAVES = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;      // 128 (or 64) x 128 outputs per wave
     constexpr int FM = TM / 16, FN = TN / 16;      // token blocks, weight blocks
     constexpr int KCH = BK / 16, DROWS = 1024 / BK;
     constexpr int SLOT = (BM + BN) * BK;
-    constexpr int CPW = SLOT / 1024 / WAVES;       // copy instructions per wave per step
+    constexpr int CPA = BM / DROWS / WAVES;        // copy instructions per wave per step: A rows,
+    constexpr int CPB = BN / DROWS / WAVES;        // B rows
+    constexpr int CPW = CPA + CPB;
     constexpr int STAGE_OUT = BM * BN * 2;
     constexpr int RING = STAGES * SLOT;
     constexpr int SMEM = RING > STAGE_OUT ? RING : STAGE_OUT;
     constexpr int THREADS = 64 * WAVES;
     constexpr int OCH = BN / 8;
-    constexpr int kBarAt = 20, kDmaFrom = 20, kDmaTo = 48;
-    static_assert(FM == 8 && FN == 8 && (SLOT / 1024) % WAVES == 0, "shape");
-    static_assert(kBarAt >= 16 && kBarAt <= 32 && kDmaFrom >= kBarAt && kDmaTo <= 64 && kDmaTo - kDmaFrom >= CPW,
+    constexpr int HALF = FN * FM / 2;              // MFMAs per half step
+    // the step's one barrier, and the MFMAs that carry the copies
+    constexpr int kBarAt = BM == 256 ? 20 : 10, kDmaFrom = kBarAt, kDmaTo = BM == 256 ? 48 : 28;
+    static_assert((BM == 256 || BM == 128) && FN == 8 && CPA % 2 == 0 && CPB % 2 == 0 && CPW % 2 == 0, "shape");
+    static_assert(STAGES >= 2 && RING <= 160 * 1024, "ring");
+    static_assert(kBarAt >= 4 * (FM / 2 - 1) + 2 && kBarAt <= HALF && kDmaFrom >= kBarAt && kDmaTo <= 2 * HALF &&
+                      kDmaTo - kDmaFrom >= CPW,
                   "schedule: the barrier after the first half's reads, before the second half's");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
@@ -632,45 +641,60 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     const v4i srdA = make_srd(a_base, rows_bytes(rows_m, p.lda));
     const v4i srdB = make_srd(b_base, rows_bytes(rows_n, p.ldb));
 
-    // ---- copies.  Per step the tile is 64 copy instructions of 8 rows x 128
-    // bytes, 16 per wave: waves 0-1 copy A's 256 rows, waves 2-3 B's.  Copy i
-    // of a wave fills ring rows 8 qq .. 8 qq + 7 of its operand (qq = i + 16
-    // (wave mod 2)); lane l deposits row l / 8, stored chunk l % 8, loading
-    // logical chunk (l % 8) ^ key(row).  The key of row 8 qq + r is
+    // ---- copies.  Per step the tile is (BM + BN) / 8 copy instructions of 8
+    // rows x 128 bytes, CPW per wave.  Copy qq of an operand fills its ring
+    // rows 8 qq .. 8 qq + 7; lane l deposits row l / 8, stored chunk l % 8,
+    // loading logical chunk (l % 8) ^ key(row).  The key of row 8 qq + r is
     // ((qq & 1) * 4 + (r >> 1)) & 7, so a lane's offset within the tile is
     // fixed per copy and kept in a register; each step only moves the
     // descriptor's base by the step's K offset (and shrinks its byte count by
-    // as much, so rows past the tile's valid rows still read zeros), and
-    // past the last step the byte count is 0.  The loop then spends one
-    // scalar instruction per copy (the M0 address) and no vector ones.
+    // as much, so rows past the tile's valid rows still read zeros), and past
+    // the last step the byte count is 0.  The loop then spends one scalar
+    // instruction per copy (the M0 address) and no vector ones.
+    //   UNI (256-row tiles): waves 0-1 copy A's rows, waves 2-3 B's, copy i of
+    //     wave w being copy w CPW + i of the tile; one descriptor per wave.
+    //   otherwise (128-row tiles): wave w issues A's copies w CPA .. + CPA - 1
+    //     and B's w CPB .. + CPB - 1 (measured 0.2-1.3% slower than UNI on the
+    //     256-row tiles: one more descriptor to move per step).
+    constexpr bool UNI = (BM / DROWS) % CPW == 0;
     auto key16 = [](uint32_t row) { return (row >> 1) & 7u; };
     const uint32_t lrow_in = (uint32_t)lane / KCH;
     const uint32_t dkc0 = (((uint32_t)lane % KCH) ^ key16(lrow_in)) * 16u;
     const uint32_t dkc1 = (((uint32_t)lane % KCH) ^ key16(DROWS + lrow_in)) * 16u;
     const int nk = (p.K + BK - 1) / BK;
-    const bool wA = wave * CPW < BM / DROWS;       // wave-uniform
-    const v4i srd0 = wA ? srdA : srdB;
-    const int64_t ld = wA ? p.lda : p.ldb;
-    uint32_t lo_q[CPW];
+    const bool wA = wave * CPW < BM / DROWS;       // UNI: this wave copies A (wave-uniform)
+    uint32_t lo_q[CPW];                            // UNI: this wave's copies; else A's, then B's
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
-        const int qq = (wave * CPW + i) % (BM / DROWS);
-        lo_q[i] = (uint32_t)(qq * DROWS + (int)lrow_in) * (uint32_t)ld + ((qq & 1) ? dkc1 : dkc0);
+        const bool isA = UNI ? wA : i < CPA;
+        const int qq = UNI ? (wave * CPW + i) % (BM / DROWS) : (isA ? wave * CPA + i : wave * CPB + (i - CPA));
+        lo_q[i] = (uint32_t)(qq * DROWS + (int)lrow_in) * (uint32_t)(isA ? p.lda : p.ldb) + ((qq & 1) ? dkc1 : dkc0);
     }
-    const uint64_t base0 = ((uint64_t)(uint32_t)srd0[1] << 32) | (uint32_t)srd0[0];
-    const uint32_t lds_wave = lds0 + (uint32_t)(wave * CPW) * 1024u;
-    v4i srdk = srd0;
-    uint32_t lds_slot = 0;
+    const v4i srd0A = UNI ? (wA ? srdA : srdB) : srdA;
+    const uint64_t baseA = ((uint64_t)(uint32_t)srd0A[1] << 32) | (uint32_t)srd0A[0];
+    const uint64_t baseB = ((uint64_t)(uint32_t)srdB[1] << 32) | (uint32_t)srdB[0];
+    const uint32_t lds_wa = lds0 + (uint32_t)(wave * (UNI ? CPW : CPA)) * 1024u;
+    const uint32_t lds_wb = lds0 + (uint32_t)(BM / DROWS + wave * CPB) * 1024u;
+    v4i srdAk = srd0A, srdBk = srdB;
+    uint32_t lds_a = 0, lds_b = 0;
     // K tail (K not a multiple of 128): on the last step, lanes whose chunk
     // starts at or past K add kOobOffset (their offset, below 2^31 before,
-    // then lies in [2^31, 2^32): past every descriptor).
+    // then lies in [2^31, 2^32): past every descriptor).  CPW, CPA and CPB are
+    // even, so the key parity of copy i is that of i.
     uint32_t ko0 = 0, ko1 = 0;
     auto set_step = [&](int kd) {                  // the copies of step kd follow
-        const uint64_t b = base0 + (uint64_t)kd * BK;
-        srdk[0] = (int)(uint32_t)b;
-        srdk[1] = (int)(uint32_t)(b >> 32);
-        srdk[2] = kd < nk ? srd0[2] - kd * BK : 0;
-        lds_slot = lds_wave + (uint32_t)(kd % STAGES) * SLOT;
+        const uint64_t ba = baseA + (uint64_t)kd * BK;
+        srdAk[0] = (int)(uint32_t)ba;
+        srdAk[1] = (int)(uint32_t)(ba >> 32);
+        srdAk[2] = kd < nk ? srd0A[2] - kd * BK : 0;
+        lds_a = lds_wa + (uint32_t)(kd % STAGES) * SLOT;
+        if (!UNI) {
+            const uint64_t bb = baseB + (uint64_t)kd * BK;
+            srdBk[0] = (int)(uint32_t)bb;
+            srdBk[1] = (int)(uint32_t)(bb >> 32);
+            srdBk[2] = kd < nk ? srdB[2] - kd * BK : 0;
+            lds_b = lds_wb + (uint32_t)(kd % STAGES) * SLOT;
+        }
         if (KTAIL) {
             const int lim = p.K - kd * BK;
             ko0 = (int)dkc0 < lim ? 0u : kOobOffset;
@@ -679,7 +703,8 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     };
     auto issue_one = [&](int i) {
         const uint32_t voff = KTAIL ? lo_q[i] + ((i & 1) ? ko1 : ko0) : lo_q[i];
-        dma16_m0(srdk, voff, lds_slot + (uint32_t)i * 1024u);
+        if (UNI || i < CPA) dma16_m0(srdAk, voff, lds_a + (uint32_t)i * 1024u);
+        else dma16_m0(srdBk, voff, lds_b + (uint32_t)(i - CPA) * 1024u);
     };
 
     // ---- fragments (blocks start at multiples of 16 rows, so the key of a
@@ -713,9 +738,9 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
 #pragma unroll
                 for (int ii = 0; ii < FM / 2; ++ii) {
                     const int i = h * (FM / 2) + ii;
-                    const int t = h * (FN * FM / 2) + j * (FM / 2) + ii;
+                    const int t = h * HALF + j * (FM / 2) + ii;
                     if (t == kBarAt) {
-                        vmcnt_wait<0>();           // this wave's copies of step kt + 1 have landed
+                        vmcnt_wait<CPW * (STAGES - 2)>();   // this wave's copies of step kt + 1 have landed
                         __syncthreads();           // everyone's have; step kt's slot is no longer read
                     }
                     acc[j][i] = mfma16x16x128<FB, FA>(wf[j], tf[i], acc[j][i]);
@@ -737,7 +762,9 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     };
 
     // ---- main loop (past the last step the copy offsets are out of range:
-    // zeros, no memory access, never read)
+    // zeros, no memory access, never read).  With STAGES slots the copies of
+    // step kt + STAGES refill step kt's slot, so STAGES - 1 steps of copies are
+    // in flight.
 #pragma unroll
     for (int st = 0; st < STAGES; ++st) {
         set_step(st);
@@ -764,7 +791,7 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     // output columns of one output row: scale, round to BF16, stage in LDS as
     // ring_kernel does, then 16-byte stores of whole row segments.  (The lane
     // index is taken afresh here so that no lane value stays live across the
-    // loop next to the 256 accumulators.)
+    // loop next to the accumulators.)
     const int el = (int)__lane_id();
     const int er16 = el & 15, ekg = el >> 4;
     auto put = [&](int i, int j, v2u v) {

@@ -250,14 +250,14 @@ int launch_tile16(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s)
 // (4 x 2 waves and a 2-slot ring for 256 rows, 2 x 4 and 3 slots for 128).
 template <int MODE, int SCL = 0>
 int launch_tile256(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    if constexpr (SCL != fp8g::SCALE_BLOCK && MODE == fp8g::MODE_DENSE) {
+    if constexpr (MODE == fp8g::MODE_DENSE) {
         if (fa != fp8g::FMT_BF16) return launch_tile16<256, 2, MODE, SCL>(fa, fb, p, grid, s);
     }
     return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE, SCL>(fa, fb, p, grid, s);
 }
 template <int MODE, int SCL = 0>
 int launch_tile128(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    if constexpr (SCL != fp8g::SCALE_BLOCK && MODE == fp8g::MODE_DENSE) {
+    if constexpr (MODE == fp8g::MODE_DENSE) {
         if (fa != fp8g::FMT_BF16) return launch_tile16<128, 3, MODE, SCL>(fa, fb, p, grid, s);
     }
     return launch_ring<128, 256, TILE128_WM, TILE128_WN, T128_ST, T128_BK, MODE, SCL>(fa, fb, p, grid, s);

@@ -593,12 +593,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 template <int BM, int STAGES, int FA, int FB, int MODE, int SCL, bool KTAIL>
 __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
-    constexpr bool CHN = SCL == SCALE_CHANNEL;
+    constexpr bool CHN = SCL == SCALE_CHANNEL, BLK = SCL == SCALE_BLOCK;
     // The contiguous grouped form stays on ring_kernel: there, with every
     // expert's weights streaming from HBM, this kernel measured 4% slower
     // (1.90 against 1.82 ms on the 65536-row prefill).
-    static_assert(FA != FMT_BF16 && FB != FMT_BF16 && SCL != SCALE_BLOCK && MODE == MODE_DENSE,
-                  "FP8 operands, dense form, per-tensor or per-channel scales");
+    static_assert(FA != FMT_BF16 && FB != FMT_BF16 && MODE == MODE_DENSE, "FP8 operands, dense form");
     constexpr int BN = 256, BK = 128, WM = 2, WN = 2, WAVES = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;      // 128 (or 64) x 128 outputs per wave
     constexpr int FM = TM / 16, FN = TN / 16;      // token blocks, weight blocks
@@ -608,7 +607,11 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     constexpr int CPB = BN / DROWS / WAVES;        // B rows
     constexpr int CPW = CPA + CPB;
     constexpr int STAGE_OUT = BM * BN * 2;
-    constexpr int RING = STAGES * SLOT;
+    // Block scales (BLK): per ring slot, the step's E8M0 scale of each tile row
+    // of A (bytes 0 .. BM-1, in A's row order) and the scale dword holding the
+    // step's K block of each 128-row block of B (from byte 256).
+    constexpr int SCS = BLK ? 512 : 0;
+    constexpr int RING = STAGES * (SLOT + SCS);
     constexpr int SMEM = RING > STAGE_OUT ? RING : STAGE_OUT;
     constexpr int THREADS = 64 * WAVES;
     constexpr int OCH = BN / 8;
@@ -636,7 +639,7 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
     const uint8_t *a_base = p.A + (int64_t)m0 * p.lda;
     const uint8_t *b_base = p.B + (int64_t)n0 * p.ldb;
-    const float sc = CHN ? 1.0f : p.scale_a[0] * p.scale_b[0];
+    const float sc = (CHN || BLK) ? 1.0f : p.scale_a[0] * p.scale_b[0];
     // Rows past rows_m / rows_n fall outside the descriptors: zeros, no memory access.
     const v4i srdA = make_srd(a_base, rows_bytes(rows_m, p.lda));
     const v4i srdB = make_srd(b_base, rows_bytes(rows_n, p.ldb));
@@ -663,12 +666,18 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     const uint32_t dkc1 = (((uint32_t)lane % KCH) ^ key16(DROWS + lrow_in)) * 16u;
     const int nk = (p.K + BK - 1) / BK;
     const bool wA = wave * CPW < BM / DROWS;       // UNI: this wave copies A (wave-uniform)
+    // BLK: within each wave's TM rows, ring row 16 i + c holds tile row
+    // FM c + i, so that token block i, column c is tile row FM c + i and a
+    // lane's FM token-row scales are FM consecutive bytes (the fragment reads
+    // are unchanged; only the rows the copies fetch move).
+    auto a_row = [&](int s) { return BLK ? (s / TM) * TM + FM * (s % 16) + (s % TM) / 16 : s; };
     uint32_t lo_q[CPW];                            // UNI: this wave's copies; else A's, then B's
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
         const bool isA = UNI ? wA : i < CPA;
         const int qq = UNI ? (wave * CPW + i) % (BM / DROWS) : (isA ? wave * CPA + i : wave * CPB + (i - CPA));
-        lo_q[i] = (uint32_t)(qq * DROWS + (int)lrow_in) * (uint32_t)(isA ? p.lda : p.ldb) + ((qq & 1) ? dkc1 : dkc0);
+        const int row = qq * DROWS + (int)lrow_in;
+        lo_q[i] = (uint32_t)(isA ? a_row(row) : row) * (uint32_t)(isA ? p.lda : p.ldb) + ((qq & 1) ? dkc1 : dkc0);
     }
     const v4i srd0A = UNI ? (wA ? srdA : srdB) : srdA;
     const uint64_t baseA = ((uint64_t)(uint32_t)srd0A[1] << 32) | (uint32_t)srd0A[0];
@@ -706,6 +715,27 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
         if (UNI || i < CPA) dma16_m0(srdAk, voff, lds_a + (uint32_t)i * 1024u);
         else dma16_m0(srdBk, voff, lds_b + (uint32_t)(i - CPA) * 1024u);
     };
+    // BLK: every wave copies step kd's scales into the scale slot of its ring
+    // slot: A's BM row scales (4 per lane) and B's scale dwords (one per
+    // 128-row block, the dword holding K block kd).  The four waves write the
+    // same bytes; leaving it to one wave put a branch in the loop, across
+    // which the compiler moved the first half's MFMAs behind the barrier.
+    // Rows past the scale array (or steps past the last) read zeros; bytes of
+    // rows past M only reach outputs that are not written.
+    const int64_t sa_bytes = (int64_t)((p.K + 127) / 128) * p.lds_sa;
+    const int64_t sb_bytes = (int64_t)((p.N + 127) / 128) * p.lds_sb;
+    const v4i srdSA = BLK ? make_srd(p.sfa, (uint32_t)sa_bytes) : v4i{0, 0, 0, 0};
+    const v4i srdSB = BLK ? make_srd(p.sfb, (uint32_t)sb_bytes) : v4i{0, 0, 0, 0};
+    const uint32_t scl_base = lds0 + STAGES * SLOT;
+    constexpr int SCW = BLK ? 2 : 0;               // scale copies per wave per step
+    auto issue_scales = [&](int kd) {
+        if (!BLK) return;
+        const uint32_t slot = scl_base + (uint32_t)(kd % STAGES) * SCS;
+        const bool ka = kd < nk && 4 * lane < BM;
+        dma4(srdSA, ka ? (uint32_t)(kd * p.lds_sa + m0 + 4 * lane) : kOobOffset, slot);
+        const bool kb = kd < nk && lane < BN / 128;
+        dma4(srdSB, kb ? (uint32_t)((n0 / 128 + lane) * p.lds_sb + (kd & ~3)) : kOobOffset, slot + 256);
+    };
 
     // ---- fragments (blocks start at multiples of 16 rows, so the key of a
     // lane's row depends on l % 16 only)
@@ -728,9 +758,36 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
         for (int i = 0; i < FM; ++i) acc[j][i] = (v4f){0, 0, 0, 0};
     v8i wf[FN], tf[FM];                            // one register set per block, reused in place
 
+    // BLK: this lane's token-row scales of a step, FM bytes (rows FM c + i,
+    // c = l % 16), and the wave's weight-block scale; read one step ahead.
+    uint32_t sa_lo = 0, sa_hi = 0, nsa_lo = 0, nsa_hi = 0;
+    int scb = 0, nscb = 0;
+    auto read_scales = [&](int kt) {
+        if (!BLK) return;
+        const uint8_t *slot = smem + STAGES * SLOT + (kt % STAGES) * SCS;
+        const uint8_t *ra = slot + wm * TM + FM * r16;
+        if (FM == 8) {
+            const v2u v = *reinterpret_cast<const v2u *>(ra);
+            nsa_lo = v[0];
+            nsa_hi = v[1];
+        } else {
+            nsa_lo = *reinterpret_cast<const uint32_t *>(ra);
+        }
+        nscb = slot[256 + 4 * wn + (kt & 3)];
+    };
+    auto token_scale = [&](int i) {
+        const uint32_t w = i < 4 ? sa_lo : sa_hi;
+        return (int)((w >> (8 * (i & 3))) & 0xFFu);
+    };
+
     auto step = [&](int kt) {
         const uint8_t *cur = smem + (kt % STAGES) * SLOT;
         const uint8_t *nxt = smem + ((kt + 1) % STAGES) * SLOT;
+        if (BLK) {
+            sa_lo = nsa_lo;
+            sa_hi = nsa_hi;
+            scb = nscb;
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -740,17 +797,23 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
                     const int i = h * (FM / 2) + ii;
                     const int t = h * HALF + j * (FM / 2) + ii;
                     if (t == kBarAt) {
-                        vmcnt_wait<CPW * (STAGES - 2)>();   // this wave's copies of step kt + 1 have landed
+                        // this wave's copies of step kt + 1 have landed
+                        vmcnt_wait<(CPW + SCW) * (STAGES - 2)>();
                         __syncthreads();           // everyone's have; step kt's slot is no longer read
                     }
-                    acc[j][i] = mfma16x16x128<FB, FA>(wf[j], tf[i], acc[j][i]);
+                    if (BLK) acc[j][i] = mfma16x16x128_s<FB, FA>(wf[j], tf[i], acc[j][i], scb, token_scale(i));
+                    else acc[j][i] = mfma16x16x128<FB, FA>(wf[j], tf[i], acc[j][i]);
+                    if (BLK && t == kBarAt) read_scales(kt + 1);
                     if (h == 0) {
                         if (t % 4 == 1 && t / 4 < FM / 2) tf[FM / 2 + t / 4] = frag(cur, a_frag, FM / 2 + t / 4);
                     } else {
                         if (j < FM / 2 && ii == 1) tf[j] = frag(nxt, a_frag, j);
                         if (ii == FM / 2 - 1) wf[j] = frag(nxt, b_frag, j);
                     }
-                    if (t == kDmaFrom) set_step(kt + STAGES);
+                    if (t == kDmaFrom) {
+                        set_step(kt + STAGES);
+                        issue_scales(kt + STAGES);
+                    }
                     if (t >= kDmaFrom && t < kDmaTo) {
                         constexpr int SPAN = kDmaTo - kDmaFrom;
                         const int u = t - kDmaFrom;
@@ -768,11 +831,14 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
 #pragma unroll
     for (int st = 0; st < STAGES; ++st) {
         set_step(st);
+        issue_scales(st);
 #pragma unroll
         for (int i = 0; i < CPW; ++i) issue_one(i);
     }
-    vmcnt_wait<CPW * (STAGES - 1)>();              // this wave's part of step 0 has landed
+    // this wave's part of step 0 has landed
+    vmcnt_wait<(CPW + SCW) * (STAGES - 1)>();
     __syncthreads();
+    read_scales(0);
 #pragma unroll
     for (int j = 0; j < FN; ++j) wf[j] = frag(smem, b_frag, j);
 #pragma unroll
@@ -795,7 +861,7 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     const int el = (int)__lane_id();
     const int er16 = el & 15, ekg = el >> 4;
     auto put = [&](int i, int j, v2u v) {
-        const uint32_t m = (uint32_t)(wm * TM + i * 16 + er16);
+        const uint32_t m = (uint32_t)(wm * TM + (BLK ? FM * er16 + i : i * 16 + er16));
         const uint32_t n = (uint32_t)(wn * TN + j * 16 + ekg * 4);
         const uint32_t chunk = (n >> 3) ^ (m % OCH);
         *reinterpret_cast<v2u *>(smem + m * (BN * 2) + chunk * 16 + (n & 4) * 2) = v;

@@ -179,6 +179,18 @@ __device__ __forceinline__ v4f mfma16x16x128_s(v8i a, v8i b, v4f c, int sa, int 
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
 }
 
+// The same with the second operand's scale taken from byte `byte` (0..3) of
+// sb4 (the instruction's scale byte select), so four scales share a register.
+template <int FA, int FB>
+__device__ __forceinline__ v4f mfma16x16x128_sb(v8i a, v8i b, v4f c, int sa, int sb4, int byte) {
+    switch (byte & 3) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb4);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 1, sb4);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 2, sb4);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 3, sb4);
+    }
+}
+
 // BF16 round-to-nearest-even of four floats, packed little-endian.  Converting
 // float pairs as vectors makes the compiler emit one v_cvt_pk_bf16_f32 per
 // pair; element-wise casts give one per value plus a shift and an OR to pack.

@@ -775,10 +775,6 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
         }
         nscb = slot[256 + 4 * wn + (kt & 3)];
     };
-    auto token_scale = [&](int i) {
-        const uint32_t w = i < 4 ? sa_lo : sa_hi;
-        return (int)((w >> (8 * (i & 3))) & 0xFFu);
-    };
 
     auto step = [&](int kt) {
         const uint8_t *cur = smem + (kt % STAGES) * SLOT;
@@ -801,7 +797,8 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
                         vmcnt_wait<(CPW + SCW) * (STAGES - 2)>();
                         __syncthreads();           // everyone's have; step kt's slot is no longer read
                     }
-                    if (BLK) acc[j][i] = mfma16x16x128_s<FB, FA>(wf[j], tf[i], acc[j][i], scb, token_scale(i));
+                    if (BLK)                       // token block i's scale: byte i % 4 of its word
+                        acc[j][i] = mfma16x16x128_sb<FB, FA>(wf[j], tf[i], acc[j][i], scb, (int)(i < 4 ? sa_lo : sa_hi), i);
                     else acc[j][i] = mfma16x16x128<FB, FA>(wf[j], tf[i], acc[j][i]);
                     if (BLK && t == kBarAt) read_scales(kt + 1);
                     if (h == 0) {

@@ -49,9 +49,22 @@ def check_full(w, d, strict=False):
     (130, 136, 272, E5M2, E4M3),
     (129, 392, 144, E4M3, E5M2),
     (17, 520, 384, E4M3, E4M3),      # few rows
-    (513, 256, 128, E5M2, E5M2),     # one K block; 256x256 tiles
+    (513, 256, 128, E5M2, E5M2),     # one K block
 ])
 def test_blockscaled_matches_oracle(M, N, K, fa, fb):
+    w = workloads.dense_blockscaled(M, N, K, seed=M + N + K, a_fmt=fa, b_fmt=fb)
+    check_full(w, run_bs(w))
+
+
+@pytest.mark.parametrize("M,N,K,fa,fb", [
+    (4000, 3000, 528, E4M3, E4M3),      # M, N and K tails (K = 4 * 128 + 16)
+    (3968, 3840, 1040, E5M2, E4M3),
+])
+def test_blockscaled_256_tiles_full(M, N, K, fa, fb):
+    """The 256 x 256 tiles (the plan picks them for these shapes; their ring
+    stores each wave's token rows permuted so that a lane's row scales are
+    consecutive bytes) with partial tiles on every edge: the whole output."""
+    assert _lib().plan(3, M, N, K).variant == 1
     w = workloads.dense_blockscaled(M, N, K, seed=M + N + K, a_fmt=fa, b_fmt=fb)
     check_full(w, run_bs(w))
 
@@ -82,20 +95,24 @@ def test_uniform_scales_equal_per_tensor_entry_point():
         assert np.array_equal(d1, gpu_bits(d0)), (ea, eb)
 
 
-def test_scale_shift_is_bit_exact():
+@pytest.mark.parametrize("M,N,a_rows,b_blocks", [
+    (260, 300, [(0, 0), (131, 2), (259, 3)], [(0, 1), (2, 3)]),
+    (3968, 3840, [(0, 0), (7, 1), (136, 2), (2063, 3), (3967, 0)], [(0, 1), (29, 3)]),   # 256-row tiles
+])
+def test_scale_shift_is_bit_exact(M, N, a_rows, b_blocks):
     """Doubling the values of one (row, K block) of A and decrementing its
     scale, or the same for one (128-row block, K block) of B, leaves the GPU
     output bit-identical; the uncorrected change moves only the affected rows."""
     rng = np.random.default_rng(23)
-    M, N, K = 260, 300, 400
+    K = 400
     e = rng.integers(1, 13, size=(M, K))
     A = ((rng.integers(0, 2, size=(M, K)) << 7) | (e << 3) | rng.integers(0, 8, size=(M, K))).astype(np.uint8)
     e = rng.integers(1, 13, size=(N, K))
     B = ((rng.integers(0, 2, size=(N, K)) << 7) | (e << 3) | rng.integers(0, 8, size=(N, K))).astype(np.uint8)
     sa = rng.integers(112, 118, size=(4, M)).astype(np.uint8)
-    sb = rng.integers(112, 118, size=(3, 4)).astype(np.uint8)
+    sb = rng.integers(112, 118, size=((N + 127) // 128, 4)).astype(np.uint8)
     base = run_bs(workloads.BlockScaled(A, B, sa, sb, name="base"))
-    for (m, b) in [(0, 0), (131, 2), (259, 3)]:
+    for (m, b) in a_rows:
         A2, sa2 = A.copy(), sa.copy()
         ks = slice(128 * b, min(128 * b + 128, K))
         A2[m, ks] += 8
@@ -103,7 +120,7 @@ def test_scale_shift_is_bit_exact():
         assert np.array_equal(run_bs(workloads.BlockScaled(A2, B, sa2, sb, name="shift A")), base), (m, b)
         moved = run_bs(workloads.BlockScaled(A2, B, sa, sb, name="unshifted A"))
         assert list(np.unique(np.nonzero(moved != base)[0])) == [m]
-    for (nb, b) in [(0, 1), (2, 3)]:
+    for (nb, b) in b_blocks:
         B2, sb2 = B.copy(), sb.copy()
         rows = slice(128 * nb, min(128 * nb + 128, N))
         ks = slice(128 * b, min(128 * b + 128, K))

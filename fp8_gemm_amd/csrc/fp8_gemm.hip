@@ -205,23 +205,25 @@ int launch_status(const char *what) {
 // ---------------------------------------------------------------------------
 // Launch helpers: one instantiation per (operand formats, tile shape, mode).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int STAGES, int BK, int MODE, int SCL = 0>
+// BF16: the BF16 instantiation only (dense, no scales); otherwise the four
+// FP8 format pairs.
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, int MODE, int SCL = 0, bool BF16 = false>
 int launch_ring(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     const dim3 block(64 * WM * WN);
 #define FP8G_RING(FA, FB) \
     hipLaunchKernelGGL((fp8g::ring_kernel<BM, BN, WM, WN, FA, FB, MODE, STAGES, BK, SCL>), grid, block, 0, s, p)
-    if constexpr (MODE == fp8g::MODE_DENSE && SCL == fp8g::SCALE_TENSOR) {
-        if (fa == fp8g::FMT_BF16) {
-            FP8G_RING(fp8g::FMT_BF16, fp8g::FMT_BF16);
-            return launch_status("tiled kernel (BF16)");
-        }
+    if constexpr (BF16) {
+        static_assert(MODE == fp8g::MODE_DENSE && SCL == fp8g::SCALE_TENSOR, "BF16: dense, no scales");
+        FP8G_RING(fp8g::FMT_BF16, fp8g::FMT_BF16);
+        return launch_status("tiled kernel (BF16)");
+    } else {
+        if (fa == 0 && fb == 0) FP8G_RING(0, 0);
+        else if (fa == 0 && fb == 1) FP8G_RING(0, 1);
+        else if (fa == 1 && fb == 0) FP8G_RING(1, 0);
+        else FP8G_RING(1, 1);
+        return launch_status("tiled kernel");
     }
-    if (fa == 0 && fb == 0) FP8G_RING(0, 0);
-    else if (fa == 0 && fb == 1) FP8G_RING(0, 1);
-    else if (fa == 1 && fb == 0) FP8G_RING(1, 0);
-    else FP8G_RING(1, 1);
 #undef FP8G_RING
-    return launch_status("tiled kernel");
 }
 
 template <int BM, int STAGES, int MODE, int SCL>
@@ -243,24 +245,34 @@ int launch_tile16(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s)
     return launch_status("tiled kernel (16x16x128)");
 }
 
-// Tile shapes of the tiled kernels: 256 x 256 and 128 x 256.  Dense FP8 with
-// per-tensor or per-channel scales runs on 4 waves and the 16x16x128
-// instruction (2-slot ring, 128 KB of LDS, for 256 rows; 3-slot, 144 KB, for
-// 128 rows); block scales, BF16 and the grouped forms on 8 waves and 32x32x64
-// (4 x 2 waves and a 2-slot ring for 256 rows, 2 x 4 and 3 slots for 128).
+// Tile shapes of the tiled kernels: 256 x 256 and 128 x 256.  Dense FP8 (any
+// scale form) runs on 4 waves and the 16x16x128 instruction (2-slot ring,
+// 128 KB of LDS, for 256 rows; 3-slot, 144 KB, for 128 rows); BF16 and the
+// grouped forms on 8 waves and 32x32x64 (4 x 2 waves and a 2-slot ring for 256
+// rows, 2 x 4 and 3 slots for 128).
 template <int MODE, int SCL = 0>
 int launch_tile256(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     if constexpr (MODE == fp8g::MODE_DENSE) {
         if (fa != fp8g::FMT_BF16) return launch_tile16<256, 2, MODE, SCL>(fa, fb, p, grid, s);
+        if constexpr (SCL == fp8g::SCALE_TENSOR)
+            return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE, SCL, true>(fa, fb, p, grid, s);
+        else
+            return fail(FP8G_ERR_ARG, "BF16 operands take no scales");
+    } else {
+        return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE, SCL>(fa, fb, p, grid, s);
     }
-    return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE, SCL>(fa, fb, p, grid, s);
 }
 template <int MODE, int SCL = 0>
 int launch_tile128(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     if constexpr (MODE == fp8g::MODE_DENSE) {
         if (fa != fp8g::FMT_BF16) return launch_tile16<128, 3, MODE, SCL>(fa, fb, p, grid, s);
+        if constexpr (SCL == fp8g::SCALE_TENSOR)
+            return launch_ring<128, 256, TILE128_WM, TILE128_WN, T128_ST, T128_BK, MODE, SCL, true>(fa, fb, p, grid, s);
+        else
+            return fail(FP8G_ERR_ARG, "BF16 operands take no scales");
+    } else {
+        return launch_ring<128, 256, TILE128_WM, TILE128_WN, T128_ST, T128_BK, MODE, SCL>(fa, fb, p, grid, s);
     }
-    return launch_ring<128, 256, TILE128_WM, TILE128_WN, T128_ST, T128_BK, MODE, SCL>(fa, fb, p, grid, s);
 }
 
 template <int WR, int CB, int MODE, int SCL = 0>

@@ -10,13 +10,13 @@
 //   tile16_kernel  LDS-tiled, 256 x 256 or 128 x 256 output tile per
 //                  workgroup of 4 waves on v_mfma 16x16x128, K in steps of 128
 //                  bytes, both operand tiles staged through a direct-to-LDS,
-//                  XOR-swizzled ring.  Dense FP8 (M > 64) with per-tensor or
-//                  per-channel scales.
+//                  XOR-swizzled ring.  Dense FP8 (M > 64) with per-tensor,
+//                  per-channel or block scales.
 //   ring_kernel    the same ring with 8 waves on v_mfma 32x32x64, BM x BN
-//                  = 256 x 256 or 128 x 256: block-scaled dense, masked
-//                  grouped with many rows per group, contiguous grouped, and
-//                  the BF16 comparison path (same bytes, two v_mfma 32x32x16
-//                  BF16 per fragment).
+//                  = 256 x 256 or 128 x 256: masked grouped with many rows per
+//                  group, contiguous grouped (both also block-scaled), and the
+//                  BF16 comparison path (same bytes, two v_mfma 32x32x16 BF16
+//                  per fragment).
 //   swap_kernel    streaming "swap-AB" form for few tokens: each wave streams
 //                  its own weight rows (every weight byte is used by exactly
 //                  one wave) through a private LDS ring into the 16x16x128
@@ -274,7 +274,7 @@ __device__ __forceinline__ uint32_t ring_key(uint32_t row) {
 
 template <int BM, int BN, int WM, int WN, int FA, int FB, int MODE, int STAGES, int BK, int SCL>
 __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
-    constexpr bool BLK = SCL == SCALE_BLOCK, CHN = SCL == SCALE_CHANNEL;
+    constexpr bool BLK = SCL == SCALE_BLOCK;
     // BF16 operands: the ring moves bytes, so K, lda and ldb arrive in bytes
     // and only the instruction changes (see mfma32x32x16_bf16_part).
     constexpr bool BF = FA == FMT_BF16;
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     // Block scales (BLK): per ring slot, the step's scale of each tile row of A
     // (bytes 0..BM-1) and one dword per 128-row block of B (from byte 256).
     static_assert(!BLK || (BK == 128 && BM <= 256 && BN % 128 == 0), "block scales: 128-byte K steps");
-    static_assert(!CHN || MODE == MODE_DENSE, "per-channel scales: dense form");
+    static_assert(SCL != SCALE_CHANNEL, "per-channel scales: tile16_kernel");
     constexpr int SCS = BLK ? 512 : 0;
     constexpr int RING = STAGES * (SLOT + SCS);
     constexpr int SMEM = RING > STAGE_OUT ? RING : STAGE_OUT;
@@ -536,22 +536,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
         const uint32_t m = (uint32_t)(wm * TM + j * 32 + lrow);
-        const float sam = CHN && p.ch_sa && (int)m < rows_m ? p.ch_sa[m0 + m] : 1.0f;
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 const uint32_t n = (uint32_t)(wn * TN + i * 32 + b * 8 + khalf * 4);
                 const v16f &c = acc[i][j];
-                v2u v;
-                if (CHN) {
-                    float s4[4], b4[4];
-                    channel_terms(p, n0 + (int)n, s4, b4);
-                    v = pack_bf16x4(c[4 * b] * sam * s4[0] + b4[0], c[4 * b + 1] * sam * s4[1] + b4[1],
-                                    c[4 * b + 2] * sam * s4[2] + b4[2], c[4 * b + 3] * sam * s4[3] + b4[3]);
-                } else {
-                    v = pack_bf16x4(c[4 * b] * sc, c[4 * b + 1] * sc, c[4 * b + 2] * sc, c[4 * b + 3] * sc);
-                }
+                const v2u v = pack_bf16x4(c[4 * b] * sc, c[4 * b + 1] * sc, c[4 * b + 2] * sc, c[4 * b + 3] * sc);
                 const uint32_t chunk = (n >> 3) ^ (m % OCH);
                 *reinterpret_cast<v2u *>(smem + m * (BN * 2) + chunk * 16 + (n & 4) * 2) = v;
             }
@@ -563,7 +554,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 
 // ---------------------------------------------------------------------------
 // Four-wave tiled kernel on the 16x16x128 instruction (FP8, dense form,
-// per-tensor or per-channel scales).
+// per-tensor, per-channel or block scales).
 // BM x 256 output tile (BM = 256, or 128 where the 256-row tiles leave too
 // many CUs idle); 4 waves as 2 x 2, each owning BM/2 x 128 outputs as 8
 // weight blocks x BM/32 token blocks of 16 rows; a STAGES-slot direct-to-LDS

@@ -227,6 +227,8 @@ def test_dense_4096_config_sampled(fmt):
     (3900, 3800, 1040, E5M2, E4M3),     # K = 8 * 128 + 16
     (4000, 3000, 1024, E4M3, E5M2),     # M and N tails only
     (3968, 3840, 272, E5M2, E5M2),
+    (3968, 3840, 16, E4M3, E4M3),       # one partial K step (the ring's second slot only prefetches)
+    (4000, 3000, 144, E4M3, E5M2),      # two steps, the second partial
 ])
 def test_256_tiles_ragged_full(M, N, K, fa, fb):
     """The 256 x 256-tile kernel (the plan picks it for these shapes) with

@@ -148,9 +148,10 @@ int fp8_gemm_nt_channelwise(const void *A, int64_t lda, int a_dtype,
  *   Strides in elements: lda, ldb >= K and multiples of 8 (16 bytes), at most
  *     (2^23 - 16) / 2; ldd >= N, a multiple of 8.  K % 8 == 0.  A, B, D
  *     16-byte aligned.  K = 0 writes zeros.
- * The LDS-tiled kernel of the FP8 dense form with M > 64 (tile chosen the same
- * way, for every M): it stages the same bytes, and each 32-byte fragment feeds
- * two BF16 instructions instead of one FP8 instruction.
+ * Runs on the 8-wave LDS-tiled kernel of the grouped forms, for every M, with
+ * the tile chosen as for the FP8 dense form: it stages the same bytes, and
+ * each 32-byte fragment feeds two BF16 instructions instead of one FP8
+ * instruction.
  */
 int bf16_gemm_nt(const void *A, int64_t lda, const void *B, int64_t ldb,
                  void *D, int64_t ldd, int M, int N, int K, void *stream);
@@ -248,7 +249,9 @@ int fp8_grouped_gemm_contig_blockscaled(const void *A, int a_dtype, const void *
  * pointers excepted).
  */
 typedef struct {
-    int variant;        /* 1 = tiled 256x256, 2 = tiled 128x256 (m x n),
+    int variant;        /* 1 = tiled 256x256, 2 = tiled 128x256 (m x n; FP8
+                           dense forms on 4 waves and 16x16x128, grouped and
+                           BF16 forms on 8 waves and 32x32x64),
                            3 = swapped streaming (grouped forms),
                            4 = swapped decode, K split over 4 waves (dense
                            forms, m <= 64), 0 = nothing to launch */

@@ -381,9 +381,46 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
         dma4(srdSB, kb ? (uint32_t)((n0 / 128 + lane) * p.lds_sb + (kt & ~3)) : kOobOffset, slot + 256);
     };
     constexpr int SCW = BLK ? 2 : 0;               // scale DMA instructions per step of wave 0
-    auto issue = [&](int kt) {
+    // 256-row tiles (UNI): each wave copies one operand's rows, so, as in
+    // tile16_kernel, a lane's offset within the tile is fixed per copy and
+    // kept in a register, each step only moves the descriptor's base (and
+    // shrinks its byte count) and M0 goes to the compiler as an operand.  The
+    // lanes whose K chunk starts at or past K add kOobOffset (every lane,
+    // past the last step, where the byte count is also 0).
+    constexpr bool UNI = BK == 128 && (BM / DROWS) % CPW == 0;
+    const bool wA = wave * CPW < BM / DROWS;       // wave-uniform
+    uint32_t lo_q[CPW];
+    if (UNI) {
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) issue_one(kt, i);
+        for (int i = 0; i < CPW; ++i) {
+            const int qq = (wave * CPW + i) % (BM / DROWS);
+            lo_q[i] = (uint32_t)(qq * DROWS + (int)lrow_in) * (uint32_t)(wA ? p.lda : p.ldb) + ((qq & 1) ? dkc1 : dkc0);
+        }
+    }
+    const v4i srd0 = wA ? srdA : srdB;
+    const uint64_t base0 = ((uint64_t)(uint32_t)srd0[1] << 32) | (uint32_t)srd0[0];
+    v4i srdk = srd0;
+    uint32_t lds_slot = 0, ko0 = 0, ko1 = 0;
+    auto set_step = [&](int kd) {
+        const uint64_t b = base0 + (uint64_t)kd * BK;
+        srdk[0] = (int)(uint32_t)b;
+        srdk[1] = (int)(uint32_t)(b >> 32);
+        srdk[2] = kd < nk ? srd0[2] - kd * BK : 0;
+        lds_slot = lds0 + (uint32_t)(kd % STAGES) * SLOT + (uint32_t)(wave * CPW) * 1024u;
+        const int lim = p.K - kd * BK;
+        ko0 = (int)dkc0 < lim ? 0u : kOobOffset;
+        ko1 = (int)dkc1 < lim ? 0u : kOobOffset;
+    };
+    auto issue_fast = [&](int i) {   // CPW is even, so copy i's key parity is that of i
+        dma16_m0(srdk, lo_q[i] + ((i & 1) ? ko1 : ko0), lds_slot + (uint32_t)i * 1024u);
+    };
+    auto issue = [&](int kt) {
+        if (UNI) set_step(kt);
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            if (UNI) issue_fast(i);
+            else issue_one(kt, i);
+        }
         issue_scales(kt);
     };
 
@@ -476,9 +513,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 #pragma unroll
             for (int q = (t * NFR) / NMF; q < ((t + 1) * NFR) / NMF; ++q) read_frag(nb, na, read_slot, read_h, q);
             if (refill_kt >= 0) {
-                if (t == 0) issue_scales(refill_kt);
+                if (t == 0) {
+                    issue_scales(refill_kt);
+                    if (UNI) set_step(refill_kt);
+                }
 #pragma unroll
-                for (int q = (t * CPW) / NMF; q < ((t + 1) * CPW) / NMF; ++q) issue_one(refill_kt, q);
+                for (int q = (t * CPW) / NMF; q < ((t + 1) * CPW) / NMF; ++q) {
+                    if (UNI) issue_fast(q);
+                    else issue_one(refill_kt, q);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -511,7 +554,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
         }
         // Redefined each step so that the compiler forms the DMA offsets in
         // the loop instead of keeping one register per instruction live.
-        asm volatile("" : "+v"(doA0), "+v"(doA1), "+v"(doB0), "+v"(doB1), "+v"(dkc0), "+v"(dkc1));
+        if (!UNI) asm volatile("" : "+v"(doA0), "+v"(doA1), "+v"(doB0), "+v"(doB1), "+v"(dkc0), "+v"(dkc1));
         const uint8_t *cur = smem + (kt % STAGES) * SLOT;
         const uint8_t *nxt = smem + ((kt + 1) % STAGES) * SLOT;
         __builtin_amdgcn_sched_barrier(0);

@@ -66,7 +66,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---------------------------------------------------------------------------
 // Shape-class choice.
 // ---------------------------------------------------------------------------
-enum Variant { V_NONE = 0, V_TILE_256x256 = 1, V_TILE_128x256 = 2, V_SWAP = 3, V_DECODE = 4 };
+enum Variant { V_NONE = 0, V_TILE_256x256 = 1, V_TILE_128x256 = 2, V_SWAP = 3, V_DECODE = 4, V_TILE_256x192 = 5 };
 
 // Decode kernel: 16 weight rows per workgroup, or 32 where that still gives
 // at least 256 workgroups.  Every workgroup reads all M x K token bytes, so
@@ -88,14 +88,23 @@ int token_blocks_for(int m) {
 
 // Dense tiled kernel: pick the tile whose waves of 256 workgroups (one per CU)
 // give the smallest estimated time.  A 128x256 tile does half the work of a
-// 256x256 tile at a somewhat lower efficiency (more operand traffic per FLOP).
-int pick_dense_tile(int64_t M, int64_t N) {
+// 256x256 tile at a somewhat lower efficiency (more operand traffic per FLOP);
+// a 256x192 tile (per-tensor and per-channel FP8 only) does three quarters of
+// it, and wins where whole waves of it replace a partial wave of 256x256
+// tiles (2048 x 12288: 512 tiles, two full waves, against 384).
+int pick_dense_tile(int64_t M, int64_t N, bool allow192) {
     const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
     const int64_t t128 = cdiv(M, 128) * cdiv(N, 256);
+    const int64_t t192 = cdiv(M, 256) * cdiv(N, 192);
     const double c256 = (double)cdiv(t256, 256) * 2.0;
     const double c128 = (double)cdiv(t128, 256) * 1.15;
-    return c256 <= c128 ? V_TILE_256x256 : V_TILE_128x256;
+    const double c192 = allow192 ? (double)cdiv(t192, 256) * 1.65 : 1e30;
+    if (c256 <= c128 && c256 <= c192) return V_TILE_256x256;
+    return c192 < c128 ? V_TILE_256x192 : V_TILE_128x256;
 }
+
+int tile_m_of(int variant) { return variant == V_TILE_128x256 ? 128 : 256; }
+int tile_n_of(int variant) { return variant == V_TILE_256x192 ? 192 : 256; }
 
 int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan *out) {
     memset(out, 0, sizeof *out);
@@ -113,10 +122,10 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
             out->token_blocks = token_blocks_for(m);
             out->workgroups = cdiv(n, out->tile_n);
         } else {
-            out->variant = pick_dense_tile(m, n);
-            out->tile_m = out->variant == V_TILE_256x256 ? 256 : 128;
-            out->tile_n = 256;
-            out->workgroups = cdiv(m, out->tile_m) * cdiv(n, 256);
+            out->variant = pick_dense_tile(m, n, true);
+            out->tile_m = tile_m_of(out->variant);
+            out->tile_n = tile_n_of(out->variant);
+            out->workgroups = cdiv(m, out->tile_m) * cdiv(n, out->tile_n);
         }
         return ok();
     }
@@ -162,8 +171,8 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
             out->workgroups = cdiv(n, out->tile_n);
             return ok();
         }
-        out->variant = pick_dense_tile(m, n);
-        out->tile_m = out->variant == V_TILE_256x256 ? 256 : 128;
+        out->variant = pick_dense_tile(m, n, false);
+        out->tile_m = tile_m_of(out->variant);
         out->tile_n = 256;
         out->workgroups = cdiv(m, out->tile_m) * cdiv(n, 256);
         return ok();
@@ -171,8 +180,8 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
     if (op == 4) {
         // BF16 comparison path: always the tiled kernel.
         if (m == 0 || n == 0) return ok();
-        out->variant = pick_dense_tile(m, n);
-        out->tile_m = out->variant == V_TILE_256x256 ? 256 : 128;
+        out->variant = pick_dense_tile(m, n, false);
+        out->tile_m = tile_m_of(out->variant);
         out->tile_n = 256;
         out->workgroups = cdiv(m, out->tile_m) * cdiv(n, 256);
         return ok();
@@ -226,16 +235,16 @@ int launch_ring(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
 #undef FP8G_RING
 }
 
-template <int BM, int STAGES, int MODE, int SCL>
+template <int BM, int STAGES, int MODE, int SCL, int BN = 256>
 int launch_tile16(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     const dim3 block(256);
     // K not a multiple of 128: the variant with the per-lane check of the last step
 #define FP8G_T16(FA, FB)                                                                                     \
     do {                                                                                                      \
         if (p.K % 128)                                                                                        \
-            hipLaunchKernelGGL((fp8g::tile16_kernel<BM, STAGES, FA, FB, MODE, SCL, true>), grid, block, 0, s, p); \
+            hipLaunchKernelGGL((fp8g::tile16_kernel<BM, BN, STAGES, FA, FB, MODE, SCL, true>), grid, block, 0, s, p); \
         else                                                                                                  \
-            hipLaunchKernelGGL((fp8g::tile16_kernel<BM, STAGES, FA, FB, MODE, SCL, false>), grid, block, 0, s, p); \
+            hipLaunchKernelGGL((fp8g::tile16_kernel<BM, BN, STAGES, FA, FB, MODE, SCL, false>), grid, block, 0, s, p); \
     } while (0)
     if (fa == 0 && fb == 0) FP8G_T16(0, 0);
     else if (fa == 0 && fb == 1) FP8G_T16(0, 1);
@@ -261,6 +270,12 @@ int launch_tile256(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s
     } else {
         return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE, SCL>(fa, fb, p, grid, s);
     }
+}
+// 256 x 192 tiles: dense FP8 with per-tensor or per-channel scales.
+template <int SCL>
+int launch_tile256x192(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    static_assert(SCL != fp8g::SCALE_BLOCK, "block scales: 256-column tiles");
+    return launch_tile16<256, 2, fp8g::MODE_DENSE, SCL, 192>(fa, fb, p, grid, s);
 }
 template <int MODE, int SCL = 0>
 int launch_tile128(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
@@ -402,6 +417,7 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t 
     p.tiles_n = (int)cdiv(N, plan.tile_n);
     const dim3 grid((unsigned)plan.workgroups);
     if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE>(fa, fb, p, grid, s);
+    if (plan.variant == V_TILE_256x192) return launch_tile256x192<fp8g::SCALE_TENSOR>(fa, fb, p, grid, s);
     return launch_tile128<fp8g::MODE_DENSE>(fa, fb, p, grid, s);
 }
 
@@ -626,6 +642,7 @@ int fp8_gemm_nt_channelwise(const void *A, int64_t lda, int a_dtype, const void 
     p.tiles_m = (int)cdiv(M, plan.tile_m);
     p.tiles_n = (int)cdiv(N, plan.tile_n);
     if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE, fp8g::SCALE_CHANNEL>(fa, fb, p, grid, s);
+    if (plan.variant == V_TILE_256x192) return launch_tile256x192<fp8g::SCALE_CHANNEL>(fa, fb, p, grid, s);
     return launch_tile128<fp8g::MODE_DENSE, fp8g::SCALE_CHANNEL>(fa, fb, p, grid, s);
 }
 

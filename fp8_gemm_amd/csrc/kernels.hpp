@@ -218,8 +218,17 @@ __device__ __forceinline__ bool place_tile(const GemmParams &p, int lane, TileSp
     return true;
 }
 
+// Stored position of 16-byte chunk c of staged output row r (OCH chunks per
+// row): c ^ (r % OCH) when OCH is a power of two, else (c + r) % OCH.  Either
+// way a row keeps its chunks, and the rows one staging write touches land on
+// different chunk positions.
+template <int OCH>
+__device__ __forceinline__ uint32_t stage_chunk(uint32_t c, uint32_t r) {
+    return (OCH & (OCH - 1)) == 0 ? (c ^ (r % OCH)) : (c + r) % OCH;
+}
+
 // Write a BF16 output tile staged in LDS (row r at r * BN * 2 bytes, 16-byte
-// chunk c stored at c ^ (r % (BN / 8))) with 16-byte stores of whole row
+// chunk c stored at stage_chunk(c, r)) with 16-byte stores of whole row
 // segments; the contiguous form writes only the rows of the tile's expert.
 template <int BM, int BN, int THREADS, int MODE>
 __device__ __forceinline__ void store_staged(const GemmParams &p, const uint8_t *smem, int tid, const TileSpot &t,
@@ -235,7 +244,7 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const uint8_t 
         const int m = t.m0 + r;
         if (MODE == MODE_CONTIG && p.grp_idx[m] != t.expert) continue;
         const int n = t.n0 + c * 8;
-        const v4u v = *reinterpret_cast<const v4u *>(smem + r * (BN * 2) + ((c ^ (r % OCH)) * 16));
+        const v4u v = *reinterpret_cast<const v4u *>(smem + r * (BN * 2) + stage_chunk<OCH>(c, r) * 16);
         uint16_t *dst = d_base + (int64_t)m * p.ldd + n;
         const int nvalid = p.N - n;
         if (nvalid >= 8) {
@@ -625,14 +634,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 //   - second half: each register set takes step kt + 1's fragment as soon as
 //     its last use in step kt has issued.
 // ---------------------------------------------------------------------------
-template <int BM, int STAGES, int FA, int FB, int MODE, int SCL, bool KTAIL>
+template <int BM, int BN, int STAGES, int FA, int FB, int MODE, int SCL, bool KTAIL>
 __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     constexpr bool CHN = SCL == SCALE_CHANNEL, BLK = SCL == SCALE_BLOCK;
     // The contiguous grouped form stays on ring_kernel: there, with every
     // expert's weights streaming from HBM, this kernel measured 4% slower
     // (1.90 against 1.82 ms on the 65536-row prefill).
     static_assert(FA != FMT_BF16 && FB != FMT_BF16 && MODE == MODE_DENSE, "FP8 operands, dense form");
-    constexpr int BN = 256, BK = 128, WM = 2, WN = 2, WAVES = WM * WN;
+    constexpr int BK = 128, WM = 2, WN = 2, WAVES = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;      // 128 (or 64) x 128 outputs per wave
     constexpr int FM = TM / 16, FN = TN / 16;      // token blocks, weight blocks
     constexpr int KCH = BK / 16, DROWS = 1024 / BK;
@@ -651,8 +660,12 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     constexpr int OCH = BN / 8;
     constexpr int HALF = FN * FM / 2;              // MFMAs per half step
     // the step's one barrier, and the MFMAs that carry the copies
-    constexpr int kBarAt = BM == 256 ? 20 : 10, kDmaFrom = kBarAt, kDmaTo = BM == 256 ? 48 : 28;
-    static_assert((BM == 256 || BM == 128) && FN == 8 && CPA % 2 == 0 && CPB % 2 == 0 && CPW % 2 == 0, "shape");
+    constexpr int kBarAt = BM == 128 ? 10 : (BN == 256 ? 20 : 16), kDmaFrom = kBarAt,
+                  kDmaTo = BM == 128 ? 28 : (BN == 256 ? 48 : 44);
+    static_assert(((BM == 256 && (BN == 256 || BN == 192)) || (BM == 128 && BN == 256)) && FN >= FM / 2 &&
+                      CPA % 2 == 0 && CPB % 2 == 0 && CPW % 2 == 0, "shape");
+    // block scales: each wave's weight rows must lie in one 128-row scale block
+    static_assert(!BLK || BN == 256, "block scales: 256-column tiles");
     static_assert(STAGES >= 2 && RING <= 160 * 1024, "ring");
     static_assert(kBarAt >= 4 * (FM / 2 - 1) + 2 && kBarAt <= HALF && kDmaFrom >= kBarAt && kDmaTo <= 2 * HALF &&
                       kDmaTo - kDmaFrom >= CPW,
@@ -894,7 +907,7 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     auto put = [&](int i, int j, v2u v) {
         const uint32_t m = (uint32_t)(wm * TM + (BLK ? FM * er16 + i : i * 16 + er16));
         const uint32_t n = (uint32_t)(wn * TN + j * 16 + ekg * 4);
-        const uint32_t chunk = (n >> 3) ^ (m % OCH);
+        const uint32_t chunk = stage_chunk<OCH>(n >> 3, m);
         *reinterpret_cast<v2u *>(smem + m * (BN * 2) + chunk * 16 + (n & 4) * 2) = v;
     };
     // The loop orders below are the ones that keep the compiler's copies of

@@ -46,8 +46,9 @@ def run(w, sa, sb, bias):
     (20, 8204, 512, E4M3, E4M3, "abc"),     # decode kernel with 32-row workgroups, N tail of 12
     (300, 264, 400, E4M3, E5M2, "abc"),     # 128x256 tiles
     (513, 300, 256, E4M3, E4M3, "c"),       # 128x256 tiles, bias only
-    (4000, 3000, 528, E4M3, E4M3, "abc"),   # 256x256 tiles, every edge partial, K tail
+    (4000, 3800, 528, E4M3, E4M3, "abc"),   # 256x256 tiles, every edge partial, K tail
     (3968, 3840, 1024, E5M2, E4M3, "b"),    # 256x256 tiles, channel scales only
+    (2000, 12000, 528, E4M3, E4M3, "abc"),  # 256x192 tiles, every edge partial, K tail
     (129, 136, 128, E5M2, E5M2, "ab"),
 ])
 def test_channelwise_matches_oracle(M, N, K, fa, fb, which):

@@ -223,12 +223,12 @@ def test_dense_4096_config_sampled(fmt):
 
 
 @pytest.mark.parametrize("M,N,K,fa,fb", [
-    (4000, 3000, 528, E4M3, E4M3),      # M, N and K tails (K = 4 * 128 + 16)
+    (4000, 3800, 528, E4M3, E4M3),      # M, N and K tails (K = 4 * 128 + 16)
     (3900, 3800, 1040, E5M2, E4M3),     # K = 8 * 128 + 16
-    (4000, 3000, 1024, E4M3, E5M2),     # M and N tails only
+    (4000, 3800, 1024, E4M3, E5M2),     # M and N tails only
     (3968, 3840, 272, E5M2, E5M2),
     (3968, 3840, 16, E4M3, E4M3),       # one partial K step (the ring's second slot only prefetches)
-    (4000, 3000, 144, E4M3, E5M2),      # two steps, the second partial
+    (4000, 3800, 144, E4M3, E5M2),      # two steps, the second partial
 ])
 def test_256_tiles_ragged_full(M, N, K, fa, fb):
     """The 256 x 256-tile kernel (the plan picks it for these shapes) with
@@ -237,6 +237,18 @@ def test_256_tiles_ragged_full(M, N, K, fa, fb):
     assert _lib().plan(0, M, N, K).variant == 1
     w = workloads.dense_random(M, N, K, seed=M + N + K, a_fmt=fa, b_fmt=fb, std=1.0, scales=(0.5, 1.5))
     _check_dense(w, f"256-tile {M}x{N}x{K} fmt ({fa},{fb})")
+
+
+@pytest.mark.parametrize("M,N,K,fa,fb", [
+    (2000, 12000, 1040, E4M3, E4M3),    # 256 x 192 tiles: partial tiles on both edges, K tail
+    (1900, 11600, 528, E5M2, E4M3),
+])
+def test_256x192_tiles_full(M, N, K, fa, fb):
+    """The 256 x 192 tiles (picked where whole waves of them replace a partial
+    wave of 256 x 256 tiles): the whole output against the oracle."""
+    assert _lib().plan(0, M, N, K).variant == 5
+    w = workloads.dense_random(M, N, K, seed=M + N + K, a_fmt=fa, b_fmt=fb, std=1.0, scales=(0.5, 1.5))
+    _check_dense(w, f"256x192-tile {M}x{N}x{K} fmt ({fa},{fb})")
 
 
 @pytest.mark.parametrize("M,N,K", [(6144, 6144, 1280), (4096, 4096, 1024)])

@@ -55,6 +55,9 @@ def test_abi_version(f):
     ((0, 64, 4096, 7168), 4),            # M <= 64: swap-AB decode kernel
     ((0, 65, 4096, 7168), 2),
     ((0, 1, 16, 16), 4),
+    ((0, 2048, 12288, 4096), 5),         # 512 tiles of 256x192 (2 waves) against 384 of 256x256
+    ((3, 2048, 12288, 4096), 2),         # block scales: no 256x192 tiles
+    ((4, 2048, 12288, 4096), 2),         # BF16: no 256x192 tiles
 ])
 def test_dense_plan(f, args, variant):
     p = f.plan(*args)
@@ -64,6 +67,8 @@ def test_dense_plan(f, args, variant):
 def test_dense_plan_grid(f):
     p = f.plan(0, 4096, 4096, 4096)
     assert (p.tile_m, p.tile_n, p.workgroups) == (256, 256, 256)
+    p = f.plan(0, 2000, 12000, 1040)
+    assert (p.variant, p.tile_m, p.tile_n, p.workgroups) == (5, 256, 192, 8 * 63)
     p = f.plan(0, 17, 4096, 7168)                  # decode kernel: 16 weight rows per workgroup
     assert p.token_blocks == 2 and p.tile_n == 16 and p.workgroups == 4096 // 16
     # 32 rows per workgroup once that still gives >= 256 workgroups

@@ -394,7 +394,7 @@ def bench_copy(torch, steps, warmup, timer, nbytes=1 << 30):
 
 # Kernel-name patterns of the launches each counter summary covers.
 COUNTER_TARGETS = {
-    "dense_4096_e4m3": ("tile16_kernel<256, 2, 0, 0, 0, 0,", "dense 4096^3 E4M3 GEMM"),
+    "dense_4096_e4m3": ("tile16_kernel<256, 256, 2, 0, 0, 0, 0,", "dense 4096^3 E4M3 GEMM"),
     "masked_decode": ("swap_kernel<", "masked grouped decode GEMM G=32 cap=64 N=4096 K=7168 m_g~U{0..32}"),
 }
 COPY_PATTERN = "neg_kernel"

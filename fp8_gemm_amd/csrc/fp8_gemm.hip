@@ -66,7 +66,9 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---------------------------------------------------------------------------
 // Shape-class choice.
 // ---------------------------------------------------------------------------
-enum Variant { V_NONE = 0, V_TILE_256x256 = 1, V_TILE_128x256 = 2, V_SWAP = 3, V_DECODE = 4, V_TILE_256x192 = 5 };
+enum Variant {
+    V_NONE = 0, V_TILE_256x256 = 1, V_TILE_128x256 = 2, V_SWAP = 3, V_DECODE = 4, V_TILE_256x192 = 5, V_TILE_256x224 = 6
+};
 
 // Decode kernel: 16 weight rows per workgroup, or 32 where that still gives
 // at least 256 workgroups.  Every workgroup reads all M x K token bytes, so
@@ -89,22 +91,29 @@ int token_blocks_for(int m) {
 // Dense tiled kernel: pick the tile whose waves of 256 workgroups (one per CU)
 // give the smallest estimated time.  A 128x256 tile does half the work of a
 // 256x256 tile at a somewhat lower efficiency (more operand traffic per FLOP);
-// a 256x192 tile (per-tensor and per-channel FP8 only) does three quarters of
-// it, and wins where whole waves of it replace a partial wave of 256x256
-// tiles (2048 x 12288: 512 tiles, two full waves, against 384).
-int pick_dense_tile(int64_t M, int64_t N, bool allow192) {
+// 256x224 and 256x192 tiles (per-tensor and per-channel FP8 only) do seven
+// eighths and three quarters of it, and win where whole waves of them replace
+// a partial wave of 256x256 tiles (2048 x 14336: 512 tiles of 256x224, two
+// full waves, against 448; 2048 x 12288: 512 of 256x192 against 384).
+int pick_dense_tile(int64_t M, int64_t N, bool allow_narrow) {
     const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
     const int64_t t128 = cdiv(M, 128) * cdiv(N, 256);
+    const int64_t t224 = cdiv(M, 256) * cdiv(N, 224);
     const int64_t t192 = cdiv(M, 256) * cdiv(N, 192);
     const double c256 = (double)cdiv(t256, 256) * 2.0;
     const double c128 = (double)cdiv(t128, 256) * 1.15;
-    const double c192 = allow192 ? (double)cdiv(t192, 256) * 1.65 : 1e30;
-    if (c256 <= c128 && c256 <= c192) return V_TILE_256x256;
-    return c192 < c128 ? V_TILE_256x192 : V_TILE_128x256;
+    const double c224 = allow_narrow ? (double)cdiv(t224, 256) * 1.85 : 1e30;
+    const double c192 = allow_narrow ? (double)cdiv(t192, 256) * 1.65 : 1e30;
+    int best = V_TILE_256x256;
+    double cost = c256;
+    if (c224 < cost) best = V_TILE_256x224, cost = c224;
+    if (c192 < cost) best = V_TILE_256x192, cost = c192;
+    if (c128 < cost) best = V_TILE_128x256, cost = c128;
+    return best;
 }
 
 int tile_m_of(int variant) { return variant == V_TILE_128x256 ? 128 : 256; }
-int tile_n_of(int variant) { return variant == V_TILE_256x192 ? 192 : 256; }
+int tile_n_of(int variant) { return variant == V_TILE_256x192 ? 192 : variant == V_TILE_256x224 ? 224 : 256; }
 
 int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan *out) {
     memset(out, 0, sizeof *out);
@@ -271,10 +280,11 @@ int launch_tile256(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s
         return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE, SCL>(fa, fb, p, grid, s);
     }
 }
-// 256 x 192 tiles: dense FP8 with per-tensor or per-channel scales.
+// 256 x 224 and 256 x 192 tiles: dense FP8 with per-tensor or per-channel scales.
 template <int SCL>
-int launch_tile256x192(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+int launch_tile256_narrow(int variant, int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     static_assert(SCL != fp8g::SCALE_BLOCK, "block scales: 256-column tiles");
+    if (variant == V_TILE_256x224) return launch_tile16<256, 2, fp8g::MODE_DENSE, SCL, 224>(fa, fb, p, grid, s);
     return launch_tile16<256, 2, fp8g::MODE_DENSE, SCL, 192>(fa, fb, p, grid, s);
 }
 template <int MODE, int SCL = 0>
@@ -417,7 +427,8 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t 
     p.tiles_n = (int)cdiv(N, plan.tile_n);
     const dim3 grid((unsigned)plan.workgroups);
     if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE>(fa, fb, p, grid, s);
-    if (plan.variant == V_TILE_256x192) return launch_tile256x192<fp8g::SCALE_TENSOR>(fa, fb, p, grid, s);
+    if (plan.variant == V_TILE_256x192 || plan.variant == V_TILE_256x224)
+        return launch_tile256_narrow<fp8g::SCALE_TENSOR>(plan.variant, fa, fb, p, grid, s);
     return launch_tile128<fp8g::MODE_DENSE>(fa, fb, p, grid, s);
 }
 
@@ -642,7 +653,8 @@ int fp8_gemm_nt_channelwise(const void *A, int64_t lda, int a_dtype, const void 
     p.tiles_m = (int)cdiv(M, plan.tile_m);
     p.tiles_n = (int)cdiv(N, plan.tile_n);
     if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE, fp8g::SCALE_CHANNEL>(fa, fb, p, grid, s);
-    if (plan.variant == V_TILE_256x192) return launch_tile256x192<fp8g::SCALE_CHANNEL>(fa, fb, p, grid, s);
+    if (plan.variant == V_TILE_256x192 || plan.variant == V_TILE_256x224)
+        return launch_tile256_narrow<fp8g::SCALE_CHANNEL>(plan.variant, fa, fb, p, grid, s);
     return launch_tile128<fp8g::MODE_DENSE, fp8g::SCALE_CHANNEL>(fa, fb, p, grid, s);
 }
 

@@ -7,8 +7,8 @@
 // consecutive output columns n of one output row m, so the epilogue writes
 // 8-byte packed BF16 runs straight from registers.
 //
-//   tile16_kernel  LDS-tiled, 256 x 256 or 128 x 256 output tile per
-//                  workgroup of 4 waves on v_mfma 16x16x128, K in steps of 128
+//   tile16_kernel  LDS-tiled, 256 x 256, 128 x 256, 256 x 224 or 256 x 192
+//                  output tile per workgroup of 4 waves on v_mfma 16x16x128, K in steps of 128
 //                  bytes, both operand tiles staged through a direct-to-LDS,
 //                  XOR-swizzled ring.  Dense FP8 (M > 64) with per-tensor,
 //                  per-channel or block scales.
@@ -607,11 +607,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 // Four-wave tiled kernel on the 16x16x128 instruction (FP8, dense form,
 // per-tensor, per-channel or block scales).
-// BM x 256 output tile (BM = 256, or 128 where the 256-row tiles leave too
-// many CUs idle); 4 waves as 2 x 2, each owning BM/2 x 128 outputs as 8
-// weight blocks x BM/32 token blocks of 16 rows; a STAGES-slot direct-to-LDS
-// ring of 128-byte K steps (2 slots of 64 KB for BM = 256, 3 of 48 KB for
-// BM = 128).  Against ring_kernel's 8 waves of 64 x 128 on 32x32x64 the
+// BM x BN output tile: 256 x 256; 128 x 256 where the 256-row tiles leave
+// too many CUs idle; 256 x 224 or 256 x 192 where whole waves of those
+// replace a partial wave of 256 x 256 tiles.  4 waves as 2 x 2, each owning
+// BM/2 x BN/2 outputs as BN/32 weight blocks x BM/32 token blocks of 16 rows;
+// a STAGES-slot direct-to-LDS ring of 128-byte K steps (2 slots of
+// (256 + BN) x 128 bytes for BM = 256, 3 of 48 KB for BM = 128).  Against ring_kernel's 8 waves of 64 x 128 on 32x32x64 the
 // 256-row form reads a third fewer LDS bytes per FLOP, and the
 // 16x16x128 form draws less power per FLOP, so the chip, power-limited under
 // this load, holds a higher clock.  One instruction spans the whole 128-byte
@@ -623,7 +624,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 // the lanes the LDS serves together in a fragment read hit distinct banks;
 // ring_key, made for 32-row reads, leaves 2-way conflicts here (measured).
 //
-// Per K step kt, 8 x BM/32 MFMAs per wave in two halves (the first and the
+// Per K step kt, BN/32 x BM/32 MFMAs per wave in two halves (the first and the
 // second half of the token blocks), each weight-block major:
 //   - first half: the second half's token blocks of step kt are read in
 //     between (their registers were freed by the last MFMAs of step kt - 1);
@@ -660,10 +661,10 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     constexpr int OCH = BN / 8;
     constexpr int HALF = FN * FM / 2;              // MFMAs per half step
     // the step's one barrier, and the MFMAs that carry the copies
-    constexpr int kBarAt = BM == 128 ? 10 : (BN == 256 ? 20 : 16), kDmaFrom = kBarAt,
-                  kDmaTo = BM == 128 ? 28 : (BN == 256 ? 48 : 44);
-    static_assert(((BM == 256 && (BN == 256 || BN == 192)) || (BM == 128 && BN == 256)) && FN >= FM / 2 &&
-                      CPA % 2 == 0 && CPB % 2 == 0 && CPW % 2 == 0, "shape");
+    constexpr int kBarAt = BM == 128 ? 10 : (BN == 256 ? 20 : BN == 224 ? 18 : 16), kDmaFrom = kBarAt,
+                  kDmaTo = BM == 128 ? 28 : (BN == 256 ? 48 : BN == 224 ? 46 : 44);
+    static_assert(((BM == 256 && (BN == 256 || BN == 224 || BN == 192)) || (BM == 128 && BN == 256)) &&
+                      FN >= FM / 2 && CPA % 2 == 0, "shape");
     // block scales: each wave's weight rows must lie in one 128-row scale block
     static_assert(!BLK || BN == 256, "block scales: 256-column tiles");
     static_assert(STAGES >= 2 && RING <= 160 * 1024, "ring");
@@ -735,9 +736,14 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     uint32_t lds_a = 0, lds_b = 0;
     // K tail (K not a multiple of 128): on the last step, lanes whose chunk
     // starts at or past K add kOobOffset (their offset, below 2^31 before,
-    // then lies in [2^31, 2^32): past every descriptor).  CPW, CPA and CPB are
-    // even, so the key parity of copy i is that of i.
-    uint32_t ko0 = 0, ko1 = 0;
+    // then lies in [2^31, 2^32): past every descriptor).  The lane's chunk
+    // depends on the key parity of its copy's row group qq.  CPA is even, and
+    // so is CPW where UNI holds, so for A's copies (and all of UNI's) that is
+    // the parity of i; B's copy i is qq = wave CPB + i - CPA, whose parity
+    // for odd CPB (224-column tiles) also flips with the wave's.
+    constexpr bool FLIPB = !UNI && (CPB & 1);
+    const bool flipb = FLIPB && (wave & 1);
+    uint32_t ko0 = 0, ko1 = 0, kob0 = 0, kob1 = 0;
     auto set_step = [&](int kd) {                  // the copies of step kd follow
         const uint64_t ba = baseA + (uint64_t)kd * BK;
         srdAk[0] = (int)(uint32_t)ba;
@@ -755,10 +761,13 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
             const int lim = p.K - kd * BK;
             ko0 = (int)dkc0 < lim ? 0u : kOobOffset;
             ko1 = (int)dkc1 < lim ? 0u : kOobOffset;
+            kob0 = flipb ? ko1 : ko0;
+            kob1 = flipb ? ko0 : ko1;
         }
     };
     auto issue_one = [&](int i) {
-        const uint32_t voff = KTAIL ? lo_q[i] + ((i & 1) ? ko1 : ko0) : lo_q[i];
+        const bool inB = FLIPB && i >= CPA;
+        const uint32_t voff = KTAIL ? lo_q[i] + ((i & 1) ? (inB ? kob1 : ko1) : (inB ? kob0 : ko0)) : lo_q[i];
         if (UNI || i < CPA) dma16_m0(srdAk, voff, lds_a + (uint32_t)i * 1024u);
         else dma16_m0(srdBk, voff, lds_b + (uint32_t)(i - CPA) * 1024u);
     };

@@ -254,9 +254,9 @@ typedef struct {
                            BF16 forms on 8 waves and 32x32x64),
                            3 = swapped streaming (grouped forms),
                            4 = swapped decode, K split over 4 waves (dense
-                           forms, m <= 64), 5 = tiled 256x192 (FP8 dense,
-                           per-tensor or per-channel scales), 0 = nothing to
-                           launch */
+                           forms, m <= 64), 5 = tiled 256x192 and
+                           6 = tiled 256x224 (both FP8 dense, per-tensor or
+                           per-channel scales), 0 = nothing to launch */
     int tile_m;         /* rows of D per workgroup tile (tokens) */
     int tile_n;         /* columns of D per workgroup tile (weight rows: 256
                            or 512 for variant 3, 16 or 32 for variant 4) */

@@ -49,6 +49,7 @@ def run(w, sa, sb, bias):
     (4000, 3800, 528, E4M3, E4M3, "abc"),   # 256x256 tiles, every edge partial, K tail
     (3968, 3840, 1024, E5M2, E4M3, "b"),    # 256x256 tiles, channel scales only
     (2000, 12000, 528, E4M3, E4M3, "abc"),  # 256x192 tiles, every edge partial, K tail
+    (2000, 14000, 528, E5M2, E4M3, "abc"),  # 256x224 tiles, every edge partial, K tail
     (129, 136, 128, E5M2, E5M2, "ab"),
 ])
 def test_channelwise_matches_oracle(M, N, K, fa, fb, which):
@@ -68,7 +69,7 @@ def test_channelwise_matches_oracle(M, N, K, fa, fb, which):
 def test_zero_weights_give_the_rounded_bias():
     """With B = 0 every output is bf16(bias[n]) exactly, on every kernel."""
     rng = np.random.default_rng(31)
-    for M, N in [(3, 100), (200, 264), (700, 512), (3968, 3840)]:
+    for M, N in [(3, 100), (200, 264), (700, 512), (3968, 3840), (2000, 12000), (2000, 14000)]:
         w = workloads.dense_random(M, N, 256, seed=31 + M)
         w.B[:] = 0
         sa, _, bias = _vectors(rng, M, N, "ac")

@@ -251,6 +251,21 @@ def test_256x192_tiles_full(M, N, K, fa, fb):
     _check_dense(w, f"256x192-tile {M}x{N}x{K} fmt ({fa},{fb})")
 
 
+@pytest.mark.parametrize("M,N,K,fa,fb", [
+    (2000, 14000, 1040, E4M3, E4M3),    # 256 x 224 tiles: partial tiles on both edges, K tail
+    (1900, 13900, 528, E5M2, E4M3),
+    (2000, 14000, 144, E5M2, E5M2),     # second K step partial
+    (2048, 14336, 384, E4M3, E5M2),     # whole tiles, no K tail
+])
+def test_256x224_tiles_full(M, N, K, fa, fb):
+    """The 256 x 224 tiles (7 weight blocks per wave, an odd number of B
+    copies per wave, so the K-tail key parity flips with the wave): the whole
+    output against the oracle."""
+    assert _lib().plan(0, M, N, K).variant == 6
+    w = workloads.dense_random(M, N, K, seed=M + N + K, a_fmt=fa, b_fmt=fb, std=1.0, scales=(0.5, 1.5))
+    _check_dense(w, f"256x224-tile {M}x{N}x{K} fmt ({fa},{fb})")
+
+
 @pytest.mark.parametrize("M,N,K", [(6144, 6144, 1280), (4096, 4096, 1024)])
 def test_k_tail_regression_shapes_sampled(M, N, K):
     """Shapes from "DeepGEMM on Hopper Tensor Cores", section 6.1: one failed

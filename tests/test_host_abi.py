@@ -56,6 +56,8 @@ def test_abi_version(f):
     ((0, 65, 4096, 7168), 2),
     ((0, 1, 16, 16), 4),
     ((0, 2048, 12288, 4096), 5),         # 512 tiles of 256x192 (2 waves) against 384 of 256x256
+    ((0, 2048, 14336, 4096), 6),         # 512 tiles of 256x224 (2 waves) against 448 of 256x256
+    ((3, 2048, 14336, 4096), 1),         # block scales: no 256x224 tiles
     ((3, 2048, 12288, 4096), 2),         # block scales: no 256x192 tiles
     ((4, 2048, 12288, 4096), 2),         # BF16: no 256x192 tiles
 ])
@@ -69,6 +71,8 @@ def test_dense_plan_grid(f):
     assert (p.tile_m, p.tile_n, p.workgroups) == (256, 256, 256)
     p = f.plan(0, 2000, 12000, 1040)
     assert (p.variant, p.tile_m, p.tile_n, p.workgroups) == (5, 256, 192, 8 * 63)
+    p = f.plan(0, 2000, 14000, 1040)
+    assert (p.variant, p.tile_m, p.tile_n, p.workgroups) == (6, 256, 224, 8 * 63)
     p = f.plan(0, 17, 4096, 7168)                  # decode kernel: 16 weight rows per workgroup
     assert p.token_blocks == 2 and p.tile_n == 16 and p.workgroups == 4096 // 16
     # 32 rows per workgroup once that still gives >= 256 workgroups

@@ -263,11 +263,12 @@ int launch_tile16(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s)
     return launch_status("tiled kernel (16x16x128)");
 }
 
-// Tile shapes of the tiled kernels: 256 x 256 and 128 x 256.  Dense FP8 (any
-// scale form) runs on 4 waves and the 16x16x128 instruction (2-slot ring,
-// 128 KB of LDS, for 256 rows; 3-slot, 144 KB, for 128 rows); BF16 and the
-// grouped forms on 8 waves and 32x32x64 (4 x 2 waves and a 2-slot ring for 256
-// rows, 2 x 4 and 3 slots for 128).
+// Tile shapes of the tiled kernels: 256 x 256 and 128 x 256 (and, below, 256 x
+// 224 and 256 x 192 for dense FP8 without block scales).  Dense FP8 (any scale
+// form) runs on 4 waves and the 16x16x128 instruction (2-slot ring, 128 KB of
+// LDS, for 256 rows; 3-slot, 144 KB, for 128 rows); BF16 and the grouped forms
+// on 8 waves and 32x32x64 (4 x 2 waves and a 2-slot ring for 256 rows, 2 x 4
+// and 3 slots for 128).
 template <int MODE, int SCL = 0>
 int launch_tile256(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     if constexpr (MODE == fp8g::MODE_DENSE) {

@@ -665,8 +665,8 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     constexpr int OCH = BN / 8;
     constexpr int HALF = FN * FM / 2;              // MFMAs per half step
     // the step's one barrier, and the MFMAs that carry the copies
-    constexpr int kBarAt = BM == 128 ? 10 : (BN == 256 ? 20 : BN == 224 ? 18 : 16), kDmaFrom = kBarAt,
-                  kDmaTo = BM == 128 ? 28 : (BN == 256 ? 48 : BN == 224 ? 46 : 44);
+    constexpr int kBarAt = BM == 128 ? 10 : (BN == 192 ? 18 : 20), kDmaFrom = kBarAt,
+                  kDmaTo = BM == 128 ? 28 : (BN == 192 ? 46 : 48);
     static_assert(((BM == 256 && (BN == 256 || BN == 224 || BN == 192)) || (BM == 128 && BN == 256)) &&
                       FN >= FM / 2 && CPA % 2 == 0, "shape");
     // block scales: each wave's weight rows must lie in one 128-row scale block

@@ -3,8 +3,9 @@
 "DeepGEMM: FP8 matrix-multiply kernels on Hopper Tensor Cores", section 1.3: a
 BF16 path kept beside the FP8 one for precision experiments.  Calls go through
 the C ABI (via the Python binding).  Bit-exact where the exact result is a BF16
-value (one-hot layout, identity weights, specials); the element-wise bound of
-tests/_parity.py elsewhere, with the BF16 allowance measured by the probe below.
+value (one-hot layout, identity weights, specials); elsewhere the stated
+element-wise bound of tests/_parity.py on every element (the instruction's
+summation, measured by the probe below, never matters on these random inputs).
 """
 import numpy as np
 import pytest
@@ -12,7 +13,7 @@ import torch
 
 import oracle
 import workloads
-from tests._parity import assert_within_bound, check, gpu_bits, hw_allowance_bf16
+from tests._parity import assert_within_bound, check, gpu_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -37,10 +38,10 @@ def run_bf16(A, B, out=None):
     return gpu_bits(d)
 
 
-def _check_bf16(A, B, what, strict=False):
+def _check_bf16(A, B, what):
     got = run_bf16(A, B)
     ref, r, s = oracle.gemm_nt_bf16(A, B)
-    return check(got, r, s, 1.0, hw_allowance_bf16(A, B, s), ref_bits=ref, what=what, strict=strict)
+    return check(got, r, s, 1.0, ref_bits=ref, what=what)
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 260, 392), (40, 96, 136)])
@@ -163,7 +164,7 @@ def test_specials_propagate():
     B[250, 5] = 0xFF80                # -inf: column 250
     got = run_bf16(A, B)
     ref, r, s = oracle.gemm_nt_bf16(A, B)
-    check(got, r, s, 1.0, hw_allowance_bf16(A, B, s), ref_bits=ref, what="bf16 specials")
+    check(got, r, s, 1.0, ref_bits=ref, what="bf16 specials")
     nan = lambda x: ((x & 0x7F80) == 0x7F80) & ((x & 0x7F) != 0)
     assert nan(got[3]).all() and nan(got[100, 9])
 
@@ -180,7 +181,7 @@ def test_strided_operands_and_output():
     _lib().gemm_nt_bf16(_dev(A)[:, :K], _dev(B)[:, :K], out=out)
     torch.cuda.synchronize()
     ref, r, s = oracle.gemm_nt_bf16(w.A, w.B)
-    check(gpu_bits(out), r, s, 1.0, hw_allowance_bf16(w.A, w.B, s), ref_bits=ref, what="bf16 strided")
+    check(gpu_bits(out), r, s, 1.0, ref_bits=ref, what="bf16 strided")
     assert (big[:, N:] == -7.0).all()
 
 

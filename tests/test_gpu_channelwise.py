@@ -8,7 +8,7 @@ import torch
 import oracle
 import workloads
 from tests._exact import bf16_nearest_even
-from tests._parity import check, gpu_bits, hw_allowance, hw_allowance_points
+from tests._parity import check, gpu_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -58,12 +58,7 @@ def test_channelwise_matches_oracle(M, N, K, fa, fb, which):
     sa, sb, bias = _vectors(rng, M, N, which)
     d = run(w, sa, sb, bias)
     ref, r, s = oracle.gemm_nt_channelwise(w.A, w.B, sa, sb, bias, fa, fb)
-    # the hardware allowance per element, times that element's |sa[m] sb[n]|
-    sam = np.abs(sa) if sa is not None else np.ones(M)
-    sbn = np.abs(sb) if sb is not None else np.ones(N)
-    _, _, s_unscaled, _ = oracle.gemm_nt(w.A, w.B, fa, fb)
-    allow = hw_allowance(w.A, w.B, fa, fb, 1.0, s_unscaled) * np.outer(sam, sbn)
-    check(d, r, s, 1.0, allow, ref_bits=ref, what=f"channelwise {M}x{N}x{K} {which}")
+    check(d, r, s, 1.0, ref_bits=ref, what=f"channelwise {M}x{N}x{K} {which}")
 
 
 def test_zero_weights_give_the_rounded_bias():
@@ -110,4 +105,4 @@ def test_channelwise_4096_sampled():
     r = R * sc + bias[jj].astype(np.float64)
     s = S * np.abs(sc)
     ref = np.array([bf16_nearest_even(float(x)) for x in r], np.uint16)
-    check(d[ii, jj], r, s, 1.0, None, ref_bits=ref, what="channelwise 4096^3", strict=True)
+    check(d[ii, jj], r, s, 1.0, ref_bits=ref, what="channelwise 4096^3")

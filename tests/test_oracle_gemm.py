@@ -10,6 +10,7 @@ Each pin is independent of the oracle's code: exact rational arithmetic on
 torch-decoded values, numpy float64 matmul, closed forms, invariants.
 """
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -102,6 +103,60 @@ def test_dense_e5m2_close_to_numpy():
     ref = _torch_decode(w.A, E5M2) @ _torch_decode(w.B, E5M2).T
     assert np.all(np.abs(R - ref) <= 1e-12 * S)
     assert (EX == 1).all()    # N(0,1) data: no rounding at all in FP64
+
+
+def _exact_dot(a_codes, b_codes, a_fmt, b_fmt):
+    va, vb = fp8_values(a_fmt), fp8_values(b_fmt)
+    return sum((Fraction(va[int(x)]) * Fraction(vb[int(y)]) for x, y in zip(a_codes, b_codes)), Fraction(0))
+
+
+def test_exactness_flag_reports_rounded_fp64_sums():
+    """E5M2 products reach from 2^-32 (the smallest subnormal squared) to
+    57344^2 = 0xC4000000: their sum needs up to 64 significant bits, more than
+    FP64's 53, so the oracle's FP64 sum then rounds and its exactness flag must
+    say 0.  Built cases (57344 at k = 0 against a small term at k = 9):
+      57344^2 + 2^-32  (2^-16 * 2^-16): 64 bits       -> rounded, flag 0
+      57344^2 + 2^-30  (2^-16 * 2^-14): 62 bits       -> rounded, flag 0
+      57344^2 + 2^-28  (2^-14 * 2^-14): 60 bits       -> rounded, flag 0
+      57344^2 + 2^-16  (2^-16 * 1.0):   48 bits       -> exact,   flag 1
+      57344^2 + 2^-14  (2^-14 * 1.0):   46 bits       -> exact,   flag 1
+    The flag is checked against exact rational sums of torch-decoded values."""
+    K = 16
+    A = np.zeros((2, K), np.uint8)
+    B = np.zeros((3, K), np.uint8)
+    A[:, 0] = 0x7B                       # 57344
+    B[:, 0] = 0x7B
+    A[0, 9], A[1, 9] = 0x01, 0x04        # 2^-16, 2^-14
+    B[0, 9], B[1, 9], B[2, 9] = 0x01, 0x3C, 0x04   # 2^-16, 1.0, 2^-14
+    D, R, S, EX = oracle.gemm_nt(A, B, E5M2, E5M2, want_exact=True)
+    assert EX.tolist() == [[0, 1, 0], [0, 1, 0]]
+    for i in range(2):
+        for j in range(3):
+            exact = _exact_dot(A[i], B[j], E5M2, E5M2)
+            assert (Fraction(float(R[i, j])) == exact) == bool(EX[i, j] == 1)
+    # the rounded sums lose exactly the small term
+    assert R[0, 0] == 57344.0 ** 2 and R[1, 2] == 57344.0 ** 2
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", [(E5M2, E5M2), (E4M3, E5M2), (E5M2, E4M3)])
+def test_exactness_flag_matches_exact_arithmetic(a_fmt, b_fmt):
+    """Codes drawn from every finite value of the formats: the flag is 1
+    exactly where the FP64 result equals the exact rational sum.  E5M2 x E5M2
+    products span 64 bits, so both outcomes occur; E4M3 x E5M2 products span
+    2^-25 .. 2^24.6, about 50 bits, so those sums are almost always exact."""
+    rng = np.random.default_rng(7 + 3 * a_fmt + b_fmt)
+    M, N, K = 7, 9, 24
+    A = rng.choice(_finite_codes(a_fmt), size=(M, K))
+    B = rng.choice(_finite_codes(b_fmt), size=(N, K))
+    _, R, _, EX = oracle.gemm_nt(A, B, a_fmt, b_fmt, want_exact=True)
+    got = np.zeros((M, N), bool)
+    for i in range(M):
+        for j in range(N):
+            got[i, j] = Fraction(float(R[i, j])) == _exact_dot(A[i], B[j], a_fmt, b_fmt)
+    assert np.array_equal(EX == 1, got)
+    assert got.any()
+    if a_fmt == b_fmt == E5M2:
+        assert (~got).any()
 
 
 # ---------------------------------------------------------------------------

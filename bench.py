@@ -12,21 +12,36 @@ GEMM, the block-scaled and the per-channel 4096^3 GEMMs, the dense few-token
 (decode) GEMMs against the HBM roofline and the eight transformer-projection
 shapes.
 
-The average launch duration of each leg is the interval between two HIP events
-recorded around its K back-to-back launches on the stream the kernels run on
-(torch's current stream, which the library is handed), divided by K.  The CPU
-baseline is the oracle, timed on a bounded sample of the dense 4096^3 problem
-(whole-problem passes until about 10-15 s have passed).  The 1 GiB copy leg
-calibrates the rocprofv3 HBM byte counters (--counters-summary).
+Timing ("the median of repeated event-timed launches"): each leg's average
+launch duration is the interval between two HIP events recorded around its K
+back-to-back launches on the stream the kernels run on (torch's current
+stream, which the library is handed), divided by K.  Each leg then runs 30
+further windows of L back-to-back launches (L chosen so a window lasts at
+least 0.5 ms), with an event between windows; the first 5 windows are
+discarded and the median, p10 and p90 of the per-launch time over the other
+25 are reported.
+
+CPU baseline: the oracle, timed after the GPU legs on the host threads this
+process may use (its CPU affinity, capped by OMP_NUM_THREADS where that is
+set), on a bounded sample of each configuration (rows of the problem, whole
+problems where they are small), about 20-30 s in all.
+
+Counters: `--profile-run` launches each profiled workload a few times eagerly
+(no timing) for rocprofv3; `--counters-summary` turns one kernel-trace pass and
+three --pmc passes (FETCH_SIZE; WRITE_SIZE; SQ/GRBM counters) into
+profiles/<kernel>_<workload>_counters.txt, the HBM byte counters scaled by what
+they read for a 1 GiB copy of known size.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--only NAME ...] [--no-cpu]
-    python bench.py --counters-summary FETCH_DIR WRITE_DIR --counters-command "..."
+    python bench.py --profile-run
+    python bench.py --counters-summary TRACE_DIR FETCH_DIR WRITE_DIR SQ_DIR --counters-command "..."
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -38,6 +53,7 @@ sys.path.insert(0, ROOT)
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 matrix peak (no sparsity)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 matrix peak (no sparsity)
+SIMDS = 1024                  # 256 CUs x 4 SIMDs
 METRIC = "FP8 TFLOPS (+% MFMA peak) dense 4096³; HBM GB/s masked grouped m≤32"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -54,18 +70,30 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(name: str):
-    """HBM bytes per launch recorded from rocprofv3 counters for `name`, or None
-    when no summary exists or the kernels changed since it was taken."""
-    path = os.path.join(PROFILE_DIR, f"{name}_hbm_counters.txt")
+def read_counters(name: str):
+    """Per-launch figures recorded from rocprofv3 for counter target `name`, or
+    None when no summary exists or the kernels changed since it was taken."""
+    path = os.path.join(PROFILE_DIR, f"{COUNTER_TARGETS[name][0]}_counters.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or m_hash.group(1) != kernel_source_hash():
         return None
-    return float(m_bytes.group(1))
+    out = {}
+    for key in ("hbm_bytes_per_launch", "mfma_busy_fraction", "effective_clock_ghz", "lds_bank_conflict_fraction"):
+        m = re.search(rf"{key}:\s*([0-9.eE+-]+)", text)
+        if m:
+            out[key] = float(m.group(1))
+    return out
+
+
+def _stats(vals):
+    import numpy as np
+
+    v = np.asarray(vals, dtype=np.float64)
+    return {"median_ms": float(np.median(v)), "p10_ms": float(np.percentile(v, 10)),
+            "p90_ms": float(np.percentile(v, 90))}
 
 
 class Timer:
@@ -74,7 +102,11 @@ class Timer:
     clock ramps up over the first few milliseconds of load after idle), then
     exactly `steps` back-to-back calls between one pair of HIP events recorded
     on that stream, with a synchronize on both sides of the timed region.  The
-    average launch duration is the event interval over `steps`."""
+    average launch duration is the event interval over `steps`.  Then the
+    spread: WINDOWS windows of back-to-back calls, an event between windows,
+    the first DISCARD dropped."""
+
+    WINDOWS, DISCARD, MIN_WINDOW_MS = 30, 5, 0.5
 
     def __init__(self, torch, min_warm_s=0.25):
         self.torch = torch
@@ -99,14 +131,35 @@ class Timer:
         e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return {"wall_s": wall, "kernel_ms_mean": e0.elapsed_time(e1) / steps, "warmup_calls": done}
+        mean = e0.elapsed_time(e1) / steps
+        out = {"wall_s": wall, "kernel_ms_mean": mean, "warmup_calls": done}
+        out.update(self.spread(fn, mean))
+        return out
 
-    def run_graph(self, fn, n, replays=5):
+    def spread(self, fn, mean_ms):
+        torch = self.torch
+        per = max(2, int(math.ceil(self.MIN_WINDOW_MS / max(mean_ms, 1e-4))))
+        stream = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(self.WINDOWS + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for w in range(self.WINDOWS):
+            for _ in range(per):
+                fn()
+            ev[w + 1].record(stream)
+        torch.cuda.synchronize()
+        vals = [ev[w].elapsed_time(ev[w + 1]) / per for w in range(self.DISCARD, self.WINDOWS)]
+        out = _stats(vals)
+        out.update({"windows": self.WINDOWS - self.DISCARD, "launches_per_window": per})
+        return out
+
+    def run_graph(self, fn, n, replays=None):
         """For launches shorter than the host's per-call cost (~10 us through
         Python): fn(j) for j < n captured once in a graph, which is replayed
-        for at least `min_warm_s` seconds, then `replays` times between one
-        pair of events on the replay stream.  The average launch duration is
-        the event interval over replays * n."""
+        for at least `min_warm_s` seconds, then WINDOWS times with an event
+        between replays on the replay stream.  The average launch duration is
+        the interval over the last WINDOWS - DISCARD replays over their
+        launches; median, p10 and p90 are per replay."""
         torch = self.torch
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -124,16 +177,26 @@ class Timer:
             g.replay()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(replays):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(self.WINDOWS + 1)]
+        ev[0].record(stream)
+        for w in range(self.WINDOWS):
             g.replay()
-        e1.record(stream)
+            ev[w + 1].record(stream)
         torch.cuda.synchronize()
         del g
-        return {"kernel_ms_mean": e0.elapsed_time(e1) / (replays * n), "launches": replays * n}
+        vals = [ev[w].elapsed_time(ev[w + 1]) / n for w in range(self.DISCARD, self.WINDOWS)]
+        out = _stats(vals)
+        kept = self.WINDOWS - self.DISCARD
+        out.update({"kernel_ms_mean": ev[self.DISCARD].elapsed_time(ev[self.WINDOWS]) / (kept * n),
+                    "launches": kept * n, "windows": kept, "launches_per_window": n})
+        return out
 
 
+def timing_fields(t, scale=1.0):
+    """The spread of a Timer result in microseconds (times scale)."""
+    return {"us_median": t["median_ms"] * 1e3 * scale, "us_p10": t["p10_ms"] * 1e3 * scale,
+            "us_p90": t["p90_ms"] * 1e3 * scale, "windows": t["windows"],
+            "launches_per_window": t["launches_per_window"]}
 def dev(torch, x):
     return torch.from_numpy(x).cuda()
 
@@ -285,7 +348,7 @@ def bench_masked_table(torch, f, steps, warmup, timer, G=16, seed=40):
             flops = 2.0 * G * m * n * k
             nbytes = float(G * n * k + G * m * k + 2 * G * m * n)
             ms = t["kernel_ms_mean"]
-            out.append({"m": m, "n": n, "k": k, "groups": G, "kernel_us_mean": ms * 1e3,
+            out.append({"m": m, "n": n, "k": k, "groups": G, "kernel_us_mean": ms * 1e3, **timing_fields(t),
                         "tflops": flops / (ms * 1e-3) / 1e12, "gbs": nbytes / (ms * 1e-3) / 1e9,
                         "variant": f.plan(1, cap, n, k, G, m).variant})
         del a, b, sb, o, w
@@ -347,37 +410,6 @@ def bench_contig(torch, f, w, steps, warmup, timer):
     return t
 
 
-def cpu_baseline(w, target_s=15.0, max_passes=20):
-    """The oracle on the dense problem: rows 0..R-1 (all columns, full K), R
-    chosen so one pass takes about target_s seconds; when the whole problem
-    takes less than that, whole-problem passes are repeated until about
-    target_s seconds have passed (at most max_passes)."""
-    import oracle
-
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or oracle.default_threads()
-    threads = max(1, min(threads, oracle.default_threads(), 16))
-    M, N, K = w.shape
-    r0 = 8
-    t0 = time.perf_counter()
-    oracle.gemm_nt(w.A[:r0], w.B, w.a_fmt, w.b_fmt, w.sa, w.sb, threads=threads)
-    probe = time.perf_counter() - t0
-    rows = int(min(M, max(threads, r0 * target_s / max(probe, 1e-3))))
-    rows = M if rows >= M else max(threads, (rows // threads) * threads)
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.gemm_nt(w.A[:rows], w.B, w.a_fmt, w.b_fmt, w.sa, w.sb, threads=threads)
-        passes += 1
-        el = time.perf_counter() - t0
-        if rows < M or el >= 0.67 * target_s or passes >= max_passes:
-            break
-    flops = 2.0 * rows * N * K * passes
-    what = (f"rows 0..{rows - 1} of the {M}x{N}x{K} E4M3 problem (all {N} columns, full K)" if rows < M
-            else f"the whole {M}x{N}x{K} E4M3 problem, {passes} pass(es)")
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{what}, {el:.1f} s on {threads} host threads", "seconds": el}
-
-
 def bench_copy(torch, steps, warmup, timer, nbytes=1 << 30):
     """A plain elementwise copy of known size (fp32 negation: reads nbytes,
     writes nbytes) that calibrates the HBM byte counters."""
@@ -393,25 +425,225 @@ def bench_copy(torch, steps, warmup, timer, nbytes=1 << 30):
 
 
 # Kernel-name patterns of the launches each counter summary covers.
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on bounded samples of each configuration.
+# ---------------------------------------------------------------------------
+
+def cpu_threads():
+    """(threads used, CPUs in this process's affinity): the affinity set,
+    capped by OMP_NUM_THREADS where that is set (the CPU share of one GPU)."""
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = os.cpu_count() or 1
+    omp = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    return (min(aff, omp) if omp > 0 else aff), aff
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_dense(w, target_s, label, m_full=None):
+    """The oracle on rows 0..R-1 of a dense problem (all columns, full K), R
+    sized from a probe so that the pass takes about target_s; a problem that
+    takes less than that whole is repeated (at most 20 passes).  w may hold
+    only the first rows of A of a problem with m_full rows."""
+    import oracle
+
+    threads, _ = cpu_threads()
+    M, N, K = w.shape
+    r0 = min(M, max(threads, 8))
+    t0 = time.perf_counter()
+    oracle.gemm_nt(w.A[:r0], w.B, w.a_fmt, w.b_fmt, w.sa, w.sb, threads=threads)
+    probe = max(time.perf_counter() - t0, 1e-4)
+    rows = int(min(M, max(r0, r0 * target_s / probe)))
+    if rows < M:
+        rows = max(r0, (rows // threads) * threads)
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.gemm_nt(w.A[:rows], w.B, w.a_fmt, w.b_fmt, w.sa, w.sb, threads=threads)
+        passes += 1
+        el = time.perf_counter() - t0
+        if rows < M or el >= 0.67 * target_s or passes >= 20:
+            break
+    flops = 2.0 * rows * N * K * passes
+    mf = m_full or M
+    what = (f"rows 0..{rows - 1} of {mf}x{N}x{K} (all {N} columns, full K), {passes} pass(es)" if rows < mf
+            else f"the whole {M}x{N}x{K} problem, {passes} pass(es)")
+    return {"config": label, "value": flops / el / 1e9, "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": el, "sample": what}
+
+
+def cpu_masked(w, label):
+    """The oracle on the whole masked grouped problem (every valid row)."""
+    import numpy as np
+    import oracle
+
+    threads, _ = cpu_threads()
+    G, cap, K = w.A.shape
+    N = w.B.shape[1]
+    t0 = time.perf_counter()
+    oracle.grouped_masked(w.A, w.B, w.masked_m, w.sb, w.a_fmt, w.b_fmt, w.sa, threads=threads)
+    el = time.perf_counter() - t0
+    m = np.clip(w.masked_m.astype(np.int64), 0, cap)
+    active = int((m > 0).sum())
+    nbytes = active * N * K + int(m.sum()) * K + 2 * int(m.sum()) * N + 4 * G + 4 * (G + 1)
+    return {"config": label, "value": nbytes / el / 1e9, "unit": "GB/s (algorithmic bytes)",
+            "gflops": 2.0 * int(m.sum()) * N * K / el / 1e9, "cores": threads, "kind": "oracle", "seconds": el,
+            "sample": f"the whole problem: {int(m.sum())} valid rows over {active} experts"}
+
+
+def cpu_contig(w, target_s, label, m_full=None):
+    """The oracle on the first R rows of the contiguous grouped problem (their
+    experts' runs and padding), R sized from a probe; w may hold only the
+    first rows of a problem with m_full rows."""
+    import numpy as np
+    import oracle
+
+    threads, _ = cpu_threads()
+    M_total, K = w.A.shape
+    G, N, _ = w.B.shape
+    r0 = 256
+    t0 = time.perf_counter()
+    oracle.grouped_contig(w.A[:r0], w.B, w.grp_idx[:r0], w.sb, w.a_fmt, w.b_fmt, w.sa, threads=threads)
+    probe = max(time.perf_counter() - t0, 1e-4)
+    rows = int(min(M_total, max(r0, r0 * target_s / probe)))
+    t0 = time.perf_counter()
+    oracle.grouped_contig(w.A[:rows], w.B, w.grp_idx[:rows], w.sb, w.a_fmt, w.b_fmt, w.sa, threads=threads)
+    el = time.perf_counter() - t0
+    valid = int((w.grp_idx[:rows] >= 0).sum())
+    experts = len(np.unique(w.grp_idx[:rows][w.grp_idx[:rows] >= 0]))
+    return {"config": label, "value": 2.0 * valid * N * K / el / 1e9, "unit": "GFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": el,
+            "sample": f"rows 0..{rows - 1} of {m_full or M_total} ({valid} valid rows over {experts} expert(s))"}
+
+
+# ---------------------------------------------------------------------------
+# Profiling: eager launches for rocprofv3, and the counter summaries.
+# ---------------------------------------------------------------------------
+
+# Counter target -> (summary file stem, kernel-name pattern of its dispatches
+# in --profile-run, workload, algorithmic FLOPs and bytes per launch or None).
 COUNTER_TARGETS = {
-    "dense_4096_e4m3": ("tile16_kernel<256, 256, 2, 0, 0, 0, 0,", "dense 4096^3 E4M3 GEMM"),
-    "masked_decode": ("swap_kernel<", "masked grouped decode GEMM G=32 cap=64 N=4096 K=7168 m_g~U{0..32}"),
+    "dense_4096_e4m3": ("tile16_kernel_dense_4096_e4m3", "tile16_kernel<256, 256, 2, 0, 0, 0, 0, false>",
+                        "dense 4096^3 E4M3 GEMM (seed 2)"),
+    "masked_decode": ("swap_kernel_masked_decode", "swap_kernel<",
+                      "masked grouped decode GEMM G=32 cap=64 N=4096 K=7168 m_g~U{0..32} (seed 4)"),
+    "contig_prefill": ("ring_kernel_contig_prefill", "ring_kernel<256, 256, 4, 2, 0, 0, 2, 2, 128, 0>",
+                       "contiguous grouped prefill GEMM, 65536 routed rows over 32 experts, N=4096 K=7168 (seed 5)"),
+    "decode_64": ("decode_kernel_dense_64x4096x7168", "decode_kernel<4, 1, 4, 0, 0, 2, 0>",
+                  "dense few-token GEMM M=64 N=4096 K=7168 (seed 13)"),
 }
 COPY_PATTERN = "neg_kernel"
+PROFILE_LAUNCHES = 6
+
+
+def profile_run():
+    """Eager launches of each counter target's workload (and the 1 GiB copy
+    that calibrates the byte counters), PROFILE_LAUNCHES each, for rocprofv3.
+    Prints the algorithmic work of each target as one JSON line."""
+    import numpy as np
+    import torch
+
+    import fp8_gemm_amd as f
+    import workloads
+
+    f.load_library()
+    work = {}
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(PROFILE_LAUNCHES):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+    log("profile: dense 4096^3 E4M3")
+    w = workloads.dense_square(workloads.E4M3)
+    a, b = dev(torch, w.A), dev(torch, w.B)
+    sa = torch.tensor([w.sa], dtype=torch.float32, device="cuda")
+    sb = torch.tensor([w.sb], dtype=torch.float32, device="cuda")
+    out = torch.empty((4096, 4096), dtype=torch.bfloat16, device="cuda")
+    for _ in range(PROFILE_LAUNCHES):
+        f.gemm_nt(a, b, sa, sb, out=out, a_dtype=w.a_fmt, b_dtype=w.b_fmt)
+    torch.cuda.synchronize()
+    fl, by = dense_work(4096, 4096, 4096)
+    work["dense_4096_e4m3"] = {"flops": fl, "bytes": by}
+    del a, b, out
+
+    log("profile: dense decode 64x4096x7168")
+    wd = workloads.dense_random(64, 4096, 7168, seed=13, std=1.0)
+    a, b = dev(torch, wd.A), dev(torch, wd.B)
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    out = torch.empty((64, 4096), dtype=torch.bfloat16, device="cuda")
+    for _ in range(PROFILE_LAUNCHES):
+        f.gemm_nt(a, b, one, one, out=out, a_dtype=wd.a_fmt, b_dtype=wd.b_fmt)
+    torch.cuda.synchronize()
+    fl, by = dense_work(64, 4096, 7168)
+    work["decode_64"] = {"flops": fl, "bytes": by}
+    del a, b, out
+
+    log("profile: masked grouped decode")
+    wm = workloads.masked_decode()
+    G, cap, K = wm.A.shape
+    N = wm.B.shape[1]
+    a, b = dev(torch, wm.A), dev(torch, wm.B)
+    sa = torch.tensor([wm.sa], dtype=torch.float32, device="cuda")
+    sb, mm = dev(torch, wm.sb), dev(torch, wm.masked_m)
+    out = torch.empty((G, cap, N), dtype=torch.bfloat16, device="cuda")
+    for _ in range(PROFILE_LAUNCHES):
+        f.grouped_gemm_masked(a, b, sa, sb, mm, out=out, expected_m=32, a_dtype=wm.a_fmt, b_dtype=wm.b_fmt)
+    torch.cuda.synchronize()
+    m = np.clip(wm.masked_m.astype(np.int64), 0, cap)
+    active = int((m > 0).sum())
+    work["masked_decode"] = {"flops": 2.0 * int(m.sum()) * N * K,
+                             "bytes": float(active * N * K + int(m.sum()) * K + 2 * int(m.sum()) * N + 4 * G + 4 * (G + 1))}
+    del a, b, out, wm
+
+    log("profile: contiguous grouped prefill")
+    wc = workloads.contig_prefill()
+    M_total, K = wc.A.shape
+    G, N, _ = wc.B.shape
+    a, b = dev(torch, wc.A), dev(torch, wc.B)
+    sa = torch.tensor([wc.sa], dtype=torch.float32, device="cuda")
+    sb, gi = dev(torch, wc.sb), dev(torch, wc.grp_idx)
+    out = torch.empty((M_total, N), dtype=torch.bfloat16, device="cuda")
+    for _ in range(PROFILE_LAUNCHES):
+        f.grouped_gemm_contig(a, b, sa, sb, gi, out=out, a_dtype=wc.a_fmt, b_dtype=wc.b_fmt)
+    torch.cuda.synchronize()
+    valid = int((wc.grp_idx >= 0).sum())
+    work["contig_prefill"] = {"flops": 2.0 * valid * N * K, "bytes": float(M_total * K + G * N * K + 2 * valid * N)}
+    print(json.dumps({"profile_run": True, "work": work}), flush=True)
+
+
+def _csv_files(directory, suffix):
+    import glob
+
+    files = glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return files
 
 
 def _counter_rows(directory):
     import csv
-    import glob
 
-    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
-    if not files:
-        raise SystemExit(f"no *counter_collection.csv under {directory}")
     out = {}
-    for fpath in files:
+    for fpath in _csv_files(directory, "counter_collection.csv"):
         with open(fpath, newline="") as fh:
             for row in csv.DictReader(fh):
-                key = (row["Dispatch_Id"], row["Kernel_Name"])
+                key = (fpath, row["Dispatch_Id"], row["Kernel_Name"])
                 out.setdefault(key, {})
                 name = row["Counter_Name"]
                 out[key][name] = out[key].get(name, 0.0) + float(row["Counter_Value"])
@@ -419,42 +651,139 @@ def _counter_rows(directory):
 
 
 def _per_dispatch(rows, pattern, counter):
-    vals = [c[counter] for (d, k), c in rows.items() if pattern in k and counter in c]
+    vals = [c[counter] for (_, d, k), c in rows.items() if pattern in k and counter in c]
     if not vals:
         raise SystemExit(f"no dispatch of a kernel matching {pattern!r} with counter {counter}")
     return sum(vals) / len(vals), len(vals)
 
 
-def counters_summary(fetch_dir, write_dir, command):
-    """Writes profiles/<name>_hbm_counters.txt from a rocprofv3 --pmc FETCH_SIZE
-    run and a --pmc WRITE_SIZE run (KiB per dispatch), each scaled by what the
-    same counter reads for the copy kernel of known size."""
-    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+def _pmc_durations(directory):
+    """{(file, dispatch id, kernel name): seconds} from the start and end
+    timestamps a --pmc pass records with each dispatch's counters."""
+    import csv
+
+    out = {}
+    for fpath in _csv_files(directory, "counter_collection.csv"):
+        with open(fpath, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if "Start_Timestamp" in row and row["Start_Timestamp"]:
+                    out[(fpath, row["Dispatch_Id"], row["Kernel_Name"])] = \
+                        (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9
+    return out
+
+
+def _clock_and_busy(rows, durs, pattern):
+    """Mean over matching dispatches of the --pmc pass: the kernel's cycles
+    (GRBM_GUI_ACTIVE, summed over the 8 XCDs' GRBM blocks, over 8), the clock
+    (those cycles over the dispatch's own duration) and the MFMA-busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES, summed over the 1024 SIMDs, over 1024 x the
+    kernel's cycles)."""
+    clk, busy, cyc, dur = [], [], [], []
+    for key, c in rows.items():
+        if pattern not in key[2] or "GRBM_GUI_ACTIVE" not in c or key not in durs:
+            continue
+        g = c["GRBM_GUI_ACTIVE"] / 8.0
+        cyc.append(g)
+        dur.append(durs[key])
+        clk.append(g / durs[key] / 1e9)
+        busy.append(c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (SIMDS * g) if g else float("nan"))
+    n = len(clk)
+    if not n:
+        raise SystemExit(f"no --pmc dispatch of a kernel matching {pattern!r} with GRBM_GUI_ACTIVE")
+    return sum(cyc) / n, sum(dur) / n, sum(clk) / n, sum(busy) / n, n
+
+
+def _trace_durations(directory, pattern):
+    import csv
+
+    durs = []
+    for fpath in _csv_files(directory, "kernel_trace.csv"):
+        with open(fpath, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if pattern in row["Kernel_Name"]:
+                    durs.append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9)
+    if not durs:
+        raise SystemExit(f"no traced dispatch of a kernel matching {pattern!r}")
+    return durs
+
+
+SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+               "SQ_INSTS_LDS", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "GRBM_GUI_ACTIVE", "GRBM_COUNT")
+
+
+def counters_summary(trace_dir, fetch_dir, write_dir, sq_dir, command, work_json):
+    """Writes profiles/<kernel>_<workload>_counters.txt for every counter target
+    from a --kernel-trace pass and three --pmc passes over `--profile-run`."""
+    import statistics
+
+    work = json.loads(work_json)["work"] if work_json else {}
+    fr, wr, sr = _counter_rows(fetch_dir), _counter_rows(write_dir), _counter_rows(sq_dir)
+    sq_durs = _pmc_durations(sq_dir)
+    copy_cyc, copy_dur, copy_clk, _, _ = _clock_and_busy(sr, sq_durs, COPY_PATTERN)
     copy_f, ncf = _per_dispatch(fr, COPY_PATTERN, "FETCH_SIZE")
     copy_w, ncw = _per_dispatch(wr, COPY_PATTERN, "WRITE_SIZE")
     nbytes = float(1 << 30)
     kf, kw = nbytes / (copy_f * 1024.0), nbytes / (copy_w * 1024.0)
     h = kernel_source_hash()
-    for name, (pattern, what) in COUNTER_TARGETS.items():
+    for name, (stem, pattern, what) in COUNTER_TARGETS.items():
+        durs = _trace_durations(trace_dir, pattern)
+        dur = statistics.mean(durs)
         f_kib, nf = _per_dispatch(fr, pattern, "FETCH_SIZE")
         w_kib, nw = _per_dispatch(wr, pattern, "WRITE_SIZE")
         rd, wt = f_kib * 1024.0 * kf, w_kib * 1024.0 * kw
-        text = (f"rocprofv3 HBM byte counters: {what}\n\n"
-                f"commands (from the repository root):\n{command}\n\n"
-                f"kernel_source_hash: {h}\n"
-                f"kernel name pattern: {pattern}  (dispatches: FETCH {nf}, WRITE {nw})\n"
-                f"FETCH_SIZE per dispatch: {f_kib:.1f} KiB\n"
-                f"WRITE_SIZE per dispatch: {w_kib:.1f} KiB\n"
-                f"calibration, fp32 negation of 1 GiB (reads 1 GiB, writes 1 GiB), {ncf}/{ncw} dispatches:\n"
-                f"  FETCH_SIZE {copy_f:.1f} KiB -> read factor {kf:.4f}\n"
-                f"  WRITE_SIZE {copy_w:.1f} KiB -> write factor {kw:.4f}\n"
-                f"hbm_read_bytes_per_launch: {rd:.0f}\n"
-                f"hbm_write_bytes_per_launch: {wt:.0f}\n"
-                f"hbm_bytes_per_launch: {rd + wt:.0f}\n")
-        path = os.path.join(PROFILE_DIR, f"{name}_hbm_counters.txt")
+        sq = {}
+        for c in SQ_COUNTERS:
+            sq[c] = _per_dispatch(sr, pattern, c)[0]
+        cyc, pmc_dur, clock, mfma_busy, npmc = _clock_and_busy(sr, sq_durs, pattern)
+        w = work.get(name, {})
+        lines = [
+            f"rocprofv3 counters: {what}",
+            "",
+            "commands (from the repository root; each pass its own rocprofv3 run over the same program):",
+            command,
+            "",
+            f"kernel_source_hash: {h}",
+            f"kernel name pattern: {pattern}",
+            f"dispatches: trace {len(durs)}, FETCH {nf}, WRITE {nw}, SQ/GRBM {_per_dispatch(sr, pattern, 'GRBM_GUI_ACTIVE')[1]}",
+            f"kernel duration (trace pass, mean over dispatches): {dur * 1e6:.2f} us "
+            f"(min {min(durs) * 1e6:.2f}, max {max(durs) * 1e6:.2f})",
+            "",
+            "HBM traffic (FETCH_SIZE / WRITE_SIZE passes):",
+            f"  FETCH_SIZE per dispatch: {f_kib:.1f} KiB; WRITE_SIZE per dispatch: {w_kib:.1f} KiB",
+            f"  calibration, fp32 negation of 1 GiB (reads 1 GiB, writes 1 GiB), {ncf}/{ncw} dispatches: "
+            f"FETCH_SIZE {copy_f:.1f} KiB -> read factor {kf:.4f}; WRITE_SIZE {copy_w:.1f} KiB -> write factor {kw:.4f}",
+            f"  hbm_read_bytes_per_launch: {rd:.0f}",
+            f"  hbm_write_bytes_per_launch: {wt:.0f}",
+            f"  hbm_bytes_per_launch: {rd + wt:.0f}",
+        ]
+        if w:
+            lines += [f"  algorithmic_bytes_per_launch: {w['bytes']:.0f}  (traffic / algorithmic = {(rd + wt) / w['bytes']:.3f})",
+                      f"  algorithmic_flops_per_launch: {w['flops']:.0f}",
+                      f"  achieved over the traced duration: {w['flops'] / dur / 1e12:.1f} TFLOP/s, "
+                      f"{w['bytes'] / dur / 1e9:.0f} GB/s algorithmic, {(rd + wt) / dur / 1e9:.0f} GB/s counted"]
+        lines += [
+            "",
+            "SQ / GRBM pass (values per dispatch, summed over the counter's instances):",
+        ] + [f"  {c}: {sq[c]:.0f}" for c in SQ_COUNTERS] + [
+            "",
+            f"derived (SQ / GRBM pass, {npmc} dispatches, their own timestamps; counter collection serialises "
+            "the launches and lengthens them):",
+            f"  dispatch duration in this pass: {pmc_dur * 1e6:.2f} us",
+            f"  kernel cycles (GRBM_GUI_ACTIVE / 8 XCDs): {cyc:.0f}",
+            f"  effective_clock_ghz: {clock:.3f}  (kernel cycles / dispatch duration; the memory-bound 1 GiB copy "
+            f"reads {copy_clk:.3f} GHz the same way)",
+            f"  mfma_busy_fraction: {mfma_busy:.4f}  (SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x kernel cycles); the "
+            f"counter counts each 16x16x128 FP8 instruction as 32 cycles)",
+            f"  lds_bank_conflict_fraction: {sq['SQ_LDS_BANK_CONFLICT'] / sq['SQ_LDS_IDX_ACTIVE'] if sq['SQ_LDS_IDX_ACTIVE'] else 0.0:.4f}"
+            f"  (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE)",
+        ]
+        if w.get("flops"):
+            lines.append(f"  MFMA-bound time at the effective clock: {w['flops'] / (SIMDS * 2048.0 * clock * 1e9) * 1e6:.2f} us "
+                         f"(against {dur * 1e6:.2f} us traced)")
+        path = os.path.join(PROFILE_DIR, f"{stem}_counters.txt")
         with open(path, "w") as fh:
-            fh.write(text)
-        log(f"wrote {path}: {(rd + wt) / 1e6:.1f} MB per launch")
+            fh.write("\n".join(lines) + "\n")
+        log(f"wrote {path}")
 
 
 def main():
@@ -463,19 +792,20 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: dense masked masked_table masked_bs contig contig_bs small e5m2 blockscaled channelwise bf16 decode "
-                         "proj copy "
-                         "(default: all)")
+                    help="subset of: dense masked masked_table masked_bs contig contig_bs small e5m2 blockscaled "
+                         "channelwise bf16 decode proj copy (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
-                    help="write profiles/*_hbm_counters.txt from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
-                         "output directories (no GPU work)")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="eager launches of the counter targets' workloads, for rocprofv3 (no timing)")
+    ap.add_argument("--counters-summary", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "SQ_DIR"),
+                    default=None, help="write profiles/*_counters.txt from rocprofv3 output directories (no GPU work)")
     ap.add_argument("--counters-command", default="",
-                    help="the commands that produced the counter directories (recorded in the summary)")
+                    help="the commands that produced the counter directories (recorded in the summaries)")
+    ap.add_argument("--counters-work", default="", help="the JSON line --profile-run printed")
     args = ap.parse_args()
 
     if args.counters_summary:
-        counters_summary(args.counters_summary[0], args.counters_summary[1], args.counters_command)
+        counters_summary(*args.counters_summary, args.counters_command, args.counters_work)
         return
 
     if args.gpus != 1:
@@ -492,11 +822,16 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.profile_run:
+        profile_run()
+        return
     timer = Timer(torch)
-    want = set(args.only) if args.only else {"dense", "masked", "masked_table", "masked_bs", "contig", "contig_bs", "small", "e5m2", "blockscaled",
-                                           "channelwise", "bf16", "decode", "proj", "copy"}
+    want = set(args.only) if args.only else {"dense", "masked", "masked_table", "masked_bs", "contig", "contig_bs",
+                                           "small", "e5m2", "blockscaled", "channelwise", "bf16", "decode", "proj",
+                                           "copy"}
     steps, warmup = args.steps, args.warmup
     extra = {}
+    cpu_jobs = []           # oracle samples, run after every GPU leg
 
     log("generating dense 4096^3 E4M3 inputs")
     wd = workloads.dense_square(workloads.E4M3)
@@ -504,14 +839,18 @@ def main():
     if "dense" in want:
         log("timing dense 4096^3 E4M3")
         dense = bench_dense(torch, f, wd, steps, warmup, timer)
-        log(f"  {dense['tflops_kernel']:.1f} TFLOP/s per launch, {dense['tflops_wall']:.1f} whole-job")
+        log(f"  {dense['tflops_kernel']:.1f} TFLOP/s per launch, {dense['tflops_wall']:.1f} whole-job; "
+            f"median {dense['median_ms'] * 1e3:.2f} us (p10 {dense['p10_ms'] * 1e3:.2f}, p90 {dense['p90_ms'] * 1e3:.2f})")
+        cpu_jobs.append(lambda: cpu_dense(wd, 6.0, "dense 4096^3 E4M3"))
     if "e5m2" in want:
         log("timing dense 4096^3 E5M2")
         w5 = workloads.dense_square(workloads.E5M2)
         r = bench_dense(torch, f, w5, steps, warmup, timer)
         extra["dense_4096_e5m2"] = {"tflops_kernel": r["tflops_kernel"], "tflops_wall": r["tflops_wall"],
                                     "kernel_ms_mean": r["kernel_ms_mean"],
-                                    "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS}
+                                    "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS, **timing_fields(r)}
+        w5s = workloads.Dense(w5.A[:1024].copy(), w5.B, w5.sa, w5.sb, w5.a_fmt, w5.b_fmt, w5.name)
+        cpu_jobs.append(lambda: cpu_dense(w5s, 2.0, "dense 4096^3 E5M2", m_full=4096))
         del w5
     if "blockscaled" in want:
         log("timing block-scaled dense 4096^3 E4M3 (power-of-two scales per 1x128 / 128x128 block)")
@@ -521,7 +860,7 @@ def main():
             "workload": "dense 4096^3 E4M3, activations N(0,1) per 1x128 block and weights N(0,0.02) per "
                         "128x128 block, each with its own power-of-two (E8M0) scale (seed 6)",
             "tflops_kernel": r["tflops_kernel"], "kernel_ms_mean": r["kernel_ms_mean"],
-            "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS}
+            "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS, **timing_fields(r)}
         log(f"  {r['tflops_kernel']:.1f} TFLOP/s")
         del wbs
     if "channelwise" in want:
@@ -531,7 +870,7 @@ def main():
             "workload": "dense 4096^3 E4M3 (seed 2 operands), row scales and channel scales U[0.5,2], "
                         "bias N(0,1), applied in the epilogue",
             "tflops_kernel": r["tflops_kernel"], "kernel_ms_mean": r["kernel_ms_mean"],
-            "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS}
+            "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS, **timing_fields(r)}
         log(f"  {r['tflops_kernel']:.1f} TFLOP/s")
     if "bf16" in want:
         log("timing the BF16 comparison path, 4096^3")
@@ -539,7 +878,7 @@ def main():
         r = bench_bf16(torch, f, wb, steps, warmup, timer)
         extra["dense_4096_bf16"] = {
             "workload": "BF16 comparison GEMM 4096^3, the seed-2 draws of the FP8 case rounded to BF16, no scales",
-            "tflops_kernel": r["tflops_kernel"], "kernel_ms_mean": r["kernel_ms_mean"],
+            "tflops_kernel": r["tflops_kernel"], "kernel_ms_mean": r["kernel_ms_mean"], **timing_fields(r),
             "roofline": {"bound": "mfma", "achieved": r["tflops_kernel"], "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": r["tflops_kernel"] / PEAK_BF16_TFLOPS},
             "context_torch_matmul": {"tflops": r["torch_matmul_tflops"], "ms_mean": r["torch_matmul_ms_mean"]}}
@@ -550,15 +889,17 @@ def main():
         for (N, K) in ((4096, 7168), (14336, 4096)):
             for M in (1, 16, 32, 64):
                 r = bench_decode(torch, f, M, N, K, steps, warmup, timer)
-                out.append({"M": M, "N": N, "K": K, "kernel_us_mean": r["kernel_ms_mean"] * 1e3,
+                out.append({"M": M, "N": N, "K": K, "kernel_us_mean": r["kernel_ms_mean"] * 1e3, **timing_fields(r),
+                            "variant": f.plan(0, M, N, K).variant,
                             "roofline": {"bound": "hbm", "achieved": r["gbs_kernel"], "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": r["gbs_kernel"] / PEAK_HBM_GBS,
                                          "algorithmic_bytes": r["bytes"]}})
-                log(f"  decode {M}x{N}x{K}: {r['kernel_ms_mean'] * 1e3:.1f} us, {r['gbs_kernel']:.0f} GB/s")
+                log(f"  decode {M}x{N}x{K}: {r['kernel_ms_mean'] * 1e3:.2f} us, {r['gbs_kernel']:.0f} GB/s")
         extra["dense_decode"] = {
             "workload": "dense few-token GEMMs, A ~N(0,1), B ~N(0,1) E4M3 (seed 13), weights rotated over "
                         "> 512 MB of copies so each launch reads them from HBM",
-            "timing": "launches captured in a graph and replayed (eager calls through Python cost ~10 us each)",
+            "timing": "launches captured in a graph and replayed (eager calls through Python cost ~10 us each); "
+                      "median/p10/p90 per replay",
             "shapes": out}
     if "small" in want:
         log("timing dense 256^3")
@@ -570,22 +911,27 @@ def main():
         g = timer.run_graph(lambda j: f.gemm_nt(a, b, one, one, out=o, a_dtype=ws.a_fmt, b_dtype=ws.b_fmt), 100)
         extra["dense_256"] = {"kernel_us_mean": r["kernel_ms_mean"] * 1e3,
                               "us_per_call_wall": r["wall_s"] / steps * 1e6, "bound": "launch latency",
-                              "kernel_us_graph": g["kernel_ms_mean"] * 1e3}
+                              "kernel_us_graph": g["kernel_ms_mean"] * 1e3, "graph": timing_fields(g),
+                              "eager": timing_fields(r), "variant": f.plan(0, 256, 256, 256).variant}
+        cpu_jobs.append(lambda: cpu_dense(ws, 0.5, "dense 256^3"))
         del a, b, o
     if "masked" in want:
         log("generating masked grouped decode inputs (G=32, cap=64, N=4096, K=7168)")
         wm = workloads.masked_decode()
         log("timing masked grouped decode")
         r = bench_masked(torch, f, wm, steps, warmup, timer)
+        ctr = read_counters("masked_decode")
         extra["masked_grouped"] = {
             "workload": "masked grouped FP8 GEMM, G=32, cap=64, N=4096, K=7168, m_g~U{0..32} (seed 4), E4M3, swap-AB",
             "gbs_kernel": r["gbs_kernel"], "gbs_wall": r["gbs_wall"], "kernel_ms_mean": r["kernel_ms_mean"],
+            **timing_fields(r),
             "tflops_kernel": r["tflops_kernel"], "active_experts": r["active_experts"], "valid_rows": r["valid_rows"],
             "roofline": {"bound": "hbm", "achieved": r["gbs_kernel"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": r["gbs_kernel"] / PEAK_HBM_GBS, "traffic": read_traffic("masked_decode"),
+                         "frac": r["gbs_kernel"] / PEAK_HBM_GBS,
+                         "traffic": ctr.get("hbm_bytes_per_launch") if ctr else None,
                          "algorithmic_bytes": r["bytes"]}}
         log(f"  {r['gbs_kernel']:.0f} GB/s ({r['gbs_kernel'] / PEAK_HBM_GBS:.1%} of HBM peak)")
-        del wm
+        cpu_jobs.append(lambda: cpu_masked(wm, "masked grouped decode G=32 cap=64 N=4096 K=7168"))
     if "masked_table" in want:
         log("timing the swap-AB benchmark table shapes (16 groups, m in {32, 96, 160})")
         rows = bench_masked_table(torch, f, max(10, steps // 4), max(2, warmup // 4), timer)
@@ -602,7 +948,7 @@ def main():
         extra["masked_grouped_blockscaled"] = {
             "workload": "block-scaled masked grouped FP8 GEMM, G=32, cap=64, N=4096, K=7168, m_g~U{0..32} (seed 8), "
                         "E8M0 scales per 1x128 token block and 128x128 weight block, swap-AB",
-            "kernel_ms_mean": r["kernel_ms_mean"],
+            "kernel_ms_mean": r["kernel_ms_mean"], **timing_fields(r),
             "roofline": {"bound": "hbm", "achieved": r["gbs_kernel"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": r["gbs_kernel"] / PEAK_HBM_GBS, "algorithmic_bytes": r["bytes"]}}
         log(f"  {r['gbs_kernel']:.0f} GB/s")
@@ -616,9 +962,14 @@ def main():
             "workload": "contiguous grouped FP8 GEMM, 8192 tokens x top-8 over 32 experts, N=4096, K=7168 (seed 5)",
             "tflops_kernel": r["tflops_kernel"], "tflops_wall": r["tflops_wall"],
             "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS, "kernel_ms_mean": r["kernel_ms_mean"],
+            **timing_fields(r),
             "rows_total": r["rows_total"], "rows_valid": r["rows_valid"],
             "tflops_kernel_incl_padding": r["tflops_kernel_incl_padding"]}
         log(f"  {r['tflops_kernel']:.1f} TFLOP/s")
+        wcs = workloads.Contig(A=wc.A[:4096].copy(), B=wc.B, grp_idx=wc.grp_idx[:4096].copy(), sa=wc.sa, sb=wc.sb,
+                               a_fmt=wc.a_fmt, b_fmt=wc.b_fmt, name=wc.name)
+        mt = wc.A.shape[0]
+        cpu_jobs.append(lambda: cpu_contig(wcs, 3.0, "contiguous grouped prefill 65536 rows, N=4096 K=7168", m_full=mt))
         del wc
     if "contig_bs" in want:
         log("generating block-scaled contiguous grouped prefill inputs")
@@ -627,7 +978,7 @@ def main():
         extra["contig_grouped_blockscaled"] = {
             "workload": "block-scaled contiguous grouped FP8 GEMM, 8192 tokens x top-8 over 32 experts, N=4096, "
                         "K=7168, E8M0 scales per 1x128 token block and 128x128 weight block (seed 9)",
-            "tflops_kernel": r["tflops_kernel"], "kernel_ms_mean": r["kernel_ms_mean"],
+            "tflops_kernel": r["tflops_kernel"], "kernel_ms_mean": r["kernel_ms_mean"], **timing_fields(r),
             "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS}
         log(f"  {r['tflops_kernel']:.1f} TFLOP/s")
         del wcb
@@ -639,8 +990,10 @@ def main():
             M, N, K = wp.shape
             out.append({"M": M, "N": N, "K": K, "tflops_kernel": r["tflops_kernel"],
                         "frac_of_peak": r["tflops_kernel"] / PEAK_FP8_TFLOPS, "kernel_ms_mean": r["kernel_ms_mean"],
-                        "variant": f.plan(0, M, N, K).variant})
+                        **timing_fields(r), "variant": f.plan(0, M, N, K).variant})
             log(f"  projection {M}x{N}x{K}: {r['tflops_kernel']:.1f} TFLOP/s")
+            wps = workloads.Dense(wp.A[:256].copy(), wp.B, wp.sa, wp.sb, wp.a_fmt, wp.b_fmt, wp.name)
+            cpu_jobs.append(lambda wps=wps, M=M, N=N, K=K: cpu_dense(wps, 1.0, f"projection {M}x{N}x{K}", m_full=M))
             del wp
         extra["projections"] = out
 
@@ -651,13 +1004,26 @@ def main():
         log(f"  {r['gbs_kernel']:.0f} GB/s read+write")
 
     cpu = None
-    if not args.no_cpu and dense is not None:
-        log("timing the CPU oracle on a row sample")
-        cpu = cpu_baseline(wd)
+    if not args.no_cpu and cpu_jobs:
+        threads, aff = cpu_threads()
+        log(f"timing the CPU oracle on samples of {len(cpu_jobs)} configurations ({threads} threads)")
+        per_config = []
+        for job in cpu_jobs:
+            res = job()
+            log(f"  {res['config']}: {res['value']:.2f} {res['unit']} over {res['seconds']:.1f} s ({res['sample']})")
+            per_config.append(res)
+        head = per_config[0] if dense is not None else None
+        cpu = {"value": head["value"] / 1e3 if head else None, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": (f"{head['sample']} of the dense 4096^3 E4M3 problem, {head['seconds']:.1f} s on {threads} "
+                          f"host threads" if head else None),
+               "affinity_cpus": aff, "cpu_model": cpu_model(),
+               "threads_note": "the process's CPU affinity, capped by OMP_NUM_THREADS where set",
+               "per_config": per_config}
 
     if dense is None:
-        print(json.dumps({"metric": METRIC, "partial": True, **extra}))
+        print(json.dumps({"metric": METRIC, "partial": True, "cpu_baseline": cpu, **extra}))
         return
+    ctr = read_counters("dense_4096_e4m3")
     line = {
         "metric": METRIC,
         "value": dense["tflops_wall"],
@@ -675,8 +1041,11 @@ def main():
                                "entries N(0,1)*0.5, per-tensor scales U[0.5,2], FP32 accumulate, BF16 out (seed 2)",
                    "M": 4096, "N": 4096, "K": 4096},
         "roofline": {"bound": "mfma", "achieved": dense["tflops_kernel"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": dense["tflops_kernel"] / PEAK_FP8_TFLOPS, "traffic": read_traffic("dense_4096_e4m3"),
-                     "kernel_ms_mean": dense["kernel_ms_mean"],
+                     "frac": dense["tflops_kernel"] / PEAK_FP8_TFLOPS,
+                     "traffic": ctr.get("hbm_bytes_per_launch") if ctr else None,
+                     "kernel_ms_mean": dense["kernel_ms_mean"], **timing_fields(dense),
+                     "mfma_busy_fraction": ctr.get("mfma_busy_fraction") if ctr else None,
+                     "effective_clock_ghz": ctr.get("effective_clock_ghz") if ctr else None,
                      "algorithmic_flops": dense["flops"], "algorithmic_bytes": dense["bytes"]},
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),

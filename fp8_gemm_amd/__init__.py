@@ -35,7 +35,7 @@ class Fp8GemmError(RuntimeError):
 
 class Plan(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int), ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int),
-                ("token_blocks", ctypes.c_int), ("workgroups", ctypes.c_int64)]
+                ("token_blocks", ctypes.c_int), ("workgroups", ctypes.c_int64), ("k_splits", ctypes.c_int)]
 
 
 SYMBOLS = ("fp8_gemm_nt", "fp8_gemm_nt_blockscaled", "fp8_gemm_nt_channelwise",
@@ -161,9 +161,9 @@ def gemm_nt(a, b, scale_a, scale_b, out=None, a_dtype=None, b_dtype=None):
     lda = a.stride(0) if (M > 1 and K > 0) else max(16, ((K + 15) // 16) * 16)
     ldb = b.stride(0) if (N > 1 and K > 0) else max(16, ((K + 15) // 16) * 16)
     ldd = out.stride(0) if M > 1 else max(8, ((N + 7) // 8) * 8)
-    _check(load_library().fp8_gemm_nt(a.data_ptr(), lda, fa, b.data_ptr(), ldb, fb,
-                                      scale_a.data_ptr(), scale_b.data_ptr(), out.data_ptr(), ldd,
-                                      M, N, K, _stream()))
+    lib = load_library()
+    _check(lib.fp8_gemm_nt(a.data_ptr(), lda, fa, b.data_ptr(), ldb, fb, scale_a.data_ptr(), scale_b.data_ptr(), out.data_ptr(),
+              ldd, M, N, K, _stream()))
     return out
 
 

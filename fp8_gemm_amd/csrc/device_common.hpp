@@ -78,6 +78,15 @@ __device__ __forceinline__ void dma4(v4i srd, uint32_t voff, uint32_t lds_base) 
                  : "memory", "m0");
 }
 
+// The lane index (0..63), computed where it is called: the volatile
+// assembly is neither merged with an earlier computation nor hoisted out of
+// a loop, so the value is not kept live across the code in between.
+__device__ __forceinline__ int lane_id_here() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // s_waitcnt vmcnt(N) (N < 64), leaving the other counters unconstrained.
 template <int N>
 __device__ __forceinline__ void vmcnt_wait() {

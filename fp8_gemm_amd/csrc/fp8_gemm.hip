@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/fp8_gemm.h"
 #include "kernels.hpp"
 
@@ -32,7 +34,8 @@ int ok() {
 }
 
 constexpr int64_t kMaxRowStride = (int64_t(1) << 23) - 16;   // keeps 256 rows of offsets below 2^31
-constexpr int kSwapMaxM = 64;                                  // swap-AB threshold on the token count
+constexpr int kSwapMaxM = 64;                                  // swap-AB threshold of the dense form
+constexpr int kSwapWideMaxM = 192;                             // masked form: one pass over the weights up to here
 #ifndef SWAP_DEPTH
 #define SWAP_DEPTH 2
 #endif
@@ -70,12 +73,6 @@ enum Variant {
     V_NONE = 0, V_TILE_256x256 = 1, V_TILE_128x256 = 2, V_SWAP = 3, V_DECODE = 4, V_TILE_256x192 = 5, V_TILE_256x224 = 6
 };
 
-// Decode kernel: 16 weight rows per workgroup, or 32 where that still gives
-// at least 256 workgroups.  Every workgroup reads all M x K token bytes, so
-// fewer, larger row blocks cut the token traffic per CU (N = 14336: 896
-// workgroups of 16 rows read 3.5 copies of the tokens per CU, 448 of 32 rows
-// 1.75).
-int decode_rows_for(int64_t n) { return cdiv(n, 2 * kDecodeRows) >= 256 ? 2 * kDecodeRows : kDecodeRows; }
 
 // Swapped streaming kernel: 128 weight rows per wave (512 per workgroup), or
 // 64 when that would leave CUs idle (16 groups of N = 4096: 128 workgroups
@@ -85,7 +82,65 @@ int swap_wave_rows(int64_t groups, int64_t n) { return groups * cdiv(n, 4 * kSwa
 int token_blocks_for(int m) {
     if (m <= 16) return 1;
     if (m <= 32) return 2;
-    return 4;
+    if (m <= 64) return 4;
+    if (m <= 128) return 8;
+    return 12;
+}
+
+// Decode kernel (M <= 64): a workgroup takes 16 RB weight rows and the
+// 16 CB-row token blocks, over all K or over one split of the K steps.
+// Every workgroup reads all its split's token bytes, so fewer, larger row
+// blocks cut the token traffic per CU: 32 rows (RB = 2) where that still
+// leaves at least 256 workgroups (N = 14336: 896 workgroups of 16 rows read
+// 3.5 copies of the tokens per CU, 448 of 32 rows 1.75).  When the row blocks
+// are fewer than 256 (N < 4096), K is split over up to ceil(256 / blocks)
+// workgroups per block (at least 4 K steps each, one per wave) so the chip
+// stays full; their FP32 partial sums meet in a workspace (kSplitWs below).
+// With 256 blocks or more K is not split: measured at M = 64 and N = 4096, a
+// split over 4 workgroups of 64 rows (a quarter of the token traffic) took
+// 15.1 us against 12.1 unsplit, since each split's 14 K steps leave its load
+// latency, the partial-sum exchange and the last split's reads exposed.
+struct DecodeShape {
+    int rb, cb, blocks, splits, ksteps;
+};
+
+DecodeShape decode_shape(int64_t m, int64_t n, int64_t k) {
+    DecodeShape d;
+    d.cb = token_blocks_for((int)m);
+    d.rb = cdiv(n, 2 * kDecodeRows) >= 256 ? 2 : 1;
+    d.blocks = (int)cdiv(n, 16 * d.rb);
+    const int nk = (int)cdiv(k, 128);
+    d.splits = 1;
+    d.ksteps = nk;
+    if (d.blocks < 256 && nk >= 8) {
+        int want = (int)cdiv(256, d.blocks);
+        if (want > nk / 4) want = nk / 4;
+        if (want > 1) {
+            d.ksteps = (int)cdiv(nk, want);
+            d.splits = (int)cdiv(nk, d.ksteps);   // no empty split
+        }
+    }
+    return d;
+}
+
+// Workspace of the split-K few-token path, per device: the FP32 partial sums
+// of the splits (16 RB x 16 CB outputs, at most 64 x 64, per workgroup) and
+// one arrival count per block of weight rows.  Splits happen only with fewer
+// than 256 blocks, so blocks x splits < 256 + blocks < 512 workgroups: at most
+// 512 x 16 KiB of partial sums and 256 counts, whatever the shape.
+constexpr int kSplitMaxWgs = 512;
+constexpr int kSplitMaxBlocks = 256;
+constexpr size_t kSplitPartialBytes = (size_t)kSplitMaxWgs * 64 * 64 * sizeof(float);
+constexpr size_t kSplitWsBytes = kSplitPartialBytes + kSplitMaxBlocks * sizeof(int);
+
+// Masked form with 65..192 tokens per group ("wide"): 8 or 12 token blocks
+// in one pass over the weights, 64 weight rows per wave (the accumulators of
+// 12 blocks x 8 weight blocks would not fit a wave's registers).  The weights
+// stream from HBM once, as for few tokens; 128-row tiles read each group's
+// weights once per 128 tokens and were measured slower at 96 and 160 tokens
+// (the swap-AB benchmark table).
+int swap_rows_for(int64_t groups, int64_t n, int token_blocks) {
+    return token_blocks >= 8 ? kSwapWaveRows / 2 : swap_wave_rows(groups, n);
 }
 
 // Dense tiled kernel: pick the tile whose waves of 256 workgroups (one per CU)
@@ -112,11 +167,41 @@ int pick_dense_tile(int64_t M, int64_t N, bool allow_narrow) {
     return best;
 }
 
+void fill_decode_plan(int m, int n, int k, fp8g_plan *out) {
+    const DecodeShape d = decode_shape(m, n, k);
+    out->variant = V_DECODE;
+    out->tile_m = 16 * d.cb;
+    out->tile_n = 16 * d.rb;
+    out->token_blocks = d.cb;
+    out->k_splits = d.splits;
+    out->workgroups = (int64_t)d.blocks * d.splits;
+}
+
+// Small problems (M <= 256 where the tiled kernel would start at most 2
+// workgroups, as for 256^3): the decode kernel over 64-token tiles instead,
+// one workgroup per (16 weight rows, 64 tokens), K not split.  The work is
+// a few microseconds of latency either way; 64 workgroups load and store
+// their parts in parallel where 2 would each carry half of the problem.
+constexpr int kSmallMaxM = 256;
+constexpr int kSmallMaxTiles = 2;
+
+bool small_class(int m, int64_t tiled_workgroups) { return m > kSwapMaxM && m <= kSmallMaxM && tiled_workgroups <= kSmallMaxTiles; }
+
+void fill_small_plan(int m, int n, fp8g_plan *out) {
+    out->variant = V_DECODE;
+    out->tile_m = 64;
+    out->tile_n = 16;
+    out->token_blocks = 4;
+    out->k_splits = 1;
+    out->workgroups = cdiv(n, 16) * cdiv(m, 64);
+}
+
 int tile_m_of(int variant) { return variant == V_TILE_128x256 ? 128 : 256; }
 int tile_n_of(int variant) { return variant == V_TILE_256x192 ? 192 : variant == V_TILE_256x224 ? 224 : 256; }
 
 int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan *out) {
     memset(out, 0, sizeof *out);
+    out->k_splits = 1;
     if (m < 0 || n < 0 || k < 0 || groups < 0) return fail(FP8G_ERR_SHAPE, "negative size (m=%d n=%d k=%d groups=%d)", m, n, k, groups);
     // K in bytes: 16-byte chunks of the ring (BF16: 2 bytes per element)
     const int64_t kbytes = op == 4 ? 2 * (int64_t)k : k;
@@ -125,16 +210,13 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
     if (op == 0) {
         if (m == 0 || n == 0) return ok();
         if (m <= kSwapMaxM) {
-            out->variant = V_DECODE;
-            out->tile_m = 16 * token_blocks_for(m);
-            out->tile_n = decode_rows_for(n);
-            out->token_blocks = token_blocks_for(m);
-            out->workgroups = cdiv(n, out->tile_n);
+            fill_decode_plan(m, n, k, out);
         } else {
             out->variant = pick_dense_tile(m, n, true);
             out->tile_m = tile_m_of(out->variant);
             out->tile_n = tile_n_of(out->variant);
             out->workgroups = cdiv(m, out->tile_m) * cdiv(n, out->tile_n);
+            if (small_class(m, out->workgroups)) fill_small_plan(m, n, out);
         }
         return ok();
     }
@@ -143,11 +225,11 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
             return fail(FP8G_ERR_ARG, "expected_m=%d outside [0, cap=%d]", expected_m, m);
         if (groups == 0 || m == 0 || n == 0) return ok();
         const int hint = expected_m > 0 ? expected_m : m;
-        if (hint <= kSwapMaxM) {
+        if (hint <= kSwapWideMaxM) {
             out->variant = V_SWAP;
-            out->tile_m = 16 * token_blocks_for(hint);
-            out->tile_n = 4 * swap_wave_rows(groups, n);
             out->token_blocks = token_blocks_for(hint);
+            out->tile_m = 16 * out->token_blocks;
+            out->tile_n = 4 * swap_rows_for(groups, n, out->token_blocks);
             out->workgroups = (int64_t)groups * cdiv(n, out->tile_n);
         } else {
             out->variant = V_TILE_128x256;
@@ -157,15 +239,23 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
         }
         return ok();
     }
-    if (op == 2) {
+    if (op == 2 || op == 5) {
         if (m == 0 || n == 0) return ok();
         if (groups == 0) return fail(FP8G_ERR_SHAPE, "G=0 with M_total=%d rows", m);
-        // 256-row tiles, then one workgroup per tile for its second 128-row
-        // block, which computes only when that block's expert differs.
         out->variant = V_TILE_256x256;
         out->tile_m = 2 * kContigAlign;
         out->tile_n = 256;
-        out->workgroups = 2 * cdiv(m, 2 * kContigAlign) * cdiv(n, 256);
+        if (op == 2)
+            // 256-row tiles on the 8-wave kernel, then one workgroup per tile
+            // for its second 128-row block, which computes only when that
+            // block's expert differs
+            out->workgroups = 2 * cdiv(m, 2 * kContigAlign) * cdiv(n, 256);
+        else
+            // block scales: run-aligned 256-row tiles (128 rows at the end of
+            // a run with an odd number of 128-row blocks) on the 4-wave
+            // kernel; one workgroup per slot of two blocks computes the tiles
+            // that start in it
+            out->workgroups = cdiv(cdiv(m, kContigAlign), 2) * cdiv(n, 256);
         return ok();
     }
     if (op == 3) {
@@ -173,17 +263,14 @@ int plan_impl(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan
         // kernel (block scales applied per 128-byte K step of its ring).
         if (m == 0 || n == 0) return ok();
         if (m <= kSwapMaxM) {
-            out->variant = V_DECODE;
-            out->tile_m = 16 * token_blocks_for(m);
-            out->tile_n = decode_rows_for(n);
-            out->token_blocks = token_blocks_for(m);
-            out->workgroups = cdiv(n, out->tile_n);
+            fill_decode_plan(m, n, k, out);
             return ok();
         }
         out->variant = pick_dense_tile(m, n, false);
         out->tile_m = tile_m_of(out->variant);
         out->tile_n = 256;
         out->workgroups = cdiv(m, out->tile_m) * cdiv(n, 256);
+        if (small_class(m, out->workgroups)) fill_small_plan(m, n, out);
         return ok();
     }
     if (op == 4) {
@@ -264,22 +351,19 @@ int launch_tile16(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s)
 }
 
 // Tile shapes of the tiled kernels: 256 x 256 and 128 x 256 (and, below, 256 x
-// 224 and 256 x 192 for dense FP8 without block scales).  Dense FP8 (any scale
-// form) runs on 4 waves and the 16x16x128 instruction (2-slot ring, 128 KB of
-// LDS, for 256 rows; 3-slot, 144 KB, for 128 rows); BF16 and the grouped forms
-// on 8 waves and 32x32x64 (4 x 2 waves and a 2-slot ring for 256 rows, 2 x 4
-// and 3 slots for 128).
+// 224 and 256 x 192 for dense FP8 without block scales).  FP8 (dense forms and
+// the contiguous grouped form) runs on 4 waves and the 16x16x128 instruction
+// (2-slot ring, 128 KB of LDS, for 256 rows; 3-slot, 144 KB, for 128 rows);
+// BF16 and the masked grouped form's tiles on 8 waves and 32x32x64 (4 x 2
+// waves and a 2-slot ring for 256 rows, 2 x 4 and 3 slots for 128).
 template <int MODE, int SCL = 0>
 int launch_tile256(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    if constexpr (MODE == fp8g::MODE_DENSE) {
-        if (fa != fp8g::FMT_BF16) return launch_tile16<256, 2, MODE, SCL>(fa, fb, p, grid, s);
-        if constexpr (SCL == fp8g::SCALE_TENSOR)
-            return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE, SCL, true>(fa, fb, p, grid, s);
-        else
-            return fail(FP8G_ERR_ARG, "BF16 operands take no scales");
-    } else {
-        return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE, SCL>(fa, fb, p, grid, s);
-    }
+    static_assert(MODE == fp8g::MODE_DENSE, "256-row tiles of the dense forms");
+    if (fa != fp8g::FMT_BF16) return launch_tile16<256, 2, MODE, SCL>(fa, fb, p, grid, s);
+    if constexpr (SCL == fp8g::SCALE_TENSOR)
+        return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, MODE, SCL, true>(fa, fb, p, grid, s);
+    else
+        return fail(FP8G_ERR_ARG, "BF16 operands take no scales");
 }
 // 256 x 224 and 256 x 192 tiles: dense FP8 with per-tensor or per-channel scales.
 template <int SCL>
@@ -325,6 +409,8 @@ int launch_swap_wr(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipSt
 template <int MODE, int SCL = 0>
 int launch_swap(const fp8g_plan &plan, int fa, int fb, const GemmParams &p, hipStream_t s) {
     const dim3 grid((unsigned)plan.workgroups);
+    if (plan.token_blocks == 8) return launch_swap_cb<kSwapWaveRows / 2, 8, MODE, SCL>(fa, fb, p, grid, s);
+    if (plan.token_blocks == 12) return launch_swap_cb<kSwapWaveRows / 2, 12, MODE, SCL>(fa, fb, p, grid, s);
     if (plan.tile_n == 4 * kSwapWaveRows) return launch_swap_wr<kSwapWaveRows, MODE, SCL>(plan.token_blocks, fa, fb, p, grid, s);
     return launch_swap_wr<kSwapWaveRows / 2, MODE, SCL>(plan.token_blocks, fa, fb, p, grid, s);
 }
@@ -332,9 +418,48 @@ int launch_swap(const fp8g_plan &plan, int fa, int fb, const GemmParams &p, hipS
 // Decode kernel: 4 waves per workgroup and per-wave LDS rings, as deep as fits
 // in 80 KB so that two workgroups share a CU: 5, 3 or 2 steps for 1, 2 or 4
 // token blocks with one weight block, 3, 2, 2 with two (the last needs 96 KB:
-// one workgroup per CU).  Measured best against 8 waves and deeper rings with
-// one workgroup per CU.  Block scales add 512 bytes per slot.
+// one workgroup per CU).  Measured best against 8 waves and against deeper
+// rings with one workgroup per CU: rings of 8, 6 and 4 steps (160 KB) where
+// the grid is at most one workgroup per CU took 7.97 / 12.97 us at M = 1 / 64,
+// N = 4096, K = 7168, against 7.39 / 12.34 us with these.  Block scales add
+// 512 bytes per slot.
 constexpr int kDecodeWaves = 4;
+
+// The split-K workspace of each device, allocated (and its counts zeroed) by
+// the first call on that device that splits K; the kernels leave the counts
+// at zero again.  Calls that split K and overlap on one device share it.
+struct SplitWs {
+    float *partial = nullptr;
+    int *count = nullptr;
+};
+std::mutex g_ws_mutex;
+SplitWs g_ws[64];
+
+// The device's workspace in `ws`, or none (ws.partial == NULL: the caller does
+// not split K) when it does not exist yet and `stream` is being captured into
+// a graph, where no allocation may happen.
+int split_workspace(hipStream_t stream, SplitWs &ws) {
+    ws = SplitWs{};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(FP8G_ERR_UNSUPPORTED, "no usable HIP device");
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if (!g_ws[dev].partial) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return ok();
+        void *mem = nullptr;
+        if (hipMalloc(&mem, kSplitWsBytes) != hipSuccess)
+            return fail(FP8G_ERR_LAUNCH, "cannot allocate the %zu-byte split-K workspace", kSplitWsBytes);
+        int *count = reinterpret_cast<int *>(static_cast<char *>(mem) + kSplitPartialBytes);
+        if (hipMemsetAsync(count, 0, kSplitMaxBlocks * sizeof(int), stream) != hipSuccess) {
+            (void)hipFree(mem);
+            return fail(FP8G_ERR_LAUNCH, "cannot clear the split-K workspace");
+        }
+        g_ws[dev].partial = static_cast<float *>(mem);
+        g_ws[dev].count = count;
+    }
+    ws = g_ws[dev];
+    return ok();
+}
 
 template <int RB, int CB, int SCL>
 int launch_decode_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
@@ -357,11 +482,33 @@ int launch_decode_rb(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hip
     return launch_decode_cb<RB, 4, SCL>(fa, fb, p, grid, s);
 }
 
+// K split as the plan says when `ws` holds a workspace, else over the 4 waves
+// only.
 template <int SCL>
-int launch_decode(const fp8g_plan &plan, int fa, int fb, const GemmParams &p, hipStream_t s) {
-    const dim3 grid((unsigned)plan.workgroups);
-    if (plan.tile_n == 2 * kDecodeRows) return launch_decode_rb<2, SCL>(plan.token_blocks, fa, fb, p, grid, s);
-    return launch_decode_rb<1, SCL>(plan.token_blocks, fa, fb, p, grid, s);
+int launch_decode(const fp8g_plan &plan, int fa, int fb, GemmParams p, const SplitWs &ws, hipStream_t s) {
+    const int rb = plan.tile_n / 16, cb = plan.token_blocks;
+    int64_t wgs = plan.workgroups;
+    p.splits = 1;
+    if (plan.k_splits > 1 && ws.partial) {
+        p.splits = plan.k_splits;
+        p.ksteps = (int)cdiv(cdiv(p.K, 128), plan.k_splits);
+        p.ws = ws.partial;
+        p.cnt = ws.count;
+    } else {
+        wgs /= plan.k_splits;
+    }
+    // token tiles along y: all M at once for M <= 64, else 64-row tiles
+    const unsigned mtiles = p.M > kSwapMaxM ? (unsigned)cdiv(p.M, 64) : 1u;
+    const dim3 grid((unsigned)(wgs / mtiles), mtiles);
+    if (rb == 2) return launch_decode_rb<2, SCL>(cb, fa, fb, p, grid, s);
+    return launch_decode_rb<1, SCL>(cb, fa, fb, p, grid, s);
+}
+
+// The workspace a decode plan needs (none unless it splits K).
+int decode_workspace(const fp8g_plan &plan, hipStream_t s, SplitWs &ws) {
+    ws = SplitWs{};
+    if (plan.variant != V_DECODE || plan.k_splits <= 1) return ok();
+    return split_workspace(s, ws);
 }
 
 }  // namespace
@@ -394,9 +541,14 @@ int fp8_gemm_plan(int op, int m, int n, int k, int groups, int expected_m, fp8g_
     return plan_impl(op, m, n, k, groups, expected_m, out);
 }
 
-int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t ldb, int b_dtype,
-                const float *scale_a, const float *scale_b, void *D, int64_t ldd, int M, int N, int K,
-                void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The body of fp8_gemm_nt.
+int gemm_nt_impl(const void *A, int64_t lda, int a_dtype, const void *B, int64_t ldb, int b_dtype,
+                 const float *scale_a, const float *scale_b, void *D, int64_t ldd, int M, int N, int K,
+                 void *stream) {
     if (!dtype_ok(a_dtype) || !dtype_ok(b_dtype)) return fail(FP8G_ERR_DTYPE, "dtypes %d, %d", a_dtype, b_dtype);
     fp8g_plan plan;
     int st = plan_impl(0, M, N, K, 1, 0, &plan);
@@ -422,8 +574,12 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t 
     p.scale_a = scale_a; p.scale_b = scale_b;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int fa = a_dtype, fb = b_dtype;
-    if (plan.variant == V_DECODE)
-        return launch_decode<fp8g::SCALE_TENSOR>(plan, fa, fb, p, s);
+    if (plan.variant == V_DECODE) {
+        SplitWs ws;
+        st = decode_workspace(plan, s, ws);
+        if (st != FP8G_OK) return st;
+        return launch_decode<fp8g::SCALE_TENSOR>(plan, fa, fb, p, ws, s);
+    }
     p.tiles_m = (int)cdiv(M, plan.tile_m);
     p.tiles_n = (int)cdiv(N, plan.tile_n);
     const dim3 grid((unsigned)plan.workgroups);
@@ -431,6 +587,16 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t 
     if (plan.variant == V_TILE_256x192 || plan.variant == V_TILE_256x224)
         return launch_tile256_narrow<fp8g::SCALE_TENSOR>(plan.variant, fa, fb, p, grid, s);
     return launch_tile128<fp8g::MODE_DENSE>(fa, fb, p, grid, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t ldb, int b_dtype,
+                const float *scale_a, const float *scale_b, void *D, int64_t ldd, int M, int N, int K,
+                void *stream) {
+    return gemm_nt_impl(A, lda, a_dtype, B, ldb, b_dtype, scale_a, scale_b, D, ldd, M, N, K, stream);
 }
 
 int bf16_gemm_nt(const void *A, int64_t lda, const void *B, int64_t ldb, void *D, int64_t ldd, int M, int N, int K,
@@ -576,7 +742,10 @@ int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dty
     hipStream_t s = static_cast<hipStream_t>(stream);
     p.tiles_m = (int)cdiv(M_total, 2 * kContigAlign);
     p.tiles_n = (int)cdiv(N, 256);
-    return launch_tile256<fp8g::MODE_CONTIG>(a_dtype, b_dtype, p, dim3((unsigned)plan.workgroups), s);
+    // 8 waves: measured faster than the 4-wave kernel here (every expert's
+    // weights stream from HBM); block scales are the other way round.
+    return launch_ring<256, 256, T256_WM, T256_WN, T256_ST, T256_BK, fp8g::MODE_CONTIG, fp8g::SCALE_TENSOR>(
+        a_dtype, b_dtype, p, dim3((unsigned)plan.workgroups), s);
 }
 
 int fp8_gemm_nt_blockscaled(const void *A, int64_t lda, int a_dtype, const void *B, int64_t ldb, int b_dtype,
@@ -614,7 +783,11 @@ int fp8_gemm_nt_blockscaled(const void *A, int64_t lda, int a_dtype, const void 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int fa = a_dtype, fb = b_dtype;
     const dim3 grid((unsigned)plan.workgroups);
-    if (plan.variant == V_DECODE) return launch_decode<fp8g::SCALE_BLOCK>(plan, fa, fb, p, s);
+    if (plan.variant == V_DECODE) {
+        SplitWs ws;
+        if ((st = decode_workspace(plan, s, ws)) != FP8G_OK) return st;
+        return launch_decode<fp8g::SCALE_BLOCK>(plan, fa, fb, p, ws, s);
+    }
     p.tiles_m = (int)cdiv(M, plan.tile_m);
     p.tiles_n = (int)cdiv(N, plan.tile_n);
     if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE, fp8g::SCALE_BLOCK>(fa, fb, p, grid, s);
@@ -650,7 +823,11 @@ int fp8_gemm_nt_channelwise(const void *A, int64_t lda, int a_dtype, const void 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int fa = a_dtype, fb = b_dtype;
     const dim3 grid((unsigned)plan.workgroups);
-    if (plan.variant == V_DECODE) return launch_decode<fp8g::SCALE_CHANNEL>(plan, fa, fb, p, s);
+    if (plan.variant == V_DECODE) {
+        SplitWs ws;
+        if ((st = decode_workspace(plan, s, ws)) != FP8G_OK) return st;
+        return launch_decode<fp8g::SCALE_CHANNEL>(plan, fa, fb, p, ws, s);
+    }
     p.tiles_m = (int)cdiv(M, plan.tile_m);
     p.tiles_n = (int)cdiv(N, plan.tile_n);
     if (plan.variant == V_TILE_256x256) return launch_tile256<fp8g::MODE_DENSE, fp8g::SCALE_CHANNEL>(fa, fb, p, grid, s);
@@ -666,7 +843,7 @@ int fp8_grouped_gemm_contig_blockscaled(const void *A, int a_dtype, const void *
     if (!dtype_ok(a_dtype) || !dtype_ok(b_dtype)) return fail(FP8G_ERR_DTYPE, "dtypes %d, %d", a_dtype, b_dtype);
     if (G < 0 || M_total < 0) return fail(FP8G_ERR_SHAPE, "negative G=%d or M_total=%d", G, M_total);
     fp8g_plan plan;
-    int st = plan_impl(2, M_total, N, K, G, 0, &plan);
+    int st = plan_impl(5, M_total, N, K, G, 0, &plan);
     if (st != FP8G_OK) return st;
     if (plan.variant == V_NONE) return ok();
     if ((K > 0 && (!A || !B || !scale_a || !scale_b)) || !D || !grp_idx)
@@ -694,9 +871,10 @@ int fp8_grouped_gemm_contig_blockscaled(const void *A, int a_dtype, const void *
     p.grp_idx = grp_idx;
     p.sfa = scale_a; p.sfb = scale_b; p.lds_sa = lds_a; p.lds_sb = lds_b;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    p.tiles_m = (int)cdiv(M_total, 2 * kContigAlign);
+    p.tiles_m = (int)cdiv(cdiv(M_total, kContigAlign), 2);
     p.tiles_n = (int)cdiv(N, 256);
-    return launch_tile256<fp8g::MODE_CONTIG, fp8g::SCALE_BLOCK>(a_dtype, b_dtype, p, dim3((unsigned)plan.workgroups), s);
+    return launch_tile16<256, 2, fp8g::MODE_CONTIG, fp8g::SCALE_BLOCK>(a_dtype, b_dtype, p,
+                                                                     dim3((unsigned)plan.workgroups), s);
 }
 
 }  // extern "C"

@@ -11,12 +11,12 @@
 //                  output tile per workgroup of 4 waves on v_mfma 16x16x128, K in steps of 128
 //                  bytes, both operand tiles staged through a direct-to-LDS,
 //                  XOR-swizzled ring.  Dense FP8 (M > 64) with per-tensor,
-//                  per-channel or block scales.
+//                  per-channel or block scales; contiguous grouped FP8 (also
+//                  block-scaled) on run-aligned 256 x 256 tiles.
 //   ring_kernel    the same ring with 8 waves on v_mfma 32x32x64, BM x BN
-//                  = 256 x 256 or 128 x 256: masked grouped with many rows per
-//                  group, contiguous grouped (both also block-scaled), and the
-//                  BF16 comparison path (same bytes, two v_mfma 32x32x16 BF16
-//                  per fragment).
+//                  = 256 x 256 or 128 x 256: masked grouped with more than 192
+//                  rows per group (also block-scaled), and the BF16 comparison
+//                  path (same bytes, two v_mfma 32x32x16 BF16 per fragment).
 //   swap_kernel    streaming "swap-AB" form for few tokens: each wave streams
 //                  its own weight rows (every weight byte is used by exactly
 //                  one wave) through a private LDS ring into the 16x16x128
@@ -66,6 +66,13 @@ struct GemmParams {
     // Per-channel form: row scales of A [M], channel scales [N] and bias [N]
     // (each may be NULL: 1, 1, 0).
     const float *ch_sa, *ch_sb, *bias;
+    // Few-token form with K split over workgroups (splits > 1): `splits`
+    // workgroups per block of weight rows take `ksteps` 128-byte K steps each,
+    // leave their FP32 partial sums in ws, and count their arrivals in
+    // cnt[block]; the last to arrive adds the partial sums in split order.
+    float *ws;
+    int *cnt;
+    int splits, ksteps;
 };
 
 // Epilogue terms of the per-channel form for four consecutive output channels
@@ -142,11 +149,10 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 }
 
 // ---------------------------------------------------------------------------
-// Placement of one output tile of the tiled kernels: tile coordinates, group,
-// expert, first row and the valid rows and columns.  Returns false when the
-// workgroup has nothing to compute (masked tile past the group's count,
-// all-padding contiguous block, or a second-block workgroup whose block needs
-// no separate pass).
+// Placement of one output tile of the tiled kernels (dense and masked forms):
+// tile coordinates, group, first row and the valid rows and columns.  Returns
+// false when the workgroup has nothing to compute (masked tile past the
+// group's count).
 // ---------------------------------------------------------------------------
 struct TileSpot {
     int tm, tn, g, m0, rows_m, n0, rows_n, expert;
@@ -154,13 +160,15 @@ struct TileSpot {
 
 template <int BM, int BN, int MODE>
 __device__ __forceinline__ bool place_tile(const GemmParams &p, int lane, TileSpot &t) {
+    static_assert(MODE != MODE_CONTIG, "contiguous grouped form: place_contig_tile");
+    (void)lane;
     t.g = 0;
     t.expert = 0;
     if (MODE == MODE_DENSE) {
         tile_coords<false>(blockIdx.x, p.tiles_m, p.tiles_n, t.tm, t.tn);
         t.m0 = t.tm * BM;
         t.rows_m = min(p.M - t.m0, BM);
-    } else if (MODE == MODE_MASKED) {
+    } else {
         t.tm = blockIdx.x / p.tiles_n;
         t.tn = blockIdx.x % p.tiles_n;
         t.g = blockIdx.y;
@@ -169,54 +177,170 @@ __device__ __forceinline__ bool place_tile(const GemmParams &p, int lane, TileSp
         if (t.m0 >= mg) return false;              // nothing valid in this tile: no load at all
         t.rows_m = min(mg - t.m0, BM);
         t.expert = t.g;
-    } else {
-        // The expert of a block of rows is that of its first row naming a
-        // valid expert; a block with none is all padding.  Rows of any other
-        // expert in the block are not written by this tile.
-        auto first_expert = [&](int r0, int nrows) {
-            for (int base = 0; base < nrows; base += 64) {
-                const int r = base + lane;
-                int e = -1;
-                if (r < nrows) e = p.grp_idx[r0 + r];
-                const bool ok = (e >= 0) && (e < p.G);
-                const unsigned long long ball = __ballot(ok);
-                if (ball) return __builtin_amdgcn_readfirstlane(__shfl(e, __builtin_ctzll(ball)));
-            }
-            return -1;
-        };
-        const int ntiles = p.tiles_m * p.tiles_n;
-        if (BM != 256 || (int)blockIdx.x < ntiles) {
-            tile_coords<true>(blockIdx.x, p.tiles_m, p.tiles_n, t.tm, t.tn);
-            t.m0 = t.tm * BM;
-            t.rows_m = min(p.M - t.m0, BM);
-            t.expert = first_expert(t.m0, t.rows_m);
-            if (t.expert < 0) return false;
-        } else {
-            // A 256-row tile covers two 128-row blocks, each of at most one
-            // expert, and writes the rows of the expert of its first valid
-            // row.  The second half of the grid (one workgroup per tile)
-            // covers the second block when its expert differs: it computes
-            // that block alone (tile rows 128..255 read zeros).  These
-            // workgroups come last in dispatch order, where the last partial
-            // wave of full tiles leaves CUs idle.
-            const int w2 = blockIdx.x - ntiles;
-            t.tm = w2 / p.tiles_n;
-            t.tn = w2 % p.tiles_n;
-            const int base = t.tm * BM;
-            const int r2 = min(p.M - (base + 128), 128);
-            if (r2 <= 0) return false;
-            const int e1 = first_expert(base, min(p.M - base, BM));
-            const int e2 = first_expert(base + 128, r2);
-            if (e2 < 0 || e2 == e1) return false;
-            t.m0 = base + 128;
-            t.rows_m = r2;
-            t.expert = e2;
-        }
     }
     t.n0 = t.tn * BN;
     t.rows_n = min(p.N - t.n0, BN);
     return true;
 }
+
+// ---------------------------------------------------------------------------
+// Paired tiles of the contiguous grouped form (8-wave kernel).
+// A 256-row tile covers two 128-row blocks, each of at most one expert, and
+// writes the rows of the expert of its first valid row.  A second set of
+// workgroups, one per tile, appended to the grid, covers the second block
+// when its expert differs: it computes that block alone (tile rows 128..255
+// read zeros).  They come last in dispatch order, where the last partial
+// wave of full tiles leaves CUs idle.  Measured against run-aligned tiles on
+// the 8-wave kernel (fewer tiles, 4384 against 4480 tile passes on the
+// 65536-row prefill, but up to two per workgroup): 1.72 against 1.78 ms.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool place_contig_pair(const GemmParams &p, int lane, TileSpot &t) {
+    // the expert of a block of rows: that of its first row naming a valid
+    // expert, -1 for a block of padding only
+    auto first_expert = [&](int r0, int nrows) {
+        for (int base = 0; base < nrows; base += 64) {
+            const int r = base + lane;
+            int e = -1;
+            if (r < nrows) e = p.grp_idx[r0 + r];
+            const bool ok = (e >= 0) && (e < p.G);
+            const unsigned long long ball = __ballot(ok);
+            if (ball) return __builtin_amdgcn_readfirstlane(__shfl(e, __builtin_ctzll(ball)));
+        }
+        return -1;
+    };
+    const int ntiles = p.tiles_m * p.tiles_n;
+    t.g = 0;
+    if ((int)blockIdx.x < ntiles) {
+        tile_coords<true>(blockIdx.x, p.tiles_m, p.tiles_n, t.tm, t.tn);
+        t.m0 = t.tm * 256;
+        t.rows_m = min(p.M - t.m0, 256);
+        t.expert = first_expert(t.m0, t.rows_m);
+        if (t.expert < 0) return false;
+    } else {
+        const int w2 = blockIdx.x - ntiles;
+        t.tm = w2 / p.tiles_n;
+        t.tn = w2 % p.tiles_n;
+        const int base = t.tm * 256;
+        const int r2 = min(p.M - (base + 128), 128);
+        if (r2 <= 0) return false;
+        const int e1 = first_expert(base, min(p.M - base, 256));
+        const int e2 = first_expert(base + 128, r2);
+        if (e2 < 0 || e2 == e1) return false;
+        t.m0 = base + 128;
+        t.rows_m = r2;
+        t.expert = e2;
+    }
+    t.n0 = t.tn * 256;
+    t.rows_n = min(p.N - t.n0, 256);
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Run-aligned tiles of the contiguous grouped form (4-wave kernel).
+// The rows of one expert form a run of consecutive 128-row blocks.  Each run
+// is covered by 256-row tiles from its first block on, the last one 128 rows
+// when the run has an odd number of blocks, so no tile holds two experts and
+// no block is computed twice.  A tile therefore starts at block b when b holds
+// an expert and lies an even number of blocks past the start of its run.
+// Workgroup slot t (of ceil(blocks / 2)) computes the tiles starting at blocks
+// 2t and 2t + 1: zero, one or two of them.  Nothing is planned on the host, so
+// the per-expert counts never leave the device.
+// ---------------------------------------------------------------------------
+// The expert of 128-row block b: that of its first row naming a valid expert,
+// or -1 when the block is all padding.
+__device__ __forceinline__ int contig_block_expert(const GemmParams &p, int b) {
+    const int r0 = b * 128;
+    const int n = min(128, p.M - r0);
+    for (int i = 0; i < n; ++i) {
+        const int e = p.grp_idx[r0 + i];
+        if (e >= 0 && e < p.G) return e;
+    }
+    return -1;
+}
+
+// The tiles of this workgroup's slot t (blocks 2t, 2t + 1): found once, with
+// one load per lane: lane l reads the expert of block 2t + 2 - l, which covers
+// the next block after the slot (does a tile's run go on?) and 61 blocks
+// before it (where does the run start?); longer runs take further rounds of 64
+// blocks.  Returns, per pass (0: block 2t, 1: block 2t + 1), the tile's
+// expert (or -1 when no tile starts there) and its number of blocks.
+struct ContigSlot {
+    int expert[2], nblk[2];
+};
+
+__device__ __forceinline__ ContigSlot contig_slot_tiles(const GemmParams &p, int lane, int t) {
+    const int nb = (p.M + 127) / 128;
+    const int b0 = 2 * t;
+    auto expert_of = [&](int b) { return b >= 0 && b < nb ? contig_block_expert(p, b) : -1; };
+    const int el = expert_of(b0 + 2 - lane);
+    // blocks 2t + 2, 2t + 1, 2t
+    const int e2 = __builtin_amdgcn_readfirstlane(__shfl(el, 0));
+    const int e1 = __builtin_amdgcn_readfirstlane(__shfl(el, 1));
+    const int e0 = __builtin_amdgcn_readfirstlane(__shfl(el, 2));
+    // dist = blocks of expert e0 just before block 2t (its run start is 2t - dist)
+    int dist = 0;
+    if (e0 >= 0) {
+        unsigned long long other = __ballot(lane >= 3 && el != e0);
+        if (other) {
+            dist = __builtin_ctzll(other) - 3;
+        } else {
+            dist = 61;
+            for (int base = b0 - 62;; base -= 64) {
+                const unsigned long long o = __ballot(expert_of(base - lane) != e0);
+                if (o) {
+                    dist += __builtin_ctzll(o);
+                    break;
+                }
+                dist += 64;
+            }
+        }
+    }
+    ContigSlot s;
+    // a tile starts at 2t when it holds an expert an even number of blocks
+    // into its run; at 2t + 1 when it starts a run, or continues 2t's run
+    // from an odd distance
+    const bool at0 = e0 >= 0 && (dist & 1) == 0;
+    const bool at1 = e1 >= 0 && (e1 != e0 || (dist & 1) == 1);
+    // (uniform values, kept in scalar registers across the passes)
+    s.expert[0] = __builtin_amdgcn_readfirstlane(at0 ? e0 : -1);
+    s.nblk[0] = __builtin_amdgcn_readfirstlane(e1 == e0 ? 2 : 1);
+    s.expert[1] = __builtin_amdgcn_readfirstlane(at1 ? e1 : -1);
+    s.nblk[1] = __builtin_amdgcn_readfirstlane(e2 == e1 ? 2 : 1);
+    return s;
+}
+
+// Placement of the tile of this workgroup's slot that starts at block
+// 2t + pass, if any.
+__device__ __forceinline__ bool place_contig_tile(const GemmParams &p, const ContigSlot &cs, int pass, TileSpot &t) {
+    tile_coords<true>(blockIdx.x, p.tiles_m, p.tiles_n, t.tm, t.tn);
+    const int e = cs.expert[pass];
+    if (e < 0) return false;
+    t.g = 0;
+    t.expert = e;
+    t.m0 = (2 * t.tm + pass) * 128;
+    t.rows_m = min(p.M - t.m0, 128 * cs.nblk[pass]);
+    t.n0 = t.tn * 256;
+    t.rows_n = min(p.N - t.n0, 256);
+    return true;
+}
+
+// Rows of a contiguous-form tile that belong to its expert: BM / 64 masks of
+// 64 bits (bit r % 64 of mask r / 64 is row r of the tile), written to LDS
+// with one ballot per 64 rows before the main loop (whose barriers publish
+// them).  The epilogue's stores then test a bit; loading grp_idx for the row
+// of every 16-byte chunk made each store wait on a global load.
+template <int BM, int WAVES>
+__device__ __forceinline__ void contig_row_mask(const GemmParams &p, const TileSpot &t, int wave, int lane,
+                                                uint64_t *mask) {
+    for (int g = wave; g < BM / 64; g += WAVES) {
+        const int r = g * 64 + lane;
+        const bool mine = r < t.rows_m && p.grp_idx[t.m0 + r] == t.expert;
+        const uint64_t bits = __ballot(mine);
+        if (lane == 0) mask[g] = bits;
+    }
+}
+
+__device__ __forceinline__ bool row_in_mask(const uint64_t *mask, int r) { return (mask[r >> 6] >> (r & 63)) & 1; }
 
 // Stored position of 16-byte chunk c of staged output row r (OCH chunks per
 // row): c ^ (r % OCH) when OCH is a power of two, else (c + r) % OCH.  Either
@@ -247,10 +371,11 @@ __device__ __forceinline__ void store_chunk(uint16_t *dst, v4u v, int nvalid) {
 
 // Write a BF16 output tile staged in LDS (row r at r * BN * 2 bytes, 16-byte
 // chunk c stored at stage_chunk(c, r)) with 16-byte stores of whole row
-// segments; the contiguous form writes only the rows of the tile's expert.
+// segments; the contiguous form writes only the rows of the tile's expert
+// (rowmask, see contig_row_mask).
 template <int BM, int BN, int THREADS, int MODE>
 __device__ __forceinline__ void store_staged(const GemmParams &p, const uint8_t *smem, int tid, const TileSpot &t,
-                                             uint16_t *d_base) {
+                                             uint16_t *d_base, const uint64_t *rowmask = nullptr) {
     constexpr int OCH = BN / 8;
     constexpr int OUT_CHUNKS = BM * OCH;
     static_assert(OUT_CHUNKS % THREADS == 0, "staged tile splits evenly over the threads");
@@ -260,7 +385,7 @@ __device__ __forceinline__ void store_staged(const GemmParams &p, const uint8_t 
         const int c = q % OCH;
         if (r >= t.rows_m) continue;
         const int m = t.m0 + r;
-        if (MODE == MODE_CONTIG && p.grp_idx[m] != t.expert) continue;
+        if (MODE == MODE_CONTIG && !row_in_mask(rowmask, r)) continue;
         const int n = t.n0 + c * 8;
         const v4u v = *reinterpret_cast<const v4u *>(smem + r * (BN * 2) + stage_chunk<OCH>(c, r) * 16);
         store_chunk<MODE>(d_base + (int64_t)m * p.ldd + n, v, p.N - n);
@@ -312,10 +437,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
     static_assert(SCL != SCALE_CHANNEL, "per-channel scales: tile16_kernel");
     constexpr int SCS = BLK ? 512 : 0;
     constexpr int RING = STAGES * (SLOT + SCS);
-    constexpr int SMEM = RING > STAGE_OUT ? RING : STAGE_OUT;
+    constexpr int MASK_AT = RING > STAGE_OUT ? RING : STAGE_OUT;   // contiguous form: the tile's row mask
+    constexpr int SMEM = MASK_AT + (MODE == MODE_CONTIG ? BM / 8 : 0);
     constexpr int THREADS = 64 * WAVES;
     constexpr int OCH = BN / 8;                    // 16-byte chunks per staged output row
     static_assert(OCH == 32 || OCH == 16, "staged row width");
+    static_assert(MODE != MODE_CONTIG || (BM == 256 && BN == 256), "contiguous grouped form: 256 x 256 tiles");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
@@ -327,9 +454,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
 
     // ---- tile coordinates and per-mode operand bases (64-bit arithmetic) ----
     TileSpot spot;
-    if (!place_tile<BM, BN, MODE>(p, lane, spot)) return;
+    if constexpr (MODE == MODE_CONTIG) {
+        if (!place_contig_pair(p, lane, spot)) return;
+    } else {
+        if (!place_tile<BM, BN, MODE>(p, lane, spot)) return;
+    }
     const int g = spot.g, m0 = spot.m0, rows_m = spot.rows_m, expert = spot.expert;
     const int n0 = spot.n0, rows_n = spot.rows_n;
+    uint64_t *const rowmask = reinterpret_cast<uint64_t *>(smem + MASK_AT);
+    if constexpr (MODE == MODE_CONTIG) contig_row_mask<BM, WAVES>(p, spot, wave, lane, rowmask);
     uint16_t *d_base = p.D + (MODE == MODE_MASKED ? (int64_t)g * p.d_gstride : 0);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
 
@@ -605,7 +738,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ring_kernel(GemmParams p) {
         }
     }
     __syncthreads();
-    store_staged<BM, BN, THREADS, MODE>(p, smem, tid, spot, d_base);
+    store_staged<BM, BN, THREADS, MODE>(p, smem, tid, spot, d_base, rowmask);
 }
 
 // ---------------------------------------------------------------------------
@@ -645,7 +778,8 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     // The contiguous grouped form stays on ring_kernel: there, with every
     // expert's weights streaming from HBM, this kernel measured 4% slower
     // (1.90 against 1.82 ms on the 65536-row prefill).
-    static_assert(FA != FMT_BF16 && FB != FMT_BF16 && MODE == MODE_DENSE, "FP8 operands, dense form");
+    static_assert(FA != FMT_BF16 && FB != FMT_BF16 && (MODE == MODE_DENSE || (MODE == MODE_CONTIG && BM == 256 && BN == 256)),
+                  "FP8 operands; dense form, or contiguous grouped with 256 x 256 tiles");
     constexpr int BK = 128, WM = 2, WN = 2, WAVES = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;      // 128 (or 64) x 128 outputs per wave
     constexpr int FM = TM / 16, FN = TN / 16;      // token blocks, weight blocks
@@ -660,7 +794,8 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     // step's K block of each 128-row block of B (from byte 256).
     constexpr int SCS = BLK ? 512 : 0;
     constexpr int RING = STAGES * (SLOT + SCS);
-    constexpr int SMEM = RING > STAGE_OUT ? RING : STAGE_OUT;
+    constexpr int MASK_AT = RING > STAGE_OUT ? RING : STAGE_OUT;   // contiguous form: the tile's row mask
+    constexpr int SMEM = MASK_AT + (MODE == MODE_CONTIG ? BM / 8 : 0);
     constexpr int THREADS = 64 * WAVES;
     constexpr int OCH = BN / 8;
     constexpr int HALF = FN * FM / 2;              // MFMAs per half step
@@ -678,20 +813,42 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
-    const int tid = threadIdx.x;
+    // The contiguous grouped form computes up to two run-aligned tiles per
+    // workgroup (place_contig_tile), one after the other; the dense form one.
+    constexpr int PASSES = MODE == MODE_CONTIG ? 2 : 1;
+    const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    ContigSlot cs{};
+    if constexpr (MODE == MODE_CONTIG) {
+        int tm, tn;
+        tile_coords<true>(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+        cs = contig_slot_tiles(p, lane_id_here(), tm);
+    }
+#pragma unroll 1
+    for (int pass = 0; pass < PASSES; ++pass) {
+    // With two passes the lane index is taken afresh in each (lane_id_here),
+    // so that nothing derived from it (copy and fragment offsets) is hoisted
+    // out of the loop and kept live next to the accumulators; threadIdx.x
+    // itself would have to stay live since the kernel's start.
+    const int tid = PASSES > 1 ? wave0 * 64 + lane_id_here() : (int)threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = wave0;
     const int wm = wave % WM;
     const int wn = wave / WM;
-
     TileSpot spot;
-    if (!place_tile<BM, BN, MODE>(p, lane, spot)) return;
+    if constexpr (MODE == MODE_CONTIG) {
+        if (!place_contig_tile(p, cs, pass, spot)) continue;   // uniform over the workgroup
+    } else {
+        if (!place_tile<BM, BN, MODE>(p, lane, spot)) return;
+    }
     const int m0 = spot.m0, rows_m = spot.rows_m;
     const int n0 = spot.n0, rows_n = spot.rows_n;
+    const int expert = spot.expert;
+    uint64_t *const rowmask = reinterpret_cast<uint64_t *>(smem + MASK_AT);
+    if constexpr (MODE == MODE_CONTIG) contig_row_mask<BM, WAVES>(p, spot, wave, lane, rowmask);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
     const uint8_t *a_base = p.A + (int64_t)m0 * p.lda;
-    const uint8_t *b_base = p.B + (int64_t)n0 * p.ldb;
-    const float sc = (CHN || BLK) ? 1.0f : p.scale_a[0] * p.scale_b[0];
+    const uint8_t *b_base = p.B + (int64_t)expert * p.b_gstride + (int64_t)n0 * p.ldb;
+    const float sc = (CHN || BLK) ? 1.0f : p.scale_a[0] * p.scale_b[expert];
     // Rows past rows_m / rows_n fall outside the descriptors: zeros, no memory access.
     const v4i srdA = make_srd(a_base, rows_bytes(rows_m, p.lda));
     const v4i srdB = make_srd(b_base, rows_bytes(rows_n, p.ldb));
@@ -784,8 +941,9 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     // rows past M only reach outputs that are not written.
     const int64_t sa_bytes = (int64_t)((p.K + 127) / 128) * p.lds_sa;
     const int64_t sb_bytes = (int64_t)((p.N + 127) / 128) * p.lds_sb;
+    // (contiguous form: token-row scales by global row, weight-block scales of the tile's expert)
     const v4i srdSA = BLK ? make_srd(p.sfa, (uint32_t)sa_bytes) : v4i{0, 0, 0, 0};
-    const v4i srdSB = BLK ? make_srd(p.sfb, (uint32_t)sb_bytes) : v4i{0, 0, 0, 0};
+    const v4i srdSB = BLK ? make_srd(p.sfb + (int64_t)expert * sb_bytes, (uint32_t)sb_bytes) : v4i{0, 0, 0, 0};
     const uint32_t scl_base = lds0 + STAGES * SLOT;
     constexpr int SCW = BLK ? 2 : 0;               // scale copies per wave per step
     auto issue_scales = [&](int kd) {
@@ -915,7 +1073,7 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     // ring_kernel does, then 16-byte stores of whole row segments.  (The lane
     // index is taken afresh here so that no lane value stays live across the
     // loop next to the accumulators.)
-    const int el = (int)__lane_id();
+    const int el = PASSES > 1 ? lane_id_here() : (int)__lane_id();
     const int er16 = el & 15, ekg = el >> 4;
     auto put = [&](int i, int j, v2u v) {
         const uint32_t m = (uint32_t)(wm * TM + i * 16 + er16);
@@ -960,7 +1118,8 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     }
     if constexpr (!BLK) {
         __syncthreads();
-        store_staged<BM, BN, THREADS, MODE>(p, smem, tid, spot, p.D);
+        const int etid = PASSES > 1 ? wave * 64 + el : tid;   // formed afresh, as above
+        store_staged<BM, BN, THREADS, MODE>(p, smem, etid, spot, p.D, rowmask);
     } else {
         // Block scales: each wave stages its own TM x TN outputs in a private
         // part of the (now free) ring, in its token-block order (row r =
@@ -994,18 +1153,23 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
                 const v4u v = *reinterpret_cast<const v4u *>(ws + wr * WROW + stage_chunk<WCH>(cc, wr) * 16);
                 const int m = wm * TM + FM * rr + i;   // token block i, column rr
                 const int n = ncol0 + cc * 8;
-                if (m < rows_m) store_chunk<MODE>(p.D + (int64_t)(m0 + m) * p.ldd + n, v, p.N - n);
+                if (m < rows_m && (MODE != MODE_CONTIG || row_in_mask(rowmask, m)))
+                    store_chunk<MODE>(p.D + (int64_t)(m0 + m) * p.ldd + n, v, p.N - n);
             }
             __builtin_amdgcn_sched_barrier(0);     // one token block at a time: bounded live registers
         }
+    }
+    if (PASSES > 1) __syncthreads();               // the staged tile is read out before the ring refills
     }
 }
 
 // ---------------------------------------------------------------------------
 // Streaming swap-AB kernel.
 // 4 waves; wave w streams weight rows [n0 + w*WR, +WR) (WR = 128, or 64 when
-// there are too few groups to fill the CUs) as WR/16 row blocks of the
-// 16x16x128 instruction.  Every weight byte is used by exactly one wave; it
+// there are too few groups to fill the CUs or the token blocks are many) as
+// WR/16 row blocks of the 16x16x128 instruction.  Tokens: CB blocks of 16
+// per pass over the weights, CB in {1, 2, 4} for few tokens and {8, 12} for
+// up to 128 / 192 (with WR = 64, so that the WR/16 x CB accumulators fit).  Every weight byte is used by exactly one wave; it
 // still passes through the wave's own LDS ring, because copying whole lines
 // there and reading the operand layout back beats loading that layout
 // directly (see the weight-copy comment below).  Tokens form up to CB column
@@ -1267,14 +1431,26 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n0 = blockIdx.x * 16 * RB;
+    // workgroup = (block of 16 RB weight rows, split of the K steps); the
+    // splits of one block are neighbours in dispatch order
+    const int splits = max(p.splits, 1);
+    const int nb = blockIdx.x / splits, sp = blockIdx.x % splits;
+    const int n0 = nb * 16 * RB;
     const int rows_w = min(p.N - n0, 16 * RB);
     // Rows past N (weights) or past M (tokens) lie outside the descriptors and
     // read zeros without touching memory.
     const v4i srdW = make_srd(p.B + (int64_t)n0 * p.ldb, rows_bytes(rows_w, p.ldb));
-    const v4i srdT = make_srd(p.A, rows_bytes(p.M, p.lda));
+    // token tile: all M tokens (M <= 64), or 64-row tile blockIdx.y of them
+    // (the small-shape class, never split over K)
+    const int tm0 = blockIdx.y * 64;
+    const int rows_t = min(p.M - tm0, 64);
+    const v4i srdT = make_srd(p.A + (int64_t)tm0 * p.lda, rows_bytes(rows_t, p.lda));
     const int nk = (p.K + 127) / 128;
-    const int my = nk > wave ? (nk - wave + WAVES - 1) / WAVES : 0;   // steps kt = wave + WAVES s
+    // this split's K steps [kt0, kt1), taken by the waves round-robin
+    const int kt0 = splits > 1 ? sp * p.ksteps : 0;
+    const int kt1 = splits > 1 ? min(nk, kt0 + p.ksteps) : nk;
+    const int nkw = kt1 - kt0;
+    const int my = nkw > wave ? (nkw - wave + WAVES - 1) / WAVES : 0;   // steps kt = kt0 + wave + WAVES s
     const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem +
                           (uint32_t)wave * WRING;
 
@@ -1302,7 +1478,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
     const v4i srdSB = BLK ? make_srd(p.sfb, (uint32_t)((int64_t)((p.N + 127) / 128) * p.lds_sb)) : v4i{0, 0, 0, 0};
     const uint32_t sb_row = (uint32_t)(n0 / 128) * (uint32_t)p.lds_sb;
     auto issue = [&](int s, int slot) {
-        const int kt = wave + WAVES * s;
+        const int kt = kt0 + wave + WAVES * s;
         const uint32_t k0 = (uint32_t)kt * 128u;
         const bool ok = s < my;
         const bool in0 = ok && (int)(k0 + dch0) < p.K, in1 = ok && (int)(k0 + dch1) < p.K;
@@ -1320,7 +1496,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
         }
         if (BLK) {
             const uint32_t sbase = base + NB * 2048u;
-            dma4(srdSA, ok && lane < 4 * CB ? (uint32_t)kt * (uint32_t)p.lds_sa + 4u * (uint32_t)lane : kOobOffset, sbase);
+            dma4(srdSA, ok && lane < 4 * CB ? (uint32_t)kt * (uint32_t)p.lds_sa + (uint32_t)tm0 + 4u * (uint32_t)lane : kOobOffset,
+                 sbase);
             dma4(srdSB, ok && lane == 0 ? sb_row + ((uint32_t)kt & ~3u) : kOobOffset, sbase + 256u);
         }
     };
@@ -1354,7 +1531,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
             for (int r = 0; r < RB; ++r)
                 wf[r] = pack8(*reinterpret_cast<const v4u *>(slot + 2048 * r + ro0),
                               *reinterpret_cast<const v4u *>(slot + 2048 * r + ro1));
-            const int kt = wave + WAVES * (s0 + d);
+            const int kt = kt0 + wave + WAVES * (s0 + d);
             const int ssb = BLK ? slot[NB * 2048 + 256 + (kt & 3)] : 127;
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
@@ -1382,27 +1559,82 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
 #pragma unroll
         for (int c = 0; c < CB; ++c) red[((wave * RB + r) * CB + c) * 64 + lane] = acc[r][c];
     __syncthreads();
-    // output block (r, c) = weight rows 16 r .. of this workgroup x token block c
-    for (int idx = wave; idx < RB * CB; idx += WAVES) {
-        const int r = idx / CB, c = idx % CB;
+    // output block idx = (r, c): weight rows 16 r .. of this workgroup x token
+    // block c; wave w takes blocks w, w + WAVES, ...
+    constexpr int NBLK = RB * CB, PER = (NBLK + WAVES - 1) / WAVES;
+    v4f sums[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int idx = wave + WAVES * j;
+        if (idx >= NBLK) break;
         v4f sum = red[idx * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < WAVES; ++w) sum += red[(w * RB * CB + idx) * 64 + lane];
+        for (int w = 1; w < WAVES; ++w) sum += red[(w * NBLK + idx) * 64 + lane];
+        sums[j] = sum;
+    }
+    if (splits > 1) {
+        // Split K: leave this split's partial sums, then count the arrival.
+        // The sums are written and read with system-coherent cache bits (sc0
+        // sc1: through the XCD's L2, which is not coherent with the other
+        // XCDs' L2s, to memory and back), and the stores have completed before
+        // the count moves, so the last split sees every other split's sums.
+        // Device-wide fences would do the same by writing back and
+        // invalidating the whole L2, which also evicts the token tiles every
+        // workgroup rereads (measured 4x slower).  The last split of the block
+        // to arrive adds all of them in split order 0, 1, ..., so the result
+        // does not depend on which split finished last, and resets the count
+        // for the next call.
+        constexpr int kCoherent = 1 | 16;          // sc0 | sc1
+        const int64_t base = (int64_t)nb * splits * NBLK * 64 * 16;
+        const __amdgpu_buffer_rsrc_t part = make_rsrc(reinterpret_cast<const uint8_t *>(p.ws) + base,
+                                                      (uint32_t)(splits * NBLK * 64 * 16));
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int idx = wave + WAVES * j;
+            if (idx < NBLK)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, sums[j]), part,
+                                                       (uint32_t)(((sp * NBLK + idx) * 64 + lane) * 16), 0, kCoherent);
+        }
+        __shared__ int last_split;
+        vmcnt_wait<0>();                           // this thread's sums are in memory
+        __syncthreads();                           // and every thread's
+        if (threadIdx.x == 0)
+            last_split = __hip_atomic_fetch_add(p.cnt + nb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == splits - 1;
+        __syncthreads();
+        if (!last_split) return;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int idx = wave + WAVES * j;
+            if (idx >= NBLK) break;
+            v4f sum = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(part, (uint32_t)((idx * 64 + lane) * 16), 0, kCoherent));
+            for (int t = 1; t < splits; ++t)
+                sum += __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   part, (uint32_t)(((t * NBLK + idx) * 64 + lane) * 16), 0, kCoherent));
+            sums[j] = sum;
+        }
+        if (threadIdx.x == 0) __hip_atomic_exchange(p.cnt + nb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int idx = wave + WAVES * j;
+        if (idx >= NBLK) break;
+        const int r = idx / CB, c = idx % CB;
+        const v4f sum = sums[j];
         const float sc = SCL != SCALE_TENSOR ? 1.0f : p.scale_a[0] * p.scale_b[0];
         const int tok = c * 16 + r16;
-        if (tok < p.M) {
+        if (tok < rows_t) {
             const int n = n0 + r * 16 + kg * 4;
             v2u v;
             if (CHN) {
                 float s4[4], b4[4];
                 channel_terms(p, n, s4, b4);
-                const float sam = p.ch_sa ? p.ch_sa[tok] : 1.0f;
+                const float sam = p.ch_sa ? p.ch_sa[tm0 + tok] : 1.0f;
                 v = pack_bf16x4(sum[0] * sam * s4[0] + b4[0], sum[1] * sam * s4[1] + b4[1],
                                 sum[2] * sam * s4[2] + b4[2], sum[3] * sam * s4[3] + b4[3]);
             } else {
                 v = pack_bf16x4(sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc);
             }
-            store_bf16x4(p.D + (int64_t)tok * p.ldd, n, p.N - n, v);
+            store_bf16x4(p.D + (int64_t)(tm0 + tok) * p.ldd, n, p.N - n, v);
         }
     }
 }

@@ -21,9 +21,22 @@
  *
  * Conventions for every entry point:
  *   - All pointers except `stream` are DEVICE pointers (memory the caller
- *     allocated, e.g. through PyTorch).  The caller owns every buffer; the
- *     library allocates nothing, keeps no pointer after returning, and never
+ *     allocated, e.g. through PyTorch).  The caller owns every buffer it
+ *     passes; the library keeps no pointer to them after returning and never
  *     synchronises the stream.
+ *   - Workspace: the dense forms with M <= 64 split K over workgroups when
+ *     the weight rows alone would leave the chip part-empty (fewer than 256
+ *     blocks of 16-64 rows).  The splits' FP32 partial sums meet in a
+ *     workspace of 8 MiB + 1 KiB per device, which the library allocates
+ *     with hipMalloc on the first such call on that device (and keeps until
+ *     the process ends); if that first call happens while `stream` is being
+ *     captured into a graph, it runs unsplit instead (nothing allocated; the
+ *     same bound holds, though the FP32 sums are added in another order).
+ *     The partial sums are added in a fixed order, so repeated calls give
+ *     bit-identical results whichever split finishes last.  Calls that split K and overlap
+ *     on one device (different streams or threads without ordering) share
+ *     the workspace and race: order them.  No other path uses device memory
+ *     beyond the caller's buffers.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
  *     Results are valid once that stream's work has completed.
  *   - FP8 operands are byte arrays of codes; dtypes are FP8G_E4M3 (OCP E4M3FN:
@@ -44,8 +57,8 @@
  *   - Values that live on the device (masked_m, grp_idx) cannot be checked
  *     without a synchronisation: masked_m[g] is clamped to [0, cap], and any
  *     grp_idx entry outside [0, G) marks a padding row.
- *   - Results are deterministic: no atomics, no split-K; the same call on the
- *     same inputs gives bit-identical D.
+ *   - Results are deterministic: no floating-point atomics; the same call on
+ *     the same inputs gives bit-identical D.
  */
 #ifndef FP8_GEMM_H
 #define FP8_GEMM_H
@@ -56,7 +69,7 @@
 extern "C" {
 #endif
 
-#define FP8G_ABI_VERSION 3
+#define FP8G_ABI_VERSION 4
 
 typedef enum { FP8G_E4M3 = 0, FP8G_E5M2 = 1 } fp8g_dtype;
 
@@ -80,8 +93,9 @@ typedef enum {
  *   D: [M x N] BF16, row stride ldd elements.
  *   D[i][j] = bf16_rne( (scale_a * scale_b) * sum_k A[i][k] * B[j][k] ).
  * M <= 64 takes the swapped (weights-on-rows, tokens-on-columns) decode
- * kernel; larger M takes the LDS-tiled kernel.  The choice never changes
- * which elements are written.
+ * kernel, with K split over workgroups when the weight rows are few (see
+ * Workspace above); larger M takes the LDS-tiled kernel.  The choice never
+ * changes which elements are written.
  */
 int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype,
                 const void *B, int64_t ldb, int b_dtype,
@@ -167,8 +181,11 @@ int bf16_gemm_nt(const void *A, int64_t lda, const void *B, int64_t ldb,
  *   Rows i >= m_g of A are never read and rows i >= m_g of D are never written.
  *   A group with m_g = 0 reads nothing.
  *   expected_m: host hint of the typical m_g, 0 <= expected_m <= cap (0 = use
- *     cap).  It only picks the kernel variant (the swapped streaming kernel
- *     when it is <= 64) and never changes results.
+ *     cap).  It only picks the kernel variant and never changes results: up
+ *     to 192 the swapped streaming kernel, which reads each group's weights
+ *     once for up to 16 (1..16), 32, 64, 128 or 192 (129..192) tokens and
+ *     loops over token blocks when a group has more; above 192 the tiled
+ *     kernel with 128-row tiles.
  */
 int fp8_grouped_gemm_masked(const void *A, int a_dtype, const void *B, int b_dtype,
                             const float *scale_a, const float *scale_b,
@@ -231,6 +248,11 @@ int fp8_grouped_gemm_contig(const void *A, int a_dtype, const void *B, int b_dty
  *   Row r with a valid expert e = grp_idx[r]:
  *     D[r][j] = bf16_rne( sum_kb 2^(ea(r,kb) - 127) 2^(eb(e,j/128,kb) - 127) sum_{k in kb} A[r][k] B[e][j][k] ).
  *   Padding rows are not written; their scale bytes may be read.
+ * Work is split into tiles aligned to each expert's run of 128-row blocks:
+ * 256 rows, and 128 rows at the end of a run with an odd number of blocks, so
+ * no block is computed twice.  The runs are found on the device (the counts
+ * never pass through the host); a block's expert is that of its first row
+ * naming a valid expert.
  */
 int fp8_grouped_gemm_contig_blockscaled(const void *A, int a_dtype, const void *B, int b_dtype,
                                         const uint8_t *scale_a, int64_t lds_a,
@@ -243,7 +265,7 @@ int fp8_grouped_gemm_contig_blockscaled(const void *A, int a_dtype, const void *
  *   op: 0 = dense (m = M), 1 = masked grouped (m = cap, hint = expected_m,
  *   groups = G), 2 = contiguous grouped (m = M_total, groups = G),
  *   3 = block-scaled dense (m = M), 4 = BF16 dense (m = M, k in BF16
- *   elements).
+ *   elements), 5 = block-scaled contiguous grouped (m = M_total, groups = G).
  * Fills the variant id, the tile sizes along M and N, and the number of
  * workgroups of the launch.  Returns an fp8g_status (validation as above,
  * pointers excepted).
@@ -252,16 +274,20 @@ typedef struct {
     int variant;        /* 1 = tiled 256x256, 2 = tiled 128x256 (m x n; FP8
                            dense forms on 4 waves and 16x16x128, grouped and
                            BF16 forms on 8 waves and 32x32x64),
-                           3 = swapped streaming (grouped forms),
-                           4 = swapped decode, K split over 4 waves (dense
-                           forms, m <= 64), 5 = tiled 256x192 and
+                           3 = swapped streaming (masked grouped forms,
+                           16 * token_blocks tokens per pass),
+                           4 = swapped decode, K split over 4 waves and
+                           over k_splits workgroups (dense forms, m <= 64), 5 = tiled 256x192 and
                            6 = tiled 256x224 (both FP8 dense, per-tensor or
                            per-channel scales), 0 = nothing to launch */
     int tile_m;         /* rows of D per workgroup tile (tokens) */
     int tile_n;         /* columns of D per workgroup tile (weight rows: 256
                            or 512 for variant 3, 16 or 32 for variant 4) */
-    int token_blocks;   /* swapped kernel: 16-token column blocks per pass */
+    int token_blocks;   /* swapped kernels: 16-token column blocks per pass
+                           (1, 2, 4; the masked form also 8 and 12) */
     int64_t workgroups; /* grid size */
+    int k_splits;       /* variant 4: workgroups sharing one block of weight
+                           rows, each over a part of K (1 = no split) */
 } fp8g_plan;
 
 int fp8_gemm_plan(int op, int m, int n, int k, int groups, int expected_m, fp8g_plan *out);

@@ -21,17 +21,23 @@ with ea / eb = floor(log2) of the group's largest |a| / |b|, E <= ea + eb + 1, s
 bounds it; F_ij = |sa sb| * (K / 8) * 2^-24 * S bounds FP32 rounding when every
 group sum is added separately.
 
-The truncation shows only where a sum cancels, so that |r| is far below S: then
-the 2^-8 |r| term no longer covers it.  On random data that is rare enough that
-it never happens in the checked inputs but for one short (K = 16) case, so
-check() asserts bound (1) alone on every element unless a test passes the
-allowance H + F explicitly.  Only tests whose inputs are built to cancel (or
-that exist to show the short cancelling case) pass it, and those must also
-name a cap on how many elements may need it; every such element must then be
-a cancellation and satisfy (1) + H + F.  Per group the truncation is below
-2^-10 times the group's largest product, so in all below 2^-10 |sa sb| S, and
-it can break (1) only where 2^-8 |r| < 2^-10 |sa sb| S + F: a cancellation is
-|r| < 2^-2 |sa sb| S (F is far smaller).
+The GPU's own BF16 rounding can take the whole 2^-8 |r| term, so the
+truncation breaks (1) wherever it exceeds about 1e-5 |sa sb| S.  Per group it
+is below 2^-10 times the group's largest product; relative to S it shrinks as
+K grows (S grows with every group, the truncation only with the square root
+of their number on random data), and it shows most where a sum cancels.
+Measured on random data: 1.7e-4 of the elements at K = 16, 2e-7 at K = 144
+with an E5M2 operand, none at K >= 256 in E4M3.
+
+So check() asserts bound (1) alone unless a test passes the allowance H + F
+explicitly, and then only a capped number of elements may need it, each
+within (1) + H + F:
+  - the seeded workload configurations pass nothing (bound (1) alone);
+  - random inputs pass it with random_cap(): at most 1 in 10^3 elements for
+    K <= 32 (at most four groups of 8), 2 in 10^6 otherwise, and at least 4.
+    A systematic error (a dropped or repeated K chunk, a wrong scale, a
+    misplaced tile) moves far more elements than that and fails;
+  - inputs built to cancel pass it with no cap.
 """
 from __future__ import annotations
 
@@ -81,6 +87,46 @@ def hw_allowance(A_rows, B_rows, a_fmt, b_fmt, scale_abs, S):
     return np.asarray(scale_abs, dtype=np.float64) * (H + F)
 
 
+def hw_allowance_points(A, B, ii, jj, a_fmt, b_fmt, scale_abs, S):
+    """H + F at sampled points (ii[p], jj[p])."""
+    K = A.shape[1]
+    ui, inv_i = np.unique(ii, return_inverse=True)
+    uj, inv_j = np.unique(jj, return_inverse=True)
+    wa = group_exponent_weights(A[ui], a_fmt)
+    wb = group_exponent_weights(B[uj], b_fmt)
+    H = 2.0 ** -9 * np.einsum("pg,pg->p", wa[inv_i], wb[inv_j])
+    F = (max(K, 8) / 8.0) * 2.0 ** -24 * np.asarray(S, dtype=np.float64)
+    return np.asarray(scale_abs, dtype=np.float64) * (H + F)
+
+
+def _block_scaled_weights(w, scales):
+    """Group weights [rows, G] times each group's block scale: scales[rows, KB]
+    are E8M0 codes of the 128-element K block (16 groups of 8) a group is in."""
+    G = w.shape[1]
+    kb = np.minimum(np.arange(G) // 16, scales.shape[1] - 1)
+    return w * np.exp2(scales[:, kb].astype(np.float64) - 127.0)
+
+
+def hw_allowance_blockscaled(A, B, a_fmt, b_fmt, scale_a, scale_b, S, ii=None, jj=None):
+    """H + F of the module docstring with per-block scales: the block-scaled
+    GEMM's S already includes the scales, and every group of 8 K indices lies
+    in one 128-element scale block, so the group terms of (2) take that block's
+    scales.  scale_a: [KB, >= M] codes (row m of A: column m); scale_b:
+    [ceil(N/128), >= KB] codes.  Full [M, N] output, or points (ii, jj)."""
+    K = A.shape[1]
+    kb = (K + 127) // 128
+    rows_a = np.arange(A.shape[0]) if ii is None else np.unique(ii)
+    rows_b = np.arange(B.shape[0]) if jj is None else np.unique(jj)
+    wa = _block_scaled_weights(group_exponent_weights(A[rows_a], a_fmt), scale_a[:kb, rows_a].T)
+    wb = _block_scaled_weights(group_exponent_weights(B[rows_b], b_fmt), scale_b[rows_b // 128, :kb])
+    F = (max(K, 8) / 8.0) * 2.0 ** -24 * np.asarray(S, dtype=np.float64)
+    if ii is None:
+        return 2.0 ** -9 * (wa @ wb.T) + F
+    ia = np.searchsorted(rows_a, ii)
+    ib = np.searchsorted(rows_b, jj)
+    return 2.0 ** -9 * np.einsum("pg,pg->p", wa[ia], wb[ib]) + F
+
+
 def violations(d_bits, r, s, scale_abs, extra=0.0):
     """Boolean mask of elements outside bound (1) plus `extra`."""
     d = bf16_bits_to_f64(d_bits)
@@ -114,11 +160,10 @@ def _report(bad, d_bits, r, s, what, label):
 def check(d_bits, r, s, scale_abs, ref_bits=None, what="", allowance=None, max_allowed=0):
     """Assert bound (1) on every element.
 
-    allowance: H + F of the module docstring, passed only by tests whose inputs
-    make sums cancel.  Then at most `max_allowed` elements may lie outside (1);
-    each of them must be a cancellation (|r| < 2^-2 |sa sb| S) and lie within
-    (1) + allowance.  Returns (elements outside (1), bit-identical fraction
-    against ref_bits or None)."""
+    allowance: H + F of the module docstring, passed only for inputs built to
+    cancel and random inputs with short sums.  Then at most `max_allowed`
+    elements may lie outside (1), each within (1) + allowance.  Returns
+    (elements outside (1), bit-identical fraction against ref_bits or None)."""
     plain = violations(d_bits, r, s, scale_abs)
     n_plain = int(plain.sum())
     if n_plain and allowance is None:
@@ -130,10 +175,6 @@ def check(d_bits, r, s, scale_abs, ref_bits=None, what="", allowance=None, max_a
         wide = violations(d_bits, r, s, scale_abs, extra=allowance)
         if wide.any():
             raise AssertionError(_report(wide, d_bits, r, s, what, "the stated bound plus the matrix-core truncation allowance"))
-        rr = np.broadcast_to(np.abs(np.asarray(r, dtype=np.float64)), plain.shape)[plain]
-        ss = np.broadcast_to(np.asarray(s, dtype=np.float64) * np.asarray(scale_abs, dtype=np.float64), plain.shape)[plain]
-        if not (rr < 2.0 ** -2 * ss).all():
-            raise AssertionError(_report(plain, d_bits, r, s, what, "the stated bound, and they are not cancellations"))
     frac = None
     if ref_bits is not None:
         same = np.asarray(d_bits) == np.asarray(ref_bits)
@@ -144,6 +185,61 @@ def check(d_bits, r, s, scale_abs, ref_bits=None, what="", allowance=None, max_a
     return n_plain, frac
 
 
+def random_cap(n, K):
+    """How many of n elements of a random-data check may need the allowance."""
+    frac = 1e-3 if K <= 32 else 2e-6
+    return max(4, int(np.ceil(n * frac)))
+
+
+def random_allowance(A_rows, B_rows, a_fmt, b_fmt, scale_abs, S):
+    """check() keyword arguments for a random-data FP8 check of the full
+    outer product of A_rows and B_rows."""
+    n = A_rows.shape[0] * B_rows.shape[0]
+    return {"allowance": hw_allowance(A_rows, B_rows, a_fmt, b_fmt, scale_abs, S),
+            "max_allowed": random_cap(n, A_rows.shape[1])}
+
+
 def assert_within_bound(d_bits, r, s, scale_abs, ref_bits=None, what=""):
     """Bound (1) on every element; returns the bit-identical fraction."""
     return check(d_bits, r, s, scale_abs, ref_bits=ref_bits, what=what)[1]
+
+
+def _bf16_group_weights(bits, group):
+    """[rows, ceil(K/group)]: 2^floor(log2(max |x|)) over each aligned group of
+    BF16 values (0 for an all-zero group; non-finite values are ignored)."""
+    v = np.abs(bf16_bits_to_f64(bits))
+    v[~np.isfinite(v)] = 0.0
+    rows, K = v.shape
+    G = (K + group - 1) // group
+    if K % group:
+        v = np.pad(v, ((0, 0), (0, G * group - K)))
+    mx = v.reshape(rows, G, group).max(axis=2)
+    out = np.zeros_like(mx)
+    nz = mx > 0
+    out[nz] = np.exp2(np.floor(np.log2(mx[nz])))
+    return out
+
+
+def hw_allowance_bf16(A, B, S, ii=None, jj=None):
+    """Allowance of the BF16 comparison path (A, B: BF16 bit patterns; S: sum
+    of |products|), measured by tests/test_gpu_bf16.py: inside one BF16
+    instruction the (exact) products are cut toward zero to multiples of
+    2^(E - 24), E the exponent of the instruction's largest product, and the
+    sum is rounded to FP32.  An instruction's 16 K indices lie in one aligned
+    group of 32 (the tiled kernel's 64-byte K half), two instructions per
+    group, so with ea / eb the group's floor(log2 max |a|) / |b| (E <= ea + eb
+    + 1) the cut costs less than 32 * 2^(ea + eb + 1 - 24) per group:
+
+        H_bf = 2^-18 * sum_g 2^(ea_g) 2^(eb_g)
+
+    plus F of the module docstring for the FP32 roundings.  Full [M, N]
+    output, or points (ii, jj)."""
+    K = A.shape[1]
+    F = (max(K, 8) / 8.0) * 2.0 ** -24 * np.asarray(S, dtype=np.float64)
+    if ii is None:
+        return 2.0 ** -18 * (_bf16_group_weights(A, 32) @ _bf16_group_weights(B, 32).T) + F
+    ui, inv_i = np.unique(ii, return_inverse=True)
+    uj, inv_j = np.unique(jj, return_inverse=True)
+    wa = _bf16_group_weights(A[ui], 32)
+    wb = _bf16_group_weights(B[uj], 32)
+    return 2.0 ** -18 * np.einsum("pg,pg->p", wa[inv_i], wb[inv_j]) + F

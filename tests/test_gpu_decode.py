@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads
-from tests._parity import check, gpu_bits
+from tests._parity import check, gpu_bits, hw_allowance, hw_allowance_blockscaled, random_allowance, random_cap
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +29,10 @@ def _dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
+# K splits (workgroups per block of weight rows) these take: (16, 100, 1040)
+# 2 (5 + 4 K steps), (24, 264, 4096) 8, (33, 264, 2048) 4, (64, 1000, 1536)
+# 3 with an 8-row last block, (40, 2056, 7168) 2 (28 steps each, 8-row last
+# block); the others 1.
 @pytest.mark.parametrize("M,N,K,fa,fb", [
     (1, 16, 16, E4M3, E4M3),          # one K chunk: 3 of 4 waves idle
     (1, 4104, 7168, E4M3, E4M3),      # N tail inside a workgroup
@@ -38,20 +42,24 @@ def _dev(x):
     (33, 264, 2048, E5M2, E5M2),      # four token blocks, 4 steps per wave through a 2-slot ring
     (64, 4096, 1024, E4M3, E4M3),
     (48, 40, 272, E4M3, E4M3),
+    (64, 1000, 1536, E4M3, E4M3),
+    (40, 2056, 7168, E5M2, E4M3),
     (1, 8200, 1040, E4M3, E4M3),      # N >= 8192: 32 weight rows per workgroup, 8-row tail
     (17, 8192, 2048, E5M2, E4M3),     # 32-row workgroups, two token blocks
     (64, 8232, 1024, E4M3, E4M3),     # 32-row workgroups, four token blocks, 8-row tail
 ])
 def test_decode_matches_oracle(M, N, K, fa, fb):
     w = workloads.dense_random(M, N, K, seed=M * 7 + N + K, a_fmt=fa, b_fmt=fb, scales=(0.75, 1.5))
-    assert _f().plan(0, M, N, K).variant == 4
-    print(f"[decode] M={M} N={N} K={K} fmt=({fa},{fb})", flush=True)
+    plan = _f().plan(0, M, N, K)
+    assert plan.variant == 4
+    print(f"[decode] M={M} N={N} K={K} fmt=({fa},{fb}) rows/wg={plan.tile_n} k_splits={plan.k_splits}", flush=True)
     d = _f().gemm_nt(_dev(w.A), _dev(w.B), torch.tensor([w.sa], device="cuda"), torch.tensor([w.sb], device="cuda"),
                      a_dtype=fa, b_dtype=fb)
     torch.cuda.synchronize()
     d = gpu_bits(d)
     ref, r, s, _ = oracle.gemm_nt(w.A, w.B, fa, fb, w.sa, w.sb)
-    check(d, r, s, abs(w.sa * w.sb), ref_bits=ref, what=f"decode {M}x{N}x{K}")
+    sc = abs(w.sa * w.sb)
+    check(d, r, s, sc, ref_bits=ref, what=f"decode {M}x{N}x{K}", **random_allowance(w.A, w.B, fa, fb, sc, s))
 
 
 def test_decode_all_ones_exact():
@@ -76,7 +84,8 @@ def test_decode_blockscaled(M, N, K):
     torch.cuda.synchronize()
     d = gpu_bits(d)
     ref, r, s = oracle.gemm_nt_blockscaled(w.A, w.B, w.sa, w.sb)
-    check(d, r, s, 1.0, ref_bits=ref, what=f"decode blockscaled {M}x{N}x{K}")
+    check(d, r, s, 1.0, ref_bits=ref, what=f"decode blockscaled {M}x{N}x{K}",
+          allowance=hw_allowance_blockscaled(w.A, w.B, 0, 0, w.sa, w.sb, s), max_allowed=random_cap(d.size, K))
 
 
 def test_decode_deterministic():
@@ -85,3 +94,78 @@ def test_decode_deterministic():
     one = torch.ones(1, device="cuda")
     outs = [gpu_bits(_f().gemm_nt(a, b, one, one, a_dtype=E4M3, b_dtype=E4M3)) for _ in range(3)]
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_decode_split_k_graph_replays():
+    """The split-K few-token path captured in a graph and replayed four times,
+    with eager launches (another split shape, a fill) between the replays:
+    every replay equals the eager result bit for bit, so the arrival counts
+    are back at zero after each launch and the partial sums are added in the
+    same order whichever split finishes last."""
+    f = _f()
+    w = workloads.dense_random(64, 1024, 7168, seed=91)
+    w2 = workloads.dense_random(33, 1000, 2048, seed=92)
+    assert f.plan(0, 64, 1024, 7168).k_splits == 4 and f.plan(0, 33, 1000, 2048).k_splits > 1
+    a, b = _dev(w.A), _dev(w.B)
+    a2, b2 = _dev(w2.A), _dev(w2.B)
+    one = torch.ones(1, device="cuda")
+    eager = gpu_bits(f.gemm_nt(a, b, one, one, a_dtype=E4M3, b_dtype=E4M3))
+    eager2 = gpu_bits(f.gemm_nt(a2, b2, one, one, a_dtype=E4M3, b_dtype=E4M3))
+    out = torch.empty((64, 1024), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        f.gemm_nt(a, b, one, one, out=out, a_dtype=E4M3, b_dtype=E4M3)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        f.gemm_nt(a, b, one, one, out=out, a_dtype=E4M3, b_dtype=E4M3)
+    for i in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(gpu_bits(out), eager), f"replay {i}"
+        d2 = gpu_bits(f.gemm_nt(a2, b2, one, one, a_dtype=E4M3, b_dtype=E4M3))
+        torch.cuda.synchronize()
+        assert np.array_equal(d2, eager2), f"eager call after replay {i}"
+    del g
+    ref, r, s, _ = oracle.gemm_nt(w.A, w.B)
+    check(eager, r, s, 1.0, ref_bits=ref, what="split-K 64x1024x7168", **random_allowance(w.A, w.B, E4M3, E4M3, 1.0, s))
+
+
+@pytest.mark.parametrize("M,N,K,fa,fb", [
+    (65, 64, 128, E4M3, E4M3),        # two token tiles, the second of 1 row
+    (200, 100, 1040, E5M2, E4M3),     # 4 token tiles (the last 8 rows), N tail, K tail
+    (256, 256, 256, E4M3, E5M2),      # the 256^3 shape: 16 x 4 workgroups
+])
+def test_small_class_token_tiles(M, N, K, fa, fb):
+    """Small problems (M <= 256 where the tiled kernel would start at most 2
+    workgroups) run the decode kernel over 64-token tiles: per-tensor,
+    per-channel and block-scaled forms against the oracle."""
+    f = _f()
+    plan = f.plan(0, M, N, K)
+    assert plan.variant == 4 and plan.tile_m == 64 and f.plan(3, M, N, K).variant == 4
+    print(f"[small] M={M} N={N} K={K} fmt=({fa},{fb}) workgroups={plan.workgroups}", flush=True)
+    w = workloads.dense_random(M, N, K, seed=M + N + K, a_fmt=fa, b_fmt=fb, scales=(0.75, 1.5))
+    d = gpu_bits(f.gemm_nt(_dev(w.A), _dev(w.B), torch.tensor([w.sa], device="cuda"), torch.tensor([w.sb], device="cuda"),
+                           a_dtype=fa, b_dtype=fb))
+    ref, r, s, _ = oracle.gemm_nt(w.A, w.B, fa, fb, w.sa, w.sb)
+    sc = abs(w.sa * w.sb)
+    check(d, r, s, sc, ref_bits=ref, what=f"small {M}x{N}x{K}", **random_allowance(w.A, w.B, fa, fb, sc, s))
+    rng = np.random.default_rng(M)
+    csa = rng.uniform(0.5, 2, M).astype(np.float32)
+    csb = rng.uniform(0.5, 2, N).astype(np.float32)
+    bias = rng.normal(0, 4, N).astype(np.float32)
+    d = gpu_bits(f.gemm_nt_channelwise(_dev(w.A), _dev(w.B), _dev(csa), _dev(csb), _dev(bias), a_dtype=fa, b_dtype=fb))
+    ref, r, s = oracle.gemm_nt_channelwise(w.A, w.B, csa, csb, bias, fa, fb)
+    _, _, s1, _ = oracle.gemm_nt(w.A, w.B, fa, fb)
+    allow = hw_allowance(w.A, w.B, fa, fb, 1.0, s1) * np.outer(csa, csb)
+    check(d, r, s, 1.0, ref_bits=ref, what=f"small channelwise {M}x{N}x{K}", allowance=allow,
+          max_allowed=random_cap(d.size, K))
+    wb = workloads.dense_blockscaled(M, N, K, seed=M + 2 * N + K, lds_pad=5, pad_code=255)
+    d = gpu_bits(f.gemm_nt_blockscaled(_dev(wb.A), _dev(wb.B), _dev(wb.sa), _dev(wb.sb), a_dtype=E4M3, b_dtype=E4M3))
+    ref, r, s = oracle.gemm_nt_blockscaled(wb.A, wb.B, wb.sa, wb.sb)
+    check(d, r, s, 1.0, ref_bits=ref, what=f"small blockscaled {M}x{N}x{K}",
+          allowance=hw_allowance_blockscaled(wb.A, wb.B, 0, 0, wb.sa, wb.sb, s), max_allowed=random_cap(d.size, K))
+

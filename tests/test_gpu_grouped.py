@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads
-from tests._parity import check, gpu_bits
+from tests._parity import check, gpu_bits, random_allowance
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +46,10 @@ def run_masked(w, expected_m=0):
     return gpu_bits(out)
 
 
-def check_masked(w, d, rows_per_group=None):
+def check_masked(w, d, rows_per_group=None, seeded=False):
+    """Rows past each count keep the sentinel; valid rows against the oracle
+    (random inputs with the capped allowance, seeded configurations on the
+    stated bound alone)."""
     G, cap, K = w.A.shape
     m = np.clip(w.masked_m, 0, cap)
     for g in range(G):
@@ -55,8 +58,9 @@ def check_masked(w, d, rows_per_group=None):
         ref, r, s, _ = oracle.grouped_masked(w.A, w.B, w.masked_m, w.sb, w.a_fmt, w.b_fmt, w.sa)
         for g in range(G):
             if m[g]:
-                check(d[g, :m[g]], r[g, :m[g]], s[g, :m[g]], abs(w.sa * w.sb[g]), ref_bits=ref[g, :m[g]],
-                      what=f"group {g}")
+                sc = abs(w.sa * w.sb[g])
+                extra = {} if seeded else random_allowance(w.A[g, :m[g]], w.B[g], w.a_fmt, w.b_fmt, sc, s[g, :m[g]])
+                check(d[g, :m[g]], r[g, :m[g]], s[g, :m[g]], sc, ref_bits=ref[g, :m[g]], what=f"group {g}", **extra)
         return
     rng = np.random.default_rng(0)
     for g in range(G):
@@ -64,7 +68,9 @@ def check_masked(w, d, rows_per_group=None):
             continue
         rows = np.unique(np.concatenate([[0, m[g] - 1], rng.integers(0, m[g], rows_per_group)]))
         ref, r, s, _ = oracle.gemm_nt(w.A[g, rows], w.B[g], w.a_fmt, w.b_fmt, w.sa, float(w.sb[g]))
-        check(d[g, rows], r, s, abs(w.sa * w.sb[g]), ref_bits=ref, what=f"group {g}")
+        sc = abs(w.sa * w.sb[g])
+        extra = {} if seeded else random_allowance(w.A[g, rows], w.B[g], w.a_fmt, w.b_fmt, sc, s)
+        check(d[g, rows], r, s, sc, ref_bits=ref, what=f"group {g}", **extra)
 
 
 COUNTS = [0, 1, 16, 17, 32, 33, 64, 40]
@@ -80,10 +86,35 @@ def test_masked_all_count_classes(hint):
 
 
 def test_masked_large_counts_take_tiled_kernel():
-    w = workloads.masked_random(4, 192, 264, 384, seed=42, m_values=[0, 100, 192, 129])
-    assert _lib().plan(1, 192, 264, 384, 4, 0).variant != 3
+    w = workloads.masked_random(4, 256, 264, 384, seed=42, m_values=[0, 200, 256, 129])
+    assert _lib().plan(1, 256, 264, 384, 4, 0).variant == 2
     d = run_masked(w)
     check_masked(w, d)
+
+
+@pytest.mark.parametrize("hint", [0, 96, 150])
+def test_masked_wide_token_counts(hint):
+    """65..192 tokens per group: the swapped kernel with 12 (hints 0 = cap
+    192 and 150) or 8 (hint 96) token blocks of 16 in one pass over each
+    expert's weights; with 8 blocks the counts above 128 take a second pass.
+    Counts on both sides of every pass and block edge, and an empty group."""
+    w = workloads.masked_random(9, 192, 264, 640, seed=47, m_values=[0, 65, 96, 128, 129, 160, 192, 1, 17])
+    plan = _lib().plan(1, 192, 264, 640, 9, hint)
+    assert plan.variant == 3 and plan.token_blocks == (8 if hint == 96 else 12)
+    d = run_masked(w, expected_m=hint)
+    check_masked(w, d)
+
+
+@pytest.mark.parametrize("m", [96, 160])
+def test_masked_swapab_table_shapes_sampled(m):
+    """The swap-AB benchmark table's 16 groups of m = 96 and 160 rows at
+    n = 4096, k = 7168 ("One transpose, half the compute", section 4): the
+    one-pass swapped kernel, sampled rows of every group under the stated
+    bound, every row past the count byte for byte."""
+    w = workloads.masked_random(16, 160, 4096, 7168, seed=40, m_values=[m] * 16)
+    assert _lib().plan(1, 160, 4096, 7168, 16, m).variant == 3
+    d = run_masked(w, expected_m=m)
+    check_masked(w, d, rows_per_group=4)
 
 
 def test_masked_clamps_counts():
@@ -110,7 +141,7 @@ def test_masked_decode_config_sampled():
     checked byte for byte, valid rows are sampled per group."""
     w = workloads.masked_decode()
     d = run_masked(w, expected_m=32)
-    check_masked(w, d, rows_per_group=3)
+    check_masked(w, d, rows_per_group=3, seeded=True)
 
 
 def test_grouped_equals_per_group_dense():
@@ -125,8 +156,9 @@ def test_grouped_equals_per_group_dense():
         dd = gpu_bits(out)
         ref, r, s, _ = oracle.gemm_nt(w.A[g, :m], w.B[g], sa=w.sa, sb=float(w.sb[g]))
         sc = abs(w.sa * w.sb[g])
-        check(dd, r, s, sc, ref_bits=ref, what=f"dense group {g}")
-        check(d[g, :m], r, s, sc, ref_bits=ref, what=f"grouped group {g}")
+        extra = random_allowance(w.A[g, :m], w.B[g], E4M3, E4M3, sc, s)
+        check(dd, r, s, sc, ref_bits=ref, what=f"dense group {g}", **extra)
+        check(d[g, :m], r, s, sc, ref_bits=ref, what=f"grouped group {g}", **extra)
 
 
 # ---------------------------------------------------------------------------
@@ -145,14 +177,16 @@ def run_contig(w):
     return gpu_bits(out)
 
 
-def check_contig(w, d, sample_rows=None):
+def check_contig(w, d, sample_rows=None, seeded=False):
     pad = w.grp_idx < 0
     assert (d[pad] == SENT).all(), "padding rows were written"
     if sample_rows is None:
         ref, r, s, _ = oracle.grouped_contig(w.A, w.B, w.grp_idx, w.sb, w.a_fmt, w.b_fmt, w.sa)
         for g in np.unique(w.grp_idx[~pad]):
             rg = np.flatnonzero(w.grp_idx == g)
-            check(d[rg], r[rg], s[rg], abs(w.sa * w.sb[g]), ref_bits=ref[rg], what=f"contig expert {g}")
+            sc = abs(w.sa * w.sb[g])
+            extra = {} if seeded else random_allowance(w.A[rg], w.B[g], w.a_fmt, w.b_fmt, sc, s[rg])
+            check(d[rg], r[rg], s[rg], sc, ref_bits=ref[rg], what=f"contig expert {g}", **extra)
         return
     rng = np.random.default_rng(1)
     real_rows = np.flatnonzero(~pad)
@@ -160,7 +194,9 @@ def check_contig(w, d, sample_rows=None):
     for g in np.unique(w.grp_idx[rows]):
         rg = rows[w.grp_idx[rows] == g]
         ref, r, s, _ = oracle.gemm_nt(w.A[rg], w.B[g], w.a_fmt, w.b_fmt, w.sa, float(w.sb[g]))
-        check(d[rg], r, s, abs(w.sa * w.sb[g]), ref_bits=ref, what=f"contig expert {g}")
+        sc = abs(w.sa * w.sb[g])
+        extra = {} if seeded else random_allowance(w.A[rg], w.B[g], w.a_fmt, w.b_fmt, sc, s)
+        check(d[rg], r, s, sc, ref_bits=ref, what=f"contig expert {g}", **extra)
 
 
 def test_contig_small():
@@ -196,6 +232,17 @@ def test_contig_all_padding_halves():
     check_contig(w, d)
 
 
+def test_contig_long_runs():
+    """Run-aligned tiles: a run of 70 128-row blocks starting at an odd block
+    (its tiles start at odd blocks, and finding a tile start scans back over
+    more than 64 blocks), then a 3-block run (a 256-row tile and a 128-row
+    one) and a single-block run; N tail inside a 256-column tile."""
+    w = workloads.contig_random(tokens=0, topk=1, G=4, N=136, K=256, seed=56, counts=[100, 70 * 128 - 5, 300, 1])
+    assert w.A.shape[0] == (1 + 70 + 3 + 1) * 128
+    d = run_contig(w)
+    check_contig(w, d)
+
+
 def test_contig_formats():
     w = workloads.contig_random(tokens=200, topk=1, G=3, N=136, K=384, seed=53, a_fmt=E5M2, b_fmt=E4M3)
     d = run_contig(w)
@@ -206,4 +253,4 @@ def test_contig_prefill_config_sampled():
     """8192 tokens x top-8 over 32 experts, N=4096, K=7168."""
     w = workloads.contig_prefill()
     d = run_contig(w)
-    check_contig(w, d, sample_rows=192)
+    check_contig(w, d, sample_rows=192, seeded=True)

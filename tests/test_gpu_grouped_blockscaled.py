@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads
-from tests._parity import check, gpu_bits
+from tests._parity import check, gpu_bits, hw_allowance_blockscaled, random_cap
 
 pytestmark = pytest.mark.gpu
 
@@ -40,6 +40,7 @@ def run(w, hint):
 
 
 def check_groups(w, d, rows=None):
+    """Random inputs: the capped truncation allowance."""
     G, cap, K = w.A.shape
     for g in range(G):
         m = int(min(max(w.masked_m[g], 0), cap))
@@ -47,13 +48,27 @@ def check_groups(w, d, rows=None):
         if not m:
             continue
         ref, r, s = oracle.gemm_nt_blockscaled(w.A[g, :m], w.B[g], w.sa[g], w.sb[g])
-        check(d[g, :m], r, s, 1.0, ref_bits=ref, what=f"{w.name} group {g}")
+        check(d[g, :m], r, s, 1.0, ref_bits=ref, what=f"{w.name} group {g}",
+              allowance=hw_allowance_blockscaled(w.A[g, :m], w.B[g], 0, 0, w.sa[g], w.sb[g], s),
+              max_allowed=random_cap(s.size, K))
 
 
 @pytest.mark.parametrize("hint", [0, 16, 32, 64])
 def test_swap_counts(hint):
     w = workloads.masked_blockscaled(8, 64, 520, 400, seed=60 + hint, m_values=[0, 1, 16, 17, 32, 33, 64, 40],
                                      lds_pad=5)
+    check_groups(w, run(w, hint))
+
+
+@pytest.mark.parametrize("hint", [96, 0])
+def test_wide_token_counts(hint):
+    """65..192 tokens per group with block scales: the swapped kernel with 8
+    (hint 96; counts above 128 take a second pass) or 12 (hint 0 = cap 192)
+    token blocks; NaN codes and scales behind every count."""
+    w = workloads.masked_blockscaled(6, 192, 520, 400, seed=66 + hint, m_values=[0, 65, 128, 129, 192, 100],
+                                     lds_pad=5)
+    p = _f().plan(1, 192, 520, 400, 6, hint)
+    assert p.variant == 3 and p.token_blocks == (8 if hint == 96 else 12)
     check_groups(w, run(w, hint))
 
 
@@ -118,7 +133,7 @@ def run_contig(w):
     return gpu_bits(out)
 
 
-def check_contig(w, d, rows=None):
+def check_contig(w, d, rows=None, seeded=False):
     pad = w.grp_idx < 0
     assert (d[pad] == SENT).all(), "a padding row was written"
     real = np.flatnonzero(~pad)
@@ -127,7 +142,10 @@ def check_contig(w, d, rows=None):
     for g in np.unique(w.grp_idx[real]):
         rg = real[w.grp_idx[real] == g]
         ref, r, s = oracle.gemm_nt_blockscaled(w.A[rg], w.B[g], w.sa[:, rg], w.sb[g])
-        check(d[rg], r, s, 1.0, ref_bits=ref, what=f"{w.name} expert {g}")
+        extra = {} if seeded else {
+            "allowance": hw_allowance_blockscaled(w.A[rg], w.B[g], 0, 0, w.sa[:, rg], w.sb[g], s),
+            "max_allowed": random_cap(s.size, w.A.shape[1])}
+        check(d[rg], r, s, 1.0, ref_bits=ref, what=f"{w.name} expert {g}", **extra)
 
 
 @pytest.mark.parametrize("counts", [[128, 256, 1, 127, 0, 300, 5], [100, 256, 300, 128]])
@@ -140,4 +158,4 @@ def test_contig_expert_changes(counts):
 
 def test_contig_prefill_sampled():
     w = workloads.contig_blockscaled(8192, 8, 32, 4096, 7168, seed=9)
-    check_contig(w, run_contig(w), rows=256)
+    check_contig(w, run_contig(w), rows=256, seeded=True)

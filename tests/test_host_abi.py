@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(f):
 
 
 def test_abi_version(f):
-    assert f.load_library().fp8_gemm_abi_version() == 3
+    assert f.load_library().fp8_gemm_abi_version() == 4
 
 
 @pytest.mark.parametrize("args,variant", [
@@ -73,13 +73,32 @@ def test_dense_plan_grid(f):
     assert (p.variant, p.tile_m, p.tile_n, p.workgroups) == (5, 256, 192, 8 * 63)
     p = f.plan(0, 2000, 14000, 1040)
     assert (p.variant, p.tile_m, p.tile_n, p.workgroups) == (6, 256, 224, 8 * 63)
-    p = f.plan(0, 17, 4096, 7168)                  # decode kernel: 16 weight rows per workgroup
-    assert p.token_blocks == 2 and p.tile_n == 16 and p.workgroups == 4096 // 16
-    # 32 rows per workgroup once that still gives >= 256 workgroups
-    assert (f.plan(0, 64, 8160, 4096).tile_n, f.plan(0, 64, 8160, 4096).workgroups) == (16, 510)
-    assert (f.plan(0, 64, 8192, 4096).tile_n, f.plan(0, 64, 8192, 4096).workgroups) == (32, 256)
-    assert (f.plan(0, 1, 14336, 4096).tile_n, f.plan(0, 1, 14336, 4096).workgroups) == (32, 448)
-    assert f.plan(3, 33, 8200, 1152).tile_n == 32  # block-scaled decode likewise
+    def dec(*a):
+        p = f.plan(*a)
+        assert p.variant == 4
+        return p.token_blocks, p.tile_n, p.k_splits, p.workgroups
+    # decode kernel: 16 weight rows per workgroup, 32 where that still gives
+    # >= 256 row blocks; K split over workgroups while the row blocks are
+    # fewer than 256, each split >= 4 K steps
+    assert dec(0, 1, 4096, 7168) == (1, 16, 1, 256)
+    assert dec(0, 17, 4096, 7168) == (2, 16, 1, 256)
+    assert dec(0, 64, 4096, 7168) == (4, 16, 1, 256)
+    assert dec(0, 64, 8160, 4096) == (4, 16, 1, 510)
+    assert dec(0, 64, 8192, 4096) == (4, 32, 1, 256)
+    assert dec(0, 1, 14336, 4096) == (1, 32, 1, 448)
+    assert dec(0, 64, 1024, 7168) == (4, 16, 4, 256)
+    assert dec(0, 64, 2000, 7168) == (4, 16, 3, 375)    # 56 K steps: 3 splits of 19, 19, 18
+    assert dec(0, 64, 1024, 512) == (4, 16, 1, 64)      # 4 K steps: no split
+    assert dec(0, 64, 1024, 1024) == (4, 16, 2, 128)    # 8 K steps: 2 splits of 4
+    assert dec(3, 33, 1000, 1152) == (4, 16, 2, 126)    # block-scaled decode likewise (9 steps: 5 + 4)
+    # small problems (M <= 256, at most 2 tiled workgroups): the decode kernel
+    # over 64-token tiles, one workgroup per 16 weight rows and token tile
+    assert dec(0, 256, 256, 256) == (4, 16, 1, 16 * 4)
+    assert dec(0, 65, 64, 128) == (4, 16, 1, 4 * 2)
+    assert dec(3, 200, 100, 1040) == (4, 16, 1, 7 * 4)
+    assert f.plan(0, 256, 256, 256).tile_m == 64
+    assert f.plan(0, 257, 256, 256).variant == 2         # M > 256: tiled
+    assert f.plan(0, 256, 257, 256).variant == 2         # 4 tiled workgroups: tiled
 
 
 def test_masked_plan_uses_hint_not_results(f):
@@ -90,8 +109,13 @@ def test_masked_plan_uses_hint_not_results(f):
     assert p.variant == 3 and p.tile_n == 256 and p.workgroups == 16 * (4096 // 256)
     p = f.plan(1, 64, 4096, 7168, 32, 0)           # hint 0 -> capacity
     assert p.variant == 3 and p.token_blocks == 4
-    p = f.plan(1, 256, 4096, 7168, 8, 0)           # many rows per group -> tiled
+    p = f.plan(1, 256, 4096, 7168, 8, 0)           # more than 192 rows per group -> tiled
     assert p.variant == 2 and p.workgroups == 8 * 2 * 16
+    # 65..192 rows: one pass over the weights with 8 or 12 token blocks, 64 weight rows per wave
+    for hint, cb in ((65, 8), (96, 8), (128, 8), (129, 12), (160, 12), (192, 12)):
+        p = f.plan(1, 256, 4096, 7168, 16, hint)
+        assert (p.variant, p.token_blocks, p.tile_n, p.workgroups) == (3, cb, 256, 16 * 16), hint
+    assert f.plan(1, 256, 4096, 7168, 16, 193).variant == 2
     with pytest.raises(f.Fp8GemmError) as e:
         f.plan(1, 64, 4096, 7168, 32, 65)          # hint above capacity
     assert e.value.status == -8
@@ -102,13 +126,18 @@ def test_contig_plan(f):
     # 256-row tiles, plus one workgroup per tile for a second expert in its
     # second 128-row block
     assert p.variant == 1 and p.tile_m == 256 and p.workgroups == 2 * (67584 // 256) * 16
+    # block-scaled: one workgroup per slot of two 128-row blocks and 256
+    # columns; it computes the run-aligned tiles that start in its slot
+    p = f.plan(5, 67584, 4096, 7168, 32)
+    assert p.variant == 1 and p.tile_m == 256 and p.workgroups == (67584 // 256) * 16
+    assert f.plan(5, 67584 + 128, 4096, 7168, 32).workgroups == (67584 // 256 + 1) * 16
 
 
 @pytest.mark.parametrize("args,status", [
     ((0, 10, 10, 17), -2),       # K % 16
     ((0, -1, 10, 16), -2),
     ((0, 10, 10, 1 << 23), -2),  # K above the stride limit
-    ((5, 10, 10, 16), -8),       # unknown op
+    ((6, 10, 10, 16), -8),       # unknown op
     ((4, 10, 10, 12), -2),       # BF16: K % 8
     ((4, 10, 10, 1 << 22), -2),  # BF16: 2 K bytes above the stride limit
 ])
@@ -198,7 +227,7 @@ def test_blockscaled_plan(f):
     p = f.plan(3, 4096, 4096, 4096)
     assert (p.variant, p.tile_m, p.workgroups) == (1, 256, 256)
     p = f.plan(3, 17, 4096, 7168)                  # few tokens: the decode kernel
-    assert p.variant == 4 and p.tile_n == 16 and p.workgroups == 256
+    assert p.variant == 4 and p.tile_n == 16 and p.k_splits == 1 and p.workgroups == 256
 
 
 def test_blockscaled_validation(f):

@@ -707,6 +707,77 @@ def _trace_durations(directory, pattern):
     return durs
 
 
+def trace_summary(trace_dir, bench_json, command):
+    """Writes profiles/bench_kernel_trace.txt from a `rocprofv3 --kernel-trace
+    --stats` run of the default bench: rocprofv3's per-kernel statistics, then
+    per kernel and grid the dispatch count and mean / median / min duration
+    (warm-up and timed launches alike), and beside them the launch durations
+    the same bench run measured with its HIP events."""
+    import csv
+    import gzip
+    import glob
+    import statistics
+
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    traces = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv*"), recursive=True)
+    if not stats or not traces:
+        raise SystemExit(f"no kernel_stats.csv / kernel_trace.csv under {trace_dir}")
+    groups = {}
+    for fpath in traces:
+        opener = gzip.open if fpath.endswith(".gz") else open
+        with opener(fpath, "rt", newline="") as fh:
+            for row in csv.DictReader(fh):
+                name = row["Kernel_Name"]
+                if "fp8g::" not in name and "Cijk" not in name:
+                    continue
+                short = re.sub(r"^void fp8g::|\(fp8g::GemmParams\)$", "", name)
+                wg = int(row["Workgroup_Size_X"]) * int(row["Workgroup_Size_Y"]) * int(row["Workgroup_Size_Z"])
+                grid = (int(row["Grid_Size_X"]) * int(row["Grid_Size_Y"]) * int(row["Grid_Size_Z"])) // max(wg, 1)
+                d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-3
+                groups.setdefault((short, grid), []).append(d)
+    bench = {}
+    with open(bench_json) as fh:
+        for line in fh:
+            if line.startswith("{") and '"metric"' in line:
+                bench = json.loads(line)
+    lines = [
+        "rocprofv3 kernel trace of the default benchmark run (every leg; warm-up launches included)",
+        "",
+        "command (on the GPU host, from the repository root R):",
+        command,
+        "",
+        f"kernel_source_hash: {kernel_source_hash()}",
+        "",
+        "kernel_stats.csv (rocprofv3 --stats):",
+    ]
+    with open(stats[0]) as fh:
+        for row in csv.reader(fh):
+            if row[0] == "Name" or "fp8g::" in row[0] or "Cijk" in row[0]:
+                lines.append(",".join(row[:7]))
+    lines += ["", "per kernel and grid (workgroups): dispatches, mean / median / min duration in us"]
+    for (short, grid), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"  {short:60s} grid {grid:6d}: {len(ds):6d}  {statistics.mean(ds):10.2f} "
+                     f"{statistics.median(ds):10.2f} {min(ds):10.2f}")
+    if bench:
+        r = bench["roofline"]
+        lines += ["", "the same run's HIP-event figures (bench.py's JSON line):",
+                  f"  dense 4096^3 E4M3 (tile16_kernel<256, 256, 2, 0, 0, 0, 0, false>, grid 256): "
+                  f"mean {r['kernel_ms_mean'] * 1e3:.2f} us, median {r['us_median']:.2f} us, "
+                  f"{r['achieved']:.0f} TFLOP/s"]
+        for key, label in (("dense_4096_e5m2", "dense 4096^3 E5M2"), ("dense_4096_blockscaled", "block-scaled 4096^3"),
+                           ("dense_4096_channelwise", "per-channel 4096^3"), ("masked_grouped", "masked decode"),
+                           ("masked_grouped_blockscaled", "block-scaled masked decode"),
+                           ("contig_grouped", "contiguous prefill"),
+                           ("contig_grouped_blockscaled", "block-scaled contiguous prefill")):
+            if key in bench:
+                lines.append(f"  {label}: mean {bench[key]['kernel_ms_mean'] * 1e3:.2f} us, "
+                             f"median {bench[key]['us_median']:.2f} us")
+    path = os.path.join(PROFILE_DIR, "bench_kernel_trace.txt")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    log(f"wrote {path}")
+
+
 SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
                "SQ_INSTS_LDS", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "GRBM_GUI_ACTIVE", "GRBM_COUNT")
 
@@ -735,6 +806,10 @@ def counters_summary(trace_dir, fetch_dir, write_dir, sq_dir, command, work_json
         for c in SQ_COUNTERS:
             sq[c] = _per_dispatch(sr, pattern, c)[0]
         cyc, pmc_dur, clock, mfma_busy, npmc = _clock_and_busy(sr, sq_durs, pattern)
+        # GRBM_GUI_ACTIVE counts the whole collection window; for a dispatch of
+        # a few microseconds that window is longer than the kernel, and the
+        # ratio reads above any clock the part runs at
+        clock_ok = clock <= 1.05 * copy_clk
         w = work.get(name, {})
         lines = [
             f"rocprofv3 counters: {what}",
@@ -770,14 +845,18 @@ def counters_summary(trace_dir, fetch_dir, write_dir, sq_dir, command, work_json
             "the launches and lengthens them):",
             f"  dispatch duration in this pass: {pmc_dur * 1e6:.2f} us",
             f"  kernel cycles (GRBM_GUI_ACTIVE / 8 XCDs): {cyc:.0f}",
-            f"  effective_clock_ghz: {clock:.3f}  (kernel cycles / dispatch duration; the memory-bound 1 GiB copy "
-            f"reads {copy_clk:.3f} GHz the same way)",
-            f"  mfma_busy_fraction: {mfma_busy:.4f}  (SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x kernel cycles); the "
-            f"counter counts each 16x16x128 FP8 instruction as 32 cycles)",
+            (f"  effective_clock_ghz: {clock:.3f}  (kernel cycles / dispatch duration; the memory-bound 1 GiB copy "
+             f"reads {copy_clk:.3f} GHz the same way)") if clock_ok else
+            (f"  effective clock: not measurable ({clock:.3f} GHz from the ratio, above the copy's {copy_clk:.3f}: "
+             f"the counter window is longer than this short dispatch)"),
+            (f"  mfma_busy_fraction: {mfma_busy:.4f}  (SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x kernel cycles); the "
+             f"counter counts each 16x16x128 FP8 instruction as 32 cycles)") if clock_ok else
+            (f"  MFMA busy: at most {mfma_busy:.4f} of the counter window (SQ_VALU_MFMA_BUSY_CYCLES / "
+             f"(1024 SIMDs x window cycles))"),
             f"  lds_bank_conflict_fraction: {sq['SQ_LDS_BANK_CONFLICT'] / sq['SQ_LDS_IDX_ACTIVE'] if sq['SQ_LDS_IDX_ACTIVE'] else 0.0:.4f}"
             f"  (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE)",
         ]
-        if w.get("flops"):
+        if w.get("flops") and clock_ok:
             lines.append(f"  MFMA-bound time at the effective clock: {w['flops'] / (SIMDS * 2048.0 * clock * 1e9) * 1e6:.2f} us "
                          f"(against {dur * 1e6:.2f} us traced)")
         path = os.path.join(PROFILE_DIR, f"{stem}_counters.txt")
@@ -802,10 +881,15 @@ def main():
     ap.add_argument("--counters-command", default="",
                     help="the commands that produced the counter directories (recorded in the summaries)")
     ap.add_argument("--counters-work", default="", help="the JSON line --profile-run printed")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                    help="write profiles/bench_kernel_trace.txt from a --kernel-trace --stats run of the bench")
     args = ap.parse_args()
 
     if args.counters_summary:
         counters_summary(*args.counters_summary, args.counters_command, args.counters_work)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary, args.counters_command)
         return
 
     if args.gpus != 1:

@@ -38,7 +38,7 @@ class Plan(ctypes.Structure):
                 ("token_blocks", ctypes.c_int), ("workgroups", ctypes.c_int64), ("k_splits", ctypes.c_int)]
 
 
-SYMBOLS = ("fp8_gemm_nt", "fp8_gemm_nt_blockscaled", "fp8_gemm_nt_channelwise",
+SYMBOLS = ("fp8_gemm_nt", "fp8_gemm_nt_noalloc", "fp8_gemm_nt_blockscaled", "fp8_gemm_nt_channelwise",
            "fp8_grouped_gemm_masked_blockscaled", "fp8_grouped_gemm_contig_blockscaled", "fp8_grouped_gemm_masked", "fp8_grouped_gemm_contig",
            "bf16_gemm_nt", "fp8_gemm_plan", "fp8_gemm_strerror", "fp8_gemm_abi_version")
 
@@ -54,6 +54,8 @@ def load_library(path: str = LIB_PATH):
     P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.fp8_gemm_nt.argtypes = [P, I64, I, P, I64, I, P, P, P, I64, I, I, I, P]
     lib.fp8_gemm_nt.restype = I
+    lib.fp8_gemm_nt_noalloc.argtypes = [P, I64, I, P, I64, I, P, P, P, I64, I, I, I, P]
+    lib.fp8_gemm_nt_noalloc.restype = I
     lib.fp8_gemm_nt_blockscaled.argtypes = [P, I64, I, P, I64, I, P, I64, P, I64, P, I64, I, I, I, P]
     lib.fp8_gemm_nt_blockscaled.restype = I
     lib.fp8_gemm_nt_channelwise.argtypes = [P, I64, I, P, I64, I, P, P, P, P, I64, I, I, I, P]
@@ -134,9 +136,14 @@ def _stream():
     return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
 
 
-def gemm_nt(a, b, scale_a, scale_b, out=None, a_dtype=None, b_dtype=None):
-    """D[M, N] = bf16(scale_a * scale_b * a[M, K] . b[N, K]^T)."""
+def gemm_nt(a, b, scale_a, scale_b, out=None, a_dtype=None, b_dtype=None, no_alloc=False):
+    """D[M, N] = bf16(scale_a * scale_b * a[M, K] . b[N, K]^T).  no_alloc:
+    call fp8_gemm_nt_noalloc (the library's fixed scratch array instead of
+    its workspace; `out` must then be given, so nothing is allocated here
+    either)."""
     torch = _torch()
+    if no_alloc and out is None:
+        raise ValueError("no_alloc=True needs out")
     fa = _fp8_code(a, a_dtype, "a")
     fb = _fp8_code(b, b_dtype, "b")
     if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
@@ -162,7 +169,8 @@ def gemm_nt(a, b, scale_a, scale_b, out=None, a_dtype=None, b_dtype=None):
     ldb = b.stride(0) if (N > 1 and K > 0) else max(16, ((K + 15) // 16) * 16)
     ldd = out.stride(0) if M > 1 else max(8, ((N + 7) // 8) * 8)
     lib = load_library()
-    _check(lib.fp8_gemm_nt(a.data_ptr(), lda, fa, b.data_ptr(), ldb, fb, scale_a.data_ptr(), scale_b.data_ptr(), out.data_ptr(),
+    fn = lib.fp8_gemm_nt_noalloc if no_alloc else lib.fp8_gemm_nt
+    _check(fn(a.data_ptr(), lda, fa, b.data_ptr(), ldb, fb, scale_a.data_ptr(), scale_b.data_ptr(), out.data_ptr(),
               ldd, M, N, K, _stream()))
     return out
 

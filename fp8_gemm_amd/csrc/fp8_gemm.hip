@@ -511,6 +511,64 @@ int decode_workspace(const fp8g_plan &plan, hipStream_t s, SplitWs &ws) {
     return split_workspace(s, ws);
 }
 
+__global__ void clear_counts(int *count, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) count[i] = 0;
+}
+
+}  // namespace
+
+// Scratch of the allocation-free entry point (fp8_gemm_nt_noalloc): the
+// split-K workspace's layout and bound (kSplitWsBytes: 8 MiB of partial sums
+// and 256 counts) in a device array of this library's code object.  Each
+// device holds its own copy, from the library's load until the process ends.
+// In host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress (scratch_workspace below).
+static __device__ __align__(256) unsigned char scratch[kSplitWsBytes];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+SplitWs g_scratch[64];
+
+// The scratch array of the current device as a split-K workspace.  The first
+// call on a device looks up the array's address there (and keeps it) and
+// clears its counts with a small kernel on `stream` (no memset: the call may
+// be captured into a graph); no memory is allocated.
+int scratch_workspace(hipStream_t stream, SplitWs &ws) {
+    ws = SplitWs{};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(FP8G_ERR_UNSUPPORTED, "no usable HIP device");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[dev].partial) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(FP8G_ERR_LAUNCH, "no address for the scratch array on device %d: %s", dev, hipGetErrorString(e));
+        int *count = reinterpret_cast<int *>(static_cast<char *>(ptr) + kSplitPartialBytes);
+        hipLaunchKernelGGL(clear_counts, dim3(1), dim3(kSplitMaxBlocks), 0, stream, count, kSplitMaxBlocks);
+        const hipError_t le = hipGetLastError();
+        if (le != hipSuccess) return fail(FP8G_ERR_LAUNCH, "clearing the scratch counts failed: %s", hipGetErrorString(le));
+        g_scratch[dev].partial = static_cast<float *>(ptr);
+        g_scratch[dev].count = count;
+    }
+    ws = g_scratch[dev];
+    return ok();
+}
+
+// The scratch a decode plan needs, from the scratch array; sizes beyond the
+// array are refused (none arise: see kSplitWsBytes).
+int decode_scratch(const fp8g_plan &plan, hipStream_t s, SplitWs &ws) {
+    ws = SplitWs{};
+    if (plan.variant != V_DECODE || plan.k_splits <= 1) return ok();
+    const int64_t blocks = plan.workgroups / plan.k_splits;
+    const int64_t need = plan.workgroups * (int64_t)(plan.tile_n / 16) * plan.token_blocks * 64 * 16;
+    if (blocks > kSplitMaxBlocks || need > (int64_t)kSplitPartialBytes)
+        return fail(FP8G_ERR_ARG, "the split-K sums need %lld bytes and %lld counts, above the scratch maximum "
+                    "of %zu bytes and %d counts", (long long)need, (long long)blocks, kSplitPartialBytes, kSplitMaxBlocks);
+    return scratch_workspace(s, ws);
+}
+
 }  // namespace
 
 extern "C" {
@@ -545,10 +603,11 @@ int fp8_gemm_plan(int op, int m, int n, int k, int groups, int expected_m, fp8g_
 
 namespace {
 
-// The body of fp8_gemm_nt.
+// fp8_gemm_nt and fp8_gemm_nt_noalloc: the same kernels; the split-K decode
+// path's workspace is the library-allocated one or the scratch array.
 int gemm_nt_impl(const void *A, int64_t lda, int a_dtype, const void *B, int64_t ldb, int b_dtype,
                  const float *scale_a, const float *scale_b, void *D, int64_t ldd, int M, int N, int K,
-                 void *stream) {
+                 void *stream, bool no_alloc) {
     if (!dtype_ok(a_dtype) || !dtype_ok(b_dtype)) return fail(FP8G_ERR_DTYPE, "dtypes %d, %d", a_dtype, b_dtype);
     fp8g_plan plan;
     int st = plan_impl(0, M, N, K, 1, 0, &plan);
@@ -576,7 +635,7 @@ int gemm_nt_impl(const void *A, int64_t lda, int a_dtype, const void *B, int64_t
     const int fa = a_dtype, fb = b_dtype;
     if (plan.variant == V_DECODE) {
         SplitWs ws;
-        st = decode_workspace(plan, s, ws);
+        st = no_alloc ? decode_scratch(plan, s, ws) : decode_workspace(plan, s, ws);
         if (st != FP8G_OK) return st;
         return launch_decode<fp8g::SCALE_TENSOR>(plan, fa, fb, p, ws, s);
     }
@@ -596,7 +655,13 @@ extern "C" {
 int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype, const void *B, int64_t ldb, int b_dtype,
                 const float *scale_a, const float *scale_b, void *D, int64_t ldd, int M, int N, int K,
                 void *stream) {
-    return gemm_nt_impl(A, lda, a_dtype, B, ldb, b_dtype, scale_a, scale_b, D, ldd, M, N, K, stream);
+    return gemm_nt_impl(A, lda, a_dtype, B, ldb, b_dtype, scale_a, scale_b, D, ldd, M, N, K, stream, false);
+}
+
+int fp8_gemm_nt_noalloc(const void *A, int64_t lda, int a_dtype, const void *B, int64_t ldb, int b_dtype,
+                        const float *scale_a, const float *scale_b, void *D, int64_t ldd, int M, int N, int K,
+                        void *stream) {
+    return gemm_nt_impl(A, lda, a_dtype, B, ldb, b_dtype, scale_a, scale_b, D, ldd, M, N, K, stream, true);
 }
 
 int bf16_gemm_nt(const void *A, int64_t lda, const void *B, int64_t ldb, void *D, int64_t ldd, int M, int N, int K,

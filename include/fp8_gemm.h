@@ -104,6 +104,25 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype,
                 int M, int N, int K, void *stream);
 
 /*
+ * fp8_gemm_nt for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, kernels and results, but the split-K few-token path keeps
+ * its partial sums in a fixed scratch array inside the library's code object
+ * (8 MiB of FP32 sums and 256 arrival counts per device, held from the
+ * library's load until the process ends) instead of a workspace allocated on
+ * first use.  It calls no allocation routine.  Every shape fits the array
+ * (the split-K path splits only while fewer than 256 blocks of weight rows
+ * exist); a larger need would be refused with FP8G_ERR_ARG.  All calls on a
+ * device share its array, which keeps the last call's contents (the counts
+ * return to zero after every call): calls that overlap on one device race.
+ */
+int fp8_gemm_nt_noalloc(const void *A, int64_t lda, int a_dtype,
+                        const void *B, int64_t ldb, int b_dtype,
+                        const float *scale_a, const float *scale_b,
+                        void *D, int64_t ldd,
+                        int M, int N, int K, void *stream);
+
+/*
  * Block-scaled dense GEMM, "nt" layout, with power-of-two block scales: one
  * per row of A and 128-element block of K, one per 128 rows of B and
  * 128-element block of K ("DeepGEMM: FP8 matrix-multiply kernels on Hopper

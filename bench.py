@@ -542,7 +542,7 @@ COUNTER_TARGETS = {
                       "masked grouped decode GEMM G=32 cap=64 N=4096 K=7168 m_g~U{0..32} (seed 4)"),
     "contig_prefill": ("ring_kernel_contig_prefill", "ring_kernel<256, 256, 4, 2, 0, 0, 2, 2, 128, 0>",
                        "contiguous grouped prefill GEMM, 65536 routed rows over 32 experts, N=4096 K=7168 (seed 5)"),
-    "decode_64": ("decode_kernel_dense_64x4096x7168", "decode_kernel<4, 1, 4, 0, 0, 2, 0>",
+    "decode_64": ("decode_kernel_dense_64x4096x7168", "decode_kernel<4, 1, 4, 0, 0, 2, 0, 1>",
                   "dense few-token GEMM M=64 N=4096 K=7168 (seed 13)"),
 }
 COPY_PATTERN = "neg_kernel"

@@ -125,13 +125,15 @@ DecodeShape decode_shape(int64_t m, int64_t n, int64_t k) {
 
 // Workspace of the split-K few-token path, per device: the FP32 partial sums
 // of the splits (16 RB x 16 CB outputs, at most 64 x 64, per workgroup) and
-// one arrival count per block of weight rows.  Splits happen only with fewer
-// than 256 blocks, so blocks x splits < 256 + blocks < 512 workgroups: at most
-// 512 x 16 KiB of partial sums and 256 counts, whatever the shape.
+// one arrival count per block of weight rows, each in its own 128-byte line.
+// Splits happen only with fewer than 256 blocks, so blocks x splits < 256 +
+// blocks < 512 workgroups: at most 512 x 16 KiB of partial sums and 256
+// counts (32 KiB), whatever the shape.
 constexpr int kSplitMaxWgs = 512;
 constexpr int kSplitMaxBlocks = 256;
 constexpr size_t kSplitPartialBytes = (size_t)kSplitMaxWgs * 64 * 64 * sizeof(float);
-constexpr size_t kSplitWsBytes = kSplitPartialBytes + kSplitMaxBlocks * sizeof(int);
+constexpr size_t kSplitCountBytes = (size_t)kSplitMaxBlocks * fp8g::kCountStride * sizeof(int);
+constexpr size_t kSplitWsBytes = kSplitPartialBytes + kSplitCountBytes;
 
 // Masked form with 65..192 tokens per group ("wide"): 8 or 12 token blocks
 // in one pass over the weights, 64 weight rows per wave (the accumulators of
@@ -174,7 +176,9 @@ void fill_decode_plan(int m, int n, int k, fp8g_plan *out) {
     out->tile_n = 16 * d.rb;
     out->token_blocks = d.cb;
     out->k_splits = d.splits;
-    out->workgroups = (int64_t)d.blocks * d.splits;
+    // split K: 8 ceil(blocks / 8) x splits workgroups, so that all splits of
+    // a block run on one XCD (the kernel's placement)
+    out->workgroups = d.splits > 1 ? (int64_t)8 * cdiv(d.blocks, 8) * d.splits : (int64_t)d.blocks;
 }
 
 // Small problems (M <= 256 where the tiled kernel would start at most 2
@@ -450,7 +454,7 @@ int split_workspace(hipStream_t stream, SplitWs &ws) {
         if (hipMalloc(&mem, kSplitWsBytes) != hipSuccess)
             return fail(FP8G_ERR_LAUNCH, "cannot allocate the %zu-byte split-K workspace", kSplitWsBytes);
         int *count = reinterpret_cast<int *>(static_cast<char *>(mem) + kSplitPartialBytes);
-        if (hipMemsetAsync(count, 0, kSplitMaxBlocks * sizeof(int), stream) != hipSuccess) {
+        if (hipMemsetAsync(count, 0, kSplitCountBytes, stream) != hipSuccess) {
             (void)hipFree(mem);
             return fail(FP8G_ERR_LAUNCH, "cannot clear the split-K workspace");
         }
@@ -461,12 +465,25 @@ int split_workspace(hipStream_t stream, SplitWs &ws) {
     return ok();
 }
 
+// Grids of at most 256 workgroups take the one-per-CU build, with 16 KB of
+// dynamic LDS that takes every instance past 80 KB, so that no CU holds two
+// of them while another holds none; larger grids take the two-per-CU build
+// (N = 7168, 448 workgroups: 10.07 -> 9.38 us at M = 1, K = 4096).
+constexpr unsigned kDecodeSpreadPad = 16 * 1024;
+
 template <int RB, int CB, int SCL>
 int launch_decode_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     constexpr int D = RB == 1 ? (CB == 1 ? 5 : (CB == 2 ? 3 : 2)) : (CB == 1 ? 3 : 2);
     const dim3 block(64 * kDecodeWaves);
-#define FP8G_DEC(FA, FB) \
-    hipLaunchKernelGGL((fp8g::decode_kernel<kDecodeWaves, RB, CB, FA, FB, D, SCL>), grid, block, 0, s, p)
+    const bool one = (int64_t)grid.x * grid.y <= 256;
+#define FP8G_DEC(FA, FB)                                                                                   \
+    do {                                                                                                    \
+        if (one)                                                                                            \
+            hipLaunchKernelGGL((fp8g::decode_kernel<kDecodeWaves, RB, CB, FA, FB, D, SCL, 1>), grid, block, \
+                               kDecodeSpreadPad, s, p);                                                     \
+        else                                                                                                \
+            hipLaunchKernelGGL((fp8g::decode_kernel<kDecodeWaves, RB, CB, FA, FB, D, SCL, 2>), grid, block, 0, s, p); \
+    } while (0)
     if (fa == 0 && fb == 0) FP8G_DEC(0, 0);
     else if (fa == 0 && fb == 1) FP8G_DEC(0, 1);
     else if (fa == 1 && fb == 0) FP8G_DEC(1, 0);
@@ -487,19 +504,19 @@ int launch_decode_rb(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hip
 template <int SCL>
 int launch_decode(const fp8g_plan &plan, int fa, int fb, GemmParams p, const SplitWs &ws, hipStream_t s) {
     const int rb = plan.tile_n / 16, cb = plan.token_blocks;
-    int64_t wgs = plan.workgroups;
+    // x: one workgroup per block of weight rows; y: the 64-token tiles (all M
+    // at once for M <= 64), or (split K, M <= 64) the splits, x then padded
+    // to a multiple of 8 so that all splits of a block run on one XCD
+    const unsigned mtiles = p.M > kSwapMaxM ? (unsigned)cdiv(p.M, 64) : 1u;
+    dim3 grid((unsigned)cdiv(p.N, 16 * rb), mtiles);
     p.splits = 1;
     if (plan.k_splits > 1 && ws.partial) {
         p.splits = plan.k_splits;
         p.ksteps = (int)cdiv(cdiv(p.K, 128), plan.k_splits);
         p.ws = ws.partial;
         p.cnt = ws.count;
-    } else {
-        wgs /= plan.k_splits;
+        grid = dim3((unsigned)(8 * cdiv(grid.x, 8)), (unsigned)plan.k_splits);
     }
-    // token tiles along y: all M at once for M <= 64, else 64-row tiles
-    const unsigned mtiles = p.M > kSwapMaxM ? (unsigned)cdiv(p.M, 64) : 1u;
-    const dim3 grid((unsigned)(wgs / mtiles), mtiles);
     if (rb == 2) return launch_decode_rb<2, SCL>(cb, fa, fb, p, grid, s);
     return launch_decode_rb<1, SCL>(cb, fa, fb, p, grid, s);
 }
@@ -513,7 +530,7 @@ int decode_workspace(const fp8g_plan &plan, hipStream_t s, SplitWs &ws) {
 
 __global__ void clear_counts(int *count, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) count[i] = 0;
+    if (i < n) count[fp8g::kCountStride * i] = 0;
 }
 
 }  // namespace

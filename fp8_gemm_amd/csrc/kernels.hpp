@@ -69,11 +69,15 @@ struct GemmParams {
     // Few-token form with K split over workgroups (splits > 1): `splits`
     // workgroups per block of weight rows take `ksteps` 128-byte K steps each,
     // leave their FP32 partial sums in ws, and count their arrivals in
-    // cnt[block]; the last to arrive adds the partial sums in split order.
+    // cnt[kCountStride * block]; the last to arrive adds the partial sums in
+    // split order.
     float *ws;
     int *cnt;
     int splits, ksteps;
 };
+
+// Ints per arrival count of the split-K workspace: one 128-byte line each.
+constexpr int kCountStride = 32;
 
 // Epilogue terms of the per-channel form for four consecutive output channels
 // n .. n+3: their scales and biases.  Channels at or past N take scale 0 and
@@ -1413,9 +1417,13 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
 //   wave, each holding one K step of the 16 weight rows and the CB token blocks
 //   (and, with block scales, that step's scale bytes); the partial sums of the
 //   waves are added through LDS at the end.
+//   OCC: workgroups per CU the build allows for.  Grids of at most 256
+//   workgroups run one per CU (OCC = 1: the compiler may keep the
+//   accumulators in AGPRs, which gave the faster loop: 7.45 against 7.74 us
+//   at M = 1, N = 4096, K = 7168); larger grids share CUs two at a time.
 // ---------------------------------------------------------------------------
-template <int WAVES, int RB, int CB, int FA, int FB, int D, int SCL>
-__global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
+template <int WAVES, int RB, int CB, int FA, int FB, int D, int SCL, int OCC>
+__global__ __launch_bounds__(64 * WAVES, OCC) void decode_kernel(GemmParams p) {
     constexpr bool BLK = SCL == SCALE_BLOCK, CHN = SCL == SCALE_CHANNEL;
     constexpr int NB = RB + CB;                    // 16-row blocks per step: RB of weights, then CB of tokens
     constexpr int NQ = 2 * NB + (BLK ? 2 : 0);     // DMA instructions per step (8 rows x 128 B each,
@@ -1431,19 +1439,29 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // workgroup = (block of 16 RB weight rows, split of the K steps); the
-    // splits of one block are neighbours in dispatch order
+    // workgroup = (block of 16 RB weight rows, split of the K steps).  Split
+    // K: the grid is 8 ceil(blocks / 8) x splits, workgroup (x, y) taking
+    // block x and split y.  Workgroups go to the 8 XCDs in turn in the order
+    // x + y 8 ceil(blocks / 8), so all splits of a block run on one XCD and
+    // meet in its L2 (see the exchange below).  Those of blocks past the last
+    // (live false) read nothing (no rows in their descriptors) and leave
+    // before the exchange; an exit at the top made the compiler load the
+    // remaining kernel arguments only after the branch, a second round of
+    // scalar loads that cost every launch ~0.3 us.  Unsplit, grid y counts
+    // the 64-token tiles of the small-shape class.
     const int splits = max(p.splits, 1);
-    const int nb = blockIdx.x / splits, sp = blockIdx.x % splits;
+    const int nb = blockIdx.x;
+    const int sp = splits > 1 ? (int)blockIdx.y : 0;
+    const bool live = nb < (p.N + 16 * RB - 1) / (16 * RB);
     const int n0 = nb * 16 * RB;
-    const int rows_w = min(p.N - n0, 16 * RB);
+    const int rows_w = live ? min(p.N - n0, 16 * RB) : 0;
     // Rows past N (weights) or past M (tokens) lie outside the descriptors and
     // read zeros without touching memory.
     const v4i srdW = make_srd(p.B + (int64_t)n0 * p.ldb, rows_bytes(rows_w, p.ldb));
     // token tile: all M tokens (M <= 64), or 64-row tile blockIdx.y of them
     // (the small-shape class, never split over K)
-    const int tm0 = blockIdx.y * 64;
-    const int rows_t = min(p.M - tm0, 64);
+    const int tm0 = splits > 1 ? 0 : (int)blockIdx.y * 64;
+    const int rows_t = live ? min(p.M - tm0, 64) : 0;
     const v4i srdT = make_srd(p.A + (int64_t)tm0 * p.lda, rows_bytes(rows_t, p.lda));
     const int nk = (p.K + 127) / 128;
     // this split's K steps [kt0, kt1), taken by the waves round-robin
@@ -1573,18 +1591,23 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
         sums[j] = sum;
     }
     if (splits > 1) {
+        if (!live) return;                         // (uniform: padding workgroup)
         // Split K: leave this split's partial sums, then count the arrival.
-        // The sums are written and read with system-coherent cache bits (sc0
-        // sc1: through the XCD's L2, which is not coherent with the other
-        // XCDs' L2s, to memory and back), and the stores have completed before
+        // All splits of the block run on one XCD, so they meet in its L2: the
+        // sums are stored plainly (the vector L1 writes through to the L2),
+        // the count is an L2 atomic, and the last split reads the sums with
+        // sc0 (past its L1, from the L2).  The stores have completed before
         // the count moves, so the last split sees every other split's sums.
-        // Device-wide fences would do the same by writing back and
-        // invalidating the whole L2, which also evicts the token tiles every
-        // workgroup rereads (measured 4x slower).  The last split of the block
-        // to arrive adds all of them in split order 0, 1, ..., so the result
-        // does not depend on which split finished last, and resets the count
-        // for the next call.
-        constexpr int kCoherent = 1 | 16;          // sc0 | sc1
+        // Each count sits alone in a 128-byte line, so that no line is
+        // updated in two XCDs' L2s, which are not coherent with each other.
+        // (Sums and count written through to memory with sc0 sc1 and a
+        // system-scope atomic, for splits spread over the XCDs, took 8.02
+        // against 7.07 us at M = 64, N = 1024, K = 7168; device-wide fences,
+        // which write back and invalidate the whole L2, were 4x slower.)  The
+        // last split of the block to arrive adds all of them in split order
+        // 0, 1, ..., so the result does not depend on which split finished
+        // last, and resets the count for the next call.
+        constexpr int kStore = 0, kLoad = 1;       // cache bits: plain store, sc0 load
         const int64_t base = (int64_t)nb * splits * NBLK * 64 * 16;
         const __amdgpu_buffer_rsrc_t part = make_rsrc(reinterpret_cast<const uint8_t *>(p.ws) + base,
                                                       (uint32_t)(splits * NBLK * 64 * 16));
@@ -1593,26 +1616,31 @@ __global__ __launch_bounds__(64 * WAVES, 2) void decode_kernel(GemmParams p) {
             const int idx = wave + WAVES * j;
             if (idx < NBLK)
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, sums[j]), part,
-                                                       (uint32_t)(((sp * NBLK + idx) * 64 + lane) * 16), 0, kCoherent);
+                                                       (uint32_t)(((sp * NBLK + idx) * 64 + lane) * 16), 0, kStore);
         }
-        __shared__ int last_split;
-        vmcnt_wait<0>();                           // this thread's sums are in memory
+        // (the flag takes the ring's first bytes: every wave has read its
+        // share of the reduction by the first barrier below; a variable of
+        // its own would take the LDS past 80 KB, one workgroup per CU)
+        int *const last_split = reinterpret_cast<int *>(smem);
+        vmcnt_wait<0>();                           // this thread's sums are in the L2
         __syncthreads();                           // and every thread's
         if (threadIdx.x == 0)
-            last_split = __hip_atomic_fetch_add(p.cnt + nb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == splits - 1;
+            *last_split = __hip_atomic_fetch_add(p.cnt + kCountStride * nb, 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
         __syncthreads();
-        if (!last_split) return;
+        if (!*last_split) return;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int idx = wave + WAVES * j;
             if (idx >= NBLK) break;
-            v4f sum = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(part, (uint32_t)((idx * 64 + lane) * 16), 0, kCoherent));
+            v4f sum = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(part, (uint32_t)((idx * 64 + lane) * 16), 0, kLoad));
             for (int t = 1; t < splits; ++t)
                 sum += __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   part, (uint32_t)(((t * NBLK + idx) * 64 + lane) * 16), 0, kCoherent));
+                                                   part, (uint32_t)(((t * NBLK + idx) * 64 + lane) * 16), 0, kLoad));
             sums[j] = sum;
         }
-        if (threadIdx.x == 0) __hip_atomic_exchange(p.cnt + nb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (threadIdx.x == 0)
+            __hip_atomic_exchange(p.cnt + kCountStride * nb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {

@@ -27,7 +27,7 @@
  *   - Workspace: the dense forms with M <= 64 split K over workgroups when
  *     the weight rows alone would leave the chip part-empty (fewer than 256
  *     blocks of 16-64 rows).  The splits' FP32 partial sums meet in a
- *     workspace of 8 MiB + 1 KiB per device, which the library allocates
+ *     workspace of 8 MiB + 32 KiB per device, which the library allocates
  *     with hipMalloc on the first such call on that device (and keeps until
  *     the process ends); if that first call happens while `stream` is being
  *     captured into a graph, it runs unsplit instead (nothing allocated; the
@@ -108,7 +108,8 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype,
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same arguments, kernels and results, but the split-K few-token path keeps
  * its partial sums in a fixed scratch array inside the library's code object
- * (8 MiB of FP32 sums and 256 arrival counts per device, held from the
+ * (8 MiB of FP32 sums and 256 arrival counts of 128 bytes each per device,
+ * 8 MiB + 32 KiB, held from the
  * library's load until the process ends) instead of a workspace allocated on
  * first use.  It calls no allocation routine.  Every shape fits the array
  * (the split-K path splits only while fewer than 256 blocks of weight rows

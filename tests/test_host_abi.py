@@ -79,7 +79,8 @@ def test_dense_plan_grid(f):
         return p.token_blocks, p.tile_n, p.k_splits, p.workgroups
     # decode kernel: 16 weight rows per workgroup, 32 where that still gives
     # >= 256 row blocks; K split over workgroups while the row blocks are
-    # fewer than 256, each split >= 4 K steps
+    # fewer than 256, each split >= 4 K steps, over 8 ceil(blocks / 8) x
+    # splits workgroups (all splits of a block on one XCD)
     assert dec(0, 1, 4096, 7168) == (1, 16, 1, 256)
     assert dec(0, 17, 4096, 7168) == (2, 16, 1, 256)
     assert dec(0, 64, 4096, 7168) == (4, 16, 1, 256)
@@ -87,10 +88,10 @@ def test_dense_plan_grid(f):
     assert dec(0, 64, 8192, 4096) == (4, 32, 1, 256)
     assert dec(0, 1, 14336, 4096) == (1, 32, 1, 448)
     assert dec(0, 64, 1024, 7168) == (4, 16, 4, 256)
-    assert dec(0, 64, 2000, 7168) == (4, 16, 3, 375)    # 56 K steps: 3 splits of 19, 19, 18
+    assert dec(0, 64, 2000, 7168) == (4, 16, 3, 128 * 3)   # 125 blocks, 56 K steps: 3 splits of 19, 19, 18
     assert dec(0, 64, 1024, 512) == (4, 16, 1, 64)      # 4 K steps: no split
     assert dec(0, 64, 1024, 1024) == (4, 16, 2, 128)    # 8 K steps: 2 splits of 4
-    assert dec(3, 33, 1000, 1152) == (4, 16, 2, 126)    # block-scaled decode likewise (9 steps: 5 + 4)
+    assert dec(3, 33, 1000, 1152) == (4, 16, 2, 64 * 2)    # block-scaled decode likewise (63 blocks, 9 steps: 5 + 4)
     # small problems (M <= 256, at most 2 tiled workgroups): the decode kernel
     # over 64-token tiles, one workgroup per 16 weight rows and token tile
     assert dec(0, 256, 256, 256) == (4, 16, 1, 16 * 4)

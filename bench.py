@@ -970,11 +970,11 @@ def main():
         del wb
     if "decode" in want:
         out = []
-        for (N, K) in ((4096, 7168), (14336, 4096)):
-            for M in (1, 16, 32, 64):
+        for (N, K, Ms) in ((4096, 7168, (1, 16, 32, 64)), (14336, 4096, (1, 16, 32, 64)), (2048, 7168, (1, 64))):
+            for M in Ms:
                 r = bench_decode(torch, f, M, N, K, steps, warmup, timer)
                 out.append({"M": M, "N": N, "K": K, "kernel_us_mean": r["kernel_ms_mean"] * 1e3, **timing_fields(r),
-                            "variant": f.plan(0, M, N, K).variant,
+                            "variant": f.plan(0, M, N, K).variant, "k_splits": f.plan(0, M, N, K).k_splits,
                             "roofline": {"bound": "hbm", "achieved": r["gbs_kernel"], "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": r["gbs_kernel"] / PEAK_HBM_GBS,
                                          "algorithmic_bytes": r["bytes"]}})

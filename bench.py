@@ -707,6 +707,50 @@ def _trace_durations(directory, pattern):
     return durs
 
 
+def pmc_table(dirs, command, out_name):
+    """Writes profiles/<out_name>: for each counter target's kernel, the mean
+    per dispatch of every counter collected in the given --pmc passes over
+    `--profile-run` (one pass per directory), with the derived memory-path
+    figures (average L2 read latency seen from the L1, TA cycles per buffer
+    instruction)."""
+    import csv
+    import glob
+
+    vals = {}
+    for d in dirs:
+        for fpath in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(fpath, newline="") as fh:
+                for row in csv.DictReader(fh):
+                    for name, (stem, pattern, what) in COUNTER_TARGETS.items():
+                        if pattern in row["Kernel_Name"]:
+                            key = (name, row["Counter_Name"])
+                            disp = (d, row["Dispatch_Id"])     # dispatch ids restart in every pass
+                            vals.setdefault(key, {}).setdefault(disp, 0.0)
+                            vals[key][disp] += float(row["Counter_Value"])
+    lines = ["rocprofv3 --pmc counters per dispatch (mean over dispatches) of the profiled kernels", "",
+             "commands (from the repository root R; each pass its own rocprofv3 run over the same program):",
+             command, "", f"kernel_source_hash: {kernel_source_hash()}", ""]
+    for name, (stem, pattern, what) in COUNTER_TARGETS.items():
+        cs = sorted(c for (n, c) in vals if n == name)
+        if not cs:
+            continue
+        lines.append(f"{what} ({pattern}):")
+        mean = {c: sum(vals[(name, c)].values()) / len(vals[(name, c)]) for c in cs}
+        for c in cs:
+            lines.append(f"  {c}: {mean[c]:.0f}")
+        if mean.get("TCP_TCC_READ_REQ_sum"):
+            lines.append(f"  derived: L2 read latency seen from the L1, mean {mean.get('TCP_TCC_READ_REQ_LATENCY_sum', 0) / mean['TCP_TCC_READ_REQ_sum']:.0f} cycles; "
+                         f"{mean['TCP_TCC_READ_REQ_sum'] / 256:.0f} L2 read requests per CU")
+        if mean.get("TA_BUFFER_WAVEFRONTS_sum"):
+            lines.append(f"  derived: {mean.get('TA_BUFFER_TOTAL_CYCLES_sum', 0) / mean['TA_BUFFER_WAVEFRONTS_sum']:.1f} TA cycles per buffer "
+                         f"instruction; {mean.get('TA_BUFFER_TOTAL_CYCLES_sum', 0) / 256:.0f} per CU")
+        lines.append("")
+    path = os.path.join(PROFILE_DIR, out_name)
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines))
+    log(f"wrote {path}")
+
+
 def trace_summary(trace_dir, bench_json, command):
     """Writes profiles/bench_kernel_trace.txt from a `rocprofv3 --kernel-trace
     --stats` run of the default bench: rocprofv3's per-kernel statistics, then
@@ -881,6 +925,8 @@ def main():
     ap.add_argument("--counters-command", default="",
                     help="the commands that produced the counter directories (recorded in the summaries)")
     ap.add_argument("--counters-work", default="", help="the JSON line --profile-run printed")
+    ap.add_argument("--pmc-table", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/memory_path_counters.txt from --pmc passes over --profile-run")
     ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
                     help="write profiles/bench_kernel_trace.txt from a --kernel-trace --stats run of the bench")
     args = ap.parse_args()
@@ -890,6 +936,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(*args.trace_summary, args.counters_command)
+        return
+    if args.pmc_table:
+        pmc_table(args.pmc_table, args.counters_command, "memory_path_counters.txt")
         return
 
     if args.gpus != 1:

@@ -134,6 +134,38 @@ def test_decode_split_k_graph_replays():
     check(eager, r, s, 1.0, ref_bits=ref, what="split-K 64x1024x7168", **random_allowance(w.A, w.B, E4M3, E4M3, 1.0, s))
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 1024, 7168), (17, 1000, 2048), (40, 2056, 7168)])
+def test_decode_split_k_repeats(M, N, K):
+    """50 launches in a row of one split shape, alternating two output
+    buffers: every result equals the first bit for bit, and the first is
+    within the bound of the oracle.  All splits of a block meet in one XCD's
+    L2 (workgroups (x, y) with x a multiple of 8 apart go to the same XCD);
+    were a split's partial sums not yet visible to the last one, some launch
+    would differ.  (1000 rows: 63 blocks, a padding column of workgroups;
+    2056 rows: 129 blocks, a grid above 256 workgroups, two per CU.)"""
+    f = _f()
+    plan = f.plan(0, M, N, K)
+    assert plan.k_splits > 1 and plan.workgroups % 8 == 0
+    print(f"[split repeats] M={M} N={N} K={K} k_splits={plan.k_splits} workgroups={plan.workgroups}", flush=True)
+    w = workloads.dense_random(M, N, K, seed=M + N + K)
+    a, b = _dev(w.A), _dev(w.B)
+    one = torch.ones(1, device="cuda")
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    first = None
+    for i in range(50):
+        o = outs[i % 2]
+        o.fill_(7.0)
+        f.gemm_nt(a, b, one, one, out=o, a_dtype=E4M3, b_dtype=E4M3)
+        torch.cuda.synchronize()
+        d = gpu_bits(o)
+        if first is None:
+            first = d
+        else:
+            assert np.array_equal(d, first), f"launch {i} differs in {int((d != first).sum())} elements"
+    ref, r, s, _ = oracle.gemm_nt(w.A, w.B)
+    check(first, r, s, 1.0, ref_bits=ref, what=f"split-K {M}x{N}x{K}", **random_allowance(w.A, w.B, E4M3, E4M3, 1.0, s))
+
+
 @pytest.mark.parametrize("M,N,K,fa,fb", [
     (65, 64, 128, E4M3, E4M3),        # two token tiles, the second of 1 row
     (200, 100, 1040, E5M2, E4M3),     # 4 token tiles (the last 8 rows), N tail, K tail

@@ -1191,21 +1191,32 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
     constexpr int ROWB = 128;                      // K bytes per pipeline stage
     constexpr int TR = CB <= 2 ? 32 : 16 * CB;     // token rows staged per stage (>= 32: one DMA per wave)
     constexpr int TDMA = TR / 32;                  // token DMA instructions per wave per stage (8 rows each)
-    constexpr int TS = DEPTH + 1;                  // token ring slots
+    // 12 token blocks (up to 192 tokens): each step's 48 MFMAs per wave take
+    // about as long as a weight copy from HBM, so the weights get two steps in
+    // flight (DW = 3 slots per wave) and the tokens, L2 hits, one: both copies
+    // of a step are issued after its barrier, tokens first, which lets 2 token
+    // slots do (no wave still reads the slot being refilled) and lets the wait
+    // before a step leave the newest weight copies in flight.  Measured with
+    // 16 groups of 160 tokens: 121.5 -> 115.3 us at 4096 x 7168, 71.7 -> 65.4
+    // us at 7168 x 2048; with 8 blocks (96 tokens) -1% and +2%, so those keep
+    // the 2-step ring.
+    constexpr bool DEEPW = CB >= 12;
+    constexpr int DW = DEEPW ? 3 : DEPTH;          // weight ring slots per wave
+    constexpr int TS = DEEPW ? 2 : DEPTH + 1;      // token ring slots
     constexpr int TSLOT = TR * ROWB;
     constexpr int WLOADS = RB * 2 + (BLK ? 1 : 0); // weight loads (and the block scale) per wave per stage
     constexpr int SDMA = BLK ? 1 : 0;              // token-scale DMA of wave 0 per stage
     constexpr int SCS = BLK ? 256 : 0;             // token-scale bytes per ring slot
     constexpr int WSLOT = WR * ROWB;               // one stage of one wave's weight rows
-    constexpr int WRING = 4 * DEPTH * WSLOT;       // the four waves' weight rings
+    constexpr int WRING = 4 * DW * WSLOT;          // the four waves' weight rings
     constexpr int WSC = BLK ? 256 : 0;             // one stage of one wave's weight-scale copy
     constexpr int WSC_OFF = WRING + TS * TSLOT + TS * SCS;
     static_assert(RB >= 1 && CB >= 1 && DEPTH >= 2, "shape");
-    static_assert((DEPTH - 1) * (WLOADS + TDMA + SDMA) < 64, "loads in flight");
-    static_assert(WSC_OFF + 4 * DEPTH * WSC <= 160 * 1024, "LDS");
+    static_assert((DEPTH - 1) * (WLOADS + TDMA + SDMA) < 64 && 2 * WLOADS + TDMA + SDMA < 64, "loads in flight");
+    static_assert(WSC_OFF + 4 * DW * WSC <= 160 * 1024, "LDS");
 
     // [weight rings of the 4 waves | token ring | token-scale ring | weight-scale slots]
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[WSC_OFF + 4 * DEPTH * WSC];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[WSC_OFF + 4 * DW * WSC];
     uint8_t *const tsm = smem + WRING;
 
     const int lane = threadIdx.x & 63;
@@ -1237,7 +1248,7 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
     const uint32_t sb_row = BLK ? (uint32_t)(min(nw, p.N) / 128) * (uint32_t)p.lds_sb : 0u;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)tsm;
     const uint32_t wlds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem +
-                          (uint32_t)wave * (DEPTH * WSLOT);
+                          (uint32_t)wave * (DW * WSLOT);
 
     // Operand layout used for both operands of v_mfma 16x16x128: lane l
     // carries row (l & 15) and, of each 128-byte K block, the bytes
@@ -1307,7 +1318,7 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
         // One stage: this wave's weight copies (into its own slot), then its
         // token DMA.  Past the last K block every offset is out of range: no
         // memory traffic, zeros, and the stage is never consumed.
-        auto load = [&](int slot, int kt) {
+        auto load_w = [&](int slot, int kt) {
             const uint32_t k0 = (uint32_t)kt * ROWB;
             const bool in0 = (kt < nk) && (int)(k0 + wch0) < p.K;
             const bool in1 = (kt < nk) && (int)(k0 + wch1) < p.K;
@@ -1323,7 +1334,10 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
             // load of the stage is counted by the waits below)
             if (BLK)
                 dma4(srdSB, kt < nk && lane == 0 ? sb_row + ((uint32_t)kt & ~3u) : kOobOffset,
-                     lds0 - (uint32_t)WRING + (uint32_t)(WSC_OFF + (wave * DEPTH + slot) * WSC));
+                     lds0 - (uint32_t)WRING + (uint32_t)(WSC_OFF + (wave * DW + slot) * WSC));
+        };
+        auto load_t = [&](int kt) {
+            const uint32_t k0 = (uint32_t)kt * ROWB;
 #pragma unroll
             for (int i = 0; i < TDMA; ++i) {
                 const bool in = (kt < nk) && (int)(k0 + t_dma_kc[i]) < p.K;
@@ -1336,46 +1350,77 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
                      lds0 + (uint32_t)(TS * TSLOT) + (uint32_t)((kt % TS) * SCS));
             }
         };
-
-        // Software pipeline over K blocks, branch-free: the scheduling
-        // barriers keep the load groups in slot order, so every wait is exact.
+        auto load = [&](int slot, int kt) {
+            load_w(slot, kt);
+            load_t(kt);
+        };
+        // Step kt's MFMAs: token fragments of token slot kt % TS, weight
+        // fragments of this wave's weight slot `wslot`.
+        auto compute = [&](int kt, int wslot) {
+            const uint8_t *ts = tsm + (kt % TS) * TSLOT;
+            v8i tf[CB];
+            int tsc[CB];
 #pragma unroll
-        for (int s = 0; s < DEPTH - 1; ++s) {
-            load(s, s);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        for (int kb = 0; kb < nk; kb += DEPTH) {
+            for (int c = 0; c < CB; ++c) {
+                tf[c] = pack8(*reinterpret_cast<const v4u *>(ts + t_frag[c][0]),
+                              *reinterpret_cast<const v4u *>(ts + t_frag[c][1]));
+                tsc[c] = BLK ? (int)tsm[TS * TSLOT + (kt % TS) * SCS + c * 16 + r16] : 127;
+            }
+            const uint8_t *ws = smem + wave * (DW * WSLOT) + wslot * WSLOT;
+            const int wsc = BLK ? (int)smem[WSC_OFF + (wave * DW + wslot) * WSC + (kt & 3)] : 127;
 #pragma unroll
-            for (int s = 0; s < DEPTH; ++s) {
-                const int kt = kb + s;
-                load((s + DEPTH - 1) % DEPTH, kt + DEPTH - 1);
-                __builtin_amdgcn_sched_barrier(0);
-                // every load of step kt (older than the DEPTH - 1 newer stages) has landed
-                if (BLK && wave == 0) vmcnt_wait<(DEPTH - 1) * (WLOADS + TDMA + SDMA)>();
-                else vmcnt_wait<(DEPTH - 1) * (WLOADS + TDMA)>();
-                __syncthreads();                   // every wave's token DMA of step kt has landed
-                const uint8_t *ts = tsm + (kt % TS) * TSLOT;
-                v8i tf[CB];
-                int tsc[CB];
+            for (int r = 0; r < RB; ++r) {
+                const v8i wf = pack8(*reinterpret_cast<const v4u *>(ws + r * 2048 + wf0),
+                                     *reinterpret_cast<const v4u *>(ws + r * 2048 + wf1));
 #pragma unroll
                 for (int c = 0; c < CB; ++c) {
-                    tf[c] = pack8(*reinterpret_cast<const v4u *>(ts + t_frag[c][0]),
-                                  *reinterpret_cast<const v4u *>(ts + t_frag[c][1]));
-                    tsc[c] = BLK ? (int)tsm[TS * TSLOT + (kt % TS) * SCS + c * 16 + r16] : 127;
+                    if (BLK) acc[r][c] = mfma16x16x128_s<FB, FA>(wf, tf[c], acc[r][c], wsc, tsc[c]);
+                    else acc[r][c] = mfma16x16x128<FB, FA>(wf, tf[c], acc[r][c]);
                 }
-                const uint8_t *ws = smem + wave * (DEPTH * WSLOT) + s * WSLOT;
-                const int wsc = BLK ? (int)smem[WSC_OFF + (wave * DEPTH + s) * WSC + (kt & 3)] : 127;
-#pragma unroll
-                for (int r = 0; r < RB; ++r) {
-                    const v8i wf = pack8(*reinterpret_cast<const v4u *>(ws + r * 2048 + wf0),
-                                         *reinterpret_cast<const v4u *>(ws + r * 2048 + wf1));
-#pragma unroll
-                    for (int c = 0; c < CB; ++c) {
-                        if (BLK) acc[r][c] = mfma16x16x128_s<FB, FA>(wf, tf[c], acc[r][c], wsc, tsc[c]);
-                        else acc[r][c] = mfma16x16x128<FB, FA>(wf, tf[c], acc[r][c]);
-                    }
-                }
+            }
+        };
+
+        if constexpr (DEEPW) {
+            // Copies in issue order: T0 W0 W1 | T1 W2 | T2 W3 | ... (Tk: step
+            // k's tokens, Wk: this wave's weights of step k, the group after
+            // "|" issued in step k - 1 after its barrier).  Before step kt only
+            // W(kt + 1) may still be in flight; T(kt + 1) refills the token slot
+            // of step kt - 1, which every wave has read before the barrier, and
+            // W(kt + 2) this wave's weight slot of step kt - 1.
+            load_t(0);
+            load_w(0, 0);
+            load_w(1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            for (int kt = 0; kt < nk; ++kt) {
+                vmcnt_wait<WLOADS>();              // every copy of step kt has landed
+                __syncthreads();                   // every wave's, and step kt - 1 is read
+                load_t(kt + 1);
+                load_w((kt + 2) % DW, kt + 2);
                 __builtin_amdgcn_sched_barrier(0);
+                compute(kt, kt % DW);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            // Software pipeline over K blocks, branch-free: the scheduling
+            // barriers keep the load groups in slot order, so every wait is exact.
+#pragma unroll
+            for (int s = 0; s < DEPTH - 1; ++s) {
+                load(s, s);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            for (int kb = 0; kb < nk; kb += DEPTH) {
+#pragma unroll
+                for (int s = 0; s < DEPTH; ++s) {
+                    const int kt = kb + s;
+                    load((s + DEPTH - 1) % DEPTH, kt + DEPTH - 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    // every load of step kt (older than the DEPTH - 1 newer stages) has landed
+                    if (BLK && wave == 0) vmcnt_wait<(DEPTH - 1) * (WLOADS + TDMA + SDMA)>();
+                    else vmcnt_wait<(DEPTH - 1) * (WLOADS + TDMA)>();
+                    __syncthreads();               // every wave's token DMA of step kt has landed
+                    compute(kt, s);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
         vmcnt_wait<0>();                           // drain the out-of-range prefetches

@@ -96,10 +96,22 @@ int token_blocks_for(int m) {
 // are fewer than 256 (N < 4096), K is split over up to ceil(256 / blocks)
 // workgroups per block (at least 4 K steps each, one per wave) so the chip
 // stays full; their FP32 partial sums meet in a workspace (kSplitWs below).
-// With 256 blocks or more K is not split: measured at M = 64 and N = 4096, a
-// split over 4 workgroups of 64 rows (a quarter of the token traffic) took
-// 15.1 us against 12.1 unsplit, since each split's 14 K steps leave its load
-// latency, the partial-sum exchange and the last split's reads exposed.
+//
+// The waves-on-rows kernel (RB = 4: 64 weight rows per workgroup, the 4
+// waves on 16 rows each, sharing one copy of the tokens per K step) is taken
+// instead where it measured faster, graph-timed on one box:
+//  - where the blocks above leave the CUs unevenly loaded (more than 256, not
+//    a multiple of 256), at every M: N = 5120 .. 14336 (64 x 14336 x 4096:
+//    19.9 -> 15.7 us, 64 x 7168 x 4096: 13.9 -> 11.3, 1 x 7168 x 4096: 8.9 ->
+//    8.3, 64 x 5120 x 7168: 21.1 -> 13.9);
+//  - with more than 32 tokens and at least 28 K steps per split, where the
+//    token copies dominate (64 x 4096 x 14336: 21.9 -> 18.6 us, 64 x 16384 x
+//    4096: 21.3 -> 17.2, 64 x 8192 x 7168: 16.8 -> 16.3).
+// Its splits: as many as keep at least 16 K steps each and at most 256
+// workgroups (512 with one token block); not taken below 160 workgroups or
+// 16 K steps.
+// At 64 x 4096 x 7168 (4 splits of 14 steps) it measured 13.2 against 12.4
+// us, and with 32 or fewer tokens on balanced grids it was 1-7% slower.
 struct DecodeShape {
     int rb, cb, blocks, splits, ksteps;
 };
@@ -119,6 +131,21 @@ DecodeShape decode_shape(int64_t m, int64_t n, int64_t k) {
             d.ksteps = (int)cdiv(nk, want);
             d.splits = (int)cdiv(nk, d.ksteps);   // no empty split
         }
+        return d;
+    }
+    // waves on rows
+    const int64_t rblocks = cdiv(n, 64);
+    const bool uneven = d.blocks % 256 != 0;
+    int64_t want = (d.cb == 1 ? 512 : 256) / rblocks;
+    if (want > nk / 16) want = nk / 16;
+    if (want < 1) want = 1;
+    const int64_t ksteps = cdiv(nk, want);
+    const int64_t splits = cdiv(nk, ksteps);
+    if (nk >= 16 && rblocks * splits >= 160 && (uneven || (d.cb == 4 && ksteps >= 28))) {
+        d.rb = 4;
+        d.blocks = (int)rblocks;
+        d.splits = (int)splits;
+        d.ksteps = (int)ksteps;
     }
     return d;
 }
@@ -126,9 +153,11 @@ DecodeShape decode_shape(int64_t m, int64_t n, int64_t k) {
 // Workspace of the split-K few-token path, per device: the FP32 partial sums
 // of the splits (16 RB x 16 CB outputs, at most 64 x 64, per workgroup) and
 // one arrival count per block of weight rows, each in its own 128-byte line.
-// Splits happen only with fewer than 256 blocks, so blocks x splits < 256 +
-// blocks < 512 workgroups: at most 512 x 16 KiB of partial sums and 256
-// counts (32 KiB), whatever the shape.
+// The waves-on-K kernel splits only with fewer than 256 blocks, so blocks x
+// splits < 256 + blocks < 512 workgroups; the waves-on-rows kernel at most
+// 256 blocks over 256 workgroups (512 with one token block, 4 KiB of sums
+// each).  So at most 512 x 16 KiB of partial sums and 256 counts (32 KiB),
+// whatever the shape.
 constexpr int kSplitMaxWgs = 512;
 constexpr int kSplitMaxBlocks = 256;
 constexpr size_t kSplitPartialBytes = (size_t)kSplitMaxWgs * 64 * 64 * sizeof(float);
@@ -471,6 +500,10 @@ int split_workspace(hipStream_t stream, SplitWs &ws) {
 // (N = 7168, 448 workgroups: 10.07 -> 9.38 us at M = 1, K = 4096).
 constexpr unsigned kDecodeSpreadPad = 16 * 1024;
 
+// Steps of token copies in flight in the waves-on-rows decode kernel (the
+// weights run one step further ahead).
+constexpr int kDecodeRowsLead = 1;
+
 template <int RB, int CB, int SCL>
 int launch_decode_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
     constexpr int D = RB == 1 ? (CB == 1 ? 5 : (CB == 2 ? 3 : 2)) : (CB == 1 ? 3 : 2);
@@ -499,8 +532,32 @@ int launch_decode_rb(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hip
     return launch_decode_cb<RB, 4, SCL>(fa, fb, p, grid, s);
 }
 
+// The waves-on-rows decode kernel (64 weight rows per workgroup).  Grids of
+// at most 256 workgroups are spread one per CU, as above: dynamic LDS takes
+// every instance past half of the CU's 160 KB.
+template <int CB, int SCL, int LT>
+int launch_decode_rows_lt(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    constexpr int smem = fp8g::RowsDecodeLayout<CB, SCL, LT>::SMEM;
+    const unsigned pad = (int64_t)grid.x * grid.y <= 256 && smem <= 80 * 1024 ? (unsigned)(80 * 1024 + 1024 - smem) : 0u;
+    const dim3 block(256);
+#define FP8G_DROWS(FA, FB) hipLaunchKernelGGL((fp8g::decode_rows_kernel<CB, FA, FB, SCL, LT, 1>), grid, block, pad, s, p)
+    if (fa == 0 && fb == 0) FP8G_DROWS(0, 0);
+    else if (fa == 0 && fb == 1) FP8G_DROWS(0, 1);
+    else if (fa == 1 && fb == 0) FP8G_DROWS(1, 0);
+    else FP8G_DROWS(1, 1);
+#undef FP8G_DROWS
+    return launch_status("decode kernel (waves on rows)");
+}
+
+template <int SCL>
+int launch_decode_rows(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    if (cb == 1) return launch_decode_rows_lt<1, SCL, kDecodeRowsLead>(fa, fb, p, grid, s);
+    if (cb == 2) return launch_decode_rows_lt<2, SCL, kDecodeRowsLead>(fa, fb, p, grid, s);
+    return launch_decode_rows_lt<4, SCL, kDecodeRowsLead>(fa, fb, p, grid, s);
+}
+
 // K split as the plan says when `ws` holds a workspace, else over the 4 waves
-// only.
+// only (waves on K), or not at all (waves on rows).
 template <int SCL>
 int launch_decode(const fp8g_plan &plan, int fa, int fb, GemmParams p, const SplitWs &ws, hipStream_t s) {
     const int rb = plan.tile_n / 16, cb = plan.token_blocks;
@@ -517,6 +574,7 @@ int launch_decode(const fp8g_plan &plan, int fa, int fb, GemmParams p, const Spl
         p.cnt = ws.count;
         grid = dim3((unsigned)(8 * cdiv(grid.x, 8)), (unsigned)plan.k_splits);
     }
+    if (rb == 4) return launch_decode_rows<SCL>(cb, fa, fb, p, grid, s);
     if (rb == 2) return launch_decode_rb<2, SCL>(cb, fa, fb, p, grid, s);
     return launch_decode_rb<1, SCL>(cb, fa, fb, p, grid, s);
 }

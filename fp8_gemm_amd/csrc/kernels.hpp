@@ -1712,4 +1712,244 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void decode_kernel(GemmParams p) {
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Few-token kernel with the waves on weight rows: the dense form with M <= 64
+// where the weight rows are few enough that K is split over workgroups
+// anyway.  Wave w owns weight rows 64 b + 16 w .. +16 of the workgroup's
+// block b, and the 4 waves share one LDS ring of token rows: each K step's
+// tokens are copied once for 64 weight rows, where the waves-on-K kernel
+// above copies them once for 16.  Every 1 KB direct-to-LDS copy costs the
+// texture addresser 16 cycles, so at M = 64 (4 token blocks) the token
+// copies are four fifths of that kernel's copy instructions; with the token
+// and weight copies aimed out of range (no memory traffic) it still took
+// 6.45 us at M = 64, N = 4096, K = 7168 against 4.0 at M = 1.
+//   K: grid y splits the K steps (`ksteps` each) as in the kernel above, the
+//   grid x padded to a multiple of 8 so that all splits of a block run on
+//   one XCD and meet in its L2; every wave runs all of its split's steps.
+//   Ring: TS = LT + 1 token slots shared by the waves and LT + 2 weight
+//   slots per wave.  The copies of step s + LT (tokens, L2 hits) and of step
+//   s + LT + 1 (this wave's weights, from HBM) are issued after step s's
+//   barrier, tokens first, so the weights run one step further ahead and the
+//   wait before a step leaves the newest weight copies in flight (copies
+//   complete in issue order).
+// ---------------------------------------------------------------------------
+template <int CB, int SCL, int LT>
+struct RowsDecodeLayout {
+    static constexpr bool BLK = SCL == SCALE_BLOCK;
+    static constexpr int TR = CB <= 2 ? 32 : 16 * CB;   // token rows per step (>= 32: one copy per wave)
+    static constexpr int TDMA = TR / 32;                // token copies per wave per step (8 rows each)
+    static constexpr int TS = LT + 1;                   // token slots
+    static constexpr int DW = LT + 2;                   // weight slots per wave
+    static constexpr int TSLOT = TR * 128;
+    static constexpr int WSLOT = 16 * 128;
+    static constexpr int SCS = BLK ? 256 : 0;           // token-scale bytes per token slot
+    static constexpr int WSC = BLK ? 256 : 0;           // weight-scale bytes per weight slot
+    static constexpr int T_OFF = 4 * DW * WSLOT;        // [weight rings | token ring | token scales |
+    static constexpr int TSC_OFF = T_OFF + TS * TSLOT;  //  weight scales | arrival flag]
+    static constexpr int WSC_OFF = TSC_OFF + TS * SCS;
+    static constexpr int FLAG_OFF = WSC_OFF + 4 * DW * WSC;
+    static constexpr int SMEM = FLAG_OFF + 16;
+};
+
+template <int CB, int FA, int FB, int SCL, int LT, int OCC>
+__global__ __launch_bounds__(256, OCC) void decode_rows_kernel(GemmParams p) {
+    using L = RowsDecodeLayout<CB, SCL, LT>;
+    constexpr bool BLK = L::BLK, CHN = SCL == SCALE_CHANNEL;
+    constexpr int TDMA = L::TDMA, TS = L::TS, DW = L::DW;
+    constexpr int WLOADS = 2 + (BLK ? 1 : 0);      // this wave's weight copies (and block scale) per step
+    constexpr int SDMA = BLK ? 1 : 0;              // wave 0: the token rows' scales per step
+    constexpr int WAIT = WLOADS + (LT - 1) * (TDMA + WLOADS);
+    constexpr int WAIT0 = WLOADS + (LT - 1) * (TDMA + SDMA + WLOADS);
+    static_assert(LT >= 1 && WAIT0 < 64, "copies in flight");
+    static_assert(L::SMEM <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::SMEM];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // workgroup (x, y) = (block of 64 weight rows, split of the K steps);
+    // blocks past the last (padding of the grid x) read nothing and leave
+    // before the exchange
+    const int splits = max(p.splits, 1);
+    const int nb = blockIdx.x;
+    const int sp = splits > 1 ? (int)blockIdx.y : 0;
+    const bool live = nb < (p.N + 63) / 64;
+    const int nw = nb * 64 + wave * 16;            // this wave's first weight row
+    const int rows_w = live ? max(0, min(p.N - nw, 16)) : 0;
+    const int rows_t = live ? p.M : 0;
+    // Rows past N (weights) or past M (tokens) lie outside the descriptors and
+    // read zeros without touching memory.
+    const v4i srdW = make_srd(p.B + (int64_t)min(nw, p.N) * p.ldb, rows_bytes(rows_w, p.ldb));
+    const v4i srdT = make_srd(p.A, rows_bytes(rows_t, p.lda));
+    const int nk = (p.K + 127) / 128;
+    const int kt0 = splits > 1 ? sp * p.ksteps : 0;
+    const int nks = splits > 1 ? max(0, min(nk, kt0 + p.ksteps) - kt0) : nk;
+    // Block scales: the token rows' scales of K block kt at sfa[kt lds_sa ..],
+    // and the dword of scale_b holding K block kt of the 128-row scale block
+    // that this workgroup's 64 rows lie in.
+    const v4i srdSA = BLK ? make_srd(p.sfa, (uint32_t)((int64_t)nk * p.lds_sa)) : v4i{0, 0, 0, 0};
+    const v4i srdSB = BLK ? make_srd(p.sfb, (uint32_t)((int64_t)((p.N + 127) / 128) * p.lds_sb)) : v4i{0, 0, 0, 0};
+    const uint32_t sb_row = BLK ? (uint32_t)(min(nb * 64, p.N) / 128) * (uint32_t)p.lds_sb : 0u;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
+    const uint32_t wring = lds0 + (uint32_t)(wave * DW * L::WSLOT);
+
+    // Weight copies: instruction h fills rows 8 h .. 8 h + 7 of the wave's
+    // slot; lane l takes row 8 h + l / 8 and deposits 16 bytes at position
+    // l % 8 of it, holding logical chunk (l % 8) ^ ((row >> 1) & 7), which puts
+    // the 16 rows of one logical chunk on 16 different bank groups for the
+    // fragment reads.
+    const uint32_t wrow = (uint32_t)lane >> 3;
+    const uint32_t wch0 = (((uint32_t)lane & 7u) ^ ((wrow >> 1) & 7u)) * 16u;
+    const uint32_t wch1 = (((uint32_t)lane & 7u) ^ (((wrow + 8u) >> 1) & 7u)) * 16u;
+    const uint32_t wo0 = wrow * (uint32_t)p.ldb + wch0, wo1 = (wrow + 8u) * (uint32_t)p.ldb + wch1;
+    const int r16 = lane & 15;
+    const int kg = lane >> 4;
+    const uint32_t wkey = ((uint32_t)r16 >> 1) & 7u;
+    const uint32_t wf0 = (uint32_t)r16 * 128u + (((uint32_t)kg ^ wkey) * 16u);
+    const uint32_t wf1 = (uint32_t)r16 * 128u + (((uint32_t)(4 + kg) ^ wkey) * 16u);
+    // Token copies: instruction i of wave w fills token rows (w TDMA + i) 8 ..
+    // +8 of the slot, lane l row l / 8, position l % 8 holding logical chunk
+    // (l % 8) ^ f(row), f(r) = (r & 7) ^ ((r >> 3) & 1) (the swizzle of swz()).
+    uint32_t t_off[TDMA], t_kc[TDMA];
+#pragma unroll
+    for (int i = 0; i < TDMA; ++i) {
+        const uint32_t row = (uint32_t)((wave * TDMA + i) * 8 + (lane >> 3));
+        const uint32_t c = ((uint32_t)(lane & 7) ^ (row & 7u) ^ ((row >> 3) & 1u)) & 7u;
+        t_kc[i] = c * 16u;
+        t_off[i] = row * (uint32_t)p.lda + c * 16u;
+    }
+    uint32_t t_frag[CB][2];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+        const uint32_t row = (uint32_t)(c * 16 + r16);
+        const uint32_t key = (row & 7u) ^ ((row >> 3) & 1u);
+        t_frag[c][0] = row * 128u + ((((uint32_t)kg) ^ key) & 7u) * 16u;
+        t_frag[c][1] = row * 128u + ((((uint32_t)kg + 4u) ^ key) & 7u) * 16u;
+    }
+
+    // The copies of local step s (K block kt0 + s); past the split's last step
+    // every offset is out of range: zeros, no traffic, never consumed.
+    auto load_w = [&](int s) {
+        const int kt = kt0 + s;
+        const uint32_t k0 = (uint32_t)kt * 128u;
+        const bool ok = s < nks;
+        const bool in0 = ok && (int)(k0 + wch0) < p.K, in1 = ok && (int)(k0 + wch1) < p.K;
+        const uint32_t dst = wring + (uint32_t)((s % DW) * L::WSLOT);
+        dma16(srdW, in0 ? wo0 + k0 : kOobOffset, dst);
+        dma16(srdW, in1 ? wo1 + k0 : kOobOffset, dst + 1024u);
+        if (BLK)
+            dma4(srdSB, ok && lane == 0 ? sb_row + ((uint32_t)kt & ~3u) : kOobOffset,
+                 lds0 + (uint32_t)(L::WSC_OFF + (wave * DW + s % DW) * L::WSC));
+    };
+    auto load_t = [&](int s) {
+        const int kt = kt0 + s;
+        const uint32_t k0 = (uint32_t)kt * 128u;
+        const bool ok = s < nks;
+        const uint32_t dst = lds0 + (uint32_t)(L::T_OFF + (s % TS) * L::TSLOT);
+#pragma unroll
+        for (int i = 0; i < TDMA; ++i) {
+            const bool in = ok && (int)(k0 + t_kc[i]) < p.K;
+            dma16(srdT, in ? t_off[i] + k0 : kOobOffset, dst + (uint32_t)(wave * TDMA + i) * 1024u);
+        }
+        if (BLK && wave == 0)
+            dma4(srdSA, ok && 4 * lane < 16 * CB ? (uint32_t)kt * (uint32_t)p.lds_sa + 4u * (uint32_t)lane : kOobOffset,
+                 lds0 + (uint32_t)(L::TSC_OFF + (s % TS) * L::SCS));
+    };
+
+    v4f acc[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) acc[c] = (v4f){0, 0, 0, 0};
+    // issue order: W0 | T0 W1 | ... | T(LT-1) W(LT), then per step s after its
+    // barrier T(s+LT) W(s+LT+1)
+    load_w(0);
+#pragma unroll
+    for (int j = 0; j < LT; ++j) {
+        load_t(j);
+        load_w(j + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < nks; ++s) {
+        // every copy of step s has landed (this wave's), then every wave's; the
+        // slots of step s - 1 are no longer read
+        if (BLK && wave == 0) vmcnt_wait<WAIT0>();
+        else vmcnt_wait<WAIT>();
+        __syncthreads();
+        load_t(s + LT);
+        load_w(s + LT + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t *ts = smem + L::T_OFF + (s % TS) * L::TSLOT;
+        const uint8_t *ws = smem + (wave * DW + s % DW) * L::WSLOT;
+        const v8i wf = pack8(*reinterpret_cast<const v4u *>(ws + wf0), *reinterpret_cast<const v4u *>(ws + wf1));
+        const int ssb = BLK ? (int)smem[L::WSC_OFF + (wave * DW + s % DW) * L::WSC + ((kt0 + s) & 3)] : 127;
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            const v8i tf = pack8(*reinterpret_cast<const v4u *>(ts + t_frag[c][0]),
+                                 *reinterpret_cast<const v4u *>(ts + t_frag[c][1]));
+            const int ssa = BLK ? (int)smem[L::TSC_OFF + (s % TS) * L::SCS + c * 16 + r16] : 127;
+            if (BLK) acc[c] = mfma16x16x128_s<FB, FA>(wf, tf, acc[c], ssb, ssa);
+            else acc[c] = mfma16x16x128<FB, FA>(wf, tf, acc[c]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    vmcnt_wait<0>();                               // drain the copies past the last step
+
+    if (splits > 1) {
+        if (!live) return;                         // (uniform: padding workgroup)
+        // Split K, as in the kernel above: this split's sums stored plainly
+        // (the vector L1 writes through to the XCD's L2), the arrival counted
+        // with an L2 atomic on the block's own 128-byte line, and the last
+        // split to arrive adds every split's sums, read with sc0 from the L2,
+        // in split order, then resets the count.
+        constexpr int kStore = 0, kLoad = 1;
+        constexpr int PART = 4 * CB * 1024;        // one split's sums: 4 waves x CB blocks x 64 lanes x 16 B
+        const __amdgpu_buffer_rsrc_t part =
+            make_rsrc(reinterpret_cast<const uint8_t *>(p.ws) + (int64_t)nb * splits * PART, (uint32_t)(splits * PART));
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc[c]), part,
+                                                   (uint32_t)(sp * PART + (wave * CB + c) * 1024 + lane * 16), 0, kStore);
+        int *const last_split = reinterpret_cast<int *>(smem + L::FLAG_OFF);
+        vmcnt_wait<0>();                           // this thread's sums are in the L2
+        __syncthreads();                           // and every thread's
+        if (threadIdx.x == 0)
+            *last_split = __hip_atomic_fetch_add(p.cnt + kCountStride * nb, 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
+        __syncthreads();
+        if (!*last_split) return;
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            const uint32_t off = (uint32_t)((wave * CB + c) * 1024 + lane * 16);
+            v4f sum = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(part, off, 0, kLoad));
+            for (int t = 1; t < splits; ++t)
+                sum += __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(part, (uint32_t)(t * PART) + off, 0, kLoad));
+            acc[c] = sum;
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_exchange(p.cnt + kCountStride * nb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // Scale, round, store: register q of block c holds weight row nw + 4 kg + q
+    // and token c 16 + r16, so a lane writes four consecutive outputs of one
+    // token row.
+    const float sc = SCL != SCALE_TENSOR ? 1.0f : p.scale_a[0] * p.scale_b[0];
+    const int n = nw + kg * 4;
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+        const int tok = c * 16 + r16;
+        if (tok < rows_t) {
+            const v4f sum = acc[c];
+            v2u v;
+            if (CHN) {
+                float s4[4], b4[4];
+                channel_terms(p, n, s4, b4);
+                const float sam = p.ch_sa ? p.ch_sa[tok] : 1.0f;
+                v = pack_bf16x4(sum[0] * sam * s4[0] + b4[0], sum[1] * sam * s4[1] + b4[1],
+                                sum[2] * sam * s4[2] + b4[2], sum[3] * sam * s4[3] + b4[3]);
+            } else {
+                v = pack_bf16x4(sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc);
+            }
+            store_bf16x4(p.D + (int64_t)tok * p.ldd, n, p.N - n, v);
+        }
+    }
+}
+
 }  // namespace fp8g

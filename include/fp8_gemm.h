@@ -25,8 +25,9 @@
  *     passes; the library keeps no pointer to them after returning and never
  *     synchronises the stream.
  *   - Workspace: the dense forms with M <= 64 split K over workgroups when
- *     the weight rows alone would leave the chip part-empty (fewer than 256
- *     blocks of 16-64 rows).  The splits' FP32 partial sums meet in a
+ *     the weight rows alone would leave the chip part-empty or unevenly
+ *     loaded (fewer than 256 blocks of 16 rows, or 64-row blocks; at most
+ *     256 blocks and 512 workgroups).  The splits' FP32 partial sums meet in a
  *     workspace of 8 MiB + 32 KiB per device, which the library allocates
  *     with hipMalloc on the first such call on that device (and keeps until
  *     the process ends); if that first call happens while `stream` is being
@@ -112,8 +113,9 @@ int fp8_gemm_nt(const void *A, int64_t lda, int a_dtype,
  * 8 MiB + 32 KiB, held from the
  * library's load until the process ends) instead of a workspace allocated on
  * first use.  It calls no allocation routine.  Every shape fits the array
- * (the split-K path splits only while fewer than 256 blocks of weight rows
- * exist); a larger need would be refused with FP8G_ERR_ARG.  All calls on a
+ * (the split-K path splits at most 256 blocks of weight rows over at most
+ * 512 workgroups of at most 16 KiB of sums); a larger need would be refused
+ * with FP8G_ERR_ARG.  All calls on a
  * device share its array, which keeps the last call's contents (the counts
  * return to zero after every call): calls that overlap on one device race.
  */
@@ -296,13 +298,15 @@ typedef struct {
                            BF16 forms on 8 waves and 32x32x64),
                            3 = swapped streaming (masked grouped forms,
                            16 * token_blocks tokens per pass),
-                           4 = swapped decode, K split over 4 waves and
-                           over k_splits workgroups (dense forms, m <= 64), 5 = tiled 256x192 and
+                           4 = swapped decode (dense forms, m <= 64): 16
+                           or 32 weight rows per workgroup with K split over
+                           its 4 waves, or 64 with each wave on 16 of them;
+                           K also split over k_splits workgroups, 5 = tiled 256x192 and
                            6 = tiled 256x224 (both FP8 dense, per-tensor or
                            per-channel scales), 0 = nothing to launch */
     int tile_m;         /* rows of D per workgroup tile (tokens) */
     int tile_n;         /* columns of D per workgroup tile (weight rows: 256
-                           or 512 for variant 3, 16 or 32 for variant 4) */
+                           or 512 for variant 3, 16, 32 or 64 for variant 4) */
     int token_blocks;   /* swapped kernels: 16-token column blocks per pass
                            (1, 2, 4; the masked form also 8 and 12) */
     int64_t workgroups; /* grid size */

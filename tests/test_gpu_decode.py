@@ -1,6 +1,6 @@
-"""GPU parity of the dense few-token (M <= 64) path, the swap-AB decode kernel
-with K split over 4 waves and per-wave LDS rings, against the CPU oracle,
-through the C ABI.
+"""GPU parity of the dense few-token (M <= 64) path, the swap-AB decode kernels
+(K split over 4 waves with per-wave LDS rings, or the 4 waves on 16 weight
+rows each sharing the token copies) against the CPU oracle, through the C ABI.
 
 Edges specific to it: fewer K blocks than waves (some waves have no work),
 a short last K block, N not a multiple of the 16 weight rows per workgroup,
@@ -88,6 +88,47 @@ def test_decode_blockscaled(M, N, K):
           allowance=hw_allowance_blockscaled(w.A, w.B, 0, 0, w.sa, w.sb, s), max_allowed=random_cap(d.size, K))
 
 
+@pytest.mark.parametrize("M,N,K,fa,fb", [
+    (1, 4104, 7168, E4M3, E4M3),      # 3 splits of 19/19/18 steps; last block 8 rows (3 waves without rows); padding column
+    (37, 7160, 4000, E5M2, E4M3),     # 2 splits, K tail of 32 bytes, last block 56 rows
+    (16, 10240, 2048, E4M3, E5M2),    # one token block, K not split (160 workgroups)
+    (32, 14336, 4096, E4M3, E4M3),    # two token blocks, K not split (224 workgroups)
+    (64, 5120, 7168, E5M2, E5M2),     # 3 splits of 19/19/18 steps, four token blocks
+    (20, 7168, 4096, E4M3, E4M3),     # 2 splits, two token blocks
+])
+def test_decode_rows_matches_oracle(M, N, K, fa, fb):
+    """The waves-on-rows few-token kernel (64 weight rows per workgroup, the 4
+    waves on 16 rows each, one shared copy of the tokens per K step): the
+    per-tensor, per-channel and block-scaled forms against the oracle, over
+    ragged M, N and K, split and unsplit."""
+    f = _f()
+    plan = f.plan(0, M, N, K)
+    assert plan.variant == 4 and plan.tile_n == 64 and f.plan(3, M, N, K).tile_n == 64
+    print(f"[decode rows] M={M} N={N} K={K} fmt=({fa},{fb}) k_splits={plan.k_splits} workgroups={plan.workgroups}",
+          flush=True)
+    w = workloads.dense_random(M, N, K, seed=M * 5 + N + K, a_fmt=fa, b_fmt=fb, scales=(0.75, 1.5))
+    d = gpu_bits(f.gemm_nt(_dev(w.A), _dev(w.B), torch.tensor([w.sa], device="cuda"), torch.tensor([w.sb], device="cuda"),
+                           a_dtype=fa, b_dtype=fb))
+    ref, r, s, _ = oracle.gemm_nt(w.A, w.B, fa, fb, w.sa, w.sb)
+    sc = abs(w.sa * w.sb)
+    check(d, r, s, sc, ref_bits=ref, what=f"decode rows {M}x{N}x{K}", **random_allowance(w.A, w.B, fa, fb, sc, s))
+    rng = np.random.default_rng(M + N)
+    csa = rng.uniform(0.5, 2, M).astype(np.float32)
+    csb = rng.uniform(0.5, 2, N).astype(np.float32)
+    bias = rng.normal(0, 4, N).astype(np.float32)
+    d = gpu_bits(f.gemm_nt_channelwise(_dev(w.A), _dev(w.B), _dev(csa), _dev(csb), _dev(bias), a_dtype=fa, b_dtype=fb))
+    ref, r, s = oracle.gemm_nt_channelwise(w.A, w.B, csa, csb, bias, fa, fb)
+    _, _, s1, _ = oracle.gemm_nt(w.A, w.B, fa, fb)
+    allow = hw_allowance(w.A, w.B, fa, fb, 1.0, s1) * np.outer(csa, csb)
+    check(d, r, s, 1.0, ref_bits=ref, what=f"decode rows channelwise {M}x{N}x{K}", allowance=allow,
+          max_allowed=random_cap(d.size, K))
+    wb = workloads.dense_blockscaled(M, N, K, seed=M + 2 * N + K, lds_pad=5, pad_code=255)
+    d = gpu_bits(f.gemm_nt_blockscaled(_dev(wb.A), _dev(wb.B), _dev(wb.sa), _dev(wb.sb), a_dtype=E4M3, b_dtype=E4M3))
+    ref, r, s = oracle.gemm_nt_blockscaled(wb.A, wb.B, wb.sa, wb.sb)
+    check(d, r, s, 1.0, ref_bits=ref, what=f"decode rows blockscaled {M}x{N}x{K}",
+          allowance=hw_allowance_blockscaled(wb.A, wb.B, 0, 0, wb.sa, wb.sb, s), max_allowed=random_cap(d.size, K))
+
+
 def test_decode_deterministic():
     w = workloads.dense_random(32, 4096, 7168, seed=77)
     a, b = _dev(w.A), _dev(w.B)
@@ -96,22 +137,25 @@ def test_decode_deterministic():
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
-def test_decode_split_k_graph_replays():
-    """The split-K few-token path captured in a graph and replayed four times,
-    with eager launches (another split shape, a fill) between the replays:
-    every replay equals the eager result bit for bit, so the arrival counts
-    are back at zero after each launch and the partial sums are added in the
-    same order whichever split finishes last."""
+@pytest.mark.parametrize("M,N,K,rows", [(64, 1024, 7168, 16), (64, 7168, 4096, 64)])
+def test_decode_split_k_graph_replays(M, N, K, rows):
+    """The split-K few-token path (both kernels: waves on K, 16 rows per
+    workgroup, and waves on rows, 64) captured in a graph and replayed four
+    times, with eager launches (another split shape, a fill) between the
+    replays: every replay equals the eager result bit for bit, so the arrival
+    counts are back at zero after each launch and the partial sums are added
+    in the same order whichever split finishes last."""
     f = _f()
-    w = workloads.dense_random(64, 1024, 7168, seed=91)
+    w = workloads.dense_random(M, N, K, seed=91)
     w2 = workloads.dense_random(33, 1000, 2048, seed=92)
-    assert f.plan(0, 64, 1024, 7168).k_splits == 4 and f.plan(0, 33, 1000, 2048).k_splits > 1
+    plan = f.plan(0, M, N, K)
+    assert plan.k_splits > 1 and plan.tile_n == rows and f.plan(0, 33, 1000, 2048).k_splits > 1
     a, b = _dev(w.A), _dev(w.B)
     a2, b2 = _dev(w2.A), _dev(w2.B)
     one = torch.ones(1, device="cuda")
     eager = gpu_bits(f.gemm_nt(a, b, one, one, a_dtype=E4M3, b_dtype=E4M3))
     eager2 = gpu_bits(f.gemm_nt(a2, b2, one, one, a_dtype=E4M3, b_dtype=E4M3))
-    out = torch.empty((64, 1024), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -131,10 +175,11 @@ def test_decode_split_k_graph_replays():
         assert np.array_equal(d2, eager2), f"eager call after replay {i}"
     del g
     ref, r, s, _ = oracle.gemm_nt(w.A, w.B)
-    check(eager, r, s, 1.0, ref_bits=ref, what="split-K 64x1024x7168", **random_allowance(w.A, w.B, E4M3, E4M3, 1.0, s))
+    check(eager, r, s, 1.0, ref_bits=ref, what=f"split-K {M}x{N}x{K}", **random_allowance(w.A, w.B, E4M3, E4M3, 1.0, s))
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 1024, 7168), (17, 1000, 2048), (40, 2056, 7168)])
+@pytest.mark.parametrize("M,N,K", [(64, 1024, 7168), (17, 1000, 2048), (40, 2056, 7168),
+                                   (64, 7168, 4096), (1, 14336, 4096), (1, 4104, 7168)])
 def test_decode_split_k_repeats(M, N, K):
     """50 launches in a row of one split shape, alternating two output
     buffers: every result equals the first bit for bit, and the first is
@@ -142,7 +187,10 @@ def test_decode_split_k_repeats(M, N, K):
     L2 (workgroups (x, y) with x a multiple of 8 apart go to the same XCD);
     were a split's partial sums not yet visible to the last one, some launch
     would differ.  (1000 rows: 63 blocks, a padding column of workgroups;
-    2056 rows: 129 blocks, a grid above 256 workgroups, two per CU.)"""
+    2056 rows: 129 blocks, a grid above 256 workgroups, two per CU; the last
+    three take the waves-on-rows kernel: 2 splits of 112 blocks, 2 splits of
+    224 blocks over 448 workgroups, 3 splits of 65 blocks with a padding
+    column.)"""
     f = _f()
     plan = f.plan(0, M, N, K)
     assert plan.k_splits > 1 and plan.workgroups % 8 == 0

@@ -84,9 +84,30 @@ def test_dense_plan_grid(f):
     assert dec(0, 1, 4096, 7168) == (1, 16, 1, 256)
     assert dec(0, 17, 4096, 7168) == (2, 16, 1, 256)
     assert dec(0, 64, 4096, 7168) == (4, 16, 1, 256)
-    assert dec(0, 64, 8160, 4096) == (4, 16, 1, 510)
     assert dec(0, 64, 8192, 4096) == (4, 32, 1, 256)
-    assert dec(0, 1, 14336, 4096) == (1, 32, 1, 448)
+    assert dec(0, 17, 8192, 7168) == (2, 32, 1, 256)
+    assert dec(0, 1, 16384, 4096) == (1, 32, 1, 512)
+    assert dec(0, 64, 8232, 1024) == (4, 32, 1, 258)    # 8 K steps: never waves on rows
+    # waves on rows (64 weight rows per workgroup): where the blocks above
+    # would load the CUs unevenly (more than 256, not a multiple of 256), and
+    # with more than 32 tokens and >= 28 K steps per split; splits keep >= 16
+    # K steps each and <= 256 workgroups (512 with one token block)
+    assert dec(0, 64, 8160, 4096) == (4, 64, 2, 256)     # 510 blocks of 16: 128 of 64, 2 splits
+    assert dec(0, 1, 14336, 4096) == (1, 64, 2, 448)     # 224 blocks of 64, one token block: 2 splits
+    assert dec(0, 16, 14336, 4096) == (1, 64, 2, 448)
+    assert dec(0, 32, 14336, 4096) == (2, 64, 1, 224)
+    assert dec(0, 64, 14336, 4096) == (4, 64, 1, 224)
+    assert dec(0, 64, 7168, 4096) == (4, 64, 2, 224)
+    assert dec(0, 64, 5120, 7168) == (4, 64, 3, 240)     # 80 blocks, 56 K steps: 3 splits of 19, 19, 18
+    assert dec(0, 1, 4104, 7168) == (1, 64, 3, 72 * 3)   # 257 blocks of 16; 65 of 64 (grid x padded to 72)
+    assert dec(0, 37, 7160, 4000) == (4, 64, 2, 224)     # 32 K steps (the last 32 bytes)
+    assert dec(0, 16, 10240, 2048) == (1, 64, 1, 160)    # 16 K steps: one split
+    assert dec(0, 64, 4096, 14336) == (4, 64, 4, 256)    # 112 K steps: 4 splits of 28
+    assert dec(0, 64, 16384, 4096) == (4, 64, 1, 256)
+    assert dec(0, 64, 8192, 7168) == (4, 64, 2, 256)
+    assert dec(0, 32, 4096, 14336) == (2, 16, 1, 256)    # 32 tokens, balanced: waves on K
+    assert dec(0, 64, 7168, 2048) == (4, 16, 1, 448)     # 16 K steps: 1 split of 112 blocks, < 160 workgroups
+    assert dec(3, 64, 7168, 4096) == (4, 64, 2, 224)     # block-scaled likewise
     assert dec(0, 64, 1024, 7168) == (4, 16, 4, 256)
     assert dec(0, 64, 2000, 7168) == (4, 16, 3, 128 * 3)   # 125 blocks, 56 K steps: 3 splits of 19, 19, 18
     assert dec(0, 64, 1024, 512) == (4, 16, 1, 64)      # 4 K steps: no split

@@ -2,10 +2,11 @@
 fp8_gemm_nt, through the C ABI: the same kernels, so the outputs must be
 bit-identical; also within the stated bound of the oracle.
 
-Two calls in a row on the split-K few-token path, the second with a smaller
-input (fewer weight-row blocks and splits, so the scratch array holds the
-first call's partial sums and counts that must not leak into the second), then
-a call on the tiled path (no scratch).  Collected last so that a failure here
+Calls in a row on the split-K few-token path (the waves-on-rows kernel, then
+the waves-on-K kernel twice), each with smaller weights than the one before
+and the last with fewer weight-row blocks and splits than the second (the
+scratch array keeps each call's partial sums and counts, which must not leak
+into the next), then a call on the tiled path (no scratch).  Collected last so that a failure here
 hides no other test."""
 import numpy as np
 import pytest
@@ -37,7 +38,7 @@ def _run(w, no_alloc):
 
 @pytest.mark.parametrize("order", ["noalloc_first", "alloc_first"])
 def test_noalloc_matches_fp8_gemm_nt(order):
-    shapes = [(64, 1024, 7168, 1), (20, 512, 1536, 2), (300, 520, 384, 3)]
+    shapes = [(64, 7168, 4096, 4), (64, 1024, 7168, 1), (20, 512, 1536, 2), (300, 520, 384, 3)]
     for M, N, K, seed in shapes:
         w = workloads.dense_random(M, N, K, seed=seed, scales=(0.75, 1.5))
         plan = _f().plan(0, M, N, K)
@@ -54,6 +55,7 @@ def test_noalloc_matches_fp8_gemm_nt(order):
         check(d_na, r, s, sc, ref_bits=ref, what=f"noalloc {M}x{N}x{K}",
               **random_allowance(w.A, w.B, w.a_fmt, w.b_fmt, sc, s))
     assert _f().plan(0, 64, 1024, 7168).k_splits == 4 and _f().plan(0, 20, 512, 1536).k_splits == 3
+    assert _f().plan(0, 64, 7168, 4096).tile_n == 64 and _f().plan(0, 64, 7168, 4096).k_splits == 2
 
 
 def test_noalloc_needs_out():

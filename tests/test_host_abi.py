@@ -108,6 +108,11 @@ def test_dense_plan_grid(f):
     assert dec(0, 32, 4096, 14336) == (2, 16, 1, 256)    # 32 tokens, balanced: waves on K
     assert dec(0, 64, 7168, 2048) == (4, 16, 1, 448)     # 16 K steps: 1 split of 112 blocks, < 160 workgroups
     assert dec(3, 64, 7168, 4096) == (4, 64, 2, 224)     # block-scaled likewise
+    # K = 0 and short K never reach the split arithmetic of either kernel
+    assert dec(0, 40, 24, 0) == (4, 16, 1, 2)
+    assert dec(3, 40, 24, 0) == (4, 16, 1, 2)
+    assert dec(0, 1, 14336, 0) == (1, 32, 1, 448)
+    assert dec(0, 64, 14336, 1920) == (4, 32, 1, 448)    # 15 K steps
     assert dec(0, 64, 1024, 7168) == (4, 16, 4, 256)
     assert dec(0, 64, 2000, 7168) == (4, 16, 3, 128 * 3)   # 125 blocks, 56 K steps: 3 splits of 19, 19, 18
     assert dec(0, 64, 1024, 512) == (4, 16, 1, 64)      # 4 K steps: no split
@@ -121,6 +126,23 @@ def test_dense_plan_grid(f):
     assert f.plan(0, 256, 256, 256).tile_m == 64
     assert f.plan(0, 257, 256, 256).variant == 2         # M > 256: tiled
     assert f.plan(0, 256, 257, 256).variant == 2         # 4 tiled workgroups: tiled
+
+
+def test_dense_plan_edges_never_fault(f):
+    """The plan over a grid of edge sizes (zeros, one, block and step
+    boundaries) for the dense forms: every call returns, and every decode plan
+    is self-consistent (K splits >= 1, a grid of whole blocks x splits)."""
+    for m in (0, 1, 16, 17, 33, 64, 65):
+        for n in (0, 1, 15, 16, 63, 64, 65, 2048, 4096, 4104, 8192, 14336, 16384, 16448):
+            for k in (0, 16, 112, 128, 1024, 1920, 2048, 4096, 7168, 14336):
+                for op in (0, 3):
+                    p = f.plan(op, m, n, k)
+                    if p.variant == 4:
+                        assert p.k_splits >= 1 and p.workgroups >= 1, (op, m, n, k)
+                        blocks = -(-n // p.tile_n)
+                        if p.k_splits > 1:
+                            assert p.workgroups == 8 * (-(-blocks // 8)) * p.k_splits, (op, m, n, k)
+                            assert -(-(-(-k // 128)) // p.k_splits) >= 1, (op, m, n, k)
 
 
 def test_masked_plan_uses_hint_not_results(f):

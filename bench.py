@@ -1024,6 +1024,7 @@ def main():
                 r = bench_decode(torch, f, M, N, K, steps, warmup, timer)
                 out.append({"M": M, "N": N, "K": K, "kernel_us_mean": r["kernel_ms_mean"] * 1e3, **timing_fields(r),
                             "variant": f.plan(0, M, N, K).variant, "k_splits": f.plan(0, M, N, K).k_splits,
+                            "rows_per_workgroup": f.plan(0, M, N, K).tile_n,
                             "roofline": {"bound": "hbm", "achieved": r["gbs_kernel"], "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": r["gbs_kernel"] / PEAK_HBM_GBS,
                                          "algorithmic_bytes": r["bytes"]}})

@@ -129,6 +129,26 @@ def test_decode_rows_matches_oracle(M, N, K, fa, fb):
           allowance=hw_allowance_blockscaled(wb.A, wb.B, 0, 0, wb.sa, wb.sb, s), max_allowed=random_cap(d.size, K))
 
 
+@pytest.mark.parametrize("M,N,K,rows", [
+    (1, 4096, 7168, 16), (16, 4096, 7168, 16), (32, 4096, 7168, 16), (64, 4096, 7168, 16),
+    (1, 14336, 4096, 64), (16, 14336, 4096, 64), (32, 14336, 4096, 64), (64, 14336, 4096, 64),
+    (1, 2048, 7168, 16), (64, 2048, 7168, 16),
+])
+def test_bench_decode_shapes_full(M, N, K, rows):
+    """Every few-token shape the benchmark times, with its inputs (A and B
+    ~N(0,1) E4M3, seed 13) and in its launch configuration (the plan's kernel
+    and K splits), every output against the oracle under the stated bound."""
+    f = _f()
+    plan = f.plan(0, M, N, K)
+    assert plan.variant == 4 and plan.tile_n == rows
+    print(f"[bench decode] M={M} N={N} K={K} rows/wg={plan.tile_n} k_splits={plan.k_splits}", flush=True)
+    w = workloads.dense_random(M, N, K, seed=13, std=1.0)
+    one = torch.ones(1, device="cuda")
+    d = gpu_bits(f.gemm_nt(_dev(w.A), _dev(w.B), one, one, a_dtype=w.a_fmt, b_dtype=w.b_fmt))
+    ref, r, s, _ = oracle.gemm_nt(w.A, w.B, w.a_fmt, w.b_fmt)
+    check(d, r, s, 1.0, ref_bits=ref, what=f"bench decode {M}x{N}x{K}")
+
+
 def test_decode_deterministic():
     w = workloads.dense_random(32, 4096, 7168, seed=77)
     a, b = _dev(w.A), _dev(w.B)

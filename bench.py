@@ -544,6 +544,8 @@ COUNTER_TARGETS = {
                        "contiguous grouped prefill GEMM, 65536 routed rows over 32 experts, N=4096 K=7168 (seed 5)"),
     "decode_64": ("decode_kernel_dense_64x4096x7168", "decode_kernel<4, 1, 4, 0, 0, 2, 0, 1>",
                   "dense few-token GEMM M=64 N=4096 K=7168 (seed 13)"),
+    "decode_rows_64": ("decode_rows_kernel_dense_64x14336x4096", "decode_rows_kernel<4, 0, 0, 0, 2, 1>",
+                       "dense few-token GEMM M=64 N=14336 K=4096, waves on rows (seed 13)"),
 }
 COPY_PATTERN = "neg_kernel"
 PROFILE_LAUNCHES = 6
@@ -592,6 +594,17 @@ def profile_run():
     torch.cuda.synchronize()
     fl, by = dense_work(64, 4096, 7168)
     work["decode_64"] = {"flops": fl, "bytes": by}
+    del a, b, out
+
+    log("profile: dense decode 64x14336x4096 (waves on rows)")
+    wd = workloads.dense_random(64, 14336, 4096, seed=13, std=1.0)
+    a, b = dev(torch, wd.A), dev(torch, wd.B)
+    out = torch.empty((64, 14336), dtype=torch.bfloat16, device="cuda")
+    for _ in range(PROFILE_LAUNCHES):
+        f.gemm_nt(a, b, one, one, out=out, a_dtype=wd.a_fmt, b_dtype=wd.b_fmt)
+    torch.cuda.synchronize()
+    fl, by = dense_work(64, 14336, 4096)
+    work["decode_rows_64"] = {"flops": fl, "bytes": by}
     del a, b, out
 
     log("profile: masked grouped decode")

@@ -149,6 +149,32 @@ def test_bench_decode_shapes_full(M, N, K, rows):
     check(d, r, s, 1.0, ref_bits=ref, what=f"bench decode {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,rows", [(40, 1000, 2048, 16), (37, 7160, 4000, 64), (16, 10240, 2048, 64), (64, 8232, 1024, 32)])
+def test_decode_strided_operands_and_output(M, N, K, rows):
+    """Both few-token kernels (split and unsplit) with row strides above K
+    for A and B and above N for D: the outputs match the oracle and the
+    padding columns of D keep their sentinel."""
+    f = _f()
+    assert f.plan(0, M, N, K).tile_n == rows
+    print(f"[decode strided] M={M} N={N} K={K} rows/wg={rows}", flush=True)
+    w = workloads.dense_random(M, N, K, seed=M + N + K + 1)
+    A = np.zeros((M, K + 48), np.uint8)
+    A[:, :K] = w.A
+    B = np.zeros((N, K + 16), np.uint8)
+    B[:, :K] = w.B
+    a = _dev(A)[:, :K]
+    b = _dev(B)[:, :K]
+    big = torch.full((M, N + 40), -7.0, dtype=torch.bfloat16, device="cuda")
+    out = big[:, :N]
+    one = torch.ones(1, device="cuda")
+    f.gemm_nt(a, b, one, one, out=out, a_dtype=E4M3, b_dtype=E4M3)
+    torch.cuda.synchronize()
+    ref, r, s, _ = oracle.gemm_nt(w.A, w.B)
+    check(gpu_bits(out), r, s, 1.0, ref_bits=ref, what=f"decode strided {M}x{N}x{K}",
+          **random_allowance(w.A, w.B, E4M3, E4M3, 1.0, s))
+    assert (big[:, N:] == -7.0).all()
+
+
 def test_decode_deterministic():
     w = workloads.dense_random(32, 4096, 7168, seed=77)
     a, b = _dev(w.A), _dev(w.B)

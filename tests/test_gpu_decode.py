@@ -175,6 +175,31 @@ def test_decode_strided_operands_and_output(M, N, K, rows):
     assert (big[:, N:] == -7.0).all()
 
 
+# Drawn once with numpy's default_rng(2024): M in [1, 64], N in [4000, 15500),
+# K a multiple of 16 in [1920, 8320); the plan's rows per workgroup and K
+# splits recorded beside each (waves on rows for 9 of the 14).
+@pytest.mark.parametrize("M,N,K,rows,splits", [
+    (16, 11772, 2496, 64, 1), (14, 7652, 3888, 16, 1), (59, 13193, 7776, 64, 1), (64, 4903, 2816, 16, 1),
+    (56, 4905, 2976, 16, 1), (12, 14508, 4208, 64, 2), (17, 5950, 4848, 64, 2), (38, 13202, 5856, 64, 1),
+    (64, 5211, 5040, 64, 2), (37, 11906, 1936, 64, 1), (13, 9348, 2336, 32, 1), (63, 11377, 7024, 64, 1),
+    (33, 10863, 4128, 64, 1), (21, 5490, 3232, 16, 1),
+])
+def test_decode_random_shapes(M, N, K, rows, splits):
+    """Random few-token shapes around the plan's boundaries between the two
+    kernels (ragged M, N and K): the plan is the recorded one and every output
+    matches the oracle."""
+    f = _f()
+    plan = f.plan(0, M, N, K)
+    assert (plan.tile_n, plan.k_splits) == (rows, splits)
+    print(f"[decode random] M={M} N={N} K={K} rows/wg={rows} k_splits={splits}", flush=True)
+    w = workloads.dense_random(M, N, K, seed=N + K, scales=(0.5, 1.25))
+    d = gpu_bits(f.gemm_nt(_dev(w.A), _dev(w.B), torch.tensor([w.sa], device="cuda"), torch.tensor([w.sb], device="cuda"),
+                           a_dtype=w.a_fmt, b_dtype=w.b_fmt))
+    ref, r, s, _ = oracle.gemm_nt(w.A, w.B, w.a_fmt, w.b_fmt, w.sa, w.sb)
+    sc = abs(w.sa * w.sb)
+    check(d, r, s, sc, ref_bits=ref, what=f"decode random {M}x{N}x{K}", **random_allowance(w.A, w.B, w.a_fmt, w.b_fmt, sc, s))
+
+
 def test_decode_deterministic():
     w = workloads.dense_random(32, 4096, 7168, seed=77)
     a, b = _dev(w.A), _dev(w.B)

@@ -1297,14 +1297,15 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
 
     // Token DMA: instruction i of this wave covers staged rows
     // (wave * TDMA + i) * 8 .. +8; lane l deposits row l / 8, stored chunk
-    // l % 8, loading logical chunk (l % 8) ^ key(row) (the 128-byte-row
-    // swizzle of swz()).
+    // l % 8, loading logical chunk (l % 8) ^ key(row) with the weights' key
+    // (row >> 1) & 7, under which the fragment reads of any 16 rows are free of
+    // bank conflicts.
     uint32_t t_dma_off[TDMA];
     uint32_t t_dma_kc[TDMA];
 #pragma unroll
     for (int i = 0; i < TDMA; ++i) {
         const int row = (wave * TDMA + i) * 8 + (lane >> 3);
-        const uint32_t c = ((uint32_t)(lane & 7) ^ (row & 7u) ^ ((row >> 3) & 1u)) & 7u;
+        const uint32_t c = ((uint32_t)(lane & 7) ^ (((uint32_t)row >> 1) & 7u)) & 7u;
         t_dma_kc[i] = c * 16;
         t_dma_off[i] = (uint32_t)((int64_t)row * p.lda) + c * 16;
     }
@@ -1313,7 +1314,7 @@ __global__ __launch_bounds__(256, 1) void swap_kernel(GemmParams p) {
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
         const uint32_t row = (uint32_t)(c * 16 + r16);
-        const uint32_t key = (row & 7u) ^ ((row >> 3) & 1u);
+        const uint32_t key = (row >> 1) & 7u;
         t_frag[c][0] = row * ROWB + ((((uint32_t)kg) ^ key) & 7u) * 16u;
         t_frag[c][1] = row * ROWB + ((((uint32_t)kg + 4u) ^ key) & 7u) * 16u;
     }
@@ -1832,12 +1833,14 @@ __global__ __launch_bounds__(256, OCC) void decode_rows_kernel(GemmParams p) {
     const uint32_t wf1 = (uint32_t)r16 * 128u + (((uint32_t)(4 + kg) ^ wkey) * 16u);
     // Token copies: instruction i of wave w fills token rows (w TDMA + i) 8 ..
     // +8 of the slot, lane l row l / 8, position l % 8 holding logical chunk
-    // (l % 8) ^ f(row), f(r) = (r & 7) ^ ((r >> 3) & 1) (the swizzle of swz()).
+    // (l % 8) ^ ((row >> 1) & 7), the weights' key: the fragment reads of any
+    // 16 rows are then free of bank conflicts.  (The key (r & 7) ^ ((r >> 3) &
+    // 1) of swz() left 44% of the LDS-active cycles in conflicts here.)
     uint32_t t_off[TDMA], t_kc[TDMA];
 #pragma unroll
     for (int i = 0; i < TDMA; ++i) {
         const uint32_t row = (uint32_t)((wave * TDMA + i) * 8 + (lane >> 3));
-        const uint32_t c = ((uint32_t)(lane & 7) ^ (row & 7u) ^ ((row >> 3) & 1u)) & 7u;
+        const uint32_t c = ((uint32_t)(lane & 7) ^ ((row >> 1) & 7u)) & 7u;
         t_kc[i] = c * 16u;
         t_off[i] = row * (uint32_t)p.lda + c * 16u;
     }
@@ -1845,7 +1848,7 @@ __global__ __launch_bounds__(256, OCC) void decode_rows_kernel(GemmParams p) {
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
         const uint32_t row = (uint32_t)(c * 16 + r16);
-        const uint32_t key = (row & 7u) ^ ((row >> 3) & 1u);
+        const uint32_t key = (row >> 1) & 7u;
         t_frag[c][0] = row * 128u + ((((uint32_t)kg) ^ key) & 7u) * 16u;
         t_frag[c][1] = row * 128u + ((((uint32_t)kg + 4u) ^ key) & 7u) * 16u;
     }

@@ -109,7 +109,10 @@ int token_blocks_for(int m) {
 //    4096: 21.3 -> 17.2, 64 x 8192 x 7168: 16.8 -> 16.3).
 // Its splits: as many as keep at least 16 K steps each and at most 256
 // workgroups (512 with one token block); not taken below 160 workgroups or
-// 16 K steps.
+// 16 K steps, nor with one token block over 16-row blocks beyond 64 K steps
+// (1 x 7168 x 16384: 24.4 us on the waves-on-K kernel, 27.6-35.5 with 1-4
+// splits; 16 x 7168 x 16384: 26.8 against 28.0; up to 64 steps it won,
+// 1 x 7168 x 8192 with 4 splits 14.25 -> 13.87).
 // At 64 x 4096 x 7168 (4 splits of 14 steps) it measured 13.2 against 12.4
 // us, and with 32 or fewer tokens on balanced grids it was 1-7% slower.
 struct DecodeShape {
@@ -142,7 +145,10 @@ DecodeShape decode_shape(int64_t m, int64_t n, int64_t k) {
     if (want < 1) want = 1;
     const int64_t ksteps = cdiv(nk, want);
     const int64_t splits = cdiv(nk, ksteps);
-    if (rblocks * splits >= 160 && (uneven || (d.cb == 4 && ksteps >= 28))) {
+    // one token block over 16-row blocks: the waves-on-K kernel's long loops
+    // (two workgroups on most CUs) stream as fast beyond 64 K steps
+    const bool short_tokens_long_k = d.cb == 1 && d.rb == 1 && nk > 64;
+    if (rblocks * splits >= 160 && !short_tokens_long_k && (uneven || (d.cb == 4 && ksteps >= 28))) {
         d.rb = 4;
         d.blocks = (int)rblocks;
         d.splits = (int)splits;

@@ -107,6 +107,10 @@ def test_dense_plan_grid(f):
     assert dec(0, 64, 8192, 7168) == (4, 64, 2, 256)
     assert dec(0, 32, 4096, 14336) == (2, 16, 1, 256)    # 32 tokens, balanced: waves on K
     assert dec(0, 64, 7168, 2048) == (4, 16, 1, 448)     # 16 K steps: 1 split of 112 blocks, < 160 workgroups
+    assert dec(0, 1, 7168, 8192) == (1, 64, 4, 448)      # one token block, 64 K steps: waves on rows
+    assert dec(0, 16, 7168, 16384) == (1, 16, 1, 448)    # one token block over 16-row blocks, 128 K steps: waves on K
+    assert dec(0, 17, 7168, 16384) == (2, 64, 2, 224)    # two token blocks: waves on rows
+    assert dec(0, 1, 10240, 16384) == (1, 64, 3, 480)    # 32-row blocks: waves on rows, 3 splits
     assert dec(3, 64, 7168, 4096) == (4, 64, 2, 224)     # block-scaled likewise
     # K = 0 and short K never reach the split arithmetic of either kernel
     assert dec(0, 40, 24, 0) == (4, 16, 1, 2)

@@ -200,6 +200,52 @@ def test_decode_random_shapes(M, N, K, rows, splits):
     check(d, r, s, sc, ref_bits=ref, what=f"decode random {M}x{N}x{K}", **random_allowance(w.A, w.B, w.a_fmt, w.b_fmt, sc, s))
 
 
+_FIRST_CALL_CAPTURED = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np, torch
+import fp8_gemm_amd as f, oracle, workloads
+from tests._parity import check, gpu_bits, random_allowance
+M, N, K = 64, 7168, 4096
+plan = f.plan(0, M, N, K)
+assert plan.tile_n == 64 and plan.k_splits == 2, (plan.tile_n, plan.k_splits)
+w = workloads.dense_random(M, N, K, seed=93)
+a = torch.from_numpy(w.A).cuda()
+b = torch.from_numpy(w.B).cuda()
+one = torch.ones(1, device="cuda")
+out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):
+    f.gemm_nt(a, b, one, one, out=out, a_dtype=0, b_dtype=0)
+ref, r, s, _ = oracle.gemm_nt(w.A, w.B)
+allow = random_allowance(w.A, w.B, 0, 0, 1.0, s)
+for i in range(2):
+    out.fill_(7.0)
+    g.replay()
+    torch.cuda.synchronize()
+    check(gpu_bits(out), r, s, 1.0, ref_bits=ref, what=f"captured first call, replay {i}", **allow)
+eager = gpu_bits(f.gemm_nt(a, b, one, one, a_dtype=0, b_dtype=0))
+check(eager, r, s, 1.0, ref_bits=ref, what="eager call after the capture", **allow)
+print("ok")
+"""
+
+
+def test_split_k_first_call_under_capture():
+    """In a fresh process, the first call of a shape that splits K is captured
+    into a graph: the library allocates nothing during capture and runs that
+    call unsplit, so the replays are correct (within the bound), and the
+    eager call after it (which allocates the workspace and splits) is too."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    print("[capture first call] M=64 N=7168 K=4096 in a subprocess", flush=True)
+    res = subprocess.run([sys.executable, "-c", _FIRST_CALL_CAPTURED, root], cwd=root, capture_output=True,
+                         text=True, timeout=240)
+    assert res.returncode == 0 and res.stdout.strip().endswith("ok"), res.stdout[-2000:] + res.stderr[-4000:]
+
+
 def test_decode_deterministic():
     w = workloads.dense_random(32, 4096, 7168, seed=77)
     a, b = _dev(w.A), _dev(w.B)

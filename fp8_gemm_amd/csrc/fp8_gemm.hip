@@ -510,8 +510,11 @@ constexpr unsigned kDecodeSpreadPad = 16 * 1024;
 // Steps of token copies in flight in the waves-on-rows decode kernel (the
 // weights run one step further ahead).  2 measured up to 13% faster than 1
 // (64 x 14336 x 4096: 18.0 -> 15.7 us; 64 x 4096 x 7168 with 4 splits: 14.4
-// -> 13.2), 3 within 2% of 2.
+// -> 13.2).  Without a K split 3 is 1-2% faster still (32 x 14336 x 4096:
+// 14.71 -> 14.43 us, 64 x 12288 x 4096: 14.76 -> 14.53); with splits 3 was
+// even with 2 or slower (1 x 14336 x 4096, 2 splits: 13.44 -> 13.69).
 constexpr int kDecodeRowsLead = 2;
+constexpr int kDecodeRowsLeadUnsplit = 3;
 
 template <int RB, int CB, int SCL>
 int launch_decode_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
@@ -558,11 +561,17 @@ int launch_decode_rows_lt(int fa, int fb, const GemmParams &p, dim3 grid, hipStr
     return launch_status("decode kernel (waves on rows)");
 }
 
+template <int SCL, int LT>
+int launch_decode_rows_cb(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
+    if (cb == 1) return launch_decode_rows_lt<1, SCL, LT>(fa, fb, p, grid, s);
+    if (cb == 2) return launch_decode_rows_lt<2, SCL, LT>(fa, fb, p, grid, s);
+    return launch_decode_rows_lt<4, SCL, LT>(fa, fb, p, grid, s);
+}
+
 template <int SCL>
 int launch_decode_rows(int cb, int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    if (cb == 1) return launch_decode_rows_lt<1, SCL, kDecodeRowsLead>(fa, fb, p, grid, s);
-    if (cb == 2) return launch_decode_rows_lt<2, SCL, kDecodeRowsLead>(fa, fb, p, grid, s);
-    return launch_decode_rows_lt<4, SCL, kDecodeRowsLead>(fa, fb, p, grid, s);
+    if (p.splits > 1) return launch_decode_rows_cb<SCL, kDecodeRowsLead>(cb, fa, fb, p, grid, s);
+    return launch_decode_rows_cb<SCL, kDecodeRowsLeadUnsplit>(cb, fa, fb, p, grid, s);
 }
 
 // K split as the plan says when `ws` holds a workspace, else over the 4 waves

@@ -544,7 +544,7 @@ COUNTER_TARGETS = {
                        "contiguous grouped prefill GEMM, 65536 routed rows over 32 experts, N=4096 K=7168 (seed 5)"),
     "decode_64": ("decode_kernel_dense_64x4096x7168", "decode_kernel<4, 1, 4, 0, 0, 2, 0, 1>",
                   "dense few-token GEMM M=64 N=4096 K=7168 (seed 13)"),
-    "decode_rows_64": ("decode_rows_kernel_dense_64x14336x4096", "decode_rows_kernel<4, 0, 0, 0, 2, 1>",
+    "decode_rows_64": ("decode_rows_kernel_dense_64x14336x4096", "decode_rows_kernel<4, 0, 0, 0, 3, 1>",
                        "dense few-token GEMM M=64 N=14336 K=4096, waves on rows (seed 13)"),
 }
 COPY_PATTERN = "neg_kernel"

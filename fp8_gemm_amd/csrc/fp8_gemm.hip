@@ -516,9 +516,16 @@ constexpr unsigned kDecodeSpreadPad = 16 * 1024;
 constexpr int kDecodeRowsLead = 2;
 constexpr int kDecodeRowsLeadUnsplit = 3;
 
+// Ring slots per wave of the waves-on-K decode kernel: 3 with one token
+// block over 16-row blocks, else 2.  Deeper rings measured slower, shallower
+// ones faster, interleaved on one box (1 x 4096 x 7168: 7.48 us with 5 slots,
+// 7.31 with 3; 16 x 4096 x 7168 8.16 -> 7.97; 1 x 4096 x 4096 6.22 -> 5.95;
+// 32 x 4096 x 7168 with 2 instead of 3 slots 9.69 -> 9.54; 16 x 8192 x 7168
+// with 2 instead of 3, 12.21 -> 11.92): with one step of weights already in
+// flight per wave across 4 waves, more slots only delay the first step.
 template <int RB, int CB, int SCL>
 int launch_decode_cb(int fa, int fb, const GemmParams &p, dim3 grid, hipStream_t s) {
-    constexpr int D = RB == 1 ? (CB == 1 ? 5 : (CB == 2 ? 3 : 2)) : (CB == 1 ? 3 : 2);
+    constexpr int D = RB == 1 && CB == 1 ? 3 : 2;
     const dim3 block(64 * kDecodeWaves);
     const bool one = (int64_t)grid.x * grid.y <= 256;
 #define FP8G_DEC(FA, FB)                                                                                   \

@@ -33,7 +33,7 @@ profiles/<kernel>_<workload>_counters.txt, the HBM byte counters scaled by what
 they read for a 1 GiB copy of known size.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--only NAME ...] [--no-cpu]
-    python bench.py --profile-run
+    python bench.py --profile-run [--profile-targets NAME ...]
     python bench.py --counters-summary TRACE_DIR FETCH_DIR WRITE_DIR SQ_DIR --counters-command "..."
 """
 from __future__ import annotations
@@ -546,15 +546,26 @@ COUNTER_TARGETS = {
                   "dense few-token GEMM M=64 N=4096 K=7168 (seed 13)"),
     "decode_rows_64": ("decode_rows_kernel_dense_64x14336x4096", "decode_rows_kernel<4, 0, 0, 0, 3, 1>",
                        "dense few-token GEMM M=64 N=14336 K=4096, waves on rows (seed 13)"),
+    "contig_prefill_blockscaled": ("tile16_kernel_contig_prefill_blockscaled",
+                                   "tile16_kernel<256, 256, 2, 0, 0, 2, 1, false>",
+                                   "block-scaled contiguous grouped prefill GEMM, 65536 routed rows over 32 experts, "
+                                   "N=4096 K=7168 (seed 9)"),
+    "dense_4096_bf16": ("ring_kernel_dense_4096_bf16", "ring_kernel<256, 256, 4, 2, 16, 16, 0, 2, 128, 0>",
+                        "dense 4096^3 BF16 GEMM, the comparison path (seed 2)"),
 }
+# Dense matrix-core FLOPs per SIMD per cycle of each target's instruction
+# (FP8 by default; BF16 runs at half that rate).
+MFMA_FLOPS_PER_CYCLE = {"dense_4096_bf16": 1024.0}
+MFMA_COUNT_NOTE = {"dense_4096_bf16": "each 32x32x16 BF16 instruction as 32 cycles, 1024 FLOPs per cycle"}
 COPY_PATTERN = "neg_kernel"
 PROFILE_LAUNCHES = 6
 
 
-def profile_run():
-    """Eager launches of each counter target's workload (and the 1 GiB copy
-    that calibrates the byte counters), PROFILE_LAUNCHES each, for rocprofv3.
-    Prints the algorithmic work of each target as one JSON line."""
+def profile_run(targets=None):
+    """Eager launches of each counter target's workload (all, or those named in
+    `targets`) and of the 1 GiB copy that calibrates the byte counters,
+    PROFILE_LAUNCHES each, for rocprofv3.  Prints the algorithmic work of each
+    target launched as one JSON line."""
     import numpy as np
     import torch
 
@@ -563,6 +574,7 @@ def profile_run():
 
     f.load_library()
     work = {}
+    on = lambda name: targets is None or name in targets
     n = 1 << 28
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -571,72 +583,109 @@ def profile_run():
     torch.cuda.synchronize()
     del src, dst
 
-    log("profile: dense 4096^3 E4M3")
-    w = workloads.dense_square(workloads.E4M3)
-    a, b = dev(torch, w.A), dev(torch, w.B)
-    sa = torch.tensor([w.sa], dtype=torch.float32, device="cuda")
-    sb = torch.tensor([w.sb], dtype=torch.float32, device="cuda")
-    out = torch.empty((4096, 4096), dtype=torch.bfloat16, device="cuda")
-    for _ in range(PROFILE_LAUNCHES):
-        f.gemm_nt(a, b, sa, sb, out=out, a_dtype=w.a_fmt, b_dtype=w.b_fmt)
-    torch.cuda.synchronize()
-    fl, by = dense_work(4096, 4096, 4096)
-    work["dense_4096_e4m3"] = {"flops": fl, "bytes": by}
-    del a, b, out
+    if on("dense_4096_e4m3"):
+        log("profile: dense 4096^3 E4M3")
+        w = workloads.dense_square(workloads.E4M3)
+        a, b = dev(torch, w.A), dev(torch, w.B)
+        sa = torch.tensor([w.sa], dtype=torch.float32, device="cuda")
+        sb = torch.tensor([w.sb], dtype=torch.float32, device="cuda")
+        out = torch.empty((4096, 4096), dtype=torch.bfloat16, device="cuda")
+        for _ in range(PROFILE_LAUNCHES):
+            f.gemm_nt(a, b, sa, sb, out=out, a_dtype=w.a_fmt, b_dtype=w.b_fmt)
+        torch.cuda.synchronize()
+        fl, by = dense_work(4096, 4096, 4096)
+        work["dense_4096_e4m3"] = {"flops": fl, "bytes": by}
+        del a, b, out
 
-    log("profile: dense decode 64x4096x7168")
-    wd = workloads.dense_random(64, 4096, 7168, seed=13, std=1.0)
-    a, b = dev(torch, wd.A), dev(torch, wd.B)
+    if on("dense_4096_bf16"):
+        log("profile: dense 4096^3 BF16")
+        wb = workloads.dense_bf16_square()
+        a = torch.from_numpy(wb.A.view(np.int16)).cuda().view(torch.bfloat16)
+        b = torch.from_numpy(wb.B.view(np.int16)).cuda().view(torch.bfloat16)
+        out = torch.empty((4096, 4096), dtype=torch.bfloat16, device="cuda")
+        for _ in range(PROFILE_LAUNCHES):
+            f.gemm_nt_bf16(a, b, out=out)
+        torch.cuda.synchronize()
+        work["dense_4096_bf16"] = {"flops": 2.0 * 4096 ** 3, "bytes": float(3 * 2 * 4096 * 4096)}
+        del a, b, out, wb
+
     one = torch.ones(1, dtype=torch.float32, device="cuda")
-    out = torch.empty((64, 4096), dtype=torch.bfloat16, device="cuda")
-    for _ in range(PROFILE_LAUNCHES):
-        f.gemm_nt(a, b, one, one, out=out, a_dtype=wd.a_fmt, b_dtype=wd.b_fmt)
-    torch.cuda.synchronize()
-    fl, by = dense_work(64, 4096, 7168)
-    work["decode_64"] = {"flops": fl, "bytes": by}
-    del a, b, out
+    if on("decode_64"):
+        log("profile: dense decode 64x4096x7168")
+        wd = workloads.dense_random(64, 4096, 7168, seed=13, std=1.0)
+        a, b = dev(torch, wd.A), dev(torch, wd.B)
+        out = torch.empty((64, 4096), dtype=torch.bfloat16, device="cuda")
+        for _ in range(PROFILE_LAUNCHES):
+            f.gemm_nt(a, b, one, one, out=out, a_dtype=wd.a_fmt, b_dtype=wd.b_fmt)
+        torch.cuda.synchronize()
+        fl, by = dense_work(64, 4096, 7168)
+        work["decode_64"] = {"flops": fl, "bytes": by}
+        del a, b, out
 
-    log("profile: dense decode 64x14336x4096 (waves on rows)")
-    wd = workloads.dense_random(64, 14336, 4096, seed=13, std=1.0)
-    a, b = dev(torch, wd.A), dev(torch, wd.B)
-    out = torch.empty((64, 14336), dtype=torch.bfloat16, device="cuda")
-    for _ in range(PROFILE_LAUNCHES):
-        f.gemm_nt(a, b, one, one, out=out, a_dtype=wd.a_fmt, b_dtype=wd.b_fmt)
-    torch.cuda.synchronize()
-    fl, by = dense_work(64, 14336, 4096)
-    work["decode_rows_64"] = {"flops": fl, "bytes": by}
-    del a, b, out
+    if on("decode_rows_64"):
+        log("profile: dense decode 64x14336x4096 (waves on rows)")
+        wd = workloads.dense_random(64, 14336, 4096, seed=13, std=1.0)
+        a, b = dev(torch, wd.A), dev(torch, wd.B)
+        out = torch.empty((64, 14336), dtype=torch.bfloat16, device="cuda")
+        for _ in range(PROFILE_LAUNCHES):
+            f.gemm_nt(a, b, one, one, out=out, a_dtype=wd.a_fmt, b_dtype=wd.b_fmt)
+        torch.cuda.synchronize()
+        fl, by = dense_work(64, 14336, 4096)
+        work["decode_rows_64"] = {"flops": fl, "bytes": by}
+        del a, b, out
 
-    log("profile: masked grouped decode")
-    wm = workloads.masked_decode()
-    G, cap, K = wm.A.shape
-    N = wm.B.shape[1]
-    a, b = dev(torch, wm.A), dev(torch, wm.B)
-    sa = torch.tensor([wm.sa], dtype=torch.float32, device="cuda")
-    sb, mm = dev(torch, wm.sb), dev(torch, wm.masked_m)
-    out = torch.empty((G, cap, N), dtype=torch.bfloat16, device="cuda")
-    for _ in range(PROFILE_LAUNCHES):
-        f.grouped_gemm_masked(a, b, sa, sb, mm, out=out, expected_m=32, a_dtype=wm.a_fmt, b_dtype=wm.b_fmt)
-    torch.cuda.synchronize()
-    m = np.clip(wm.masked_m.astype(np.int64), 0, cap)
-    active = int((m > 0).sum())
-    work["masked_decode"] = {"flops": 2.0 * int(m.sum()) * N * K,
-                             "bytes": float(active * N * K + int(m.sum()) * K + 2 * int(m.sum()) * N + 4 * G + 4 * (G + 1))}
-    del a, b, out, wm
+    if on("masked_decode"):
+        log("profile: masked grouped decode")
+        wm = workloads.masked_decode()
+        G, cap, K = wm.A.shape
+        N = wm.B.shape[1]
+        a, b = dev(torch, wm.A), dev(torch, wm.B)
+        sa = torch.tensor([wm.sa], dtype=torch.float32, device="cuda")
+        sb, mm = dev(torch, wm.sb), dev(torch, wm.masked_m)
+        out = torch.empty((G, cap, N), dtype=torch.bfloat16, device="cuda")
+        for _ in range(PROFILE_LAUNCHES):
+            f.grouped_gemm_masked(a, b, sa, sb, mm, out=out, expected_m=32, a_dtype=wm.a_fmt, b_dtype=wm.b_fmt)
+        torch.cuda.synchronize()
+        m = np.clip(wm.masked_m.astype(np.int64), 0, cap)
+        active = int((m > 0).sum())
+        work["masked_decode"] = {"flops": 2.0 * int(m.sum()) * N * K,
+                                 "bytes": float(active * N * K + int(m.sum()) * K + 2 * int(m.sum()) * N
+                                                + 4 * G + 4 * (G + 1))}
+        del a, b, out, wm
 
-    log("profile: contiguous grouped prefill")
-    wc = workloads.contig_prefill()
-    M_total, K = wc.A.shape
-    G, N, _ = wc.B.shape
-    a, b = dev(torch, wc.A), dev(torch, wc.B)
-    sa = torch.tensor([wc.sa], dtype=torch.float32, device="cuda")
-    sb, gi = dev(torch, wc.sb), dev(torch, wc.grp_idx)
-    out = torch.empty((M_total, N), dtype=torch.bfloat16, device="cuda")
-    for _ in range(PROFILE_LAUNCHES):
-        f.grouped_gemm_contig(a, b, sa, sb, gi, out=out, a_dtype=wc.a_fmt, b_dtype=wc.b_fmt)
-    torch.cuda.synchronize()
-    valid = int((wc.grp_idx >= 0).sum())
-    work["contig_prefill"] = {"flops": 2.0 * valid * N * K, "bytes": float(M_total * K + G * N * K + 2 * valid * N)}
+    if on("contig_prefill"):
+        log("profile: contiguous grouped prefill")
+        wc = workloads.contig_prefill()
+        M_total, K = wc.A.shape
+        G, N, _ = wc.B.shape
+        a, b = dev(torch, wc.A), dev(torch, wc.B)
+        sa = torch.tensor([wc.sa], dtype=torch.float32, device="cuda")
+        sb, gi = dev(torch, wc.sb), dev(torch, wc.grp_idx)
+        out = torch.empty((M_total, N), dtype=torch.bfloat16, device="cuda")
+        for _ in range(PROFILE_LAUNCHES):
+            f.grouped_gemm_contig(a, b, sa, sb, gi, out=out, a_dtype=wc.a_fmt, b_dtype=wc.b_fmt)
+        torch.cuda.synchronize()
+        valid = int((wc.grp_idx >= 0).sum())
+        work["contig_prefill"] = {"flops": 2.0 * valid * N * K,
+                                  "bytes": float(M_total * K + G * N * K + 2 * valid * N)}
+        del a, b, sb, gi, out, wc
+
+    if on("contig_prefill_blockscaled"):
+        log("profile: block-scaled contiguous grouped prefill")
+        wc = workloads.contig_blockscaled(8192, 8, 32, 4096, 7168, seed=9)
+        M_total, K = wc.A.shape
+        G, N, _ = wc.B.shape
+        a, b = dev(torch, wc.A), dev(torch, wc.B)
+        sa, sb, gi = dev(torch, wc.sa), dev(torch, wc.sb), dev(torch, wc.grp_idx)
+        out = torch.empty((M_total, N), dtype=torch.bfloat16, device="cuda")
+        for _ in range(PROFILE_LAUNCHES):
+            f.grouped_gemm_contig_blockscaled(a, b, sa, sb, gi, out=out, a_dtype=wc.a_fmt, b_dtype=wc.b_fmt)
+        torch.cuda.synchronize()
+        valid = int((wc.grp_idx >= 0).sum())
+        work["contig_prefill_blockscaled"] = {"flops": 2.0 * valid * N * K,
+                                              "bytes": float(M_total * K + G * N * K + 2 * valid * N
+                                                             + wc.sa.nbytes + wc.sb.nbytes)}
+        del a, b, sa, sb, gi, out, wc
     print(json.dumps({"profile_run": True, "work": work}), flush=True)
 
 
@@ -854,6 +903,8 @@ def counters_summary(trace_dir, fetch_dir, write_dir, sq_dir, command, work_json
     kf, kw = nbytes / (copy_f * 1024.0), nbytes / (copy_w * 1024.0)
     h = kernel_source_hash()
     for name, (stem, pattern, what) in COUNTER_TARGETS.items():
+        if work and name not in work:
+            continue                # not launched by this --profile-run
         durs = _trace_durations(trace_dir, pattern)
         dur = statistics.mean(durs)
         f_kib, nf = _per_dispatch(fr, pattern, "FETCH_SIZE")
@@ -907,14 +958,15 @@ def counters_summary(trace_dir, fetch_dir, write_dir, sq_dir, command, work_json
             (f"  effective clock: not measurable ({clock:.3f} GHz from the ratio, above the copy's {copy_clk:.3f}: "
              f"the counter window is longer than this short dispatch)"),
             (f"  mfma_busy_fraction: {mfma_busy:.4f}  (SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x kernel cycles); the "
-             f"counter counts each 16x16x128 FP8 instruction as 32 cycles)") if clock_ok else
+             f"counter counts {MFMA_COUNT_NOTE.get(name, 'each 16x16x128 FP8 instruction as 32 cycles')})") if clock_ok else
             (f"  MFMA busy: at most {mfma_busy:.4f} of the counter window (SQ_VALU_MFMA_BUSY_CYCLES / "
              f"(1024 SIMDs x window cycles))"),
             f"  lds_bank_conflict_fraction: {sq['SQ_LDS_BANK_CONFLICT'] / sq['SQ_LDS_IDX_ACTIVE'] if sq['SQ_LDS_IDX_ACTIVE'] else 0.0:.4f}"
             f"  (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE)",
         ]
         if w.get("flops") and clock_ok:
-            lines.append(f"  MFMA-bound time at the effective clock: {w['flops'] / (SIMDS * 2048.0 * clock * 1e9) * 1e6:.2f} us "
+            rate = MFMA_FLOPS_PER_CYCLE.get(name, 2048.0)
+            lines.append(f"  MFMA-bound time at the effective clock: {w['flops'] / (SIMDS * rate * clock * 1e9) * 1e6:.2f} us "
                          f"(against {dur * 1e6:.2f} us traced)")
         path = os.path.join(PROFILE_DIR, f"{stem}_counters.txt")
         with open(path, "w") as fh:
@@ -933,6 +985,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--profile-run", action="store_true",
                     help="eager launches of the counter targets' workloads, for rocprofv3 (no timing)")
+    ap.add_argument("--profile-targets", nargs="+", default=None, choices=sorted(COUNTER_TARGETS),
+                    help="with --profile-run: only these counter targets (default: all)")
     ap.add_argument("--counters-summary", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "SQ_DIR"),
                     default=None, help="write profiles/*_counters.txt from rocprofv3 output directories (no GPU work)")
     ap.add_argument("--counters-command", default="",
@@ -969,7 +1023,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     if args.profile_run:
-        profile_run()
+        profile_run(args.profile_targets)
         return
     timer = Timer(torch)
     want = set(args.only) if args.only else {"dense", "masked", "masked_table", "masked_bs", "contig", "contig_bs",

@@ -342,6 +342,23 @@ def test_k_tail_regression_shapes_sampled(M, N, K):
           allowance=hw_allowance_points(w.A, w.B, ii, jj, E4M3, E4M3, 1.0, s), max_allowed=random_cap(len(ii), K))
 
 
+# Seeded random shapes (M 65..4096, N 16..16384, K a multiple of 16 up to
+# 2048, random formats), three for each tile class the planner picks: the
+# plan is the recorded one (tile class, workgroups) and every output matches
+# the oracle.
+@pytest.mark.parametrize("M,N,K,a_fmt,b_fmt,variant,workgroups", [
+    (2155, 7030, 576, 1, 0, 1, 252), (3804, 4201, 400, 1, 1, 1, 255), (1432, 9417, 560, 1, 0, 1, 222),
+    (154, 6359, 1904, 1, 1, 2, 50), (1688, 3972, 1184, 1, 1, 2, 224), (2075, 1076, 80, 1, 1, 2, 85),
+    (1019, 8752, 1328, 0, 0, 5, 184), (2223, 4482, 1056, 0, 0, 5, 216), (722, 11269, 1120, 1, 0, 5, 177),
+    (2485, 10412, 384, 0, 0, 6, 470), (3354, 11734, 176, 1, 1, 6, 742), (1844, 13866, 48, 1, 1, 6, 496),
+])
+def test_tiled_random_shapes(M, N, K, a_fmt, b_fmt, variant, workgroups):
+    plan = _lib().plan(0, M, N, K)
+    assert (plan.variant, plan.workgroups) == (variant, workgroups)
+    w = workloads.dense_random(M, N, K, seed=M + N + K, a_fmt=a_fmt, b_fmt=b_fmt, scales=(0.5, 1.25))
+    _check_dense(w, f"random {M}x{N}x{K} fmt ({a_fmt},{b_fmt}) variant {variant}")
+
+
 def test_deterministic_repeats():
     w = workloads.dense_random(512, 384, 1024, seed=3)
     outs = [run_dense(w.A, w.B, E4M3, E4M3) for _ in range(3)]

@@ -117,6 +117,25 @@ def test_masked_swapab_table_shapes_sampled(m):
     check_masked(w, d, rows_per_group=4)
 
 
+# Seeded random masked configurations (G 1..12, cap 1..300, N a multiple of 8,
+# K a multiple of 16, counts U{0..cap}, random hints and formats): the plan is
+# the recorded one (variant, token blocks of the swapped kernel: 1..12, and
+# the tiled kernel), rows past each count keep the sentinel, and every valid
+# row matches the oracle.
+@pytest.mark.parametrize("G,cap,N,K,hint,a_fmt,b_fmt,variant,token_blocks", [
+    (11, 184, 1128, 928, 18, 0, 1, 3, 2), (6, 162, 1584, 1760, 0, 1, 0, 3, 12), (7, 211, 1344, 256, 0, 0, 1, 2, 0),
+    (8, 127, 1408, 96, 0, 0, 0, 3, 8), (8, 39, 32, 480, 0, 0, 1, 3, 4), (11, 15, 2432, 160, 0, 1, 1, 3, 1),
+    (12, 69, 2128, 544, 54, 1, 0, 3, 4), (1, 219, 2408, 1856, 0, 0, 0, 2, 0), (7, 142, 1208, 2336, 0, 0, 0, 3, 12),
+    (7, 30, 304, 1152, 0, 1, 0, 3, 2),
+])
+def test_masked_random_configs(G, cap, N, K, hint, a_fmt, b_fmt, variant, token_blocks):
+    p = _lib().plan(1, cap, N, K, G, hint)
+    assert (p.variant, p.token_blocks) == (variant, token_blocks)
+    w = workloads.masked_random(G, cap, N, K, seed=G * cap + N + K, a_fmt=a_fmt, b_fmt=b_fmt)
+    d = run_masked(w, expected_m=hint)
+    check_masked(w, d)
+
+
 def test_masked_clamps_counts():
     w = workloads.masked_random(3, 32, 128, 256, seed=43, m_values=[-5, 1000, 7])
     d = run_masked(w)
@@ -245,6 +264,21 @@ def test_contig_long_runs():
 
 def test_contig_formats():
     w = workloads.contig_random(tokens=200, topk=1, G=3, N=136, K=384, seed=53, a_fmt=E5M2, b_fmt=E4M3)
+    d = run_contig(w)
+    check_contig(w, d)
+
+
+# Seeded random contiguous configurations (1..16 experts, Dirichlet-multinomial
+# counts with empty experts, N a multiple of 8, K a multiple of 16, random
+# formats): padding rows keep the sentinel and every routed row matches the
+# oracle.
+@pytest.mark.parametrize("tokens,topk,G,N,K,a_fmt,b_fmt", [
+    (429, 3, 13, 104, 208, 1, 1), (920, 3, 8, 640, 880, 1, 0), (111, 4, 4, 112, 400, 0, 0),
+    (1035, 4, 10, 224, 1152, 1, 0), (366, 3, 7, 3856, 96, 1, 0), (1081, 3, 1, 1240, 272, 0, 0),
+    (903, 2, 1, 224, 160, 1, 0), (308, 1, 16, 3904, 192, 1, 0),
+])
+def test_contig_random_configs(tokens, topk, G, N, K, a_fmt, b_fmt):
+    w = workloads.contig_random(tokens, topk, G, N, K, seed=tokens + G + N + K, a_fmt=a_fmt, b_fmt=b_fmt)
     d = run_contig(w)
     check_contig(w, d)
 

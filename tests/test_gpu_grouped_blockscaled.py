@@ -156,6 +156,32 @@ def test_contig_expert_changes(counts):
     check_contig(w, run_contig(w))
 
 
+def _random_counts(seed, G, long_run):
+    """Per-expert counts: empty experts, partial blocks, runs of a few blocks
+    and, with long_run, one run of more than 64 blocks (the slot's backward
+    scan then takes further rounds)."""
+    rng = np.random.default_rng(seed)
+    c = rng.choice([0, 1, 127, 128, 129, 255, 256, 257, 384, 500, 1000], size=G).astype(np.int64)
+    c += rng.integers(0, 40, size=G) * (c > 0)
+    if long_run:
+        c[int(rng.integers(0, G))] = 66 * 128 + int(rng.integers(1, 128))
+    return c
+
+
+# Seeded random run layouts for the run-aligned tiles: the expert changes at
+# odd and even 128-row blocks, runs of 1 to 67 blocks, empty experts; N a
+# multiple of 8 with a tail inside a 256-column tile, K a multiple of 16.
+@pytest.mark.parametrize("seed,G,N,K,long_run", [
+    (101, 9, 264, 400, False), (102, 12, 136, 256, False), (103, 5, 520, 144, True),
+    (104, 7, 392, 1040, False), (105, 3, 1032, 128, True), (106, 11, 24, 272, False),
+])
+def test_contig_random_runs(seed, G, N, K, long_run):
+    counts = _random_counts(seed, G, long_run)
+    w = workloads.contig_blockscaled(0, 1, G, N, K, seed=seed, counts=counts.tolist(), lds_pad=seed % 9)
+    print(f"[contig bs random] counts={counts.tolist()}", flush=True)
+    check_contig(w, run_contig(w))
+
+
 def test_contig_prefill_sampled():
     w = workloads.contig_blockscaled(8192, 8, 32, 4096, 7168, seed=9)
     check_contig(w, run_contig(w), rows=256, seeded=True)

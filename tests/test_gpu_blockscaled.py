@@ -58,6 +58,22 @@ def test_blockscaled_matches_oracle(M, N, K, fa, fb):
     check_full(w, run_bs(w))
 
 
+# Seeded random shapes (few tokens, 128-row and 256-row tiles; N a multiple of
+# 8, K a multiple of 16, random formats), three per kernel the planner picks:
+# the plan is the recorded one (variant, K splits) and every output matches the
+# oracle.
+@pytest.mark.parametrize("M,N,K,fa,fb,variant,splits", [
+    (16, 9120, 576, E5M2, E4M3, 4, 1), (10, 1696, 992, E5M2, E4M3, 4, 2), (29, 6896, 2432, E5M2, E5M2, 4, 1),
+    (2128, 552, 2096, E5M2, E5M2, 2, 1), (3755, 728, 2304, E5M2, E4M3, 2, 1), (1616, 1288, 464, E4M3, E4M3, 2, 1),
+    (1660, 7416, 592, E5M2, E4M3, 1, 1), (2321, 10600, 32, E4M3, E4M3, 1, 1), (2208, 5016, 608, E4M3, E4M3, 1, 1),
+])
+def test_blockscaled_random_shapes(M, N, K, fa, fb, variant, splits):
+    p = _lib().plan(3, M, N, K)
+    assert (p.variant, p.k_splits) == (variant, splits)
+    w = workloads.dense_blockscaled(M, N, K, seed=2 * M + N + K, a_fmt=fa, b_fmt=fb)
+    check_full(w, run_bs(w))
+
+
 @pytest.mark.parametrize("M,N,K,fa,fb", [
     (4000, 3000, 528, E4M3, E4M3),      # M, N and K tails (K = 4 * 128 + 16)
     (3968, 3840, 1040, E5M2, E4M3),

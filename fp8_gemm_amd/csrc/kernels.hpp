@@ -1570,6 +1570,12 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void decode_kernel(GemmParams p) {
         const bool ok = s < my;
         const bool in0 = ok && (int)(k0 + dch0) < p.K, in1 = ok && (int)(k0 + dch1) < p.K;
         const uint32_t base = ring + (uint32_t)slot * SLOT;
+        // The slot refilled here was read by an earlier step, and no barrier
+        // separates those reads from this copy: the compiler may place that
+        // step's matrix instructions, and with them the wait for its reads,
+        // after this point.  So every LDS read issued so far must have
+        // returned before the copy can overwrite the slot.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
             const uint32_t wb = (uint32_t)(16 * b) * (uint32_t)p.ldb + k0;
@@ -1612,6 +1618,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void decode_kernel(GemmParams p) {
             // values fed the previous step's matrix instructions)
             issue(s0 + d + D - 1, (d + D - 1) % D);
             vmcnt_wait<(D - 1) * NQ>();            // step s0 + d has landed
+            asm volatile("" ::: "memory");         // (and no read of it moves above the wait)
             const uint8_t *slot = wbase + d * SLOT;
             v8i wf[RB];
 #pragma unroll

@@ -10,6 +10,10 @@ repository's own kernels (CPU only: hipcc cross-compiles).
   M0.
 * No kernel spills to scratch memory.
 * No packed FP32 VALU operations and no scalar-memory writes appear anywhere.
+* The waves-on-K few-token kernel (each wave refills its own ring slots, with
+  no barrier between a slot's reads and its refill) issues no direct-to-LDS
+  copy while an LDS read may still be outstanding: in code order, an
+  `s_waitcnt lgkmcnt(0)` lies between every `ds_read` and the next copy.
 """
 import os
 import re
@@ -72,3 +76,41 @@ def test_no_packed_fp32_and_no_scalar_writes(asm):
         op = s.split()[0]
         assert not re.match(r"v_pk_(add|mul|fma)_f32", op), s
         assert not re.match(r"s_(buffer_)?(store|atomic)|s_dcache_(wb|discard)", op), s
+
+
+def _kernels(text):
+    """(mangled name, code lines) of every kernel in the assembly."""
+    name, body = None, []
+    for line in text.splitlines():
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            name, body = m.group(1), []
+        elif name and line.startswith(".Lfunc_end"):
+            yield name, list(_code_lines("\n".join(body)))
+            name = None
+        elif name:
+            body.append(line)
+
+
+def test_decode_ring_refills_wait_for_lds_reads(asm):
+    """A copy into a slot that an earlier step read must not overtake that
+    read.  The block-scaled builds once placed a step's matrix instructions
+    (and the compiler's wait for their LDS reads) after the next refill, so a
+    refill could overwrite a slot before its reads returned: wrong sums in one
+    workgroup now and then."""
+    kernels = copies = 0
+    for name, body in _kernels(asm):
+        if "13decode_kernelI" not in name:
+            continue
+        kernels += 1
+        pending = False
+        for s in body:
+            op = s.split()[0]
+            if op.startswith("ds_read"):
+                pending = True
+            elif op == "s_waitcnt" and re.search(r"lgkmcnt\(0\)", s):
+                pending = False
+            elif re.match(r"buffer_load_dword(x4)? ", s) and s.endswith(" lds"):
+                assert not pending, f"{name}: LDS copy issued with an LDS read outstanding: {s}"
+                copies += 1
+    assert kernels > 0 and copies > 0

@@ -14,6 +14,9 @@ repository's own kernels (CPU only: hipcc cross-compiles).
   no barrier between a slot's reads and its refill) issues no direct-to-LDS
   copy while an LDS read may still be outstanding: in code order, an
   `s_waitcnt lgkmcnt(0)` lies between every `ds_read` and the next copy.
+* The other kernels refill a slot only after a barrier that follows every
+  read of it, so every `s_barrier` must come after an `s_waitcnt lgkmcnt(0)`
+  that follows the last `ds_read` before it.
 """
 import os
 import re
@@ -114,3 +117,22 @@ def test_decode_ring_refills_wait_for_lds_reads(asm):
                 assert not pending, f"{name}: LDS copy issued with an LDS read outstanding: {s}"
                 copies += 1
     assert kernels > 0 and copies > 0
+
+
+def test_barriers_wait_for_lds_reads(asm):
+    """The tiled, swapped and waves-on-rows kernels refill ring slots right
+    after a barrier; that is safe only if no LDS read is outstanding at the
+    barrier (the barrier's fence waits for them)."""
+    barriers = 0
+    for name, body in _kernels(asm):
+        pending = False
+        for s in body:
+            op = s.split()[0]
+            if op.startswith("ds_read"):
+                pending = True
+            elif op == "s_waitcnt" and re.search(r"lgkmcnt\(0\)", s):
+                pending = False
+            elif op == "s_barrier":
+                assert not pending, f"{name}: barrier with an LDS read outstanding"
+                barriers += 1
+    assert barriers > 0

@@ -28,15 +28,18 @@ K grows (S grows with every group, the truncation only with the square root
 of their number on random data), and it shows most where a sum cancels.
 Measured on random data: 1.7e-4 of the elements at K = 16; 1.4e-5 at K = 48
 and 2.7e-6 at K = 80 (E5M2 x E5M2); 2e-7 to 6e-6 at K = 96..144 (an E5M2
-operand, or block scales); none at K >= 256 in E4M3.
+operand, or block scales); none at K >= 256 in E4M3.  Over 280 random
+configurations of every entry point (1482 checks), the largest share in one
+check was 4e-4 for K <= 32, 1.5e-4 for K <= 128 (block-scaled masked groups
+of a few thousand elements), 2.1e-6 for K <= 256 and 0 beyond.
 
 So check() asserts bound (1) alone unless a test passes the allowance H + F
 explicitly, and then only a capped number of elements may need it, each
 within (1) + H + F:
   - the seeded workload configurations pass nothing (bound (1) alone);
   - random inputs pass it with random_cap(): at most 1 in 10^3 elements for
-    K <= 32 (at most four groups of 8), 5 in 10^5 for K <= 256 (at most 32
-    groups), 2 in 10^6 beyond, and at least 4.
+    K <= 32 (at most four groups of 8), 2 in 10^4 for K <= 128, 2 in 10^5 for
+    K <= 256, 2 in 10^6 beyond, and at least 4.
     A systematic error (a dropped or repeated K chunk, a wrong scale, a
     misplaced tile) moves far more elements than that and fails;
   - inputs built to cancel pass it with no cap.
@@ -189,7 +192,7 @@ def check(d_bits, r, s, scale_abs, ref_bits=None, what="", allowance=None, max_a
 
 def random_cap(n, K):
     """How many of n elements of a random-data check may need the allowance."""
-    frac = 1e-3 if K <= 32 else (5e-5 if K <= 256 else 2e-6)
+    frac = 1e-3 if K <= 32 else (2e-4 if K <= 128 else (2e-5 if K <= 256 else 2e-6))
     return max(4, int(np.ceil(n * frac)))
 
 

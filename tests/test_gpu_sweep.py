@@ -7,8 +7,9 @@ forms; shapes, counts, formats, scale-array padding and expected-count hints
 at random, within each entry point's layout rules.  Every output goes through
 the same checks as the targeted tests: the stated bound, with the capped
 matrix-core truncation allowance for random data, and sentinels on every row
-the call must not write.  A sweep of this kind found a race between a ring
-slot's reads and its refill in the few-token kernel's block-scaled builds.
+the call must not write.  (Random shapes of this kind, in the block-scaled
+dense tests, exposed a race between a ring slot's reads and its refill in the
+few-token kernel.)
 """
 import numpy as np
 import pytest

@@ -2,8 +2,8 @@
 
 Each case draws its own configuration from a generator seeded with its index:
 dense (few-token and tiled shapes), block-scaled dense, per-channel dense,
-masked grouped, contiguous grouped, and the block-scaled masked and contiguous
-forms; shapes, counts, formats, scale-array padding and expected-count hints
+masked grouped, contiguous grouped, the block-scaled masked and contiguous
+forms, and the BF16 comparison path; shapes, counts, formats, scale-array padding and expected-count hints
 at random, within each entry point's layout rules.  Every output goes through
 the same checks as the targeted tests: the stated bound, with the capped
 matrix-core truncation allowance for random data, and sentinels on every row
@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 
 import workloads
+from tests import test_gpu_bf16 as TBF
 from tests import test_gpu_blockscaled as TB
 from tests import test_gpu_channelwise as TC
 from tests import test_gpu_dense as TD
@@ -23,7 +24,7 @@ from tests import test_gpu_grouped_blockscaled as TGB
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ("dense", "blockscaled", "channelwise", "masked", "contig", "masked_bs", "contig_bs")
+KINDS = ("dense", "blockscaled", "channelwise", "masked", "contig", "masked_bs", "contig_bs", "bf16")
 CASES = 10                                          # per entry point
 
 
@@ -54,6 +55,10 @@ def test_random_entry_point(i):
         M, N, K = _draw(rng, 2e9, lambda: (m := rows(), n := ri(1, 9000), k := 16 * ri(1, 120), m * n * k))
         which = "".join(c for c in "abc" if rng.random() < 0.6) or "c"
         TC.test_channelwise_matches_oracle(M, N, K, fa, fb, which)
+    elif kind == "bf16":
+        M, N, K = _draw(rng, 1.5e9, lambda: (m := rows(), n := ri(1, 6000), k := 8 * ri(1, 200), m * n * k))
+        w = workloads.dense_bf16_random(M, N, K, seed=i)
+        TBF._check_bf16(w.A, w.B, f"sweep {i} bf16 {M}x{N}x{K}")
     elif kind in ("masked", "masked_bs"):
         G, cap, N, K = _draw(rng, 3e9, lambda: (g := ri(1, 17), c := ri(1, 300), n := 8 * ri(1, 500),
                                                  k := 16 * ri(1, 160), g * c * n * k))

@@ -807,8 +807,12 @@ __global__ __launch_bounds__(256, 1) void tile16_kernel(GemmParams p) {
     constexpr int OCH = BN / 8;
     constexpr int HALF = FN * FM / 2;              // MFMAs per half step
     // the step's one barrier, and the MFMAs that carry the copies
+    // (256 x 256 dense tiles spread their copies up to MFMA 58: 0.3-0.5% faster
+    // than up to 48 at 4096^3 and 8192 x 4096 x 4096 on one box, 1.0-1.5% on a
+    // slower one, where up to 40 was 2.6% slower; the contiguous form, whose
+    // weights come from HBM, keeps 48, having measured 0.7% slower at 58)
     constexpr int kBarAt = BM == 128 ? 10 : (BN == 192 ? 18 : 20), kDmaFrom = kBarAt,
-                  kDmaTo = BM == 128 ? 28 : (BN == 192 ? 46 : 48);
+                  kDmaTo = BM == 128 ? 28 : (BN == 192 ? 46 : (BN == 256 && MODE == MODE_DENSE ? 58 : 48));
     static_assert(((BM == 256 && (BN == 256 || BN == 224 || BN == 192)) || (BM == 128 && BN == 256)) &&
                       FN >= FM / 2 && CPA % 2 == 0, "shape");
     // block scales: each wave's weight rows must lie in one 128-row scale block

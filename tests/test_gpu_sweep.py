@@ -3,7 +3,8 @@
 Each case draws its own configuration from a generator seeded with its index:
 dense (few-token and tiled shapes), block-scaled dense, per-channel dense,
 masked grouped, contiguous grouped, the block-scaled masked and contiguous
-forms, and the BF16 comparison path; shapes, counts, formats, scale-array padding and expected-count hints
+forms, the BF16 comparison path, and the allocation-free dense entry point on
+few-token shapes (with and without split K); shapes, counts, formats, scale-array padding and expected-count hints
 at random, within each entry point's layout rules.  Every output goes through
 the same checks as the targeted tests: the stated bound, with the capped
 matrix-core truncation allowance for random data, and sentinels on every row
@@ -13,8 +14,11 @@ few-token kernel.)
 """
 import numpy as np
 import pytest
+import torch
 
+import oracle
 import workloads
+from tests._parity import check, random_allowance
 from tests import test_gpu_bf16 as TBF
 from tests import test_gpu_blockscaled as TB
 from tests import test_gpu_channelwise as TC
@@ -24,7 +28,7 @@ from tests import test_gpu_grouped_blockscaled as TGB
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ("dense", "blockscaled", "channelwise", "masked", "contig", "masked_bs", "contig_bs", "bf16")
+KINDS = ("dense", "blockscaled", "channelwise", "masked", "contig", "masked_bs", "contig_bs", "bf16", "noalloc")
 CASES = 10                                          # per entry point
 
 
@@ -55,6 +59,19 @@ def test_random_entry_point(i):
         M, N, K = _draw(rng, 2e9, lambda: (m := rows(), n := ri(1, 9000), k := 16 * ri(1, 120), m * n * k))
         which = "".join(c for c in "abc" if rng.random() < 0.6) or "c"
         TC.test_channelwise_matches_oracle(M, N, K, fa, fb, which)
+    elif kind == "noalloc":
+        M, N, K = ri(1, 65), 8 * ri(1, 2000), 16 * ri(16, 600)
+        print(f"[sweep {i}] no-alloc M={M} N={N} K={K} fmt=({fa},{fb}) k_splits={TD._lib().plan(0, M, N, K).k_splits}",
+              flush=True)
+        w = workloads.dense_random(M, N, K, seed=i, a_fmt=fa, b_fmt=fb, scales=(0.75, 1.5))
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        TD._lib().gemm_nt(TD._dev(w.A), TD._dev(w.B), TD._scale(w.sa), TD._scale(w.sb), out=out,
+                          a_dtype=fa, b_dtype=fb, no_alloc=True)
+        torch.cuda.synchronize()
+        d = TD.gpu_bits(out)
+        ref, r, s, _ = oracle.gemm_nt(w.A, w.B, fa, fb, w.sa, w.sb)
+        sc = abs(w.sa * w.sb)
+        check(d, r, s, sc, ref_bits=ref, what=f"sweep {i} no-alloc", **random_allowance(w.A, w.B, fa, fb, sc, s))
     elif kind == "bf16":
         M, N, K = _draw(rng, 1.5e9, lambda: (m := rows(), n := ri(1, 6000), k := 8 * ri(1, 200), m * n * k))
         w = workloads.dense_bf16_random(M, N, K, seed=i)
